@@ -1,0 +1,270 @@
+"""Plain fp64 CPU oracle for BlockRank's block-sparse prefill attention and score readout.
+
+TEST INFRASTRUCTURE.  Only the test suite, the package's smoke check and the bench's
+CPU-baseline leg may import this module.  It shares no code with the HIP path: it is written
+from the pages' definitions, slowly and explicitly, in float64 over the same bf16 input
+values the GPU reads.
+
+Sources (page title, then section / equation):
+  [BR]  "Scalable In-context Ranking with Generative Models" summary (BlockRank), section 3.4:
+        "Blockwise Structured Attention" (token-type rules, chunked implementation),
+        "Score computation procedure" (steps 1-4), "Efficient Attention-Based Inference".
+  [BLOG] BlockRank blog post (hongjun7.github.io): sections on directed attention (mask
+        matrix M with causal diagonal blocks C), complexity (allowed-pair closed form and
+        the p=q=32, N=100, l=128 example), attention supervision (z, alpha', s_k and the
+        identity sum_k s_k = |S|) and direct output (argmax / sorted list).
+  [BS]  "Can Language Models Actually Retrieve In-Context?" (BlockSearch), section 3.2
+        "Block-sparse attention": documents attend causally within their own block, the
+        query block over everything and causally to itself, no instruction prefix.
+
+Readings taken where the pages are silent or disagree (each also listed in the design notes):
+  * Causality inside every segment, diagonal included ([BLOG] diagonal blocks C, [BS] 3.2);
+    [BR] does not say "causal" for documents or the query.
+  * Ragged segments, no padding tokens ([BLOG] ragged l_i) rather than [BR]'s padded chunks.
+  * Query head h reads KV head floor(h / G), G = Hq / Hkv (grouped-query attention; the
+    grouping is not on the pages).
+  * Scale 1/sqrt(d) with d the head dimension, for attention and readout ([BR] step 2);
+    callers may pass another scale.
+  * Readout: per-head softmax over all document tokens of the prompt, summed over signal
+    tokens, averaged over the Hq heads, so sum_k s_k = |S| ([BLOG]); head_scores keeps the
+    per-head sums.  Sum, not mean, over signal tokens ([BR] "sum is used in practice").
+  * Prompts in one call are independent: no attention across prompts, one sort per prompt.
+  * Rank: descending score, ties to the lower document index.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+KIND_I, KIND_D, KIND_Q = 0, 1, 2
+
+
+# --------------------------------------------------------------------------------------
+# inputs
+# --------------------------------------------------------------------------------------
+def to_f64(x: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64; float arrays are just widened."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def token_tables(segment_offsets: np.ndarray, seg_ptr: np.ndarray):
+    """Per token: prompt id, global segment id and kind (I / D / Q).
+
+    Prompt b's segments are [o_0, o_1) = instruction, [o_k, o_{k+1}) = document k for
+    k = 1..N, and the last span = final query, with o = segment_offsets[seg_ptr[b]:seg_ptr[b+1]].
+    """
+    so = np.asarray(segment_offsets, dtype=np.int64)
+    sp = np.asarray(seg_ptr, dtype=np.int64)
+    T = int(so[sp[-1] - 1])
+    prompt = np.full(T, -1, dtype=np.int64)
+    seg = np.full(T, -1, dtype=np.int64)
+    kind = np.full(T, -1, dtype=np.int64)
+    gseg = 0
+    for b in range(len(sp) - 1):
+        offs = so[sp[b]:sp[b + 1]]
+        nseg = len(offs) - 1
+        for s in range(nseg):
+            a, e = int(offs[s]), int(offs[s + 1])
+            prompt[a:e] = b
+            seg[a:e] = gseg
+            kind[a:e] = KIND_I if s == 0 else (KIND_Q if s == nseg - 1 else KIND_D)
+            gseg += 1
+    assert (prompt >= 0).all(), "segment table does not cover every token"
+    return prompt, seg, kind
+
+
+# --------------------------------------------------------------------------------------
+# the mask ([BR] token-type rules; [BLOG] mask matrix M; [BS] 3.2)
+# --------------------------------------------------------------------------------------
+def allowed(i, j, tables) -> np.ndarray:
+    """May row token i read key token j?  (broadcasting over index arrays)
+
+    Same prompt, j <= i, and one of: j in i's own segment (causal diagonal block), j in the
+    instruction (every row after it reads the whole prefix), or i in the final query (the
+    query reads everything before it).
+    """
+    prompt, seg, kind = tables
+    i = np.asarray(i); j = np.asarray(j)
+    same_prompt = prompt[i] == prompt[j]
+    causal = j <= i
+    same_seg = seg[i] == seg[j]
+    return same_prompt & causal & (same_seg | (kind[j] == KIND_I) | (kind[i] == KIND_Q))
+
+
+def allowed_full_diagonal(i, j, tables) -> np.ndarray:
+    """The same block pattern with each diagonal block C counted whole (no causal cut).
+
+    This is the pattern whose size the blog's closed form counts: whole blocks C_I, C_{d_k},
+    C_q plus the instruction column block for documents and the full query row block.
+    """
+    prompt, seg, kind = tables
+    i = np.asarray(i); j = np.asarray(j)
+    same_prompt = prompt[i] == prompt[j]
+    same_seg = seg[i] == seg[j]
+    doc_reads_prefix = (kind[i] == KIND_D) & (kind[j] == KIND_I)
+    return same_prompt & (same_seg | doc_reads_prefix | (kind[i] == KIND_Q))
+
+
+def count_pairs(segment_offsets, seg_ptr, full_diagonal: bool = False, row_block: int = 512) -> int:
+    """Count allowed (row, key) pairs by evaluating the predicate on every pair of each prompt."""
+    tables = token_tables(segment_offsets, seg_ptr)
+    pred = allowed_full_diagonal if full_diagonal else allowed
+    so = np.asarray(segment_offsets, dtype=np.int64); sp = np.asarray(seg_ptr, dtype=np.int64)
+    total = 0
+    for b in range(len(sp) - 1):
+        a, e = int(so[sp[b]]), int(so[sp[b + 1] - 1])
+        keys = np.arange(a, e)
+        for r0 in range(a, e, row_block):
+            rows = np.arange(r0, min(r0 + row_block, e))
+            total += int(pred(rows[:, None], keys[None, :], tables).sum())
+    return total
+
+
+def closed_form_pairs(p: int, lengths: Sequence[int], q: int) -> int:
+    """[BLOG] complexity section: p^2 + sum_i (l_i^2 + p l_i) + q (p + q + sum_i l_i)."""
+    D = sum(int(l) for l in lengths)
+    return p * p + sum(int(l) * int(l) + p * int(l) for l in lengths) + q * (p + q + D)
+
+
+# --------------------------------------------------------------------------------------
+# attention: softmax(Q K^T * scale + M) V  ([BLOG] directed attention)
+# --------------------------------------------------------------------------------------
+def kv_head(h: int, num_q_heads: int, num_kv_heads: int) -> int:
+    """Grouped-query attention: query head h reads KV head floor(h / G), G = Hq / Hkv."""
+    return h // (num_q_heads // num_kv_heads)
+
+
+def _scale(d: int, scale: Optional[float]) -> float:
+    return 1.0 / math.sqrt(d) if (scale is None or scale <= 0) else float(scale)
+
+
+def _masked_softmax_av(q, k, v, mask, scale):
+    """q [R,d], k/v [C,d], mask [R,C] -> (out [R,d], lse [R]) in float64."""
+    s = (q @ k.T) * scale
+    s = np.where(mask, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True)
+    out = (p @ v) / l
+    lse = (m + np.log(l))[:, 0]
+    return out, lse
+
+
+def attn_dense(Q, K, V, segment_offsets, seg_ptr, scale: Optional[float] = None):
+    """Materialise the whole T x T boolean mask and run masked softmax attention per head.
+
+    For small inputs only.  Returns (O [T,Hq,d], lse [T,Hq]) in float64.
+    """
+    Qf, Kf, Vf = to_f64(Q), to_f64(K), to_f64(V)
+    T, Hq, d = Qf.shape
+    Hkv = Kf.shape[1]
+    sc = _scale(d, scale)
+    tables = token_tables(segment_offsets, seg_ptr)
+    idx = np.arange(T)
+    mask = allowed(idx[:, None], idx[None, :], tables)
+    O = np.zeros((T, Hq, d)); lse = np.zeros((T, Hq))
+    for h in range(Hq):
+        g = kv_head(h, Hq, Hkv)
+        O[:, h], lse[:, h] = _masked_softmax_av(Qf[:, h], Kf[:, g], Vf[:, g], mask, sc)
+    return O, lse
+
+
+def attn_rows(Q, K, V, segment_offsets, seg_ptr, rows=None, scale: Optional[float] = None,
+              row_block: int = 256):
+    """Attention for selected rows: per block of rows of one segment, evaluate the predicate
+    against every key of the prompt, gather the keys any row may read, and run a dense
+    float64 masked softmax over them.
+
+    rows: absolute token indices (default: all).  Returns (O [R,Hq,d], lse [R,Hq]) in the
+    order of ``rows``.
+    """
+    T = int(np.asarray(segment_offsets)[-1])
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    Kf, Vf = to_f64(K), to_f64(V)
+    Hkv, d = Kf.shape[1], Kf.shape[2]
+    Hq = np.asarray(Q).shape[1]
+    sc = _scale(d, scale)
+    tables = token_tables(segment_offsets, seg_ptr)
+    prompt, seg, _ = tables
+    so = np.asarray(segment_offsets, dtype=np.int64); sp = np.asarray(seg_ptr, dtype=np.int64)
+    O = np.zeros((len(rows), Hq, d)); lse = np.zeros((len(rows), Hq))
+    order = np.argsort(seg[rows], kind="stable")
+    # blocks of rows that share a segment
+    starts = [0] + [n for n in range(1, len(order)) if seg[rows[order[n]]] != seg[rows[order[n - 1]]]]
+    starts.append(len(order))
+    for a_, e_ in zip(starts[:-1], starts[1:]):
+        for c0 in range(a_, e_, row_block):
+            sel = order[c0:min(c0 + row_block, e_)]
+            r = rows[sel]
+            b = int(prompt[r[0]])
+            pa, pe = int(so[sp[b]]), int(so[sp[b + 1] - 1])
+            keys = np.arange(pa, pe)
+            m = allowed(r[:, None], keys[None, :], tables)
+            cols = keys[m.any(axis=0)]
+            mc = m[:, m.any(axis=0)]
+            qr = to_f64(np.asarray(Q)[r])
+            for h in range(Hq):
+                g = kv_head(h, Hq, Hkv)
+                O[sel, h], lse[sel, h] = _masked_softmax_av(qr[:, h], Kf[cols, g], Vf[cols, g], mc, sc)
+    return O, lse
+
+
+# --------------------------------------------------------------------------------------
+# score readout ([BR] score computation steps 1-4; [BLOG] attention supervision)
+# --------------------------------------------------------------------------------------
+def doc_scores(Q_S, K, doc_offsets, doc_ptr, num_q_heads: Optional[int] = None,
+               scale: Optional[float] = None):
+    """s_k = (1/Hq) sum_h sum_{i in S} sum_{j in d_k} alpha'_{ihj}, alpha' = softmax over all
+    document tokens of the prompt of z_{ihj} = Q_S[i,h] . K[j, h/G] * scale.
+
+    Q_S [B, S, Hq, d]; K [T, Hkv, d]; doc_offsets / doc_ptr as in the segment-table format.
+    Returns (scores [sum N_b], head_scores [Hq, sum N_b]) in float64, where head_scores[h, k]
+    is the signal-token sum for head h alone (scores = head_scores.mean(axis=0)).
+    """
+    Qs, Kf = to_f64(Q_S), to_f64(K)
+    B, S, Hq, d = Qs.shape
+    Hkv = Kf.shape[1]
+    sc = _scale(d, scale)
+    do = np.asarray(doc_offsets, dtype=np.int64); dp = np.asarray(doc_ptr, dtype=np.int64)
+    n_total = int(len(do) - B)
+    head_scores = np.zeros((Hq, n_total))
+    base = 0
+    for b in range(B):
+        offs = do[dp[b]:dp[b + 1]]
+        N = len(offs) - 1
+        a, e = int(offs[0]), int(offs[-1])
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            z = (Qs[b, :, h, :] @ Kf[a:e, g, :].T) * sc          # [S, D]
+            z = z - z.max(axis=1, keepdims=True)
+            w = np.exp(z)
+            alpha = w / w.sum(axis=1, keepdims=True)              # softmax over T_docs
+            per_doc = np.add.reduceat(alpha, offs[:-1] - a, axis=1)  # [S, N]
+            head_scores[h, base:base + N] = per_doc.sum(axis=0)    # sum over signal tokens
+        base += N
+    return head_scores.mean(axis=0), head_scores
+
+
+def rank(scores, doc_ptr) -> np.ndarray:
+    """Per prompt, local document indices in descending score order, ties to the lower index
+    ([BR] argmax / arg-top-K; [BLOG] direct output: a sorted list)."""
+    s = np.asarray(scores)
+    dp = np.asarray(doc_ptr, dtype=np.int64)
+    out: List[int] = []
+    base = 0
+    for b in range(len(dp) - 1):
+        N = int(dp[b + 1] - dp[b] - 1)
+        local = [float(x) for x in s[base:base + N]]
+        out.extend(sorted(range(N), key=lambda k: (-local[k], k)))
+        base += N
+    return np.asarray(out, dtype=np.int32)
+
+
+def allowed_pair_counts(segment_offsets, seg_ptr) -> Tuple[int, int]:
+    """(exact causal count, count with diagonal blocks whole), both by brute-force counting."""
+    return (count_pairs(segment_offsets, seg_ptr, False), count_pairs(segment_offsets, seg_ptr, True))

@@ -1,0 +1,344 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics fix.
+
+Each ``pin_*`` takes the oracle module and raises AssertionError when the oracle disagrees
+with a closed form, a printed number, an invariant, a library routine or a brute-force
+evaluation.  The mutation tests run every pin against deliberately broken copies of the
+oracle and require at least one pin to fail for each, so the pins are known to have teeth.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+import random
+
+import numpy as np
+import torch
+
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# --------------------------------------------------------------------------------------
+# small random inputs
+# --------------------------------------------------------------------------------------
+def random_prompts(rng: random.Random, batch=1, p_max=40, n_max=6, l_max=70, q_max=40, p_min=0):
+    prompts = []
+    for _ in range(batch):
+        p = rng.randint(p_min, p_max)
+        n = rng.randint(1, n_max)
+        lens = [rng.randint(1, l_max) for _ in range(n)]
+        q = rng.randint(1, q_max)
+        prompts.append((p, lens, q))
+    return prompts
+
+
+def small_case(seed, hq=2, hkv=1, d=8, batch=2, n_signal=1, **kw):
+    rng = random.Random(seed)
+    prompts = random_prompts(rng, batch=batch, **kw)
+    prompts = [(p, l, max(q, n_signal)) for (p, l, q) in prompts]
+    return workloads.make_custom(prompts, hq, hkv, d, n_signal, seed)
+
+
+def _f64(x):
+    return (np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------------------
+# mask / pair counts
+# --------------------------------------------------------------------------------------
+def pin_closed_form_counts(orc):
+    """Counting the explicit mask reproduces the blog's closed form (diagonal blocks whole),
+    and the causal count is that minus n(n-1)/2 per segment."""
+    rng = random.Random(1234)
+    for t in range(25):
+        prompts = random_prompts(rng, batch=rng.randint(1, 3), p_min=0)
+        seg, sp, _, _ = workloads.segment_tables(prompts)
+        blk = orc.count_pairs(seg, sp, full_diagonal=True)
+        exact = orc.count_pairs(seg, sp, full_diagonal=False)
+        want_blk = sum(orc.closed_form_pairs(p, l, q) for (p, l, q) in prompts)
+        # closed form, typed independently here from the blog's complexity section
+        ref_blk = sum(p * p + sum(x * x + p * x for x in l) + q * (p + q + sum(l)) for (p, l, q) in prompts)
+        diag = sum(n * (n - 1) // 2 for (p, l, q) in prompts for n in [p, q] + list(l))
+        assert want_blk == ref_blk, (prompts, want_blk, ref_blk)
+        assert blk == ref_blk, (prompts, blk, ref_blk)
+        assert exact == ref_blk - diag, (prompts, exact, ref_blk - diag)
+
+
+def pin_worked_example(orc):
+    """The blog's worked example: p=q=32, N=100, l=128 -> L=12,864, ~165.48M dense pairs,
+    2.46M allowed pairs (printed rounded)."""
+    with open(os.path.join(GOLDEN, "blog_worked_example.json")) as f:
+        g = json.load(f)
+    prompts = [(g["p"], [g["doc_len"]] * g["n_docs"], g["q"])]
+    seg, sp, _, _ = workloads.segment_tables(prompts)
+    L = int(seg[-1])
+    assert L == g["dense_side_printed"]
+    assert round(L * L / 1e6, 2) == g["dense_pairs_printed_millions"]
+    blk = orc.count_pairs(seg, sp, full_diagonal=True)
+    assert round(blk / 1e6, 2) == g["allowed_pairs_printed_millions"], blk
+    assert blk == orc.closed_form_pairs(g["p"], [g["doc_len"]] * g["n_docs"], g["q"])
+
+
+# --------------------------------------------------------------------------------------
+# attention rows reduce to textbook causal attention
+# --------------------------------------------------------------------------------------
+def _sdpa_causal(q, k, v):
+    """torch's scaled_dot_product_attention, causal, float64, GQA by its own rule.
+
+    q [n, Hq, d], k/v [n, Hkv, d] -> [n, Hq, d]"""
+    qt = torch.from_numpy(q).permute(1, 0, 2).unsqueeze(0)
+    kt = torch.from_numpy(k).permute(1, 0, 2).unsqueeze(0)
+    vt = torch.from_numpy(v).permute(1, 0, 2).unsqueeze(0)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True,
+                                                         enable_gqa=qt.shape[1] != kt.shape[1])
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def _check_textbook(orc, w, O, tol=1e-10):
+    Q, K, V = _f64(w.Q), _f64(w.K), _f64(w.V)
+    so, sp = w.segment_offsets, w.seg_ptr
+    for b in range(w.num_prompts):
+        offs = [int(x) for x in so[sp[b]:sp[b + 1]]]
+        a, p_end, q_start, e = offs[0], offs[1], offs[-2], offs[-1]
+        full = _sdpa_causal(Q[a:e], K[a:e], V[a:e])
+        # instruction rows and query rows = rows of plain causal attention over the prompt
+        np.testing.assert_allclose(O[a:p_end], full[:p_end - a], rtol=0, atol=tol)
+        np.testing.assert_allclose(O[q_start:e], full[q_start - a:], rtol=0, atol=tol)
+        # document k rows = last l_k rows of causal attention over [instruction ; d_k]
+        for s in range(1, len(offs) - 2):
+            da, de = offs[s], offs[s + 1]
+            idx = np.r_[a:p_end, da:de]
+            sub = _sdpa_causal(Q[idx], K[idx], V[idx])
+            np.testing.assert_allclose(O[da:de], sub[p_end - a:], rtol=0, atol=tol)
+
+
+def pin_textbook_rows(orc):
+    for seed, (hq, hkv, d) in enumerate([(2, 1, 8), (4, 2, 16), (3, 3, 8), (8, 2, 8)]):
+        w = small_case(100 + seed, hq=hq, hkv=hkv, d=d, batch=2)
+        O, _ = orc.attn_dense(w.Q, w.K, w.V, w.segment_offsets, w.seg_ptr)
+        _check_textbook(orc, w, O)
+        O2, _ = orc.attn_rows(w.Q, w.K, w.V, w.segment_offsets, w.seg_ptr, row_block=7)
+        _check_textbook(orc, w, O2)
+
+
+def pin_textbook_rows_no_prefix(orc):
+    """p = 0 (BlockSearch drops the instruction prefix)."""
+    rng = random.Random(77)
+    prompts = [(0, [rng.randint(1, 30) for _ in range(4)], 9), (0, [5, 1, 17], 3)]
+    w = workloads.make_custom(prompts, 4, 2, 8, 1, 77)
+    O, _ = orc.attn_rows(w.Q, w.K, w.V, w.segment_offsets, w.seg_ptr)
+    _check_textbook(orc, w, O)
+
+
+# --------------------------------------------------------------------------------------
+# brute force from the chunked formulation (BlockRank summary, chunked implementation):
+# documents attend to [K_Inst, K_k], the query to everything, the instruction causally.
+# --------------------------------------------------------------------------------------
+def _brute_chunked(w, scale=None):
+    Q, K, V = _f64(w.Q), _f64(w.K), _f64(w.V)
+    T, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    O = np.zeros_like(Q)
+    so, sp = w.segment_offsets, w.seg_ptr
+    for b in range(w.num_prompts):
+        offs = [int(x) for x in so[sp[b]:sp[b + 1]]]
+        inst = list(range(offs[0], offs[1]))
+        for s in range(len(offs) - 1):
+            seg = list(range(offs[s], offs[s + 1]))
+            for i in seg:
+                if s == 0:
+                    keys = [j for j in inst if j <= i]
+                elif s == len(offs) - 2:
+                    keys = list(range(offs[0], i + 1))
+                else:
+                    keys = inst + [j for j in seg if j <= i]
+                for h in range(Hq):
+                    g = h * Hkv // Hq
+                    z = [sum(Q[i, h, t] * K[j, g, t] for t in range(d)) * sc for j in keys]
+                    mz = max(z)
+                    e = [math.exp(x - mz) for x in z]
+                    tot = sum(e)
+                    for t in range(d):
+                        O[i, h, t] = sum(e[n] * V[keys[n], g, t] for n in range(len(keys))) / tot
+    return O
+
+
+def pin_bruteforce_chunked(orc):
+    for seed, (hq, hkv) in enumerate([(2, 1), (1, 1), (4, 2)]):
+        rng = random.Random(500 + seed)
+        prompts = random_prompts(rng, batch=2, p_max=5, n_max=3, l_max=6, q_max=5)
+        w = workloads.make_custom(prompts, hq, hkv, 4, 1, 500 + seed)
+        ref = _brute_chunked(w)
+        O, _ = orc.attn_dense(w.Q, w.K, w.V, w.segment_offsets, w.seg_ptr)
+        O2, _ = orc.attn_rows(w.Q, w.K, w.V, w.segment_offsets, w.seg_ptr, row_block=3)
+        np.testing.assert_allclose(O, ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(O2, ref, rtol=0, atol=1e-12)
+
+
+def pin_special_rows(orc):
+    """A row that may only read itself returns its own V; its LSE is its own logit."""
+    w = small_case(9, hq=2, hkv=1, d=8, batch=1, p_min=1)
+    O, lse = orc.attn_dense(w.Q, w.K, w.V, w.segment_offsets, w.seg_ptr)
+    Q, K, V = _f64(w.Q), _f64(w.K), _f64(w.V)
+    for h in range(2):
+        np.testing.assert_array_equal(O[0, h], V[0, 0])
+        assert abs(lse[0, h] - Q[0, h] @ K[0, 0] / math.sqrt(8)) < 1e-12
+    # without a prefix, the first token of every document reads only itself
+    prompts = [(0, [3, 1, 4], 2)]
+    w = workloads.make_custom(prompts, 2, 1, 8, 1, 10)
+    O, lse = orc.attn_rows(w.Q, w.K, w.V, w.segment_offsets, w.seg_ptr)
+    V = _f64(w.V)
+    for t in (0, 3, 4):
+        for h in range(2):
+            np.testing.assert_array_equal(O[t, h], V[t, 0])
+
+
+def pin_document_isolation(orc):
+    """A document's outputs do not change when other documents (or the query) change, and
+    move with the document when documents are permuted."""
+    rng = random.Random(31)
+    lens = [rng.randint(3, 20) for _ in range(5)]
+    w = workloads.make_custom([(6, lens, 4)], 4, 2, 8, 1, 31)
+    O, _ = orc.attn_rows(w.Q, w.K, w.V, w.segment_offsets, w.seg_ptr)
+    so = [int(x) for x in w.segment_offsets]
+    # alter every document except doc 2 and the query
+    Q2, K2, V2 = w.Q.copy(), w.K.copy(), w.V.copy()
+    keep = range(so[3], so[4])
+    noise = np.random.default_rng(5)
+    for t in range(so[1], so[-1]):
+        if t not in keep:
+            K2[t] = noise.integers(0x3000, 0x4000, size=K2[t].shape, dtype=np.uint16)
+            V2[t] = noise.integers(0x3000, 0x4000, size=V2[t].shape, dtype=np.uint16)
+            Q2[t] = noise.integers(0x3000, 0x4000, size=Q2[t].shape, dtype=np.uint16)
+    O2, _ = orc.attn_rows(Q2, K2, V2, w.segment_offsets, w.seg_ptr)
+    np.testing.assert_array_equal(O2[so[3]:so[4]], O[so[3]:so[4]])
+    np.testing.assert_array_equal(O2[:so[1]], O[:so[1]])
+    # permute the documents: each document's block moves unchanged
+    perm = [3, 0, 4, 2, 1]
+    spans = [(so[1 + k], so[2 + k]) for k in range(5)]
+    idx = np.r_[0:so[1], np.concatenate([np.arange(*spans[k]) for k in perm]), so[-2]:so[-1]]
+    wp_seg, wp_sp, _, _ = workloads.segment_tables([(6, [lens[k] for k in perm], 4)])
+    Op, _ = orc.attn_rows(w.Q[idx], w.K[idx], w.V[idx], wp_seg, wp_sp)
+    pos = so[1]
+    for k in perm:
+        a, e = spans[k]
+        np.testing.assert_array_equal(Op[pos:pos + (e - a)], O[a:e])
+        pos += e - a
+    # query rows: unchanged up to summation order
+    np.testing.assert_allclose(Op[-4:], O[-4:], rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------------------
+# readout (BlockRank summary, score computation steps 1-4; blog, attention supervision)
+# --------------------------------------------------------------------------------------
+def _brute_scores(w, scale=None):
+    Qs, K = _f64(w.Q_S), _f64(w.K)
+    B, S, Hq, d = Qs.shape
+    Hkv = K.shape[1]
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    out = []
+    for b in range(B):
+        offs = [int(x) for x in w.doc_offsets[w.doc_ptr[b]:w.doc_ptr[b + 1]]]
+        docs = list(range(offs[0], offs[-1]))
+        s = [0.0] * (len(offs) - 1)
+        for h in range(Hq):
+            g = h * Hkv // Hq
+            for i in range(S):
+                z = {j: sum(Qs[b, i, h, t] * K[j, g, t] for t in range(d)) * sc for j in docs}
+                mz = max(z.values())
+                den = sum(math.exp(v - mz) for v in z.values())
+                for k in range(len(offs) - 1):
+                    s[k] += sum(math.exp(z[j] - mz) for j in range(offs[k], offs[k + 1])) / den / Hq
+        out.extend(s)
+    return np.asarray(out)
+
+
+def pin_readout_bruteforce(orc):
+    for seed, (hq, hkv) in enumerate([(2, 1), (4, 2), (1, 1)]):
+        rng = random.Random(900 + seed)
+        prompts = random_prompts(rng, batch=2, p_max=4, n_max=4, l_max=6, q_max=4)
+        prompts = [(p, l, max(q, 2)) for (p, l, q) in prompts]
+        w = workloads.make_custom(prompts, hq, hkv, 4, 2, 900 + seed)
+        s, hs = orc.doc_scores(w.Q_S, w.K, w.doc_offsets, w.doc_ptr)
+        np.testing.assert_allclose(s, _brute_scores(w), rtol=1e-12, atol=1e-14)
+
+
+def pin_readout_mass(orc):
+    """sum_k s_k = |S| per prompt (blog, attention supervision); scores = mean of head_scores."""
+    w = small_case(41, hq=4, hkv=2, d=16, batch=3, n_signal=3, n_max=8)
+    s, hs = orc.doc_scores(w.Q_S, w.K, w.doc_offsets, w.doc_ptr)
+    base = 0
+    for b in range(w.num_prompts):
+        N = int(w.doc_ptr[b + 1] - w.doc_ptr[b] - 1)
+        assert abs(s[base:base + N].sum() - w.n_signal) < 1e-12
+        np.testing.assert_allclose(hs[:, base:base + N].sum(axis=1), w.n_signal, rtol=0, atol=1e-12)
+        base += N
+    np.testing.assert_allclose(s, hs.mean(axis=0), rtol=0, atol=1e-15)
+
+
+def pin_readout_uniform(orc):
+    """All document keys equal (per KV head), or Q_S = 0 -> every document token gets the same
+    weight, so s_k = |S| l_k / D.  One document -> s_1 = |S|."""
+    rng = random.Random(8)
+    prompts = random_prompts(rng, batch=2, p_max=5, n_max=6, l_max=12, q_max=6)
+    prompts = [(p, l, max(q, 3)) for (p, l, q) in prompts]
+    w = workloads.make_custom(prompts, 4, 2, 8, 3, 8)
+    K = w.K.copy()
+    for b in range(w.num_prompts):
+        a = int(w.doc_offsets[w.doc_ptr[b]]); e = int(w.doc_offsets[w.doc_ptr[b + 1] - 1])
+        K[a:e] = K[a]
+    zeroQ = np.zeros_like(w.Q_S)
+    for (qs, kk) in ((w.Q_S, K), (zeroQ, w.K)):
+        s, _ = orc.doc_scores(qs, kk, w.doc_offsets, w.doc_ptr)
+        want = []
+        for (p, l, q) in w.prompts:
+            want.extend([3 * x / sum(l) for x in l])
+        np.testing.assert_allclose(s, want, rtol=1e-12, atol=0)
+    w1 = workloads.make_custom([(4, [7], 3), (0, [1], 5)], 2, 1, 8, 3, 3)
+    s, _ = orc.doc_scores(w1.Q_S, w1.K, w1.doc_offsets, w1.doc_ptr)
+    np.testing.assert_allclose(s, [3.0, 3.0], rtol=1e-14)
+
+
+def pin_readout_permutation(orc):
+    """Permuting the documents permutes the scores."""
+    lens = [4, 9, 2, 7, 5]
+    w = workloads.make_custom([(3, lens, 4)], 4, 2, 8, 2, 55)
+    s, _ = orc.doc_scores(w.Q_S, w.K, w.doc_offsets, w.doc_ptr)
+    perm = [2, 4, 0, 1, 3]
+    so = [int(x) for x in w.segment_offsets]
+    idx = np.r_[0:so[1], np.concatenate([np.arange(so[1 + k], so[2 + k]) for k in perm]), so[-2]:so[-1]]
+    _, _, dp_o, dp_p = workloads.segment_tables([(3, [lens[k] for k in perm], 4)])
+    sp_, _ = orc.doc_scores(w.Q_S, w.K[idx], dp_o, dp_p)
+    np.testing.assert_allclose(sp_, s[perm], rtol=1e-12, atol=0)
+
+
+# --------------------------------------------------------------------------------------
+# rank (BlockRank summary, attention-based inference step 3; blog, direct output)
+# --------------------------------------------------------------------------------------
+def pin_rank_bruteforce(orc):
+    """Position of document k = number of documents with a larger score, plus the number of
+    lower-indexed documents with an equal score."""
+    r = np.random.default_rng(3)
+    for n_list in ([1], [5, 1, 9], [64, 3], [200]):
+        scores = np.concatenate([np.round(r.random(n) * 4) / 4 for n in n_list])  # many ties
+        dp = np.cumsum([0] + [n + 1 for n in n_list])
+        order = orc.rank(scores, dp)
+        base = 0
+        for n in n_list:
+            s = scores[base:base + n]
+            want = np.empty(n, dtype=np.int64)
+            for k in range(n):
+                pos = sum(1 for j in range(n) if s[j] > s[k] or (s[j] == s[k] and j < k))
+                want[pos] = k
+            np.testing.assert_array_equal(order[base:base + n], want)
+            base += n
+
+
+ALL_PINS = [
+    pin_closed_form_counts, pin_worked_example, pin_textbook_rows, pin_textbook_rows_no_prefix,
+    pin_bruteforce_chunked, pin_special_rows, pin_document_isolation, pin_readout_bruteforce,
+    pin_readout_mass, pin_readout_uniform, pin_readout_permutation, pin_rank_bruteforce,
+]

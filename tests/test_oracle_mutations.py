@@ -1,0 +1,171 @@
+"""Plant plausible mistakes in the oracle (CPU only) and require some pin to catch each.
+
+Every mutation swaps one oracle function for a broken copy; the pins then run against the
+patched module.  A mutation that no pin detects would mean the pins leave that part of the
+oracle unchecked.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle.oracle as orc
+from pins import ALL_PINS
+
+I, D, Q = orc.KIND_I, orc.KIND_D, orc.KIND_Q
+
+
+def _no_causal(i, j, t):
+    prompt, seg, kind = t
+    i = np.asarray(i); j = np.asarray(j)
+    return (prompt[i] == prompt[j]) & ((seg[i] == seg[j]) | ((kind[j] == I) & (j <= i)) | (kind[i] == Q))
+
+
+def _docs_skip_prefix(i, j, t):
+    prompt, seg, kind = t
+    i = np.asarray(i); j = np.asarray(j)
+    return (prompt[i] == prompt[j]) & (j <= i) & ((seg[i] == seg[j]) | (kind[i] == Q))
+
+
+def _query_skips_docs(i, j, t):
+    prompt, seg, kind = t
+    i = np.asarray(i); j = np.asarray(j)
+    return (prompt[i] == prompt[j]) & (j <= i) & ((seg[i] == seg[j]) | (kind[j] == I))
+
+
+def _cross_prompt(i, j, t):
+    prompt, seg, kind = t
+    i = np.asarray(i); j = np.asarray(j)
+    return (j <= i) & ((seg[i] == seg[j]) | (kind[j] == I) | (kind[i] == Q))
+
+
+def _docs_read_query(i, j, t):
+    prompt, seg, kind = t
+    i = np.asarray(i); j = np.asarray(j)
+    return (prompt[i] == prompt[j]) & (j <= i) & ((seg[i] == seg[j]) | (kind[j] == I) | (kind[i] == Q)) \
+        | ((prompt[i] == prompt[j]) & (kind[i] == D) & (kind[j] == Q))
+
+
+def _closed_form_no_prefix_term(p, lengths, q):
+    D_ = sum(lengths)
+    return p * p + sum(l * l for l in lengths) + q * (p + q + D_)
+
+
+def _full_diag_no_query(i, j, t):
+    prompt, seg, kind = t
+    i = np.asarray(i); j = np.asarray(j)
+    return (prompt[i] == prompt[j]) & ((seg[i] == seg[j]) | ((kind[i] == D) & (kind[j] == I)))
+
+
+def _gqa_modulo(h, hq, hkv):
+    return h % hkv
+
+
+def _softmax_no_scale(q, k, v, mask, scale):
+    return _ORIG_SOFTMAX(q, k, v, mask, 1.0)
+
+
+def _softmax_sum_not_normalised(q, k, v, mask, scale):
+    s = (q @ k.T) * scale
+    s = np.where(mask, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    return p @ v, m[:, 0]
+
+
+def _scores_mean_over_signal(Q_S, K, doc_offsets, doc_ptr, num_q_heads=None, scale=None):
+    s, hs = _ORIG_SCORES(Q_S, K, doc_offsets, doc_ptr, num_q_heads, scale)
+    S = np.asarray(Q_S).shape[1]
+    return s / S, hs / S
+
+
+def _scores_sum_over_heads(Q_S, K, doc_offsets, doc_ptr, num_q_heads=None, scale=None):
+    s, hs = _ORIG_SCORES(Q_S, K, doc_offsets, doc_ptr, num_q_heads, scale)
+    return hs.sum(axis=0), hs
+
+
+def _scores_softmax_over_prompt(Q_S, K, doc_offsets, doc_ptr, num_q_heads=None, scale=None):
+    # normalise over the documents plus the token before them (an instruction/query leak)
+    Qs, Kf = orc.to_f64(Q_S), orc.to_f64(K)
+    B, S, Hq, d = Qs.shape
+    Hkv = Kf.shape[1]
+    sc = 1 / math.sqrt(d)
+    do = np.asarray(doc_offsets, dtype=np.int64); dp = np.asarray(doc_ptr, dtype=np.int64)
+    hs = np.zeros((Hq, len(do) - B)); base = 0
+    for b in range(B):
+        offs = do[dp[b]:dp[b + 1]]; N = len(offs) - 1
+        a, e = int(offs[0]), int(offs[-1])
+        lo = max(a - 1, 0)
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            z = (Qs[b, :, h] @ Kf[lo:e, g].T) * sc
+            w = np.exp(z - z.max(1, keepdims=True)); w /= w.sum(1, keepdims=True)
+            hs[h, base:base + N] = np.add.reduceat(w[:, a - lo:], offs[:-1] - a, axis=1).sum(0)
+        base += N
+    return hs.mean(0), hs
+
+
+def _scores_shifted_boundaries(Q_S, K, doc_offsets, doc_ptr, num_q_heads=None, scale=None):
+    do = np.asarray(doc_offsets).copy()
+    B = len(doc_ptr) - 1
+    for b in range(B):
+        a, e = doc_ptr[b], doc_ptr[b + 1]
+        inner = do[a + 1:e - 1]
+        do[a + 1:e - 1] = np.minimum(inner + 1, do[e - 1] - 1)
+    return _ORIG_SCORES(Q_S, K, do, doc_ptr, num_q_heads, scale)
+
+
+def _rank_ties_high(scores, doc_ptr):
+    s = np.asarray(scores); dp = np.asarray(doc_ptr); out = []; base = 0
+    for b in range(len(dp) - 1):
+        N = int(dp[b + 1] - dp[b] - 1)
+        loc = list(s[base:base + N])
+        out.extend(sorted(range(N), key=lambda k: (-loc[k], -k)))
+        base += N
+    return np.asarray(out, dtype=np.int32)
+
+
+def _rank_ascending(scores, doc_ptr):
+    s = np.asarray(scores); dp = np.asarray(doc_ptr); out = []; base = 0
+    for b in range(len(dp) - 1):
+        N = int(dp[b + 1] - dp[b] - 1)
+        loc = list(s[base:base + N])
+        out.extend(sorted(range(N), key=lambda k: (loc[k], k)))
+        base += N
+    return np.asarray(out, dtype=np.int32)
+
+
+_ORIG_SOFTMAX = orc._masked_softmax_av
+_ORIG_SCORES = orc.doc_scores
+
+MUTATIONS = {
+    "mask_no_causal": ("allowed", _no_causal),
+    "mask_docs_skip_prefix": ("allowed", _docs_skip_prefix),
+    "mask_query_skips_docs": ("allowed", _query_skips_docs),
+    "mask_cross_prompt": ("allowed", _cross_prompt),
+    "mask_docs_read_query": ("allowed", _docs_read_query),
+    "closed_form_drops_pl": ("closed_form_pairs", _closed_form_no_prefix_term),
+    "full_diag_drops_query_rows": ("allowed_full_diagonal", _full_diag_no_query),
+    "gqa_modulo": ("kv_head", _gqa_modulo),
+    "softmax_no_scale": ("_masked_softmax_av", _softmax_no_scale),
+    "softmax_not_normalised": ("_masked_softmax_av", _softmax_sum_not_normalised),
+    "scores_mean_over_signal": ("doc_scores", _scores_mean_over_signal),
+    "scores_sum_over_heads": ("doc_scores", _scores_sum_over_heads),
+    "scores_softmax_leaks_outside_docs": ("doc_scores", _scores_softmax_over_prompt),
+    "scores_shifted_boundaries": ("doc_scores", _scores_shifted_boundaries),
+    "rank_ties_high": ("rank", _rank_ties_high),
+    "rank_ascending": ("rank", _rank_ascending),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(orc, attr, fn)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin detects mutation {name}"
