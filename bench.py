@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark of the BlockRank hot path on one MI355X.
+
+A step is one pass of the whole path over one synthetic prompt batch: block-sparse prefill
+attention (br_attn_fwd), attention-mass document scores (br_doc_scores) and the per-prompt
+ranking (br_sort_docs), inputs resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is allowed-pair TFLOP/s of the whole step, counting
+4 * d * Hq FLOPs per allowed (query, key) pair with the blog's closed-form pair count
+(diagonal blocks whole); the exact causal count is reported beside it.  `roofline` covers the
+attention kernel (the dominant one), timed with HIP events recorded on the launch stream
+around the kernel itself.  `cpu_baseline` times the fp64 CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "block-sparse prefill TFLOP/s (allowed pairs) + prompts/s at N=100,500; % MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+WORKLOAD_NAMES = {
+    "tiny": "tiny: 1 head, d=64, p=32, N=4 x l=64, q=32 (L=320), |S|=4",
+    "worked": "worked: p=32, q=32, N=100 x l=128 (L=12864), 32 Q / 8 KV heads, d=128, |S|=8, B=1",
+    "long": "long: p=64, q=32, N=500 x l=200 (L=100096), 32 Q / 8 KV heads, d=128, |S|=8, B=1",
+    "ragged": "ragged: p=48, q=24, N=200, l~U{32..256}, 32 Q / 8 KV heads, d=128, |S|=8, B=1",
+    "batched": "batched: B=16 x (p=32, q=32, N=100, l~U{64..192}), 32 Q / 8 KV heads, d=128, |S|=8",
+}
+
+
+def pair_counts(w):
+    """Allowed pairs per the blog's closed form (diagonal blocks whole) and the causal count."""
+    blk = exact = 0
+    for (p, lens, q) in w.prompts:
+        D = sum(lens)
+        b = p * p + sum(l * l + p * l for l in lens) + q * (p + q + D)
+        blk += b
+        exact += b - sum(n * (n - 1) // 2 for n in [p, q] + list(lens))
+    return blk, exact
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (libamdhip64) so the library can record them on its launch stream."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            self.ev.append(e.value)
+
+    def elapsed_ms(self, a, b):
+        out = ctypes.c_float()
+        self.hip.hipEventSynchronize(ctypes.c_void_p(self.ev[b]))
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(self.ev[a]), ctypes.c_void_p(self.ev[b]))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(out.value)
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def measure(config, seed, steps, warmup, log):
+    import torch
+
+    import block_sparse_attention_segment_amd as br
+    import workloads
+
+    t0 = time.time()
+    w = workloads.make(config, seed)
+    log(f"[bench] generated {config} (T={w.total_tokens}) in {time.time() - t0:.1f}s")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    Q, K, V, Q_S = dev(w.Q), dev(w.K), dev(w.V), dev(w.Q_S)
+    T, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    dims = br.make_dims(w.num_prompts, Hq, Hkv, d, T)
+    out = torch.empty_like(Q)
+    scores = torch.empty(w.num_docs, dtype=torch.float32, device="cuda")
+    order = torch.empty(w.num_docs, dtype=torch.int32, device="cuda")
+    ws_a = torch.empty(br.attn_workspace_bytes(dims, w.segment_offsets, w.seg_ptr), dtype=torch.uint8, device="cuda")
+    ws_s = torch.empty(br.doc_scores_workspace_bytes(dims, w.n_signal, w.doc_offsets, w.doc_ptr), dtype=torch.uint8,
+                       device="cuda")
+    ev = HipEvents(2 * steps)
+    stream = torch.cuda.current_stream()
+
+    def step(kernel_events=None):
+        br.attn_fwd(Q, K, V, w.segment_offsets, w.seg_ptr, out=out, workspace=ws_a, stream=stream,
+                    kernel_events=kernel_events)
+        br.doc_scores(Q_S, K, w.doc_offsets, w.doc_ptr, scores=scores, workspace=ws_s, stream=stream)
+        br.sort_docs(scores, w.doc_ptr, order=order, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] {config}: {warmup} warm-up steps done")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        step(kernel_events=(ev.ev[2 * i], ev.ev[2 * i + 1]))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = e0.elapsed_time(e1) / steps
+    kern = [ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(steps)]
+    ev.close()
+    log(f"[bench] {config}: {steps} timed steps, {ms_step:.4f} ms/step, attention kernel {np.mean(kern):.4f} ms")
+    blk, exact = pair_counts(w)
+    flop_blk = 4.0 * d * Hq * blk
+    flop_exact = 4.0 * d * Hq * exact
+    kernel_s = float(np.mean(kern)) / 1e3
+    bytes_alg = float(T) * (2 * Hq + 2 * Hkv) * d * 2
+    return dict(w=w, ms_step=ms_step, wall_s=wall, kernel_ms=float(np.mean(kern)), kernel_ms_p50=float(np.median(kern)),
+                flop_blk=flop_blk, flop_exact=flop_exact, pairs_blk=blk, pairs_exact=exact, bytes_alg=bytes_alg,
+                kernel_s=kernel_s)
+
+
+def cpu_baseline(w, n_docs_sample, log):
+    """Time the fp64 oracle on a bounded sample of the same prompt and scale to the whole step."""
+    import oracle.oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    so, sp = w.segment_offsets, w.seg_ptr
+    offs = so[sp[0]:sp[1]]
+    N = len(offs) - 3
+    k = min(n_docs_sample, N)
+    inst = np.arange(int(offs[0]), int(offs[1]))
+    docs = np.arange(int(offs[1]), int(offs[1 + k]))
+    query = np.arange(int(offs[-2]), int(offs[-1]))
+    timings = {}
+    for name, rows in (("instruction", inst), ("docs", docs), ("query", query)):
+        t = time.perf_counter()
+        if len(rows):
+            orc.attn_rows(w.Q, w.K, w.V, so, sp, rows=rows)
+        timings[name] = time.perf_counter() - t
+    t = time.perf_counter()
+    s, _ = orc.doc_scores(w.Q_S, w.K, w.doc_offsets, w.doc_ptr)
+    timings["scores"] = time.perf_counter() - t
+    t = time.perf_counter()
+    orc.rank(s, w.doc_ptr)
+    timings["rank"] = time.perf_counter() - t
+    est = timings["instruction"] + timings["docs"] * (N / k) + timings["query"] + timings["scores"] + timings["rank"]
+    log(f"[bench] cpu oracle sample: {json.dumps({a: round(b, 3) for a, b in timings.items()})}, "
+        f"estimated full step {est:.1f}s")
+    return dict(est_s=est, threads=threads, k=k, N=N, sampled_s=sum(timings.values()))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="long", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--secondary", default="worked", help="extra config timed in the same run ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-docs", type=int, default=24, help="documents in the CPU oracle's timed sample")
+    ap.add_argument("--traffic", default="", help="JSON file with measured HBM bytes per attention launch")
+    args = ap.parse_args()
+    log = lambda m: print(m, file=sys.stderr, flush=True)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path shards with no "
+              "cross-GPU traffic for document rows, but no multi-GPU run is implemented", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    r = measure(args.config, args.seed, args.steps, args.warmup, log)
+    w = r["w"]
+    step_s = r["ms_step"] / 1e3
+    value = r["flop_blk"] / step_s / 1e12
+    attn_tflops_blk = r["flop_blk"] / r["kernel_s"] / 1e12
+    achieved_gbps = r["bytes_alg"] / r["kernel_s"] / 1e9
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get("bytes_per_launch")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.config], "seed": args.seed, "global_batch": w.num_prompts,
+                   "seq_len": w.total_tokens, "parallelism": "single-gpu"},
+        "prompts_per_s": round(w.num_prompts / step_s, 2),
+        "tflops_exact_pairs": round(r["flop_exact"] / step_s / 1e12, 3),
+        "mfma_peak_frac_step": round(value / PEAK_BF16_TFLOPS, 4),
+        "allowed_pairs": {"closed_form": r["pairs_blk"], "exact_causal": r["pairs_exact"]},
+        "attention_kernel": {"ms": round(r["kernel_ms"], 5), "ms_p50": round(r["kernel_ms_p50"], 5),
+                             "tflops_closed_form_pairs": round(attn_tflops_blk, 3),
+                             "mfma_peak_frac": round(attn_tflops_blk / PEAK_BF16_TFLOPS, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                     "kernel": "attn_fwd_kernel", "bytes_per_launch": r["bytes_alg"]},
+    }
+    if args.secondary and args.secondary != args.config:
+        r2 = measure(args.secondary, args.seed, args.steps, args.warmup, log)
+        s2 = r2["ms_step"] / 1e3
+        line["secondary"] = {"workload": WORKLOAD_NAMES[args.secondary], "ms_per_step": round(r2["ms_step"], 5),
+                             "prompts_per_s": round(r2["w"].num_prompts / s2, 2),
+                             "tflops_closed_form_pairs": round(r2["flop_blk"] / s2 / 1e12, 3),
+                             "attention_kernel_ms": round(r2["kernel_ms"], 5)}
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(w, args.cpu_docs, log)
+        line["cpu_baseline"] = {
+            "value": round(r["flop_blk"] / cb["est_s"] / 1e12, 6), "unit": "TFLOP/s", "cores": cb["threads"],
+            "kind": "oracle",
+            "sample": (f"fp64 NumPy oracle on instruction rows, {cb['k']} of {cb['N']} documents' rows and all "
+                       f"query rows, plus the full readout and rank ({cb['sampled_s']:.1f}s measured); time "
+                       f"scaled to all {cb['N']} documents ({cb['est_s']:.1f}s per step); host "
+                       f"{platform.processor() or platform.machine()}, os.cpu_count()={os.cpu_count()}"),
+        }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,230 @@
+"""ctypes binding of libblockrank (the C ABI in include/blockrank.h).
+
+Argument marshalling only: every step of the computation runs in the HIP library.  PyTorch
+provides device memory (tensors) and the stream (torch.cuda.current_stream()).  If the built
+library is missing, loading raises: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libblockrank.so")
+
+BR_OK, BR_ERR_INVALID_ARG, BR_ERR_UNSUPPORTED, BR_ERR_WORKSPACE, BR_ERR_HIP = range(5)
+
+# Symbols the header declares; the CPU test checks the library exports each of them.
+EXPORTED = ("br_attn_workspace_bytes", "br_attn_fwd", "br_attn_fwd_timed", "br_doc_scores_workspace_bytes", "br_doc_scores",
+            "br_sort_docs", "br_attn_plan_items", "br_status_string", "br_last_error", "br_version")
+
+
+class BrDims(ctypes.Structure):
+    _fields_ = [("num_prompts", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("total_tokens", ctypes.c_int64)]
+
+
+class BlockRankError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_P = ctypes.c_void_p
+_I32P = ctypes.POINTER(ctypes.c_int32)
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libblockrank.so from the package directory (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m block_sparse_attention_segment_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    dims_p = ctypes.POINTER(BrDims)
+    sz_p = ctypes.POINTER(ctypes.c_size_t)
+    sig = {
+        "br_attn_workspace_bytes": [dims_p, _I32P, _I32P, sz_p],
+        "br_attn_fwd": [dims_p, _P, _P, _P, _I32P, _I32P, _P, _P, ctypes.c_float, _P, ctypes.c_size_t, _P],
+        "br_attn_fwd_timed": [dims_p, _P, _P, _P, _I32P, _I32P, _P, _P, ctypes.c_float, _P, ctypes.c_size_t, _P,
+                              _P, _P],
+        "br_doc_scores_workspace_bytes": [dims_p, ctypes.c_int32, _I32P, _I32P, sz_p],
+        "br_doc_scores": [dims_p, _P, ctypes.c_int32, _P, _I32P, _I32P, _P, _P, ctypes.c_float, _P,
+                          ctypes.c_size_t, _P],
+        "br_sort_docs": [_P, _I32P, ctypes.c_int32, _P, _P],
+        "br_attn_plan_items": [dims_p, _I32P, _I32P, _I32P, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64),
+                               ctypes.POINTER(ctypes.c_int32)],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    lib.br_status_string.argtypes = [ctypes.c_int]
+    lib.br_status_string.restype = ctypes.c_char_p
+    lib.br_last_error.argtypes = []
+    lib.br_last_error.restype = ctypes.c_char_p
+    lib.br_version.argtypes = []
+    lib.br_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _status_name(status: int) -> str:
+    try:
+        return load_library().br_status_string(status).decode()
+    except Exception:  # pragma: no cover - only while reporting another failure
+        return f"status {status}"
+
+
+def _check(status: int) -> None:
+    if status != BR_OK:
+        raise BlockRankError(status, load_library().br_last_error().decode())
+
+
+def _host_i32(a) -> np.ndarray:
+    arr = np.ascontiguousarray(np.asarray(a), dtype=np.int32)
+    return arr
+
+
+def _ptr_i32(arr: np.ndarray):
+    return arr.ctypes.data_as(_I32P)
+
+
+def make_dims(num_prompts: int, num_q_heads: int, num_kv_heads: int, head_dim: int, total_tokens: int) -> BrDims:
+    return BrDims(int(num_prompts), int(num_q_heads), int(num_kv_heads), int(head_dim), int(total_tokens))
+
+
+def _dev_ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def attn_workspace_bytes(dims: BrDims, segment_offsets, seg_ptr) -> int:
+    lib = load_library()
+    so, sp = _host_i32(segment_offsets), _host_i32(seg_ptr)
+    out = ctypes.c_size_t(0)
+    _check(lib.br_attn_workspace_bytes(ctypes.byref(dims), _ptr_i32(so), _ptr_i32(sp), ctypes.byref(out)))
+    return int(out.value)
+
+
+def attn_plan_items(dims: BrDims, segment_offsets, seg_ptr) -> Tuple[np.ndarray, int]:
+    """Host-only: the attention work list, [n, 8] int32, and the token rows per tile."""
+    lib = load_library()
+    so, sp = _host_i32(segment_offsets), _host_i32(seg_ptr)
+    n = ctypes.c_int64(0)
+    tm = ctypes.c_int32(0)
+    _check(lib.br_attn_plan_items(ctypes.byref(dims), _ptr_i32(so), _ptr_i32(sp), None, 0, ctypes.byref(n),
+                                  ctypes.byref(tm)))
+    items = np.zeros((max(int(n.value), 1), 8), dtype=np.int32)
+    _check(lib.br_attn_plan_items(ctypes.byref(dims), _ptr_i32(so), _ptr_i32(sp), _ptr_i32(items), int(n.value),
+                                  ctypes.byref(n), ctypes.byref(tm)))
+    return items[:int(n.value)], int(tm.value)
+
+
+def attn_fwd(Q, K, V, segment_offsets, seg_ptr, out=None, lse=None, softmax_scale: float = 0.0,
+             workspace=None, stream=None, kernel_events=None):
+    """Block-sparse prefill attention.  Q [T,Hq,d], K/V [T,Hkv,d] bf16 CUDA tensors.
+
+    Returns out (bf16 [T,Hq,d]); when ``lse`` is True a new fp32 [T,Hq] tensor is also
+    returned (or pass a preallocated tensor).  ``kernel_events`` = (start, stop) raw hipEvent_t
+    handles recorded around the attention kernel itself.
+    """
+    import torch
+    lib = load_library()
+    for name, t in (("Q", Q), ("K", K), ("V", V)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 3:
+            raise ValueError(f"{name} must be a contiguous 3-D bfloat16 CUDA tensor")
+    T, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    if K.shape != (T, Hkv, d) or V.shape != K.shape:
+        raise ValueError("K and V must be [T, Hkv, d] matching Q")
+    so, sp = _host_i32(segment_offsets), _host_i32(seg_ptr)
+    dims = make_dims(len(sp) - 1, Hq, Hkv, d, T)
+    if out is None:
+        out = torch.empty_like(Q)
+    want_lse = lse is True
+    if want_lse:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=Q.device)
+    elif lse is False:
+        lse = None
+    nbytes = attn_workspace_bytes(dims, so, sp)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+    ev0, ev1 = kernel_events if kernel_events is not None else (None, None)
+    _check(lib.br_attn_fwd_timed(ctypes.byref(dims), Q.data_ptr(), K.data_ptr(), V.data_ptr(), _ptr_i32(so),
+                                 _ptr_i32(sp), out.data_ptr(), _dev_ptr(lse), float(softmax_scale),
+                                 workspace.data_ptr(), workspace.numel(), _stream_handle(stream), ev0, ev1))
+    return (out, lse) if lse is not None else out
+
+
+def doc_scores_workspace_bytes(dims: BrDims, n_signal: int, doc_offsets, doc_ptr) -> int:
+    lib = load_library()
+    do, dp = _host_i32(doc_offsets), _host_i32(doc_ptr)
+    out = ctypes.c_size_t(0)
+    _check(lib.br_doc_scores_workspace_bytes(ctypes.byref(dims), int(n_signal), _ptr_i32(do), _ptr_i32(dp),
+                                             ctypes.byref(out)))
+    return int(out.value)
+
+
+def doc_scores(Q_S, K, doc_offsets, doc_ptr, head_scores: bool = False, softmax_scale: float = 0.0,
+               scores=None, workspace=None, stream=None):
+    """Attention-mass scores.  Q_S [B,S,Hq,d], K [T,Hkv,d] bf16 CUDA tensors.
+
+    Returns scores fp32 [sum N_b] (and head_scores [Hq, sum N_b] if requested)."""
+    import torch
+    lib = load_library()
+    for name, t in (("Q_S", Q_S), ("K", K)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 CUDA tensor")
+    if Q_S.dim() != 4 or K.dim() != 3 or Q_S.shape[3] != K.shape[2]:
+        raise ValueError("Q_S must be [B, S, Hq, d] and K [T, Hkv, d]")
+    B, S, Hq, d = Q_S.shape
+    T, Hkv, _ = K.shape
+    do, dp = _host_i32(doc_offsets), _host_i32(doc_ptr)
+    if len(dp) != B + 1:
+        raise ValueError("doc_ptr must have B + 1 entries")
+    dims = make_dims(B, Hq, Hkv, d, T)
+    n_docs = int(dp[-1]) - B
+    if scores is None:
+        scores = torch.empty(n_docs, dtype=torch.float32, device=K.device)
+    hs = torch.empty((Hq, n_docs), dtype=torch.float32, device=K.device) if head_scores else None
+    nbytes = doc_scores_workspace_bytes(dims, S, do, dp)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=K.device)
+    _check(lib.br_doc_scores(ctypes.byref(dims), Q_S.data_ptr(), int(S), K.data_ptr(), _ptr_i32(do), _ptr_i32(dp),
+                             scores.data_ptr(), _dev_ptr(hs), float(softmax_scale), workspace.data_ptr(),
+                             workspace.numel(), _stream_handle(stream)))
+    return (scores, hs) if head_scores else scores
+
+
+def sort_docs(scores, doc_ptr, order=None, stream=None):
+    """Per-prompt local document indices by descending score (ties: lower index)."""
+    import torch
+    lib = load_library()
+    if scores.dtype != torch.float32 or not scores.is_cuda or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous float32 CUDA tensor")
+    dp = _host_i32(doc_ptr)
+    if order is None:
+        order = torch.empty(scores.numel(), dtype=torch.int32, device=scores.device)
+    _check(lib.br_sort_docs(scores.data_ptr(), _ptr_i32(dp), len(dp) - 1, order.data_ptr(),
+                            _stream_handle(stream)))
+    return order
+
+
+def version() -> str:
+    return load_library().br_version().decode()

@@ -1,0 +1,336 @@
+// extern "C" entry points of libblockrank (declared in include/blockrank.h).
+//
+// Each compute call: validate everything on the host, build the work plan, copy the plan into
+// the caller's workspace through a pinned staging buffer (hipMemcpyAsync on the caller's
+// stream), then enqueue the kernels on that stream.  Nothing blocks the host except the first
+// use of a staging buffer size (pinned allocation).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <exception>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "blockrank.h"
+#include "launch.h"
+#include "plan.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+br_status record(const br::Error& e) {
+  g_last_error = e.msg;
+  return e.status;
+}
+br_status record(br_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+br_status hip_fail(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return BR_ERR_HIP;
+}
+
+// Pinned host buffers for plan uploads.  A buffer is reused once the copy that last read it has
+// completed (tracked by an event recorded after the copy on the caller's stream).
+class StagingPool {
+ public:
+  struct Lease {
+    int index = -1;
+    void* ptr = nullptr;
+  };
+
+  hipError_t acquire(size_t bytes, Lease* lease) {
+    std::lock_guard<std::mutex> lock(mu_);
+    for (size_t i = 0; i < bufs_.size(); ++i) {
+      Buf& b = bufs_[i];
+      if (b.busy || b.cap < bytes) continue;
+      if (b.recorded) {
+        hipError_t q = hipEventQuery(b.ev);
+        if (q == hipErrorNotReady) continue;
+        if (q != hipSuccess) return q;
+      }
+      b.busy = true;
+      *lease = Lease{int(i), b.host};
+      return hipSuccess;
+    }
+    Buf nb;
+    nb.cap = bytes < (size_t(64) << 10) ? (size_t(64) << 10) : bytes;
+    hipError_t e = hipHostMalloc(&nb.host, nb.cap, hipHostMallocDefault);
+    if (e != hipSuccess) return e;
+    e = hipEventCreateWithFlags(&nb.ev, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      (void)hipHostFree(nb.host);
+      return e;
+    }
+    nb.busy = true;
+    bufs_.push_back(nb);
+    *lease = Lease{int(bufs_.size() - 1), nb.host};
+    return hipSuccess;
+  }
+
+  // Record that the lease's contents are consumed by work already enqueued on `stream`.
+  hipError_t release(const Lease& lease, hipStream_t stream, bool enqueued) {
+    std::lock_guard<std::mutex> lock(mu_);
+    Buf& b = bufs_[size_t(lease.index)];
+    hipError_t e = hipSuccess;
+    if (enqueued) {
+      e = hipEventRecord(b.ev, stream);
+      b.recorded = e == hipSuccess;
+    }
+    b.busy = false;
+    return e;
+  }
+
+ private:
+  struct Buf {
+    void* host = nullptr;
+    size_t cap = 0;
+    hipEvent_t ev = nullptr;
+    bool busy = false;
+    bool recorded = false;
+  };
+  std::mutex mu_;
+  std::vector<Buf> bufs_;  // kept for the life of the process
+};
+
+StagingPool& staging() {
+  static StagingPool* pool = new StagingPool();  // intentionally never destroyed
+  return *pool;
+}
+
+// Copy `bytes` from `src` (host) into device memory `dst` on `stream` via pinned staging.
+br_status upload(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return BR_OK;
+  StagingPool::Lease lease;
+  hipError_t e = staging().acquire(bytes, &lease);
+  if (e != hipSuccess) return hip_fail(e, "pinned staging allocation");
+  std::memcpy(lease.ptr, src, bytes);
+  e = hipMemcpyAsync(dst, lease.ptr, bytes, hipMemcpyHostToDevice, stream);
+  hipError_t r = staging().release(lease, stream, e == hipSuccess);
+  if (e != hipSuccess) return hip_fail(e, "plan upload (hipMemcpyAsync)");
+  if (r != hipSuccess) return hip_fail(r, "plan upload (hipEventRecord)");
+  return BR_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+float resolve_scale(float scale, int d) { return scale > 0.f ? scale : 1.0f / std::sqrt(float(d)); }
+
+template <class F>
+br_status guarded(F&& f) {
+  try {
+    return f();
+  } catch (const std::exception& ex) {
+    return record(BR_ERR_INVALID_ARG, std::string("internal error: ") + ex.what());
+  } catch (...) {
+    return record(BR_ERR_INVALID_ARG, "internal error");
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* br_status_string(br_status s) {
+  switch (s) {
+    case BR_OK: return "BR_OK";
+    case BR_ERR_INVALID_ARG: return "BR_ERR_INVALID_ARG";
+    case BR_ERR_UNSUPPORTED: return "BR_ERR_UNSUPPORTED";
+    case BR_ERR_WORKSPACE: return "BR_ERR_WORKSPACE";
+    case BR_ERR_HIP: return "BR_ERR_HIP";
+  }
+  return "BR_ERR_UNKNOWN";
+}
+
+const char* br_last_error(void) { return g_last_error.c_str(); }
+
+const char* br_version(void) { return "blockrank-gfx950 0.1.0"; }
+
+br_status br_attn_workspace_bytes(const br_dims* dims, const int32_t* segment_offsets, const int32_t* seg_ptr,
+                                  size_t* bytes) {
+  return guarded([&]() -> br_status {
+    if (!bytes) return record(BR_ERR_INVALID_ARG, "bytes is NULL");
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    br::AttnPlan plan;
+    e = br::build_attn_plan(*dims, segment_offsets, seg_ptr, &plan);
+    if (!e.ok()) return record(e);
+    *bytes = plan.total_bytes;
+    return BR_OK;
+  });
+}
+
+br_status br_attn_plan_items(const br_dims* dims, const int32_t* segment_offsets, const int32_t* seg_ptr,
+                             int32_t* items, int64_t capacity, int64_t* n_items, int32_t* rows_per_tile) {
+  return guarded([&]() -> br_status {
+    if (!n_items) return record(BR_ERR_INVALID_ARG, "n_items is NULL");
+    if (capacity < 0 || (capacity > 0 && !items)) return record(BR_ERR_INVALID_ARG, "items buffer is NULL");
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    br::AttnPlan plan;
+    e = br::build_attn_plan(*dims, segment_offsets, seg_ptr, &plan);
+    if (!e.ok()) return record(e);
+    *n_items = int64_t(plan.items.size());
+    if (rows_per_tile) *rows_per_tile = plan.rows_per_tile;
+    const int64_t n = capacity < *n_items ? capacity : *n_items;
+    if (n > 0) std::memcpy(items, plan.items.data(), size_t(n) * sizeof(br::AttnItem));
+    return BR_OK;
+  });
+}
+
+br_status br_attn_fwd_timed(const br_dims* dims, const void* Q, const void* K, const void* V,
+                            const int32_t* segment_offsets, const int32_t* seg_ptr, void* out, float* lse,
+                            float softmax_scale, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                            hipEvent_t kernel_start, hipEvent_t kernel_stop) {
+  return guarded([&]() -> br_status {
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    if (!Q || !K || !V || !out) return record(BR_ERR_INVALID_ARG, "Q, K, V and out must be non-NULL device pointers");
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 16))
+      return record(BR_ERR_INVALID_ARG, "Q, K, V and out must be 16-byte aligned");
+    if (lse && !aligned(lse, 4)) return record(BR_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    if (std::isnan(softmax_scale) || std::isinf(softmax_scale))
+      return record(BR_ERR_INVALID_ARG, "softmax_scale must be finite");
+    br::AttnPlan plan;
+    e = br::build_attn_plan(*dims, segment_offsets, seg_ptr, &plan);
+    if (!e.ok()) return record(e);
+    if (!workspace || workspace_bytes < plan.total_bytes)
+      return record(BR_ERR_WORKSPACE, "workspace is NULL or smaller than br_attn_workspace_bytes() = " +
+                                          std::to_string(plan.total_bytes));
+    if (!aligned(workspace, 16)) return record(BR_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+    // Host image of the plan region of the workspace: [items | merges].
+    std::vector<unsigned char> host(plan.off_part_o, 0);
+    std::memcpy(host.data() + plan.off_items, plan.items.data(), plan.items.size() * sizeof(br::AttnItem));
+    if (!plan.merges.empty())
+      std::memcpy(host.data() + plan.off_merges, plan.merges.data(), plan.merges.size() * sizeof(br::MergeItem));
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    br_status st = upload(ws, host.data(), host.size(), stream);
+    if (st != BR_OK) return st;
+
+    br::AttnLaunch a;
+    a.Q = static_cast<const uint16_t*>(Q);
+    a.K = static_cast<const uint16_t*>(K);
+    a.V = static_cast<const uint16_t*>(V);
+    a.O = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    a.items = reinterpret_cast<const br::AttnItem*>(ws + plan.off_items);
+    a.merges = reinterpret_cast<const br::MergeItem*>(ws + plan.off_merges);
+    a.part_o = reinterpret_cast<float*>(ws + plan.off_part_o);
+    a.part_ml = reinterpret_cast<float*>(ws + plan.off_part_ml);
+    a.n_items = int64_t(plan.items.size());
+    a.n_merges = int64_t(plan.merges.size());
+    a.num_q_heads = dims->num_q_heads;
+    a.num_kv_heads = dims->num_kv_heads;
+    a.head_dim = dims->head_dim;
+    a.scale_log2 = resolve_scale(softmax_scale, dims->head_dim) * 1.4426950408889634f;
+    a.ev_start = kernel_start;
+    a.ev_stop = kernel_stop;
+    hipError_t he = br::launch_attn(a, stream);
+    if (he != hipSuccess) return hip_fail(he, "attention kernel launch");
+    return BR_OK;
+  });
+}
+
+br_status br_attn_fwd(const br_dims* dims, const void* Q, const void* K, const void* V,
+                      const int32_t* segment_offsets, const int32_t* seg_ptr, void* out, float* lse,
+                      float softmax_scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return br_attn_fwd_timed(dims, Q, K, V, segment_offsets, seg_ptr, out, lse, softmax_scale, workspace,
+                           workspace_bytes, stream, nullptr, nullptr);
+}
+
+br_status br_doc_scores_workspace_bytes(const br_dims* dims, int32_t n_signal, const int32_t* doc_offsets,
+                                        const int32_t* doc_ptr, size_t* bytes) {
+  return guarded([&]() -> br_status {
+    if (!bytes) return record(BR_ERR_INVALID_ARG, "bytes is NULL");
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    br::ScorePlan plan;
+    e = br::build_score_plan(*dims, n_signal, doc_offsets, doc_ptr, &plan);
+    if (!e.ok()) return record(e);
+    *bytes = plan.total_bytes;
+    return BR_OK;
+  });
+}
+
+br_status br_doc_scores(const br_dims* dims, const void* Q_S, int32_t n_signal, const void* K,
+                        const int32_t* doc_offsets, const int32_t* doc_ptr, float* scores, float* head_scores,
+                        float softmax_scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return guarded([&]() -> br_status {
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    if (!Q_S || !K || !scores) return record(BR_ERR_INVALID_ARG, "Q_S, K and scores must be non-NULL device pointers");
+    if (!aligned(Q_S, 16) || !aligned(K, 16)) return record(BR_ERR_INVALID_ARG, "Q_S and K must be 16-byte aligned");
+    if (!aligned(scores, 4) || (head_scores && !aligned(head_scores, 4)))
+      return record(BR_ERR_INVALID_ARG, "scores and head_scores must be 4-byte aligned");
+    if (std::isnan(softmax_scale) || std::isinf(softmax_scale))
+      return record(BR_ERR_INVALID_ARG, "softmax_scale must be finite");
+    br::ScorePlan plan;
+    e = br::build_score_plan(*dims, n_signal, doc_offsets, doc_ptr, &plan);
+    if (!e.ok()) return record(e);
+    if (!workspace || workspace_bytes < plan.total_bytes)
+      return record(BR_ERR_WORKSPACE, "workspace is NULL or smaller than br_doc_scores_workspace_bytes() = " +
+                                          std::to_string(plan.total_bytes));
+    if (!aligned(workspace, 16)) return record(BR_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+    const int B = dims->num_prompts;
+    std::vector<unsigned char> host(plan.off_ml, 0);
+    std::memcpy(host.data() + plan.off_items, plan.items.data(), plan.items.size() * sizeof(br::ScoreItem));
+    std::memcpy(host.data() + plan.off_doc_offsets, doc_offsets, size_t(doc_ptr[B]) * sizeof(int32_t));
+    std::memcpy(host.data() + plan.off_prompt_base, plan.prompt_score_base.data(), size_t(B + 1) * sizeof(int32_t));
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    br_status st = upload(ws, host.data(), host.size(), stream);
+    if (st != BR_OK) return st;
+
+    br::ScoreLaunch a;
+    a.Q_S = static_cast<const uint16_t*>(Q_S);
+    a.K = static_cast<const uint16_t*>(K);
+    a.items = reinterpret_cast<const br::ScoreItem*>(ws + plan.off_items);
+    a.doc_offsets = reinterpret_cast<const int32_t*>(ws + plan.off_doc_offsets);
+    a.prompt_base = reinterpret_cast<const int32_t*>(ws + plan.off_prompt_base);
+    a.ml = reinterpret_cast<float2*>(ws + plan.off_ml);
+    a.scores = scores;
+    a.head_scores = head_scores;
+    a.n_items = int64_t(plan.items.size());
+    a.num_prompts = B;
+    a.num_q_heads = dims->num_q_heads;
+    a.num_kv_heads = dims->num_kv_heads;
+    a.head_dim = dims->head_dim;
+    a.n_signal = n_signal;
+    a.row_blocks = plan.row_blocks;
+    a.n_docs = plan.n_docs;
+    a.scale_log2 = resolve_scale(softmax_scale, dims->head_dim) * 1.4426950408889634f;
+    hipError_t he = br::launch_doc_scores(a, stream);
+    if (he != hipSuccess) return hip_fail(he, "doc score kernel launch");
+    return BR_OK;
+  });
+}
+
+br_status br_sort_docs(const float* scores, const int32_t* doc_ptr, int32_t num_prompts, int32_t* order,
+                       hipStream_t stream) {
+  return guarded([&]() -> br_status {
+    if (!scores || !order) return record(BR_ERR_INVALID_ARG, "scores and order must be non-NULL device pointers");
+    if (!doc_ptr) return record(BR_ERR_INVALID_ARG, "doc_ptr must be a non-NULL host array");
+    if (num_prompts < 1) return record(BR_ERR_INVALID_ARG, "num_prompts must be >= 1");
+    if (!aligned(scores, 4) || !aligned(order, 4)) return record(BR_ERR_INVALID_ARG, "scores/order misaligned");
+    std::vector<int32_t> base(size_t(num_prompts) + 1);
+    for (int b = 0; b <= num_prompts; ++b) base[size_t(b)] = doc_ptr[b] - b;
+    if (base[0] != 0) return record(BR_ERR_INVALID_ARG, "doc_ptr[0] must be 0");
+    for (int b = 0; b < num_prompts; ++b) {
+      const int32_t n = base[size_t(b) + 1] - base[size_t(b)];
+      if (n < 1) return record(BR_ERR_INVALID_ARG, "prompt " + std::to_string(b) + " has no documents");
+      if (n > br::kSortMaxDocs)
+        return record(BR_ERR_UNSUPPORTED, "prompt " + std::to_string(b) + " has " + std::to_string(n) +
+                                              " documents; at most " + std::to_string(br::kSortMaxDocs));
+    }
+    hipError_t he = br::launch_sort_docs(scores, base.data(), num_prompts, order, stream);
+    if (he != hipSuccess) return hip_fail(he, "sort kernel launch");
+    return BR_OK;
+  });
+}
+
+}  // extern "C"

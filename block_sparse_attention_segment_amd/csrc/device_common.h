@@ -1,0 +1,56 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, bf16 packing, the
+// 32x32x16 bf16 MFMA and cross-half wave exchange.
+//
+// MFMA v_mfma_f32_32x32x16_bf16 lane layout (checked on the device): with l the lane,
+//   A (32 x 16, M x K): lane l holds A[l % 32][8 * (l / 32) + t], t = 0..7
+//   B (16 x 32, K x N): lane l holds B[8 * (l / 32) + t][l % 32]
+//   D (32 x 32):        lane l, register r holds D[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32]
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace br {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Round two floats to bf16 (nearest even) and pack them, low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value held by lane l ^ 32 (the other half of the wave), via v_permlane32_swap.
+__device__ __forceinline__ float other_half(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  // r[0] is the lower half's value and r[1] the upper half's, in every lane.
+  const bool upper = (threadIdx.x & 32) != 0;
+  return __uint_as_float(upper ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ float max_halves(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ u32x4_t load16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+
+}  // namespace br

@@ -1,0 +1,207 @@
+// Attention-mass document scores on gfx950 (BlockRank summary, "Score computation procedure"
+// steps 1-4; blog, attention supervision):
+//   z_{ihj}      = Q_S[i,h] . K[j, h/G] * scale          for j in the prompt's document tokens
+//   alpha'_{ihj} = softmax over all document tokens j of z_{ihj}
+//   s_k          = (1/Hq) sum_h sum_i sum_{j in d_k} alpha'_{ihj}
+//
+// Three kernels, all streaming each document key once from HBM:
+//   1. doc_partial_kernel: one wave per (document group, KV head, 32-row block).  The wave's
+//      rows are (signal token, query head) pairs of one KV group; logits come from the
+//      32x32x16 bf16 MFMA with keys on M.  For every document it keeps a running (max, sum of
+//      exp2) per row and writes (m_k, e_k) at the document's end (a segmented reduction over
+//      document spans; key tiles start at each document's first token).
+//   2. doc_rowstat_kernel: per row, M = max_k m_k and Z = sum_k e_k 2^(m_k - M).
+//   3. doc_final_kernel: per document, head_scores[h,k] = sum_i e_k 2^(m_k - M)/Z and
+//      s_k = mean over heads, summed in a fixed order (deterministic).
+#include "device_common.h"
+#include "launch.h"
+#include "plan.h"
+
+namespace br {
+
+template <int D>
+__global__ __launch_bounds__(256) void doc_partial_kernel(const uint16_t* __restrict__ Q_S,
+                                                          const uint16_t* __restrict__ K,
+                                                          const ScoreItem* __restrict__ items,
+                                                          const int32_t* __restrict__ dof, float2* __restrict__ ml,
+                                                          int64_t n_items, int Hq, int Hkv, int n_signal,
+                                                          int row_blocks, float scale_log2) {
+  constexpr int DSTEPS = D / 16;
+  const int lane = threadIdx.x & 63, n = lane & 31, half = lane >> 5;
+  const int64_t wid = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (wid >= n_items * Hkv * row_blocks) return;  // whole wave exits together
+  const int g = int(wid % Hkv);
+  const int64_t rest = wid / Hkv;
+  const int rb = int(rest % row_blocks);
+  const ScoreItem it = items[rest / row_blocks];
+  const int G = Hq / Hkv;
+  const int rho = rb * 32 + n;
+  const bool row_ok = rho < n_signal * G;
+  const int i = rho / G, h = g * G + rho % G;
+  const int RT = n_signal * Hq;
+  const int64_t kv_stride = int64_t(Hkv) * D;
+
+  // Head-dim order inside the MFMA contraction: lane half `half` supplies elements
+  // half*D/2 + 8*st .. +8 at step st (any order works if Q and K agree; this one makes each
+  // lane's loads one contiguous run).
+  u32x4_t qf[DSTEPS];
+  {
+    const uint16_t* qp = Q_S + ((int64_t(it.prompt) * n_signal + i) * Hq + h) * D + half * (D / 2);
+#pragma unroll
+    for (int s = 0; s < DSTEPS; ++s) qf[s] = row_ok ? load16(qp + 8 * s) : u32x4_t{0, 0, 0, 0};
+  }
+  const uint16_t* kbase = K + int64_t(g) * D + half * (D / 2);
+  auto load_tile = [&](int t0, int end, u32x4_t* kf) {
+    const int j = t0 + n;
+    const uint16_t* kp = kbase + int64_t(j) * kv_stride;
+#pragma unroll
+    for (int s = 0; s < DSTEPS; ++s) kf[s] = j < end ? load16(kp + 8 * s) : u32x4_t{0, 0, 0, 0};
+  };
+
+  int d = it.d0;
+  int a = dof[d], e = dof[d + 1];
+  int t0 = a;
+  u32x4_t kcur[DSTEPS], knext[DSTEPS];
+  load_tile(t0, e, kcur);
+  float m_run = -INFINITY, e_run = 0.f;
+  while (true) {
+    int nd = d, nt0 = t0 + 32, ne = e;
+    if (nt0 >= e) {
+      nd = d + 1;
+      if (nd < it.d1) { nt0 = dof[nd]; ne = dof[nd + 1]; }
+    }
+    const bool has_next = nd < it.d1;
+    if (has_next) load_tile(nt0, ne, knext);
+
+    f32x16_t s = f32x16_t{};
+#pragma unroll
+    for (int st = 0; st < DSTEPS; ++st) s = mfma32(kcur[st], qf[st], s);
+    if (t0 + 32 > e) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = t0 + 8 * (r >> 2) + 4 * half + (r & 3);
+        s[r] = j < e ? s[r] : -INFINITY;
+      }
+    }
+    float mt = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+    const float m_new = fmaxf(m_run, mt * scale_log2);
+    const float mu = m_new == -INFINITY ? 0.f : m_new;
+    float acc = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc += fast_exp2(fmaf(s[r], scale_log2, -mu));
+    e_run = e_run * fast_exp2(m_run - mu) + acc;
+    m_run = m_new;
+
+    if (t0 + 32 >= e) {  // document d is complete: combine the two halves and store (m_k, e_k)
+      const float mo = other_half(m_run), eo = other_half(e_run);
+      const float M = fmaxf(m_run, mo);
+      const float E = e_run * fast_exp2(m_run - M) + eo * fast_exp2(mo - M);
+      if (row_ok && half == 0) ml[int64_t(it.score_base + (d - it.d0)) * RT + int64_t(i) * Hq + h] = float2{M, E};
+      m_run = -INFINITY;
+      e_run = 0.f;
+    }
+    if (!has_next) break;
+#pragma unroll
+    for (int st = 0; st < DSTEPS; ++st) kcur[st] = knext[st];
+    d = nd; t0 = nt0; e = ne;
+  }
+}
+
+// rowstat[b * RT + r] = (M, 1/Z) for row r = i*Hq + h of prompt b.  256 threads: 16 rows x 16
+// document lanes.
+__global__ __launch_bounds__(256) void doc_rowstat_kernel(const float2* __restrict__ ml,
+                                                          const int32_t* __restrict__ prompt_base,
+                                                          float2* __restrict__ rowstat, int RT, int row_groups) {
+  __shared__ float red[16][17];
+  __shared__ float Ms[16];
+  const int b = blockIdx.x / row_groups, rg = blockIdx.x % row_groups;
+  const int rl = threadIdx.x & 15, kl = threadIdx.x >> 4;
+  const int r = rg * 16 + rl;
+  const int k0 = prompt_base[b], k1 = prompt_base[b + 1];
+  float M = -INFINITY;
+  if (r < RT)
+    for (int k = k0 + kl; k < k1; k += 16) M = fmaxf(M, ml[int64_t(k) * RT + r].x);
+  red[rl][kl] = M;
+  __syncthreads();
+  if (kl == 0) {
+    float mm = red[rl][0];
+    for (int t = 1; t < 16; ++t) mm = fmaxf(mm, red[rl][t]);
+    Ms[rl] = mm;
+  }
+  __syncthreads();
+  M = Ms[rl];
+  float Z = 0.f;
+  if (r < RT)
+    for (int k = k0 + kl; k < k1; k += 16) {
+      const float2 v = ml[int64_t(k) * RT + r];
+      Z += v.y * fast_exp2(v.x - M);
+    }
+  __syncthreads();
+  red[rl][kl] = Z;
+  __syncthreads();
+  if (kl == 0 && r < RT) {
+    float zz = 0.f;
+    for (int t = 0; t < 16; ++t) zz += red[rl][t];
+    rowstat[int64_t(b) * RT + r] = float2{M, 1.f / zz};
+  }
+}
+
+__global__ __launch_bounds__(256) void doc_final_kernel(const float2* __restrict__ ml,
+                                                        const float2* __restrict__ rowstat,
+                                                        const int32_t* __restrict__ prompt_base,
+                                                        float* __restrict__ scores, float* __restrict__ head_scores,
+                                                        int num_prompts, int n_signal, int Hq, int n_docs) {
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= n_docs) return;
+  int lo = 0, hi = num_prompts;  // prompt b with prompt_base[b] <= k < prompt_base[b+1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (prompt_base[mid] <= k) lo = mid; else hi = mid;
+  }
+  const int RT = n_signal * Hq;
+  const float2* mk = ml + int64_t(k) * RT;
+  const float2* rs = rowstat + int64_t(lo) * RT;
+  float total = 0.f;
+  for (int h = 0; h < Hq; ++h) {
+    float hs = 0.f;
+    for (int i = 0; i < n_signal; ++i) {
+      const float2 v = mk[i * Hq + h];
+      const float2 st = rs[i * Hq + h];
+      hs += v.y * fast_exp2(v.x - st.x) * st.y;
+    }
+    if (head_scores) head_scores[int64_t(h) * n_docs + k] = hs;
+    total += hs;
+  }
+  scores[k] = total / float(Hq);
+}
+
+hipError_t launch_doc_scores(const ScoreLaunch& a, hipStream_t stream) {
+  const int64_t waves = a.n_items * a.num_kv_heads * a.row_blocks;
+  const dim3 grid(unsigned((waves + 3) / 4));
+  if (a.head_dim == 128)
+    doc_partial_kernel<128><<<grid, 256, 0, stream>>>(a.Q_S, a.K, a.items, a.doc_offsets, a.ml, a.n_items,
+                                                      a.num_q_heads, a.num_kv_heads, a.n_signal, a.row_blocks,
+                                                      a.scale_log2);
+  else if (a.head_dim == 64)
+    doc_partial_kernel<64><<<grid, 256, 0, stream>>>(a.Q_S, a.K, a.items, a.doc_offsets, a.ml, a.n_items,
+                                                     a.num_q_heads, a.num_kv_heads, a.n_signal, a.row_blocks,
+                                                     a.scale_log2);
+  else
+    return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int RT = a.n_signal * a.num_q_heads;
+  const int row_groups = (RT + 15) / 16;
+  float2* rowstat = a.ml + int64_t(a.n_docs) * RT;
+  doc_rowstat_kernel<<<dim3(unsigned(a.num_prompts * row_groups)), 256, 0, stream>>>(a.ml, a.prompt_base, rowstat,
+                                                                                      RT, row_groups);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  doc_final_kernel<<<dim3(unsigned((a.n_docs + 255) / 256)), 256, 0, stream>>>(
+      a.ml, rowstat, a.prompt_base, a.scores, a.head_scores, a.num_prompts, a.n_signal, a.num_q_heads, a.n_docs);
+  return hipGetLastError();
+}
+
+}  // namespace br

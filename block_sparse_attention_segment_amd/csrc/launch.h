@@ -1,0 +1,48 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.h"
+
+namespace br {
+
+struct AttnLaunch {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  uint16_t* O;
+  float* lse;
+  const AttnItem* items;    // device copy of the plan's items
+  const MergeItem* merges;  // device copy of the plan's merges
+  float* part_o;
+  float* part_ml;
+  int64_t n_items, n_merges;
+  int num_q_heads, num_kv_heads, head_dim;
+  float scale_log2;         // softmax scale * log2(e)
+  hipEvent_t ev_start = nullptr, ev_stop = nullptr;  // optional, recorded around the main kernel
+};
+hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream);
+
+struct ScoreLaunch {
+  const uint16_t* Q_S;
+  const uint16_t* K;
+  const ScoreItem* items;
+  const int32_t* doc_offsets;   // device copy
+  const int32_t* prompt_base;   // device copy, [B + 1] score index of each prompt's first document
+  float2* ml;                   // [n_docs, n_signal * Hq] partial (max, sum)
+  float* scores;
+  float* head_scores;
+  int64_t n_items;
+  int num_prompts, num_q_heads, num_kv_heads, head_dim, n_signal, row_blocks, n_docs;
+  float scale_log2;
+};
+hipError_t launch_doc_scores(const ScoreLaunch& a, hipStream_t stream);
+
+constexpr int kSortMaxDocs = 8192;
+constexpr int kSortPromptsPerLaunch = 256;
+hipError_t launch_sort_docs(const float* scores, const int32_t* prompt_base, int num_prompts, int32_t* order,
+                            hipStream_t stream);
+
+}  // namespace br

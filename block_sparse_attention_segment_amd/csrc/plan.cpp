@@ -1,0 +1,219 @@
+// Validation of the segment / document tables and construction of the work plans.
+//
+// The attention plan realises the BlockRank token-type rules (BlockRank summary, section 3.4
+// "Blockwise Structured Attention"; blog, block mask M) as a list of row tiles, each with at
+// most two key ranges: an unmasked range (the instruction, or a chunk of everything before the
+// final query) and a causal range (the tile's own segment up to its last row).  Only these
+// ranges are ever visited, so no forbidden block is formed.  Key tiles of the causal range
+// start at the segment start and key tiles of the instruction range at the prompt start, so a
+// document's arithmetic does not depend on where the document sits in the prompt.
+#include "plan.h"
+
+#include <algorithm>
+#include <cstdio>
+
+namespace br {
+namespace {
+
+Error fail(br_status s, const char* fmt, long long a = 0, long long b = 0, long long c = 0) {
+  char buf[256];
+  std::snprintf(buf, sizeof(buf), fmt, a, b, c);
+  return Error{s, buf};
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+Error validate_dims(const br_dims* dims) {
+  if (!dims) return fail(BR_ERR_INVALID_ARG, "dims is NULL");
+  if (dims->num_prompts < 1) return fail(BR_ERR_INVALID_ARG, "num_prompts must be >= 1 (got %lld)", dims->num_prompts);
+  if (dims->num_q_heads < 1 || dims->num_kv_heads < 1)
+    return fail(BR_ERR_INVALID_ARG, "head counts must be >= 1 (Hq=%lld, Hkv=%lld)", dims->num_q_heads, dims->num_kv_heads);
+  if (dims->num_q_heads % dims->num_kv_heads)
+    return fail(BR_ERR_INVALID_ARG, "num_q_heads (%lld) is not a multiple of num_kv_heads (%lld)", dims->num_q_heads,
+                dims->num_kv_heads);
+  int g = dims->num_q_heads / dims->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(BR_ERR_UNSUPPORTED, "query heads per KV head must be 1, 2, 4 or 8 (got %lld)", g);
+  if (dims->head_dim <= 0) return fail(BR_ERR_INVALID_ARG, "head_dim must be positive (got %lld)", dims->head_dim);
+  if (dims->head_dim != 64 && dims->head_dim != 128)
+    return fail(BR_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %lld)", dims->head_dim);
+  if (dims->total_tokens < 1) return fail(BR_ERR_INVALID_ARG, "total_tokens must be >= 1 (got %lld)", dims->total_tokens);
+  if (dims->total_tokens > (int64_t(1) << 30))
+    return fail(BR_ERR_UNSUPPORTED, "total_tokens %lld exceeds 2^30", dims->total_tokens);
+  return {};
+}
+
+Error validate_segments(const br_dims& dims, const int32_t* so, const int32_t* sp) {
+  if (!so || !sp) return fail(BR_ERR_INVALID_ARG, "segment_offsets and seg_ptr must be non-NULL host arrays");
+  if (sp[0] != 0) return fail(BR_ERR_INVALID_ARG, "seg_ptr[0] must be 0 (got %lld)", sp[0]);
+  int64_t prev_end = 0;
+  for (int b = 0; b < dims.num_prompts; ++b) {
+    int64_t n = int64_t(sp[b + 1]) - sp[b];
+    if (n < 4)
+      return fail(BR_ERR_INVALID_ARG, "prompt %lld has %lld segment offsets; need >= 4 (instruction, >= 1 document, query)", b, n);
+    const int32_t* o = so + sp[b];
+    if (o[0] != prev_end)
+      return fail(BR_ERR_INVALID_ARG, "prompt %lld starts at %lld but the previous prompt ends at %lld", b, o[0], prev_end);
+    if (o[1] < o[0]) return fail(BR_ERR_INVALID_ARG, "prompt %lld: instruction end %lld before its start", b, o[1]);
+    for (int64_t k = 1; k < n - 1; ++k)
+      if (o[k + 1] <= o[k])
+        return fail(BR_ERR_INVALID_ARG, "prompt %lld: segment %lld is empty or reversed (offset %lld)", b, k, o[k + 1]);
+    prev_end = o[n - 1];
+    if (prev_end > dims.total_tokens)
+      return fail(BR_ERR_INVALID_ARG, "prompt %lld ends at %lld beyond total_tokens %lld", b, prev_end, dims.total_tokens);
+  }
+  if (prev_end != dims.total_tokens)
+    return fail(BR_ERR_INVALID_ARG, "last segment offset %lld != total_tokens %lld", prev_end, dims.total_tokens);
+  return {};
+}
+
+Error build_attn_plan(const br_dims& dims, const int32_t* so, const int32_t* sp, AttnPlan* plan) {
+  Error e = validate_dims(&dims);
+  if (!e.ok()) return e;
+  e = validate_segments(dims, so, sp);
+  if (!e.ok()) return e;
+
+  AttnPlan& P = *plan;
+  P = AttnPlan{};
+  P.group = dims.num_q_heads / dims.num_kv_heads;
+  P.rows_per_tile = tokens_per_tile(P.group);
+  P.key_tile = kKeyTile;
+  const int TM = P.rows_per_tile, BN = P.key_tile;
+
+  // Split-key chunk for the final query's rows: aim for ~16 chunks of the longest prefix,
+  // each 4..64 key tiles, so long query tiles spread over many workgroups.
+  int64_t max_prefix = 0;
+  for (int b = 0; b < dims.num_prompts; ++b) {
+    const int32_t* o = so + sp[b];
+    int n = sp[b + 1] - sp[b];
+    max_prefix = std::max<int64_t>(max_prefix, o[n - 2] - o[0]);
+  }
+  int64_t chunk_tiles = std::min<int64_t>(64, std::max<int64_t>(4, cdiv(cdiv(max_prefix, BN), 16)));
+  P.chunk_keys = int(chunk_tiles * BN);
+  const int64_t CK = P.chunk_keys;
+
+  auto tiles = [&](int64_t a, int64_t b) { return int32_t(b > a ? cdiv(b - a, BN) : 0); };
+  auto item = [&](int64_t row0, int64_t lim, int64_t a0, int64_t a1, int64_t b0, int64_t b1, int32_t slot) {
+    if (a1 <= a0) a0 = a1 = 0;
+    if (b1 <= b0) b0 = b1 = 0;
+    return AttnItem{int32_t(row0), int32_t(lim), int32_t(a0), int32_t(a1), int32_t(b0), int32_t(b1), slot,
+                    tiles(a0, a1) + tiles(b0, b1)};
+  };
+
+  std::vector<AttnItem> query_items, other_items;
+  for (int b = 0; b < dims.num_prompts; ++b) {
+    const int32_t* o = so + sp[b];
+    const int n = sp[b + 1] - sp[b];
+    const int64_t ps = o[0], pe = o[1], qs = o[n - 2], qe = o[n - 1];
+    // instruction rows: causal within the instruction
+    for (int64_t r0 = ps; r0 < pe; r0 += TM) other_items.push_back(item(r0, pe, 0, 0, ps, std::min(r0 + TM, pe), -1));
+    // document rows: whole instruction, then own document causally; last row tile first
+    for (int k = 1; k <= n - 3; ++k) {
+      const int64_t ds = o[k], de = o[k + 1];
+      const int64_t ntile = cdiv(de - ds, TM);
+      for (int64_t t = ntile - 1; t >= 0; --t) {
+        const int64_t r0 = ds + t * TM;
+        other_items.push_back(item(r0, de, ps, pe, ds, std::min(r0 + TM, de), -1));
+      }
+    }
+    // final-query rows: everything before the query unmasked, the query causally
+    for (int64_t r0 = qs; r0 < qe; r0 += TM) {
+      const int64_t b1 = std::min(r0 + TM, qe);
+      const int64_t nchunk = std::max<int64_t>(1, cdiv(qs - ps, CK));
+      if (nchunk == 1) {
+        query_items.push_back(item(r0, qe, ps, qs, qs, b1, -1));
+        continue;
+      }
+      const int32_t slot0 = P.n_slots;
+      for (int64_t c = 0; c < nchunk; ++c) {
+        const int64_t a0 = ps + c * CK, a1 = std::min(ps + (c + 1) * CK, qs);
+        const bool last = c == nchunk - 1;
+        query_items.push_back(item(r0, qe, a0, a1, last ? qs : 0, last ? b1 : 0, slot0 + int32_t(c)));
+      }
+      P.merges.push_back(MergeItem{int32_t(r0), int32_t(qe), slot0, int32_t(nchunk)});
+      P.n_slots += int32_t(nchunk);
+    }
+  }
+  // Longest items first: the query chunks, then instruction and document tiles in prompt order
+  // (the row tiles of one document stay adjacent so they share its keys in cache).
+  std::stable_sort(query_items.begin(), query_items.end(),
+                   [](const AttnItem& x, const AttnItem& y) { return x.ntiles > y.ntiles; });
+  P.items = std::move(query_items);
+  P.items.insert(P.items.end(), other_items.begin(), other_items.end());
+
+  const size_t hkv = size_t(dims.num_kv_heads), d = size_t(dims.head_dim);
+  P.off_items = 0;
+  P.off_merges = align_up(P.items.size() * sizeof(AttnItem), 256);
+  P.off_part_o = align_up(P.off_merges + P.merges.size() * sizeof(MergeItem), 256);
+  P.off_part_ml = align_up(P.off_part_o + size_t(P.n_slots) * hkv * kRowsPerTile * d * 4, 256);
+  P.total_bytes = align_up(P.off_part_ml + size_t(P.n_slots) * hkv * kRowsPerTile * 2 * 4, 256);
+  return {};
+}
+
+Error validate_docs(const br_dims& dims, int32_t n_signal, const int32_t* dof, const int32_t* dp) {
+  Error e = validate_dims(&dims);
+  if (!e.ok()) return e;
+  if (!dof || !dp) return fail(BR_ERR_INVALID_ARG, "doc_offsets and doc_ptr must be non-NULL host arrays");
+  if (n_signal < 1) return fail(BR_ERR_INVALID_ARG, "n_signal must be >= 1 (got %lld)", n_signal);
+  if (n_signal > 64) return fail(BR_ERR_UNSUPPORTED, "n_signal %lld exceeds 64", n_signal);
+  if (int64_t(n_signal) * dims.num_q_heads > 4096)
+    return fail(BR_ERR_UNSUPPORTED, "n_signal * num_q_heads = %lld exceeds 4096", int64_t(n_signal) * dims.num_q_heads);
+  if (dp[0] != 0) return fail(BR_ERR_INVALID_ARG, "doc_ptr[0] must be 0 (got %lld)", dp[0]);
+  for (int b = 0; b < dims.num_prompts; ++b) {
+    int64_t n = int64_t(dp[b + 1]) - dp[b];
+    if (n < 2) return fail(BR_ERR_INVALID_ARG, "prompt %lld has %lld document offsets; need >= 2", b, n);
+    const int32_t* o = dof + dp[b];
+    if (o[0] < 0) return fail(BR_ERR_INVALID_ARG, "prompt %lld: document offset %lld is negative", b, o[0]);
+    for (int64_t k = 0; k + 1 < n; ++k)
+      if (o[k + 1] <= o[k])
+        return fail(BR_ERR_INVALID_ARG, "prompt %lld: document %lld is empty or reversed (offset %lld)", b, k, o[k + 1]);
+    if (o[n - 1] > dims.total_tokens)
+      return fail(BR_ERR_INVALID_ARG, "prompt %lld: documents end at %lld beyond total_tokens %lld", b, o[n - 1],
+                  dims.total_tokens);
+  }
+  return {};
+}
+
+Error build_score_plan(const br_dims& dims, int32_t n_signal, const int32_t* dof, const int32_t* dp, ScorePlan* plan) {
+  Error e = validate_docs(dims, n_signal, dof, dp);
+  if (!e.ok()) return e;
+  ScorePlan& P = *plan;
+  P = ScorePlan{};
+  P.group = dims.num_q_heads / dims.num_kv_heads;
+  P.n_signal = n_signal;
+  P.rows_per_kv = n_signal * P.group;
+  P.row_blocks = int(cdiv(P.rows_per_kv, kRowsPerWave));
+  const int B = dims.num_prompts;
+  int64_t doc_tokens = 0;
+  P.prompt_score_base.resize(B + 1);
+  for (int b = 0; b <= B; ++b) P.prompt_score_base[b] = dp[b] - b;
+  P.n_docs = P.prompt_score_base[B];
+  for (int b = 0; b < B; ++b) doc_tokens += dof[dp[b + 1] - 1] - dof[dp[b]];
+  // About 4096 waves in total; each wave streams whole documents.
+  const int64_t waves_per_item = int64_t(dims.num_kv_heads) * P.row_blocks;
+  const int64_t want_items = std::max<int64_t>(1, 4096 / waves_per_item);
+  const int64_t target = std::max<int64_t>(32, cdiv(doc_tokens, want_items));
+  for (int b = 0; b < B; ++b) {
+    int32_t d0 = dp[b];
+    const int32_t dend = dp[b + 1] - 1;  // global index one past the last document of prompt b
+    while (d0 < dend) {
+      int32_t d1 = d0 + 1;
+      while (d1 < dend && dof[d1] - dof[d0] < target) ++d1;
+      P.items.push_back(ScoreItem{b, d0, d1, P.prompt_score_base[b] + (d0 - dp[b])});
+      d0 = d1;
+    }
+  }
+  const size_t n_off = size_t(dp[B]);
+  P.off_items = 0;
+  P.off_doc_offsets = align_up(P.items.size() * sizeof(ScoreItem), 256);
+  P.off_prompt_base = align_up(P.off_doc_offsets + n_off * 4, 256);
+  P.off_ml = align_up(P.off_prompt_base + size_t(B + 1) * 4, 256);
+  // [n_docs, RT] per-document (max, sum) partials followed by [B, RT] per-row (max, 1/Z)
+  const size_t rt = size_t(n_signal) * size_t(dims.num_q_heads);
+  P.total_bytes = align_up(P.off_ml + (size_t(P.n_docs) + size_t(B)) * rt * 8, 256);
+  return {};
+}
+
+}  // namespace br

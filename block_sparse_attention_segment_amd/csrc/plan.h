@@ -1,0 +1,86 @@
+// Host-side validation and work planning for the BlockRank attention and readout kernels.
+// Pure C++ (no HIP calls), so it is unit-testable without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "blockrank.h"
+
+namespace br {
+
+// Attention tiling shared by the planner and the kernels.
+constexpr int kRowsPerWave = 32;                  // one 32x32 MFMA block of query rows per wave
+constexpr int kWaves = 4;                         // waves per workgroup
+constexpr int kRowsPerTile = kRowsPerWave * kWaves;  // 128 (token, head) rows per work item
+constexpr int kKeyTile = 64;                      // keys staged in LDS per step
+
+inline int tokens_per_tile(int group) { return kRowsPerTile / group; }
+
+// One attention work item; the same list is run for every KV head.
+// Rows: tokens [row0, min(row0 + TM, row_limit)) of the G query heads of the KV head.
+// Keys: [a_start, a_end) read unmasked, then [b_start, b_end) read causally.
+struct AttnItem {
+  int32_t row0, row_limit;
+  int32_t a_start, a_end;
+  int32_t b_start, b_end;
+  int32_t slot;    // -1: write the output rows; >= 0: write split-key partials to this slot
+  int32_t ntiles;  // key tiles visited (for scheduling and accounting)
+};
+static_assert(sizeof(AttnItem) == 32, "AttnItem is read as two int4 by the kernel");
+
+// One split query tile: merge partial slots [slot0, slot0 + nslots) into rows.
+struct MergeItem {
+  int32_t row0, row_limit, slot0, nslots;
+};
+
+struct AttnPlan {
+  int group = 1;             // G = Hq / Hkv
+  int rows_per_tile = 128;   // TM tokens per tile
+  int key_tile = kKeyTile;
+  int chunk_keys = 0;        // split-key chunk length for query rows
+  std::vector<AttnItem> items;
+  std::vector<MergeItem> merges;
+  int32_t n_slots = 0;       // partial slots per KV head
+  // workspace layout (bytes from the workspace base)
+  size_t off_items = 0, off_merges = 0, off_part_o = 0, off_part_ml = 0, total_bytes = 0;
+};
+
+struct ScoreItem {
+  int32_t prompt;      // prompt index b
+  int32_t d0, d1;      // global indices into doc_offsets: documents [d0, d1) (d1 - d0 >= 1)
+  int32_t score_base;  // scores index of document d0
+};
+
+struct ScorePlan {
+  int group = 1;
+  int n_signal = 1;
+  int rows_per_kv = 1;   // n_signal * G
+  int row_blocks = 1;    // ceil(rows_per_kv / 32)
+  int32_t n_docs = 0;    // sum_b N_b
+  std::vector<ScoreItem> items;
+  std::vector<int32_t> prompt_score_base;  // [B + 1]
+  size_t off_items = 0, off_doc_offsets = 0, off_prompt_base = 0, off_ml = 0, total_bytes = 0;
+};
+
+// Status plus message; the API layer stores the message in the thread-local error slot.
+struct Error {
+  br_status status = BR_OK;
+  std::string msg;
+  bool ok() const { return status == BR_OK; }
+};
+
+Error validate_dims(const br_dims* dims);
+Error validate_segments(const br_dims& dims, const int32_t* segment_offsets, const int32_t* seg_ptr);
+Error build_attn_plan(const br_dims& dims, const int32_t* segment_offsets, const int32_t* seg_ptr,
+                      AttnPlan* plan);
+Error validate_docs(const br_dims& dims, int32_t n_signal, const int32_t* doc_offsets,
+                    const int32_t* doc_ptr);
+Error build_score_plan(const br_dims& dims, int32_t n_signal, const int32_t* doc_offsets,
+                       const int32_t* doc_ptr, ScorePlan* plan);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace br

@@ -1,0 +1,167 @@
+/*
+ * blockrank.h -- C ABI of the MI355X (gfx950) BlockRank hot path.
+ *
+ * BlockRank ("Scalable In-context Ranking with Generative Models") ranks N candidate
+ * documents with one LLM prompt P = I || d_1 || ... || d_N || q (instruction prefix,
+ * documents, final query; BlockRank blog, candidate arrangement).  This library computes,
+ * for one attention layer:
+ *
+ *   br_attn_fwd     block-sparse prefill attention softmax(Q K^T * scale + M) V, where the
+ *                   mask M lets instruction tokens read the instruction causally, each
+ *                   document read the whole instruction plus itself causally, and the
+ *                   final query read everything before it plus itself causally
+ *                   (BlockRank summary, section 3.4 "Blockwise Structured Attention";
+ *                   blog, directed-attention section: block mask with causal diagonal
+ *                   blocks C).  Forbidden blocks are never computed.
+ *   br_doc_scores   the attention-mass readout: for each signal query row i and head h,
+ *                   a softmax of z = Q_S[i,h] . K[j, h/G] * scale over the prompt's
+ *                   document tokens only, summed per document and over signal rows and
+ *                   averaged over heads (BlockRank summary, "Score computation procedure"
+ *                   steps 1-4; blog, attention supervision: s_k, sum_k s_k = |S|).
+ *   br_sort_docs    per prompt, document indices by descending s_k (ties: lower index)
+ *                   (BlockRank summary, "Efficient Attention-Based Inference" step 3;
+ *                   blog, direct output).
+ *
+ * Conventions (all entry points):
+ *   - Every function returns br_status; BR_OK == 0.  Nothing aborts or throws.
+ *   - All argument checks run on the host before any HIP call; on failure nothing is
+ *     enqueued and br_last_error() (thread-local) holds a message.  A HIP runtime error
+ *     maps to BR_ERR_HIP with hipGetErrorString's text.  Outputs are undefined on error.
+ *   - Device buffers (Q, K, V, out, lse, Q_S, scores, head_scores, order, workspace) are
+ *     owned by the caller and must stay alive until the work enqueued on `stream`
+ *     completes.  Host arrays (segment_offsets, seg_ptr, doc_offsets, doc_ptr) are read
+ *     only during the call.  The library keeps no per-call device state; it owns only a
+ *     small pool of pinned host staging buffers for uploading the work plan.
+ *   - Every compute call only enqueues work on `stream` (hipStream_t; 0 = null stream).
+ *     The calling thread's current HIP device must be the stream's device.
+ *   - Tensors are token-major and packed over all prompts ("THD"), bf16 = IEEE bfloat16
+ *     bit patterns, contiguous, 16-byte aligned base pointers.
+ *   - Supported: head_dim in {64, 128}; num_q_heads % num_kv_heads == 0 with
+ *     G = num_q_heads / num_kv_heads in {1, 2, 4, 8}; query head h reads KV head h / G.
+ */
+#ifndef BLOCKRANK_H
+#define BLOCKRANK_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BR_OK = 0,
+  BR_ERR_INVALID_ARG = 1,  /* malformed sizes, tables or pointers */
+  BR_ERR_UNSUPPORTED = 2,  /* well-formed but outside the supported shapes */
+  BR_ERR_WORKSPACE = 3,    /* workspace missing or smaller than *_workspace_bytes */
+  BR_ERR_HIP = 4           /* a HIP runtime call failed */
+} br_status;
+
+typedef struct {
+  int32_t num_prompts;   /* B >= 1 */
+  int32_t num_q_heads;   /* Hq */
+  int32_t num_kv_heads;  /* Hkv, divides Hq */
+  int32_t head_dim;      /* d: 64 or 128 */
+  int64_t total_tokens;  /* T = sum of prompt lengths = last segment offset */
+} br_dims;
+
+/*
+ * Segment table (host int32).  Prompt b owns
+ *   segment_offsets[seg_ptr[b] .. seg_ptr[b+1]) = {s, s+p, s+p+l_1, ..., s+p+D, s+L}
+ * i.e. N_b + 3 absolute token offsets, N_b >= 1: segment 0 is the instruction (p >= 0
+ * tokens, may be empty), the last segment is the final query (q >= 1 tokens), the ones
+ * between are the N_b documents (each l_k >= 1 token).  Prompts are contiguous:
+ * segment_offsets[0] == 0, prompt b+1 starts where prompt b ends, and the last offset
+ * equals dims->total_tokens.  seg_ptr is int32[B + 1] with seg_ptr[0] == 0.
+ */
+
+/* Bytes of device workspace br_attn_fwd needs for this table (plan + split-key partials). */
+br_status br_attn_workspace_bytes(const br_dims* dims, const int32_t* segment_offsets,
+                                  const int32_t* seg_ptr, size_t* bytes);
+
+/*
+ * Block-sparse prefill attention for one layer.
+ *   Q    device bf16 [T, Hq, d]      K, V  device bf16 [T, Hkv, d]
+ *   out  device bf16 [T, Hq, d]      every row is written (no row has an empty key set:
+ *                                    each token may read itself)
+ *   lse  device fp32 [T, Hq] or NULL natural-log log-sum-exp of the scaled logits per row
+ *   softmax_scale  <= 0 selects 1/sqrt(d)
+ *   workspace      device, >= br_attn_workspace_bytes(), 256-byte aligned
+ * Arithmetic: bf16 operands, fp32 accumulation and softmax statistics, probabilities
+ * rounded to bf16 before the P.V product, output rounded to nearest even bf16.
+ */
+br_status br_attn_fwd(const br_dims* dims, const void* Q, const void* K, const void* V,
+                      const int32_t* segment_offsets, const int32_t* seg_ptr, void* out,
+                      float* lse, float softmax_scale, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/*
+ * br_attn_fwd, plus timing: records `kernel_start` on `stream` immediately before the main
+ * attention kernel is enqueued and `kernel_stop` immediately after it (the split-key merge
+ * kernel, if any, follows `kernel_stop`).  Either event may be NULL.  For measuring the
+ * attention kernel's own duration with hipEventElapsedTime; results are identical to
+ * br_attn_fwd.
+ */
+br_status br_attn_fwd_timed(const br_dims* dims, const void* Q, const void* K, const void* V,
+                            const int32_t* segment_offsets, const int32_t* seg_ptr, void* out,
+                            float* lse, float softmax_scale, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream, hipEvent_t kernel_start,
+                            hipEvent_t kernel_stop);
+
+/*
+ * Document spans (host int32).  Prompt b owns doc_offsets[doc_ptr[b] .. doc_ptr[b+1]),
+ * N_b + 1 increasing absolute token offsets (normally segment_offsets[1 .. N_b+2) of that
+ * prompt); document k of prompt b is [doc_offsets[doc_ptr[b]+k], doc_offsets[doc_ptr[b]+k+1]).
+ * Its score is stored at index doc_ptr[b] - b + k.  Spans must lie inside [0, T).
+ */
+br_status br_doc_scores_workspace_bytes(const br_dims* dims, int32_t n_signal,
+                                        const int32_t* doc_offsets, const int32_t* doc_ptr,
+                                        size_t* bytes);
+
+/*
+ * Attention-mass document scores.
+ *   Q_S          device bf16 [B, n_signal, Hq, d]: the signal-carrier query rows
+ *   K            device bf16 [T, Hkv, d] (the same layer's keys as the attention)
+ *   scores       device fp32 [sum_b N_b]: s_k = (1/Hq) sum_h sum_i sum_{j in d_k} alpha'_{ihj}
+ *   head_scores  device fp32 [Hq, sum_b N_b] (per-head signal-row sums) or NULL
+ *   softmax_scale <= 0 selects 1/sqrt(d)
+ * n_signal in [1, 64]; sum_k s_k = n_signal per prompt up to rounding.
+ */
+br_status br_doc_scores(const br_dims* dims, const void* Q_S, int32_t n_signal, const void* K,
+                        const int32_t* doc_offsets, const int32_t* doc_ptr, float* scores,
+                        float* head_scores, float softmax_scale, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Per-prompt ranking.  scores: device fp32 [sum_b N_b] laid out as br_doc_scores writes
+ * them; doc_ptr: host int32[B + 1] as above (only differences are used: N_b =
+ * doc_ptr[b+1] - doc_ptr[b] - 1).  order: device int32 [sum_b N_b]; for prompt b, entries
+ * doc_ptr[b]-b .. +N_b hold local document indices in descending score order, ties to the
+ * lower index; NaN scores rank as -infinity.  N_b <= 8192.
+ */
+br_status br_sort_docs(const float* scores, const int32_t* doc_ptr, int32_t num_prompts,
+                       int32_t* order, hipStream_t stream);
+
+/*
+ * Host-only introspection of the attention work plan (no HIP call).  Writes up to
+ * `capacity` work items of 8 int32 each, {row0, row_limit, a_start, a_end, b_start, b_end,
+ * partial_slot, tile_count}: the row tile starts at token row0 and covers the tokens
+ * [row0, min(row0 + rows_per_tile, row_limit)) of every query head of a KV group; it reads
+ * keys [a_start, a_end) unmasked and [b_start, b_end) causally (key <= row token).
+ * partial_slot >= 0 marks one chunk of a split query tile.  The list is the same for
+ * every KV head.  *n_items receives the item count, *rows_per_tile the token rows per tile.
+ */
+br_status br_attn_plan_items(const br_dims* dims, const int32_t* segment_offsets,
+                             const int32_t* seg_ptr, int32_t* items, int64_t capacity,
+                             int64_t* n_items, int32_t* rows_per_tile);
+
+const char* br_status_string(br_status status);
+const char* br_last_error(void);
+const char* br_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLOCKRANK_H */

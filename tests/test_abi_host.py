@@ -1,0 +1,175 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every declared symbol, rejects bad
+arguments before any HIP call, and its attention plan covers exactly the allowed pairs."""
+import ctypes
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_segment_amd as br
+import oracle.oracle as orc
+import workloads
+from pins import random_prompts
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_header_symbol():
+    lib = br.load_library()
+    with open(os.path.join(ROOT, "include", "blockrank.h")) as f:
+        header = f.read()
+    declared = set(re.findall(r"\b(br_[a-z_]+)\s*\(", header))
+    assert declared == set(br.EXPORTED), declared ^ set(br.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert br.version().startswith("blockrank-gfx950")
+
+
+def _covered_pairs(items, tm, T):
+    """(row, key) pairs the plan visits after its own masking."""
+    pairs = set()
+    for (row0, lim, a0, a1, b0, b1, slot, nt) in items:
+        rows = range(row0, min(row0 + tm, lim))
+        for i in rows:
+            for j in range(a0, a1):
+                pairs.add((i, j))
+            for j in range(b0, min(b1, i + 1)):
+                pairs.add((i, j))
+    return pairs
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_plan_covers_exactly_the_mask(seed):
+    rng = random.Random(seed)
+    prompts = random_prompts(rng, batch=rng.randint(1, 3), p_max=70, n_max=5, l_max=150, q_max=140)
+    hq, hkv = rng.choice([(1, 1), (2, 1), (4, 1), (8, 1), (32, 8)])
+    seg, sp, _, _ = workloads.segment_tables(prompts)
+    T = int(seg[-1])
+    dims = br.make_dims(len(prompts), hq, hkv, 64, T)
+    items, tm = br.attn_plan_items(dims, seg, sp)
+    assert tm == 128 // (hq // hkv)
+    got = _covered_pairs(items, tm, T)
+    tables = orc.token_tables(seg, sp)
+    idx = np.arange(T)
+    mask = orc.allowed(idx[:, None], idx[None, :], tables)
+    want = set(zip(*np.nonzero(mask)))
+    assert got == {(int(a), int(b)) for a, b in want}
+    # every row is owned by exactly one direct item or one split query tile
+    owners = np.zeros(T, dtype=np.int64)
+    split_tiles = set()
+    for (row0, lim, a0, a1, b0, b1, slot, nt) in items:
+        assert 0 <= row0 < lim <= T and 0 <= a0 <= a1 <= T and 0 <= b0 <= b1 <= T
+        if slot < 0:
+            owners[row0:min(row0 + tm, lim)] += 1
+        elif (row0, lim) not in split_tiles:
+            split_tiles.add((row0, lim))
+            owners[row0:min(row0 + tm, lim)] += 1
+    assert (owners == 1).all()
+
+
+def test_plan_visits_no_forbidden_tile_at_worked_shape():
+    w_seg, w_sp, _, _ = workloads.segment_tables([(32, [128] * 100, 32)])
+    dims = br.make_dims(1, 32, 8, 128, int(w_seg[-1]))
+    items, tm = br.attn_plan_items(dims, w_seg, w_sp)
+    assert tm == 32
+    # documents read only [0, 32) and their own span; the query reads [0, L)
+    offs = list(map(int, w_seg))
+    for (row0, lim, a0, a1, b0, b1, slot, nt) in items:
+        if row0 >= offs[-2]:
+            continue
+        k = np.searchsorted(offs, row0, side="right") - 1
+        if k == 0:
+            assert (a0, a1) == (0, 0) and (b0, b1) == (0, min(row0 + tm, 32))
+        else:
+            assert (a0, a1) == (0, 32) and b0 == offs[k] and b1 <= offs[k + 1]
+
+
+def _fake(n=1):
+    return ctypes.c_void_p(0x10000)  # non-NULL, 16-byte aligned; never dereferenced on error paths
+
+
+BAD_TABLES = [
+    ("seg_ptr0", [0, 4, 6, 8, 10], [1, 5], br._lib.BR_ERR_INVALID_ARG),
+    ("too_few_offsets", [0, 4, 8], [0, 3], br._lib.BR_ERR_INVALID_ARG),
+    ("empty_doc", [0, 4, 4, 8, 10], [0, 5], br._lib.BR_ERR_INVALID_ARG),
+    ("empty_query", [0, 4, 6, 10, 10], [0, 5], br._lib.BR_ERR_INVALID_ARG),
+    ("reversed", [0, 4, 3, 8, 10], [0, 5], br._lib.BR_ERR_INVALID_ARG),
+    ("not_starting_at_0", [2, 4, 6, 8, 10], [0, 5], br._lib.BR_ERR_INVALID_ARG),
+    ("total_mismatch", [0, 4, 6, 8, 9], [0, 5], br._lib.BR_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,seg,sp,status", BAD_TABLES, ids=[t[0] for t in BAD_TABLES])
+def test_bad_segment_tables_rejected(name, seg, sp, status):
+    dims = br.make_dims(1, 4, 2, 64, 10)
+    with pytest.raises(br.BlockRankError) as ei:
+        br.attn_workspace_bytes(dims, seg, sp)
+    assert ei.value.status == status
+
+
+def test_noncontiguous_prompts_rejected():
+    dims = br.make_dims(2, 4, 2, 64, 20)
+    with pytest.raises(br.BlockRankError) as ei:
+        br.attn_workspace_bytes(dims, [0, 2, 5, 10, 11, 13, 16, 20], [0, 4, 8])
+    assert "previous prompt" in ei.value.message
+
+
+@pytest.mark.parametrize("hq,hkv,d,status", [(4, 3, 64, 1), (16, 1, 64, 2), (4, 2, 96, 2), (4, 2, 0, 1),
+                                             (0, 1, 64, 1)])
+def test_bad_dims_rejected(hq, hkv, d, status):
+    dims = br.make_dims(1, hq, hkv, d, 10)
+    with pytest.raises(br.BlockRankError) as ei:
+        br.attn_workspace_bytes(dims, [0, 4, 6, 8, 10], [0, 5])
+    assert ei.value.status == status
+
+
+def test_attn_fwd_rejects_before_any_hip_call():
+    lib = br.load_library()
+    seg = np.array([0, 4, 6, 8, 10], dtype=np.int32)
+    sp = np.array([0, 5], dtype=np.int32)
+    p = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    dims = br.make_dims(1, 4, 2, 64, 10)
+    need = br.attn_workspace_bytes(dims, seg, sp)
+    f = _fake()
+    # workspace too small
+    st = lib.br_attn_fwd(ctypes.byref(dims), f, f, f, p(seg), p(sp), f, None, 0.0, f, need - 1, None)
+    assert st == br._lib.BR_ERR_WORKSPACE
+    # NULL input
+    st = lib.br_attn_fwd(ctypes.byref(dims), None, f, f, p(seg), p(sp), f, None, 0.0, f, need, None)
+    assert st == br._lib.BR_ERR_INVALID_ARG
+    # misaligned output
+    st = lib.br_attn_fwd(ctypes.byref(dims), f, f, f, p(seg), p(sp), ctypes.c_void_p(0x10002), None, 0.0, f,
+                         need, None)
+    assert st == br._lib.BR_ERR_INVALID_ARG
+    # non-finite scale
+    st = lib.br_attn_fwd(ctypes.byref(dims), f, f, f, p(seg), p(sp), f, None, float("nan"), f, need, None)
+    assert st == br._lib.BR_ERR_INVALID_ARG
+    assert b"finite" in lib.br_last_error()
+
+
+def test_doc_scores_and_sort_reject_bad_arguments():
+    lib = br.load_library()
+    p = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    dims = br.make_dims(1, 4, 2, 64, 10)
+    f = _fake()
+    do = np.array([4, 6, 8], dtype=np.int32)
+    dp = np.array([0, 3], dtype=np.int32)
+    need = br.doc_scores_workspace_bytes(dims, 2, do, dp)
+    assert lib.br_doc_scores(ctypes.byref(dims), f, 2, f, p(do), p(dp), f, None, 0.0, f, need - 1,
+                             None) == br._lib.BR_ERR_WORKSPACE
+    assert lib.br_doc_scores(ctypes.byref(dims), f, 0, f, p(do), p(dp), f, None, 0.0, f, need,
+                             None) == br._lib.BR_ERR_INVALID_ARG
+    assert lib.br_doc_scores(ctypes.byref(dims), f, 65, f, p(do), p(dp), f, None, 0.0, f, need,
+                             None) == br._lib.BR_ERR_UNSUPPORTED
+    bad = np.array([4, 4, 8], dtype=np.int32)
+    assert lib.br_doc_scores(ctypes.byref(dims), f, 2, f, p(bad), p(dp), f, None, 0.0, f, need,
+                             None) == br._lib.BR_ERR_INVALID_ARG
+    beyond = np.array([4, 6, 11], dtype=np.int32)
+    assert lib.br_doc_scores(ctypes.byref(dims), f, 2, f, p(beyond), p(dp), f, None, 0.0, f, need,
+                             None) == br._lib.BR_ERR_INVALID_ARG
+    big = np.array([0, 8194], dtype=np.int32)
+    assert lib.br_sort_docs(f, p(big), 1, f, None) == br._lib.BR_ERR_UNSUPPORTED
+    assert lib.br_sort_docs(f, p(np.array([0, 1], dtype=np.int32)), 1, f, None) == br._lib.BR_ERR_INVALID_ARG
+    assert lib.br_sort_docs(None, p(dp), 1, f, None) == br._lib.BR_ERR_INVALID_ARG

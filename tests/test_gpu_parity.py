@@ -1,0 +1,149 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on seeded inputs.
+
+Tolerances: attention max-abs <= 2e-2, LSE relative 1e-3, scores relative 1e-3 (+1e-6*|S|),
+argmax / order agreement wherever the oracle's gap exceeds 1e-3, document rows bit-exact under
+changes to other documents, and bitwise run-to-run determinism.
+"""
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_segment_amd as br
+import oracle.oracle as orc
+import workloads
+from gpu_util import (ATTN_ATOL, LSE_RTOL, check_attn, check_order, check_scores, log, run_attn, to_f64,
+                      upload)
+from pins import random_prompts
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_check(w, what, scale=0.0):
+    log(f"[gpu] {what}: T={w.total_tokens} Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim}")
+    dev = upload(w)
+    out, lse = run_attn(w, dev, lse=True, scale=scale)
+    sc = None if scale <= 0 else scale
+    ref, ref_lse = orc.attn_dense(w.Q, w.K, w.V, w.segment_offsets, w.seg_ptr, scale=sc)
+    err = check_attn(out, ref, what=what)
+    lg = to_f64(lse)
+    rel = np.abs(lg - ref_lse) / np.maximum(np.abs(ref_lse), 1.0)
+    assert rel.max() <= LSE_RTOL, f"{what}: lse rel err {rel.max():.3e}"
+    scores, hs = br.doc_scores(dev["Q_S"], dev["K"], w.doc_offsets, w.doc_ptr, head_scores=True,
+                               softmax_scale=scale)
+    order = br.sort_docs(scores, w.doc_ptr)
+    torch.cuda.synchronize()
+    ref_s, ref_hs = orc.doc_scores(w.Q_S, w.K, w.doc_offsets, w.doc_ptr, scale=sc)
+    check_scores(scores.cpu().numpy().astype(np.float64), ref_s, w.n_signal, what)
+    check_scores(hs.cpu().numpy().astype(np.float64).ravel(), ref_hs.ravel(), w.n_signal, what + " head_scores")
+    check_order(order.cpu().numpy(), ref_s, w.doc_ptr, what)
+    return err
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_tiny_config(seed):
+    w = workloads.make("tiny", seed)
+    _full_check(w, f"tiny seed={seed}")
+
+
+SHAPES = [(1, 1, 64), (2, 1, 64), (4, 1, 128), (8, 1, 64), (8, 2, 128), (32, 8, 128), (4, 4, 128), (16, 2, 64)]
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_small_tables(case):
+    rng = random.Random(1000 + case)
+    hq, hkv, d = SHAPES[case % len(SHAPES)]
+    prompts = random_prompts(rng, batch=rng.randint(1, 3), p_max=40, n_max=6, l_max=70, q_max=40,
+                             p_min=0 if case % 4 == 0 else 1)
+    prompts = [(p, l, max(q, 2)) for (p, l, q) in prompts]
+    w = workloads.make_custom(prompts, hq, hkv, d, 2, 1000 + case)
+    _full_check(w, f"random case={case} prompts={prompts}")
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_ragged_tails_and_long_segments(case):
+    """Segments longer than several tiles with ragged tails; a long prefix that forces the split-key
+    query path with several chunks."""
+    rng = random.Random(2000 + case)
+    prompts = [(rng.randint(60, 200), [rng.randint(1, 300) for _ in range(rng.randint(3, 9))],
+                rng.randint(30, 150)) for _ in range(rng.randint(1, 2))]
+    hq, hkv, d = [(8, 2, 128), (4, 1, 64), (32, 8, 128), (2, 2, 128)][case]
+    w = workloads.make_custom(prompts, hq, hkv, d, 4, 2000 + case)
+    _full_check(w, f"ragged-tail case={case}")
+
+
+def test_sharp_softmax_stress():
+    rng = random.Random(77)
+    prompts = random_prompts(rng, batch=2, p_max=40, n_max=6, l_max=90, q_max=40, p_min=1)
+    prompts = [(p, l, max(q, 4)) for (p, l, q) in prompts]
+    w = workloads.make_custom(prompts, 8, 2, 128, 4, 77, q_scale=8.0)
+    _full_check(w, "sharp softmax (Q x 8)")
+
+
+def test_custom_scale():
+    rng = random.Random(78)
+    prompts = random_prompts(rng, batch=1, p_max=30, n_max=4, l_max=60, q_max=30, p_min=1)
+    prompts = [(p, l, max(q, 2)) for (p, l, q) in prompts]
+    w = workloads.make_custom(prompts, 4, 2, 64, 2, 78)
+    _full_check(w, "custom scale 0.05", scale=0.05)
+
+
+def test_document_isolation_bit_exact():
+    """Document rows do not change, bit for bit, when other documents are permuted or altered."""
+    lens = [37, 64, 129, 5, 90, 64]
+    w = workloads.make_custom([(40, lens, 30)], 8, 2, 128, 2, 91)
+    log("[gpu] isolation: base run")
+    dev = upload(w)
+    base = run_attn(w, dev).cpu()
+    so = [int(x) for x in w.segment_offsets]
+    spans = [(so[1 + k], so[2 + k]) for k in range(len(lens))]
+    perm = [4, 2, 0, 5, 3, 1]
+    idx = np.r_[0:so[1], np.concatenate([np.arange(*spans[k]) for k in perm]), so[-2]:so[-1]]
+    seg_p, sp_p, _, _ = workloads.segment_tables([(40, [lens[k] for k in perm], 30)])
+    wp = workloads.make_custom([(40, [lens[k] for k in perm], 30)], 8, 2, 128, 2, 91)
+    wp.Q, wp.K, wp.V = w.Q[idx].copy(), w.K[idx].copy(), w.V[idx].copy()
+    # alter document 3 (in the permuted prompt) completely
+    a3, e3 = [int(x) for x in wp.segment_offsets[4:6]]
+    noise = np.random.default_rng(3)
+    wp.K[a3:e3] = noise.integers(0x3c00, 0x4000, size=wp.K[a3:e3].shape, dtype=np.uint16)
+    wp.V[a3:e3] = noise.integers(0x3c00, 0x4000, size=wp.V[a3:e3].shape, dtype=np.uint16)
+    log("[gpu] isolation: permuted + altered run")
+    perm_out = run_attn(wp, upload(wp)).cpu()
+    pos = so[1]
+    b16 = lambda t: t.view(torch.int16).numpy()
+    for slot, k in enumerate(perm):
+        a, e = spans[k]
+        if slot != 3:
+            np.testing.assert_array_equal(b16(perm_out[pos:pos + (e - a)]), b16(base[a:e]), err_msg=f"doc {k}")
+        pos += e - a
+    np.testing.assert_array_equal(b16(perm_out[:so[1]]), b16(base[:so[1]]))
+
+
+def test_sort_matches_oracle_rank_bit_exact():
+    r = np.random.default_rng(11)
+    n_list = [1, 7, 100, 500, 33, 8192]
+    scores = np.concatenate([(np.round(r.random(n) * 64) / 64).astype(np.float32) for n in n_list])
+    scores[5] = -0.0
+    scores[6] = 0.0
+    scores[20] = np.nan
+    dp = np.cumsum([0] + [n + 1 for n in n_list]).astype(np.int32)
+    log("[gpu] sort: ties, signed zeros, NaN, N up to 8192")
+    got = br.sort_docs(torch.from_numpy(scores).cuda(), dp).cpu().numpy()
+    ref_in = np.where(np.isnan(scores), -np.inf, scores)
+    np.testing.assert_array_equal(got, orc.rank(ref_in, dp))
+
+
+def test_bitwise_determinism():
+    w = workloads.make("worked", 1)
+    dev = upload(w)
+    log("[gpu] determinism: worked seed 1, two runs")
+    r = []
+    for _ in range(2):
+        out, lse = run_attn(w, dev, lse=True)
+        s = br.doc_scores(dev["Q_S"], dev["K"], w.doc_offsets, w.doc_ptr)
+        o = br.sort_docs(s, w.doc_ptr)
+        torch.cuda.synchronize()
+        r.append((out.view(torch.int16).cpu().numpy(), lse.cpu().numpy(), s.cpu().numpy(), o.cpu().numpy()))
+    for a, b in zip(r[0], r[1]):
+        np.testing.assert_array_equal(a, b)
