@@ -179,8 +179,10 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--secondary", default="worked", help="extra config timed in the same run ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-docs", type=int, default=24, help="documents in the CPU oracle's timed sample")
+    ap.add_argument("--cpu-docs", type=int, default=200, help="documents in the CPU oracle's timed sample")
     ap.add_argument("--traffic", default="", help="JSON file with measured HBM bytes per attention launch")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     log = lambda m: print(m, file=sys.stderr, flush=True)
     if args.gpus != 1:
@@ -191,6 +193,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_mib:
+        # Calibration for HBM byte counters: each launch reads and writes exactly copy_mib MiB.
+        n = args.copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": args.steps}), flush=True)
+        return
 
     r = measure(args.config, args.seed, args.steps, args.warmup, log)
     w = r["w"]

@@ -29,7 +29,7 @@ namespace br {
 constexpr float kRescaleSlack = 8.0f;
 
 template <int D, int G>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                        const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                                                        float* __restrict__ lse, const AttnItem* __restrict__ items,
                                                        float* __restrict__ part_o, float* __restrict__ part_ml, int Hq,
@@ -231,46 +231,46 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const uint16_t* __restric
 }
 
 // Combine split-key partials of one query tile: M = max m_c, L = sum l_c 2^(m_c - M),
-// o = sum o_c 2^(m_c - M) / L.  Two threads per row, each owning half of the head dimension.
+// o = sum o_c 2^(m_c - M) / L.  One thread per (row, 8 head-dim elements); a workgroup covers
+// 256 such units, so one (query tile, KV head) spreads over 128 * D / 8 / 256 workgroups.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(uint16_t* __restrict__ O, float* __restrict__ lse,
                                                          const MergeItem* __restrict__ merges,
                                                          const float* __restrict__ part_o,
                                                          const float* __restrict__ part_ml, int Hq, int Hkv, int G) {
-  const int g = blockIdx.x % Hkv;
-  const MergeItem mi = merges[blockIdx.x / Hkv];
+  constexpr int CH = D / 8;                          // 8-element chunks per row
+  constexpr int WG_PER_TILE = kRowsPerTile * CH / 256;
+  const int tile = blockIdx.x / WG_PER_TILE, part = blockIdx.x % WG_PER_TILE;
+  const int g = tile % Hkv;
+  const MergeItem mi = merges[tile / Hkv];
+  const int unit = part * 256 + threadIdx.x;
+  const int rho = unit / CH, ch = unit % CH;
   const int TM = kRowsPerTile / G;
-  const int rho = threadIdx.x >> 1, part = threadIdx.x & 1;
   const int tok = mi.row0 + rho % TM, h = g * G + rho / TM;
   if (tok >= mi.row_limit) return;
-  auto ml_at = [&](int c) { return part_ml + ((int64_t(mi.slot0 + c) * Hkv + g) * kRowsPerTile + rho) * 2; };
+  const int64_t stride = int64_t(Hkv) * kRowsPerTile;  // rows between consecutive slots
+  const int64_t row = (int64_t(mi.slot0) * Hkv + g) * kRowsPerTile + rho;
   float M = -INFINITY;
-  for (int c = 0; c < mi.nslots; ++c) M = fmaxf(M, ml_at(c)[0]);
+  for (int c = 0; c < mi.nslots; ++c) M = fmaxf(M, part_ml[(row + c * stride) * 2]);
   float L = 0.f;
-  constexpr int HD = D / 2;
-  float acc[HD];
-#pragma unroll
-  for (int e = 0; e < HD; ++e) acc[e] = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int c = 0; c < mi.nslots; ++c) {
-    const float* ml = ml_at(c);
-    const float wgt = fast_exp2(ml[0] - M);
-    L += ml[1] * wgt;
-    const float* po = part_o + ((int64_t(mi.slot0 + c) * Hkv + g) * kRowsPerTile + rho) * D + part * HD;
+    const int64_t r = row + c * stride;
+    const float wgt = fast_exp2(part_ml[r * 2] - M);
+    L += part_ml[r * 2 + 1] * wgt;
+    const f32x4_t* po = reinterpret_cast<const f32x4_t*>(part_o + r * D + ch * 8);
+    const f32x4_t v0 = po[0], v1 = po[1];
 #pragma unroll
-    for (int e = 0; e < HD; e += 4) {
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(po + e);
-      acc[e] += wgt * v[0]; acc[e + 1] += wgt * v[1]; acc[e + 2] += wgt * v[2]; acc[e + 3] += wgt * v[3];
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += wgt * v0[e];
+      acc[4 + e] += wgt * v1[e];
     }
   }
   const float inv = 1.f / L;
-  uint16_t* op = O + (int64_t(tok) * Hq + h) * D + part * HD;
-#pragma unroll
-  for (int e = 0; e < HD; e += 8) {
-    const u32x4_t v = {pack_bf16x2(acc[e] * inv, acc[e + 1] * inv), pack_bf16x2(acc[e + 2] * inv, acc[e + 3] * inv),
-                       pack_bf16x2(acc[e + 4] * inv, acc[e + 5] * inv), pack_bf16x2(acc[e + 6] * inv, acc[e + 7] * inv)};
-    *reinterpret_cast<u32x4_t*>(op + e) = v;
-  }
-  if (lse && part == 0) lse[int64_t(tok) * Hq + h] = (M + __log2f(L)) * kLn2;
+  const u32x4_t v = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                     pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+  *reinterpret_cast<u32x4_t*>(O + (int64_t(tok) * Hq + h) * D + ch * 8) = v;
+  if (lse && ch == 0) lse[int64_t(tok) * Hq + h] = (M + __log2f(L)) * kLn2;
 }
 
 template <int D, int G>
@@ -291,7 +291,7 @@ static hipError_t launch_attn_t(const AttnLaunch& a, hipStream_t stream) {
     }
   }
   if (a.n_merges > 0) {
-    const dim3 grid(unsigned(a.n_merges * a.num_kv_heads));
+    const dim3 grid(unsigned(a.n_merges * a.num_kv_heads * (kRowsPerTile * (D / 8) / 256)));
     attn_merge_kernel<D><<<grid, 256, 0, stream>>>(a.O, a.lse, a.merges, a.part_o, a.part_ml, a.num_q_heads,
                                                    a.num_kv_heads, G);
     return hipGetLastError();

@@ -11,8 +11,8 @@
 //      exp2) per row and writes (m_k, e_k) at the document's end (a segmented reduction over
 //      document spans; key tiles start at each document's first token).
 //   2. doc_rowstat_kernel: per row, M = max_k m_k and Z = sum_k e_k 2^(m_k - M).
-//   3. doc_final_kernel: per document, head_scores[h,k] = sum_i e_k 2^(m_k - M)/Z and
-//      s_k = mean over heads, summed in a fixed order (deterministic).
+//   3. doc_final_kernel: one workgroup per document, head_scores[h,k] = sum_i e_k 2^(m_k - M)/Z
+//      and s_k = mean over heads, summed in a fixed order (deterministic).
 #include "device_common.h"
 #include "launch.h"
 #include "plan.h"
@@ -109,52 +109,48 @@ __global__ __launch_bounds__(256) void doc_partial_kernel(const uint16_t* __rest
   }
 }
 
-// rowstat[b * RT + r] = (M, 1/Z) for row r = i*Hq + h of prompt b.  256 threads: 16 rows x 16
-// document lanes.
+// rowstat[b * RT + r] = (M, 1/Z) for row r = i*Hq + h of prompt b, with M = max_k m_k and
+// Z = sum_k e_k 2^(m_k - M).  A workgroup covers 4 rows x 64 document lanes; each lane keeps an
+// online (max, sum) over its documents, and the 64 lanes of a row are combined in a fixed order.
+constexpr int kStatRows = 4;
+constexpr int kStatLanes = 64;
 __global__ __launch_bounds__(256) void doc_rowstat_kernel(const float2* __restrict__ ml,
                                                           const int32_t* __restrict__ prompt_base,
                                                           float2* __restrict__ rowstat, int RT, int row_groups) {
-  __shared__ float red[16][17];
-  __shared__ float Ms[16];
+  __shared__ float2 red[kStatRows][kStatLanes];
   const int b = blockIdx.x / row_groups, rg = blockIdx.x % row_groups;
-  const int rl = threadIdx.x & 15, kl = threadIdx.x >> 4;
-  const int r = rg * 16 + rl;
+  const int rl = threadIdx.x % kStatRows, kl = threadIdx.x / kStatRows;
+  const int r = rg * kStatRows + rl;
   const int k0 = prompt_base[b], k1 = prompt_base[b + 1];
-  float M = -INFINITY;
+  float M = -INFINITY, Z = 0.f;
   if (r < RT)
-    for (int k = k0 + kl; k < k1; k += 16) M = fmaxf(M, ml[int64_t(k) * RT + r].x);
-  red[rl][kl] = M;
-  __syncthreads();
-  if (kl == 0) {
-    float mm = red[rl][0];
-    for (int t = 1; t < 16; ++t) mm = fmaxf(mm, red[rl][t]);
-    Ms[rl] = mm;
-  }
-  __syncthreads();
-  M = Ms[rl];
-  float Z = 0.f;
-  if (r < RT)
-    for (int k = k0 + kl; k < k1; k += 16) {
+    for (int k = k0 + kl; k < k1; k += kStatLanes) {
       const float2 v = ml[int64_t(k) * RT + r];
-      Z += v.y * fast_exp2(v.x - M);
+      const float Mn = fmaxf(M, v.x);
+      Z = Z * fast_exp2(M - Mn) + v.y * fast_exp2(v.x - Mn);
+      M = Mn;
     }
-  __syncthreads();
-  red[rl][kl] = Z;
+  red[rl][kl] = float2{M, Z};
   __syncthreads();
   if (kl == 0 && r < RT) {
-    float zz = 0.f;
-    for (int t = 0; t < 16; ++t) zz += red[rl][t];
-    rowstat[int64_t(b) * RT + r] = float2{M, 1.f / zz};
+    float Mt = -INFINITY;
+    for (int t = 0; t < kStatLanes; ++t) Mt = fmaxf(Mt, red[rl][t].x);
+    float Zt = 0.f;
+    for (int t = 0; t < kStatLanes; ++t) Zt += red[rl][t].y * fast_exp2(red[rl][t].x - Mt);
+    rowstat[int64_t(b) * RT + r] = float2{Mt, 1.f / Zt};
   }
 }
 
+// One workgroup per document k: every (signal row, head) pair contributes e_k 2^(m_k - M) / Z;
+// head_scores[h,k] sums them over signal rows and s_k averages over heads, both in a fixed order.
 __global__ __launch_bounds__(256) void doc_final_kernel(const float2* __restrict__ ml,
                                                         const float2* __restrict__ rowstat,
                                                         const int32_t* __restrict__ prompt_base,
                                                         float* __restrict__ scores, float* __restrict__ head_scores,
                                                         int num_prompts, int n_signal, int Hq, int n_docs) {
-  const int k = blockIdx.x * blockDim.x + threadIdx.x;
-  if (k >= n_docs) return;
+  __shared__ float contrib[4096];
+  __shared__ float hsum[4096];
+  const int k = blockIdx.x;
   int lo = 0, hi = num_prompts;  // prompt b with prompt_base[b] <= k < prompt_base[b+1]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -163,18 +159,23 @@ __global__ __launch_bounds__(256) void doc_final_kernel(const float2* __restrict
   const int RT = n_signal * Hq;
   const float2* mk = ml + int64_t(k) * RT;
   const float2* rs = rowstat + int64_t(lo) * RT;
-  float total = 0.f;
-  for (int h = 0; h < Hq; ++h) {
-    float hs = 0.f;
-    for (int i = 0; i < n_signal; ++i) {
-      const float2 v = mk[i * Hq + h];
-      const float2 st = rs[i * Hq + h];
-      hs += v.y * fast_exp2(v.x - st.x) * st.y;
-    }
-    if (head_scores) head_scores[int64_t(h) * n_docs + k] = hs;
-    total += hs;
+  for (int r = threadIdx.x; r < RT; r += blockDim.x) {
+    const float2 v = mk[r], st = rs[r];
+    contrib[r] = v.y * fast_exp2(v.x - st.x) * st.y;
   }
-  scores[k] = total / float(Hq);
+  __syncthreads();
+  for (int h = threadIdx.x; h < Hq; h += blockDim.x) {
+    float hs = 0.f;
+    for (int i = 0; i < n_signal; ++i) hs += contrib[i * Hq + h];
+    hsum[h] = hs;
+    if (head_scores) head_scores[int64_t(h) * n_docs + k] = hs;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float total = 0.f;
+    for (int h = 0; h < Hq; ++h) total += hsum[h];
+    scores[k] = total / float(Hq);
+  }
 }
 
 hipError_t launch_doc_scores(const ScoreLaunch& a, hipStream_t stream) {
@@ -193,13 +194,13 @@ hipError_t launch_doc_scores(const ScoreLaunch& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int RT = a.n_signal * a.num_q_heads;
-  const int row_groups = (RT + 15) / 16;
+  const int row_groups = (RT + kStatRows - 1) / kStatRows;
   float2* rowstat = a.ml + int64_t(a.n_docs) * RT;
   doc_rowstat_kernel<<<dim3(unsigned(a.num_prompts * row_groups)), 256, 0, stream>>>(a.ml, a.prompt_base, rowstat,
                                                                                       RT, row_groups);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  doc_final_kernel<<<dim3(unsigned((a.n_docs + 255) / 256)), 256, 0, stream>>>(
+  doc_final_kernel<<<dim3(unsigned(a.n_docs)), 256, 0, stream>>>(
       a.ml, rowstat, a.prompt_base, a.scores, a.head_scores, a.num_prompts, a.n_signal, a.num_q_heads, a.n_docs);
   return hipGetLastError();
 }

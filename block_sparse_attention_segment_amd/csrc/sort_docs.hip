@@ -1,11 +1,11 @@
 // Per-prompt document ranking (BlockRank summary, "Efficient Attention-Based Inference" step 3:
 // argmax / arg-top-K of the scores; blog, direct output: a sorted list).
 //
-// One workgroup per prompt.  The prompt's scores sit in LDS; document k's position in the
-// descending order is the number of documents that beat it (a larger score, or an equal score
-// and a lower index), so order[position] = k.  This is a stable descending sort by counting:
-// O(N^2 / 256) comparisons per thread, exact and deterministic, a few microseconds for the
-// N <= 1000 lists re-rankers see.  NaN scores are treated as -infinity.
+// Each workgroup loads one prompt's scores into LDS and ranks 64 of its documents: document k's
+// position in the descending order is the number of documents that beat it (a larger score, or
+// an equal score and a lower index), so order[position] = k.  This is a stable descending sort
+// by counting, exact and deterministic; four threads share each document's N comparisons.
+// NaN scores are treated as -infinity.
 #include <cmath>
 
 #include "device_common.h"
@@ -17,25 +17,35 @@ struct SortArgs {
   int32_t base[kSortPromptsPerLaunch + 1];  // score index of each prompt's first document
 };
 
+constexpr int kSortDocsPerBlock = 64;   // documents ranked per workgroup
+constexpr int kSortLanesPerDoc = 4;     // threads sharing one document's comparisons
+
+// grid.x = prompt, grid.y = block of 64 documents of that prompt.
 __global__ __launch_bounds__(256) void sort_docs_kernel(const float* __restrict__ scores,
                                                         int32_t* __restrict__ order, SortArgs args) {
   __shared__ float s[kSortMaxDocs];
   const int b = blockIdx.x;
   const int base = args.base[b], N = args.base[b + 1] - base;
+  const int k0 = blockIdx.y * kSortDocsPerBlock;
+  if (k0 >= N) return;  // uniform per workgroup
   for (int k = threadIdx.x; k < N; k += blockDim.x) {
     const float v = scores[base + k];
     s[k] = isnan(v) ? -INFINITY : v;
   }
   __syncthreads();
-  for (int k = threadIdx.x; k < N; k += blockDim.x) {
+  const int k = k0 + threadIdx.x / kSortLanesPerDoc, part = threadIdx.x % kSortLanesPerDoc;
+  int pos = 0;
+  if (k < N) {
     const float sk = s[k];
-    int pos = 0;
-    for (int j = 0; j < N; ++j) {
+    for (int j = part; j < N; j += kSortLanesPerDoc) {
       const float sj = s[j];
       pos += (sj > sk) | ((sj == sk) & (j < k));
     }
-    order[base + pos] = k;
   }
+  // the 4 lanes of a document are adjacent within one wave
+  pos += __shfl_xor(pos, 1);
+  pos += __shfl_xor(pos, 2);
+  if (k < N && part == 0) order[base + pos] = k;
 }
 
 hipError_t launch_sort_docs(const float* scores, const int32_t* prompt_base, int num_prompts, int32_t* order,
@@ -43,8 +53,11 @@ hipError_t launch_sort_docs(const float* scores, const int32_t* prompt_base, int
   for (int p0 = 0; p0 < num_prompts; p0 += kSortPromptsPerLaunch) {
     const int np = num_prompts - p0 < kSortPromptsPerLaunch ? num_prompts - p0 : kSortPromptsPerLaunch;
     SortArgs args;
+    int max_n = 1;
     for (int b = 0; b <= np; ++b) args.base[b] = prompt_base[p0 + b];
-    sort_docs_kernel<<<dim3(unsigned(np)), 256, 0, stream>>>(scores, order, args);
+    for (int b = 0; b < np; ++b) max_n = args.base[b + 1] - args.base[b] > max_n ? args.base[b + 1] - args.base[b] : max_n;
+    const dim3 grid(unsigned(np), unsigned((max_n + kSortDocsPerBlock - 1) / kSortDocsPerBlock));
+    sort_docs_kernel<<<grid, 256, 0, stream>>>(scores, order, args);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
