@@ -116,6 +116,27 @@ br_status upload(void* dst, const void* src, size_t bytes, hipStream_t stream) {
   return BR_OK;
 }
 
+// Persistent attention workgroup slots of the current device (CUs x workgroups per CU), cached
+// per device.  Host-only queries (workspace sizing, plan introspection) use kDefaultCus.
+constexpr int kDefaultCus = 256;
+hipError_t attn_workgroups(int* out) {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if (size_t(dev) >= cache.size()) cache.resize(size_t(dev) + 1, 0);
+  if (cache[size_t(dev)] == 0) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cache[size_t(dev)] = (cus > 0 ? cus : kDefaultCus) * br::kAttnWgPerCu;
+  }
+  *out = cache[size_t(dev)];
+  return hipSuccess;
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 float resolve_scale(float scale, int d) { return scale > 0.f ? scale : 1.0f / std::sqrt(float(d)); }
@@ -202,10 +223,16 @@ br_status br_attn_fwd_timed(const br_dims* dims, const void* Q, const void* K, c
       return record(BR_ERR_WORKSPACE, "workspace is NULL or smaller than br_attn_workspace_bytes() = " +
                                           std::to_string(plan.total_bytes));
     if (!aligned(workspace, 16)) return record(BR_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    // All arguments are valid: only now touch the runtime (device query for the schedule).
+    int workgroups = 0;
+    hipError_t he0 = attn_workgroups(&workgroups);
+    if (he0 != hipSuccess) return hip_fail(he0, "device query");
+    br::schedule_attn_plan(dims->num_kv_heads, workgroups, &plan);
 
-    // Host image of the plan region of the workspace: [items | merges].
+    // Host image of the plan region of the workspace: [items | ranges | merges].
     std::vector<unsigned char> host(plan.off_part_o, 0);
     std::memcpy(host.data() + plan.off_items, plan.items.data(), plan.items.size() * sizeof(br::AttnItem));
+    std::memcpy(host.data() + plan.off_ranges, plan.ranges.data(), plan.ranges.size() * sizeof(int32_t));
     if (!plan.merges.empty())
       std::memcpy(host.data() + plan.off_merges, plan.merges.data(), plan.merges.size() * sizeof(br::MergeItem));
     unsigned char* ws = static_cast<unsigned char*>(workspace);
@@ -219,11 +246,13 @@ br_status br_attn_fwd_timed(const br_dims* dims, const void* Q, const void* K, c
     a.O = static_cast<uint16_t*>(out);
     a.lse = lse;
     a.items = reinterpret_cast<const br::AttnItem*>(ws + plan.off_items);
+    a.ranges = reinterpret_cast<const int32_t*>(ws + plan.off_ranges);
     a.merges = reinterpret_cast<const br::MergeItem*>(ws + plan.off_merges);
     a.part_o = reinterpret_cast<float*>(ws + plan.off_part_o);
     a.part_ml = reinterpret_cast<float*>(ws + plan.off_part_ml);
     a.n_items = int64_t(plan.items.size());
     a.n_merges = int64_t(plan.merges.size());
+    a.wg_per_head = plan.wg_per_head;
     a.num_q_heads = dims->num_q_heads;
     a.num_kv_heads = dims->num_kv_heads;
     a.head_dim = dims->head_dim;

@@ -15,9 +15,14 @@
 //                 cross-half exchange (v_permlane32_swap);
 //   online softmax in fp32 (log2 domain, exp2), lazy rescaling of the accumulator;
 //   O^T += V^T P^T with P rounded to bf16, V staged transposed in LDS.
-// K/V tiles are double-buffered in LDS with the next tile prefetched into registers.
-// Query rows of long prompts are split over key chunks; their fp32 partials (m, l, o) are
-// combined by attn_merge_kernel with the usual log-sum-exp algebra.
+//
+// The kernel is persistent: each workgroup serves one KV head and runs a contiguous run of the
+// item list.  Tiles stream through one software pipeline across item boundaries: while a tile
+// is computed, the next tile's K/V (and, on an item's last tile, the next item's Q) is loaded
+// into registers, then written to the other LDS buffer.  Loads and stores go through buffer
+// resources sized to the valid rows, so rows past a range end read as zero and writes past a
+// tile's last token are dropped by the hardware.  Query rows of long prompts are split over key
+// chunks; their fp32 partials (m, l, o) are combined by attn_merge_kernel.
 #include "device_common.h"
 #include "launch.h"
 #include "plan.h"
@@ -32,69 +37,74 @@ template <int D, int G>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                        const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                                                        float* __restrict__ lse, const AttnItem* __restrict__ items,
-                                                       float* __restrict__ part_o, float* __restrict__ part_ml, int Hq,
-                                                       int Hkv, float scale_log2) {
+                                                       const int32_t* __restrict__ ranges, float* __restrict__ part_o,
+                                                       float* __restrict__ part_ml, int Hq, int Hkv, float scale_log2) {
   constexpr int TM = kRowsPerTile / G;  // tokens per tile
   constexpr int BN = kKeyTile;          // keys per LDS tile
+  constexpr int NKB = BN / 32;          // 32-key MFMA blocks per tile
   constexpr int KROW = D + 8;           // K row stride in LDS (elements): +16 B breaks bank aliasing
   constexpr int VROW = BN + 8;          // transposed-V row stride in LDS (elements)
+  constexpr int SWZ = BN / 8 - 1;       // XOR swizzle mask over a V row's 16-byte chunks
   constexpr int DSTEPS = D / 16;        // MFMA k-steps over the head dimension
   constexpr int DBLK = D / 32;          // 32-wide output blocks over the head dimension
   constexpr int KCH = D / 8;            // 16-byte chunks per K/V row
   constexpr int KROWS_PER_PASS = 256 / KCH;
   constexpr int KPASS = BN / KROWS_PER_PASS;
   constexpr int VGROUPS = BN / 4;       // groups of 4 keys in a V tile
+  static_assert(VGROUPS * KCH <= 256, "one (key group, head-dim chunk) per thread");
 
   __shared__ __align__(16) uint16_t sk[2][BN * KROW];
   __shared__ __align__(16) uint16_t sv[2][D * VROW];
 
   const int g = blockIdx.x % Hkv;
-  const AttnItem* itp = items + blockIdx.x / Hkv;
-  const int row0 = itp->row0, row_limit = itp->row_limit, a_start = itp->a_start, a_end = itp->a_end;
-  const int b_start = itp->b_start, b_end = itp->b_end, slot = itp->slot;
+  const int wg = blockIdx.x / Hkv;
+  const int it_begin = ranges[wg], it_end = ranges[wg + 1];
+  if (it_begin >= it_end) return;  // uniform per workgroup
+
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, half = lane >> 5;
   const int rho = w * 32 + n;  // this lane's row within the tile
   const int hh = rho / TM, tt = rho % TM;
   const int h = g * G + hh;
-  const int row_tok = row0 + tt;
-  const bool row_ok = row_tok < row_limit;
-  const int64_t q_stride = int64_t(Hq) * D, kv_stride = int64_t(Hkv) * D;
+  const int q_stride = Hq * D, kv_stride = Hkv * D;  // elements between consecutive tokens
+
+  // Per-lane byte offsets inside a row block (Q, O) or a key tile (K, V).
+  const uint32_t q_off = uint32_t((tt * q_stride + hh * D + 8 * half) * 2);
+  const int kcc = tid % KCH, kr0 = tid / KCH;          // K: 16-byte chunk and first row of this thread
+  const int vdc = tid % KCH, vkg = tid / KCH;  // V: 8-element head-dim chunk and 4-key group
+  const uint32_t k_off = uint32_t((kr0 * kv_stride + 8 * kcc) * 2);
+  const uint32_t v_off = uint32_t((4 * vkg * kv_stride + 8 * vdc) * 2);
 
   // Q fragments: B operand of S^T = K Q^T (row n, head-dim elements 16 s + 8 half .. +8).
-  u32x4_t qf[DSTEPS];
-  {
-    const uint16_t* qp = Q + int64_t(row_tok) * q_stride + int64_t(h) * D + 8 * half;
+  // Resource over a tile's valid rows of a [T, Hq, D] tensor, based at its first row and head.
+  auto row_rsrc = [&](const uint16_t* base, const AttnItem& it) {
+    const int rows = min(TM, it.row_limit - it.row0);
+    return make_rsrc(base + (int64_t(it.row0) * Hq + g * G) * D, rows * q_stride * 2);
+  };
+  auto load_q = [&](const AttnItem& it, u32x4_t* dst) {
+    const rsrc_t r = row_rsrc(Q, it);
 #pragma unroll
-    for (int s = 0; s < DSTEPS; ++s) qf[s] = row_ok ? load16(qp + 16 * s) : u32x4_t{0, 0, 0, 0};
-  }
-
-  const int nA = a_end > a_start ? (a_end - a_start + BN - 1) / BN : 0;
-  const int nB = b_end > b_start ? (b_end - b_start + BN - 1) / BN : 0;
-  const int nt = nA + nB;
+    for (int s = 0; s < DSTEPS; ++s) dst[s] = buf_load16(r, q_off + 32 * s);
+  };
 
   // ---- global -> registers -> LDS staging of one K/V tile ----
-  const int kcc = tid % KCH, kr0 = tid / KCH;  // K: 16-byte chunk and first row of this thread
-  const int vdc = tid % KCH, vkg = tid / KCH;  // V: 8-element head-dim chunk and 4-key group
   u32x4_t kreg[KPASS], vreg[4];
   auto load_tile = [&](int start, int end) {
-    const uint16_t* kb = K + int64_t(g) * D + 8 * kcc;
+    const int keys = min(BN, end - start);
+    const rsrc_t rk = make_rsrc(K + int64_t(start) * kv_stride + g * D, keys * kv_stride * 2);
+    const rsrc_t rv = make_rsrc(V + int64_t(start) * kv_stride + g * D, keys * kv_stride * 2);
 #pragma unroll
-    for (int p = 0; p < KPASS; ++p) {
-      const int j = start + kr0 + p * KROWS_PER_PASS;
-      kreg[p] = j < end ? load16(kb + int64_t(j) * kv_stride) : u32x4_t{0, 0, 0, 0};
-    }
+    for (int p = 0; p < KPASS; ++p) kreg[p] = buf_load16(rk, k_off + p * KROWS_PER_PASS * kv_stride * 2);
     if (vkg < VGROUPS) {
-      const uint16_t* vb = V + int64_t(g) * D + 8 * vdc;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int j = start + 4 * vkg + c;
-        vreg[c] = j < end ? load16(vb + int64_t(j) * kv_stride) : u32x4_t{0, 0, 0, 0};
-      }
+      for (int c = 0; c < 4; ++c) vreg[c] = buf_load16(rv, v_off + c * kv_stride * 2);
     }
   };
   // V is stored transposed (row = head-dim element, column = key).  Within each 16-key group
   // the keys are stored in the order 0-3, 8-11, 4-7, 12-15, which makes the 8 keys one lane
   // feeds to a P.V MFMA contiguous; 16-byte column chunks are XOR-swizzled by (d / 16) % 8.
+  // Sixteen adjacent threads load one key row (coalesced 256-byte reads); the transposed
+  // stores and fragment reads then see a few LDS bank conflicts, which cost less on gfx950
+  // than the extra address-unit work of a conflict-free but uncoalesced load order.
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < KPASS; ++p)
@@ -108,73 +118,79 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
         const u32x2_t even = {(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
         const u32x2_t odd = {(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
         const int d0 = 8 * vdc + 2 * u, d1 = d0 + 1;
-        *reinterpret_cast<u32x2_t*>(&sv[buf][d0 * VROW + 8 * (chunk ^ ((d0 >> 4) & 7)) + sub]) = even;
-        *reinterpret_cast<u32x2_t*>(&sv[buf][d1 * VROW + 8 * (chunk ^ ((d1 >> 4) & 7)) + sub]) = odd;
+        *reinterpret_cast<u32x2_t*>(&sv[buf][d0 * VROW + 8 * (chunk ^ ((d0 >> 4) & SWZ)) + sub]) = even;
+        *reinterpret_cast<u32x2_t*>(&sv[buf][d1 * VROW + 8 * (chunk ^ ((d1 >> 4) & SWZ)) + sub]) = odd;
       }
     }
   };
-  // Key tile i: the unmasked range's tiles come first, then the causal range's.
-  auto tile_start = [&](int i) { return i < nA ? a_start + i * BN : b_start + (i - nA) * BN; };
-  auto tile_end = [&](int i) { return i < nA ? a_end : b_end; };
+
+  // Key tile i of an item: the unmasked range's tiles come first, then the causal range's.
+  auto n_unmasked = [](const AttnItem& it) { return it.a_end > it.a_start ? (it.a_end - it.a_start + BN - 1) / BN : 0; };
+  auto n_tiles = [&](const AttnItem& it) {
+    return n_unmasked(it) + (it.b_end > it.b_start ? (it.b_end - it.b_start + BN - 1) / BN : 0);
+  };
+  auto tile_start = [&](const AttnItem& it, int nA, int i) { return i < nA ? it.a_start + i * BN : it.b_start + (i - nA) * BN; };
+  auto tile_end = [&](const AttnItem& it, int nA, int i) { return i < nA ? it.a_end : it.b_end; };
 
   f32x16_t o[DBLK];
-#pragma unroll
-  for (int b = 0; b < DBLK; ++b) o[b] = f32x16_t{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run, l_run;
+  u32x4_t qf[DSTEPS], qn[DSTEPS];
 
-  auto compute = [&](int buf, int start, int end, bool causal) {
-    // S^T for keys start .. start+63 (two 32-key blocks) against this wave's 32 rows.
-    f32x16_t s[2];
+  // One tile: S^T, mask, online softmax, O^T += V^T P^T.  `row_tok` is this lane's token.
+  auto compute = [&](int buf, int start, int end, bool causal, int row0, int row_tok, bool first) {
+    f32x16_t s[NKB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
       s[kb] = f32x16_t{};
       const uint16_t* kp = &sk[buf][(kb * 32 + n) * KROW + 8 * half];
 #pragma unroll
       for (int st = 0; st < DSTEPS; ++st) s[kb] = mfma32(load16(kp + 16 * st), qf[st], s[kb]);
     }
-    // Mask only tiles that cross the range end or the causal diagonal of some row.
-    const bool need_mask = (start + BN > end) || (causal && start + BN - 1 > row0);
-    if (need_mask) {
+    // Mask only tiles that cross the range end or the causal diagonal of some row.  Register r of
+    // block kb holds key start + 32 kb + 8 (r / 4) + 4 half + r % 4.
+    if ((start + BN > end) || (causal && start + BN - 1 > row0)) {
+      const int lim = (causal ? min(end, row_tok + 1) : end) - start - 4 * half;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = start + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool ok = j < end && (!causal || j <= row_tok);
-          s[kb][r] = ok ? s[kb][r] : -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3)) < lim ? s[kb][r] : -INFINITY;
     }
     float mt = s[0][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
     mt = max_halves(mt) * scale_log2;
-    const bool need = mt > m_run + kRescaleSlack;
-    if (__any(need)) {
-      const float m_new = need ? mt : m_run;
-      const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
-      m_run = m_new;
-      l_run *= alpha;
+    if (first) {
+      m_run = mt;  // the accumulator is still zero: nothing to rescale
+    } else {
+      const bool need = mt > m_run + kRescaleSlack;
+      if (__any(need)) {
+        const float m_new = need ? mt : m_run;
+        const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int b = 0; b < DBLK; ++b) o[b] *= alpha;
+        for (int b = 0; b < DBLK; ++b) o[b] *= alpha;
+      }
     }
     const float mu = m_run == -INFINITY ? 0.f : m_run;
-    uint32_t pk[2][8];
-    float lsum = 0.f;
+    uint32_t pk[NKB][8];
+    float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // four partial row sums shorten the add chain
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const float p0 = fast_exp2(fmaf(s[kb][r], scale_log2, -mu));
         const float p1 = fast_exp2(fmaf(s[kb][r + 1], scale_log2, -mu));
-        lsum += p0 + p1;
         pk[kb][r >> 1] = pack_bf16x2(p0, p1);
+        lsum[(r >> 1) & 3] += p0 + p1;
       }
-    l_run += lsum;
+    l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
     // O^T += V^T P^T, 16 keys per MFMA.
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const u32x4_t pv = {pk[kb][4 * m], pk[kb][4 * m + 1], pk[kb][4 * m + 2], pk[kb][4 * m + 3]};
@@ -182,63 +198,106 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
 #pragma unroll
         for (int b = 0; b < DBLK; ++b) {
           const int d = 32 * b + n;
-          const u32x4_t vf = load16(&sv[buf][d * VROW + 8 * (cpos ^ ((d >> 4) & 7))]);
+          const u32x4_t vf = load16(&sv[buf][d * VROW + 8 * (cpos ^ ((d >> 4) & SWZ))]);
           o[b] = mfma32(vf, pv, o[b]);
         }
       }
   };
 
-  load_tile(tile_start(0), tile_end(0));
+  // Pipeline prologue: the first item's Q and first tile.
+  AttnItem cur = items[it_begin];
+  load_q(cur, qf);
+  {
+    const int nA = n_unmasked(cur);
+    load_tile(tile_start(cur, nA, 0), tile_end(cur, nA, 0));
+  }
   store_tile(0);
   __syncthreads();
-  for (int i = 0; i < nt; ++i) {
-    const bool has_next = i + 1 < nt;
-    if (has_next) load_tile(tile_start(i + 1), tile_end(i + 1));
-    compute(i & 1, tile_start(i), tile_end(i), i >= nA);
-    if (has_next) store_tile((i + 1) & 1);
-    __syncthreads();
-  }
+  int buf = 0;
 
-  const float l_tot = l_run + other_half(l_run);
-  if (slot < 0) {
-    if (row_ok) {
+  for (int it = it_begin; it < it_end; ++it) {
+    const bool more = it + 1 < it_end;
+    const AttnItem nxt = items[more ? it + 1 : it];
+    const int nA = n_unmasked(cur), nt = n_tiles(cur);
+    const int nA_next = n_unmasked(nxt);
+    const int row_tok = cur.row0 + tt;
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b) o[b] = f32x16_t{};
+    m_run = -INFINITY;
+    l_run = 0.f;
+
+    for (int i = 0; i < nt; ++i) {
+      const bool last = i + 1 == nt;
+      if (!last) {
+        load_tile(tile_start(cur, nA, i + 1), tile_end(cur, nA, i + 1));
+      } else if (more) {
+        load_q(nxt, qn);
+        load_tile(tile_start(nxt, nA_next, 0), tile_end(nxt, nA_next, 0));
+      }
+      compute(buf, tile_start(cur, nA, i), tile_end(cur, nA, i), i >= nA, cur.row0, row_tok, i == 0);
+      if (!last || more) store_tile(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
+
+    // Epilogue: normalise and store this item's rows (or its split-key partials).
+    const float l_tot = l_run + other_half(l_run);
+    if (cur.slot < 0) {
       const float inv = 1.f / l_tot;
-      uint16_t* op = O + int64_t(row_tok) * q_stride + int64_t(h) * D + 4 * half;
+      const rsrc_t ro = row_rsrc(O, cur);  // rows past the tile's last token are dropped
 #pragma unroll
       for (int b = 0; b < DBLK; ++b)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const u32x2_t v = {pack_bf16x2(o[b][4 * j] * inv, o[b][4 * j + 1] * inv),
-                             pack_bf16x2(o[b][4 * j + 2] * inv, o[b][4 * j + 3] * inv)};
-          *reinterpret_cast<u32x2_t*>(op + 32 * b + 8 * j) = v;
+        for (int t = 0; t < 2; ++t) {
+          // Lane half 0 holds head-dim elements 8j..8j+3 and half 1 holds 8j+4..8j+7 of each
+          // 8-element group j; swapping one group pair across halves gives every lane 8
+          // contiguous outputs: half 0 stores group 2t, half 1 stores group 2t+1.
+          const int j0 = 2 * t, j1 = 2 * t + 1;
+          const uint32_t a0 = pack_bf16x2(o[b][4 * j0] * inv, o[b][4 * j0 + 1] * inv);
+          const uint32_t a1 = pack_bf16x2(o[b][4 * j0 + 2] * inv, o[b][4 * j0 + 3] * inv);
+          const uint32_t b0 = pack_bf16x2(o[b][4 * j1] * inv, o[b][4 * j1 + 1] * inv);
+          const uint32_t b1 = pack_bf16x2(o[b][4 * j1 + 2] * inv, o[b][4 * j1 + 3] * inv);
+          const uint32_t x0 = half ? a0 : b0, x1 = half ? a1 : b1;
+          const auto r0 = __builtin_amdgcn_permlane32_swap(x0, x0, false, false);
+          const auto r1 = __builtin_amdgcn_permlane32_swap(x1, x1, false, false);
+          const u32x4_t v = half ? u32x4_t{r0[0], r1[0], b0, b1} : u32x4_t{a0, a1, r0[1], r1[1]};
+          buf_store16(v, ro, q_off + 2 * (32 * b + 16 * t));
         }
-      if (lse && half == 0) lse[int64_t(row_tok) * Hq + h] = (m_run + __log2f(l_tot)) * kLn2;
+      if (lse && half == 0 && row_tok < cur.row_limit)
+        lse[int64_t(row_tok) * Hq + h] = (m_run + __log2f(l_tot)) * kLn2;
+    } else {
+      const int64_t sl = int64_t(cur.slot) * Hkv + g;
+      float* po = part_o + (sl * kRowsPerTile + rho) * D + 4 * half;
+#pragma unroll
+      for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<f32x4_t*>(po + 32 * b + 8 * j) =
+              f32x4_t{o[b][4 * j], o[b][4 * j + 1], o[b][4 * j + 2], o[b][4 * j + 3]};
+      if (half == 0) {
+        part_ml[(sl * kRowsPerTile + rho) * 2] = m_run;
+        part_ml[(sl * kRowsPerTile + rho) * 2 + 1] = l_tot;
+      }
     }
-  } else {
-    const int64_t sl = int64_t(slot) * Hkv + g;
-    float* po = part_o + (sl * kRowsPerTile + rho) * D + 4 * half;
+    if (more) {
 #pragma unroll
-    for (int b = 0; b < DBLK; ++b)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<f32x4_t*>(po + 32 * b + 8 * j) =
-            f32x4_t{o[b][4 * j], o[b][4 * j + 1], o[b][4 * j + 2], o[b][4 * j + 3]};
-    if (half == 0) {
-      part_ml[(sl * kRowsPerTile + rho) * 2] = m_run;
-      part_ml[(sl * kRowsPerTile + rho) * 2 + 1] = l_tot;
+      for (int s = 0; s < DSTEPS; ++s) qf[s] = qn[s];
+      cur = nxt;
     }
   }
 }
 
 // Combine split-key partials of one query tile: M = max m_c, L = sum l_c 2^(m_c - M),
-// o = sum o_c 2^(m_c - M) / L.  One thread per (row, 8 head-dim elements); a workgroup covers
-// 256 such units, so one (query tile, KV head) spreads over 128 * D / 8 / 256 workgroups.
+// o = sum o_c 2^(m_c - M) / L.  One thread per (row, 4 head-dim elements); a workgroup covers
+// 256 such units, so one (query tile, KV head) spreads over 128 * D / 4 / 256 workgroups.
+// Chunks are visited four at a time so their loads are in flight together; the order of the
+// sums is fixed, so the result is deterministic.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(uint16_t* __restrict__ O, float* __restrict__ lse,
                                                          const MergeItem* __restrict__ merges,
                                                          const float* __restrict__ part_o,
                                                          const float* __restrict__ part_ml, int Hq, int Hkv, int G) {
-  constexpr int CH = D / 8;                          // 8-element chunks per row
+  constexpr int CH = D / 4;                          // 4-element units per row
   constexpr int WG_PER_TILE = kRowsPerTile * CH / 256;
   const int tile = blockIdx.x / WG_PER_TILE, part = blockIdx.x % WG_PER_TILE;
   const int g = tile % Hkv;
@@ -250,38 +309,58 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(uint16_t* __restrict__ 
   if (tok >= mi.row_limit) return;
   const int64_t stride = int64_t(Hkv) * kRowsPerTile;  // rows between consecutive slots
   const int64_t row = (int64_t(mi.slot0) * Hkv + g) * kRowsPerTile + rho;
+  const float2* ml = reinterpret_cast<const float2*>(part_ml);
+  const int n = mi.nslots;
   float M = -INFINITY;
-  for (int c = 0; c < mi.nslots; ++c) M = fmaxf(M, part_ml[(row + c * stride) * 2]);
-  float L = 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < mi.nslots; ++c) {
-    const int64_t r = row + c * stride;
-    const float wgt = fast_exp2(part_ml[r * 2] - M);
-    L += part_ml[r * 2 + 1] * wgt;
-    const f32x4_t* po = reinterpret_cast<const f32x4_t*>(part_o + r * D + ch * 8);
-    const f32x4_t v0 = po[0], v1 = po[1];
+  int c = 0;
+  for (; c + 4 <= n; c += 4) {
+    float2 v[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[e] += wgt * v0[e];
-      acc[4 + e] += wgt * v1[e];
+    for (int u = 0; u < 4; ++u) v[u] = ml[row + (c + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) M = fmaxf(M, v[u].x);
+  }
+  for (; c < n; ++c) M = fmaxf(M, ml[row + c * stride].x);
+  float L = 0.f;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  c = 0;
+  for (; c + 4 <= n; c += 4) {
+    float2 v[4];
+    f32x4_t o[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[u] = ml[row + (c + u) * stride];
+      o[u] = *reinterpret_cast<const f32x4_t*>(part_o + (row + (c + u) * stride) * D + ch * 4);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float wgt = fast_exp2(v[u].x - M);
+      L += v[u].y * wgt;
+      acc += wgt * o[u];
     }
   }
+  for (; c < n; ++c) {
+    const float2 v = ml[row + c * stride];
+    const f32x4_t o = *reinterpret_cast<const f32x4_t*>(part_o + (row + c * stride) * D + ch * 4);
+    const float wgt = fast_exp2(v.x - M);
+    L += v.y * wgt;
+    acc += wgt * o;
+  }
   const float inv = 1.f / L;
-  const u32x4_t v = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
-                     pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
-  *reinterpret_cast<u32x4_t*>(O + (int64_t(tok) * Hq + h) * D + ch * 8) = v;
+  const u32x2_t v = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  *reinterpret_cast<u32x2_t*>(O + (int64_t(tok) * Hq + h) * D + ch * 4) = v;
   if (lse && ch == 0) lse[int64_t(tok) * Hq + h] = (M + __log2f(L)) * kLn2;
 }
 
 template <int D, int G>
 static hipError_t launch_attn_t(const AttnLaunch& a, hipStream_t stream) {
   if (a.n_items > 0) {
-    const dim3 grid(unsigned(a.n_items * a.num_kv_heads));
+    const dim3 grid(unsigned(a.wg_per_head * a.num_kv_heads));
     if (a.ev_start) {
       hipError_t e = hipEventRecord(a.ev_start, stream);
       if (e != hipSuccess) return e;
     }
-    attn_fwd_kernel<D, G><<<grid, 256, 0, stream>>>(a.Q, a.K, a.V, a.O, a.lse, a.items, a.part_o, a.part_ml,
+    attn_fwd_kernel<D, G><<<grid, 256, 0, stream>>>(a.Q, a.K, a.V, a.O, a.lse, a.items, a.ranges, a.part_o, a.part_ml,
                                                     a.num_q_heads, a.num_kv_heads, a.scale_log2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -291,7 +370,7 @@ static hipError_t launch_attn_t(const AttnLaunch& a, hipStream_t stream) {
     }
   }
   if (a.n_merges > 0) {
-    const dim3 grid(unsigned(a.n_merges * a.num_kv_heads * (kRowsPerTile * (D / 8) / 256)));
+    const dim3 grid(unsigned(a.n_merges * a.num_kv_heads * (kRowsPerTile * (D / 4) / 256)));
     attn_merge_kernel<D><<<grid, 256, 0, stream>>>(a.O, a.lse, a.merges, a.part_o, a.part_ml, a.num_q_heads,
                                                    a.num_kv_heads, G);
     return hipGetLastError();

@@ -53,4 +53,25 @@ __device__ __forceinline__ float max_halves(float v) {
 
 __device__ __forceinline__ u32x4_t load16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
+// Raw buffer resources (gfx9-family descriptor, 32-bit elements, no stride).  A buffer load whose
+// byte offset is at or beyond `bytes` returns zeros and such a store is dropped, so tile edges need
+// no branches.  `bytes` must fit in 31 bits; callers build one resource per tile or row block.
+constexpr int kBufferDword3 = 0x00020000;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferDword3);
+}
+__device__ __forceinline__ u32x4_t buf_load16(rsrc_t r, uint32_t byte_offset) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0);
+}
+__device__ __forceinline__ void buf_store16(u32x4_t v, rsrc_t r, uint32_t byte_offset) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_offset, 0, 0);
+}
+// a.x * b.x + a.y * b.y + c for two packed bf16 pairs, fp32 accumulation.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 }  // namespace br

@@ -15,10 +15,12 @@ struct AttnLaunch {
   uint16_t* O;
   float* lse;
   const AttnItem* items;    // device copy of the plan's items
+  const int32_t* ranges;    // device copy of the per-workgroup item ranges [wg_per_head + 1]
   const MergeItem* merges;  // device copy of the plan's merges
   float* part_o;
   float* part_ml;
   int64_t n_items, n_merges;
+  int wg_per_head;
   int num_q_heads, num_kv_heads, head_dim;
   float scale_log2;         // softmax scale * log2(e)
   hipEvent_t ev_start = nullptr, ev_stop = nullptr;  // optional, recorded around the main kernel

@@ -145,11 +145,36 @@ Error build_attn_plan(const br_dims& dims, const int32_t* so, const int32_t* sp,
 
   const size_t hkv = size_t(dims.num_kv_heads), d = size_t(dims.head_dim);
   P.off_items = 0;
-  P.off_merges = align_up(P.items.size() * sizeof(AttnItem), 256);
+  P.off_ranges = align_up(P.items.size() * sizeof(AttnItem), 256);
+  P.off_merges = align_up(P.off_ranges + size_t(kMaxAttnWgPerHead + 1) * sizeof(int32_t), 256);
   P.off_part_o = align_up(P.off_merges + P.merges.size() * sizeof(MergeItem), 256);
   P.off_part_ml = align_up(P.off_part_o + size_t(P.n_slots) * hkv * kRowsPerTile * d * 4, 256);
   P.total_bytes = align_up(P.off_part_ml + size_t(P.n_slots) * hkv * kRowsPerTile * 2 * 4, 256);
+  schedule_attn_plan(dims.num_kv_heads, 256 * kAttnWgPerCu, plan);
   return {};
+}
+
+void schedule_attn_plan(int num_kv_heads, int workgroups, AttnPlan* plan) {
+  AttnPlan& P = *plan;
+  // Persistent schedule: split the item list into contiguous runs of near-equal cost (key tiles
+  // plus one for the row tile's Q load and output store), one run per workgroup of a KV head.
+  // Contiguous runs keep a document's row tiles on one workgroup, which re-reads that document's
+  // keys from cache.
+  const int64_t n_items = int64_t(P.items.size());
+  P.wg_per_head = int(std::max<int64_t>(1, std::min<int64_t>({n_items, int64_t(std::max(1, workgroups)) / num_kv_heads,
+                                                                int64_t(kMaxAttnWgPerHead)})));
+  {
+    int64_t total = 0;
+    for (const AttnItem& it : P.items) total += it.ntiles + 1;
+    P.ranges.assign(size_t(P.wg_per_head) + 1, 0);
+    int64_t acc = 0, idx = 0;
+    for (int w = 1; w < P.wg_per_head; ++w) {
+      const int64_t target = total * w / P.wg_per_head;
+      while (idx < n_items && acc + (P.items[size_t(idx)].ntiles + 1) / 2 <= target) acc += P.items[size_t(idx++)].ntiles + 1;
+      P.ranges[size_t(w)] = int32_t(idx);
+    }
+    P.ranges[size_t(P.wg_per_head)] = int32_t(n_items);
+  }
 }
 
 Error validate_docs(const br_dims& dims, int32_t n_signal, const int32_t* dof, const int32_t* dp) {

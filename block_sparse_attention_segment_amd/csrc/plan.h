@@ -16,6 +16,8 @@ constexpr int kRowsPerWave = 32;                  // one 32x32 MFMA block of que
 constexpr int kWaves = 4;                         // waves per workgroup
 constexpr int kRowsPerTile = kRowsPerWave * kWaves;  // 128 (token, head) rows per work item
 constexpr int kKeyTile = 64;                      // keys staged in LDS per step
+constexpr int kAttnWgPerCu = 2;                   // persistent attention workgroups per CU
+constexpr int kMaxAttnWgPerHead = 4096;           // bound on workgroups sharing one KV head
 
 inline int tokens_per_tile(int group) { return kRowsPerTile / group; }
 
@@ -44,8 +46,11 @@ struct AttnPlan {
   std::vector<AttnItem> items;
   std::vector<MergeItem> merges;
   int32_t n_slots = 0;       // partial slots per KV head
+  // Persistent schedule: workgroup w of a KV head runs items [ranges[w], ranges[w+1]).
+  int wg_per_head = 1;
+  std::vector<int32_t> ranges;
   // workspace layout (bytes from the workspace base)
-  size_t off_items = 0, off_merges = 0, off_part_o = 0, off_part_ml = 0, total_bytes = 0;
+  size_t off_items = 0, off_ranges = 0, off_merges = 0, off_part_o = 0, off_part_ml = 0, total_bytes = 0;
 };
 
 struct ScoreItem {
@@ -76,6 +81,10 @@ Error validate_dims(const br_dims* dims);
 Error validate_segments(const br_dims& dims, const int32_t* segment_offsets, const int32_t* seg_ptr);
 Error build_attn_plan(const br_dims& dims, const int32_t* segment_offsets, const int32_t* seg_ptr,
                       AttnPlan* plan);
+// Partition the item list over the persistent workgroups of each KV head.  `workgroups` = the
+// device's persistent workgroup slots (CUs x kAttnWgPerCu); it shapes only the partition, never
+// the items or the workspace size.
+void schedule_attn_plan(int num_kv_heads, int workgroups, AttnPlan* plan);
 Error validate_docs(const br_dims& dims, int32_t n_signal, const int32_t* doc_offsets,
                     const int32_t* doc_ptr);
 Error build_score_plan(const br_dims& dims, int32_t n_signal, const int32_t* doc_offsets,
