@@ -15,6 +15,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import platform
@@ -30,6 +31,11 @@ if ROOT not in sys.path:
 METRIC = "block-sparse prefill TFLOP/s (allowed pairs) + prompts/s at N=100,500; % MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+TRAFFIC_SUMMARY = {  # rocprofv3 counter summaries of the attention kernel, per workload
+    "long": os.path.join(ROOT, "profiles", "attn_fwd_long_N500_traffic.md"),
+}
+ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_segment_amd", "csrc", "attn_fwd.hip")
 
 WORKLOAD_NAMES = {
     "tiny": "tiny: 1 head, d=64, p=32, N=4 x l=64, q=32 (L=320), |S|=4",
@@ -49,6 +55,37 @@ def pair_counts(w):
         blk += b
         exact += b - sum(n * (n - 1) // 2 for n in [p, q] + list(lens))
     return blk, exact
+
+
+def measured_traffic(config):
+    """HBM bytes per attention launch from the committed counter summary, or None when there is
+    none for this workload or the kernel source changed since the counters were taken."""
+    path = TRAFFIC_SUMMARY.get(config)
+    if not path or not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(("|", "#", "`")):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    with open(ATTN_SOURCE, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()[:16]
+    if fields.get("kernel_source_sha256_16") != digest or "bytes_per_launch" not in fields:
+        return None
+    return float(fields["bytes_per_launch"])
+
+
+ATTN_ROWS_PER_TILE = 128   # (token, head) rows of one attention work item
+ATTN_KEY_TILE = 64         # keys per LDS tile of the attention kernel
+
+
+def tile_efficiency(w, dims):
+    """(token, head, key) triples the attention kernel's MFMA tiles visit: key tiles per work item
+    (from the host plan) x rows per item x keys per tile, over all KV heads."""
+    import block_sparse_attention_segment_amd as br
+    items, _ = br.attn_plan_items(dims, w.segment_offsets, w.seg_ptr)
+    return float(items[:, 7].astype(np.int64).sum()) * ATTN_ROWS_PER_TILE * ATTN_KEY_TILE * dims.num_kv_heads
 
 
 class HipEvents:
@@ -114,6 +151,8 @@ def measure(config, seed, steps, warmup, log):
         step()
     torch.cuda.synchronize()
     log(f"[bench] {config}: {warmup} warm-up steps done")
+    # Timed region: K back-to-back steps between two events; the attention kernel's own duration
+    # per step comes from events the library records around it on the same stream.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -126,6 +165,16 @@ def measure(config, seed, steps, warmup, log):
     ms_step = e0.elapsed_time(e1) / steps
     kern = [ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(steps)]
     ev.close()
+    # Per-step latency distribution (one step at a time, each between two events).
+    lat = []
+    for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        b.synchronize()
+        lat.append(a.elapsed_time(b))
+    peak_mb = torch.cuda.max_memory_allocated() / 2**20
     log(f"[bench] {config}: {steps} timed steps, {ms_step:.4f} ms/step, attention kernel {np.mean(kern):.4f} ms")
     blk, exact = pair_counts(w)
     flop_blk = 4.0 * d * Hq * blk
@@ -134,7 +183,8 @@ def measure(config, seed, steps, warmup, log):
     bytes_alg = float(T) * (2 * Hq + 2 * Hkv) * d * 2
     return dict(w=w, ms_step=ms_step, wall_s=wall, kernel_ms=float(np.mean(kern)), kernel_ms_p50=float(np.median(kern)),
                 flop_blk=flop_blk, flop_exact=flop_exact, pairs_blk=blk, pairs_exact=exact, bytes_alg=bytes_alg,
-                kernel_s=kernel_s)
+                kernel_s=kernel_s, lat_p50=float(np.percentile(lat, 50)), lat_p95=float(np.percentile(lat, 95)),
+                peak_mb=peak_mb, visited_pairs=tile_efficiency(w, dims))
 
 
 def cpu_baseline(w, n_docs_sample, log):
@@ -180,7 +230,6 @@ def main():
     ap.add_argument("--secondary", default="worked", help="extra config timed in the same run ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-docs", type=int, default=200, help="documents in the CPU oracle's timed sample")
-    ap.add_argument("--traffic", default="", help="JSON file with measured HBM bytes per attention launch")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -210,10 +259,7 @@ def main():
     value = r["flop_blk"] / step_s / 1e12
     attn_tflops_blk = r["flop_blk"] / r["kernel_s"] / 1e12
     achieved_gbps = r["bytes_alg"] / r["kernel_s"] / 1e9
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get("bytes_per_launch")
+    traffic = measured_traffic(args.config)
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -230,6 +276,10 @@ def main():
         "config": {"workload": WORKLOAD_NAMES[args.config], "seed": args.seed, "global_batch": w.num_prompts,
                    "seq_len": w.total_tokens, "parallelism": "single-gpu"},
         "prompts_per_s": round(w.num_prompts / step_s, 2),
+        "step_ms_p50": round(r["lat_p50"], 5),
+        "step_ms_p95": round(r["lat_p95"], 5),
+        "peak_device_mb": round(r["peak_mb"], 1),
+        "tile_efficiency_exact": round(r["pairs_exact"] * w.num_q_heads / r["visited_pairs"], 4),
         "tflops_exact_pairs": round(r["flop_exact"] / step_s / 1e12, 3),
         "mfma_peak_frac_step": round(value / PEAK_BF16_TFLOPS, 4),
         "allowed_pairs": {"closed_form": r["pairs_blk"], "exact_causal": r["pairs_exact"]},
@@ -238,7 +288,8 @@ def main():
                              "mfma_peak_frac": round(attn_tflops_blk / PEAK_BF16_TFLOPS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                     "kernel": "attn_fwd_kernel", "bytes_per_launch": r["bytes_alg"]},
+                     "kernel": "attn_fwd_kernel", "bytes_per_launch": r["bytes_alg"],
+                     "traffic_gbps": None if traffic is None else round(traffic / r["kernel_s"] / 1e9, 1)},
     }
     if args.secondary and args.secondary != args.config:
         r2 = measure(args.secondary, args.seed, args.steps, args.warmup, log)

@@ -18,10 +18,16 @@
 //
 // The kernel is persistent: each workgroup serves one KV head and runs a contiguous run of the
 // item list.  Tiles stream through one software pipeline across item boundaries: while a tile
-// is computed, the next tile's K/V (and, on an item's last tile, the next item's Q) is loaded
-// into registers, then written to the other LDS buffer.  Loads and stores go through buffer
-// resources sized to the valid rows, so rows past a range end read as zero and writes past a
-// tile's last token are dropped by the hardware.  Query rows of long prompts are split over key
+// is computed, the next tile's K/V (on an item's last tile, the next item's first tile) is
+// loaded into registers, then written to the other LDS buffer; the next item's Q is loaded into
+// the fragment registers as soon as the last tile is computed.  Loads and stores go through
+// buffer resources sized to the valid rows, so rows past a range end read as zero and writes
+// past a tile's last token are dropped by the hardware.
+//
+// Outputs leave through LDS: the tile buffer the item's last tile used is free until the next
+// item's second tile, so the normalised rows are staged there as [token][G * D + 8] and written
+// out as whole runs (a token's G heads are adjacent in memory), 1 KB per wave instruction over 8
+// cache lines instead of 32 partial lines.  Query rows of long prompts are split over key
 // chunks; their fp32 partials (m, l, o) are combined by attn_merge_kernel.
 #include "device_common.h"
 #include "launch.h"
@@ -53,8 +59,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
   constexpr int VGROUPS = BN / 4;       // groups of 4 keys in a V tile
   static_assert(VGROUPS * KCH <= 256, "one (key group, head-dim chunk) per thread");
 
-  __shared__ __align__(16) uint16_t sk[2][BN * KROW];
-  __shared__ __align__(16) uint16_t sv[2][D * VROW];
+  // LDS buffer b holds K tile b (BN x KROW) followed by transposed V tile b (D x VROW).  Between
+  // an item's last tile and the next item's second tile, the buffer the last tile used is free
+  // and stages that item's outputs: [token][G * D + 8].
+  constexpr int KBUF = BN * KROW;
+  constexpr int CPR = G * D / 8;         // 16-byte chunks per staged token run (G heads)
+  constexpr int SROW = G * D + 8;        // staged run stride (elements): +16 B breaks bank aliasing
+  constexpr int QCH = TM * CPR / 256;    // staged chunks per thread
+  static_assert(TM * SROW <= KBUF + D * VROW && TM * CPR == 256 * QCH, "output staging fits a tile buffer");
+  __shared__ __align__(16) uint16_t skv[2][KBUF + D * VROW];
 
   const int g = blockIdx.x % Hkv;
   const int wg = blockIdx.x / Hkv;
@@ -108,7 +121,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < KPASS; ++p)
-      *reinterpret_cast<u32x4_t*>(&sk[buf][(kr0 + p * KROWS_PER_PASS) * KROW + 8 * kcc]) = kreg[p];
+      *reinterpret_cast<u32x4_t*>(&skv[buf][(kr0 + p * KROWS_PER_PASS) * KROW + 8 * kcc]) = kreg[p];
     if (vkg < VGROUPS) {
       const int pos = 16 * (vkg >> 2) + 8 * (vkg & 1) + 4 * ((vkg >> 1) & 1);
       const int chunk = pos >> 3, sub = pos & 7;
@@ -118,8 +131,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
         const u32x2_t even = {(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
         const u32x2_t odd = {(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
         const int d0 = 8 * vdc + 2 * u, d1 = d0 + 1;
-        *reinterpret_cast<u32x2_t*>(&sv[buf][d0 * VROW + 8 * (chunk ^ ((d0 >> 4) & SWZ)) + sub]) = even;
-        *reinterpret_cast<u32x2_t*>(&sv[buf][d1 * VROW + 8 * (chunk ^ ((d1 >> 4) & SWZ)) + sub]) = odd;
+        *reinterpret_cast<u32x2_t*>(&skv[buf][KBUF + d0 * VROW + 8 * (chunk ^ ((d0 >> 4) & SWZ)) + sub]) = even;
+        *reinterpret_cast<u32x2_t*>(&skv[buf][KBUF + d1 * VROW + 8 * (chunk ^ ((d1 >> 4) & SWZ)) + sub]) = odd;
       }
     }
   };
@@ -134,7 +147,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
 
   f32x16_t o[DBLK];
   float m_run, l_run;
-  u32x4_t qf[DSTEPS], qn[DSTEPS];
+  u32x4_t qf[DSTEPS];
 
   // One tile: S^T, mask, online softmax, O^T += V^T P^T.  `row_tok` is this lane's token.
   auto compute = [&](int buf, int start, int end, bool causal, int row0, int row_tok, bool first) {
@@ -142,7 +155,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       s[kb] = f32x16_t{};
-      const uint16_t* kp = &sk[buf][(kb * 32 + n) * KROW + 8 * half];
+      const uint16_t* kp = &skv[buf][(kb * 32 + n) * KROW + 8 * half];
 #pragma unroll
       for (int st = 0; st < DSTEPS; ++st) s[kb] = mfma32(load16(kp + 16 * st), qf[st], s[kb]);
     }
@@ -198,7 +211,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
 #pragma unroll
         for (int b = 0; b < DBLK; ++b) {
           const int d = 32 * b + n;
-          const u32x4_t vf = load16(&sv[buf][d * VROW + 8 * (cpos ^ ((d >> 4) & SWZ))]);
+          const u32x4_t vf = load16(&skv[buf][KBUF + d * VROW + 8 * (cpos ^ ((d >> 4) & SWZ))]);
           o[b] = mfma32(vf, pv, o[b]);
         }
       }
@@ -219,19 +232,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
     const bool more = it + 1 < it_end;
     const AttnItem nxt = items[more ? it + 1 : it];
     const int nA = n_unmasked(cur), nt = n_tiles(cur);
-    const int nA_next = n_unmasked(nxt);
     const int row_tok = cur.row0 + tt;
 #pragma unroll
     for (int b = 0; b < DBLK; ++b) o[b] = f32x16_t{};
     m_run = -INFINITY;
     l_run = 0.f;
 
+    // Every tile prefetches the next one: the item's next tile, or on the last tile the next
+    // item's first tile.
     for (int i = 0; i < nt; ++i) {
       const bool last = i + 1 == nt;
       if (!last) {
         load_tile(tile_start(cur, nA, i + 1), tile_end(cur, nA, i + 1));
       } else if (more) {
-        load_q(nxt, qn);
+        const int nA_next = n_unmasked(nxt);
         load_tile(tile_start(nxt, nA_next, 0), tile_end(nxt, nA_next, 0));
       }
       compute(buf, tile_start(cur, nA, i), tile_end(cur, nA, i), i >= nA, cur.row0, row_tok, i == 0);
@@ -239,19 +253,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
       __syncthreads();
       buf ^= 1;
     }
+    // The Q fragments are dead now: load the next item's Q straight into them, so the loads
+    // overlap this item's output stores (and the other workgroup on the CU).
+    if (more) load_q(nxt, qf);
 
     // Epilogue: normalise and store this item's rows (or its split-key partials).
     const float l_tot = l_run + other_half(l_run);
     if (cur.slot < 0) {
       const float inv = 1.f / l_tot;
       const rsrc_t ro = row_rsrc(O, cur);  // rows past the tile's last token are dropped
+      uint16_t* const stage = skv[buf ^ 1];  // the buffer this item's last tile used
 #pragma unroll
       for (int b = 0; b < DBLK; ++b)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           // Lane half 0 holds head-dim elements 8j..8j+3 and half 1 holds 8j+4..8j+7 of each
           // 8-element group j; swapping one group pair across halves gives every lane 8
-          // contiguous outputs: half 0 stores group 2t, half 1 stores group 2t+1.
+          // contiguous outputs: half 0 stages group 2t, half 1 stages group 2t+1.
           const int j0 = 2 * t, j1 = 2 * t + 1;
           const uint32_t a0 = pack_bf16x2(o[b][4 * j0] * inv, o[b][4 * j0 + 1] * inv);
           const uint32_t a1 = pack_bf16x2(o[b][4 * j0 + 2] * inv, o[b][4 * j0 + 3] * inv);
@@ -261,10 +279,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
           const auto r0 = __builtin_amdgcn_permlane32_swap(x0, x0, false, false);
           const auto r1 = __builtin_amdgcn_permlane32_swap(x1, x1, false, false);
           const u32x4_t v = half ? u32x4_t{r0[0], r1[0], b0, b1} : u32x4_t{a0, a1, r0[1], r1[1]};
-          buf_store16(v, ro, q_off + 2 * (32 * b + 16 * t));
+          *reinterpret_cast<u32x4_t*>(&stage[tt * SROW + hh * D + 32 * b + 16 * t + 8 * half]) = v;
         }
       if (lse && half == 0 && row_tok < cur.row_limit)
         lse[int64_t(row_tok) * Hq + h] = (m_run + __log2f(l_tot)) * kLn2;
+      __syncthreads();
+      // Coalesced stores: chunk c = tid + 256 i is 16-byte chunk c % CPR of token c / CPR, and a
+      // token's G heads are one contiguous run in memory.
+#pragma unroll
+      for (int i = 0; i < QCH; ++i) {
+        const int c = tid + 256 * i, r = c / CPR, col = c % CPR;
+        buf_store16(load16(&stage[r * SROW + 8 * col]), ro, uint32_t((r * q_stride + 8 * col) * 2));
+      }
+      __syncthreads();  // the staging buffer takes the next item's second tile
     } else {
       const int64_t sl = int64_t(cur.slot) * Hkv + g;
       float* po = part_o + (sl * kRowsPerTile + rho) * D + 4 * half;
@@ -279,11 +306,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
         part_ml[(sl * kRowsPerTile + rho) * 2 + 1] = l_tot;
       }
     }
-    if (more) {
-#pragma unroll
-      for (int s = 0; s < DSTEPS; ++s) qf[s] = qn[s];
-      cur = nxt;
-    }
+    if (more) cur = nxt;
   }
 }
 
