@@ -41,21 +41,21 @@ __global__ __launch_bounds__(256) void doc_partial_kernel(const uint16_t* __rest
   const int RT = n_signal * Hq;
   const int64_t kv_stride = int64_t(Hkv) * D;
 
-  // Head-dim order inside the MFMA contraction: lane half `half` supplies elements
-  // half*D/2 + 8*st .. +8 at step st (any order works if Q and K agree; this one makes each
-  // lane's loads one contiguous run).
+  // Head-dim order inside the MFMA contraction: at step st lane half `half` supplies elements
+  // 16*st + 8*half .. +8 (any order works if Q and K agree; in this one the two halves of a key
+  // row read one contiguous 32-byte run per step, so a load instruction touches 32 cache lines).
   u32x4_t qf[DSTEPS];
   {
-    const uint16_t* qp = Q_S + ((int64_t(it.prompt) * n_signal + i) * Hq + h) * D + half * (D / 2);
+    const uint16_t* qp = Q_S + ((int64_t(it.prompt) * n_signal + i) * Hq + h) * D + 8 * half;
 #pragma unroll
-    for (int s = 0; s < DSTEPS; ++s) qf[s] = row_ok ? load16(qp + 8 * s) : u32x4_t{0, 0, 0, 0};
+    for (int s = 0; s < DSTEPS; ++s) qf[s] = row_ok ? load16(qp + 16 * s) : u32x4_t{0, 0, 0, 0};
   }
-  const uint16_t* kbase = K + int64_t(g) * D + half * (D / 2);
+  const uint16_t* kbase = K + int64_t(g) * D + 8 * half;
   auto load_tile = [&](int t0, int end, u32x4_t* kf) {
     const int j = t0 + n;
     const uint16_t* kp = kbase + int64_t(j) * kv_stride;
 #pragma unroll
-    for (int s = 0; s < DSTEPS; ++s) kf[s] = j < end ? load16(kp + 8 * s) : u32x4_t{0, 0, 0, 0};
+    for (int s = 0; s < DSTEPS; ++s) kf[s] = j < end ? load16(kp + 16 * s) : u32x4_t{0, 0, 0, 0};
   };
 
   int d = it.d0;
