@@ -35,7 +35,16 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 TRAFFIC_SUMMARY = {  # rocprofv3 counter summaries of the attention kernel, per workload
     "long": os.path.join(ROOT, "profiles", "attn_fwd_long_N500_traffic.md"),
 }
-ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_segment_amd", "csrc", "attn_fwd.hip")
+# the attention kernel and the planner whose schedule decides which K/V reads hit L2
+ATTN_SOURCES = [os.path.join(ROOT, "block_sparse_attention_segment_amd", "csrc", f) for f in ("attn_fwd.hip", "plan.cpp")]
+
+
+def attn_source_digest():
+    h = hashlib.sha256()
+    for path in ATTN_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 WORKLOAD_NAMES = {
     "tiny": "tiny: 1 head, d=64, p=32, N=4 x l=64, q=32 (L=320), |S|=4",
@@ -59,7 +68,7 @@ def pair_counts(w):
 
 def measured_traffic(config):
     """HBM bytes per attention launch from the committed counter summary, or None when there is
-    none for this workload or the kernel source changed since the counters were taken."""
+    none for this workload or the kernel or planner source changed since the counters were taken."""
     path = TRAFFIC_SUMMARY.get(config)
     if not path or not os.path.exists(path):
         return None
@@ -69,9 +78,7 @@ def measured_traffic(config):
             if ":" in line and not line.startswith(("|", "#", "`")):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    with open(ATTN_SOURCE, "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()[:16]
-    if fields.get("kernel_source_sha256_16") != digest or "bytes_per_launch" not in fields:
+    if fields.get("kernel_source_sha256_16") != attn_source_digest() or "bytes_per_launch" not in fields:
         return None
     return float(fields["bytes_per_launch"])
 

@@ -4,11 +4,11 @@ document scores and per-prompt ranking, behind the C ABI of include/blockrank.h.
 The Python layer only marshals arguments to libblockrank.so; all computation runs in its
 hand-written HIP kernels.
 """
-from ._lib import (BlockRankError, BrDims, EXPORTED, LIB_PATH, attn_fwd, attn_plan_items,
+from ._lib import (BlockRankError, BrDims, EXPORTED, LIB_PATH, attn_fwd, attn_plan_items, attn_plan_schedule,
                    attn_workspace_bytes, doc_scores, doc_scores_workspace_bytes, load_library,
                    make_dims, sort_docs, version)
 
-__all__ = ["BlockRankError", "BrDims", "EXPORTED", "LIB_PATH", "attn_fwd", "attn_plan_items",
+__all__ = ["BlockRankError", "BrDims", "EXPORTED", "LIB_PATH", "attn_fwd", "attn_plan_items", "attn_plan_schedule",
            "attn_workspace_bytes", "doc_scores", "doc_scores_workspace_bytes", "load_library",
            "make_dims", "sort_docs", "version", "rank_prompts"]
 

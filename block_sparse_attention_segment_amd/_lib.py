@@ -19,7 +19,7 @@ BR_OK, BR_ERR_INVALID_ARG, BR_ERR_UNSUPPORTED, BR_ERR_WORKSPACE, BR_ERR_HIP = ra
 
 # Symbols the header declares; the CPU test checks the library exports each of them.
 EXPORTED = ("br_attn_workspace_bytes", "br_attn_fwd", "br_attn_fwd_timed", "br_doc_scores_workspace_bytes", "br_doc_scores",
-            "br_sort_docs", "br_attn_plan_items", "br_status_string", "br_last_error", "br_version")
+            "br_sort_docs", "br_attn_plan_items", "br_attn_plan_schedule", "br_status_string", "br_last_error", "br_version")
 
 
 class BrDims(ctypes.Structure):
@@ -63,6 +63,8 @@ def load_library() -> ctypes.CDLL:
         "br_sort_docs": [_P, _I32P, ctypes.c_int32, _P, _P],
         "br_attn_plan_items": [dims_p, _I32P, _I32P, _I32P, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64),
                                ctypes.POINTER(ctypes.c_int32)],
+        "br_attn_plan_schedule": [dims_p, _I32P, _I32P, ctypes.c_int32, _I32P, ctypes.c_int64, _I32P, ctypes.c_int64,
+                                  ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -134,6 +136,21 @@ def attn_plan_items(dims: BrDims, segment_offsets, seg_ptr) -> Tuple[np.ndarray,
     _check(lib.br_attn_plan_items(ctypes.byref(dims), _ptr_i32(so), _ptr_i32(sp), _ptr_i32(items), int(n.value),
                                   ctypes.byref(n), ctypes.byref(tm)))
     return items[:int(n.value)], int(tm.value)
+
+
+def attn_plan_schedule(dims: BrDims, segment_offsets, seg_ptr, workgroups: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Host-only: the persistent schedule for `workgroups` slots: items [n, 8] int32 in run
+    order and ranges [wg_per_head + 1] (workgroup w of a KV head runs items ranges[w]..ranges[w+1])."""
+    lib = load_library()
+    so, sp = _host_i32(segment_offsets), _host_i32(seg_ptr)
+    n, wph = ctypes.c_int64(0), ctypes.c_int32(0)
+    _check(lib.br_attn_plan_schedule(ctypes.byref(dims), _ptr_i32(so), _ptr_i32(sp), int(workgroups), None, 0, None, 0,
+                                     ctypes.byref(n), ctypes.byref(wph)))
+    items = np.zeros((max(int(n.value), 1), 8), dtype=np.int32)
+    ranges = np.zeros(int(wph.value) + 1, dtype=np.int32)
+    _check(lib.br_attn_plan_schedule(ctypes.byref(dims), _ptr_i32(so), _ptr_i32(sp), int(workgroups), _ptr_i32(items),
+                                     int(n.value), _ptr_i32(ranges), ranges.size, ctypes.byref(n), ctypes.byref(wph)))
+    return items[:int(n.value)], ranges
 
 
 def attn_fwd(Q, K, V, segment_offsets, seg_ptr, out=None, lse=None, softmax_scale: float = 0.0,

@@ -203,6 +203,29 @@ br_status br_attn_plan_items(const br_dims* dims, const int32_t* segment_offsets
   });
 }
 
+br_status br_attn_plan_schedule(const br_dims* dims, const int32_t* segment_offsets, const int32_t* seg_ptr,
+                                int32_t workgroups, int32_t* sched, int64_t capacity, int32_t* ranges,
+                                int64_t ranges_capacity, int64_t* n_items, int32_t* wg_per_head) {
+  return guarded([&]() -> br_status {
+    if (!n_items || !wg_per_head) return record(BR_ERR_INVALID_ARG, "n_items and wg_per_head must be non-NULL");
+    if (workgroups < 1) return record(BR_ERR_INVALID_ARG, "workgroups must be >= 1 (got " + std::to_string(workgroups) + ")");
+    if (capacity < 0 || ranges_capacity < 0) return record(BR_ERR_INVALID_ARG, "negative buffer capacity");
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    br::AttnPlan plan;
+    e = br::build_attn_plan(*dims, segment_offsets, seg_ptr, &plan);
+    if (!e.ok()) return record(e);
+    br::schedule_attn_plan(dims->num_kv_heads, workgroups, &plan);
+    *n_items = int64_t(plan.sched.size());
+    *wg_per_head = plan.wg_per_head;
+    if (sched && capacity >= *n_items && *n_items > 0)
+      std::memcpy(sched, plan.sched.data(), plan.sched.size() * sizeof(br::AttnItem));
+    if (ranges && ranges_capacity >= int64_t(plan.ranges.size()))
+      std::memcpy(ranges, plan.ranges.data(), plan.ranges.size() * sizeof(int32_t));
+    return BR_OK;
+  });
+}
+
 br_status br_attn_fwd_timed(const br_dims* dims, const void* Q, const void* K, const void* V,
                             const int32_t* segment_offsets, const int32_t* seg_ptr, void* out, float* lse,
                             float softmax_scale, void* workspace, size_t workspace_bytes, hipStream_t stream,
@@ -231,7 +254,7 @@ br_status br_attn_fwd_timed(const br_dims* dims, const void* Q, const void* K, c
 
     // Host image of the plan region of the workspace: [items | ranges | merges].
     std::vector<unsigned char> host(plan.off_part_o, 0);
-    std::memcpy(host.data() + plan.off_items, plan.items.data(), plan.items.size() * sizeof(br::AttnItem));
+    std::memcpy(host.data() + plan.off_items, plan.sched.data(), plan.sched.size() * sizeof(br::AttnItem));
     std::memcpy(host.data() + plan.off_ranges, plan.ranges.data(), plan.ranges.size() * sizeof(int32_t));
     if (!plan.merges.empty())
       std::memcpy(host.data() + plan.off_merges, plan.merges.data(), plan.merges.size() * sizeof(br::MergeItem));

@@ -11,6 +11,9 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <functional>
+#include <queue>
+#include <utility>
 
 namespace br {
 namespace {
@@ -136,8 +139,10 @@ Error build_attn_plan(const br_dims& dims, const int32_t* so, const int32_t* sp,
       P.n_slots += int32_t(nchunk);
     }
   }
-  // Longest items first: the query chunks, then instruction and document tiles in prompt order
-  // (the row tiles of one document stay adjacent so they share its keys in cache).
+  // Time order for the list schedule: the long query chunks first, then instruction and
+  // document row tiles in prompt order.  The row tiles of one document stay adjacent, so the
+  // schedule hands them to different workgroups at about the same time and the document's keys
+  // are fetched once and re-read from the shared L2.
   std::stable_sort(query_items.begin(), query_items.end(),
                    [](const AttnItem& x, const AttnItem& y) { return x.ntiles > y.ntiles; });
   P.items = std::move(query_items);
@@ -154,27 +159,40 @@ Error build_attn_plan(const br_dims& dims, const int32_t* so, const int32_t* sp,
   return {};
 }
 
+int64_t attn_item_cost(const AttnItem& it) {
+  // Measured on gfx950: a key tile of a split query chunk (keys streamed from memory, fp32
+  // partials) costs about 1.3 document key tiles; loading a row tile's queries and storing its
+  // outputs costs about four key tiles.
+  return it.slot < 0 ? 4 * int64_t(it.ntiles) + 16 : 5 * int64_t(it.ntiles) + 24;
+}
+
 void schedule_attn_plan(int num_kv_heads, int workgroups, AttnPlan* plan) {
   AttnPlan& P = *plan;
-  // Persistent schedule: split the item list into contiguous runs of near-equal cost (key tiles
-  // plus one for the row tile's Q load and output store), one run per workgroup of a KV head.
-  // Contiguous runs keep a document's row tiles on one workgroup, which re-reads that document's
-  // keys from cache.
+  // Greedy list schedule: walk the items in time order and give each to the workgroup of the KV
+  // head that becomes free first (ties to the lowest index), as a shared work queue would at run
+  // time, but fixed in advance so the kernel needs no atomics.  Workgroups that run at the same
+  // time therefore work on neighbouring items, and the largest imbalance is one item's cost.
   const int64_t n_items = int64_t(P.items.size());
-  P.wg_per_head = int(std::max<int64_t>(1, std::min<int64_t>({n_items, int64_t(std::max(1, workgroups)) / num_kv_heads,
-                                                                int64_t(kMaxAttnWgPerHead)})));
-  {
-    int64_t total = 0;
-    for (const AttnItem& it : P.items) total += it.ntiles + 1;
-    P.ranges.assign(size_t(P.wg_per_head) + 1, 0);
-    int64_t acc = 0, idx = 0;
-    for (int w = 1; w < P.wg_per_head; ++w) {
-      const int64_t target = total * w / P.wg_per_head;
-      while (idx < n_items && acc + (P.items[size_t(idx)].ntiles + 1) / 2 <= target) acc += P.items[size_t(idx++)].ntiles + 1;
-      P.ranges[size_t(w)] = int32_t(idx);
-    }
-    P.ranges[size_t(P.wg_per_head)] = int32_t(n_items);
+  const int W = int(std::max<int64_t>(1, std::min<int64_t>({n_items, int64_t(std::max(1, workgroups)) / num_kv_heads,
+                                                             int64_t(kMaxAttnWgPerHead)})));
+  P.wg_per_head = W;
+  std::vector<int32_t> owner(static_cast<size_t>(n_items));
+  std::vector<int32_t> count(size_t(W), 0);
+  using Slot = std::pair<int64_t, int32_t>;  // (time the workgroup becomes free, workgroup)
+  std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> free_at;
+  for (int w = 0; w < W; ++w) free_at.push({0, w});
+  for (int64_t i = 0; i < n_items; ++i) {
+    const Slot s = free_at.top();
+    free_at.pop();
+    owner[size_t(i)] = s.second;
+    ++count[size_t(s.second)];
+    free_at.push({s.first + attn_item_cost(P.items[size_t(i)]), s.second});
   }
+  P.ranges.assign(size_t(W) + 1, 0);
+  for (int w = 0; w < W; ++w) P.ranges[size_t(w) + 1] = P.ranges[size_t(w)] + count[size_t(w)];
+  std::vector<int32_t> fill(P.ranges.begin(), P.ranges.end() - 1);
+  P.sched.resize(size_t(n_items));
+  for (int64_t i = 0; i < n_items; ++i) P.sched[size_t(fill[size_t(owner[size_t(i)])]++)] = P.items[size_t(i)];
 }
 
 Error validate_docs(const br_dims& dims, int32_t n_signal, const int32_t* dof, const int32_t* dp) {

@@ -46,8 +46,10 @@ struct AttnPlan {
   std::vector<AttnItem> items;
   std::vector<MergeItem> merges;
   int32_t n_slots = 0;       // partial slots per KV head
-  // Persistent schedule: workgroup w of a KV head runs items [ranges[w], ranges[w+1]).
+  // Persistent schedule: workgroup w of a KV head runs sched[ranges[w] .. ranges[w+1]), a
+  // permutation of `items` (which stays in the planner's time order).
   int wg_per_head = 1;
+  std::vector<AttnItem> sched;
   std::vector<int32_t> ranges;
   // workspace layout (bytes from the workspace base)
   size_t off_items = 0, off_ranges = 0, off_merges = 0, off_part_o = 0, off_part_ml = 0, total_bytes = 0;
@@ -83,8 +85,10 @@ Error build_attn_plan(const br_dims& dims, const int32_t* segment_offsets, const
                       AttnPlan* plan);
 // Partition the item list over the persistent workgroups of each KV head.  `workgroups` = the
 // device's persistent workgroup slots (CUs x kAttnWgPerCu); it shapes only the partition, never
-// the items or the workspace size.
+// the items or the workspace size.  Calling it again re-partitions from `items`.
 void schedule_attn_plan(int num_kv_heads, int workgroups, AttnPlan* plan);
+// Relative cost of an item in the schedule (quarter key tiles).
+int64_t attn_item_cost(const AttnItem& it);
 Error validate_docs(const br_dims& dims, int32_t n_signal, const int32_t* doc_offsets,
                     const int32_t* doc_ptr);
 Error build_score_plan(const br_dims& dims, int32_t n_signal, const int32_t* doc_offsets,

@@ -156,6 +156,20 @@ br_status br_attn_plan_items(const br_dims* dims, const int32_t* segment_offsets
                              const int32_t* seg_ptr, int32_t* items, int64_t capacity,
                              int64_t* n_items, int32_t* rows_per_tile);
 
+/*
+ * Host-only introspection of the persistent schedule (no HIP call) that br_attn_fwd builds
+ * for a device with `workgroups` persistent workgroup slots (compute units x 2 on gfx950).
+ * Workgroup w of each KV head runs the items sched[ranges[w] .. ranges[w+1]) in that order;
+ * `sched` (8 int32 per item, as br_attn_plan_items) is a permutation of the plan's item list.
+ * Buffers: sched holds `capacity` items, ranges holds `ranges_capacity` int32; each is written
+ * only if large enough (n_items items, wg_per_head + 1 offsets), else only the counts are.
+ * *n_items and *wg_per_head receive the counts.  workgroups < 1 is BR_ERR_INVALID_ARG.
+ */
+br_status br_attn_plan_schedule(const br_dims* dims, const int32_t* segment_offsets,
+                                const int32_t* seg_ptr, int32_t workgroups, int32_t* sched,
+                                int64_t capacity, int32_t* ranges, int64_t ranges_capacity,
+                                int64_t* n_items, int32_t* wg_per_head);
+
 const char* br_status_string(br_status status);
 const char* br_last_error(void);
 const char* br_version(void);

@@ -86,6 +86,53 @@ def test_plan_visits_no_forbidden_tile_at_worked_shape():
             assert (a0, a1) == (0, 32) and b0 == offs[k] and b1 <= offs[k + 1]
 
 
+def _sched_cost(item):
+    """Schedule cost of one item in quarter key tiles (direct row tile / split query chunk)."""
+    row0, lim, a0, a1, b0, b1, slot, nt = map(int, item)
+    return 4 * nt + 16 if slot < 0 else 5 * nt + 24
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("workgroups", [1, 7, 64, 512])
+def test_schedule_is_a_balanced_permutation(seed, workgroups):
+    rng = random.Random(100 + seed)
+    prompts = random_prompts(rng, batch=rng.randint(1, 3), p_max=70, n_max=12, l_max=300, q_max=140)
+    hq, hkv = rng.choice([(4, 1), (8, 2), (32, 8)])
+    seg, sp, _, _ = workloads.segment_tables(prompts)
+    dims = br.make_dims(len(prompts), hq, hkv, 128, int(seg[-1]))
+    items, _ = br.attn_plan_items(dims, seg, sp)
+    sched, ranges = br.attn_plan_schedule(dims, seg, sp, workgroups)
+    W = len(ranges) - 1
+    assert W == max(1, min(len(items), workgroups // hkv))
+    assert ranges[0] == 0 and ranges[-1] == len(items) and (np.diff(ranges) >= 0).all()
+    # a permutation of the plan's items
+    assert sorted(map(tuple, sched.tolist())) == sorted(map(tuple, items.tolist()))
+    # greedy list schedule: two workgroups' loads differ by at most one item's cost
+    loads = [sum(_sched_cost(x) for x in sched[ranges[w]:ranges[w + 1]]) for w in range(W)]
+    assert max(loads) - min(loads) <= max(_sched_cost(x) for x in items)
+
+
+def test_schedule_rejects_bad_workgroups():
+    seg, sp, _, _ = workloads.segment_tables([(8, [16, 16], 8)])
+    dims = br.make_dims(1, 4, 1, 64, int(seg[-1]))
+    with pytest.raises(br.BlockRankError) as ei:
+        br.attn_plan_schedule(dims, seg, sp, 0)
+    assert ei.value.status == br._lib.BR_ERR_INVALID_ARG
+
+
+def test_schedule_spreads_a_document_over_workgroups():
+    # the row tiles of one document are adjacent in time order, so they start on different
+    # workgroups at about the same time (their keys are then shared in L2)
+    seg, sp, _, _ = workloads.segment_tables([(64, [200] * 500, 32)])
+    dims = br.make_dims(1, 32, 8, 128, int(seg[-1]))
+    sched, ranges = br.attn_plan_schedule(dims, seg, sp, 512)
+    owner = np.repeat(np.arange(len(ranges) - 1), np.diff(ranges))
+    doc = 250
+    lo, hi = int(seg[1 + doc]), int(seg[2 + doc])
+    mine = np.nonzero((sched[:, 0] >= lo) & (sched[:, 0] < hi))[0]
+    assert len(mine) == 7 and len(set(owner[mine].tolist())) == 7
+
+
 def _fake(n=1):
     return ctypes.c_void_p(0x10000)  # non-NULL, 16-byte aligned; never dereferenced on error paths
 
