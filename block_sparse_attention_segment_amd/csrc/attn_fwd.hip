@@ -14,7 +14,8 @@
 //                 holds one query row and 32 of the tile's keys: row max/sum need only one
 //                 cross-half exchange (v_permlane32_swap);
 //   online softmax in fp32 (log2 domain, exp2), lazy rescaling of the accumulator;
-//   O^T += V^T P^T with P rounded to bf16, V staged transposed in LDS.
+//   O^T += V^T P^T with P rounded to bf16; V is staged row-major and its transposed MFMA
+//                 fragments come from transposing LDS reads (ds_read_b64_tr_b16).
 //
 // The kernel is persistent: each workgroup serves one KV head and runs a contiguous run of the
 // item list.  Tiles stream through one software pipeline across item boundaries: while a tile
@@ -49,25 +50,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
   constexpr int BN = kKeyTile;          // keys per LDS tile
   constexpr int NKB = BN / 32;          // 32-key MFMA blocks per tile
   constexpr int KROW = D + 8;           // K row stride in LDS (elements): +16 B breaks bank aliasing
-  constexpr int VROW = BN + 8;          // transposed-V row stride in LDS (elements)
-  constexpr int SWZ = BN / 8 - 1;       // XOR swizzle mask over a V row's 16-byte chunks
+  // V row stride in LDS (elements): 4 or 12 (mod 16) 16-byte units, so the 4 rows x 4 units that
+  // one half-wave of a transposing read touches fall in 16 different bank groups.
+  constexpr int VROW = D == 128 ? 160 : 96;
+  static_assert(VROW >= D && ((VROW / 8) % 16 == 4 || (VROW / 8) % 16 == 12), "V row stride");
   constexpr int DSTEPS = D / 16;        // MFMA k-steps over the head dimension
   constexpr int DBLK = D / 32;          // 32-wide output blocks over the head dimension
   constexpr int KCH = D / 8;            // 16-byte chunks per K/V row
   constexpr int KROWS_PER_PASS = 256 / KCH;
   constexpr int KPASS = BN / KROWS_PER_PASS;
-  constexpr int VGROUPS = BN / 4;       // groups of 4 keys in a V tile
-  static_assert(VGROUPS * KCH <= 256, "one (key group, head-dim chunk) per thread");
 
-  // LDS buffer b holds K tile b (BN x KROW) followed by transposed V tile b (D x VROW).  Between
-  // an item's last tile and the next item's second tile, the buffer the last tile used is free
-  // and stages that item's outputs: [token][G * D + 8].
+  // LDS buffer b holds K tile b (BN x KROW) followed by V tile b (BN x VROW), both row-major.
+  // Between an item's last tile and the next item's second tile, the buffer the last tile used
+  // is free and stages that item's outputs: [token][G * D + 8].
   constexpr int KBUF = BN * KROW;
+  constexpr int TILE = KBUF + BN * VROW;
   constexpr int CPR = G * D / 8;         // 16-byte chunks per staged token run (G heads)
   constexpr int SROW = G * D + 8;        // staged run stride (elements): +16 B breaks bank aliasing
   constexpr int QCH = TM * CPR / 256;    // staged chunks per thread
-  static_assert(TM * SROW <= KBUF + D * VROW && TM * CPR == 256 * QCH, "output staging fits a tile buffer");
-  __shared__ __align__(16) uint16_t skv[2][KBUF + D * VROW];
+  static_assert(TM * SROW <= TILE && TM * CPR == 256 * QCH, "output staging fits a tile buffer");
+  __shared__ __align__(16) uint16_t skv[2][TILE];
 
   const int g = blockIdx.x % Hkv;
   const int wg = blockIdx.x / Hkv;
@@ -82,10 +84,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
 
   // Per-lane byte offsets inside a row block (Q, O) or a key tile (K, V).
   const uint32_t q_off = uint32_t((tt * q_stride + hh * D + 8 * half) * 2);
-  const int kcc = tid % KCH, kr0 = tid / KCH;          // K: 16-byte chunk and first row of this thread
-  const int vdc = tid % KCH, vkg = tid / KCH;  // V: 8-element head-dim chunk and 4-key group
+  const int kcc = tid % KCH, kr0 = tid / KCH;  // K and V: 16-byte chunk and first row of this thread
   const uint32_t k_off = uint32_t((kr0 * kv_stride + 8 * kcc) * 2);
-  const uint32_t v_off = uint32_t((4 * vkg * kv_stride + 8 * vdc) * 2);
+  // P.V A-operand reads (transposing, see lds_read_tr16): in each 16-lane group (s = lane % 16,
+  // head-dim half dh = (lane / 16) % 2, key half `half`) lane s points at key 4 half + s / 4 and
+  // head-dim element 16 dh + 4 (s % 4) of a block; blocks differ by compile-time offsets.
+  const int vs = lane & 15, vdh = (lane >> 4) & 1;
+  const int v_lane = KBUF + (4 * half + (vs >> 2)) * VROW + 16 * vdh + 4 * (vs & 3);
 
   // Q fragments: B operand of S^T = K Q^T (row n, head-dim elements 16 s + 8 half .. +8).
   // Resource over a tile's valid rows of a [T, Hq, D] tensor, based at its first row and head.
@@ -100,40 +105,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
   };
 
   // ---- global -> registers -> LDS staging of one K/V tile ----
-  u32x4_t kreg[KPASS], vreg[4];
+  // KCH adjacent threads load one key row of K and of V (coalesced 256-byte reads) and write it
+  // to the same row of the LDS tiles.
+  u32x4_t kreg[KPASS], vreg[KPASS];
   auto load_tile = [&](int start, int end) {
     const int keys = min(BN, end - start);
     const rsrc_t rk = make_rsrc(K + int64_t(start) * kv_stride + g * D, keys * kv_stride * 2);
     const rsrc_t rv = make_rsrc(V + int64_t(start) * kv_stride + g * D, keys * kv_stride * 2);
 #pragma unroll
-    for (int p = 0; p < KPASS; ++p) kreg[p] = buf_load16(rk, k_off + p * KROWS_PER_PASS * kv_stride * 2);
-    if (vkg < VGROUPS) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) vreg[c] = buf_load16(rv, v_off + c * kv_stride * 2);
+    for (int p = 0; p < KPASS; ++p) {
+      kreg[p] = buf_load16(rk, k_off + p * KROWS_PER_PASS * kv_stride * 2);
+      vreg[p] = buf_load16(rv, k_off + p * KROWS_PER_PASS * kv_stride * 2);
     }
   };
-  // V is stored transposed (row = head-dim element, column = key).  Within each 16-key group
-  // the keys are stored in the order 0-3, 8-11, 4-7, 12-15, which makes the 8 keys one lane
-  // feeds to a P.V MFMA contiguous; 16-byte column chunks are XOR-swizzled by (d / 16) % 8.
-  // Sixteen adjacent threads load one key row (coalesced 256-byte reads); the transposed
-  // stores and fragment reads then see a few LDS bank conflicts, which cost less on gfx950
-  // than the extra address-unit work of a conflict-free but uncoalesced load order.
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int p = 0; p < KPASS; ++p)
-      *reinterpret_cast<u32x4_t*>(&skv[buf][(kr0 + p * KROWS_PER_PASS) * KROW + 8 * kcc]) = kreg[p];
-    if (vkg < VGROUPS) {
-      const int pos = 16 * (vkg >> 2) + 8 * (vkg & 1) + 4 * ((vkg >> 1) & 1);
-      const int chunk = pos >> 3, sub = pos & 7;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t w0 = vreg[0][u], w1 = vreg[1][u], w2 = vreg[2][u], w3 = vreg[3][u];
-        const u32x2_t even = {(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
-        const u32x2_t odd = {(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
-        const int d0 = 8 * vdc + 2 * u, d1 = d0 + 1;
-        *reinterpret_cast<u32x2_t*>(&skv[buf][KBUF + d0 * VROW + 8 * (chunk ^ ((d0 >> 4) & SWZ)) + sub]) = even;
-        *reinterpret_cast<u32x2_t*>(&skv[buf][KBUF + d1 * VROW + 8 * (chunk ^ ((d1 >> 4) & SWZ)) + sub]) = odd;
-      }
+    for (int p = 0; p < KPASS; ++p) {
+      const int row = kr0 + p * KROWS_PER_PASS;
+      *reinterpret_cast<u32x4_t*>(&skv[buf][row * KROW + 8 * kcc]) = kreg[p];
+      *reinterpret_cast<u32x4_t*>(&skv[buf][KBUF + row * VROW + 8 * kcc]) = vreg[p];
     }
   };
 
@@ -201,18 +191,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
         lsum[(r >> 1) & 3] += p0 + p1;
       }
     l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
-    // O^T += V^T P^T, 16 keys per MFMA.
+    // O^T += V^T P^T, 16 keys per MFMA.  Lane half h of P holds keys 16 m + 4 h + 0..3 and
+    // 16 m + 8 + 4 h + 0..3 of block kb (the S^T accumulator order); the two transposing reads
+    // give the V^T fragment the same key order.
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const u32x4_t pv = {pk[kb][4 * m], pk[kb][4 * m + 1], pk[kb][4 * m + 2], pk[kb][4 * m + 3]};
-        const int cpos = 2 * (2 * kb + m) + half;
+        const uint16_t* vp = &skv[buf][v_lane + (32 * kb + 16 * m) * VROW];
 #pragma unroll
         for (int b = 0; b < DBLK; ++b) {
-          const int d = 32 * b + n;
-          const u32x4_t vf = load16(&skv[buf][KBUF + d * VROW + 8 * (cpos ^ ((d >> 4) & SWZ))]);
-          o[b] = mfma32(vf, pv, o[b]);
+          const u32x2_t lo = lds_read_tr16(vp + 32 * b), hi = lds_read_tr16(vp + 8 * VROW + 32 * b);
+          o[b] = mfma32(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pv, o[b]);
         }
       }
   };

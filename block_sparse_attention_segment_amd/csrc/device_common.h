@@ -53,6 +53,17 @@ __device__ __forceinline__ float max_halves(float v) {
 
 __device__ __forceinline__ u32x4_t load16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element (i % 4) of the four
+// 16-bit values at the address of lane 4 j + i / 4, as its element j (j = 0..3).  Reading a
+// row-major [key][d] tile with lane 4 j + q pointing at (key0 + j, d0 + 4 q) therefore gives
+// lane i the four keys key0..key0+3 of column d0 + i: a transposed fragment.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));  // generic -> LDS address
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
 // Raw buffer resources (gfx9-family descriptor, 32-bit elements, no stride).  A buffer load whose
 // byte offset is at or beyond `bytes` returns zeros and such a store is dropped, so tile edges need
 // no branches.  `bytes` must fit in 31 bits; callers build one resource per tile or row block.
