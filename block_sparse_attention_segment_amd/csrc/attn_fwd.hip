@@ -20,7 +20,7 @@
 // The kernel is persistent: each workgroup serves one KV head and runs a contiguous run of the
 // item list.  Tiles stream through one software pipeline across item boundaries: while a tile
 // is computed, the next tile's K/V (on an item's last tile, the next item's first tile) is
-// loaded into registers, then written to the other LDS buffer; the next item's Q is loaded into
+// loaded into registers, one load per two S^T MFMAs, then written to the other LDS buffer; the next item's Q is loaded into
 // the fragment registers as soon as the last tile is computed.  Loads and stores go through
 // buffer resources sized to the valid rows, so rows past a range end read as zero and writes
 // past a tile's last token are dropped by the hardware.
@@ -108,15 +108,33 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
   // KCH adjacent threads load one key row of K and of V (coalesced 256-byte reads) and write it
   // to the same row of the LDS tiles.
   u32x4_t kreg[KPASS], vreg[KPASS];
-  auto load_tile = [&](int start, int end) {
+  // The next tile's loads are issued one at a time among the current tile's S^T MFMAs: issued
+  // together at the top of a tile, the loads of all waves on the CU queue in the texture
+  // address unit and each wave's in-order issue stalls behind them.  `next_k`/`next_v` cover
+  // the next tile's valid keys (zero bytes when there is none, so the loads read nothing).
+  rsrc_t next_k, next_v;
+  auto plan_tile = [&](int start, int end) {
     const int keys = min(BN, end - start);
-    const rsrc_t rk = make_rsrc(K + int64_t(start) * kv_stride + g * D, keys * kv_stride * 2);
-    const rsrc_t rv = make_rsrc(V + int64_t(start) * kv_stride + g * D, keys * kv_stride * 2);
+    next_k = make_rsrc(K + int64_t(start) * kv_stride + g * D, keys * kv_stride * 2);
+    next_v = make_rsrc(V + int64_t(start) * kv_stride + g * D, keys * kv_stride * 2);
+  };
+  auto no_tile = [&]() {
+    next_k = make_rsrc(K, 0);
+    next_v = make_rsrc(V, 0);
+  };
+  constexpr int LOAD_STEPS = 2 * KPASS;
+  auto load_step = [&](int j) {
+    const int p = j >> 1;
+    const uint32_t off = k_off + p * KROWS_PER_PASS * kv_stride * 2;
+    if (j & 1)
+      vreg[p] = buf_load16(next_v, off);
+    else
+      kreg[p] = buf_load16(next_k, off);
+  };
+  auto load_tile = [&](int start, int end) {
+    plan_tile(start, end);
 #pragma unroll
-    for (int p = 0; p < KPASS; ++p) {
-      kreg[p] = buf_load16(rk, k_off + p * KROWS_PER_PASS * kv_stride * 2);
-      vreg[p] = buf_load16(rv, k_off + p * KROWS_PER_PASS * kv_stride * 2);
-    }
+    for (int j = 0; j < LOAD_STEPS; ++j) load_step(j);
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
@@ -142,12 +160,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
   // One tile: S^T, mask, online softmax, O^T += V^T P^T.  `row_tok` is this lane's token.
   auto compute = [&](int buf, int start, int end, bool causal, int row0, int row_tok, bool first) {
     f32x16_t s[NKB];
+    static_assert(NKB * DSTEPS == 2 * LOAD_STEPS, "one next-tile load per two S^T MFMAs");
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       s[kb] = f32x16_t{};
       const uint16_t* kp = &skv[buf][(kb * 32 + n) * KROW + 8 * half];
 #pragma unroll
-      for (int st = 0; st < DSTEPS; ++st) s[kb] = mfma32(load16(kp + 16 * st), qf[st], s[kb]);
+      for (int st = 0; st < DSTEPS; ++st) {
+        s[kb] = mfma32(load16(kp + 16 * st), qf[st], s[kb]);
+        if (st & 1) load_step((kb * DSTEPS + st) >> 1);
+      }
+    }
+    // Instruction order for the scheduler: (2 LDS reads, 2 MFMAs, 1 global load) repeated.
+#pragma unroll
+    for (int j = 0; j < LOAD_STEPS; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     // Mask only tiles that cross the range end or the causal diagonal of some row.  Register r of
     // block kb holds key start + 32 kb + 8 (r / 4) + 4 half + r % 4.
@@ -234,10 +263,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
     for (int i = 0; i < nt; ++i) {
       const bool last = i + 1 == nt;
       if (!last) {
-        load_tile(tile_start(cur, nA, i + 1), tile_end(cur, nA, i + 1));
+        plan_tile(tile_start(cur, nA, i + 1), tile_end(cur, nA, i + 1));
       } else if (more) {
         const int nA_next = n_unmasked(nxt);
-        load_tile(tile_start(nxt, nA_next, 0), tile_end(nxt, nA_next, 0));
+        plan_tile(tile_start(nxt, nA_next, 0), tile_end(nxt, nA_next, 0));
+      } else {
+        no_tile();
       }
       compute(buf, tile_start(cur, nA, i), tile_end(cur, nA, i), i >= nA, cur.row0, row_tok, i == 0);
       if (!last || more) store_tile(buf ^ 1);
