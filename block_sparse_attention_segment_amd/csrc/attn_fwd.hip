@@ -17,18 +17,20 @@
 //   O^T += V^T P^T with P rounded to bf16; V is staged row-major and its transposed MFMA
 //                 fragments come from transposing LDS reads (ds_read_b64_tr_b16).
 //
-// The kernel is persistent: each workgroup serves one KV head and runs a contiguous run of the
-// item list.  Tiles stream through one software pipeline across item boundaries: while a tile
-// is computed, the next tile's K/V (on an item's last tile, the next item's first tile) is
-// loaded into registers, one load per two S^T MFMAs, then written to the other LDS buffer; the next item's Q is loaded into
-// the fragment registers as soon as the last tile is computed.  Loads and stores go through
-// buffer resources sized to the valid rows, so rows past a range end read as zero and writes
-// past a tile's last token are dropped by the hardware.
+// The kernel is persistent: each workgroup serves one KV head and runs its share of the item
+// list (a host-side list schedule).  Tiles stream through one software pipeline across item
+// boundaries: while a tile is computed, the next tile's K/V (on an item's last tile, the next
+// item's first tile) is loaded into registers, one load per two S^T MFMAs, then written to the
+// other LDS buffer.  Loads and stores go through buffer resources sized to the valid rows, so
+// rows past a range end read as zero and writes past a tile's last token are dropped by the
+// hardware.
 //
-// Outputs leave through LDS: the tile buffer the item's last tile used is free until the next
-// item's second tile, so the normalised rows are staged there as [token][G * D + 8] and written
-// out as whole runs (a token's G heads are adjacent in memory), 1 KB per wave instruction over 8
-// cache lines instead of 32 partial lines.  Query rows of long prompts are split over key
+// Q and O move as whole rows (1 KB per wave instruction over 8 full cache lines, instead of
+// 32 B from each of 32 rows) and are redistributed through LDS: the tile buffer the item's
+// last tile used is free until the next item's second tile.  The next item's Q rows, loaded
+// once the last tile's S^T is formed, pass through it into MFMA fragments; then this item's
+// normalised outputs are staged there as [token][G * D + 8] (a token's G heads are adjacent in
+// memory) and written out.  Query rows of long prompts are split over key
 // chunks; their fp32 partials (m, l, o) are combined by attn_merge_kernel.
 #include "device_common.h"
 #include "launch.h"
@@ -98,10 +100,34 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
     const int rows = min(TM, it.row_limit - it.row0);
     return make_rsrc(base + (int64_t(it.row0) * Hq + g * G) * D, rows * q_stride * 2);
   };
+  u32x4_t qf[DSTEPS];
   auto load_q = [&](const AttnItem& it, u32x4_t* dst) {
     const rsrc_t r = row_rsrc(Q, it);
 #pragma unroll
     for (int s = 0; s < DSTEPS; ++s) dst[s] = buf_load16(r, q_off + 32 * s);
+  };
+  // The same rows loaded coalesced: instruction s of wave w reads QRI whole rows (1 KB, 8 full
+  // cache lines) instead of 32 B from each of 32 rows; the fragments are then redistributed
+  // through LDS ([row][QROW]).  Lane l takes chunk l % KCH of row 32 w + QRI s + l / KCH.
+  constexpr int QROW = D + 8;        // staged Q row stride (elements): same bank pattern as K
+  constexpr int QRI = 512 / D;       // rows per coalesced instruction
+  static_assert(kRowsPerTile * QROW <= TILE && QRI * DSTEPS == kRowsPerWave, "Q staging fits a tile buffer");
+  auto load_q_rows = [&](const AttnItem& it, bool valid) {
+    const rsrc_t r = valid ? row_rsrc(Q, it) : make_rsrc(Q, 0);  // zero bytes: reads nothing
+#pragma unroll
+    for (int s = 0; s < DSTEPS; ++s) {
+      const int rr = 32 * w + QRI * s + lane / KCH;
+      qf[s] = buf_load16(r, uint32_t(((rr % TM) * q_stride + (rr / TM) * D + 8 * (lane % KCH)) * 2));
+    }
+  };
+  auto stage_q_rows = [&](uint16_t* st) {
+#pragma unroll
+    for (int s = 0; s < DSTEPS; ++s)
+      *reinterpret_cast<u32x4_t*>(&st[(32 * w + QRI * s + lane / KCH) * QROW + 8 * (lane % KCH)]) = qf[s];
+  };
+  auto read_q_frags = [&](const uint16_t* st) {
+#pragma unroll
+    for (int s = 0; s < DSTEPS; ++s) qf[s] = load16(&st[rho * QROW + 16 * s + 8 * half]);
   };
 
   // ---- global -> registers -> LDS staging of one K/V tile ----
@@ -155,10 +181,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
 
   f32x16_t o[DBLK];
   float m_run, l_run;
-  u32x4_t qf[DSTEPS];
 
   // One tile: S^T, mask, online softmax, O^T += V^T P^T.  `row_tok` is this lane's token.
-  auto compute = [&](int buf, int start, int end, bool causal, int row0, int row_tok, bool first) {
+  // `after_s` runs once the S^T MFMAs have consumed the Q fragments (on an item's last tile it
+  // loads the next item's Q rows into them).
+  auto compute = [&](int buf, int start, int end, bool causal, int row0, int row_tok, bool first, auto&& after_s) {
     f32x16_t s[NKB];
     static_assert(NKB * DSTEPS == 2 * LOAD_STEPS, "one next-tile load per two S^T MFMAs");
 #pragma unroll
@@ -178,6 +205,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
+    after_s();
     // Mask only tiles that cross the range end or the causal diagonal of some row.  Register r of
     // block kb holds key start + 32 kb + 8 (r / 4) + 4 half + r % 4.
     if ((start + BN > end) || (causal && start + BN - 1 > row0)) {
@@ -259,25 +287,34 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
     l_run = 0.f;
 
     // Every tile prefetches the next one: the item's next tile, or on the last tile the next
-    // item's first tile.
-    for (int i = 0; i < nt; ++i) {
-      const bool last = i + 1 == nt;
-      if (!last) {
-        plan_tile(tile_start(cur, nA, i + 1), tile_end(cur, nA, i + 1));
-      } else if (more) {
-        const int nA_next = n_unmasked(nxt);
-        plan_tile(tile_start(nxt, nA_next, 0), tile_end(nxt, nA_next, 0));
-      } else {
-        no_tile();
-      }
-      compute(buf, tile_start(cur, nA, i), tile_end(cur, nA, i), i >= nA, cur.row0, row_tok, i == 0);
-      if (!last || more) store_tile(buf ^ 1);
+    // item's first tile.  The last tile is written out separately: it also loads the next item's
+    // Q rows, so that the compiler sees those loads on that path only.
+    for (int i = 0; i + 1 < nt; ++i) {
+      plan_tile(tile_start(cur, nA, i + 1), tile_end(cur, nA, i + 1));
+      compute(buf, tile_start(cur, nA, i), tile_end(cur, nA, i), i >= nA, cur.row0, row_tok, i == 0, [] {});
+      store_tile(buf ^ 1);
       __syncthreads();
       buf ^= 1;
     }
-    // The Q fragments are dead now: load the next item's Q straight into them, so the loads
-    // overlap this item's output stores (and the other workgroup on the CU).
-    if (more) load_q(nxt, qf);
+    if (more) {
+      const int nA_next = n_unmasked(nxt);
+      plan_tile(tile_start(nxt, nA_next, 0), tile_end(nxt, nA_next, 0));
+    } else {
+      no_tile();
+    }
+    compute(buf, tile_start(cur, nA, nt - 1), tile_end(cur, nA, nt - 1), nt - 1 >= nA, cur.row0, row_tok, nt == 1,
+            [&] { load_q_rows(nxt, more); });
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    // The buffer the last tile used is free until the next item's second tile: redistribute the
+    // next item's Q rows through it, then stage this item's outputs in it.  (Done after the
+    // last item too, on zero rows, so that every path reaches the next tile with the fragments
+    // read from LDS and the compiler adds no memory-counter waits there.)
+    stage_q_rows(skv[buf ^ 1]);
+    __syncthreads();
+    read_q_frags(skv[buf ^ 1]);
+    __syncthreads();
 
     // Epilogue: normalise and store this item's rows (or its split-key partials).
     const float l_tot = l_run + other_half(l_run);
