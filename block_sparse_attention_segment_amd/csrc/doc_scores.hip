@@ -42,27 +42,41 @@ __global__ __launch_bounds__(256) void doc_partial_kernel(const uint16_t* __rest
   const int64_t kv_stride = int64_t(Hkv) * D;
 
   // Head-dim order inside the MFMA contraction: at step st lane half `half` supplies elements
-  // 16*st + 8*half .. +8 (any order works if Q and K agree; in this one the two halves of a key
-  // row read one contiguous 32-byte run per step, so a load instruction touches 32 cache lines).
+  // 16*st + 8*half .. +8 (any order works if Q and K agree).
   u32x4_t qf[DSTEPS];
   {
     const uint16_t* qp = Q_S + ((int64_t(it.prompt) * n_signal + i) * Hq + h) * D + 8 * half;
 #pragma unroll
     for (int s = 0; s < DSTEPS; ++s) qf[s] = row_ok ? load16(qp + 16 * s) : u32x4_t{0, 0, 0, 0};
   }
-  const uint16_t* kbase = K + int64_t(g) * D + 8 * half;
-  auto load_tile = [&](int t0, int end, u32x4_t* kf) {
-    const int j = t0 + n;
-    const uint16_t* kp = kbase + int64_t(j) * kv_stride;
+  // Keys move as whole rows: instruction s of a step reads KRI key rows (1 KB, 8 full cache
+  // lines; lane l takes 16-byte chunk l % KCH of row KRI s + l / KCH) instead of 32 B from each
+  // of 32 rows.  Each wave passes its 32 rows through its own LDS region [key][D + 8] into MFMA
+  // fragments; a wave's LDS operations complete in order, so no barrier is needed.
+  constexpr int KCH = D / 8, KRI = 512 / D, KROW = D + 8;
+  static_assert(KRI * DSTEPS == 32, "one key row block per step");
+  __shared__ __align__(16) uint16_t kst_all[4][32 * KROW];
+  uint16_t* const kst = kst_all[threadIdx.x >> 6];
+  const uint16_t* const kbase = K + int64_t(g) * D;
+  auto load_rows = [&](int t0, int end, u32x4_t* kr) {
+    const rsrc_t r = make_rsrc(kbase + int64_t(t0) * kv_stride, max(0, min(32, end - t0)) * int(kv_stride) * 2);
 #pragma unroll
-    for (int s = 0; s < DSTEPS; ++s) kf[s] = j < end ? load16(kp + 16 * s) : u32x4_t{0, 0, 0, 0};
+    for (int s = 0; s < DSTEPS; ++s)
+      kr[s] = buf_load16(r, uint32_t(((KRI * s + lane / KCH) * kv_stride + 8 * (lane % KCH)) * 2));
+  };
+  auto to_frags = [&](const u32x4_t* kr, u32x4_t* kf) {
+#pragma unroll
+    for (int s = 0; s < DSTEPS; ++s)
+      *reinterpret_cast<u32x4_t*>(&kst[(KRI * s + lane / KCH) * KROW + 8 * (lane % KCH)]) = kr[s];
+#pragma unroll
+    for (int s = 0; s < DSTEPS; ++s) kf[s] = load16(&kst[n * KROW + 16 * s + 8 * half]);
   };
 
   int d = it.d0;
   int a = dof[d], e = dof[d + 1];
   int t0 = a;
-  u32x4_t kcur[DSTEPS], knext[DSTEPS];
-  load_tile(t0, e, kcur);
+  u32x4_t kcur[DSTEPS], knext[DSTEPS], kf[DSTEPS];
+  load_rows(t0, e, kcur);
   float m_run = -INFINITY, e_run = 0.f;
   while (true) {
     int nd = d, nt0 = t0 + 32, ne = e;
@@ -71,11 +85,12 @@ __global__ __launch_bounds__(256) void doc_partial_kernel(const uint16_t* __rest
       if (nd < it.d1) { nt0 = dof[nd]; ne = dof[nd + 1]; }
     }
     const bool has_next = nd < it.d1;
-    if (has_next) load_tile(nt0, ne, knext);
+    if (has_next) load_rows(nt0, ne, knext);
+    to_frags(kcur, kf);
 
     f32x16_t s = f32x16_t{};
 #pragma unroll
-    for (int st = 0; st < DSTEPS; ++st) s = mfma32(kcur[st], qf[st], s);
+    for (int st = 0; st < DSTEPS; ++st) s = mfma32(kf[st], qf[st], s);
     if (t0 + 32 > e) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
