@@ -27,10 +27,9 @@
 //
 // Q and O move as whole rows (1 KB per wave instruction over 8 full cache lines, instead of
 // 32 B from each of 32 rows) and are redistributed through LDS: the tile buffer the item's
-// last tile used is free until the next item's second tile.  The next item's Q rows, loaded
-// once the last tile's S^T is formed, pass through it into MFMA fragments; then this item's
-// normalised outputs are staged there as [token][G * D + 8] (a token's G heads are adjacent in
-// memory) and written out.  Query rows of long prompts are split over key
+// last tile used is free until the next item's second tile.  Each wave passes the next item's
+// Q rows (loaded once the last tile's S^T is formed) into MFMA fragments through its own 32
+// rows of that buffer, then this item's normalised output rows the other way.  Query rows of long prompts are split over key
 // chunks; their fp32 partials (m, l, o) are combined by attn_merge_kernel.
 #include "device_common.h"
 #include "launch.h"
@@ -64,13 +63,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
 
   // LDS buffer b holds K tile b (BN x KROW) followed by V tile b (BN x VROW), both row-major.
   // Between an item's last tile and the next item's second tile, the buffer the last tile used
-  // is free and stages that item's outputs: [token][G * D + 8].
+  // is free and redistributes Q and O rows ([row][D + 8], 32 rows per wave).
   constexpr int KBUF = BN * KROW;
   constexpr int TILE = KBUF + BN * VROW;
-  constexpr int CPR = G * D / 8;         // 16-byte chunks per staged token run (G heads)
-  constexpr int SROW = G * D + 8;        // staged run stride (elements): +16 B breaks bank aliasing
-  constexpr int QCH = TM * CPR / 256;    // staged chunks per thread
-  static_assert(TM * SROW <= TILE && TM * CPR == 256 * QCH, "output staging fits a tile buffer");
   __shared__ __align__(16) uint16_t skv[2][TILE];
 
   const int g = blockIdx.x % Hkv;
@@ -307,21 +302,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
     if (more) store_tile(buf ^ 1);
     __syncthreads();
     buf ^= 1;
-    // The buffer the last tile used is free until the next item's second tile: redistribute the
-    // next item's Q rows through it, then stage this item's outputs in it.  (Done after the
-    // last item too, on zero rows, so that every path reaches the next tile with the fragments
-    // read from LDS and the compiler adds no memory-counter waits there.)
-    stage_q_rows(skv[buf ^ 1]);
-    __syncthreads();
-    read_q_frags(skv[buf ^ 1]);
-    __syncthreads();
+    // The buffer the last tile used is free until the next item's second tile.  Each wave uses
+    // its own 32 rows of it ([row][QROW]) to redistribute the next item's Q rows and then this
+    // item's outputs; a wave's LDS operations complete in order, so only the barrier at the end
+    // of the epilogue is needed.  (Done after the last item too, on zero rows, so that every
+    // path reaches the next tile with the fragments read from LDS and the compiler adds no
+    // memory-counter waits there.)
+    uint16_t* const xbuf = skv[buf ^ 1];
+    stage_q_rows(xbuf);
+    read_q_frags(xbuf);
 
     // Epilogue: normalise and store this item's rows (or its split-key partials).
     const float l_tot = l_run + other_half(l_run);
     if (cur.slot < 0) {
       const float inv = 1.f / l_tot;
       const rsrc_t ro = row_rsrc(O, cur);  // rows past the tile's last token are dropped
-      uint16_t* const stage = skv[buf ^ 1];  // the buffer this item's last tile used
 #pragma unroll
       for (int b = 0; b < DBLK; ++b)
 #pragma unroll
@@ -338,19 +333,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
           const auto r0 = __builtin_amdgcn_permlane32_swap(x0, x0, false, false);
           const auto r1 = __builtin_amdgcn_permlane32_swap(x1, x1, false, false);
           const u32x4_t v = half ? u32x4_t{r0[0], r1[0], b0, b1} : u32x4_t{a0, a1, r0[1], r1[1]};
-          *reinterpret_cast<u32x4_t*>(&stage[tt * SROW + hh * D + 32 * b + 16 * t + 8 * half]) = v;
+          *reinterpret_cast<u32x4_t*>(&xbuf[rho * QROW + 32 * b + 16 * t + 8 * half]) = v;
         }
       if (lse && half == 0 && row_tok < cur.row_limit)
         lse[int64_t(row_tok) * Hq + h] = (m_run + __log2f(l_tot)) * kLn2;
-      __syncthreads();
-      // Coalesced stores: chunk c = tid + 256 i is 16-byte chunk c % CPR of token c / CPR, and a
-      // token's G heads are one contiguous run in memory.
+      // Whole-row stores of this wave's rows: instruction s writes QRI rows (1 KB, 8 full
+      // cache lines), lane l chunk l % KCH of row 32 w + QRI s + l / KCH.
 #pragma unroll
-      for (int i = 0; i < QCH; ++i) {
-        const int c = tid + 256 * i, r = c / CPR, col = c % CPR;
-        buf_store16(load16(&stage[r * SROW + 8 * col]), ro, uint32_t((r * q_stride + 8 * col) * 2));
+      for (int s2 = 0; s2 < DSTEPS; ++s2) {
+        const int rr = 32 * w + QRI * s2 + lane / KCH;
+        buf_store16(load16(&xbuf[rr * QROW + 8 * (lane % KCH)]), ro,
+                    uint32_t(((rr % TM) * q_stride + (rr / TM) * D + 8 * (lane % KCH)) * 2));
       }
-      __syncthreads();  // the staging buffer takes the next item's second tile
     } else {
       const int64_t sl = int64_t(cur.slot) * Hkv + g;
       float* po = part_o + (sl * kRowsPerTile + rho) * D + 4 * half;
@@ -365,6 +359,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
         part_ml[(sl * kRowsPerTile + rho) * 2 + 1] = l_tot;
       }
     }
+    __syncthreads();  // the freed buffer takes the tile after the next item's first
     if (more) cur = nxt;
   }
 }
