@@ -37,6 +37,9 @@ __global__ __launch_bounds__(256) void sort_docs_kernel(const float* __restrict_
   int pos = 0;
   if (k < N) {
     const float sk = s[k];
+    // Unrolled so that several LDS reads are in flight: the loop is otherwise bound by their
+    // latency.  The counts are integers, so the order of the additions does not matter.
+#pragma unroll 8
     for (int j = part; j < N; j += kSortLanesPerDoc) {
       const float sj = s[j];
       pos += (sj > sk) | ((sj == sk) & (j < k));
