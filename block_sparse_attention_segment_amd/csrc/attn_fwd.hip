@@ -365,10 +365,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
 }
 
 // Combine split-key partials of one query tile: M = max m_c, L = sum l_c 2^(m_c - M),
-// o = sum o_c 2^(m_c - M) / L.  One thread per (row, 4 head-dim elements); a workgroup covers
-// 256 such units, so one (query tile, KV head) spreads over 128 * D / 4 / 256 workgroups.
-// Chunks are visited four at a time so their loads are in flight together; the order of the
-// sums is fixed, so the result is deterministic.
+// o = sum o_c 2^(m_c - M) / L, accumulated in one pass with a running maximum.  One thread
+// per (row, 4 head-dim elements); a workgroup covers 256 such units, so one (query tile, KV
+// head) spreads over 128 * D / 4 / 256 workgroups.  Chunks are visited eight at a time so
+// their loads are in flight together; the order of the sums is fixed, so the result is
+// deterministic.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(uint16_t* __restrict__ O, float* __restrict__ lse,
                                                          const MergeItem* __restrict__ merges,
@@ -388,41 +389,33 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(uint16_t* __restrict__ 
   const int64_t row = (int64_t(mi.slot0) * Hkv + g) * kRowsPerTile + rho;
   const float2* ml = reinterpret_cast<const float2*>(part_ml);
   const int n = mi.nslots;
-  float M = -INFINITY;
-  int c = 0;
-  for (; c + 4 <= n; c += 4) {
-    float2 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = ml[row + (c + u) * stride];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) M = fmaxf(M, v[u].x);
-  }
-  for (; c < n; ++c) M = fmaxf(M, ml[row + c * stride].x);
-  float L = 0.f;
+  // One pass with a running maximum: chunk c scales the state by 2^(M - M') and adds its own
+  // partials with weight 2^(m_c - M').  Eight chunks' loads are issued together per round.
+  float M = -INFINITY, L = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  c = 0;
-  for (; c + 4 <= n; c += 4) {
-    float2 v[4];
-    f32x4_t o[4];
+  auto add = [&](float2 v, f32x4_t o) {
+    const float Mn = fmaxf(M, v.x);
+    if (Mn == -INFINITY) return;  // nothing seen yet
+    const float a = fast_exp2(M - Mn), wgt = fast_exp2(v.x - Mn);
+    L = L * a + v.y * wgt;
+    acc = acc * a + wgt * o;
+    M = Mn;
+  };
+  constexpr int U = 8;
+  int c = 0;
+  for (; c + U <= n; c += U) {
+    float2 v[U];
+    f32x4_t o[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       v[u] = ml[row + (c + u) * stride];
       o[u] = *reinterpret_cast<const f32x4_t*>(part_o + (row + (c + u) * stride) * D + ch * 4);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float wgt = fast_exp2(v[u].x - M);
-      L += v[u].y * wgt;
-      acc += wgt * o[u];
-    }
+    for (int u = 0; u < U; ++u) add(v[u], o[u]);
   }
-  for (; c < n; ++c) {
-    const float2 v = ml[row + c * stride];
-    const f32x4_t o = *reinterpret_cast<const f32x4_t*>(part_o + (row + c * stride) * D + ch * 4);
-    const float wgt = fast_exp2(v.x - M);
-    L += v.y * wgt;
-    acc += wgt * o;
-  }
+  for (; c < n; ++c)
+    add(ml[row + c * stride], *reinterpret_cast<const f32x4_t*>(part_o + (row + c * stride) * D + ch * 4));
   const float inv = 1.f / L;
   const u32x2_t v = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
   *reinterpret_cast<u32x2_t*>(O + (int64_t(tok) * Hq + h) * D + ch * 4) = v;
