@@ -95,21 +95,25 @@ def tile_efficiency(w, dims):
     return float(items[:, 7].astype(np.int64).sum()) * ATTN_ROWS_PER_TILE * ATTN_KEY_TILE * dims.num_kv_heads
 
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence (hip_runtime_api.h)
+
+
 class HipEvents:
     """Raw hipEvent_t handles (libamdhip64) so the library can record them on its launch stream."""
 
     def __init__(self, n):
         self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.ev = []
         for _ in range(n):
             e = ctypes.c_void_p()
-            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            # timing-only events: no system-scope fence (cache writeback) when they are recorded
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE)
             if rc != 0:
-                raise RuntimeError(f"hipEventCreate failed ({rc})")
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
             self.ev.append(e.value)
 
     def elapsed_ms(self, a, b):

@@ -1,11 +1,12 @@
 // extern "C" entry points of libblockrank (declared in include/blockrank.h).
 //
 // Each compute call: validate everything on the host, build the work plan, copy the plan into
-// the caller's workspace through a pinned staging buffer (hipMemcpyAsync on the caller's
+// the caller's workspace through a pinned staging buffer (a small copy kernel on the caller's
 // stream), then enqueue the kernels on that stream.  Nothing blocks the host except the first
 // use of a staging buffer size (pinned allocation).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <exception>
@@ -34,8 +35,11 @@ br_status hip_fail(hipError_t e, const char* what) {
   return BR_ERR_HIP;
 }
 
-// Pinned host buffers for plan uploads.  A buffer is reused once the copy that last read it has
-// completed (tracked by an event recorded after the copy on the caller's stream).
+// Pinned host buffers for plan uploads.  A buffer is reused once the copy that read it is known
+// to have completed.  Recording an event between two kernels costs the stream a few
+// microseconds, so events are batched: buffers released on a stream stay pending until
+// kEventBatch of them have accumulated (or the pool has grown large), then one event recorded
+// on that stream covers them all (the copies that read them precede it in stream order).
 class StagingPool {
  public:
   struct Lease {
@@ -45,61 +49,127 @@ class StagingPool {
 
   hipError_t acquire(size_t bytes, Lease* lease) {
     std::lock_guard<std::mutex> lock(mu_);
+    hipError_t e = retire_completed();
+    if (e != hipSuccess) return e;
     for (size_t i = 0; i < bufs_.size(); ++i) {
       Buf& b = bufs_[i];
-      if (b.busy || b.cap < bytes) continue;
-      if (b.recorded) {
-        hipError_t q = hipEventQuery(b.ev);
-        if (q == hipErrorNotReady) continue;
-        if (q != hipSuccess) return q;
-      }
-      b.busy = true;
+      if (b.state != kFree || b.cap < bytes) continue;
+      b.state = kBusy;
       *lease = Lease{int(i), b.host};
       return hipSuccess;
     }
     Buf nb;
     nb.cap = bytes < (size_t(64) << 10) ? (size_t(64) << 10) : bytes;
-    hipError_t e = hipHostMalloc(&nb.host, nb.cap, hipHostMallocDefault);
+    e = hipHostMalloc(&nb.host, nb.cap, hipHostMallocDefault);
     if (e != hipSuccess) return e;
-    e = hipEventCreateWithFlags(&nb.ev, hipEventDisableTiming);
-    if (e != hipSuccess) {
-      (void)hipHostFree(nb.host);
-      return e;
-    }
-    nb.busy = true;
+    nb.state = kBusy;
     bufs_.push_back(nb);
     *lease = Lease{int(bufs_.size() - 1), nb.host};
     return hipSuccess;
   }
 
-  // Record that the lease's contents are consumed by work already enqueued on `stream`.
+  // The lease's contents are read by work already enqueued on `stream` (if `enqueued`).
   hipError_t release(const Lease& lease, hipStream_t stream, bool enqueued) {
     std::lock_guard<std::mutex> lock(mu_);
     Buf& b = bufs_[size_t(lease.index)];
-    hipError_t e = hipSuccess;
-    if (enqueued) {
-      e = hipEventRecord(b.ev, stream);
-      b.recorded = e == hipSuccess;
+    if (!enqueued) {
+      b.state = kFree;
+      return hipSuccess;
     }
-    b.busy = false;
-    return e;
+    b.state = kPending;
+    b.stream = stream;
+    int pending = 0;
+    for (const Buf& x : bufs_) pending += x.state == kPending && x.stream == stream;
+    if (pending < kEventBatch && bufs_.size() < kMaxBufs) return hipSuccess;
+    // One event after the copies that read every pending buffer of this stream.
+    hipEvent_t ev = nullptr;
+    hipError_t e = take_event(&ev);
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(ev, stream);
+    if (e != hipSuccess) {
+      events_free_.push_back(ev);
+      return e;
+    }
+    for (size_t i = 0; i < bufs_.size(); ++i)
+      if (bufs_[i].state == kPending && bufs_[i].stream == stream) {
+        bufs_[i].state = kCovered;
+        bufs_[i].event_slot = int(inflight_.size());
+      }
+    inflight_.push_back(ev);
+    return hipSuccess;
   }
 
  private:
+  static constexpr int kEventBatch = 4;
+  static constexpr size_t kMaxBufs = 32;
+  enum State { kFree, kBusy, kPending, kCovered };
   struct Buf {
     void* host = nullptr;
     size_t cap = 0;
-    hipEvent_t ev = nullptr;
-    bool busy = false;
-    bool recorded = false;
+    State state = kFree;
+    hipStream_t stream = nullptr;
+    int event_slot = -1;  // index into inflight_ while kCovered
   };
+
+  hipError_t take_event(hipEvent_t* ev) {
+    if (!events_free_.empty()) {
+      *ev = events_free_.back();
+      events_free_.pop_back();
+      return hipSuccess;
+    }
+    // Only completion matters (the host reads nothing back): a device-scope release avoids a
+    // cache writeback when the event is recorded.
+    return hipEventCreateWithFlags(ev, hipEventDisableTiming | hipEventReleaseToDevice);
+  }
+
+  // Free the buffers whose covering event has completed; recycle those events.
+  hipError_t retire_completed() {
+    std::vector<hipEvent_t> keep;
+    std::vector<int> remap(inflight_.size(), -1);
+    for (size_t k = 0; k < inflight_.size(); ++k) {
+      const hipError_t q = hipEventQuery(inflight_[k]);
+      if (q == hipSuccess) {
+        events_free_.push_back(inflight_[k]);
+      } else if (q == hipErrorNotReady) {
+        remap[k] = int(keep.size());
+        keep.push_back(inflight_[k]);
+      } else {
+        return q;
+      }
+    }
+    for (Buf& b : bufs_) {
+      if (b.state != kCovered) continue;
+      const int slot = remap[size_t(b.event_slot)];
+      if (slot < 0) {
+        b.state = kFree;
+        b.event_slot = -1;
+      } else {
+        b.event_slot = slot;
+      }
+    }
+    inflight_.swap(keep);
+    return hipSuccess;
+  }
+
   std::mutex mu_;
-  std::vector<Buf> bufs_;  // kept for the life of the process
+  std::vector<Buf> bufs_;                 // kept for the life of the process
+  std::vector<hipEvent_t> inflight_;      // recorded, not yet known complete
+  std::vector<hipEvent_t> events_free_;   // completed, reusable
 };
 
 StagingPool& staging() {
   static StagingPool* pool = new StagingPool();  // intentionally never destroyed
   return *pool;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Plan copy on the compute queue: the kernel reads the pinned staging buffer over PCIe.  A
+// host-to-device hipMemcpyAsync of the same bytes runs on a DMA engine and costs a
+// cross-engine synchronisation (tens of microseconds) before the kernel that reads the plan.
+__global__ __launch_bounds__(256) void plan_copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                        size_t n16) {
+  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += size_t(gridDim.x) * 256) dst[i] = src[i];
 }
 
 // Copy `bytes` from `src` (host) into device memory `dst` on `stream` via pinned staging.
@@ -109,9 +179,17 @@ br_status upload(void* dst, const void* src, size_t bytes, hipStream_t stream) {
   hipError_t e = staging().acquire(bytes, &lease);
   if (e != hipSuccess) return hip_fail(e, "pinned staging allocation");
   std::memcpy(lease.ptr, src, bytes);
-  e = hipMemcpyAsync(dst, lease.ptr, bytes, hipMemcpyHostToDevice, stream);
+  void* dsrc = nullptr;
+  if (bytes % 16 == 0 && aligned(dst, 16) && hipHostGetDevicePointer(&dsrc, lease.ptr, 0) == hipSuccess) {
+    const size_t n16 = bytes / 16;
+    const unsigned blocks = unsigned(std::min<size_t>(64, (n16 + 255) / 256));
+    plan_copy_kernel<<<blocks, 256, 0, stream>>>(static_cast<const uint4*>(dsrc), static_cast<uint4*>(dst), n16);
+    e = hipGetLastError();
+  } else {
+    e = hipMemcpyAsync(dst, lease.ptr, bytes, hipMemcpyHostToDevice, stream);
+  }
   hipError_t r = staging().release(lease, stream, e == hipSuccess);
-  if (e != hipSuccess) return hip_fail(e, "plan upload (hipMemcpyAsync)");
+  if (e != hipSuccess) return hip_fail(e, "plan upload");
   if (r != hipSuccess) return hip_fail(r, "plan upload (hipEventRecord)");
   return BR_OK;
 }
@@ -137,7 +215,6 @@ hipError_t attn_workgroups(int* out) {
   return hipSuccess;
 }
 
-bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 float resolve_scale(float scale, int d) { return scale > 0.f ? scale : 1.0f / std::sqrt(float(d)); }
 
