@@ -18,6 +18,17 @@
 #include "launch.h"
 #include "plan.h"
 
+namespace br {
+// Plan copy on the compute queue: the kernel reads the pinned staging buffer over PCIe.  A
+// host-to-device hipMemcpyAsync of the same bytes runs on a DMA engine and costs a
+// cross-engine synchronisation (tens of microseconds) before the kernel that reads the plan.
+__global__ __launch_bounds__(256) void plan_copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                        size_t n16) {
+  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += size_t(gridDim.x) * 256) dst[i] = src[i];
+}
+
+}  // namespace br
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -164,14 +175,6 @@ StagingPool& staging() {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Plan copy on the compute queue: the kernel reads the pinned staging buffer over PCIe.  A
-// host-to-device hipMemcpyAsync of the same bytes runs on a DMA engine and costs a
-// cross-engine synchronisation (tens of microseconds) before the kernel that reads the plan.
-__global__ __launch_bounds__(256) void plan_copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
-                                                        size_t n16) {
-  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += size_t(gridDim.x) * 256) dst[i] = src[i];
-}
-
 // Copy `bytes` from `src` (host) into device memory `dst` on `stream` via pinned staging.
 br_status upload(void* dst, const void* src, size_t bytes, hipStream_t stream) {
   if (bytes == 0) return BR_OK;
@@ -183,7 +186,7 @@ br_status upload(void* dst, const void* src, size_t bytes, hipStream_t stream) {
   if (bytes % 16 == 0 && aligned(dst, 16) && hipHostGetDevicePointer(&dsrc, lease.ptr, 0) == hipSuccess) {
     const size_t n16 = bytes / 16;
     const unsigned blocks = unsigned(std::min<size_t>(64, (n16 + 255) / 256));
-    plan_copy_kernel<<<blocks, 256, 0, stream>>>(static_cast<const uint4*>(dsrc), static_cast<uint4*>(dst), n16);
+    br::plan_copy_kernel<<<blocks, 256, 0, stream>>>(static_cast<const uint4*>(dsrc), static_cast<uint4*>(dst), n16);
     e = hipGetLastError();
   } else {
     e = hipMemcpyAsync(dst, lease.ptr, bytes, hipMemcpyHostToDevice, stream);
