@@ -30,6 +30,10 @@ Readings taken where the pages are silent or disagree (each also listed in the d
     per-head sums.  Sum, not mean, over signal tokens ([BR] "sum is used in practice").
   * Prompts in one call are independent: no attention across prompts, one sort per prompt.
   * Rank: descending score, ties to the lower document index.
+  * Query-only attention over a cached corpus ([BS] 3.2, "prefill once, score many queries"):
+    each query reads the whole corpus unmasked and its own tokens causally, never another
+    query's tokens; the corpus is whatever precedes the queries (for BlockRank, the
+    instruction and the documents).
 """
 from __future__ import annotations
 
@@ -211,6 +215,33 @@ def attn_rows(Q, K, V, segment_offsets, seg_ptr, rows=None, scale: Optional[floa
             for h in range(Hq):
                 g = kv_head(h, Hq, Hkv)
                 O[sel, h], lse[sel, h] = _masked_softmax_av(qr[:, h], Kf[cols, g], Vf[cols, g], mc, sc)
+    return O, lse
+
+
+def query_attn(Q, K, V, corpus_len: int, query_offsets, scale: Optional[float] = None):
+    """Query-only attention over a cached corpus ([BS] section 3.2: the query block attends over
+    the whole corpus and causally to itself; the corpus keys/values are computed once and reused).
+
+    K, V [T, Hkv, d]: the corpus [0, corpus_len) followed by the queries' own tokens; query b owns
+    tokens [query_offsets[b], query_offsets[b+1]).  Q [T - corpus_len, Hq, d] holds the query rows
+    only.  Row i of query b reads key j iff j < corpus_len or query_offsets[b] <= j <= i.
+    Returns (O [T - corpus_len, Hq, d], lse [T - corpus_len, Hq]) in float64.
+    """
+    Qf, Kf, Vf = to_f64(Q), to_f64(K), to_f64(V)
+    Hq, d = Qf.shape[1], Qf.shape[2]
+    Hkv = Kf.shape[1]
+    sc = _scale(d, scale)
+    qo = [int(x) for x in query_offsets]
+    O = np.zeros(Qf.shape); lse = np.zeros(Qf.shape[:2])
+    for b in range(len(qo) - 1):
+        qs, qe = qo[b], qo[b + 1]
+        rows = np.arange(qs, qe)
+        keys = np.concatenate([np.arange(0, corpus_len), np.arange(qs, qe)])
+        mask = (keys[None, :] < corpus_len) | ((keys[None, :] >= qs) & (keys[None, :] <= rows[:, None]))
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            O[qs - corpus_len:qe - corpus_len, h], lse[qs - corpus_len:qe - corpus_len, h] = _masked_softmax_av(
+                Qf[qs - corpus_len:qe - corpus_len, h], Kf[keys, g], Vf[keys, g], mask, sc)
     return O, lse
 
 

@@ -337,8 +337,74 @@ def pin_rank_bruteforce(orc):
             base += n
 
 
+# --------------------------------------------------------------------------------------
+# query-only attention over a cached corpus (BlockSearch section 3.2)
+# --------------------------------------------------------------------------------------
+def _query_case(seed, corpus, qlens, hq=4, hkv=2, d=8):
+    rng = np.random.default_rng(seed)
+    T = corpus + sum(qlens)
+    bf = lambda a: workloads.f32_to_bf16_bits(a.astype(np.float32))
+    K = bf(rng.standard_normal((T, hkv, d))); V = bf(rng.standard_normal((T, hkv, d)))
+    Q = bf(rng.standard_normal((T - corpus, hq, d)))
+    qo = np.cumsum([corpus] + list(qlens))
+    return Q, K, V, qo
+
+
+def pin_query_attn_no_corpus(orc):
+    """corpus_len = 0: every query is plain causal attention over its own tokens (torch SDPA)."""
+    Q, K, V, qo = _query_case(5, 0, [7, 1, 12, 5])
+    O, _ = orc.query_attn(Q, K, V, 0, qo)
+    for b in range(len(qo) - 1):
+        a, e = int(qo[b]), int(qo[b + 1])
+        want = _sdpa_causal(_f64(Q)[a:e], _f64(K)[a:e], _f64(V)[a:e])
+        np.testing.assert_allclose(O[a:e], want, rtol=0, atol=1e-10)
+
+
+def pin_query_attn_is_prompt_query_rows(orc):
+    """A BlockRank prompt's final-query rows are query-only attention over the corpus made of its
+    instruction and documents: compare with the rows of causal attention over the whole prompt
+    (torch SDPA) and with the prompt oracle's own query rows."""
+    for seed in range(3):
+        w = small_case(300 + seed, hq=4, hkv=2, d=8, batch=1)
+        offs = [int(x) for x in w.segment_offsets]
+        qs, qe = offs[-2], offs[-1]
+        Qf, Kf, Vf = _f64(w.Q), _f64(w.K), _f64(w.V)
+        O, lse = orc.query_attn(w.Q[qs:qe], w.K[:qe], w.V[:qe], qs, [qs, qe])
+        full = _sdpa_causal(Qf[:qe], Kf[:qe], Vf[:qe])
+        np.testing.assert_allclose(O, full[qs:qe], rtol=0, atol=1e-10)
+        O2, lse2 = orc.attn_rows(w.Q, w.K, w.V, w.segment_offsets, w.seg_ptr, rows=np.arange(qs, qe))
+        np.testing.assert_allclose(O, O2, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, lse2, rtol=0, atol=1e-12)
+
+
+def pin_query_attn_isolation(orc):
+    """A query reads the corpus and nothing of the other queries; brute force per row."""
+    corpus, qlens = 9, [4, 6, 3]
+    Q, K, V, qo = _query_case(11, corpus, qlens, hq=2, hkv=1, d=4)
+    O, _ = orc.query_attn(Q, K, V, corpus, qo)
+    Qf, Kf, Vf = _f64(Q), _f64(K), _f64(V)
+    sc = 1.0 / math.sqrt(4)
+    for b in range(len(qlens)):
+        for i in range(int(qo[b]), int(qo[b + 1])):
+            keys = list(range(corpus)) + list(range(int(qo[b]), i + 1))
+            for h in range(2):
+                z = [sum(Qf[i - corpus, h, t] * Kf[j, 0, t] for t in range(4)) * sc for j in keys]
+                m = max(z); e = [math.exp(v - m) for v in z]; s_ = sum(e)
+                want = [sum(e[n] * Vf[j, 0, t] for n, j in enumerate(keys)) / s_ for t in range(4)]
+                np.testing.assert_allclose(O[i - corpus, h], want, rtol=0, atol=1e-12)
+    # changing query 1's keys/values leaves queries 0 and 2 unchanged
+    K2, V2 = K.copy(), V.copy()
+    K2[qo[1]:qo[2]] ^= np.uint16(0x0040); V2[qo[1]:qo[2]] ^= np.uint16(0x0040)
+    O2, _ = orc.query_attn(Q, K2, V2, corpus, qo)
+    for b in (0, 2):
+        a, e = int(qo[b]) - corpus, int(qo[b + 1]) - corpus
+        np.testing.assert_array_equal(O[a:e], O2[a:e])
+    assert not np.allclose(O[qo[1] - corpus:qo[2] - corpus], O2[qo[1] - corpus:qo[2] - corpus])
+
+
 ALL_PINS = [
     pin_closed_form_counts, pin_worked_example, pin_textbook_rows, pin_textbook_rows_no_prefix,
     pin_bruteforce_chunked, pin_special_rows, pin_document_isolation, pin_readout_bruteforce,
     pin_readout_mass, pin_readout_uniform, pin_readout_permutation, pin_rank_bruteforce,
+    pin_query_attn_no_corpus, pin_query_attn_is_prompt_query_rows, pin_query_attn_isolation,
 ]

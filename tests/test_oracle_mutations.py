@@ -138,6 +138,53 @@ def _rank_ascending(scores, doc_ptr):
 _ORIG_SOFTMAX = orc._masked_softmax_av
 _ORIG_SCORES = orc.doc_scores
 
+def _query_no_causal(Q, K, V, corpus_len, query_offsets, scale=None):
+    """query rows read all of their own query's tokens"""
+    Qf, Kf, Vf = orc.to_f64(Q), orc.to_f64(K), orc.to_f64(V)
+    Hq, d = Qf.shape[1], Qf.shape[2]
+    sc = orc._scale(d, scale)
+    O = np.zeros(Qf.shape); lse = np.zeros(Qf.shape[:2])
+    qo = [int(x) for x in query_offsets]
+    for b in range(len(qo) - 1):
+        qs, qe = qo[b], qo[b + 1]
+        keys = np.r_[0:corpus_len, qs:qe]
+        mask = np.ones((qe - qs, len(keys)), dtype=bool)
+        for h in range(Hq):
+            g = orc.kv_head(h, Hq, Kf.shape[1])
+            O[qs - corpus_len:qe - corpus_len, h], lse[qs - corpus_len:qe - corpus_len, h] = orc._masked_softmax_av(
+                Qf[qs - corpus_len:qe - corpus_len, h], Kf[keys, g], Vf[keys, g], mask, sc)
+    return O, lse
+
+
+def _query_reads_previous_queries(Q, K, V, corpus_len, query_offsets, scale=None):
+    """query rows also read earlier queries' tokens (the corpus grows with each query)"""
+    qo = [int(x) for x in query_offsets]
+    O = np.zeros(np.asarray(Q).shape, dtype=np.float64); lse = np.zeros(np.asarray(Q).shape[:2])
+    for b in range(len(qo) - 1):
+        a, e = qo[b], qo[b + 1]
+        o, l = _real_query_attn(np.asarray(Q)[a - corpus_len:e - corpus_len], np.asarray(K)[:e], np.asarray(V)[:e],
+                                a, [a, e], scale)
+        O[a - corpus_len:e - corpus_len] = o
+        lse[a - corpus_len:e - corpus_len] = l
+    return O, lse
+
+
+def _query_skips_corpus(Q, K, V, corpus_len, query_offsets, scale=None):
+    """query rows read only their own tokens"""
+    qo = [int(x) for x in query_offsets]
+    O = np.zeros(np.asarray(Q).shape, dtype=np.float64); lse = np.zeros(np.asarray(Q).shape[:2])
+    for b in range(len(qo) - 1):
+        a, e = qo[b], qo[b + 1]
+        o, l = _real_query_attn(np.asarray(Q)[a - corpus_len:e - corpus_len], np.asarray(K)[a:e], np.asarray(V)[a:e],
+                                0, [0, e - a], scale)
+        O[a - corpus_len:e - corpus_len] = o
+        lse[a - corpus_len:e - corpus_len] = l
+    return O, lse
+
+
+_real_query_attn = orc.query_attn
+
+
 MUTATIONS = {
     "mask_no_causal": ("allowed", _no_causal),
     "mask_docs_skip_prefix": ("allowed", _docs_skip_prefix),
@@ -155,6 +202,9 @@ MUTATIONS = {
     "scores_shifted_boundaries": ("doc_scores", _scores_shifted_boundaries),
     "rank_ties_high": ("rank", _rank_ties_high),
     "rank_ascending": ("rank", _rank_ascending),
+    "query_no_causal": ("query_attn", _query_no_causal),
+    "query_reads_previous_queries": ("query_attn", _query_reads_previous_queries),
+    "query_skips_corpus": ("query_attn", _query_skips_corpus),
 }
 
 
