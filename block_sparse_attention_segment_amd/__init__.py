@@ -6,11 +6,11 @@ hand-written HIP kernels.
 """
 from ._lib import (BlockRankError, BrDims, EXPORTED, LIB_PATH, attn_fwd, attn_plan_items, attn_plan_schedule,
                    attn_workspace_bytes, doc_scores, doc_scores_workspace_bytes, load_library,
-                   make_dims, sort_docs, version)
+                   make_dims, query_attn, query_attn_workspace_bytes, sort_docs, version)
 
 __all__ = ["BlockRankError", "BrDims", "EXPORTED", "LIB_PATH", "attn_fwd", "attn_plan_items", "attn_plan_schedule",
            "attn_workspace_bytes", "doc_scores", "doc_scores_workspace_bytes", "load_library",
-           "make_dims", "sort_docs", "version", "rank_prompts"]
+           "make_dims", "query_attn", "query_attn_workspace_bytes", "sort_docs", "version", "rank_prompts"]
 
 
 def rank_prompts(Q, K, V, Q_S, segment_offsets, seg_ptr, doc_offsets, doc_ptr, softmax_scale=0.0,

@@ -19,7 +19,7 @@ BR_OK, BR_ERR_INVALID_ARG, BR_ERR_UNSUPPORTED, BR_ERR_WORKSPACE, BR_ERR_HIP = ra
 
 # Symbols the header declares; the CPU test checks the library exports each of them.
 EXPORTED = ("br_attn_workspace_bytes", "br_attn_fwd", "br_attn_fwd_timed", "br_doc_scores_workspace_bytes", "br_doc_scores",
-            "br_sort_docs", "br_attn_plan_items", "br_attn_plan_schedule", "br_status_string", "br_last_error", "br_version")
+            "br_sort_docs", "br_attn_plan_items", "br_attn_plan_schedule", "br_query_attn_workspace_bytes", "br_query_attn_fwd", "br_status_string", "br_last_error", "br_version")
 
 
 class BrDims(ctypes.Structure):
@@ -63,6 +63,8 @@ def load_library() -> ctypes.CDLL:
         "br_sort_docs": [_P, _I32P, ctypes.c_int32, _P, _P],
         "br_attn_plan_items": [dims_p, _I32P, _I32P, _I32P, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64),
                                ctypes.POINTER(ctypes.c_int32)],
+        "br_query_attn_workspace_bytes": [dims_p, ctypes.c_int32, _I32P, ctypes.POINTER(ctypes.c_size_t)],
+        "br_query_attn_fwd": [dims_p, _P, _P, _P, ctypes.c_int32, _I32P, _P, _P, ctypes.c_float, _P, ctypes.c_size_t, _P],
         "br_attn_plan_schedule": [dims_p, _I32P, _I32P, ctypes.c_int32, _I32P, ctypes.c_int64, _I32P, ctypes.c_int64,
                                   ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)],
     }
@@ -186,6 +188,46 @@ def attn_fwd(Q, K, V, segment_offsets, seg_ptr, out=None, lse=None, softmax_scal
     _check(lib.br_attn_fwd_timed(ctypes.byref(dims), Q.data_ptr(), K.data_ptr(), V.data_ptr(), _ptr_i32(so),
                                  _ptr_i32(sp), out.data_ptr(), _dev_ptr(lse), float(softmax_scale),
                                  workspace.data_ptr(), workspace.numel(), _stream_handle(stream), ev0, ev1))
+    return (out, lse) if lse is not None else out
+
+
+def query_attn_workspace_bytes(dims: BrDims, corpus_len: int, query_offsets) -> int:
+    lib = load_library()
+    qo = _host_i32(query_offsets)
+    out = ctypes.c_size_t(0)
+    _check(lib.br_query_attn_workspace_bytes(ctypes.byref(dims), int(corpus_len), _ptr_i32(qo), ctypes.byref(out)))
+    return int(out.value)
+
+
+def query_attn(Q, K, V, corpus_len: int, query_offsets, out=None, lse=None, softmax_scale: float = 0.0,
+               workspace=None, stream=None):
+    """Query-only attention over a cached corpus.  K/V [T,Hkv,d] hold the corpus [0, corpus_len)
+    then the queries' own tokens; Q and out are [T - corpus_len, Hq, d] (query rows only).
+    Query b owns tokens query_offsets[b] .. query_offsets[b+1] and reads the whole corpus plus
+    its own tokens causally.  ``lse`` as in attn_fwd."""
+    import torch
+    lib = load_library()
+    for name, t in (("Q", Q), ("K", K), ("V", V)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 3:
+            raise ValueError(f"{name} must be a contiguous 3-D bfloat16 CUDA tensor")
+    Tq, Hq, d = Q.shape
+    T, Hkv = K.shape[0], K.shape[1]
+    if K.shape != (T, Hkv, d) or V.shape != K.shape or Tq != T - int(corpus_len):
+        raise ValueError("K and V must be [T, Hkv, d] and Q [T - corpus_len, Hq, d]")
+    qo = _host_i32(query_offsets)
+    dims = make_dims(len(qo) - 1, Hq, Hkv, d, T)
+    if out is None:
+        out = torch.empty_like(Q)
+    if lse is True:
+        lse = torch.empty((Tq, Hq), dtype=torch.float32, device=Q.device)
+    elif lse is False:
+        lse = None
+    nbytes = query_attn_workspace_bytes(dims, corpus_len, qo)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+    _check(lib.br_query_attn_fwd(ctypes.byref(dims), Q.data_ptr(), K.data_ptr(), V.data_ptr(), int(corpus_len),
+                                 _ptr_i32(qo), out.data_ptr(), _dev_ptr(lse), float(softmax_scale),
+                                 workspace.data_ptr(), workspace.numel(), _stream_handle(stream)))
     return (out, lse) if lse is not None else out
 
 

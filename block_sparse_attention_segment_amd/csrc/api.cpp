@@ -232,6 +232,69 @@ br_status guarded(F&& f) {
   }
 }
 
+// Buffer checks shared by the attention entry points (host only).
+br_status check_attn_buffers(const void* Q, const void* K, const void* V, const void* out, const float* lse,
+                             float softmax_scale) {
+  if (!Q || !K || !V || !out) return record(BR_ERR_INVALID_ARG, "Q, K, V and out must be non-NULL device pointers");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 16))
+    return record(BR_ERR_INVALID_ARG, "Q, K, V and out must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return record(BR_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (std::isnan(softmax_scale) || std::isinf(softmax_scale))
+    return record(BR_ERR_INVALID_ARG, "softmax_scale must be finite");
+  return BR_OK;
+}
+
+// Upload a validated attention plan into the workspace and launch it.  Q, out and lse rows are
+// addressed relative to token q_row_base.
+br_status run_attn(const br_dims& dims, br::AttnPlan& plan, const void* Q, const void* K, const void* V, void* out,
+                   float* lse, float softmax_scale, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                   int q_row_base, hipEvent_t kernel_start, hipEvent_t kernel_stop) {
+  if (!workspace || workspace_bytes < plan.total_bytes)
+    return record(BR_ERR_WORKSPACE, "workspace is NULL or smaller than the workspace size query's " +
+                                        std::to_string(plan.total_bytes) + " bytes");
+  if (!aligned(workspace, 16)) return record(BR_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  // All arguments are valid: only now touch the runtime (device query for the schedule).
+  int workgroups = 0;
+  hipError_t he0 = attn_workgroups(&workgroups);
+  if (he0 != hipSuccess) return hip_fail(he0, "device query");
+  br::schedule_attn_plan(dims.num_kv_heads, workgroups, &plan);
+
+  // Host image of the plan region of the workspace: [items | ranges | merges].
+  std::vector<unsigned char> host(plan.off_part_o, 0);
+  std::memcpy(host.data() + plan.off_items, plan.sched.data(), plan.sched.size() * sizeof(br::AttnItem));
+  std::memcpy(host.data() + plan.off_ranges, plan.ranges.data(), plan.ranges.size() * sizeof(int32_t));
+  if (!plan.merges.empty())
+    std::memcpy(host.data() + plan.off_merges, plan.merges.data(), plan.merges.size() * sizeof(br::MergeItem));
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  br_status st = upload(ws, host.data(), host.size(), stream);
+  if (st != BR_OK) return st;
+
+  br::AttnLaunch a;
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.K = static_cast<const uint16_t*>(K);
+  a.V = static_cast<const uint16_t*>(V);
+  a.O = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.items = reinterpret_cast<const br::AttnItem*>(ws + plan.off_items);
+  a.ranges = reinterpret_cast<const int32_t*>(ws + plan.off_ranges);
+  a.merges = reinterpret_cast<const br::MergeItem*>(ws + plan.off_merges);
+  a.part_o = reinterpret_cast<float*>(ws + plan.off_part_o);
+  a.part_ml = reinterpret_cast<float*>(ws + plan.off_part_ml);
+  a.n_items = int64_t(plan.items.size());
+  a.n_merges = int64_t(plan.merges.size());
+  a.wg_per_head = plan.wg_per_head;
+  a.num_q_heads = dims.num_q_heads;
+  a.num_kv_heads = dims.num_kv_heads;
+  a.head_dim = dims.head_dim;
+  a.scale_log2 = resolve_scale(softmax_scale, dims.head_dim) * 1.4426950408889634f;
+  a.q_row_base = q_row_base;
+  a.ev_start = kernel_start;
+  a.ev_stop = kernel_stop;
+  hipError_t he = br::launch_attn(a, stream);
+  if (he != hipSuccess) return hip_fail(he, "attention kernel launch");
+  return BR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -313,58 +376,43 @@ br_status br_attn_fwd_timed(const br_dims* dims, const void* Q, const void* K, c
   return guarded([&]() -> br_status {
     br::Error e = br::validate_dims(dims);
     if (!e.ok()) return record(e);
-    if (!Q || !K || !V || !out) return record(BR_ERR_INVALID_ARG, "Q, K, V and out must be non-NULL device pointers");
-    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 16))
-      return record(BR_ERR_INVALID_ARG, "Q, K, V and out must be 16-byte aligned");
-    if (lse && !aligned(lse, 4)) return record(BR_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-    if (std::isnan(softmax_scale) || std::isinf(softmax_scale))
-      return record(BR_ERR_INVALID_ARG, "softmax_scale must be finite");
+    br_status st = check_attn_buffers(Q, K, V, out, lse, softmax_scale);
+    if (st != BR_OK) return st;
     br::AttnPlan plan;
     e = br::build_attn_plan(*dims, segment_offsets, seg_ptr, &plan);
     if (!e.ok()) return record(e);
-    if (!workspace || workspace_bytes < plan.total_bytes)
-      return record(BR_ERR_WORKSPACE, "workspace is NULL or smaller than br_attn_workspace_bytes() = " +
-                                          std::to_string(plan.total_bytes));
-    if (!aligned(workspace, 16)) return record(BR_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-    // All arguments are valid: only now touch the runtime (device query for the schedule).
-    int workgroups = 0;
-    hipError_t he0 = attn_workgroups(&workgroups);
-    if (he0 != hipSuccess) return hip_fail(he0, "device query");
-    br::schedule_attn_plan(dims->num_kv_heads, workgroups, &plan);
+    return run_attn(*dims, plan, Q, K, V, out, lse, softmax_scale, workspace, workspace_bytes, stream, 0, kernel_start,
+                    kernel_stop);
+  });
+}
 
-    // Host image of the plan region of the workspace: [items | ranges | merges].
-    std::vector<unsigned char> host(plan.off_part_o, 0);
-    std::memcpy(host.data() + plan.off_items, plan.sched.data(), plan.sched.size() * sizeof(br::AttnItem));
-    std::memcpy(host.data() + plan.off_ranges, plan.ranges.data(), plan.ranges.size() * sizeof(int32_t));
-    if (!plan.merges.empty())
-      std::memcpy(host.data() + plan.off_merges, plan.merges.data(), plan.merges.size() * sizeof(br::MergeItem));
-    unsigned char* ws = static_cast<unsigned char*>(workspace);
-    br_status st = upload(ws, host.data(), host.size(), stream);
-    if (st != BR_OK) return st;
-
-    br::AttnLaunch a;
-    a.Q = static_cast<const uint16_t*>(Q);
-    a.K = static_cast<const uint16_t*>(K);
-    a.V = static_cast<const uint16_t*>(V);
-    a.O = static_cast<uint16_t*>(out);
-    a.lse = lse;
-    a.items = reinterpret_cast<const br::AttnItem*>(ws + plan.off_items);
-    a.ranges = reinterpret_cast<const int32_t*>(ws + plan.off_ranges);
-    a.merges = reinterpret_cast<const br::MergeItem*>(ws + plan.off_merges);
-    a.part_o = reinterpret_cast<float*>(ws + plan.off_part_o);
-    a.part_ml = reinterpret_cast<float*>(ws + plan.off_part_ml);
-    a.n_items = int64_t(plan.items.size());
-    a.n_merges = int64_t(plan.merges.size());
-    a.wg_per_head = plan.wg_per_head;
-    a.num_q_heads = dims->num_q_heads;
-    a.num_kv_heads = dims->num_kv_heads;
-    a.head_dim = dims->head_dim;
-    a.scale_log2 = resolve_scale(softmax_scale, dims->head_dim) * 1.4426950408889634f;
-    a.ev_start = kernel_start;
-    a.ev_stop = kernel_stop;
-    hipError_t he = br::launch_attn(a, stream);
-    if (he != hipSuccess) return hip_fail(he, "attention kernel launch");
+br_status br_query_attn_workspace_bytes(const br_dims* dims, int32_t corpus_len, const int32_t* query_offsets,
+                                        size_t* bytes) {
+  return guarded([&]() -> br_status {
+    if (!bytes) return record(BR_ERR_INVALID_ARG, "bytes is NULL");
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    br::AttnPlan plan;
+    e = br::build_query_plan(*dims, corpus_len, query_offsets, &plan);
+    if (!e.ok()) return record(e);
+    *bytes = plan.total_bytes;
     return BR_OK;
+  });
+}
+
+br_status br_query_attn_fwd(const br_dims* dims, const void* Q, const void* K, const void* V, int32_t corpus_len,
+                            const int32_t* query_offsets, void* out, float* lse, float softmax_scale,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return guarded([&]() -> br_status {
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    br_status st = check_attn_buffers(Q, K, V, out, lse, softmax_scale);
+    if (st != BR_OK) return st;
+    br::AttnPlan plan;
+    e = br::build_query_plan(*dims, corpus_len, query_offsets, &plan);
+    if (!e.ok()) return record(e);
+    return run_attn(*dims, plan, Q, K, V, out, lse, softmax_scale, workspace, workspace_bytes, stream, corpus_len,
+                    nullptr, nullptr);
   });
 }
 

@@ -7,6 +7,9 @@
 // BlockSearch section 3.2 for the causal reading of the diagonal blocks).  The host plan lists
 // only allowed (row tile, key range) pairs; this kernel never visits a forbidden block.
 //
+// Row token indices address Q, O and lse relative to q_row_base (0 for whole prompts; the corpus
+// length when only query rows over a cached corpus are computed).
+//
 // Work item = 128 (token, head) rows: TM = 128 / G consecutive tokens of the G query heads
 // that share one KV head (grouped-query packing), so each K/V tile staged in LDS serves G
 // heads.  Wave w owns 32 rows.  Per 64-key tile:
@@ -46,7 +49,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
                                                        const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                                                        float* __restrict__ lse, const AttnItem* __restrict__ items,
                                                        const int32_t* __restrict__ ranges, float* __restrict__ part_o,
-                                                       float* __restrict__ part_ml, int Hq, int Hkv, float scale_log2) {
+                                                       float* __restrict__ part_ml, int Hq, int Hkv, float scale_log2,
+                                                       int q_row_base) {
   constexpr int TM = kRowsPerTile / G;  // tokens per tile
   constexpr int BN = kKeyTile;          // keys per LDS tile
   constexpr int NKB = BN / 32;          // 32-key MFMA blocks per tile
@@ -93,7 +97,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
   // Resource over a tile's valid rows of a [T, Hq, D] tensor, based at its first row and head.
   auto row_rsrc = [&](const uint16_t* base, const AttnItem& it) {
     const int rows = min(TM, it.row_limit - it.row0);
-    return make_rsrc(base + (int64_t(it.row0) * Hq + g * G) * D, rows * q_stride * 2);
+    return make_rsrc(base + (int64_t(it.row0 - q_row_base) * Hq + g * G) * D, rows * q_stride * 2);
   };
   u32x4_t qf[DSTEPS];
   auto load_q = [&](const AttnItem& it, u32x4_t* dst) {
@@ -336,7 +340,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
           *reinterpret_cast<u32x4_t*>(&xbuf[rho * QROW + 32 * b + 16 * t + 8 * half]) = v;
         }
       if (lse && half == 0 && row_tok < cur.row_limit)
-        lse[int64_t(row_tok) * Hq + h] = (m_run + __log2f(l_tot)) * kLn2;
+        lse[int64_t(row_tok - q_row_base) * Hq + h] = (m_run + __log2f(l_tot)) * kLn2;
       // Whole-row stores of this wave's rows: instruction s writes QRI rows (1 KB, 8 full
       // cache lines), lane l chunk l % KCH of row 32 w + QRI s + l / KCH.
 #pragma unroll
@@ -374,7 +378,8 @@ template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(uint16_t* __restrict__ O, float* __restrict__ lse,
                                                          const MergeItem* __restrict__ merges,
                                                          const float* __restrict__ part_o,
-                                                         const float* __restrict__ part_ml, int Hq, int Hkv, int G) {
+                                                         const float* __restrict__ part_ml, int Hq, int Hkv, int G,
+                                                         int q_row_base) {
   constexpr int CH = D / 4;                          // 4-element units per row
   constexpr int WG_PER_TILE = kRowsPerTile * CH / 256;
   const int tile = blockIdx.x / WG_PER_TILE, part = blockIdx.x % WG_PER_TILE;
@@ -418,8 +423,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(uint16_t* __restrict__ 
     add(ml[row + c * stride], *reinterpret_cast<const f32x4_t*>(part_o + (row + c * stride) * D + ch * 4));
   const float inv = 1.f / L;
   const u32x2_t v = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
-  *reinterpret_cast<u32x2_t*>(O + (int64_t(tok) * Hq + h) * D + ch * 4) = v;
-  if (lse && ch == 0) lse[int64_t(tok) * Hq + h] = (M + __log2f(L)) * kLn2;
+  *reinterpret_cast<u32x2_t*>(O + (int64_t(tok - q_row_base) * Hq + h) * D + ch * 4) = v;
+  if (lse && ch == 0) lse[int64_t(tok - q_row_base) * Hq + h] = (M + __log2f(L)) * kLn2;
 }
 
 template <int D, int G>
@@ -431,7 +436,7 @@ static hipError_t launch_attn_t(const AttnLaunch& a, hipStream_t stream) {
       if (e != hipSuccess) return e;
     }
     attn_fwd_kernel<D, G><<<grid, 256, 0, stream>>>(a.Q, a.K, a.V, a.O, a.lse, a.items, a.ranges, a.part_o, a.part_ml,
-                                                    a.num_q_heads, a.num_kv_heads, a.scale_log2);
+                                                    a.num_q_heads, a.num_kv_heads, a.scale_log2, a.q_row_base);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.ev_stop) {
@@ -442,7 +447,7 @@ static hipError_t launch_attn_t(const AttnLaunch& a, hipStream_t stream) {
   if (a.n_merges > 0) {
     const dim3 grid(unsigned(a.n_merges * a.num_kv_heads * (kRowsPerTile * (D / 4) / 256)));
     attn_merge_kernel<D><<<grid, 256, 0, stream>>>(a.O, a.lse, a.merges, a.part_o, a.part_ml, a.num_q_heads,
-                                                   a.num_kv_heads, G);
+                                                   a.num_kv_heads, G, a.q_row_base);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -23,6 +23,7 @@ struct AttnLaunch {
   int wg_per_head;
   int num_q_heads, num_kv_heads, head_dim;
   float scale_log2;         // softmax scale * log2(e)
+  int q_row_base = 0;       // token index of Q/O/lse row 0 (the corpus length for query-only runs)
   hipEvent_t ev_start = nullptr, ev_stop = nullptr;  // optional, recorded around the main kernel
 };
 hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream);

@@ -72,82 +72,60 @@ Error validate_segments(const br_dims& dims, const int32_t* so, const int32_t* s
   return {};
 }
 
-Error build_attn_plan(const br_dims& dims, const int32_t* so, const int32_t* sp, AttnPlan* plan) {
-  Error e = validate_dims(&dims);
-  if (!e.ok()) return e;
-  e = validate_segments(dims, so, sp);
-  if (!e.ok()) return e;
+namespace {
 
+// Shared by the prompt plan and the query-only plan.
+struct ItemMaker {
+  int TM, BN;
+  int64_t CK;  // split-key chunk length
+  int32_t tiles(int64_t a, int64_t b) const { return int32_t(b > a ? cdiv(b - a, BN) : 0); }
+  AttnItem operator()(int64_t row0, int64_t lim, int64_t a0, int64_t a1, int64_t b0, int64_t b1, int32_t slot) const {
+    if (a1 <= a0) a0 = a1 = 0;
+    if (b1 <= b0) b0 = b1 = 0;
+    return AttnItem{int32_t(row0), int32_t(lim), int32_t(a0), int32_t(a1), int32_t(b0), int32_t(b1), slot,
+                    tiles(a0, a1) + tiles(b0, b1)};
+  }
+};
+
+void init_plan(const br_dims& dims, int64_t max_unmasked, AttnPlan* plan, ItemMaker* mk) {
   AttnPlan& P = *plan;
   P = AttnPlan{};
   P.group = dims.num_q_heads / dims.num_kv_heads;
   P.rows_per_tile = tokens_per_tile(P.group);
   P.key_tile = kKeyTile;
-  const int TM = P.rows_per_tile, BN = P.key_tile;
+  // Split-key chunk for query rows: aim for ~16 chunks of the longest unmasked key range, each
+  // 4..64 key tiles, so long query tiles spread over many workgroups.
+  const int64_t chunk_tiles = std::min<int64_t>(64, std::max<int64_t>(4, cdiv(cdiv(max_unmasked, kKeyTile), 16)));
+  P.chunk_keys = int(chunk_tiles * kKeyTile);
+  *mk = ItemMaker{P.rows_per_tile, kKeyTile, P.chunk_keys};
+}
 
-  // Split-key chunk for the final query's rows: aim for ~16 chunks of the longest prefix,
-  // each 4..64 key tiles, so long query tiles spread over many workgroups.
-  int64_t max_prefix = 0;
-  for (int b = 0; b < dims.num_prompts; ++b) {
-    const int32_t* o = so + sp[b];
-    int n = sp[b + 1] - sp[b];
-    max_prefix = std::max<int64_t>(max_prefix, o[n - 2] - o[0]);
-  }
-  int64_t chunk_tiles = std::min<int64_t>(64, std::max<int64_t>(4, cdiv(cdiv(max_prefix, BN), 16)));
-  P.chunk_keys = int(chunk_tiles * BN);
-  const int64_t CK = P.chunk_keys;
-
-  auto tiles = [&](int64_t a, int64_t b) { return int32_t(b > a ? cdiv(b - a, BN) : 0); };
-  auto item = [&](int64_t row0, int64_t lim, int64_t a0, int64_t a1, int64_t b0, int64_t b1, int32_t slot) {
-    if (a1 <= a0) a0 = a1 = 0;
-    if (b1 <= b0) b0 = b1 = 0;
-    return AttnItem{int32_t(row0), int32_t(lim), int32_t(a0), int32_t(a1), int32_t(b0), int32_t(b1), slot,
-                    tiles(a0, a1) + tiles(b0, b1)};
-  };
-
-  std::vector<AttnItem> query_items, other_items;
-  for (int b = 0; b < dims.num_prompts; ++b) {
-    const int32_t* o = so + sp[b];
-    const int n = sp[b + 1] - sp[b];
-    const int64_t ps = o[0], pe = o[1], qs = o[n - 2], qe = o[n - 1];
-    // instruction rows: causal within the instruction
-    for (int64_t r0 = ps; r0 < pe; r0 += TM) other_items.push_back(item(r0, pe, 0, 0, ps, std::min(r0 + TM, pe), -1));
-    // document rows: whole instruction, then own document causally; last row tile first
-    for (int k = 1; k <= n - 3; ++k) {
-      const int64_t ds = o[k], de = o[k + 1];
-      const int64_t ntile = cdiv(de - ds, TM);
-      for (int64_t t = ntile - 1; t >= 0; --t) {
-        const int64_t r0 = ds + t * TM;
-        other_items.push_back(item(r0, de, ps, pe, ds, std::min(r0 + TM, de), -1));
-      }
+// Query rows [qs, qe): keys [u0, u1) unmasked (split into chunks merged afterwards when longer
+// than one chunk), then the query's own tokens [qs, row] causally.
+void add_query_rows(int64_t qs, int64_t qe, int64_t u0, int64_t u1, const ItemMaker& mk, AttnPlan* plan,
+                    std::vector<AttnItem>* out) {
+  AttnPlan& P = *plan;
+  for (int64_t r0 = qs; r0 < qe; r0 += mk.TM) {
+    const int64_t b1 = std::min(r0 + mk.TM, qe);
+    const int64_t nchunk = std::max<int64_t>(1, cdiv(u1 - u0, mk.CK));
+    if (nchunk == 1) {
+      out->push_back(mk(r0, qe, u0, u1, qs, b1, -1));
+      continue;
     }
-    // final-query rows: everything before the query unmasked, the query causally
-    for (int64_t r0 = qs; r0 < qe; r0 += TM) {
-      const int64_t b1 = std::min(r0 + TM, qe);
-      const int64_t nchunk = std::max<int64_t>(1, cdiv(qs - ps, CK));
-      if (nchunk == 1) {
-        query_items.push_back(item(r0, qe, ps, qs, qs, b1, -1));
-        continue;
-      }
-      const int32_t slot0 = P.n_slots;
-      for (int64_t c = 0; c < nchunk; ++c) {
-        const int64_t a0 = ps + c * CK, a1 = std::min(ps + (c + 1) * CK, qs);
-        const bool last = c == nchunk - 1;
-        query_items.push_back(item(r0, qe, a0, a1, last ? qs : 0, last ? b1 : 0, slot0 + int32_t(c)));
-      }
-      P.merges.push_back(MergeItem{int32_t(r0), int32_t(qe), slot0, int32_t(nchunk)});
-      P.n_slots += int32_t(nchunk);
+    const int32_t slot0 = P.n_slots;
+    for (int64_t c = 0; c < nchunk; ++c) {
+      const int64_t a0 = u0 + c * mk.CK, a1 = std::min(u0 + (c + 1) * mk.CK, u1);
+      const bool last = c == nchunk - 1;
+      out->push_back(mk(r0, qe, a0, a1, last ? qs : 0, last ? b1 : 0, slot0 + int32_t(c)));
     }
+    P.merges.push_back(MergeItem{int32_t(r0), int32_t(qe), slot0, int32_t(nchunk)});
+    P.n_slots += int32_t(nchunk);
   }
-  // Time order for the list schedule: the long query chunks first, then instruction and
-  // document row tiles in prompt order.  The row tiles of one document stay adjacent, so the
-  // schedule hands them to different workgroups at about the same time and the document's keys
-  // are fetched once and re-read from the shared L2.
-  std::stable_sort(query_items.begin(), query_items.end(),
-                   [](const AttnItem& x, const AttnItem& y) { return x.ntiles > y.ntiles; });
-  P.items = std::move(query_items);
-  P.items.insert(P.items.end(), other_items.begin(), other_items.end());
+}
 
+// Workspace layout and the default schedule.
+void finish_plan(const br_dims& dims, AttnPlan* plan) {
+  AttnPlan& P = *plan;
   const size_t hkv = size_t(dims.num_kv_heads), d = size_t(dims.head_dim);
   P.off_items = 0;
   P.off_ranges = align_up(P.items.size() * sizeof(AttnItem), 256);
@@ -156,6 +134,86 @@ Error build_attn_plan(const br_dims& dims, const int32_t* so, const int32_t* sp,
   P.off_part_ml = align_up(P.off_part_o + size_t(P.n_slots) * hkv * kRowsPerTile * d * 4, 256);
   P.total_bytes = align_up(P.off_part_ml + size_t(P.n_slots) * hkv * kRowsPerTile * 2 * 4, 256);
   schedule_attn_plan(dims.num_kv_heads, 256 * kAttnWgPerCu, plan);
+}
+
+// Longest items first (the split query chunks), the rest after in the order given.
+void order_items(std::vector<AttnItem>&& query_items, const std::vector<AttnItem>& other_items, AttnPlan* plan) {
+  std::stable_sort(query_items.begin(), query_items.end(),
+                   [](const AttnItem& x, const AttnItem& y) { return x.ntiles > y.ntiles; });
+  plan->items = std::move(query_items);
+  plan->items.insert(plan->items.end(), other_items.begin(), other_items.end());
+}
+
+}  // namespace
+
+Error build_attn_plan(const br_dims& dims, const int32_t* so, const int32_t* sp, AttnPlan* plan) {
+  Error e = validate_dims(&dims);
+  if (!e.ok()) return e;
+  e = validate_segments(dims, so, sp);
+  if (!e.ok()) return e;
+
+  int64_t max_prefix = 0;
+  for (int b = 0; b < dims.num_prompts; ++b) {
+    const int32_t* o = so + sp[b];
+    int n = sp[b + 1] - sp[b];
+    max_prefix = std::max<int64_t>(max_prefix, o[n - 2] - o[0]);
+  }
+  ItemMaker mk{};
+  init_plan(dims, max_prefix, plan, &mk);
+  const int64_t TM = mk.TM;
+
+  std::vector<AttnItem> query_items, other_items;
+  for (int b = 0; b < dims.num_prompts; ++b) {
+    const int32_t* o = so + sp[b];
+    const int n = sp[b + 1] - sp[b];
+    const int64_t ps = o[0], pe = o[1], qs = o[n - 2], qe = o[n - 1];
+    // instruction rows: causal within the instruction
+    for (int64_t r0 = ps; r0 < pe; r0 += TM) other_items.push_back(mk(r0, pe, 0, 0, ps, std::min(r0 + TM, pe), -1));
+    // document rows: whole instruction, then own document causally; last row tile first
+    for (int k = 1; k <= n - 3; ++k) {
+      const int64_t ds = o[k], de = o[k + 1];
+      const int64_t ntile = cdiv(de - ds, TM);
+      for (int64_t t = ntile - 1; t >= 0; --t) {
+        const int64_t r0 = ds + t * TM;
+        other_items.push_back(mk(r0, de, ps, pe, ds, std::min(r0 + TM, de), -1));
+      }
+    }
+    // final-query rows: everything before the query unmasked, the query causally
+    add_query_rows(qs, qe, ps, qs, mk, plan, &query_items);
+  }
+  // Time order for the list schedule: the long query chunks first, then instruction and
+  // document row tiles in prompt order.  The row tiles of one document stay adjacent, so the
+  // schedule hands them to different workgroups at about the same time and the document's keys
+  // are fetched once and re-read from the shared L2.
+  order_items(std::move(query_items), other_items, plan);
+  finish_plan(dims, plan);
+  return {};
+}
+
+Error validate_queries(const br_dims& dims, int32_t corpus_len, const int32_t* qo) {
+  if (!qo) return fail(BR_ERR_INVALID_ARG, "query_offsets must be a non-NULL host array");
+  if (corpus_len < 0) return fail(BR_ERR_INVALID_ARG, "corpus_len must be >= 0 (got %lld)", corpus_len);
+  if (qo[0] != corpus_len)
+    return fail(BR_ERR_INVALID_ARG, "query_offsets[0] (%lld) must equal corpus_len (%lld)", qo[0], corpus_len);
+  for (int b = 0; b < dims.num_prompts; ++b)
+    if (qo[b + 1] <= qo[b])
+      return fail(BR_ERR_INVALID_ARG, "query %lld is empty or reversed (offsets %lld, %lld)", b, qo[b], qo[b + 1]);
+  if (qo[dims.num_prompts] != dims.total_tokens)
+    return fail(BR_ERR_INVALID_ARG, "last query offset %lld != total_tokens %lld", qo[dims.num_prompts], dims.total_tokens);
+  return {};
+}
+
+Error build_query_plan(const br_dims& dims, int32_t corpus_len, const int32_t* qo, AttnPlan* plan) {
+  Error e = validate_dims(&dims);
+  if (!e.ok()) return e;
+  e = validate_queries(dims, corpus_len, qo);
+  if (!e.ok()) return e;
+  ItemMaker mk{};
+  init_plan(dims, corpus_len, plan, &mk);
+  std::vector<AttnItem> query_items;
+  for (int b = 0; b < dims.num_prompts; ++b) add_query_rows(qo[b], qo[b + 1], 0, corpus_len, mk, plan, &query_items);
+  order_items(std::move(query_items), {}, plan);
+  finish_plan(dims, plan);
   return {};
 }
 

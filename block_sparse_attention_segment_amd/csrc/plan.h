@@ -83,6 +83,11 @@ Error validate_dims(const br_dims* dims);
 Error validate_segments(const br_dims& dims, const int32_t* segment_offsets, const int32_t* seg_ptr);
 Error build_attn_plan(const br_dims& dims, const int32_t* segment_offsets, const int32_t* seg_ptr,
                       AttnPlan* plan);
+// Query-only plan over a cached corpus: dims.num_prompts queries; query b owns key/value tokens
+// [query_offsets[b], query_offsets[b + 1]) after the corpus [0, corpus_len) and reads the whole
+// corpus unmasked plus its own tokens causally.
+Error validate_queries(const br_dims& dims, int32_t corpus_len, const int32_t* query_offsets);
+Error build_query_plan(const br_dims& dims, int32_t corpus_len, const int32_t* query_offsets, AttnPlan* plan);
 // Partition the item list over the persistent workgroups of each KV head.  `workgroups` = the
 // device's persistent workgroup slots (CUs x kAttnWgPerCu); it shapes only the partition, never
 // the items or the workspace size.  Calling it again re-partitions from `items`.

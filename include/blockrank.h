@@ -144,6 +144,25 @@ br_status br_sort_docs(const float* scores, const int32_t* doc_ptr, int32_t num_
                        int32_t* order, hipStream_t stream);
 
 /*
+ * Query-only attention over a cached corpus ("prefill once, score many queries"; BlockSearch,
+ * section 3.2: the query block attends over the full corpus and causally to itself).
+ * The key/value token axis holds the corpus [0, corpus_len) (e.g. an instruction and its
+ * documents, already prefilled) followed by dims->num_prompts queries; query b owns tokens
+ * [query_offsets[b], query_offsets[b + 1]) and each of its rows reads every corpus key
+ * unmasked plus its own query's keys up to itself.  Corpus rows are not computed.
+ *   query_offsets: HOST int32[num_prompts + 1], query_offsets[0] == corpus_len, strictly
+ *                  increasing, last == dims->total_tokens (= corpus_len + query tokens).
+ *   Q, out: device bf16 [total_tokens - corpus_len, Hq, d] (query rows only, in token order);
+ *   K, V:   device bf16 [total_tokens, Hkv, d];  lse: device fp32 [total_tokens - corpus_len, Hq]
+ *           or NULL.  Other rules (scale, alignment, workspace, errors) as br_attn_fwd.
+ */
+br_status br_query_attn_workspace_bytes(const br_dims* dims, int32_t corpus_len, const int32_t* query_offsets,
+                                        size_t* bytes);
+br_status br_query_attn_fwd(const br_dims* dims, const void* Q, const void* K, const void* V, int32_t corpus_len,
+                            const int32_t* query_offsets, void* out, float* lse, float softmax_scale,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Host-only introspection of the attention work plan (no HIP call).  Writes up to
  * `capacity` work items of 8 int32 each, {row0, row_limit, a_start, a_end, b_start, b_end,
  * partial_slot, tile_count}: the row tile starts at token row0 and covers the tokens

@@ -220,3 +220,40 @@ def test_doc_scores_and_sort_reject_bad_arguments():
     assert lib.br_sort_docs(f, p(big), 1, f, None) == br._lib.BR_ERR_UNSUPPORTED
     assert lib.br_sort_docs(f, p(np.array([0, 1], dtype=np.int32)), 1, f, None) == br._lib.BR_ERR_INVALID_ARG
     assert lib.br_sort_docs(None, p(dp), 1, f, None) == br._lib.BR_ERR_INVALID_ARG
+
+
+# ---- query-only attention over a cached corpus (host side only) ----
+def test_query_attn_workspace_and_bad_offsets():
+    dims = br.make_dims(3, 8, 2, 128, 100 + 7 + 1 + 40)
+    qo = np.array([100, 107, 108, 148], dtype=np.int32)
+    assert br.query_attn_workspace_bytes(dims, 100, qo) > 0
+    # corpus of 0 tokens: plain causal attention per query
+    dims0 = br.make_dims(2, 8, 2, 128, 10)
+    assert br.query_attn_workspace_bytes(dims0, 0, np.array([0, 3, 10], dtype=np.int32)) > 0
+    bad = [
+        (100, [99, 107, 108, 148]),   # first offset != corpus_len
+        (100, [100, 107, 107, 148]),  # empty query
+        (100, [100, 107, 108, 147]),  # last != total_tokens
+        (-1, [-1, 107, 108, 148]),    # negative corpus
+    ]
+    for corpus, offs in bad:
+        with pytest.raises(br.BlockRankError) as ei:
+            br.query_attn_workspace_bytes(dims, corpus, np.array(offs, dtype=np.int32))
+        assert ei.value.status == br._lib.BR_ERR_INVALID_ARG, (corpus, offs)
+
+
+def test_query_attn_rejects_before_any_hip_call():
+    lib = br.load_library()
+    qo = np.array([64, 96], dtype=np.int32)
+    p = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    dims = br.make_dims(1, 8, 2, 128, 96)
+    need = br.query_attn_workspace_bytes(dims, 64, qo)
+    f = _fake()
+    st = lib.br_query_attn_fwd(ctypes.byref(dims), f, f, f, 64, p(qo), f, None, 0.0, f, need - 1, None)
+    assert st == br._lib.BR_ERR_WORKSPACE
+    st = lib.br_query_attn_fwd(ctypes.byref(dims), f, None, f, 64, p(qo), f, None, 0.0, f, need, None)
+    assert st == br._lib.BR_ERR_INVALID_ARG
+    st = lib.br_query_attn_fwd(ctypes.byref(dims), f, f, f, 64, None, f, None, 0.0, f, need, None)
+    assert st == br._lib.BR_ERR_INVALID_ARG
+    st = lib.br_query_attn_fwd(ctypes.byref(dims), f, f, f, 64, p(qo), f, None, float("inf"), f, need, None)
+    assert st == br._lib.BR_ERR_INVALID_ARG
