@@ -198,6 +198,56 @@ def measure(config, seed, steps, warmup, log):
                 peak_mb=peak_mb, visited_pairs=tile_efficiency(w, dims))
 
 
+def measure_query_only(w, n_queries, q_len, steps, warmup, seed, log):
+    """Query-only attention over a cached corpus: the corpus is the prompt's instruction and
+    documents (its K/V already prefilled), scored against n_queries new queries of q_len tokens.
+    Times whole br_query_attn_fwd calls (plan copy, attention, merge) between events."""
+    import torch
+
+    import block_sparse_attention_segment_amd as br
+    import workloads
+
+    offs = [int(x) for x in w.segment_offsets]
+    corpus = offs[-2]
+    Hq, d = w.Q.shape[1], w.Q.shape[2]
+    Hkv = w.K.shape[1]
+    rng = np.random.default_rng(seed + 1000)
+    nq = n_queries * q_len
+    bf = lambda a: workloads.f32_to_bf16_bits(a.astype(np.float32))
+    Kq, Vq = bf(rng.standard_normal((nq, Hkv, d))), bf(rng.standard_normal((nq, Hkv, d)))
+    Qq = bf(rng.standard_normal((nq, Hq, d)))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    K = torch.cat([dev(w.K[:corpus]), dev(Kq)]).contiguous()
+    V = torch.cat([dev(w.V[:corpus]), dev(Vq)]).contiguous()
+    Q = dev(Qq)
+    qo = np.arange(n_queries + 1, dtype=np.int64) * q_len + corpus
+    dims = br.make_dims(n_queries, Hq, Hkv, d, corpus + nq)
+    ws = torch.empty(br.query_attn_workspace_bytes(dims, corpus, qo), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(Q)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        br.query_attn(Q, K, V, corpus, qo, out=out, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        br.query_attn(Q, K, V, corpus, qo, out=out, workspace=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    pairs = n_queries * (q_len * corpus + q_len * (q_len + 1) // 2)
+    flop = 4.0 * d * Hq * pairs
+    alg_bytes = float(corpus) * Hkv * d * 2 * 2 + float(nq) * (2 * Hq + 2 * Hkv) * d * 2
+    log(f"[bench] query-only: {n_queries} x {q_len} tokens over a {corpus}-token corpus, {ms:.4f} ms/call")
+    return {"workload": f"{n_queries} queries x {q_len} tokens over the long prompt's cached corpus "
+                        f"(instruction + 500 documents, {corpus} tokens), {Hq} Q / {Hkv} KV heads, d={d}",
+            "bound": "mfma",  # each corpus K/V byte serves every query: ~2000 FLOP/B, far above the ridge
+            "ms": round(ms, 5), "tflops_allowed_pairs": round(flop / (ms / 1e3) / 1e12, 3),
+            "mfma_peak_frac": round(flop / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_gbps": round(alg_bytes / (ms / 1e3) / 1e9, 1),
+            "hbm_roofline_frac": round(alg_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)}
+
+
 def cpu_baseline(w, n_docs_sample, log):
     """Time the fp64 oracle on a bounded sample of the same prompt and scale to the whole step."""
     import oracle.oracle as orc
@@ -239,6 +289,8 @@ def main():
     ap.add_argument("--config", default="long", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--secondary", default="worked", help="extra config timed in the same run ('' for none)")
+    ap.add_argument("--query-only", type=int, default=1,
+                    help="also time query-only attention over the long prompt's cached corpus (0 to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-docs", type=int, default=200, help="documents in the CPU oracle's timed sample")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -309,6 +361,8 @@ def main():
                              "prompts_per_s": round(r2["w"].num_prompts / s2, 2),
                              "tflops_closed_form_pairs": round(r2["flop_blk"] / s2 / 1e12, 3),
                              "attention_kernel_ms": round(r2["kernel_ms"], 5)}
+    if args.query_only and args.config == "long":
+        line["query_only"] = measure_query_only(w, 16, 32, args.steps, args.warmup, args.seed, log)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, args.cpu_docs, log)
         line["cpu_baseline"] = {

@@ -212,7 +212,11 @@ Error build_query_plan(const br_dims& dims, int32_t corpus_len, const int32_t* q
   init_plan(dims, corpus_len, plan, &mk);
   std::vector<AttnItem> query_items;
   for (int b = 0; b < dims.num_prompts; ++b) add_query_rows(qo[b], qo[b + 1], 0, corpus_len, mk, plan, &query_items);
-  order_items(std::move(query_items), {}, plan);
+  // Time order: corpus chunk by chunk, every query's row tiles for one chunk adjacent, so the
+  // list schedule runs them at the same time and the chunk's keys are fetched once into L2.
+  std::stable_sort(query_items.begin(), query_items.end(),
+                   [](const AttnItem& x, const AttnItem& y) { return x.a_start < y.a_start; });
+  plan->items = std::move(query_items);
   finish_plan(dims, plan);
   return {};
 }
