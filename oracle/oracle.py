@@ -30,6 +30,8 @@ Readings taken where the pages are silent or disagree (each also listed in the d
     per-head sums.  Sum, not mean, over signal tokens ([BR] "sum is used in practice").
   * Prompts in one call are independent: no attention across prompts, one sort per prompt.
   * Rank: descending score, ties to the lower document index.
+  * Top-B routing ([BS] 5.1): dropped documents leave the attention altogether (their rows are
+    not computed, no row reads their keys); the instruction and the query always stay.
   * Query-only attention over a cached corpus ([BS] 3.2, "prefill once, score many queries"):
     each query reads the whole corpus unmasked and its own tokens causally, never another
     query's tokens; the corpus is whatever precedes the queries (for BlockRank, the
@@ -242,6 +244,53 @@ def query_attn(Q, K, V, corpus_len: int, query_offsets, scale: Optional[float] =
             g = kv_head(h, Hq, Hkv)
             O[qs - corpus_len:qe - corpus_len, h], lse[qs - corpus_len:qe - corpus_len, h] = _masked_softmax_av(
                 Qf[qs - corpus_len:qe - corpus_len, h], Kf[keys, g], Vf[keys, g], mask, sc)
+    return O, lse
+
+
+def dropped_tokens(segment_offsets, seg_ptr, keep_ptr, keep) -> np.ndarray:
+    """Boolean per token: True for the tokens of documents that top-B routing drops."""
+    so = np.asarray(segment_offsets, dtype=np.int64); sp = np.asarray(seg_ptr, dtype=np.int64)
+    T = int(so[-1])
+    out = np.zeros(T, dtype=bool)
+    for b in range(len(sp) - 1):
+        offs = so[sp[b]:sp[b + 1]]
+        kept = set(int(k) for k in np.asarray(keep)[int(keep_ptr[b]):int(keep_ptr[b + 1])])
+        for k in range(len(offs) - 3):
+            if k not in kept:
+                out[int(offs[k + 1]):int(offs[k + 2])] = True
+    return out
+
+
+def attn_routed(Q, K, V, segment_offsets, seg_ptr, keep_ptr, keep, rows, scale: Optional[float] = None):
+    """Top-B routed attention ([BS] section 5.1, document-level sparse attention): only the kept
+    documents take part.  Row i reads key j iff the prompt rule allows it and j is not a token of
+    a dropped document (the instruction and the query are never dropped).  Dropped documents'
+    own rows are not part of the output; asking for them raises.
+
+    rows: absolute token indices.  Returns (O [R,Hq,d], lse [R,Hq]) in float64.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    dropped = dropped_tokens(segment_offsets, seg_ptr, keep_ptr, keep)
+    if dropped[rows].any():
+        raise ValueError("rows of dropped documents are not computed")
+    Kf, Vf = to_f64(K), to_f64(V)
+    Hkv, d = Kf.shape[1], Kf.shape[2]
+    Hq = np.asarray(Q).shape[1]
+    sc = _scale(d, scale)
+    tables = token_tables(segment_offsets, seg_ptr)
+    prompt = tables[0]
+    so = np.asarray(segment_offsets, dtype=np.int64); sp = np.asarray(seg_ptr, dtype=np.int64)
+    O = np.zeros((len(rows), Hq, d)); lse = np.zeros((len(rows), Hq))
+    for n, i in enumerate(rows):
+        b = int(prompt[i])
+        keys = np.arange(int(so[sp[b]]), int(so[sp[b + 1] - 1]))
+        m = allowed(np.array([i])[:, None], keys[None, :], tables) & ~dropped[keys][None, :]
+        cols = keys[m[0]]
+        qi = to_f64(np.asarray(Q)[i:i + 1])
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            o, l = _masked_softmax_av(qi[:, h], Kf[cols, g], Vf[cols, g], np.ones((1, len(cols)), bool), sc)
+            O[n, h], lse[n, h] = o[0], l[0]
     return O, lse
 
 

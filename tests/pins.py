@@ -402,9 +402,84 @@ def pin_query_attn_isolation(orc):
     assert not np.allclose(O[qo[1] - corpus:qo[2] - corpus], O2[qo[1] - corpus:qo[2] - corpus])
 
 
+# --------------------------------------------------------------------------------------
+# top-B routing (BlockSearch section 5.1)
+# --------------------------------------------------------------------------------------
+def _routing_case(seed):
+    rng = random.Random(seed)
+    prompts = random_prompts(rng, batch=2, p_max=12, n_max=6, l_max=20, q_max=9, p_min=1)
+    w = workloads.make_custom(prompts, 4, 2, 8, 1, seed)
+    keep_ptr, keep = [0], []
+    for (_, lens, _) in prompts:
+        ks = sorted(rng.sample(range(len(lens)), rng.randint(0, len(lens))))
+        rng.shuffle(ks)
+        keep += ks
+        keep_ptr.append(len(keep))
+    return w, prompts, np.array(keep_ptr), np.array(keep, dtype=np.int64)
+
+
+def _computed_rows(w, keep_ptr, keep, orc):
+    dropped = orc.dropped_tokens(w.segment_offsets, w.seg_ptr, keep_ptr, keep)
+    return np.nonzero(~dropped)[0]
+
+
+def pin_routing_keep_all(orc):
+    """Keeping every document is the unrouted prompt."""
+    w = small_case(401, hq=4, hkv=2, d=8, batch=2)
+    n_docs = [int(w.seg_ptr[b + 1] - w.seg_ptr[b] - 3) for b in range(w.num_prompts)]
+    keep_ptr = np.cumsum([0] + n_docs); keep = np.concatenate([np.arange(n)[::-1] for n in n_docs])
+    rows = np.arange(int(w.segment_offsets[-1]))
+    O, lse = orc.attn_routed(w.Q, w.K, w.V, w.segment_offsets, w.seg_ptr, keep_ptr, keep, rows)
+    O2, lse2 = orc.attn_rows(w.Q, w.K, w.V, w.segment_offsets, w.seg_ptr)
+    np.testing.assert_allclose(O, O2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse2, rtol=0, atol=1e-12)
+
+
+def pin_routing_is_compaction(orc):
+    """Routing equals dropping the documents from the prompt: gather the instruction, the kept
+    documents (in prompt order) and the query into a shorter prompt and run the prompt oracle."""
+    for seed in range(3):
+        w, prompts, keep_ptr, keep = _routing_case(500 + seed)
+        so = [int(x) for x in w.segment_offsets]; sp = [int(x) for x in w.seg_ptr]
+        gather, new_offs, new_ptr = [], [], [0]
+        for b, (p, lens, q) in enumerate(prompts):
+            offs = so[sp[b]:sp[b + 1]]
+            kept = set(int(k) for k in keep[keep_ptr[b]:keep_ptr[b + 1]])
+            docs = [k for k in range(len(lens)) if k in kept]
+            if not docs:
+                continue  # a prompt needs at least one document; check it below by rows only
+            base = len(gather)
+            seg = [(offs[0], offs[1])] + [(offs[k + 1], offs[k + 2]) for k in docs] + [(offs[-2], offs[-1])]
+            cur = base
+            new_offs.append(cur)
+            for a, e in seg:
+                gather.extend(range(a, e)); cur += e - a; new_offs.append(cur)
+            new_ptr.append(len(new_offs))
+        if not gather:
+            continue
+        g = np.array(gather)
+        O_c, _ = orc.attn_rows(w.Q[g], w.K[g], w.V[g], np.array(new_offs), np.array(new_ptr))
+        O_r, _ = orc.attn_routed(w.Q, w.K, w.V, w.segment_offsets, w.seg_ptr, keep_ptr, keep, g)
+        np.testing.assert_allclose(O_r, O_c, rtol=0, atol=1e-12)
+
+
+def pin_routing_ignores_dropped(orc):
+    """Dropped documents' keys and values change no computed row."""
+    w, prompts, keep_ptr, keep = _routing_case(600)
+    rows = _computed_rows(w, keep_ptr, keep, orc)
+    O, _ = orc.attn_routed(w.Q, w.K, w.V, w.segment_offsets, w.seg_ptr, keep_ptr, keep, rows)
+    dropped = orc.dropped_tokens(w.segment_offsets, w.seg_ptr, keep_ptr, keep)
+    assert dropped.any()
+    K2, V2 = w.K.copy(), w.V.copy()
+    K2[dropped] ^= np.uint16(0x0100); V2[dropped] ^= np.uint16(0x0100)
+    O2, _ = orc.attn_routed(w.Q, K2, V2, w.segment_offsets, w.seg_ptr, keep_ptr, keep, rows)
+    np.testing.assert_array_equal(O, O2)
+
+
 ALL_PINS = [
     pin_closed_form_counts, pin_worked_example, pin_textbook_rows, pin_textbook_rows_no_prefix,
     pin_bruteforce_chunked, pin_special_rows, pin_document_isolation, pin_readout_bruteforce,
     pin_readout_mass, pin_readout_uniform, pin_readout_permutation, pin_rank_bruteforce,
     pin_query_attn_no_corpus, pin_query_attn_is_prompt_query_rows, pin_query_attn_isolation,
+    pin_routing_keep_all, pin_routing_is_compaction, pin_routing_ignores_dropped,
 ]

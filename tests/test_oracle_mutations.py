@@ -185,6 +185,31 @@ def _query_skips_corpus(Q, K, V, corpus_len, query_offsets, scale=None):
 _real_query_attn = orc.query_attn
 
 
+def _routing_reads_dropped(Q, K, V, so, sp, keep_ptr, keep, rows, scale=None):
+    """query rows still read the dropped documents (routing ignored)"""
+    return orc.attn_rows(Q, K, V, so, sp, rows=rows, scale=scale)
+
+
+def _routing_drops_everything(Q, K, V, so, sp, keep_ptr, keep, rows, scale=None):
+    """the query reads no document at all (the kept list ignored for its keys)"""
+    rows = np.asarray(rows, dtype=np.int64)
+    kind = orc.token_tables(so, sp)[2]
+    O, lse = _real_attn_routed(Q, K, V, so, sp, keep_ptr, keep, rows, scale)
+    qrows = rows[kind[rows] == orc.KIND_Q]
+    if len(qrows):
+        n = len(np.asarray(sp)) - 1
+        # a keep list that keeps nothing, applied to the query rows only
+        o2, l2 = _real_attn_routed(Q, K, V, so, sp, np.zeros(n + 1, dtype=np.int64), np.zeros(0, dtype=np.int64),
+                                   qrows, scale)
+        sel = kind[rows] == orc.KIND_Q
+        O[sel], lse[sel] = o2, l2
+    return O, lse
+
+
+_real_attn_routed = orc.attn_routed
+
+
+
 MUTATIONS = {
     "mask_no_causal": ("allowed", _no_causal),
     "mask_docs_skip_prefix": ("allowed", _docs_skip_prefix),
@@ -205,6 +230,8 @@ MUTATIONS = {
     "query_no_causal": ("query_attn", _query_no_causal),
     "query_reads_previous_queries": ("query_attn", _query_reads_previous_queries),
     "query_skips_corpus": ("query_attn", _query_skips_corpus),
+    "routing_reads_dropped": ("attn_routed", _routing_reads_dropped),
+    "routing_drops_everything": ("attn_routed", _routing_drops_everything),
 }
 
 
