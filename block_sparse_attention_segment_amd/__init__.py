@@ -5,10 +5,12 @@ The Python layer only marshals arguments to libblockrank.so; all computation run
 hand-written HIP kernels.
 """
 from ._lib import (BlockRankError, BrDims, EXPORTED, LIB_PATH, attn_fwd, attn_plan_items, attn_plan_schedule,
+                   attn_routed, attn_routed_workspace_bytes,
                    attn_workspace_bytes, doc_scores, doc_scores_workspace_bytes, load_library,
                    make_dims, query_attn, query_attn_workspace_bytes, sort_docs, version)
 
 __all__ = ["BlockRankError", "BrDims", "EXPORTED", "LIB_PATH", "attn_fwd", "attn_plan_items", "attn_plan_schedule",
+           "attn_routed", "attn_routed_workspace_bytes",
            "attn_workspace_bytes", "doc_scores", "doc_scores_workspace_bytes", "load_library",
            "make_dims", "query_attn", "query_attn_workspace_bytes", "sort_docs", "version", "rank_prompts"]
 

@@ -19,7 +19,7 @@ BR_OK, BR_ERR_INVALID_ARG, BR_ERR_UNSUPPORTED, BR_ERR_WORKSPACE, BR_ERR_HIP = ra
 
 # Symbols the header declares; the CPU test checks the library exports each of them.
 EXPORTED = ("br_attn_workspace_bytes", "br_attn_fwd", "br_attn_fwd_timed", "br_doc_scores_workspace_bytes", "br_doc_scores",
-            "br_sort_docs", "br_attn_plan_items", "br_attn_plan_schedule", "br_query_attn_workspace_bytes", "br_query_attn_fwd", "br_status_string", "br_last_error", "br_version")
+            "br_sort_docs", "br_attn_plan_items", "br_attn_plan_schedule", "br_query_attn_workspace_bytes", "br_query_attn_fwd", "br_attn_routed_workspace_bytes", "br_attn_routed_fwd", "br_status_string", "br_last_error", "br_version")
 
 
 class BrDims(ctypes.Structure):
@@ -63,6 +63,9 @@ def load_library() -> ctypes.CDLL:
         "br_sort_docs": [_P, _I32P, ctypes.c_int32, _P, _P],
         "br_attn_plan_items": [dims_p, _I32P, _I32P, _I32P, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64),
                                ctypes.POINTER(ctypes.c_int32)],
+        "br_attn_routed_workspace_bytes": [dims_p, _I32P, _I32P, _I32P, _I32P, ctypes.POINTER(ctypes.c_size_t)],
+        "br_attn_routed_fwd": [dims_p, _P, _P, _P, _I32P, _I32P, _I32P, _I32P, _P, _P, ctypes.c_float, _P, ctypes.c_size_t,
+                               _P],
         "br_query_attn_workspace_bytes": [dims_p, ctypes.c_int32, _I32P, ctypes.POINTER(ctypes.c_size_t)],
         "br_query_attn_fwd": [dims_p, _P, _P, _P, ctypes.c_int32, _I32P, _P, _P, ctypes.c_float, _P, ctypes.c_size_t, _P],
         "br_attn_plan_schedule": [dims_p, _I32P, _I32P, ctypes.c_int32, _I32P, ctypes.c_int64, _I32P, ctypes.c_int64,
@@ -188,6 +191,49 @@ def attn_fwd(Q, K, V, segment_offsets, seg_ptr, out=None, lse=None, softmax_scal
     _check(lib.br_attn_fwd_timed(ctypes.byref(dims), Q.data_ptr(), K.data_ptr(), V.data_ptr(), _ptr_i32(so),
                                  _ptr_i32(sp), out.data_ptr(), _dev_ptr(lse), float(softmax_scale),
                                  workspace.data_ptr(), workspace.numel(), _stream_handle(stream), ev0, ev1))
+    return (out, lse) if lse is not None else out
+
+
+def attn_routed_workspace_bytes(dims: BrDims, segment_offsets, seg_ptr, keep_ptr, keep) -> int:
+    lib = load_library()
+    so, sp, kp, kk = _host_i32(segment_offsets), _host_i32(seg_ptr), _host_i32(keep_ptr), _host_i32(keep)
+    out = ctypes.c_size_t(0)
+    _check(lib.br_attn_routed_workspace_bytes(ctypes.byref(dims), _ptr_i32(so), _ptr_i32(sp), _ptr_i32(kp),
+                                              _ptr_i32(kk), ctypes.byref(out)))
+    return int(out.value)
+
+
+def attn_routed(Q, K, V, segment_offsets, seg_ptr, keep_ptr, keep, out=None, lse=None, softmax_scale: float = 0.0,
+                workspace=None, stream=None):
+    """Top-B routed attention: prompt b keeps documents keep[keep_ptr[b]:keep_ptr[b+1]] (local
+    indices); dropped documents' rows are not computed (out rows left as they were) and the final
+    query reads only the instruction and the kept documents.  Shapes as attn_fwd."""
+    import torch
+    lib = load_library()
+    for name, t in (("Q", Q), ("K", K), ("V", V)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 3:
+            raise ValueError(f"{name} must be a contiguous 3-D bfloat16 CUDA tensor")
+    T, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    if K.shape != (T, Hkv, d) or V.shape != K.shape:
+        raise ValueError("K and V must be [T, Hkv, d] matching Q")
+    so, sp, kp, kk = _host_i32(segment_offsets), _host_i32(seg_ptr), _host_i32(keep_ptr), _host_i32(keep)
+    if kk.size == 0:
+        kk = np.zeros(1, dtype=np.int32)  # a valid pointer; keep_ptr says no document is kept
+    dims = make_dims(len(sp) - 1, Hq, Hkv, d, T)
+    if out is None:
+        out = torch.zeros_like(Q)
+    if lse is True:
+        lse = torch.zeros((T, Hq), dtype=torch.float32, device=Q.device)
+    elif lse is False:
+        lse = None
+    nbytes = attn_routed_workspace_bytes(dims, so, sp, kp, kk)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+    _check(lib.br_attn_routed_fwd(ctypes.byref(dims), Q.data_ptr(), K.data_ptr(), V.data_ptr(), _ptr_i32(so),
+                                  _ptr_i32(sp), _ptr_i32(kp), _ptr_i32(kk), out.data_ptr(), _dev_ptr(lse),
+                                  float(softmax_scale), workspace.data_ptr(), workspace.numel(),
+                                  _stream_handle(stream)))
     return (out, lse) if lse is not None else out
 
 

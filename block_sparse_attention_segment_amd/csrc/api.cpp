@@ -386,6 +386,37 @@ br_status br_attn_fwd_timed(const br_dims* dims, const void* Q, const void* K, c
   });
 }
 
+br_status br_attn_routed_workspace_bytes(const br_dims* dims, const int32_t* segment_offsets, const int32_t* seg_ptr,
+                                         const int32_t* keep_ptr, const int32_t* keep, size_t* bytes) {
+  return guarded([&]() -> br_status {
+    if (!bytes) return record(BR_ERR_INVALID_ARG, "bytes is NULL");
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    br::AttnPlan plan;
+    e = br::build_routed_plan(*dims, segment_offsets, seg_ptr, keep_ptr, keep, &plan);
+    if (!e.ok()) return record(e);
+    *bytes = plan.total_bytes;
+    return BR_OK;
+  });
+}
+
+br_status br_attn_routed_fwd(const br_dims* dims, const void* Q, const void* K, const void* V,
+                             const int32_t* segment_offsets, const int32_t* seg_ptr, const int32_t* keep_ptr,
+                             const int32_t* keep, void* out, float* lse, float softmax_scale, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  return guarded([&]() -> br_status {
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    br_status st = check_attn_buffers(Q, K, V, out, lse, softmax_scale);
+    if (st != BR_OK) return st;
+    br::AttnPlan plan;
+    e = br::build_routed_plan(*dims, segment_offsets, seg_ptr, keep_ptr, keep, &plan);
+    if (!e.ok()) return record(e);
+    return run_attn(*dims, plan, Q, K, V, out, lse, softmax_scale, workspace, workspace_bytes, stream, 0, nullptr,
+                    nullptr);
+  });
+}
+
 br_status br_query_attn_workspace_bytes(const br_dims* dims, int32_t corpus_len, const int32_t* query_offsets,
                                         size_t* bytes) {
   return guarded([&]() -> br_status {

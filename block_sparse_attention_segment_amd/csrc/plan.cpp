@@ -14,6 +14,7 @@
 #include <functional>
 #include <queue>
 #include <utility>
+#include <vector>
 
 namespace br {
 namespace {
@@ -100,27 +101,37 @@ void init_plan(const br_dims& dims, int64_t max_unmasked, AttnPlan* plan, ItemMa
   *mk = ItemMaker{P.rows_per_tile, kKeyTile, P.chunk_keys};
 }
 
-// Query rows [qs, qe): keys [u0, u1) unmasked (split into chunks merged afterwards when longer
-// than one chunk), then the query's own tokens [qs, row] causally.
-void add_query_rows(int64_t qs, int64_t qe, int64_t u0, int64_t u1, const ItemMaker& mk, AttnPlan* plan,
-                    std::vector<AttnItem>* out) {
+// Query rows [qs, qe): the keys of `ranges` unmasked (each range split into chunks of at most
+// CK keys; partials merged afterwards when there is more than one chunk), then the query's own
+// tokens [qs, row] causally (attached to the last chunk).
+void add_query_rows(int64_t qs, int64_t qe, const std::vector<std::pair<int64_t, int64_t>>& ranges,
+                    const ItemMaker& mk, AttnPlan* plan, std::vector<AttnItem>* out) {
   AttnPlan& P = *plan;
+  std::vector<std::pair<int64_t, int64_t>> chunks;
+  for (const auto& r : ranges)
+    for (int64_t a = r.first; a < r.second; a += mk.CK) chunks.push_back({a, std::min(a + mk.CK, r.second)});
   for (int64_t r0 = qs; r0 < qe; r0 += mk.TM) {
     const int64_t b1 = std::min(r0 + mk.TM, qe);
-    const int64_t nchunk = std::max<int64_t>(1, cdiv(u1 - u0, mk.CK));
-    if (nchunk == 1) {
-      out->push_back(mk(r0, qe, u0, u1, qs, b1, -1));
+    if (chunks.size() <= 1) {
+      const int64_t a0 = chunks.empty() ? 0 : chunks[0].first, a1 = chunks.empty() ? 0 : chunks[0].second;
+      out->push_back(mk(r0, qe, a0, a1, qs, b1, -1));
       continue;
     }
     const int32_t slot0 = P.n_slots;
-    for (int64_t c = 0; c < nchunk; ++c) {
-      const int64_t a0 = u0 + c * mk.CK, a1 = std::min(u0 + (c + 1) * mk.CK, u1);
-      const bool last = c == nchunk - 1;
-      out->push_back(mk(r0, qe, a0, a1, last ? qs : 0, last ? b1 : 0, slot0 + int32_t(c)));
+    for (size_t c = 0; c < chunks.size(); ++c) {
+      const bool last = c + 1 == chunks.size();
+      out->push_back(mk(r0, qe, chunks[c].first, chunks[c].second, last ? qs : 0, last ? b1 : 0, slot0 + int32_t(c)));
     }
-    P.merges.push_back(MergeItem{int32_t(r0), int32_t(qe), slot0, int32_t(nchunk)});
-    P.n_slots += int32_t(nchunk);
+    P.merges.push_back(MergeItem{int32_t(r0), int32_t(qe), slot0, int32_t(chunks.size())});
+    P.n_slots += int32_t(chunks.size());
   }
+}
+
+void add_query_rows(int64_t qs, int64_t qe, int64_t u0, int64_t u1, const ItemMaker& mk, AttnPlan* plan,
+                    std::vector<AttnItem>* out) {
+  std::vector<std::pair<int64_t, int64_t>> ranges;
+  if (u1 > u0) ranges.push_back({u0, u1});
+  add_query_rows(qs, qe, ranges, mk, plan, out);
 }
 
 // Workspace layout and the default schedule.
@@ -217,6 +228,85 @@ Error build_query_plan(const br_dims& dims, int32_t corpus_len, const int32_t* q
   std::stable_sort(query_items.begin(), query_items.end(),
                    [](const AttnItem& x, const AttnItem& y) { return x.a_start < y.a_start; });
   plan->items = std::move(query_items);
+  finish_plan(dims, plan);
+  return {};
+}
+
+Error validate_keep(const br_dims& dims, const int32_t* so, const int32_t* sp, const int32_t* keep_ptr,
+                    const int32_t* keep) {
+  if (!keep_ptr || !keep) return fail(BR_ERR_INVALID_ARG, "keep_ptr and keep must be non-NULL host arrays");
+  if (keep_ptr[0] != 0) return fail(BR_ERR_INVALID_ARG, "keep_ptr[0] must be 0 (got %lld)", keep_ptr[0]);
+  for (int b = 0; b < dims.num_prompts; ++b) {
+    const int64_t n_docs = int64_t(sp[b + 1]) - sp[b] - 3;
+    const int64_t k0 = keep_ptr[b], k1 = keep_ptr[b + 1];
+    if (k1 < k0) return fail(BR_ERR_INVALID_ARG, "keep_ptr decreases at prompt %lld", b);
+    std::vector<char> seen(size_t(n_docs), 0);
+    for (int64_t k = k0; k < k1; ++k) {
+      const int32_t doc = keep[k];
+      if (doc < 0 || doc >= n_docs)
+        return fail(BR_ERR_INVALID_ARG, "prompt %lld: kept document %lld out of range [0, %lld)", b, doc, n_docs);
+      if (seen[size_t(doc)]) return fail(BR_ERR_INVALID_ARG, "prompt %lld: document %lld kept twice", b, doc);
+      seen[size_t(doc)] = 1;
+    }
+  }
+  return {};
+}
+
+Error build_routed_plan(const br_dims& dims, const int32_t* so, const int32_t* sp, const int32_t* keep_ptr,
+                        const int32_t* keep, AttnPlan* plan) {
+  Error e = validate_dims(&dims);
+  if (!e.ok()) return e;
+  e = validate_segments(dims, so, sp);
+  if (!e.ok()) return e;
+  e = validate_keep(dims, so, sp, keep_ptr, keep);
+  if (!e.ok()) return e;
+
+  // Per prompt: the unmasked key ranges of the query rows (instruction plus kept documents, runs
+  // of adjacent spans merged) and their longest total, which sizes the chunks.
+  std::vector<std::vector<std::pair<int64_t, int64_t>>> qranges(size_t(dims.num_prompts));
+  std::vector<std::vector<char>> kept(size_t(dims.num_prompts));
+  int64_t max_unmasked = 0;
+  for (int b = 0; b < dims.num_prompts; ++b) {
+    const int32_t* o = so + sp[b];
+    const int n = sp[b + 1] - sp[b];
+    kept[size_t(b)].assign(size_t(n - 3), 0);
+    for (int64_t k = keep_ptr[b]; k < keep_ptr[b + 1]; ++k) kept[size_t(b)][size_t(keep[k])] = 1;
+    auto& rs = qranges[size_t(b)];
+    auto add = [&](int64_t a, int64_t z) {
+      if (z <= a) return;
+      if (!rs.empty() && rs.back().second == a)
+        rs.back().second = z;
+      else
+        rs.push_back({a, z});
+    };
+    add(o[0], o[1]);
+    for (int k = 1; k <= n - 3; ++k)
+      if (kept[size_t(b)][size_t(k - 1)]) add(o[k], o[k + 1]);
+    int64_t tot = 0;
+    for (const auto& r : rs) tot += r.second - r.first;
+    max_unmasked = std::max(max_unmasked, tot);
+  }
+  ItemMaker mk{};
+  init_plan(dims, max_unmasked, plan, &mk);
+  const int64_t TM = mk.TM;
+  std::vector<AttnItem> query_items, other_items;
+  for (int b = 0; b < dims.num_prompts; ++b) {
+    const int32_t* o = so + sp[b];
+    const int n = sp[b + 1] - sp[b];
+    const int64_t ps = o[0], pe = o[1], qs = o[n - 2], qe = o[n - 1];
+    for (int64_t r0 = ps; r0 < pe; r0 += TM) other_items.push_back(mk(r0, pe, 0, 0, ps, std::min(r0 + TM, pe), -1));
+    for (int k = 1; k <= n - 3; ++k) {
+      if (!kept[size_t(b)][size_t(k - 1)]) continue;  // dropped documents' rows are not computed
+      const int64_t ds = o[k], de = o[k + 1];
+      const int64_t ntile = cdiv(de - ds, TM);
+      for (int64_t t = ntile - 1; t >= 0; --t) {
+        const int64_t r0 = ds + t * TM;
+        other_items.push_back(mk(r0, de, ps, pe, ds, std::min(r0 + TM, de), -1));
+      }
+    }
+    add_query_rows(qs, qe, qranges[size_t(b)], mk, plan, &query_items);
+  }
+  order_items(std::move(query_items), other_items, plan);
   finish_plan(dims, plan);
   return {};
 }

@@ -88,6 +88,13 @@ Error build_attn_plan(const br_dims& dims, const int32_t* segment_offsets, const
 // corpus unmasked plus its own tokens causally.
 Error validate_queries(const br_dims& dims, int32_t corpus_len, const int32_t* query_offsets);
 Error build_query_plan(const br_dims& dims, int32_t corpus_len, const int32_t* query_offsets, AttnPlan* plan);
+// Top-B routing: prompt b keeps documents keep[keep_ptr[b] .. keep_ptr[b + 1]) (local indices).
+// Kept documents' rows are computed as in build_attn_plan; dropped documents' rows are not
+// computed; query rows read the instruction and the kept documents unmasked, then themselves.
+Error validate_keep(const br_dims& dims, const int32_t* segment_offsets, const int32_t* seg_ptr,
+                    const int32_t* keep_ptr, const int32_t* keep);
+Error build_routed_plan(const br_dims& dims, const int32_t* segment_offsets, const int32_t* seg_ptr,
+                        const int32_t* keep_ptr, const int32_t* keep, AttnPlan* plan);
 // Partition the item list over the persistent workgroups of each KV head.  `workgroups` = the
 // device's persistent workgroup slots (CUs x kAttnWgPerCu); it shapes only the partition, never
 // the items or the workspace size.  Calling it again re-partitions from `items`.

@@ -144,6 +144,25 @@ br_status br_sort_docs(const float* scores, const int32_t* doc_ptr, int32_t num_
                        int32_t* order, hipStream_t stream);
 
 /*
+ * Top-B routed attention (BlockSearch, section 5.1 "Document-level sparse attention": only the
+ * top-B documents by score take part in attention from the routing layer on).  Prompt b keeps
+ * the documents keep[keep_ptr[b] .. keep_ptr[b + 1]) (HOST int32 local indices 0..N_b-1, each at
+ * most once, any order; keep_ptr: HOST int32[B + 1], keep_ptr[0] == 0).  Instruction rows and
+ * kept documents' rows are computed as in br_attn_fwd; dropped documents' rows are not
+ * computed (their out and lse rows are left untouched); final-query rows read the instruction
+ * and the kept documents unmasked and the query causally.  Keeping every document gives
+ * exactly br_attn_fwd's result.  Other arguments and rules as br_attn_fwd.
+ */
+br_status br_attn_routed_workspace_bytes(const br_dims* dims, const int32_t* segment_offsets,
+                                         const int32_t* seg_ptr, const int32_t* keep_ptr,
+                                         const int32_t* keep, size_t* bytes);
+br_status br_attn_routed_fwd(const br_dims* dims, const void* Q, const void* K, const void* V,
+                             const int32_t* segment_offsets, const int32_t* seg_ptr,
+                             const int32_t* keep_ptr, const int32_t* keep, void* out, float* lse,
+                             float softmax_scale, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/*
  * Query-only attention over a cached corpus ("prefill once, score many queries"; BlockSearch,
  * section 3.2: the query block attends over the full corpus and causally to itself).
  * The key/value token axis holds the corpus [0, corpus_len) (e.g. an instruction and its

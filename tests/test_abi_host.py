@@ -257,3 +257,26 @@ def test_query_attn_rejects_before_any_hip_call():
     assert st == br._lib.BR_ERR_INVALID_ARG
     st = lib.br_query_attn_fwd(ctypes.byref(dims), f, f, f, 64, p(qo), f, None, float("inf"), f, need, None)
     assert st == br._lib.BR_ERR_INVALID_ARG
+
+
+# ---- top-B routed attention (host side only) ----
+def test_routed_workspace_and_bad_keep():
+    seg, sp, _, _ = workloads.segment_tables([(8, [16, 12, 20], 8), (4, [10, 10], 6)])
+    dims = br.make_dims(2, 8, 2, 64, int(seg[-1]))
+    ok = br.attn_routed_workspace_bytes(dims, seg, sp, [0, 2, 3], [2, 0, 1])
+    assert ok > 0
+    # keeping every document sizes like the unrouted plan
+    assert br.attn_routed_workspace_bytes(dims, seg, sp, [0, 3, 5], [0, 1, 2, 0, 1]) == \
+        br.attn_workspace_bytes(dims, seg, sp)
+    # no document kept anywhere is valid
+    assert br.attn_routed_workspace_bytes(dims, seg, sp, [0, 0, 0], [0]) > 0
+    bad = [
+        ([0, 2, 3], [2, 3, 1]),   # document index out of range
+        ([0, 2, 3], [1, 1, 0]),   # kept twice
+        ([1, 2, 3], [0, 1, 0]),   # keep_ptr[0] != 0
+        ([0, 2, 1], [0, 1, 0]),   # keep_ptr decreases
+    ]
+    for kp, kk in bad:
+        with pytest.raises(br.BlockRankError) as ei:
+            br.attn_routed_workspace_bytes(dims, seg, sp, kp, kk)
+        assert ei.value.status == br._lib.BR_ERR_INVALID_ARG, (kp, kk)
