@@ -36,6 +36,17 @@ Readings taken where the pages are silent or disagree (each also listed in the d
     each query reads the whole corpus unmasked and its own tokens causally, never another
     query's tokens; the corpus is whatever precedes the queries (for BlockRank, the
     instruction and the documents).
+  * SSMax ([BS] 5.1, length-aware softmax): the pre-softmax scores q.k/sqrt(d) are multiplied
+    by s * ln N, N the number of documents of the prompt, natural logarithm; the same factor
+    serves every attention row of the prompt and the readout, whose weights are the softmax
+    of those scores.
+  * Position ids ([BR] 3.4 "Permutation-invariant position embeddings"): instruction token i
+    at i, token j of every document at p + j (p = instruction length), query token i at
+    8192 + i.  [BS] 3.2 variant: document positions restart at 0 and the query starts at 300.
+  * RoPE (RoFormer, cited by [BS] 3.2; Mistral uses it per the BlockRank analysis page): pair k
+    of a head vector turns by pos * theta^(-2k/d).  Two pairings exist in practice, adjacent
+    entries (2k, 2k+1) as in RoFormer's definition, or halves (k, k + d/2) as in the GPT-NeoX
+    layout; both are provided.  The base theta is not on the pages: a parameter.
 """
 from __future__ import annotations
 
@@ -292,6 +303,80 @@ def attn_routed(Q, K, V, segment_offsets, seg_ptr, keep_ptr, keep, rows, scale: 
             o, l = _masked_softmax_av(qi[:, h], Kf[cols, g], Vf[cols, g], np.ones((1, len(cols)), bool), sc)
             O[n, h], lse[n, h] = o[0], l[0]
     return O, lse
+
+
+# --------------------------------------------------------------------------------------
+# length-aware softmax scaling ([BS] section 5.1, SSMax)
+# --------------------------------------------------------------------------------------
+def ssmax_scale(s: float, n_docs: int, head_dim: int) -> float:
+    """Factor on q.k under SSMax: the pre-softmax score q.k / sqrt(d) times s * ln N.
+
+    N = n_docs, the corpus size in documents ([BS] 5.1 multiplies by s log N so that a gold
+    document scoring Delta above N distractors keeps weight 1 / (1 + N^(1 - s Delta)))."""
+    if n_docs < 1 or head_dim < 1:
+        raise ValueError("n_docs and head_dim must be positive")
+    return float(s) * math.log(n_docs) / math.sqrt(head_dim)
+
+
+# --------------------------------------------------------------------------------------
+# permutation-invariant positions and rotary embedding ([BR] 3.4; [BS] 3.2)
+# --------------------------------------------------------------------------------------
+def rope_positions(segment_offsets, seg_ptr, query_pos0: int = 8192,
+                   docs_after_instruction: bool = True) -> np.ndarray:
+    """Position id of every token ([BR] 3.4 "Permutation-invariant position embeddings").
+
+    Instruction token i -> i.  Token j of any document -> j + p when docs_after_instruction
+    (p = the prompt's instruction length, so every document starts at p whatever its place in
+    the list), else j ([BS] 3.2: positions reset at each document start).  Query token i ->
+    query_pos0 + i (8192 in [BR]; 300 in [BS]).  Returns int64 [T]."""
+    so = np.asarray(segment_offsets, dtype=np.int64); sp = np.asarray(seg_ptr, dtype=np.int64)
+    pos = np.full(int(so[sp[-1] - 1]), -1, dtype=np.int64)
+    for b in range(len(sp) - 1):
+        offs = [int(x) for x in so[sp[b]:sp[b + 1]]]
+        p = offs[1] - offs[0]
+        for t in range(offs[0], offs[1]):                      # instruction
+            pos[t] = t - offs[0]
+        for k in range(1, len(offs) - 2):                      # documents d_1 .. d_N
+            for t in range(offs[k], offs[k + 1]):
+                pos[t] = (t - offs[k]) + (p if docs_after_instruction else 0)
+        for t in range(offs[-2], offs[-1]):                    # final query
+            pos[t] = query_pos0 + (t - offs[-2])
+    assert (pos >= 0).all(), "segment table does not cover every token"
+    return pos
+
+
+def rope_pairs(d: int, interleaved: bool) -> Tuple[np.ndarray, np.ndarray]:
+    """Indices (a_k, b_k) of the k-th rotated pair, k = 0..d/2-1."""
+    k = np.arange(d // 2)
+    return (2 * k, 2 * k + 1) if interleaved else (k, k + d // 2)
+
+
+def rope_apply(X, positions, theta: float, interleaved: bool = False) -> np.ndarray:
+    """Rotary embedding of X [R, H, d] at positions [R] in float64.
+
+    Pair k = (a_k, b_k) turns by the angle pos * theta^(-2k/d):
+        a' = a cos - b sin,   b' = a sin + b cos."""
+    Xf = to_f64(X)
+    d = Xf.shape[-1]
+    a_idx, b_idx = rope_pairs(d, interleaved)
+    freq = float(theta) ** (-2.0 * np.arange(d // 2) / d)          # [d/2]
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * freq[None, :]  # [R, d/2]
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    a, b = Xf[..., a_idx], Xf[..., b_idx]
+    out = np.empty_like(Xf)
+    out[..., a_idx] = a * c - b * s
+    out[..., b_idx] = a * s + b * c
+    return out
+
+
+def signal_positions(segment_offsets, seg_ptr, n_signal: int, query_pos0: int = 8192) -> np.ndarray:
+    """Positions of each prompt's last n_signal query tokens (the readout's signal rows), [B, S]."""
+    so = np.asarray(segment_offsets, dtype=np.int64); sp = np.asarray(seg_ptr, dtype=np.int64)
+    out = []
+    for b in range(len(sp) - 1):
+        qlen = int(so[sp[b + 1] - 1] - so[sp[b + 1] - 2])
+        out.append(query_pos0 + np.arange(qlen - n_signal, qlen))
+    return np.asarray(out, dtype=np.int64)
 
 
 # --------------------------------------------------------------------------------------

@@ -476,10 +476,128 @@ def pin_routing_ignores_dropped(orc):
     np.testing.assert_array_equal(O, O2)
 
 
+# --------------------------------------------------------------------------------------
+# SSMax ([BS] section 5.1): scores times s * ln N
+# --------------------------------------------------------------------------------------
+def pin_ssmax_gold_weight(orc):
+    """[BS] 5.2: under SSMax a gold key scoring Delta above N equal distractors gets weight
+    1 / (1 + N^(1 - s Delta)).  Built as one query token over a corpus of one gold key and
+    N - 1 distractors (its own key is the N-th distractor); V marks the gold key."""
+    d = 4
+    for n, s, delta in [(10, 0.43, 1.0), (100, 0.43, 2.5), (1000, 0.43, 4.0), (500, 0.2, 3.0), (2, 1.0, 0.5)]:
+        K = np.zeros((n + 1, 1, d)); V = np.zeros((n + 1, 1, d))
+        gold = n // 2
+        K[gold, 0, 0] = delta
+        V[gold, 0, 0] = 1.0
+        Q = np.zeros((1, 1, d)); Q[0, 0, 0] = math.sqrt(d)          # q.k / sqrt(d) = k[0]
+        O, _ = orc.query_attn(Q, K, V, n, [n, n + 1], scale=orc.ssmax_scale(s, n, d))
+        want = 1.0 / (1.0 + n ** (1.0 - s * delta))
+        assert abs(O[0, 0, 0] - want) < 1e-12, (n, s, delta, O[0, 0, 0], want)
+
+
+def pin_ssmax_readout_gold_mass(orc):
+    """The readout under SSMax: one signal row, N one-token documents, the gold one Delta above
+    the rest, so its mass is 1 / (1 + (N - 1) N^(-s Delta)) ([BS] 5.1 scaling applied to the
+    readout's softmax over document tokens)."""
+    d = 4
+    for n, s, delta in [(8, 0.43, 2.0), (300, 0.43, 3.0)]:
+        K = np.zeros((n + 2, 1, d))            # instruction token, n documents, query token
+        gold = 1 + n // 3
+        K[gold, 0, 0] = delta
+        Q_S = np.zeros((1, 1, 1, d)); Q_S[0, 0, 0, 0] = math.sqrt(d)
+        doc_offsets = np.arange(1, n + 2)
+        scores, _ = orc.doc_scores(Q_S, K, doc_offsets, [0, n + 1], scale=orc.ssmax_scale(s, n, d))
+        want = 1.0 / (1.0 + (n - 1) * n ** (-s * delta))
+        assert abs(scores[gold - 1] - want) < 1e-12, (n, scores[gold - 1], want)
+
+
+# --------------------------------------------------------------------------------------
+# permutation-invariant positions and RoPE ([BR] 3.4; [BS] 3.2; RoFormer)
+# --------------------------------------------------------------------------------------
+def pin_rope_positions_golden(orc):
+    """Position ids against the hand-written fixture of the pages' two rules."""
+    with open(os.path.join(GOLDEN, "rope_positions.json")) as f:
+        g = json.load(f)
+    for key in ("blockrank", "blocksearch"):
+        r = g[key]
+        got = orc.rope_positions(g["segment_offsets"], g["seg_ptr"], r["query_pos0"], r["docs_after_instruction"])
+        assert got.tolist() == r["positions"], (key, got.tolist())
+
+
+def pin_rope_rotation_values(orc):
+    """Rotation by a known angle.  d = 2: the unit vector (1, 0) at position m becomes
+    (cos m, sin m).  d = 4, base 10000: the second pair turns by m * 10000^(-1/2), so exactly
+    one radian at m = 100, while the first pair turns by m radians."""
+    for m in (0, 1, 3, 17):
+        out = orc.rope_apply(np.array([[[1.0, 0.0]]]), [m], 10000.0)
+        assert np.allclose(out[0, 0], [math.cos(m), math.sin(m)], atol=1e-14)
+    for inter in (False, True):
+        x = np.zeros((1, 1, 4))
+        a0, b0 = (0, 1) if inter else (0, 2)
+        a1, b1 = (2, 3) if inter else (1, 3)
+        x[0, 0, a1] = 1.0
+        out = orc.rope_apply(x, [100], 10000.0, interleaved=inter)[0, 0]
+        assert abs(out[a1] - math.cos(1.0)) < 1e-14 and abs(out[b1] - math.sin(1.0)) < 1e-14, (inter, out)
+        assert abs(out[a0]) < 1e-15 and abs(out[b0]) < 1e-15
+        x = np.zeros((1, 1, 4)); x[0, 0, b0] = 1.0                   # (0, 1) on the first pair
+        out = orc.rope_apply(x, [100], 10000.0, interleaved=inter)[0, 0]
+        assert abs(out[a0] + math.sin(100.0)) < 1e-13 and abs(out[b0] - math.cos(100.0)) < 1e-13
+
+
+def pin_rope_relative_position(orc):
+    """RoFormer's defining property: <R(m) q, R(n) k> depends only on n - m, equals
+    <q, R(n - m) k>, and the rotation keeps norms."""
+    rng = np.random.default_rng(5)
+    for d, inter in [(8, False), (8, True), (64, False)]:
+        q = rng.standard_normal((1, 1, d)); k = rng.standard_normal((1, 1, d))
+        for m, n, c in [(3, 7, 100), (8192, 5, -4000), (0, 250, 37)]:
+            rq = lambda x, pos: orc.rope_apply(x, [pos], 10000.0, inter)[0, 0]
+            a = rq(q, m) @ rq(k, n)
+            b = rq(q, m + c) @ rq(k, n + c)
+            e = q[0, 0] @ rq(k, n - m)
+            assert abs(a - b) < 1e-9 and abs(a - e) < 1e-9, (d, inter, m, n, a, b, e)
+            assert abs(np.linalg.norm(rq(q, m)) - np.linalg.norm(q)) < 1e-12
+
+
+def pin_rope_permutation_invariance(orc):
+    """[BR] 3.4: with the shared document position space, a document's representation does not
+    depend on its place in the list.  Rotating Q and K with the prompt's positions and running
+    the block-sparse attention, each document's output rows are the same after the documents
+    are permuted."""
+    rng = np.random.default_rng(9)
+    p, lens, q = 5, [4, 7, 3, 6], 4
+    hq, hkv, d = 2, 1, 8
+    def build(order):
+        offs = [0, p]
+        for k in order:
+            offs.append(offs[-1] + lens[k])
+        offs.append(offs[-1] + q)
+        return offs
+    Xq = {k: rng.standard_normal((lens[k], hq, d)) for k in range(len(lens))}
+    Xk = {k: rng.standard_normal((lens[k], hkv, d)) for k in range(len(lens))}
+    Xv = {k: rng.standard_normal((lens[k], hkv, d)) for k in range(len(lens))}
+    inst = [rng.standard_normal((p, h, d)) for h in (hq, hkv, hkv)]
+    qry = [rng.standard_normal((q, h, d)) for h in (hq, hkv, hkv)]
+    outs = []
+    for order in ([0, 1, 2, 3], [2, 0, 3, 1]):
+        offs = build(order)
+        Q = np.concatenate([inst[0]] + [Xq[k] for k in order] + [qry[0]])
+        K = np.concatenate([inst[1]] + [Xk[k] for k in order] + [qry[1]])
+        V = np.concatenate([inst[2]] + [Xv[k] for k in order] + [qry[2]])
+        pos = orc.rope_positions(offs, [0, len(offs)])
+        O, _ = orc.attn_rows(orc.rope_apply(Q, pos, 10000.0), orc.rope_apply(K, pos, 10000.0), V, offs,
+                             [0, len(offs)], rows=np.arange(offs[-1]))
+        outs.append({k: O[offs[1 + i]:offs[2 + i]] for i, k in enumerate(order)})
+    for k in range(len(lens)):
+        assert np.abs(outs[0][k] - outs[1][k]).max() < 1e-12, k
+
+
 ALL_PINS = [
     pin_closed_form_counts, pin_worked_example, pin_textbook_rows, pin_textbook_rows_no_prefix,
     pin_bruteforce_chunked, pin_special_rows, pin_document_isolation, pin_readout_bruteforce,
     pin_readout_mass, pin_readout_uniform, pin_readout_permutation, pin_rank_bruteforce,
     pin_query_attn_no_corpus, pin_query_attn_is_prompt_query_rows, pin_query_attn_isolation,
     pin_routing_keep_all, pin_routing_is_compaction, pin_routing_ignores_dropped,
+    pin_ssmax_gold_weight, pin_ssmax_readout_gold_mass, pin_rope_positions_golden, pin_rope_rotation_values,
+    pin_rope_relative_position, pin_rope_permutation_invariance,
 ]

@@ -210,6 +210,69 @@ _real_attn_routed = orc.attn_routed
 
 
 
+_real_ssmax = orc.ssmax_scale
+_real_positions = orc.rope_positions
+
+
+def _ssmax_log2(s, n_docs, head_dim):
+    """log base 2 instead of the natural log"""
+    return float(s) * math.log2(n_docs) / math.sqrt(head_dim)
+
+
+def _ssmax_drops_sqrt_d(s, n_docs, head_dim):
+    """s * ln N used as the whole factor on q.k (the 1/sqrt(d) of the scores forgotten)"""
+    return float(s) * math.log(n_docs)
+
+
+def _positions_sequential(segment_offsets, seg_ptr, query_pos0=8192, docs_after_instruction=True):
+    """ordinary sequential positions across each prompt"""
+    so = np.asarray(segment_offsets); sp = np.asarray(seg_ptr)
+    pos = np.zeros(int(so[sp[-1] - 1]), dtype=np.int64)
+    for b in range(len(sp) - 1):
+        a, e = int(so[sp[b]]), int(so[sp[b + 1] - 1])
+        pos[a:e] = np.arange(e - a)
+    return pos
+
+
+def _positions_docs_from_zero(segment_offsets, seg_ptr, query_pos0=8192, docs_after_instruction=True):
+    """documents restart at 0 even under the instruction-offset rule"""
+    return _real_positions(segment_offsets, seg_ptr, query_pos0, False)
+
+
+def _positions_query_off_by_one(segment_offsets, seg_ptr, query_pos0=8192, docs_after_instruction=True):
+    """the query starts one position late"""
+    return _real_positions(segment_offsets, seg_ptr, query_pos0 + 1, docs_after_instruction)
+
+
+def _rope_generic(X, positions, theta, interleaved=False, sign=1.0, expo=2.0, force_half=False):
+    Xf = orc.to_f64(X)
+    d = Xf.shape[-1]
+    k = np.arange(d // 2)
+    a_idx, b_idx = (k, k + d // 2) if (force_half or not interleaved) else (2 * k, 2 * k + 1)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * (float(theta) ** (-expo * k / d))[None, :]
+    c, sn = np.cos(ang)[:, None, :], sign * np.sin(ang)[:, None, :]
+    a, b = Xf[..., a_idx], Xf[..., b_idx]
+    out = np.empty_like(Xf)
+    out[..., a_idx] = a * c - b * sn
+    out[..., b_idx] = a * sn + b * c
+    return out
+
+
+def _rope_sin_sign(X, positions, theta, interleaved=False):
+    """rotation by the negative angle"""
+    return _rope_generic(X, positions, theta, interleaved, sign=-1.0)
+
+
+def _rope_freq_exponent(X, positions, theta, interleaved=False):
+    """frequencies theta^(-k/d) instead of theta^(-2k/d)"""
+    return _rope_generic(X, positions, theta, interleaved, expo=1.0)
+
+
+def _rope_ignores_pairing(X, positions, theta, interleaved=False):
+    """half-split pairs whatever the pairing asked for"""
+    return _rope_generic(X, positions, theta, interleaved, force_half=True)
+
+
 MUTATIONS = {
     "mask_no_causal": ("allowed", _no_causal),
     "mask_docs_skip_prefix": ("allowed", _docs_skip_prefix),
@@ -232,6 +295,14 @@ MUTATIONS = {
     "query_skips_corpus": ("query_attn", _query_skips_corpus),
     "routing_reads_dropped": ("attn_routed", _routing_reads_dropped),
     "routing_drops_everything": ("attn_routed", _routing_drops_everything),
+    "ssmax_log2": ("ssmax_scale", _ssmax_log2),
+    "ssmax_drops_sqrt_d": ("ssmax_scale", _ssmax_drops_sqrt_d),
+    "positions_sequential": ("rope_positions", _positions_sequential),
+    "positions_docs_from_zero": ("rope_positions", _positions_docs_from_zero),
+    "positions_query_off_by_one": ("rope_positions", _positions_query_off_by_one),
+    "rope_sin_sign": ("rope_apply", _rope_sin_sign),
+    "rope_freq_exponent": ("rope_apply", _rope_freq_exponent),
+    "rope_ignores_pairing": ("rope_apply", _rope_ignores_pairing),
 }
 
 
