@@ -248,6 +248,85 @@ def measure_query_only(w, n_queries, q_len, steps, warmup, seed, log):
             "hbm_roofline_frac": round(alg_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)}
 
 
+def measure_routed(w, top_b, steps, warmup, log):
+    """Top-B routed attention on the prompt: the readout ranks the documents, the top_b stay.
+    Times br_attn_routed_fwd calls (plan copy, attention, merge) between events; the ranking
+    and the device-to-host copy of the kept list are outside the timed calls."""
+    import torch
+
+    import block_sparse_attention_segment_amd as br
+
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    Q, K, V, Q_S = dev(w.Q), dev(w.K), dev(w.V), dev(w.Q_S)
+    scores = br.doc_scores(Q_S, K, w.doc_offsets, w.doc_ptr)
+    keep = br.sort_docs(scores, w.doc_ptr)[:top_b].cpu().numpy().astype(np.int64)
+    kp = [0, top_b]
+    Hq, d = w.Q.shape[1], w.Q.shape[2]
+    dims = br.make_dims(1, Hq, w.K.shape[1], d, w.total_tokens)
+    ws = torch.empty(br.attn_routed_workspace_bytes(dims, w.segment_offsets, w.seg_ptr, kp, keep), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty_like(Q)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        br.attn_routed(Q, K, V, w.segment_offsets, w.seg_ptr, kp, keep, out=out, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        br.attn_routed(Q, K, V, w.segment_offsets, w.seg_ptr, kp, keep, out=out, workspace=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # allowed pairs of the routed prompt: drop the other documents and count as for a prompt
+    offs = [int(x) for x in w.segment_offsets]
+    p, q = offs[1] - offs[0], offs[-1] - offs[-2]
+    lens = [offs[k + 2] - offs[k + 1] for k in sorted(int(x) for x in keep)]
+    pairs = p * p + sum(l * l + p * l for l in lens) + q * (p + q + sum(lens))
+    flop = 4.0 * d * Hq * pairs
+    log(f"[bench] routed top-{top_b}: {ms:.4f} ms/call")
+    return {"workload": f"top-{top_b} routing of the long prompt's {w.num_docs} documents by its own readout "
+                        f"(kept documents' rows, instruction and query rows computed)",
+            "ms": round(ms, 5), "allowed_pairs_closed_form": int(pairs),
+            "tflops_allowed_pairs": round(flop / (ms / 1e3) / 1e12, 3),
+            "mfma_peak_frac": round(flop / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+def measure_rope(w, steps, warmup, log):
+    """Rotary embedding of the prompt's Q and K at BlockRank's permutation-invariant positions
+    (out of place).  HBM-bound: every element is read once and written once."""
+    import torch
+
+    import block_sparse_attention_segment_amd as br
+
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    Q, K = dev(w.Q), dev(w.K)
+    Qo, Ko = torch.empty_like(Q), torch.empty_like(K)
+    Hq, d = w.Q.shape[1], w.Q.shape[2]
+    Hkv = w.K.shape[1]
+    dims = br.make_dims(w.num_prompts, Hq, Hkv, d, w.total_tokens)
+    ws = torch.empty(br.rope_workspace_bytes(dims, w.seg_ptr), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    call = lambda: br.rope(Q, K, w.segment_offsets, w.seg_ptr, 10000.0, Q_out=Qo, K_out=Ko, workspace=ws,
+                           stream=stream)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    alg = 2.0 * w.total_tokens * (Hq + Hkv) * d * 2
+    gbps = alg / (ms / 1e3) / 1e9
+    log(f"[bench] rope Q+K: {ms:.4f} ms/call, {gbps:.0f} GB/s")
+    return {"workload": f"RoPE of the long prompt's Q and K ({w.total_tokens} tokens, {Hq} Q / {Hkv} KV heads, d={d}) "
+                        f"at permutation-invariant positions, out of place",
+            "bound": "hbm", "ms": round(ms, 5), "bytes_per_call": alg, "achieved_gbps": round(gbps, 1),
+            "hbm_roofline_frac": round(gbps / PEAK_HBM_GBPS, 4)}
+
+
 def cpu_baseline(w, n_docs_sample, log):
     """Time the fp64 oracle on a bounded sample of the same prompt and scale to the whole step."""
     import oracle.oracle as orc
@@ -290,7 +369,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--secondary", default="worked", help="extra config timed in the same run ('' for none)")
     ap.add_argument("--query-only", type=int, default=1,
-                    help="also time query-only attention over the long prompt's cached corpus (0 to skip)")
+                    help="also time query-only attention over the long prompt's cached corpus, top-256 routed "
+                         "attention and RoPE of Q and K (0 to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-docs", type=int, default=200, help="documents in the CPU oracle's timed sample")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -363,6 +443,8 @@ def main():
                              "attention_kernel_ms": round(r2["kernel_ms"], 5)}
     if args.query_only and args.config == "long":
         line["query_only"] = measure_query_only(w, 16, 32, args.steps, args.warmup, args.seed, log)
+        line["routed"] = measure_routed(w, 256, args.steps, args.warmup, log)
+        line["rope"] = measure_rope(w, args.steps, args.warmup, log)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, args.cpu_docs, log)
         line["cpu_baseline"] = {

@@ -19,7 +19,9 @@ BR_OK, BR_ERR_INVALID_ARG, BR_ERR_UNSUPPORTED, BR_ERR_WORKSPACE, BR_ERR_HIP = ra
 
 # Symbols the header declares; the CPU test checks the library exports each of them.
 EXPORTED = ("br_attn_workspace_bytes", "br_attn_fwd", "br_attn_fwd_timed", "br_doc_scores_workspace_bytes", "br_doc_scores",
-            "br_sort_docs", "br_attn_plan_items", "br_attn_plan_schedule", "br_query_attn_workspace_bytes", "br_query_attn_fwd", "br_attn_routed_workspace_bytes", "br_attn_routed_fwd", "br_status_string", "br_last_error", "br_version")
+            "br_sort_docs", "br_attn_plan_items", "br_attn_plan_schedule", "br_query_attn_workspace_bytes", "br_query_attn_fwd", "br_attn_routed_workspace_bytes", "br_attn_routed_fwd",
+            "br_ssmax_softmax_scale", "br_rope_workspace_bytes", "br_rope_fwd", "br_rope_signal_fwd", "br_rope_positions",
+            "br_status_string", "br_last_error", "br_version")
 
 
 class BrDims(ctypes.Structure):
@@ -68,6 +70,13 @@ def load_library() -> ctypes.CDLL:
                                _P],
         "br_query_attn_workspace_bytes": [dims_p, ctypes.c_int32, _I32P, ctypes.POINTER(ctypes.c_size_t)],
         "br_query_attn_fwd": [dims_p, _P, _P, _P, ctypes.c_int32, _I32P, _P, _P, ctypes.c_float, _P, ctypes.c_size_t, _P],
+        "br_ssmax_softmax_scale": [ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_float)],
+        "br_rope_workspace_bytes": [dims_p, _I32P, sz_p],
+        "br_rope_fwd": [dims_p, _P, _P, _P, _P, _I32P, _I32P, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
+                        ctypes.c_int32, _P, ctypes.c_size_t, _P],
+        "br_rope_signal_fwd": [dims_p, _P, _P, ctypes.c_int32, _I32P, _I32P, ctypes.c_float, ctypes.c_int32,
+                               ctypes.c_int32, _P, ctypes.c_size_t, _P],
+        "br_rope_positions": [dims_p, _I32P, _I32P, ctypes.c_int32, ctypes.c_int32, _I32P, ctypes.c_int64],
         "br_attn_plan_schedule": [dims_p, _I32P, _I32P, ctypes.c_int32, _I32P, ctypes.c_int64, _I32P, ctypes.c_int64,
                                   ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)],
     }
@@ -235,6 +244,98 @@ def attn_routed(Q, K, V, segment_offsets, seg_ptr, keep_ptr, keep, out=None, lse
                                   float(softmax_scale), workspace.data_ptr(), workspace.numel(),
                                   _stream_handle(stream)))
     return (out, lse) if lse is not None else out
+
+
+def ssmax_scale(s: float, n_docs: int, head_dim: int) -> float:
+    """SSMax softmax_scale for a prompt of n_docs documents: s * ln(n_docs) / sqrt(head_dim)."""
+    lib = load_library()
+    out = ctypes.c_float(0.0)
+    _check(lib.br_ssmax_softmax_scale(float(s), int(n_docs), int(head_dim), ctypes.byref(out)))
+    return float(out.value)
+
+
+def rope_workspace_bytes(dims: BrDims, seg_ptr) -> int:
+    lib = load_library()
+    sp = _host_i32(seg_ptr)
+    out = ctypes.c_size_t(0)
+    _check(lib.br_rope_workspace_bytes(ctypes.byref(dims), _ptr_i32(sp), ctypes.byref(out)))
+    return int(out.value)
+
+
+def rope_positions(dims: BrDims, segment_offsets, seg_ptr, query_pos0: int = 8192,
+                   docs_after_instruction: bool = True) -> np.ndarray:
+    """Host-side position ids of every token (int32 [total_tokens])."""
+    lib = load_library()
+    so, sp = _host_i32(segment_offsets), _host_i32(seg_ptr)
+    pos = np.zeros(int(dims.total_tokens), dtype=np.int32)
+    _check(lib.br_rope_positions(ctypes.byref(dims), _ptr_i32(so), _ptr_i32(sp), int(query_pos0),
+                                 int(bool(docs_after_instruction)), _ptr_i32(pos), pos.size))
+    return pos
+
+
+def _check_bf16(name, t, ndim):
+    import torch
+    if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != ndim:
+        raise ValueError(f"{name} must be a contiguous {ndim}-D bfloat16 CUDA tensor")
+
+
+def rope(Q, K, segment_offsets, seg_ptr, rope_theta: float = 10000.0, query_pos0: int = 8192,
+         docs_after_instruction: bool = True, interleaved: bool = False, Q_out=None, K_out=None,
+         inplace: bool = False, workspace=None, stream=None):
+    """Rotary embedding of Q [T, Hq, d] and K [T, Hkv, d] (either may be None) at the prompts'
+    permutation-invariant positions.  Returns (Q_out, K_out); in place when inplace=True."""
+    import torch
+    lib = load_library()
+    if Q is None and K is None:
+        raise ValueError("nothing to rotate")
+    if Q is not None:
+        _check_bf16("Q", Q, 3)
+    if K is not None:
+        _check_bf16("K", K, 3)
+    ref = Q if Q is not None else K
+    T, d = ref.shape[0], ref.shape[2]
+    Hq = Q.shape[1] if Q is not None else K.shape[1]
+    Hkv = K.shape[1] if K is not None else Hq
+    if Q is not None and K is not None and (K.shape[0] != T or K.shape[2] != d):
+        raise ValueError("Q and K must share T and d")
+    so, sp = _host_i32(segment_offsets), _host_i32(seg_ptr)
+    dims = make_dims(len(sp) - 1, Hq, Hkv, d, T)
+    if Q is not None and Q_out is None:
+        Q_out = Q if inplace else torch.empty_like(Q)
+    if K is not None and K_out is None:
+        K_out = K if inplace else torch.empty_like(K)
+    nbytes = rope_workspace_bytes(dims, sp)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=ref.device)
+    _check(lib.br_rope_fwd(ctypes.byref(dims), _dev_ptr(Q), _dev_ptr(K), _dev_ptr(Q_out), _dev_ptr(K_out),
+                           _ptr_i32(so), _ptr_i32(sp), float(rope_theta), int(query_pos0),
+                           int(bool(docs_after_instruction)), int(bool(interleaved)), workspace.data_ptr(),
+                           workspace.numel(), _stream_handle(stream)))
+    return Q_out, K_out
+
+
+def rope_signal(Q_S, segment_offsets, seg_ptr, rope_theta: float = 10000.0, query_pos0: int = 8192,
+                interleaved: bool = False, out=None, inplace: bool = False, num_kv_heads: Optional[int] = None,
+                workspace=None, stream=None):
+    """Rotary embedding of the signal rows Q_S [B, S, Hq, d] at the positions of each prompt's last
+    S query tokens."""
+    import torch
+    lib = load_library()
+    _check_bf16("Q_S", Q_S, 4)
+    B, S, Hq, d = Q_S.shape
+    so, sp = _host_i32(segment_offsets), _host_i32(seg_ptr)
+    if len(sp) != B + 1:
+        raise ValueError("seg_ptr must have B + 1 entries")
+    dims = make_dims(B, Hq, num_kv_heads or Hq, d, int(so[sp[-1] - 1]))
+    if out is None:
+        out = Q_S if inplace else torch.empty_like(Q_S)
+    nbytes = rope_workspace_bytes(dims, sp)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q_S.device)
+    _check(lib.br_rope_signal_fwd(ctypes.byref(dims), Q_S.data_ptr(), out.data_ptr(), int(S), _ptr_i32(so),
+                                  _ptr_i32(sp), float(rope_theta), int(query_pos0), int(bool(interleaved)),
+                                  workspace.data_ptr(), workspace.numel(), _stream_handle(stream)))
+    return out
 
 
 def query_attn_workspace_bytes(dims: BrDims, corpus_len: int, query_offsets) -> int:

@@ -295,6 +295,49 @@ br_status run_attn(const br_dims& dims, br::AttnPlan& plan, const void* Q, const
   return BR_OK;
 }
 
+// Upload a validated rotary-embedding plan into the workspace and launch the rotation.
+br_status run_rope(const br_dims& dims, const int32_t* seg_ptr, const br::RopePlan& plan, const void* Q, void* Q_out,
+                   int q_heads, const void* K, void* K_out, int k_heads, int32_t interleaved, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  if (interleaved != 0 && interleaved != 1) return record(BR_ERR_INVALID_ARG, "interleaved must be 0 or 1");
+  if (!Q != !Q_out || !K != !K_out)
+    return record(BR_ERR_INVALID_ARG, "an input and its output must both be given or both be NULL");
+  if (!Q && !K) return record(BR_ERR_INVALID_ARG, "nothing to rotate: Q and K are both NULL");
+  if ((Q && (!aligned(Q, 16) || !aligned(Q_out, 16))) || (K && (!aligned(K, 16) || !aligned(K_out, 16))))
+    return record(BR_ERR_INVALID_ARG, "Q, K and their outputs must be 16-byte aligned");
+  // the documented size (one run per segment), which bounds what this plan uses
+  const size_t required = br::rope_workspace_bytes(int64_t(seg_ptr[dims.num_prompts]) - dims.num_prompts, dims.head_dim);
+  if (!workspace || workspace_bytes < required)
+    return record(BR_ERR_WORKSPACE, "workspace is NULL or smaller than br_rope_workspace_bytes() = " +
+                                        std::to_string(required));
+  if (!aligned(workspace, 16)) return record(BR_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  std::vector<unsigned char> host(plan.total_bytes, 0);  // a multiple of 16 bytes
+  std::memcpy(host.data() + plan.off_start, plan.start.data(), plan.start.size() * sizeof(int32_t));
+  std::memcpy(host.data() + plan.off_pos0, plan.pos0.data(), plan.pos0.size() * sizeof(int32_t));
+  std::memcpy(host.data() + plan.off_freq, plan.inv_freq.data(), plan.inv_freq.size() * sizeof(double));
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  br_status st = upload(ws, host.data(), host.size(), stream);
+  if (st != BR_OK) return st;
+  br::RopeLaunch l;
+  l.q = static_cast<const uint16_t*>(Q);
+  l.q_out = static_cast<uint16_t*>(Q_out);
+  l.k = static_cast<const uint16_t*>(K);
+  l.k_out = static_cast<uint16_t*>(K_out);
+  l.run_start = reinterpret_cast<const int32_t*>(ws + plan.off_start);
+  l.run_pos0 = reinterpret_cast<const int32_t*>(ws + plan.off_pos0);
+  l.inv_freq = reinterpret_cast<const double*>(ws + plan.off_freq);
+  l.rows = plan.rows;
+  l.n_runs = int(plan.pos0.size());
+  l.q_heads = Q ? q_heads : 0;
+  l.k_heads = K ? k_heads : 0;
+  l.head_dim = dims.head_dim;
+  l.adjacent = interleaved == 1;
+  hipError_t he = br::launch_rope(l, stream);
+  if (he != hipSuccess) return hip_fail(he, "rotary embedding kernel launch");
+  return BR_OK;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -540,6 +583,87 @@ br_status br_sort_docs(const float* scores, const int32_t* doc_ptr, int32_t num_
     }
     hipError_t he = br::launch_sort_docs(scores, base.data(), num_prompts, order, stream);
     if (he != hipSuccess) return hip_fail(he, "sort kernel launch");
+    return BR_OK;
+  });
+}
+
+br_status br_ssmax_softmax_scale(float s, int32_t n_docs, int32_t head_dim, float* scale) {
+  return guarded([&]() -> br_status {
+    if (!scale) return record(BR_ERR_INVALID_ARG, "scale is NULL");
+    if (head_dim < 1) return record(BR_ERR_INVALID_ARG, "head_dim must be >= 1");
+    if (n_docs < 2)
+      return record(BR_ERR_INVALID_ARG, "SSMax needs n_docs >= 2 (ln 1 = 0 would make every logit zero, "
+                                        "and a zero softmax_scale selects 1/sqrt(d))");
+    if (!(s > 0.f) || std::isinf(s)) return record(BR_ERR_INVALID_ARG, "s must be finite and positive");
+    *scale = float(double(s) * std::log(double(n_docs)) / std::sqrt(double(head_dim)));
+    return BR_OK;
+  });
+}
+
+br_status br_rope_workspace_bytes(const br_dims* dims, const int32_t* seg_ptr, size_t* bytes) {
+  return guarded([&]() -> br_status {
+    if (!bytes) return record(BR_ERR_INVALID_ARG, "bytes is NULL");
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    if (!seg_ptr) return record(BR_ERR_INVALID_ARG, "seg_ptr must be a non-NULL host array");
+    const int64_t runs = int64_t(seg_ptr[dims->num_prompts]) - dims->num_prompts;
+    if (runs < dims->num_prompts) return record(BR_ERR_INVALID_ARG, "seg_ptr is not increasing");
+    *bytes = br::rope_workspace_bytes(runs, dims->head_dim);
+    return BR_OK;
+  });
+}
+
+
+br_status br_rope_fwd(const br_dims* dims, const void* Q, const void* K, void* Q_out, void* K_out,
+                      const int32_t* segment_offsets, const int32_t* seg_ptr, float rope_theta, int32_t query_pos0,
+                      int32_t docs_after_instruction, int32_t interleaved, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  return guarded([&]() -> br_status {
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    if (docs_after_instruction != 0 && docs_after_instruction != 1)
+      return record(BR_ERR_INVALID_ARG, "docs_after_instruction must be 0 or 1");
+    br::RopePlan plan;
+    e = br::build_rope_plan(*dims, segment_offsets, seg_ptr, rope_theta, query_pos0, docs_after_instruction, &plan);
+    if (!e.ok()) return record(e);
+    return run_rope(*dims, seg_ptr, plan, Q, Q_out, dims->num_q_heads, K, K_out, dims->num_kv_heads, interleaved, workspace,
+                    workspace_bytes, stream);
+  });
+}
+
+br_status br_rope_signal_fwd(const br_dims* dims, const void* Q_S, void* Q_S_out, int32_t n_signal,
+                             const int32_t* segment_offsets, const int32_t* seg_ptr, float rope_theta,
+                             int32_t query_pos0, int32_t interleaved, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  return guarded([&]() -> br_status {
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    if (!Q_S || !Q_S_out) return record(BR_ERR_INVALID_ARG, "Q_S and Q_S_out must be non-NULL device pointers");
+    br::RopePlan plan;
+    e = br::build_rope_signal_plan(*dims, n_signal, segment_offsets, seg_ptr, rope_theta, query_pos0, &plan);
+    if (!e.ok()) return record(e);
+    return run_rope(*dims, seg_ptr, plan, Q_S, Q_S_out, dims->num_q_heads, nullptr, nullptr, 0, interleaved, workspace,
+                    workspace_bytes, stream);
+  });
+}
+
+br_status br_rope_positions(const br_dims* dims, const int32_t* segment_offsets, const int32_t* seg_ptr,
+                            int32_t query_pos0, int32_t docs_after_instruction, int32_t* positions,
+                            int64_t capacity) {
+  return guarded([&]() -> br_status {
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    if (docs_after_instruction != 0 && docs_after_instruction != 1)
+      return record(BR_ERR_INVALID_ARG, "docs_after_instruction must be 0 or 1");
+    if (!positions) return record(BR_ERR_INVALID_ARG, "positions is NULL");
+    if (capacity < dims->total_tokens)
+      return record(BR_ERR_INVALID_ARG, "positions holds " + std::to_string(capacity) + " entries; need total_tokens = " +
+                                            std::to_string(dims->total_tokens));
+    br::RopePlan plan;
+    e = br::build_rope_plan(*dims, segment_offsets, seg_ptr, 10000.f, query_pos0, docs_after_instruction, &plan);
+    if (!e.ok()) return record(e);
+    for (size_t r = 0; r < plan.pos0.size(); ++r)
+      for (int32_t t = plan.start[r]; t < plan.start[r + 1]; ++t) positions[t] = plan.pos0[r] + (t - plan.start[r]);
     return BR_OK;
   });
 }

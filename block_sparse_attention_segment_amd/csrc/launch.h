@@ -48,4 +48,18 @@ constexpr int kSortPromptsPerLaunch = 256;
 hipError_t launch_sort_docs(const float* scores, const int32_t* prompt_base, int num_prompts, int32_t* order,
                             hipStream_t stream);
 
+struct RopeLaunch {
+  const uint16_t* q;        // [rows, q_heads, head_dim] or nullptr (q_heads == 0)
+  uint16_t* q_out;          // may equal q
+  const uint16_t* k;        // [rows, k_heads, head_dim] or nullptr (k_heads == 0)
+  uint16_t* k_out;          // may equal k
+  const int32_t* run_start;  // device copies of the plan's runs
+  const int32_t* run_pos0;
+  const double* inv_freq;
+  int64_t rows;
+  int n_runs, q_heads, k_heads, head_dim;
+  bool adjacent;            // pairs (2k, 2k+1) instead of (k, k + d/2)
+};
+hipError_t launch_rope(const RopeLaunch& a, hipStream_t stream);
+
 }  // namespace br

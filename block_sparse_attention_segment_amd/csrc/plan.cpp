@@ -10,6 +10,8 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <climits>
+#include <cmath>
 #include <cstdio>
 #include <functional>
 #include <queue>
@@ -408,6 +410,89 @@ Error build_score_plan(const br_dims& dims, int32_t n_signal, const int32_t* dof
   // [n_docs, RT] per-document (max, sum) partials followed by [B, RT] per-row (max, 1/Z)
   const size_t rt = size_t(n_signal) * size_t(dims.num_q_heads);
   P.total_bytes = align_up(P.off_ml + (size_t(P.n_docs) + size_t(B)) * rt * 8, 256);
+  return {};
+}
+
+// ---------------------------------------------------------------------------------------------
+// rotary embedding runs
+
+size_t rope_workspace_bytes(int64_t n_runs, int head_dim) {
+  return align_up(size_t(n_runs + 1) * 4, 16) + align_up(size_t(n_runs) * 4, 16) + size_t(head_dim / 2) * 8;
+}
+
+Error validate_rope(const br_dims& dims, float rope_theta, int32_t query_pos0) {
+  if (!(rope_theta > 0.f) || std::isinf(rope_theta))
+    return Error{BR_ERR_INVALID_ARG, "rope_theta must be finite and positive"};
+  if (query_pos0 < 0) return fail(BR_ERR_INVALID_ARG, "query_pos0 must be >= 0 (got %lld)", query_pos0);
+  (void)dims;
+  return {};
+}
+
+namespace {
+
+void finish_rope(const br_dims& dims, float theta, RopePlan* plan) {
+  const int half = dims.head_dim / 2;
+  plan->inv_freq.resize(size_t(half));
+  for (int k = 0; k < half; ++k) plan->inv_freq[size_t(k)] = std::pow(double(theta), -2.0 * k / dims.head_dim);
+  const int64_t n = int64_t(plan->pos0.size());
+  plan->off_start = 0;
+  plan->off_pos0 = align_up(size_t(n + 1) * 4, 16);
+  plan->off_freq = plan->off_pos0 + align_up(size_t(n) * 4, 16);
+  plan->total_bytes = plan->off_freq + size_t(half) * 8;
+}
+
+}  // namespace
+
+Error build_rope_plan(const br_dims& dims, const int32_t* so, const int32_t* sp, float rope_theta, int32_t query_pos0,
+                      int32_t docs_after_instruction, RopePlan* plan) {
+  Error e = validate_segments(dims, so, sp);
+  if (!e.ok()) return e;
+  e = validate_rope(dims, rope_theta, query_pos0);
+  if (!e.ok()) return e;
+  *plan = RopePlan{};
+  for (int b = 0; b < dims.num_prompts; ++b) {
+    const int32_t* o = so + sp[b];
+    const int64_t n = int64_t(sp[b + 1]) - sp[b];
+    const int32_t p = o[1] - o[0];
+    if (int64_t(query_pos0) + (o[n - 1] - o[n - 2]) > INT32_MAX)
+      return fail(BR_ERR_INVALID_ARG, "prompt %lld: query positions from %lld overflow int32", b, query_pos0);
+    auto add = [&](int32_t start, int32_t end, int32_t pos0) {
+      if (end <= start) return;
+      plan->start.push_back(start);
+      plan->pos0.push_back(pos0);
+    };
+    add(o[0], o[1], 0);
+    for (int64_t k = 1; k < n - 2; ++k) add(o[k], o[k + 1], docs_after_instruction ? p : 0);
+    add(o[n - 2], o[n - 1], query_pos0);
+  }
+  plan->rows = dims.total_tokens;
+  plan->start.push_back(int32_t(dims.total_tokens));
+  finish_rope(dims, rope_theta, plan);
+  return {};
+}
+
+Error build_rope_signal_plan(const br_dims& dims, int32_t n_signal, const int32_t* so, const int32_t* sp,
+                             float rope_theta, int32_t query_pos0, RopePlan* plan) {
+  Error e = validate_segments(dims, so, sp);
+  if (!e.ok()) return e;
+  e = validate_rope(dims, rope_theta, query_pos0);
+  if (!e.ok()) return e;
+  if (n_signal < 1) return fail(BR_ERR_INVALID_ARG, "n_signal must be >= 1 (got %lld)", n_signal);
+  *plan = RopePlan{};
+  for (int b = 0; b < dims.num_prompts; ++b) {
+    const int32_t* o = so + sp[b];
+    const int64_t n = int64_t(sp[b + 1]) - sp[b];
+    const int64_t q = o[n - 1] - o[n - 2];
+    if (q < n_signal)
+      return fail(BR_ERR_INVALID_ARG, "prompt %lld: query has %lld tokens, fewer than n_signal = %lld", b, q, n_signal);
+    if (int64_t(query_pos0) + q > INT32_MAX)
+      return fail(BR_ERR_INVALID_ARG, "prompt %lld: query positions from %lld overflow int32", b, query_pos0);
+    plan->start.push_back(int32_t(int64_t(b) * n_signal));
+    plan->pos0.push_back(int32_t(query_pos0 + q - n_signal));
+  }
+  plan->rows = int64_t(dims.num_prompts) * n_signal;
+  plan->start.push_back(int32_t(plan->rows));
+  finish_rope(dims, rope_theta, plan);
   return {};
 }
 

@@ -72,6 +72,16 @@ struct ScorePlan {
   size_t off_items = 0, off_doc_offsets = 0, off_prompt_base = 0, off_ml = 0, total_bytes = 0;
 };
 
+// Rotary embedding runs: rows [start[r], start[r + 1]) take positions pos0[r] + (row - start[r]).
+// Runs are non-empty and ascending; start has n_runs + 1 entries, the last being the row count.
+struct RopePlan {
+  std::vector<int32_t> start;
+  std::vector<int32_t> pos0;
+  std::vector<double> inv_freq;  // theta^(-2k/d), k = 0 .. d/2 - 1
+  int64_t rows = 0;
+  size_t off_start = 0, off_pos0 = 0, off_freq = 0, total_bytes = 0;
+};
+
 // Status plus message; the API layer stores the message in the thread-local error slot.
 struct Error {
   br_status status = BR_OK;
@@ -105,6 +115,18 @@ Error validate_docs(const br_dims& dims, int32_t n_signal, const int32_t* doc_of
                     const int32_t* doc_ptr);
 Error build_score_plan(const br_dims& dims, int32_t n_signal, const int32_t* doc_offsets,
                        const int32_t* doc_ptr, ScorePlan* plan);
+
+// Permutation-invariant positions: instruction token i at i; token j of a document at
+// j + (docs_after_instruction ? instruction length : 0); query token i at query_pos0 + i.
+Error validate_rope(const br_dims& dims, float rope_theta, int32_t query_pos0);
+Error build_rope_plan(const br_dims& dims, const int32_t* segment_offsets, const int32_t* seg_ptr,
+                      float rope_theta, int32_t query_pos0, int32_t docs_after_instruction, RopePlan* plan);
+// Signal rows [B, n_signal]: row s of prompt b sits at the position of the prompt's query token
+// q_b - n_signal + s.
+Error build_rope_signal_plan(const br_dims& dims, int32_t n_signal, const int32_t* segment_offsets,
+                             const int32_t* seg_ptr, float rope_theta, int32_t query_pos0, RopePlan* plan);
+// Workspace for either plan: enough for one run per segment of the segment table.
+size_t rope_workspace_bytes(int64_t n_runs, int head_dim);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -208,6 +208,63 @@ br_status br_attn_plan_schedule(const br_dims* dims, const int32_t* segment_offs
                                 int64_t capacity, int32_t* ranges, int64_t ranges_capacity,
                                 int64_t* n_items, int32_t* wg_per_head);
 
+/*
+ * SSMax logit factor (BlockSearch, section 5.1, length-aware softmax): SSMax multiplies the
+ * pre-softmax scores q.k / sqrt(d) by s * ln N, N the number of documents of the prompt.  Writes
+ * *scale = s * ln(n_docs) / sqrt(head_dim), the value to pass as softmax_scale to
+ * br_attn_fwd / br_attn_routed_fwd / br_query_attn_fwd and br_doc_scores for that prompt (the
+ * factor is per call, so a batch shares one N).  Host only.  n_docs < 2 is BR_ERR_INVALID_ARG
+ * (ln 1 = 0 would zero every logit, which softmax_scale cannot express: 0 selects 1/sqrt(d));
+ * s must be finite and positive; head_dim >= 1.
+ */
+br_status br_ssmax_softmax_scale(float s, int32_t n_docs, int32_t head_dim, float* scale);
+
+/*
+ * Rotary position embedding with permutation-invariant position ids (BlockRank summary,
+ * section 3.4 "Permutation-invariant position embeddings"; BlockSearch, section 3.2).
+ * Positions within prompt b (segments as for br_attn_fwd): instruction token i -> i; token j
+ * of any document -> j + (docs_after_instruction ? instruction length : 0); final-query token
+ * i -> query_pos0 + i.  BlockRank's rule is docs_after_instruction = 1, query_pos0 = 8192;
+ * BlockSearch's is docs_after_instruction = 0, query_pos0 = 300.
+ * Rotation (RoFormer): pair k of every head vector turns by pos * rope_theta^(-2k/d),
+ *   a' = a cos - b sin,  b' = a sin + b cos,
+ * with pairs (k, k + d/2) when interleaved == 0 (split halves, the GPT-NeoX / Mistral layout)
+ * or (2k, 2k + 1) when interleaved == 1.  The angle is reduced in fp64, the rotation runs in
+ * fp32 and the result is rounded to bf16 (nearest even).
+ *   Q, Q_out: device bf16 [total_tokens, Hq, d];  K, K_out: device bf16 [total_tokens, Hkv, d].
+ *   Q_out may equal Q and K_out may equal K (in place).  Q and Q_out may both be NULL, or K and
+ *   K_out, but not all four.  16-byte aligned.
+ *   rope_theta: finite, > 0 (the base is a model parameter; it is not on the pages).
+ *   query_pos0 >= 0; query positions must fit in int32.
+ *   workspace: device, >= br_rope_workspace_bytes(), 16-byte aligned, owned by the caller;
+ *   it holds the uploaded position runs while the enqueued kernel runs.
+ * Errors as in the conventions above; nothing is enqueued on error.
+ */
+br_status br_rope_workspace_bytes(const br_dims* dims, const int32_t* seg_ptr, size_t* bytes);
+br_status br_rope_fwd(const br_dims* dims, const void* Q, const void* K, void* Q_out, void* K_out,
+                      const int32_t* segment_offsets, const int32_t* seg_ptr, float rope_theta,
+                      int32_t query_pos0, int32_t docs_after_instruction, int32_t interleaved,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The same rotation for the readout's signal rows: Q_S, Q_S_out device bf16
+ * [num_prompts, n_signal, Hq, d]; row s of prompt b is the prompt's query token
+ * q_b - n_signal + s and sits at position query_pos0 + q_b - n_signal + s.  Each query must
+ * hold at least n_signal tokens.  Workspace as br_rope_workspace_bytes.
+ */
+br_status br_rope_signal_fwd(const br_dims* dims, const void* Q_S, void* Q_S_out, int32_t n_signal,
+                             const int32_t* segment_offsets, const int32_t* seg_ptr, float rope_theta,
+                             int32_t query_pos0, int32_t interleaved, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Host-only (no HIP call): the position id of every token under the rule above, written to the
+ * host array positions[total_tokens] (capacity >= total_tokens).
+ */
+br_status br_rope_positions(const br_dims* dims, const int32_t* segment_offsets, const int32_t* seg_ptr,
+                            int32_t query_pos0, int32_t docs_after_instruction, int32_t* positions,
+                            int64_t capacity);
+
 const char* br_status_string(br_status status);
 const char* br_last_error(void);
 const char* br_version(void);

@@ -592,6 +592,21 @@ def pin_rope_permutation_invariance(orc):
         assert np.abs(outs[0][k] - outs[1][k]).max() < 1e-12, k
 
 
+def pin_signal_positions(orc):
+    """The readout's signal rows are each prompt's last |S| query tokens, so their positions are
+    the prompt positions of those tokens."""
+    rng = random.Random(13)
+    for seed in range(4):
+        prompts = [(p, l, max(q, 5)) for (p, l, q) in random_prompts(rng, batch=3)]
+        seg, sp, _, _ = workloads.segment_tables(prompts)
+        for q0, after in [(8192, True), (300, False)]:
+            pos = orc.rope_positions(seg, sp, q0, after)
+            sig = orc.signal_positions(seg, sp, 5, q0)
+            for b in range(len(prompts)):
+                end = int(seg[sp[b + 1] - 1])
+                assert sig[b].tolist() == pos[end - 5:end].tolist(), (seed, b)
+
+
 ALL_PINS = [
     pin_closed_form_counts, pin_worked_example, pin_textbook_rows, pin_textbook_rows_no_prefix,
     pin_bruteforce_chunked, pin_special_rows, pin_document_isolation, pin_readout_bruteforce,
@@ -599,5 +614,5 @@ ALL_PINS = [
     pin_query_attn_no_corpus, pin_query_attn_is_prompt_query_rows, pin_query_attn_isolation,
     pin_routing_keep_all, pin_routing_is_compaction, pin_routing_ignores_dropped,
     pin_ssmax_gold_weight, pin_ssmax_readout_gold_mass, pin_rope_positions_golden, pin_rope_rotation_values,
-    pin_rope_relative_position, pin_rope_permutation_invariance,
+    pin_rope_relative_position, pin_rope_permutation_invariance, pin_signal_positions,
 ]

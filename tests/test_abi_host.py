@@ -280,3 +280,56 @@ def test_routed_workspace_and_bad_keep():
         with pytest.raises(br.BlockRankError) as ei:
             br.attn_routed_workspace_bytes(dims, seg, sp, kp, kk)
         assert ei.value.status == br._lib.BR_ERR_INVALID_ARG, (kp, kk)
+
+
+# ---- SSMax factor and rotary embedding (host side only) ----
+def test_ssmax_factor_and_bad_arguments():
+    for s, n, d in [(0.43, 2, 64), (0.43, 500, 128), (0.2, 10000, 128)]:
+        assert abs(br.ssmax_scale(s, n, d) - orc.ssmax_scale(s, n, d)) <= 1e-6 * orc.ssmax_scale(s, n, d)
+    for s, n, d in [(0.43, 1, 64), (0.43, 0, 64), (0.0, 10, 64), (-1.0, 10, 64), (float("inf"), 10, 64),
+                    (0.43, 10, 0)]:
+        with pytest.raises(br.BlockRankError) as ei:
+            br.ssmax_scale(s, n, d)
+        assert ei.value.status == br._lib.BR_ERR_INVALID_ARG, (s, n, d)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_rope_positions_match_oracle(seed):
+    rng = random.Random(seed)
+    prompts = random_prompts(rng, batch=rng.randint(1, 4), p_max=50, n_max=8, l_max=60, q_max=30)
+    seg, sp, _, _ = workloads.segment_tables(prompts)
+    dims = br.make_dims(len(prompts), 8, 2, 64, int(seg[-1]))
+    for q0, after in [(8192, True), (300, False), (0, True), (123456, False)]:
+        got = br.rope_positions(dims, seg, sp, q0, after)
+        want = orc.rope_positions(seg, sp, q0, after)
+        assert np.array_equal(got, want), (seed, q0, after)
+
+
+def test_rope_rejects_before_any_hip_call():
+    lib = br.load_library()
+    seg, sp, _, _ = workloads.segment_tables([(8, [16, 12, 20], 8), (0, [10, 10], 6)])
+    dims = br.make_dims(2, 8, 2, 64, int(seg[-1]))
+    need = br.rope_workspace_bytes(dims, sp)
+    assert need > 0
+    p = lambda a: np.ascontiguousarray(a, dtype=np.int32).ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    segp, spp = p(seg), p(sp)
+    f = _fake()
+    INV, WS = br._lib.BR_ERR_INVALID_ARG, br._lib.BR_ERR_WORKSPACE
+    call = lambda *a: lib.br_rope_fwd(ctypes.byref(dims), *a)
+    assert call(f, f, f, f, segp, spp, 10000.0, 8192, 1, 0, f, need - 1, None) == WS
+    assert call(f, f, f, f, segp, spp, 10000.0, 8192, 1, 0, None, need, None) == WS
+    assert call(f, f, f, f, segp, spp, 0.0, 8192, 1, 0, f, need, None) == INV            # theta
+    assert call(f, f, f, f, segp, spp, float("nan"), 8192, 1, 0, f, need, None) == INV
+    assert call(f, f, f, f, segp, spp, 10000.0, -1, 1, 0, f, need, None) == INV          # query_pos0
+    assert call(f, f, f, f, segp, spp, 10000.0, 2**31 - 3, 1, 0, f, need, None) == INV  # int32 overflow
+    assert call(f, f, f, f, segp, spp, 10000.0, 8192, 2, 0, f, need, None) == INV        # rule flag
+    assert call(f, f, f, f, segp, spp, 10000.0, 8192, 1, 2, f, need, None) == INV        # layout flag
+    assert call(None, None, None, None, segp, spp, 10000.0, 8192, 1, 0, f, need, None) == INV
+    assert call(f, f, None, f, segp, spp, 10000.0, 8192, 1, 0, f, need, None) == INV    # Q without Q_out
+    assert call(f, f, f, f, None, spp, 10000.0, 8192, 1, 0, f, need, None) == INV
+    sig = lambda *a: lib.br_rope_signal_fwd(ctypes.byref(dims), *a)
+    assert sig(f, f, 7, segp, spp, 10000.0, 8192, 0, f, need, None) == INV   # second query has 6 tokens
+    assert sig(f, f, 0, segp, spp, 10000.0, 8192, 0, f, need, None) == INV
+    assert sig(f, f, 4, segp, spp, 10000.0, 8192, 0, f, 0, None) == WS
+    pos = np.zeros(int(seg[-1]) - 1, dtype=np.int32)
+    assert lib.br_rope_positions(ctypes.byref(dims), segp, spp, 8192, 1, p(pos), pos.size) == INV  # too small
