@@ -47,6 +47,10 @@ Readings taken where the pages are silent or disagree (each also listed in the d
     of a head vector turns by pos * theta^(-2k/d).  Two pairings exist in practice, adjacent
     entries (2k, 2k+1) as in RoFormer's definition, or halves (k, k + d/2) as in the GPT-NeoX
     layout; both are provided.  The base theta is not on the pages: a parameter.
+  * Backward ([BR] 3.4, auxiliary loss): gradients of the block-sparse attention with respect to
+    Q, K and V for an upstream dO; the InfoNCE loss per prompt with temperature tau = 0.05 on the
+    readout scores s_k (the sum over prompts is the total); and the readout's gradient with
+    respect to Q_S and K.
 """
 from __future__ import annotations
 
@@ -303,6 +307,99 @@ def attn_routed(Q, K, V, segment_offsets, seg_ptr, keep_ptr, keep, rows, scale: 
             o, l = _masked_softmax_av(qi[:, h], Kf[cols, g], Vf[cols, g], np.ones((1, len(cols)), bool), sc)
             O[n, h], lse[n, h] = o[0], l[0]
     return O, lse
+
+
+# --------------------------------------------------------------------------------------
+# backward pass ([BR] 3.4 auxiliary loss: the gradient flows back through the attention)
+# --------------------------------------------------------------------------------------
+def attn_bwd(Q, K, V, dO, segment_offsets, seg_ptr, scale: Optional[float] = None, prompts=None):
+    """Gradients of O = softmax(scale * Q K^T + M) V with respect to Q, K and V, given dO.
+
+    Per prompt and query head h (KV head g = h // G), with the prompt's explicit mask:
+        P   = softmax over the allowed keys of scale * Q K^T
+        dV_g += P^T dO_h
+        dP  = dO_h V_g^T
+        dS  = P * (dP - rowsum(P * dP))          (the softmax Jacobian applied row by row)
+        dQ_h = scale * dS K_g,   dK_g += scale * dS^T Q_h
+    prompts: indices of the prompts to evaluate (default: all); other rows stay zero.
+    Returns (dQ [T,Hq,d], dK [T,Hkv,d], dV [T,Hkv,d]) in float64."""
+    Qf, Kf, Vf, dOf = to_f64(Q), to_f64(K), to_f64(V), to_f64(dO)
+    T, Hq, d = Qf.shape
+    Hkv = Kf.shape[1]
+    sc = _scale(d, scale)
+    tables = token_tables(segment_offsets, seg_ptr)
+    so = np.asarray(segment_offsets, dtype=np.int64); sp = np.asarray(seg_ptr, dtype=np.int64)
+    dQ, dK, dV = np.zeros_like(Qf), np.zeros_like(Kf), np.zeros_like(Vf)
+    for b in (range(len(sp) - 1) if prompts is None else prompts):
+        a, e = int(so[sp[b]]), int(so[sp[b + 1] - 1])
+        idx = np.arange(a, e)
+        mask = allowed(idx[:, None], idx[None, :], tables)
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            s = np.where(mask, (Qf[a:e, h] @ Kf[a:e, g].T) * sc, -np.inf)
+            P = np.exp(s - s.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            dV[a:e, g] += P.T @ dOf[a:e, h]
+            dP = dOf[a:e, h] @ Vf[a:e, g].T
+            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            dQ[a:e, h] = sc * (dS @ Kf[a:e, g])
+            dK[a:e, g] += sc * (dS.T @ Qf[a:e, h])
+    return dQ, dK, dV
+
+
+def infonce(scores, doc_ptr, gold, tau: float = 0.05):
+    """[BR] auxiliary loss per prompt: L_b = -log(exp(s_gold / tau) / sum_k exp(s_k / tau)) over the
+    prompt's documents; gold holds each prompt's local index of the relevant document.
+    Returns (losses [B], dL/ds [sum N_b]) for the total sum_b L_b: (softmax(s / tau) - onehot) / tau."""
+    s = np.asarray(scores, dtype=np.float64)
+    dp = np.asarray(doc_ptr, dtype=np.int64)
+    losses, grad = [], np.zeros_like(s)
+    base = 0
+    for b in range(len(dp) - 1):
+        N = int(dp[b + 1] - dp[b] - 1)
+        z = s[base:base + N] / tau
+        m = z.max()
+        lse = m + math.log(np.exp(z - m).sum())
+        k = int(gold[b])
+        losses.append(lse - z[k])
+        p = np.exp(z - lse)
+        p[k] -= 1.0
+        grad[base:base + N] = p / tau
+        base += N
+    return np.asarray(losses), grad
+
+
+def doc_scores_bwd(Q_S, K, doc_offsets, doc_ptr, dscores, scale: Optional[float] = None):
+    """Gradient of sum_k dscores_k * s_k through the readout, with respect to Q_S and K.
+
+    For signal row i, head h (KV head g) and document token j of document k(j):
+        alpha = softmax over the prompt's document tokens of z = scale * Q_S[i,h] . K[j,g]
+        dz_ij = (1/Hq) * alpha_ij * (dscores_k(j) - sum_j' alpha_ij' dscores_k(j'))
+        dQ_S[i,h] = scale * sum_j dz_ij K[j,g],   dK[j,g] += scale * sum_(i, h in g) dz_ij Q_S[i,h]
+    Returns (dQ_S [B,S,Hq,d], dK [T,Hkv,d]) in float64; dK is zero outside document tokens."""
+    Qs, Kf = to_f64(Q_S), to_f64(K)
+    B, S, Hq, d = Qs.shape
+    Hkv = Kf.shape[1]
+    sc = _scale(d, scale)
+    do = np.asarray(doc_offsets, dtype=np.int64); dp = np.asarray(doc_ptr, dtype=np.int64)
+    ds = np.asarray(dscores, dtype=np.float64)
+    dQs, dK = np.zeros_like(Qs), np.zeros_like(Kf)
+    base = 0
+    for b in range(B):
+        offs = do[dp[b]:dp[b + 1]]
+        N = len(offs) - 1
+        a, e = int(offs[0]), int(offs[-1])
+        gj = np.repeat(ds[base:base + N], np.diff(offs))           # dscores of each token's document
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            z = (Qs[b, :, h, :] @ Kf[a:e, g, :].T) * sc
+            alpha = np.exp(z - z.max(axis=1, keepdims=True))
+            alpha /= alpha.sum(axis=1, keepdims=True)
+            dz = alpha * (gj[None, :] - (alpha * gj[None, :]).sum(axis=1, keepdims=True)) / Hq
+            dQs[b, :, h, :] = sc * (dz @ Kf[a:e, g, :])
+            dK[a:e, g, :] += sc * (dz.T @ Qs[b, :, h, :])
+        base += N
+    return dQs, dK
 
 
 # --------------------------------------------------------------------------------------

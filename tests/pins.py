@@ -607,6 +607,141 @@ def pin_signal_positions(orc):
                 assert sig[b].tolist() == pos[end - 5:end].tolist(), (seed, b)
 
 
+# --------------------------------------------------------------------------------------
+# backward pass: gradients against finite differences of the pinned forward, identities,
+# and autograd through a library attention
+# --------------------------------------------------------------------------------------
+def _bwd_case(seed, hq=4, hkv=2, d=8):
+    rng = random.Random(seed)
+    prompts = random_prompts(rng, batch=2, p_max=6, n_max=3, l_max=7, q_max=5)
+    w = workloads.make_custom(prompts, hq, hkv, d, 1, 4000 + seed)
+    nrng = np.random.default_rng(seed)
+    T = w.total_tokens
+    # float64 inputs, not bf16 bit patterns: finite differences need a smooth function
+    Q, K, V = (nrng.standard_normal((T, h, d)) for h in (hq, hkv, hkv))
+    dO = nrng.standard_normal((T, hq, d))
+    return w, Q, K, V, dO
+
+
+def pin_attn_bwd_finite_differences(orc):
+    """Central differences of sum(O * dO), with O from the pinned forward oracle."""
+    for seed in (0, 1):
+        w, Q, K, V, dO = _bwd_case(seed)
+        so, sp = w.segment_offsets, w.seg_ptr
+        dQ, dK, dV = orc.attn_bwd(Q, K, V, dO, so, sp)
+        f = lambda q, k, v: float((orc.attn_rows(q, k, v, so, sp)[0] * dO).sum())
+        rng = np.random.default_rng(seed + 50)
+        eps = 1e-6
+        for name, X, G in (("Q", Q, dQ), ("K", K, dK), ("V", V, dV)):
+            for _ in range(12):
+                ix = tuple(int(rng.integers(0, n)) for n in X.shape)
+                Xp, Xm = X.copy(), X.copy()
+                Xp[ix] += eps
+                Xm[ix] -= eps
+                args_p = {"Q": (Xp, K, V), "K": (Q, Xp, V), "V": (Q, K, Xp)}[name]
+                args_m = {"Q": (Xm, K, V), "K": (Q, Xm, V), "V": (Q, K, Xm)}[name]
+                fd = (f(*args_p) - f(*args_m)) / (2 * eps)
+                assert abs(fd - G[ix]) < 1e-6 * max(1.0, abs(fd)), (seed, name, ix, fd, G[ix])
+
+
+def pin_attn_bwd_identities(orc):
+    """Every P row sums to one and every dS row to zero, so per prompt and KV head the keys' dV
+    sum to the rows' dO (over the group's heads) and the keys' dK sum to zero."""
+    for seed in (2, 3):
+        w, Q, K, V, dO = _bwd_case(seed, hq=4, hkv=1)
+        dQ, dK, dV = orc.attn_bwd(Q, K, V, dO, w.segment_offsets, w.seg_ptr)
+        so, sp = np.asarray(w.segment_offsets), np.asarray(w.seg_ptr)
+        for b in range(len(sp) - 1):
+            a, e = int(so[sp[b]]), int(so[sp[b + 1] - 1])
+            assert np.allclose(dV[a:e, 0].sum(axis=0), dO[a:e].sum(axis=(0, 1)), atol=1e-10)
+            assert np.allclose(dK[a:e, 0].sum(axis=0), 0.0, atol=1e-10)
+
+
+def pin_attn_bwd_autograd(orc):
+    """Against torch's autograd through scaled_dot_product_attention (float64, CPU) with the
+    prompt's boolean mask."""
+    w, Q, K, V, dO = _bwd_case(4, hq=4, hkv=2, d=8)
+    dQ, dK, dV = orc.attn_bwd(Q, K, V, dO, w.segment_offsets, w.seg_ptr)
+    tables = orc.token_tables(w.segment_offsets, w.seg_ptr)
+    T = w.total_tokens
+    idx = np.arange(T)
+    mask = torch.from_numpy(orc.allowed(idx[:, None], idx[None, :], tables))
+    q = torch.from_numpy(Q).permute(1, 0, 2).contiguous().requires_grad_(True)      # [Hq, T, d]
+    k = torch.from_numpy(K).permute(1, 0, 2).contiguous().requires_grad_(True)      # [Hkv, T, d]
+    v = torch.from_numpy(V).permute(1, 0, 2).contiguous().requires_grad_(True)
+    kk, vv = k.repeat_interleave(2, dim=0), v.repeat_interleave(2, dim=0)
+    out = torch.nn.functional.scaled_dot_product_attention(q, kk, vv, attn_mask=mask)
+    out.backward(torch.from_numpy(dO).permute(1, 0, 2))
+    assert np.allclose(q.grad.permute(1, 0, 2).numpy(), dQ, atol=1e-10)
+    assert np.allclose(k.grad.permute(1, 0, 2).numpy(), dK, atol=1e-10)
+    assert np.allclose(v.grad.permute(1, 0, 2).numpy(), dV, atol=1e-10)
+
+
+def pin_infonce(orc):
+    """Equal scores give loss ln N and gradient (1/N - onehot)/tau; the gradient sums to zero per
+    prompt; it matches central differences of the loss; the loss is torch's cross entropy of the
+    logits s/tau."""
+    L, g = orc.infonce(np.full(5, 0.3), [0, 6], [2], tau=0.05)
+    assert abs(L[0] - math.log(5)) < 1e-12
+    want = np.full(5, 0.2 / 0.05); want[2] -= 1.0 / 0.05
+    assert np.allclose(g, want, atol=1e-12)
+    rng = np.random.default_rng(1)
+    s = rng.uniform(0, 1, 9); dp = [0, 5, 11]; gold = [3, 1]
+    L, g = orc.infonce(s, dp, gold, tau=0.05)
+    assert abs(g[:4].sum()) < 1e-9 and abs(g[4:].sum()) < 1e-9
+    for i in range(9):
+        sp_, sm = s.copy(), s.copy()
+        sp_[i] += 1e-6; sm[i] -= 1e-6
+        fd = (orc.infonce(sp_, dp, gold)[0].sum() - orc.infonce(sm, dp, gold)[0].sum()) / 2e-6
+        assert abs(fd - g[i]) < 1e-5 * max(1.0, abs(fd)), (i, fd, g[i])
+    ce = torch.nn.functional.cross_entropy(torch.from_numpy(s[:4] / 0.05)[None], torch.tensor([3]))
+    assert abs(float(ce) - L[0]) < 1e-12
+
+
+def _readout_bwd_case(seed, hq=4, hkv=2, d=8, S=3):
+    rng = random.Random(seed)
+    prompts = [(p, l, max(q, S)) for (p, l, q) in random_prompts(rng, batch=2, p_max=5, n_max=4, l_max=6, q_max=5)]
+    w = workloads.make_custom(prompts, hq, hkv, d, S, 4100 + seed)
+    nrng = np.random.default_rng(seed)
+    Q_S = nrng.standard_normal((w.num_prompts, S, hq, d))
+    K = nrng.standard_normal((w.total_tokens, hkv, d))
+    ds = nrng.standard_normal(w.num_docs)
+    return w, Q_S, K, ds
+
+
+def pin_readout_bwd_finite_differences(orc):
+    """Central differences of sum_k dscores_k s_k, with s from the pinned readout oracle."""
+    for seed in (0, 1):
+        w, Q_S, K, ds = _readout_bwd_case(seed)
+        dQs, dK = orc.doc_scores_bwd(Q_S, K, w.doc_offsets, w.doc_ptr, ds)
+        f = lambda qs, k: float(orc.doc_scores(qs, k, w.doc_offsets, w.doc_ptr)[0] @ ds)
+        rng = np.random.default_rng(seed + 60)
+        eps = 1e-6
+        for _ in range(12):
+            ix = tuple(int(rng.integers(0, n)) for n in Q_S.shape)
+            a, b = Q_S.copy(), Q_S.copy()
+            a[ix] += eps; b[ix] -= eps
+            fd = (f(a, K) - f(b, K)) / (2 * eps)
+            assert abs(fd - dQs[ix]) < 1e-6 * max(1.0, abs(fd)), ("Q_S", ix, fd, dQs[ix])
+            jx = tuple(int(rng.integers(0, n)) for n in K.shape)
+            a, b = K.copy(), K.copy()
+            a[jx] += eps; b[jx] -= eps
+            fd = (f(Q_S, a) - f(Q_S, b)) / (2 * eps)
+            assert abs(fd - dK[jx]) < 1e-6 * max(1.0, abs(fd)), ("K", jx, fd, dK[jx])
+
+
+def pin_readout_bwd_identities(orc):
+    """The scores of a prompt sum to |S| whatever Q_S and K are, so a dscores constant over a
+    prompt's documents has zero gradient; dK is zero on instruction and query tokens."""
+    w, Q_S, K, ds = _readout_bwd_case(3)
+    const = np.repeat([0.7, -1.3], [int(w.doc_ptr[1] - 1), int(w.doc_ptr[2] - w.doc_ptr[1] - 1)])
+    dQs, dK = orc.doc_scores_bwd(Q_S, K, w.doc_offsets, w.doc_ptr, const)
+    assert np.abs(dQs).max() < 1e-12 and np.abs(dK).max() < 1e-12
+    dQs, dK = orc.doc_scores_bwd(Q_S, K, w.doc_offsets, w.doc_ptr, ds)
+    kind = orc.token_tables(w.segment_offsets, w.seg_ptr)[2]
+    assert np.abs(dK[kind != orc.KIND_D]).max() == 0.0 and np.abs(dK[kind == orc.KIND_D]).max() > 0
+
+
 ALL_PINS = [
     pin_closed_form_counts, pin_worked_example, pin_textbook_rows, pin_textbook_rows_no_prefix,
     pin_bruteforce_chunked, pin_special_rows, pin_document_isolation, pin_readout_bruteforce,
@@ -615,4 +750,6 @@ ALL_PINS = [
     pin_routing_keep_all, pin_routing_is_compaction, pin_routing_ignores_dropped,
     pin_ssmax_gold_weight, pin_ssmax_readout_gold_mass, pin_rope_positions_golden, pin_rope_rotation_values,
     pin_rope_relative_position, pin_rope_permutation_invariance, pin_signal_positions,
+    pin_attn_bwd_finite_differences, pin_attn_bwd_identities, pin_attn_bwd_autograd, pin_infonce,
+    pin_readout_bwd_finite_differences, pin_readout_bwd_identities,
 ]

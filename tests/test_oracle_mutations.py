@@ -273,6 +273,93 @@ def _rope_ignores_pairing(X, positions, theta, interleaved=False):
     return _rope_generic(X, positions, theta, interleaved, force_half=True)
 
 
+_real_attn_bwd = orc.attn_bwd
+_real_infonce = orc.infonce
+_real_readout_bwd = orc.doc_scores_bwd
+
+
+def _attn_bwd_generic(Q, K, V, dO, so, sp, scale=None, prompts=None, center=True, group=True, dk_scale=True):
+    Qf, Kf, Vf, dOf = orc.to_f64(Q), orc.to_f64(K), orc.to_f64(V), orc.to_f64(dO)
+    T, Hq, d = Qf.shape
+    Hkv = Kf.shape[1]
+    sc = orc._scale(d, scale)
+    tables = orc.token_tables(so, sp)
+    so_, sp_ = np.asarray(so), np.asarray(sp)
+    dQ, dK, dV = np.zeros_like(Qf), np.zeros_like(Kf), np.zeros_like(Vf)
+    for b in range(len(sp_) - 1):
+        a, e = int(so_[sp_[b]]), int(so_[sp_[b + 1] - 1])
+        idx = np.arange(a, e)
+        mask = orc.allowed(idx[:, None], idx[None, :], tables)
+        for h in range(Hq):
+            g = orc.kv_head(h, Hq, Hkv)
+            sco = np.where(mask, (Qf[a:e, h] @ Kf[a:e, g].T) * sc, -np.inf)
+            P = np.exp(sco - sco.max(axis=1, keepdims=True)); P /= P.sum(axis=1, keepdims=True)
+            dP = dOf[a:e, h] @ Vf[a:e, g].T
+            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True)) if center else P * dP
+            dQ[a:e, h] = sc * (dS @ Kf[a:e, g])
+            if group or h % (Hq // Hkv) == 0:
+                dV[a:e, g] += P.T @ dOf[a:e, h]
+                dK[a:e, g] += (sc if dk_scale else 1.0) * (dS.T @ Qf[a:e, h])
+    return dQ, dK, dV
+
+
+def _attn_bwd_no_centering(*a, **k):
+    """dS = P * dP (the softmax Jacobian's row-sum term dropped)"""
+    return _attn_bwd_generic(*a, center=False, **k)
+
+
+def _attn_bwd_first_head_only(*a, **k):
+    """dK and dV take only the first query head of each KV group"""
+    return _attn_bwd_generic(*a, group=False, **k)
+
+
+def _attn_bwd_dk_unscaled(*a, **k):
+    """dK without the softmax scale"""
+    return _attn_bwd_generic(*a, dk_scale=False, **k)
+
+
+def _infonce_sign(scores, doc_ptr, gold, tau=0.05):
+    """gradient with the wrong sign"""
+    L, g = _real_infonce(scores, doc_ptr, gold, tau)
+    return L, -g
+
+
+def _infonce_no_tau(scores, doc_ptr, gold, tau=0.05):
+    """gradient missing the 1/tau of the logits"""
+    L, g = _real_infonce(scores, doc_ptr, gold, tau)
+    return L, g * tau
+
+
+def _readout_bwd_no_centering(Q_S, K, doc_offsets, doc_ptr, dscores, scale=None):
+    """dz = alpha * dscores (the softmax Jacobian's centering dropped)"""
+    Qs, Kf = orc.to_f64(Q_S), orc.to_f64(K)
+    B, S, Hq, d = Qs.shape
+    sc = orc._scale(d, scale)
+    do, dp = np.asarray(doc_offsets), np.asarray(doc_ptr)
+    ds = np.asarray(dscores, dtype=np.float64)
+    dQs, dK = np.zeros_like(Qs), np.zeros_like(Kf)
+    base = 0
+    for b in range(B):
+        offs = do[dp[b]:dp[b + 1]]; N = len(offs) - 1; a, e = int(offs[0]), int(offs[-1])
+        gj = np.repeat(ds[base:base + N], np.diff(offs))
+        for h in range(Hq):
+            g = orc.kv_head(h, Hq, Kf.shape[1])
+            z = (Qs[b, :, h, :] @ Kf[a:e, g, :].T) * sc
+            al = np.exp(z - z.max(axis=1, keepdims=True)); al /= al.sum(axis=1, keepdims=True)
+            dz = al * gj[None, :] / Hq
+            dQs[b, :, h, :] = sc * (dz @ Kf[a:e, g, :])
+            dK[a:e, g, :] += sc * (dz.T @ Qs[b, :, h, :])
+        base += N
+    return dQs, dK
+
+
+def _readout_bwd_sum_heads(Q_S, K, doc_offsets, doc_ptr, dscores, scale=None):
+    """gradient of the head sum instead of the head mean (1/Hq dropped)"""
+    dQs, dK = _real_readout_bwd(Q_S, K, doc_offsets, doc_ptr, dscores, scale)
+    Hq = np.asarray(Q_S).shape[2]
+    return dQs * Hq, dK * Hq
+
+
 MUTATIONS = {
     "mask_no_causal": ("allowed", _no_causal),
     "mask_docs_skip_prefix": ("allowed", _docs_skip_prefix),
@@ -303,6 +390,13 @@ MUTATIONS = {
     "rope_sin_sign": ("rope_apply", _rope_sin_sign),
     "rope_freq_exponent": ("rope_apply", _rope_freq_exponent),
     "rope_ignores_pairing": ("rope_apply", _rope_ignores_pairing),
+    "attn_bwd_no_centering": ("attn_bwd", _attn_bwd_no_centering),
+    "attn_bwd_first_head_only": ("attn_bwd", _attn_bwd_first_head_only),
+    "attn_bwd_dk_unscaled": ("attn_bwd", _attn_bwd_dk_unscaled),
+    "infonce_sign": ("infonce", _infonce_sign),
+    "infonce_no_tau": ("infonce", _infonce_no_tau),
+    "readout_bwd_no_centering": ("doc_scores_bwd", _readout_bwd_no_centering),
+    "readout_bwd_sum_heads": ("doc_scores_bwd", _readout_bwd_sum_heads),
 }
 
 
