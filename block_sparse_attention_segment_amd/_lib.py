@@ -20,6 +20,7 @@ BR_OK, BR_ERR_INVALID_ARG, BR_ERR_UNSUPPORTED, BR_ERR_WORKSPACE, BR_ERR_HIP = ra
 # Symbols the header declares; the CPU test checks the library exports each of them.
 EXPORTED = ("br_attn_workspace_bytes", "br_attn_fwd", "br_attn_fwd_timed", "br_doc_scores_workspace_bytes", "br_doc_scores",
             "br_sort_docs", "br_attn_plan_items", "br_attn_plan_schedule", "br_query_attn_workspace_bytes", "br_query_attn_fwd", "br_attn_routed_workspace_bytes", "br_attn_routed_fwd",
+            "br_attn_bwd_workspace_bytes", "br_attn_bwd", "br_attn_bwd_plan_items",
             "br_ssmax_softmax_scale", "br_rope_workspace_bytes", "br_rope_fwd", "br_rope_signal_fwd", "br_rope_positions",
             "br_status_string", "br_last_error", "br_version")
 
@@ -70,6 +71,11 @@ def load_library() -> ctypes.CDLL:
                                _P],
         "br_query_attn_workspace_bytes": [dims_p, ctypes.c_int32, _I32P, ctypes.POINTER(ctypes.c_size_t)],
         "br_query_attn_fwd": [dims_p, _P, _P, _P, ctypes.c_int32, _I32P, _P, _P, ctypes.c_float, _P, ctypes.c_size_t, _P],
+        "br_attn_bwd_workspace_bytes": [dims_p, _I32P, _I32P, sz_p],
+        "br_attn_bwd": [dims_p, _P, _P, _P, _P, _P, _P, _I32P, _I32P, _P, _P, _P, ctypes.c_float, _P, ctypes.c_size_t,
+                        _P],
+        "br_attn_bwd_plan_items": [dims_p, _I32P, _I32P, _I32P, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64),
+                                   ctypes.POINTER(ctypes.c_int32)],
         "br_ssmax_softmax_scale": [ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_float)],
         "br_rope_workspace_bytes": [dims_p, _I32P, sz_p],
         "br_rope_fwd": [dims_p, _P, _P, _P, _P, _I32P, _I32P, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
@@ -244,6 +250,56 @@ def attn_routed(Q, K, V, segment_offsets, seg_ptr, keep_ptr, keep, out=None, lse
                                   float(softmax_scale), workspace.data_ptr(), workspace.numel(),
                                   _stream_handle(stream)))
     return (out, lse) if lse is not None else out
+
+
+def attn_bwd_workspace_bytes(dims: BrDims, segment_offsets, seg_ptr) -> int:
+    lib = load_library()
+    so, sp = _host_i32(segment_offsets), _host_i32(seg_ptr)
+    out = ctypes.c_size_t(0)
+    _check(lib.br_attn_bwd_workspace_bytes(ctypes.byref(dims), _ptr_i32(so), _ptr_i32(sp), ctypes.byref(out)))
+    return int(out.value)
+
+
+def attn_bwd_plan_items(dims: BrDims, segment_offsets, seg_ptr):
+    """Host-only: the backward's key-major items ([n, 8] int32) and the number of partial slots."""
+    lib = load_library()
+    so, sp = _host_i32(segment_offsets), _host_i32(seg_ptr)
+    n, slots = ctypes.c_int64(0), ctypes.c_int32(0)
+    _check(lib.br_attn_bwd_plan_items(ctypes.byref(dims), _ptr_i32(so), _ptr_i32(sp), None, 0, ctypes.byref(n),
+                                      ctypes.byref(slots)))
+    items = np.zeros((max(1, n.value), 8), dtype=np.int32)
+    _check(lib.br_attn_bwd_plan_items(ctypes.byref(dims), _ptr_i32(so), _ptr_i32(sp), _ptr_i32(items), n.value,
+                                      ctypes.byref(n), ctypes.byref(slots)))
+    return items[:n.value], int(slots.value)
+
+
+def attn_bwd(Q, K, V, O, dO, lse, segment_offsets, seg_ptr, softmax_scale: float = 0.0, dQ=None, dK=None, dV=None,
+             workspace=None, stream=None):
+    """Gradients (dQ [T,Hq,d], dK, dV [T,Hkv,d], fp32) of the block-sparse attention for the upstream
+    gradient dO, given the forward's output O and log-sum-exp lse [T,Hq] (same softmax_scale)."""
+    import torch
+    lib = load_library()
+    for name, t in (("Q", Q), ("K", K), ("V", V), ("O", O), ("dO", dO)):
+        _check_bf16(name, t, 3)
+    T, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    if K.shape != (T, Hkv, d) or V.shape != K.shape or O.shape != Q.shape or dO.shape != Q.shape:
+        raise ValueError("shapes: Q, O, dO [T, Hq, d]; K, V [T, Hkv, d]")
+    if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous() or tuple(lse.shape) != (T, Hq):
+        raise ValueError("lse must be a contiguous float32 CUDA tensor [T, Hq]")
+    so, sp = _host_i32(segment_offsets), _host_i32(seg_ptr)
+    dims = make_dims(len(sp) - 1, Hq, Hkv, d, T)
+    f32 = dict(dtype=torch.float32, device=Q.device)
+    dQ = torch.empty((T, Hq, d), **f32) if dQ is None else dQ
+    dK = torch.empty((T, Hkv, d), **f32) if dK is None else dK
+    dV = torch.empty((T, Hkv, d), **f32) if dV is None else dV
+    nbytes = attn_bwd_workspace_bytes(dims, so, sp)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+    _check(lib.br_attn_bwd(ctypes.byref(dims), Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), dO.data_ptr(),
+                           lse.data_ptr(), _ptr_i32(so), _ptr_i32(sp), dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(),
+                           float(softmax_scale), workspace.data_ptr(), workspace.numel(), _stream_handle(stream)))
+    return dQ, dK, dV
 
 
 def ssmax_scale(s: float, n_docs: int, head_dim: int) -> float:

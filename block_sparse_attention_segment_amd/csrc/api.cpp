@@ -668,4 +668,101 @@ br_status br_rope_positions(const br_dims* dims, const int32_t* segment_offsets,
   });
 }
 
+br_status br_attn_bwd_workspace_bytes(const br_dims* dims, const int32_t* segment_offsets, const int32_t* seg_ptr,
+                                      size_t* bytes) {
+  return guarded([&]() -> br_status {
+    if (!bytes) return record(BR_ERR_INVALID_ARG, "bytes is NULL");
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    br::BwdPlan plan;
+    e = br::build_bwd_plan(*dims, segment_offsets, seg_ptr, &plan);
+    if (!e.ok()) return record(e);
+    *bytes = plan.total_bytes;
+    return BR_OK;
+  });
+}
+
+br_status br_attn_bwd(const br_dims* dims, const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                      const float* lse, const int32_t* segment_offsets, const int32_t* seg_ptr, float* dQ, float* dK,
+                      float* dV, float softmax_scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return guarded([&]() -> br_status {
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV)
+      return record(BR_ERR_INVALID_ARG, "Q, K, V, O, dO, lse, dQ, dK and dV must be non-NULL device pointers");
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(dO, 16) ||
+        !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16) || !aligned(lse, 4))
+      return record(BR_ERR_INVALID_ARG, "tensors must be 16-byte aligned (lse 4-byte)");
+    if (std::isnan(softmax_scale) || std::isinf(softmax_scale))
+      return record(BR_ERR_INVALID_ARG, "softmax_scale must be finite");
+    br::BwdPlan plan;
+    e = br::build_bwd_plan(*dims, segment_offsets, seg_ptr, &plan);
+    if (!e.ok()) return record(e);
+    if (!workspace || workspace_bytes < plan.total_bytes)
+      return record(BR_ERR_WORKSPACE, "workspace is NULL or smaller than br_attn_bwd_workspace_bytes() = " +
+                                          std::to_string(plan.total_bytes));
+    if (!aligned(workspace, 16)) return record(BR_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    // Host image of the plan region: [items | merges | kv items | kv merges].
+    std::vector<unsigned char> host(plan.off_part_dq, 0);
+    std::memcpy(host.data() + plan.off_items, plan.fwd.items.data(), plan.fwd.items.size() * sizeof(br::AttnItem));
+    if (!plan.fwd.merges.empty())
+      std::memcpy(host.data() + plan.off_merges, plan.fwd.merges.data(),
+                  plan.fwd.merges.size() * sizeof(br::MergeItem));
+    std::memcpy(host.data() + plan.off_kv_items, plan.kv_items.data(), plan.kv_items.size() * sizeof(br::KvItem));
+    if (!plan.kv_merges.empty())
+      std::memcpy(host.data() + plan.off_kv_merges, plan.kv_merges.data(),
+                  plan.kv_merges.size() * sizeof(br::KvMerge));
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    br_status st = upload(ws, host.data(), host.size(), stream);
+    if (st != BR_OK) return st;
+    br::BwdLaunch a;
+    a.Q = static_cast<const uint16_t*>(Q);
+    a.K = static_cast<const uint16_t*>(K);
+    a.V = static_cast<const uint16_t*>(V);
+    a.O = static_cast<const uint16_t*>(O);
+    a.dO = static_cast<const uint16_t*>(dO);
+    a.lse = lse;
+    a.dQ = dQ;
+    a.dK = dK;
+    a.dV = dV;
+    a.dvec = reinterpret_cast<float*>(ws + plan.off_dvec);
+    a.items = reinterpret_cast<const br::AttnItem*>(ws + plan.off_items);
+    a.merges = reinterpret_cast<const br::MergeItem*>(ws + plan.off_merges);
+    a.part_dq = reinterpret_cast<float*>(ws + plan.off_part_dq);
+    a.kv_items = reinterpret_cast<const br::KvItem*>(ws + plan.off_kv_items);
+    a.kv_merges = reinterpret_cast<const br::KvMerge*>(ws + plan.off_kv_merges);
+    a.part_dkv = reinterpret_cast<float*>(ws + plan.off_part_dkv);
+    a.n_items = int64_t(plan.fwd.items.size());
+    a.n_merges = int64_t(plan.fwd.merges.size());
+    a.n_kv_items = int64_t(plan.kv_items.size());
+    a.n_kv_merges = int64_t(plan.kv_merges.size());
+    a.total_tokens = dims->total_tokens;
+    a.kv_slots = plan.kv_slots;
+    a.num_q_heads = dims->num_q_heads;
+    a.num_kv_heads = dims->num_kv_heads;
+    a.head_dim = dims->head_dim;
+    a.scale = resolve_scale(softmax_scale, dims->head_dim);
+    hipError_t he = br::launch_attn_bwd(a, stream);
+    if (he != hipSuccess) return hip_fail(he, "attention backward launch");
+    return BR_OK;
+  });
+}
+
+br_status br_attn_bwd_plan_items(const br_dims* dims, const int32_t* segment_offsets, const int32_t* seg_ptr,
+                                 int32_t* items, int64_t capacity, int64_t* n_items, int32_t* n_slots) {
+  return guarded([&]() -> br_status {
+    if (!n_items || !n_slots) return record(BR_ERR_INVALID_ARG, "n_items and n_slots must be non-NULL");
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    br::BwdPlan plan;
+    e = br::build_bwd_plan(*dims, segment_offsets, seg_ptr, &plan);
+    if (!e.ok()) return record(e);
+    *n_items = int64_t(plan.kv_items.size());
+    *n_slots = plan.kv_slots;
+    if (items && capacity >= *n_items)
+      std::memcpy(items, plan.kv_items.data(), plan.kv_items.size() * sizeof(br::KvItem));
+    return BR_OK;
+  });
+}
+
 }  // extern "C"

@@ -1,0 +1,426 @@
+// Backward of the block-sparse prefill attention on gfx950 (MI355X).
+//
+// For O = softmax(scale Q K^T + M) V with the BlockRank mask M (BlockRank summary, section 3.4;
+// the auxiliary loss there sends its gradient back through this attention), given dO and the
+// forward's log-sum-exp L per row:
+//   P  = exp(scale Q K^T - L)   on allowed pairs, 0 elsewhere (recomputed, never stored)
+//   Dr = rowsum(dO * O)          (= rowsum(P * dP), the softmax Jacobian's row term)
+//   dP = dO V^T,  dS = P * (dP - Dr)
+//   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO
+// Only allowed (row, key) pairs are visited, through the same host plans as the forward:
+//   attn_bwd_dq_kernel   query-major over the forward plan's row tiles (128 (token, head) rows,
+//                        4 waves of 32 rows): per 64-key tile S^T = K Q^T and dP^T = V dO^T
+//                        (keys on M), dS^T in fp32, dQ^T += K^T dS^T with dS rounded to bf16
+//                        and K^T fragments from transposing LDS reads (as V^T in the forward).
+//   attn_bwd_dkv_kernel  key-major: 64 keys of one KV head per workgroup (2 waves of 32 keys);
+//                        the rows that read them stream through LDS 32 (token, head) rows at a
+//                        time: S = Q K^T and dP = dO V^T (rows on M), then dV^T += dO^T P and
+//                        dK^T += Q^T dS with the row-side operands read transposed from LDS.
+// Long row or key ranges are split; their fp32 partials are summed by the merge kernels in a
+// fixed order, so results are deterministic.  Outputs are fp32.
+#include "device_common.h"
+#include "launch.h"
+#include "plan.h"
+
+namespace br {
+
+// Dr[t, h] = sum_d dO[t, h, d] O[t, h, d] in fp32: 16 lanes per row of D = 128 (8 for D = 64).
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_rowdot_kernel(const uint16_t* __restrict__ O,
+                                                              const uint16_t* __restrict__ dO,
+                                                              float* __restrict__ dvec, int64_t rows) {
+  constexpr int L = D / 8;
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t row = i / L;
+  const int c = int(i % L);
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4_t a = load16(O + row * D + 8 * c), b = load16(dO + row * D + 8 * c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc = fmaf(__uint_as_float(a[j] << 16), __uint_as_float(b[j] << 16), acc);
+      acc = fmaf(__uint_as_float(a[j] & 0xffff0000u), __uint_as_float(b[j] & 0xffff0000u), acc);
+    }
+  }
+#pragma unroll
+  for (int m = L / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, L);
+  if (row < rows && c == 0) dvec[row] = acc;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                          const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                                                          const float* __restrict__ lse, const float* __restrict__ dvec,
+                                                          float* __restrict__ dQ, const AttnItem* __restrict__ items,
+                                                          float* __restrict__ part_dq, int Hq, int Hkv, float scale,
+                                                          float scale_log2) {
+  constexpr int TM = kRowsPerTile / G;
+  constexpr int BN = kKeyTile;
+  constexpr int NKB = BN / 32;
+  constexpr int VROW = D == 128 ? 160 : 96;  // K: row reads and transposing reads (as V in the forward)
+  constexpr int KROW = D + 8;                // V: row reads only
+  constexpr int DSTEPS = D / 16, DBLK = D / 32, KCH = D / 8;
+  constexpr int RPP = 256 / KCH;             // key rows per load pass
+  constexpr int KPASS = BN / RPP;
+  __shared__ __align__(16) uint16_t sk[BN * VROW];
+  __shared__ __align__(16) uint16_t sv[BN * KROW];
+
+  const int g = blockIdx.x % Hkv;
+  const AttnItem it = items[blockIdx.x / Hkv];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, half = lane >> 5;
+  const int rho = w * 32 + n, hh = rho / TM, tt = rho % TM, h = g * G + hh;
+  const int row_tok = it.row0 + tt;
+  const bool row_ok = row_tok < it.row_limit;
+  const int q_stride = Hq * D, kv_stride = Hkv * D;
+
+  // This lane's row: Q and dO fragments (B operands of S^T and dP^T), log2-domain lse, Dr.
+  const int rows = min(TM, it.row_limit - it.row0);
+  const rsrc_t rq = make_rsrc(Q + (int64_t(it.row0) * Hq + g * G) * D, rows * q_stride * 2);
+  const rsrc_t rdo = make_rsrc(dO + (int64_t(it.row0) * Hq + g * G) * D, rows * q_stride * 2);
+  const uint32_t q_off = uint32_t((tt * q_stride + hh * D + 8 * half) * 2);
+  u32x4_t qf[DSTEPS], df[DSTEPS];
+#pragma unroll
+  for (int s = 0; s < DSTEPS; ++s) {
+    qf[s] = buf_load16(rq, q_off + 32 * s);
+    df[s] = buf_load16(rdo, q_off + 32 * s);
+  }
+  const int64_t rix = int64_t(row_tok) * Hq + h;
+  const float l2 = row_ok ? lse[rix] * kLog2e : 0.f;
+  const float dr = row_ok ? dvec[rix] : 0.f;
+
+  const int kcc = tid % KCH, kr0 = tid / KCH;
+  const uint32_t k_off = uint32_t((kr0 * kv_stride + 8 * kcc) * 2);
+  u32x4_t kreg[KPASS], vreg[KPASS];
+  auto load_tile = [&](int start, int end) {
+    const int keys = min(BN, end - start);
+    const rsrc_t rk = make_rsrc(K + int64_t(start) * kv_stride + g * D, keys * kv_stride * 2);
+    const rsrc_t rv = make_rsrc(V + int64_t(start) * kv_stride + g * D, keys * kv_stride * 2);
+#pragma unroll
+    for (int p = 0; p < KPASS; ++p) {
+      kreg[p] = buf_load16(rk, k_off + p * RPP * kv_stride * 2);
+      vreg[p] = buf_load16(rv, k_off + p * RPP * kv_stride * 2);
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int p = 0; p < KPASS; ++p) {
+      const int r = kr0 + p * RPP;
+      *reinterpret_cast<u32x4_t*>(&sk[r * VROW + 8 * kcc]) = kreg[p];
+      *reinterpret_cast<u32x4_t*>(&sv[r * KROW + 8 * kcc]) = vreg[p];
+    }
+  };
+  // K^T fragments for dQ^T += K^T dS^T: the forward's V^T read pattern on the K tile.
+  const int vs = lane & 15, vdh = (lane >> 4) & 1;
+  const int k_lane = (4 * half + (vs >> 2)) * VROW + 16 * vdh + 4 * (vs & 3);
+
+  const int nA = it.a_end > it.a_start ? (it.a_end - it.a_start + BN - 1) / BN : 0;
+  const int nB = it.b_end > it.b_start ? (it.b_end - it.b_start + BN - 1) / BN : 0;
+  const int nt = nA + nB;
+  auto t_start = [&](int i) { return i < nA ? it.a_start + i * BN : it.b_start + (i - nA) * BN; };
+  auto t_end = [&](int i) { return i < nA ? it.a_end : it.b_end; };
+
+  f32x16_t acc[DBLK];
+#pragma unroll
+  for (int b = 0; b < DBLK; ++b) acc[b] = f32x16_t{};
+  if (nt > 0) load_tile(t_start(0), t_end(0));
+  for (int i = 0; i < nt; ++i) {
+    __syncthreads();  // the previous tile's reads are done
+    store_tile();
+    __syncthreads();
+    if (i + 1 < nt) load_tile(t_start(i + 1), t_end(i + 1));
+    const int start = t_start(i), end = t_end(i);
+    const bool causal = i >= nA;
+    f32x16_t s[NKB], dp[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      s[kb] = f32x16_t{};
+      dp[kb] = f32x16_t{};
+      const uint16_t* kp = &sk[(kb * 32 + n) * VROW + 8 * half];
+      const uint16_t* vp = &sv[(kb * 32 + n) * KROW + 8 * half];
+#pragma unroll
+      for (int st = 0; st < DSTEPS; ++st) {
+        s[kb] = mfma32(load16(kp + 16 * st), qf[st], s[kb]);
+        dp[kb] = mfma32(load16(vp + 16 * st), df[st], dp[kb]);
+      }
+    }
+    // Register r of block kb holds key start + 32 kb + 8 (r / 4) + 4 half + r % 4.
+    const int lim = (causal ? min(end, row_tok + 1) : end) - start - 4 * half;
+    uint32_t pk[NKB][8];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const bool ok0 = row_ok && (kb * 32 + 8 * (r >> 2) + (r & 3)) < lim;
+        const bool ok1 = row_ok && (kb * 32 + 8 * (r >> 2) + (r & 3) + 1) < lim;
+        const float p0 = ok0 ? fast_exp2(fmaf(s[kb][r], scale_log2, -l2)) : 0.f;
+        const float p1 = ok1 ? fast_exp2(fmaf(s[kb][r + 1], scale_log2, -l2)) : 0.f;
+        pk[kb][r >> 1] = pack_bf16x2(p0 * (dp[kb][r] - dr), p1 * (dp[kb][r + 1] - dr));
+      }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const u32x4_t pv = {pk[kb][4 * m], pk[kb][4 * m + 1], pk[kb][4 * m + 2], pk[kb][4 * m + 3]};
+        const uint16_t* kp = &sk[k_lane + (32 * kb + 16 * m) * VROW];
+#pragma unroll
+        for (int b = 0; b < DBLK; ++b) {
+          const u32x2_t lo = lds_read_tr16(kp + 32 * b), hi = lds_read_tr16(kp + 8 * VROW + 32 * b);
+          acc[b] = mfma32(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pv, acc[b]);
+        }
+      }
+  }
+  // acc[b] register r holds head-dim element 32 b + 8 (r / 4) + 4 half + r % 4 of this lane's row.
+  if (it.slot < 0) {
+    if (!row_ok) return;
+    float* dst = dQ + rix * D + 4 * half;
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4_t*>(dst + 32 * b + 8 * j) =
+            f32x4_t{acc[b][4 * j], acc[b][4 * j + 1], acc[b][4 * j + 2], acc[b][4 * j + 3]} * scale;
+  } else {
+    float* dst = part_dq + ((int64_t(it.slot) * Hkv + g) * kRowsPerTile + rho) * D + 4 * half;
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4_t*>(dst + 32 * b + 8 * j) =
+            f32x4_t{acc[b][4 * j], acc[b][4 * j + 1], acc[b][4 * j + 2], acc[b][4 * j + 3]} * scale;
+  }
+}
+
+// Sum the split-key dQ partials of one query tile (fixed order).  One thread per (row, 4 elements).
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_dq_merge_kernel(float* __restrict__ dQ, const MergeItem* __restrict__ merges,
+                                                                const float* __restrict__ part_dq, int Hq, int Hkv,
+                                                                int G) {
+  constexpr int CH = D / 4;
+  constexpr int WG_PER_TILE = kRowsPerTile * CH / 256;
+  const int tile = blockIdx.x / WG_PER_TILE, part = blockIdx.x % WG_PER_TILE;
+  const int g = tile % Hkv;
+  const MergeItem mi = merges[tile / Hkv];
+  const int unit = part * 256 + threadIdx.x;
+  const int rho = unit / CH, ch = unit % CH;
+  const int TM = kRowsPerTile / G;
+  const int tok = mi.row0 + rho % TM, h = g * G + rho / TM;
+  if (tok >= mi.row_limit) return;
+  const int64_t stride = int64_t(Hkv) * kRowsPerTile * D;
+  const float* src = part_dq + ((int64_t(mi.slot0) * Hkv + g) * kRowsPerTile + rho) * D + 4 * ch;
+  f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < mi.nslots; ++c) a += *reinterpret_cast<const f32x4_t*>(src + c * stride);
+  *reinterpret_cast<f32x4_t*>(dQ + (int64_t(tok) * Hq + h) * D + 4 * ch) = a;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(128) void attn_bwd_dkv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                                                           const float* __restrict__ lse, const float* __restrict__ dvec,
+                                                           float* __restrict__ dK, float* __restrict__ dV,
+                                                           const KvItem* __restrict__ items, float* __restrict__ part_dkv,
+                                                           int Hq, int Hkv, int kv_slots, float scale, float scale_log2) {
+  constexpr int TR = 32 / G;                 // row tokens per 32-row step (rows: token-major, G heads each)
+  constexpr int VROW = D == 128 ? 160 : 96;  // Q and dO rows: row reads and transposing reads
+  constexpr int DSTEPS = D / 16, DBLK = D / 32, KCH = D / 8;
+  __shared__ __align__(16) uint16_t sq[32 * VROW];
+  __shared__ __align__(16) uint16_t sd[32 * VROW];
+  __shared__ float sl[32], sr[32];
+
+  const int g = blockIdx.x % Hkv;
+  const KvItem it = items[blockIdx.x / Hkv];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, half = lane >> 5;
+  const int q_stride = Hq * D, kv_stride = Hkv * D;
+  const int key = it.k0 + 32 * w + n;  // this lane's key (N index of every product)
+
+  // This lane's key row: K and V fragments (B operands of S = Q K^T and dP = dO V^T).
+  const int nkeys = it.k_limit - it.k0;
+  const rsrc_t rk = make_rsrc(K + int64_t(it.k0) * kv_stride + g * D, nkeys * kv_stride * 2);
+  const rsrc_t rv = make_rsrc(V + int64_t(it.k0) * kv_stride + g * D, nkeys * kv_stride * 2);
+  const uint32_t k_off = uint32_t(((32 * w + n) * kv_stride + 8 * half) * 2);
+  u32x4_t kf[DSTEPS], vf[DSTEPS];
+#pragma unroll
+  for (int s = 0; s < DSTEPS; ++s) {
+    kf[s] = buf_load16(rk, k_off + 32 * s);
+    vf[s] = buf_load16(rv, k_off + 32 * s);
+  }
+  // Transposed reads of the row tiles (the forward's V^T pattern, rows in place of keys).
+  const int vs = lane & 15, vdh = (lane >> 4) & 1;
+  const int r_lane = (4 * half + (vs >> 2)) * VROW + 16 * vdh + 4 * (vs & 3);
+
+  f32x16_t ak[DBLK], av[DBLK];
+#pragma unroll
+  for (int b = 0; b < DBLK; ++b) {
+    ak[b] = f32x16_t{};
+    av[b] = f32x16_t{};
+  }
+  // Row steps: the causal range first, then the unmasked one.
+  const int nC = it.c1 > it.c0 ? (it.c1 - it.c0 + TR - 1) / TR : 0;
+  const int nU = it.u1 > it.u0 ? (it.u1 - it.u0 + TR - 1) / TR : 0;
+  for (int i = 0; i < nC + nU; ++i) {
+    const bool causal = i < nC;
+    const int t0 = causal ? it.c0 + i * TR : it.u0 + (i - nC) * TR;
+    const int tend = causal ? it.c1 : it.u1;
+    const int ntok = min(TR, tend - t0);
+    __syncthreads();  // the previous step's LDS reads are done
+    {
+      // 32 rows x KCH chunks of Q and of dO: row rr = token rr / G, head g G + rr % G.
+      const rsrc_t rq = make_rsrc(Q + (int64_t(t0) * Hq + g * G) * D, ntok * q_stride * 2);
+      const rsrc_t rd = make_rsrc(dO + (int64_t(t0) * Hq + g * G) * D, ntok * q_stride * 2);
+#pragma unroll
+      for (int p = 0; p < 32 * KCH / 128; ++p) {
+        const int u = p * 128 + tid, rr = u / KCH, c = u % KCH;
+        const uint32_t off = uint32_t(((rr / G) * q_stride + (rr % G) * D + 8 * c) * 2);
+        *reinterpret_cast<u32x4_t*>(&sq[rr * VROW + 8 * c]) = buf_load16(rq, off);
+        *reinterpret_cast<u32x4_t*>(&sd[rr * VROW + 8 * c]) = buf_load16(rd, off);
+      }
+      if (tid < 32) {
+        const int tok = t0 + tid / G;
+        const bool ok = tid / G < ntok;
+        const int64_t rix = int64_t(tok) * Hq + g * G + tid % G;
+        sl[tid] = ok ? lse[rix] * kLog2e : INFINITY;  // rows past the range get P = 0
+        sr[tid] = ok ? dvec[rix] : 0.f;
+      }
+    }
+    __syncthreads();
+    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+    const uint16_t* qp = &sq[n * VROW + 8 * half];
+    const uint16_t* dq = &sd[n * VROW + 8 * half];
+#pragma unroll
+    for (int st = 0; st < DSTEPS; ++st) {
+      s = mfma32(load16(qp + 16 * st), kf[st], s);
+      dp = mfma32(load16(dq + 16 * st), vf[st], dp);
+    }
+    // Register r holds row 8 (r / 4) + 4 half + r % 4 of the step (token t0 + row / G) for this
+    // lane's key.  Causal rows read the key only if its token is not before the key.
+    uint32_t pp[8], pd[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float p[2], ds[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int rr = 8 * (r >> 2) + 4 * half + (r & 3) + e;
+        const bool ok = !causal || key <= t0 + rr / G;
+        p[e] = ok ? fast_exp2(fmaf(s[r + e], scale_log2, -sl[rr])) : 0.f;
+        ds[e] = p[e] * (dp[r + e] - sr[rr]);
+      }
+      pp[r >> 1] = pack_bf16x2(p[0], p[1]);
+      pd[r >> 1] = pack_bf16x2(ds[0], ds[1]);
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const u32x4_t bp = {pp[4 * m], pp[4 * m + 1], pp[4 * m + 2], pp[4 * m + 3]};
+      const u32x4_t bd = {pd[4 * m], pd[4 * m + 1], pd[4 * m + 2], pd[4 * m + 3]};
+      const uint16_t* dpt = &sd[r_lane + 16 * m * VROW];
+      const uint16_t* qpt = &sq[r_lane + 16 * m * VROW];
+#pragma unroll
+      for (int b = 0; b < DBLK; ++b) {
+        const u32x2_t dlo = lds_read_tr16(dpt + 32 * b), dhi = lds_read_tr16(dpt + 8 * VROW + 32 * b);
+        av[b] = mfma32(u32x4_t{dlo[0], dlo[1], dhi[0], dhi[1]}, bp, av[b]);
+        const u32x2_t qlo = lds_read_tr16(qpt + 32 * b), qhi = lds_read_tr16(qpt + 8 * VROW + 32 * b);
+        ak[b] = mfma32(u32x4_t{qlo[0], qlo[1], qhi[0], qhi[1]}, bd, ak[b]);
+      }
+    }
+  }
+  if (key >= it.k_limit) return;
+  // ak / av[b] register r holds head-dim element 32 b + 8 (r / 4) + 4 half + r % 4 of this key.
+  float *pk_, *pv_;
+  if (it.slot < 0) {
+    pk_ = dK + (int64_t(key) * Hkv + g) * D;
+    pv_ = dV + (int64_t(key) * Hkv + g) * D;
+  } else {
+    const int64_t base = ((int64_t(it.slot) * Hkv + g) * kBwdKeyTile + 32 * w + n) * D;
+    pk_ = part_dkv + base;
+    pv_ = part_dkv + int64_t(kv_slots) * Hkv * kBwdKeyTile * D + base;
+  }
+#pragma unroll
+  for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 32 * b + 8 * j + 4 * half;
+      *reinterpret_cast<f32x4_t*>(pk_ + e) =
+          f32x4_t{ak[b][4 * j], ak[b][4 * j + 1], ak[b][4 * j + 2], ak[b][4 * j + 3]} * scale;
+      *reinterpret_cast<f32x4_t*>(pv_ + e) = f32x4_t{av[b][4 * j], av[b][4 * j + 1], av[b][4 * j + 2], av[b][4 * j + 3]};
+    }
+}
+
+// Sum the split dK / dV partials of one key tile (fixed order).  One thread per (key, 4 elements).
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_dkv_merge_kernel(float* __restrict__ dK, float* __restrict__ dV,
+                                                                 const KvMerge* __restrict__ merges,
+                                                                 const float* __restrict__ part_dkv, int Hkv,
+                                                                 int kv_slots) {
+  constexpr int CH = D / 4;
+  constexpr int WG_PER_TILE = kBwdKeyTile * CH / 256;
+  const int tile = blockIdx.x / WG_PER_TILE, part = blockIdx.x % WG_PER_TILE;
+  const int g = tile % Hkv;
+  const KvMerge mi = merges[tile / Hkv];
+  const int unit = part * 256 + threadIdx.x;
+  const int kk = unit / CH, ch = unit % CH;
+  const int key = mi.k0 + kk;
+  if (key >= mi.k_limit) return;
+  const int64_t stride = int64_t(Hkv) * kBwdKeyTile * D;
+  const float* src = part_dkv + ((int64_t(mi.slot0) * Hkv + g) * kBwdKeyTile + kk) * D + 4 * ch;
+  const float* srcv = src + int64_t(kv_slots) * stride;
+  f32x4_t a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < mi.nslots; ++c) {
+    a += *reinterpret_cast<const f32x4_t*>(src + c * stride);
+    b += *reinterpret_cast<const f32x4_t*>(srcv + c * stride);
+  }
+  *reinterpret_cast<f32x4_t*>(dK + (int64_t(key) * Hkv + g) * D + 4 * ch) = a;
+  *reinterpret_cast<f32x4_t*>(dV + (int64_t(key) * Hkv + g) * D + 4 * ch) = b;
+}
+
+template <int D, int G>
+static hipError_t launch_bwd_t(const BwdLaunch& a, hipStream_t stream) {
+  const int64_t rows = a.total_tokens * a.num_q_heads;
+  const int64_t lanes = rows * (D / 8);
+  attn_bwd_rowdot_kernel<D><<<unsigned((lanes + 255) / 256), 256, 0, stream>>>(a.O, a.dO, a.dvec, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.n_items > 0) {
+    attn_bwd_dq_kernel<D, G><<<unsigned(a.n_items * a.num_kv_heads), 256, 0, stream>>>(
+        a.Q, a.K, a.V, a.dO, a.lse, a.dvec, a.dQ, a.items, a.part_dq, a.num_q_heads, a.num_kv_heads, a.scale,
+        a.scale * kLog2e);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.n_merges > 0) {
+    attn_bwd_dq_merge_kernel<D><<<unsigned(a.n_merges * a.num_kv_heads * (kRowsPerTile * (D / 4) / 256)), 256, 0,
+                                  stream>>>(a.dQ, a.merges, a.part_dq, a.num_q_heads, a.num_kv_heads, G);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.n_kv_items > 0) {
+    attn_bwd_dkv_kernel<D, G><<<unsigned(a.n_kv_items * a.num_kv_heads), 128, 0, stream>>>(
+        a.Q, a.K, a.V, a.dO, a.lse, a.dvec, a.dK, a.dV, a.kv_items, a.part_dkv, a.num_q_heads, a.num_kv_heads,
+        a.kv_slots, a.scale, a.scale * kLog2e);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.n_kv_merges > 0) {
+    attn_bwd_dkv_merge_kernel<D><<<unsigned(a.n_kv_merges * a.num_kv_heads * (kBwdKeyTile * (D / 4) / 256)), 256,
+                                   0, stream>>>(a.dK, a.dV, a.kv_merges, a.part_dkv, a.num_kv_heads, a.kv_slots);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+hipError_t launch_attn_bwd(const BwdLaunch& a, hipStream_t stream) {
+  const int G = a.num_q_heads / a.num_kv_heads;
+  if (a.head_dim == 128) {
+    switch (G) {
+      case 1: return launch_bwd_t<128, 1>(a, stream);
+      case 2: return launch_bwd_t<128, 2>(a, stream);
+      case 4: return launch_bwd_t<128, 4>(a, stream);
+      default: return launch_bwd_t<128, 8>(a, stream);
+    }
+  }
+  switch (G) {
+    case 1: return launch_bwd_t<64, 1>(a, stream);
+    case 2: return launch_bwd_t<64, 2>(a, stream);
+    case 4: return launch_bwd_t<64, 4>(a, stream);
+    default: return launch_bwd_t<64, 8>(a, stream);
+  }
+}
+
+}  // namespace br

@@ -48,6 +48,23 @@ constexpr int kSortPromptsPerLaunch = 256;
 hipError_t launch_sort_docs(const float* scores, const int32_t* prompt_base, int num_prompts, int32_t* order,
                             hipStream_t stream);
 
+struct BwdLaunch {
+  const uint16_t *Q, *K, *V, *O, *dO;
+  const float* lse;          // [T, Hq] natural-log log-sum-exp from the forward
+  float *dQ, *dK, *dV;       // fp32 outputs
+  float* dvec;               // [T, Hq] workspace: rowsum(dO * O)
+  const AttnItem* items;     // device copies of the forward plan's items and merges
+  const MergeItem* merges;
+  float* part_dq;
+  const KvItem* kv_items;    // device copies of the key-major items and merges
+  const KvMerge* kv_merges;
+  float* part_dkv;
+  int64_t n_items, n_merges, n_kv_items, n_kv_merges, total_tokens;
+  int kv_slots, num_q_heads, num_kv_heads, head_dim;
+  float scale;
+};
+hipError_t launch_attn_bwd(const BwdLaunch& a, hipStream_t stream);
+
 struct RopeLaunch {
   const uint16_t* q;        // [rows, q_heads, head_dim] or nullptr (q_heads == 0)
   uint16_t* q_out;          // may equal q

@@ -496,4 +496,56 @@ Error build_rope_signal_plan(const br_dims& dims, int32_t n_signal, const int32_
   return {};
 }
 
+// ---------------------------------------------------------------------------------------------
+// backward plan
+
+Error build_bwd_plan(const br_dims& dims, const int32_t* so, const int32_t* sp, BwdPlan* plan) {
+  *plan = BwdPlan{};
+  Error e = build_attn_plan(dims, so, sp, &plan->fwd);
+  if (!e.ok()) return e;
+  BwdPlan& P = *plan;
+  auto add_keys = [&](int64_t ks, int64_t ke, int64_t u0, int64_t u1) {
+    for (int64_t k0 = ks; k0 < ke; k0 += kBwdKeyTile) {
+      const int64_t kl = std::min<int64_t>(k0 + kBwdKeyTile, ke);
+      const int64_t nu = u1 > u0 ? u1 - u0 : 0;
+      if (nu <= kBwdRowChunk) {
+        P.kv_items.push_back(KvItem{int32_t(k0), int32_t(kl), int32_t(k0), int32_t(ke), int32_t(nu ? u0 : 0),
+                                    int32_t(nu ? u1 : 0), -1, int32_t(ke - k0 + nu)});
+        continue;
+      }
+      const int32_t slot0 = P.kv_slots;
+      int32_t n = 0;
+      for (int64_t a = u0; a < u1; a += kBwdRowChunk, ++n) {
+        const int64_t b = std::min<int64_t>(a + kBwdRowChunk, u1);
+        const bool first = a == u0;  // the first chunk also takes the causal rows
+        P.kv_items.push_back(KvItem{int32_t(k0), int32_t(kl), int32_t(first ? k0 : 0), int32_t(first ? ke : 0),
+                                    int32_t(a), int32_t(b), slot0 + n, int32_t((first ? ke - k0 : 0) + (b - a))});
+      }
+      P.kv_merges.push_back(KvMerge{int32_t(k0), int32_t(kl), slot0, n});
+      P.kv_slots += n;
+    }
+  };
+  for (int b = 0; b < dims.num_prompts; ++b) {
+    const int32_t* o = so + sp[b];
+    const int n = sp[b + 1] - sp[b];
+    const int64_t ps = o[0], pe = o[1], qs = o[n - 2], qe = o[n - 1];
+    add_keys(ps, pe, pe, qe);                                      // instruction keys: every later row
+    for (int k = 1; k <= n - 3; ++k) add_keys(o[k], o[k + 1], qs, qe);  // document keys: the query
+    add_keys(qs, qe, 0, 0);                                        // query keys: the query, causally
+  }
+  // Longest items first, so that the split instruction chunks start early.
+  std::stable_sort(P.kv_items.begin(), P.kv_items.end(),
+                   [](const KvItem& x, const KvItem& y) { return x.rows > y.rows; });
+  const size_t hkv = size_t(dims.num_kv_heads), hq = size_t(dims.num_q_heads), d = size_t(dims.head_dim);
+  P.off_items = 0;
+  P.off_merges = align_up(P.fwd.items.size() * sizeof(AttnItem), 256);
+  P.off_kv_items = align_up(P.off_merges + P.fwd.merges.size() * sizeof(MergeItem), 256);
+  P.off_kv_merges = align_up(P.off_kv_items + P.kv_items.size() * sizeof(KvItem), 256);
+  P.off_part_dq = align_up(P.off_kv_merges + P.kv_merges.size() * sizeof(KvMerge), 256);
+  P.off_part_dkv = align_up(P.off_part_dq + size_t(P.fwd.n_slots) * hkv * kRowsPerTile * d * 4, 256);
+  P.off_dvec = align_up(P.off_part_dkv + size_t(P.kv_slots) * hkv * kBwdKeyTile * d * 4 * 2, 256);
+  P.total_bytes = align_up(P.off_dvec + size_t(dims.total_tokens) * hq * 4, 256);
+  return {};
+}
+
 }  // namespace br

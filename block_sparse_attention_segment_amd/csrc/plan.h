@@ -72,6 +72,29 @@ struct ScorePlan {
   size_t off_items = 0, off_doc_offsets = 0, off_prompt_base = 0, off_ml = 0, total_bytes = 0;
 };
 
+// Backward of the attention.  dQ is query-major over the forward plan's items (split query
+// tiles write fp32 partials summed afterwards); dK and dV are key-major: an item holds keys
+// [k0, k_limit) of one segment (at most kBwdKeyTile) and the rows that read them, [c0, c1)
+// causally (row token >= key) and [u0, u1) unmasked.  Long unmasked row ranges (the rows that
+// read the instruction) are split into chunks of kBwdRowChunk tokens with fp32 partials.
+constexpr int kBwdKeyTile = 64;
+constexpr int kBwdRowChunk = 4096;
+struct KvItem {
+  int32_t k0, k_limit, c0, c1, u0, u1, slot, rows;  // rows: row tokens visited (for accounting)
+};
+static_assert(sizeof(KvItem) == 32, "KvItem is read as two int4 by the kernel");
+struct KvMerge {
+  int32_t k0, k_limit, slot0, nslots;
+};
+struct BwdPlan {
+  AttnPlan fwd;
+  std::vector<KvItem> kv_items;
+  std::vector<KvMerge> kv_merges;
+  int32_t kv_slots = 0;
+  size_t off_items = 0, off_merges = 0, off_part_dq = 0, off_kv_items = 0, off_kv_merges = 0, off_part_dkv = 0,
+         off_dvec = 0, total_bytes = 0;
+};
+
 // Rotary embedding runs: rows [start[r], start[r + 1]) take positions pos0[r] + (row - start[r]).
 // Runs are non-empty and ascending; start has n_runs + 1 entries, the last being the row count.
 struct RopePlan {
@@ -115,6 +138,9 @@ Error validate_docs(const br_dims& dims, int32_t n_signal, const int32_t* doc_of
                     const int32_t* doc_ptr);
 Error build_score_plan(const br_dims& dims, int32_t n_signal, const int32_t* doc_offsets,
                        const int32_t* doc_ptr, ScorePlan* plan);
+
+// Backward plan: the forward plan's items for dQ, key-major items for dK and dV, workspace layout.
+Error build_bwd_plan(const br_dims& dims, const int32_t* segment_offsets, const int32_t* seg_ptr, BwdPlan* plan);
 
 // Permutation-invariant positions: instruction token i at i; token j of a document at
 // j + (docs_after_instruction ? instruction length : 0); query token i at query_pos0 + i.

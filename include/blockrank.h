@@ -209,6 +209,40 @@ br_status br_attn_plan_schedule(const br_dims* dims, const int32_t* segment_offs
                                 int64_t* n_items, int32_t* wg_per_head);
 
 /*
+ * Backward of br_attn_fwd (BlockRank summary, section 3.4: the auxiliary loss's gradient flows
+ * back through this attention).  For the upstream gradient dO, with P = softmax over the allowed
+ * keys of scale * Q K^T (recomputed from lse, never stored):
+ *   dV = P^T dO,  dS = P * (dO V^T - rowsum(dO * O)),  dQ = scale * dS K,  dK = scale * dS^T Q,
+ * where grouped query heads add into their KV head's dK and dV.  Only allowed pairs are visited.
+ *   Q, O, dO: device bf16 [total_tokens, Hq, d];  K, V: device bf16 [total_tokens, Hkv, d];
+ *   lse: device fp32 [total_tokens, Hq], natural-log log-sum-exp from br_attn_fwd with the same
+ *        softmax_scale;  O: br_attn_fwd's output.
+ *   dQ: device fp32 [total_tokens, Hq, d];  dK, dV: device fp32 [total_tokens, Hkv, d]; every
+ *       element is written.
+ *   Segment tables, scale, alignment and errors as br_attn_fwd; workspace as sized by
+ *   br_attn_bwd_workspace_bytes (it also holds rowsum(dO * O) and split partial sums).
+ * Arithmetic: P and dS in fp32, rounded to bf16 for the P^T dO, dS K and dS^T Q products,
+ * fp32 accumulation; split partial sums are added in a fixed order (deterministic).
+ */
+br_status br_attn_bwd_workspace_bytes(const br_dims* dims, const int32_t* segment_offsets,
+                                      const int32_t* seg_ptr, size_t* bytes);
+br_status br_attn_bwd(const br_dims* dims, const void* Q, const void* K, const void* V, const void* O,
+                      const void* dO, const float* lse, const int32_t* segment_offsets,
+                      const int32_t* seg_ptr, float* dQ, float* dK, float* dV, float softmax_scale,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Host-only introspection of the backward's key-major plan (no HIP call).  Writes up to
+ * `capacity` items of 8 int32 each, {k0, k_limit, c0, c1, u0, u1, partial_slot, row_tokens}:
+ * keys [k0, k_limit) of one segment, read causally (row token >= key) by rows [c0, c1) and
+ * unmasked by rows [u0, u1); partial_slot >= 0 marks one chunk of a split row range.
+ * *n_items and *n_slots receive the counts; items is written only if capacity suffices.
+ */
+br_status br_attn_bwd_plan_items(const br_dims* dims, const int32_t* segment_offsets,
+                                 const int32_t* seg_ptr, int32_t* items, int64_t capacity,
+                                 int64_t* n_items, int32_t* n_slots);
+
+/*
  * SSMax logit factor (BlockSearch, section 5.1, length-aware softmax): SSMax multiplies the
  * pre-softmax scores q.k / sqrt(d) by s * ln N, N the number of documents of the prompt.  Writes
  * *scale = s * ln(n_docs) / sqrt(head_dim), the value to pass as softmax_scale to

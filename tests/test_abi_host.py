@@ -333,3 +333,40 @@ def test_rope_rejects_before_any_hip_call():
     assert sig(f, f, 4, segp, spp, 10000.0, 8192, 0, f, 0, None) == WS
     pos = np.zeros(int(seg[-1]) - 1, dtype=np.int32)
     assert lib.br_rope_positions(ctypes.byref(dims), segp, spp, 8192, 1, p(pos), pos.size) == INV  # too small
+
+
+# ---- attention backward plan (host side only) ----
+@pytest.mark.parametrize("seed", range(6))
+def test_bwd_plan_covers_exactly_the_mask(seed):
+    """Every allowed (row, key) pair is visited by exactly one key-major item, no forbidden pair is,
+    and every key lies in exactly one key tile (split tiles: the same keys in every chunk).  The
+    last case has more than 4096 rows after the instruction, so its instruction keys are split."""
+    rng = random.Random(100 + seed)
+    if seed == 5:
+        prompts = [(70, [180] * 25, 20)]
+    else:
+        prompts = random_prompts(rng, batch=rng.randint(1, 3), p_max=40, n_max=6, l_max=90, q_max=40)
+    seg, sp, _, _ = workloads.segment_tables(prompts)
+    T = int(seg[-1])
+    dims = br.make_dims(len(prompts), 8, 2, 64, T)
+    items, slots = br._lib.attn_bwd_plan_items(dims, seg, sp)
+    cover = np.zeros((T, T), dtype=np.int32)
+    key_owner = {}
+    for k0, kl, c0, c1, u0, u1, slot, _ in items:
+        assert 0 <= k0 < kl <= T and kl - k0 <= 64
+        key_owner.setdefault((k0, kl), set()).add(slot)
+        for r in range(c0, c1):
+            cover[r, k0:min(kl, r + 1)] += 1
+        if u1 > u0:
+            cover[u0:u1, k0:kl] += 1
+    tables = orc.token_tables(seg, sp)
+    idx = np.arange(T)
+    allowed = orc.allowed(idx[:, None], idx[None, :], tables)
+    assert (cover[allowed] == 1).all(), "an allowed pair is missed or visited twice"
+    assert (cover[~allowed] == 0).all(), "a forbidden pair is visited"
+    keys = sorted(key_owner)
+    assert keys[0][0] == 0 and keys[-1][1] == T
+    assert all(a[1] == b[0] for a, b in zip(keys[:-1], keys[1:])), "key tiles do not tile the keys"
+    used = sorted(s_ for v in key_owner.values() for s_ in v if s_ >= 0)
+    assert used == list(range(slots))
+    assert seed != 5 or slots > 0
