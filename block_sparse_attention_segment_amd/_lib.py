@@ -21,6 +21,7 @@ BR_OK, BR_ERR_INVALID_ARG, BR_ERR_UNSUPPORTED, BR_ERR_WORKSPACE, BR_ERR_HIP = ra
 EXPORTED = ("br_attn_workspace_bytes", "br_attn_fwd", "br_attn_fwd_timed", "br_doc_scores_workspace_bytes", "br_doc_scores",
             "br_sort_docs", "br_attn_plan_items", "br_attn_plan_schedule", "br_query_attn_workspace_bytes", "br_query_attn_fwd", "br_attn_routed_workspace_bytes", "br_attn_routed_fwd",
             "br_attn_bwd_workspace_bytes", "br_attn_bwd", "br_attn_bwd_plan_items",
+            "br_infonce_workspace_bytes", "br_infonce", "br_doc_scores_bwd_workspace_bytes", "br_doc_scores_bwd",
             "br_ssmax_softmax_scale", "br_rope_workspace_bytes", "br_rope_fwd", "br_rope_signal_fwd", "br_rope_positions",
             "br_status_string", "br_last_error", "br_version")
 
@@ -76,6 +77,11 @@ def load_library() -> ctypes.CDLL:
                         _P],
         "br_attn_bwd_plan_items": [dims_p, _I32P, _I32P, _I32P, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64),
                                    ctypes.POINTER(ctypes.c_int32)],
+        "br_infonce_workspace_bytes": [ctypes.c_int32, sz_p],
+        "br_infonce": [_P, _I32P, ctypes.c_int32, _I32P, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P],
+        "br_doc_scores_bwd_workspace_bytes": [dims_p, ctypes.c_int32, _I32P, _I32P, sz_p],
+        "br_doc_scores_bwd": [dims_p, _P, ctypes.c_int32, _P, _I32P, _I32P, _P, _P, _P, ctypes.c_int32, ctypes.c_float,
+                              _P, ctypes.c_size_t, _P],
         "br_ssmax_softmax_scale": [ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_float)],
         "br_rope_workspace_bytes": [dims_p, _I32P, sz_p],
         "br_rope_fwd": [dims_p, _P, _P, _P, _P, _I32P, _I32P, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
@@ -300,6 +306,61 @@ def attn_bwd(Q, K, V, O, dO, lse, segment_offsets, seg_ptr, softmax_scale: float
                            lse.data_ptr(), _ptr_i32(so), _ptr_i32(sp), dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(),
                            float(softmax_scale), workspace.data_ptr(), workspace.numel(), _stream_handle(stream)))
     return dQ, dK, dV
+
+
+def infonce(scores, doc_ptr, gold, tau: float = 0.05, loss=None, dscores=None, workspace=None, stream=None):
+    """Per-prompt InfoNCE loss [B] and its gradient with respect to the scores [sum N_b] (fp32)."""
+    import torch
+    lib = load_library()
+    if scores.dtype != torch.float32 or not scores.is_cuda or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous float32 CUDA tensor")
+    dp, gd = _host_i32(doc_ptr), _host_i32(gold)
+    B = len(dp) - 1
+    if len(gd) != B:
+        raise ValueError("gold must have one entry per prompt")
+    loss = torch.empty(B, dtype=torch.float32, device=scores.device) if loss is None else loss
+    dscores = torch.empty_like(scores) if dscores is None else dscores
+    out = ctypes.c_size_t(0)
+    _check(lib.br_infonce_workspace_bytes(B, ctypes.byref(out)))
+    if workspace is None or workspace.numel() < out.value:
+        workspace = torch.empty(out.value, dtype=torch.uint8, device=scores.device)
+    _check(lib.br_infonce(scores.data_ptr(), _ptr_i32(dp), B, _ptr_i32(gd), float(tau), loss.data_ptr(),
+                          dscores.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream_handle(stream)))
+    return loss, dscores
+
+
+def doc_scores_bwd_workspace_bytes(dims: BrDims, n_signal: int, doc_offsets, doc_ptr) -> int:
+    lib = load_library()
+    do, dp = _host_i32(doc_offsets), _host_i32(doc_ptr)
+    out = ctypes.c_size_t(0)
+    _check(lib.br_doc_scores_bwd_workspace_bytes(ctypes.byref(dims), int(n_signal), _ptr_i32(do), _ptr_i32(dp),
+                                                 ctypes.byref(out)))
+    return int(out.value)
+
+
+def doc_scores_bwd(Q_S, K, doc_offsets, doc_ptr, dscores, softmax_scale: float = 0.0, dQ_S=None, dK=None,
+                   accumulate: bool = False, workspace=None, stream=None):
+    """Gradient of sum_k dscores_k s_k through the readout: dQ_S [B,S,Hq,d] and dK [T,Hkv,d] (fp32).
+    dK rows of document tokens are written (or added to with accumulate=True); a new dK is zeroed."""
+    import torch
+    lib = load_library()
+    _check_bf16("Q_S", Q_S, 4)
+    _check_bf16("K", K, 3)
+    if dscores.dtype != torch.float32 or not dscores.is_cuda or not dscores.is_contiguous():
+        raise ValueError("dscores must be a contiguous float32 CUDA tensor")
+    B, S, Hq, d = Q_S.shape
+    T, Hkv, _ = K.shape
+    do, dp = _host_i32(doc_offsets), _host_i32(doc_ptr)
+    dims = make_dims(B, Hq, Hkv, d, T)
+    dQ_S = torch.empty((B, S, Hq, d), dtype=torch.float32, device=K.device) if dQ_S is None else dQ_S
+    dK = torch.zeros((T, Hkv, d), dtype=torch.float32, device=K.device) if dK is None else dK
+    nbytes = doc_scores_bwd_workspace_bytes(dims, S, do, dp)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=K.device)
+    _check(lib.br_doc_scores_bwd(ctypes.byref(dims), Q_S.data_ptr(), int(S), K.data_ptr(), _ptr_i32(do), _ptr_i32(dp),
+                                 dscores.data_ptr(), dQ_S.data_ptr(), dK.data_ptr(), int(bool(accumulate)),
+                                 float(softmax_scale), workspace.data_ptr(), workspace.numel(), _stream_handle(stream)))
+    return dQ_S, dK
 
 
 def ssmax_scale(s: float, n_docs: int, head_dim: int) -> float:

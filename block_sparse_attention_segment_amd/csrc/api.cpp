@@ -765,4 +765,142 @@ br_status br_attn_bwd_plan_items(const br_dims* dims, const int32_t* segment_off
   });
 }
 
+br_status br_infonce_workspace_bytes(int32_t num_prompts, size_t* bytes) {
+  return guarded([&]() -> br_status {
+    if (!bytes) return record(BR_ERR_INVALID_ARG, "bytes is NULL");
+    if (num_prompts < 1) return record(BR_ERR_INVALID_ARG, "num_prompts must be >= 1");
+    *bytes = br::infonce_workspace_bytes(num_prompts);
+    return BR_OK;
+  });
+}
+
+br_status br_infonce(const float* scores, const int32_t* doc_ptr, int32_t num_prompts, const int32_t* gold, float tau,
+                     float* loss, float* dscores, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return guarded([&]() -> br_status {
+    if (!scores || !loss || !dscores) return record(BR_ERR_INVALID_ARG, "scores, loss and dscores must be non-NULL");
+    if (!aligned(scores, 4) || !aligned(loss, 4) || !aligned(dscores, 4))
+      return record(BR_ERR_INVALID_ARG, "scores, loss and dscores must be 4-byte aligned");
+    br::Error e = br::validate_infonce(num_prompts, doc_ptr, gold, tau);
+    if (!e.ok()) return record(e);
+    const size_t need = br::infonce_workspace_bytes(num_prompts);
+    if (!workspace || workspace_bytes < need)
+      return record(BR_ERR_WORKSPACE, "workspace is NULL or smaller than br_infonce_workspace_bytes() = " +
+                                          std::to_string(need));
+    if (!aligned(workspace, 16)) return record(BR_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    const size_t off_gold = br::align_up(size_t(num_prompts + 1) * 4, 256);
+    std::vector<unsigned char> host(need, 0);
+    int32_t* pb = reinterpret_cast<int32_t*>(host.data());
+    for (int b = 0; b <= num_prompts; ++b) pb[b] = doc_ptr[b] - b;
+    std::memcpy(host.data() + off_gold, gold, size_t(num_prompts) * 4);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    br_status st = upload(ws, host.data(), host.size(), stream);
+    if (st != BR_OK) return st;
+    hipError_t he = br::launch_infonce(scores, reinterpret_cast<const int32_t*>(ws),
+                                       reinterpret_cast<const int32_t*>(ws + off_gold), tau, num_prompts, loss, dscores,
+                                       stream);
+    if (he != hipSuccess) return hip_fail(he, "InfoNCE kernel launch");
+    return BR_OK;
+  });
+}
+
+br_status br_doc_scores_bwd_workspace_bytes(const br_dims* dims, int32_t n_signal, const int32_t* doc_offsets,
+                                            const int32_t* doc_ptr, size_t* bytes) {
+  return guarded([&]() -> br_status {
+    if (!bytes) return record(BR_ERR_INVALID_ARG, "bytes is NULL");
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    br::DocBwdPlan plan;
+    e = br::build_doc_bwd_plan(*dims, n_signal, doc_offsets, doc_ptr, &plan);
+    if (!e.ok()) return record(e);
+    *bytes = plan.total_bytes;
+    return BR_OK;
+  });
+}
+
+br_status br_doc_scores_bwd(const br_dims* dims, const void* Q_S, int32_t n_signal, const void* K,
+                            const int32_t* doc_offsets, const int32_t* doc_ptr, const float* dscores, float* dQ_S,
+                            float* dK, int32_t accumulate, float softmax_scale, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  return guarded([&]() -> br_status {
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    if (!Q_S || !K || !dscores || !dQ_S || !dK)
+      return record(BR_ERR_INVALID_ARG, "Q_S, K, dscores, dQ_S and dK must be non-NULL device pointers");
+    if (!aligned(Q_S, 16) || !aligned(K, 16) || !aligned(dQ_S, 16) || !aligned(dK, 16) || !aligned(dscores, 4))
+      return record(BR_ERR_INVALID_ARG, "Q_S, K, dQ_S and dK must be 16-byte aligned (dscores 4-byte)");
+    if (accumulate != 0 && accumulate != 1) return record(BR_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+    if (std::isnan(softmax_scale) || std::isinf(softmax_scale))
+      return record(BR_ERR_INVALID_ARG, "softmax_scale must be finite");
+    br::DocBwdPlan plan;
+    e = br::build_doc_bwd_plan(*dims, n_signal, doc_offsets, doc_ptr, &plan);
+    if (!e.ok()) return record(e);
+    if (!workspace || workspace_bytes < plan.total_bytes)
+      return record(BR_ERR_WORKSPACE, "workspace is NULL or smaller than br_doc_scores_bwd_workspace_bytes() = " +
+                                          std::to_string(plan.total_bytes));
+    if (!aligned(workspace, 16)) return record(BR_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    const br::ScorePlan& sp = plan.fwd;
+    const int B = dims->num_prompts;
+    std::vector<unsigned char> host(sp.off_ml, 0);
+    std::memcpy(host.data() + sp.off_items, sp.items.data(), sp.items.size() * sizeof(br::ScoreItem));
+    std::memcpy(host.data() + sp.off_doc_offsets, doc_offsets, size_t(doc_ptr[B]) * sizeof(int32_t));
+    std::memcpy(host.data() + sp.off_prompt_base, sp.prompt_score_base.data(), size_t(B + 1) * sizeof(int32_t));
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    br_status st = upload(ws, host.data(), host.size(), stream);
+    if (st != BR_OK) return st;
+    std::vector<int32_t> pitems((size_t(B + 1) + 3) / 4 * 4, 0);  // padded to 16 bytes
+    std::copy(plan.prompt_items.begin(), plan.prompt_items.end(), pitems.begin());
+    st = upload(ws + plan.off_prompt_items, pitems.data(), pitems.size() * 4, stream);
+    if (st != BR_OK) return st;
+
+    br::ScoreLaunch a;
+    a.Q_S = static_cast<const uint16_t*>(Q_S);
+    a.K = static_cast<const uint16_t*>(K);
+    a.items = reinterpret_cast<const br::ScoreItem*>(ws + sp.off_items);
+    a.doc_offsets = reinterpret_cast<const int32_t*>(ws + sp.off_doc_offsets);
+    a.prompt_base = reinterpret_cast<const int32_t*>(ws + sp.off_prompt_base);
+    a.ml = reinterpret_cast<float2*>(ws + sp.off_ml);
+    a.scores = nullptr;
+    a.head_scores = nullptr;
+    a.n_items = int64_t(sp.items.size());
+    a.num_prompts = B;
+    a.num_q_heads = dims->num_q_heads;
+    a.num_kv_heads = dims->num_kv_heads;
+    a.head_dim = dims->head_dim;
+    a.n_signal = n_signal;
+    a.row_blocks = sp.row_blocks;
+    a.n_docs = sp.n_docs;
+    const float scale = resolve_scale(softmax_scale, dims->head_dim);
+    a.scale_log2 = scale * 1.4426950408889634f;
+    hipError_t he = br::launch_doc_stats(a, stream);
+    if (he != hipSuccess) return hip_fail(he, "readout statistics launch");
+
+    br::DocBwdLaunch l;
+    l.Q_S = a.Q_S;
+    l.K = a.K;
+    l.items = a.items;
+    l.doc_offsets = a.doc_offsets;
+    l.prompt_base = a.prompt_base;
+    l.prompt_items = reinterpret_cast<const int32_t*>(ws + plan.off_prompt_items);
+    l.ml = a.ml;
+    l.rowstat = a.ml + int64_t(sp.n_docs) * n_signal * dims->num_q_heads;
+    l.center = reinterpret_cast<float*>(ws + plan.off_center);
+    l.dscores = dscores;
+    l.dK = dK;
+    l.part = reinterpret_cast<float*>(ws + plan.off_part);
+    l.dQ_S = dQ_S;
+    l.n_items = a.n_items;
+    l.num_prompts = B;
+    l.num_q_heads = dims->num_q_heads;
+    l.num_kv_heads = dims->num_kv_heads;
+    l.head_dim = dims->head_dim;
+    l.n_signal = n_signal;
+    l.row_blocks = sp.row_blocks;
+    l.accumulate = accumulate;
+    l.scale = scale;
+    he = br::launch_doc_bwd(l, stream);
+    if (he != hipSuccess) return hip_fail(he, "readout backward launch");
+    return BR_OK;
+  });
+}
+
 }  // extern "C"

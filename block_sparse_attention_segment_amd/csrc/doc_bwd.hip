@@ -1,0 +1,282 @@
+// Backward of the attention-mass readout and the InfoNCE auxiliary loss on gfx950 (BlockRank
+// summary, section 3.4: L_aux = -log(exp(s_gold / tau) / sum_k exp(s_k / tau)), tau = 0.05,
+// whose gradient flows back through the readout's attention; blog, attention supervision).
+//
+//   infonce_kernel    per prompt: loss and g_k = dL/ds_k = (softmax(s / tau)_k - [k = gold]) / tau.
+//   doc_center_kernel per (prompt, signal row r): c_r = sum_k mass_rk g_k, with mass_rk the row's
+//                     readout weight on document k (from the forward's (m_k, e_k) and (M, 1/Z)).
+//   doc_bwd_kernel    one wave per (document group, KV head): streams the group's keys once,
+//                     32 at a time inside one document.  With alpha = softmax over the prompt's
+//                     document tokens of z = scale Q_S K^T and dz = alpha (g_k(j) - c_r) / Hq:
+//                       dQ_S^T += K^T dz^T   (z^T with keys on M, K^T read transposed from LDS)
+//                       dK^T    = Q_S^T dz   (z with signal rows on M, Q_S^T read transposed)
+//                     Both orientations of z come from the same register fragments.  dK rows of
+//                     the keys are written (or added) directly: each key belongs to one group.
+//   doc_bwd_reduce_kernel  sums the per-group dQ_S partials of a prompt in a fixed order.
+#include "device_common.h"
+#include "launch.h"
+#include "plan.h"
+
+namespace br {
+
+__global__ __launch_bounds__(256) void infonce_kernel(const float* __restrict__ scores,
+                                                      const int32_t* __restrict__ prompt_base,
+                                                      const int32_t* __restrict__ gold, float inv_tau,
+                                                      float* __restrict__ loss, float* __restrict__ dscores) {
+  __shared__ float red[256];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int k0 = prompt_base[b], N = prompt_base[b + 1] - k0;
+  float m = -INFINITY;
+  for (int k = tid; k < N; k += 256) m = fmaxf(m, scores[k0 + k] * inv_tau);
+  red[tid] = m;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  float z = 0.f;
+  for (int k = tid; k < N; k += 256) z += expf(scores[k0 + k] * inv_tau - M);
+  red[tid] = z;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
+    __syncthreads();
+  }
+  const float lse = M + logf(red[0]);
+  const int gd = gold[b];
+  for (int k = tid; k < N; k += 256) {
+    const float p = expf(scores[k0 + k] * inv_tau - lse);
+    dscores[k0 + k] = (p - (k == gd ? 1.f : 0.f)) * inv_tau;
+  }
+  if (tid == 0) loss[b] = lse - scores[k0 + gd] * inv_tau;
+}
+
+// c[b * RT + r] = (1/Z_r) sum_k e_k,r 2^(m_k,r - M_r) g_k over prompt b's documents.
+__global__ __launch_bounds__(256) void doc_center_kernel(const float2* __restrict__ ml,
+                                                         const float2* __restrict__ rowstat,
+                                                         const int32_t* __restrict__ prompt_base,
+                                                         const float* __restrict__ dscores, float* __restrict__ center,
+                                                         int RT, int row_groups) {
+  const int b = blockIdx.x / row_groups;
+  const int r = (blockIdx.x % row_groups) * 256 + threadIdx.x;
+  if (r >= RT) return;
+  const float2 st = rowstat[int64_t(b) * RT + r];
+  float c = 0.f;
+  for (int k = prompt_base[b]; k < prompt_base[b + 1]; ++k) {
+    const float2 v = ml[int64_t(k) * RT + r];
+    c = fmaf(v.y * fast_exp2(v.x - st.x), dscores[k], c);
+  }
+  center[int64_t(b) * RT + r] = c * st.y;
+}
+
+template <int D, int RB>
+__global__ __launch_bounds__(64) void doc_bwd_kernel(const uint16_t* __restrict__ Q_S, const uint16_t* __restrict__ K,
+                                                     const ScoreItem* __restrict__ items, const int32_t* __restrict__ dof,
+                                                     const float2* __restrict__ rowstat,
+                                                     const float* __restrict__ center, const float* __restrict__ dscores,
+                                                     float* __restrict__ dK, float* __restrict__ part, int Hq, int Hkv,
+                                                     int n_signal, float scale, float scale_log2, int accumulate) {
+  constexpr int DSTEPS = D / 16, DBLK = D / 32, KCH = D / 8;
+  constexpr int VROW = D == 128 ? 160 : 96;  // row reads and transposing reads (as V in the forward)
+  constexpr int R = RB * 32;                 // signal rows handled (padded)
+  __shared__ __align__(16) uint16_t sk[32 * VROW];
+  __shared__ __align__(16) uint16_t sq[R * VROW];
+  __shared__ float sM[R], sZ[R], sC[R];
+
+  const int g = blockIdx.x % Hkv;
+  const int item = blockIdx.x / Hkv;
+  const ScoreItem it = items[item];
+  const int lane = threadIdx.x, n = lane & 31, half = lane >> 5;
+  const int G = Hq / Hkv, rows = n_signal * G, RT = n_signal * Hq;
+  const int64_t kv_stride = int64_t(Hkv) * D;
+  const float inv_hq = 1.f / float(Hq);
+
+  // Signal rows of this KV group, row rho = (signal token rho / G, head g G + rho % G), and their
+  // readout statistics (M, 1/Z) and centering term c; padding rows get 1/Z = 0, so alpha = 0.
+  for (int u = lane; u < R * KCH; u += 64) {
+    const int rho = u / KCH, c = u % KCH;
+    u32x4_t v = {0, 0, 0, 0};
+    if (rho < rows)
+      v = load16(Q_S + ((int64_t(it.prompt) * n_signal + rho / G) * Hq + g * G + rho % G) * D + 8 * c);
+    *reinterpret_cast<u32x4_t*>(&sq[rho * VROW + 8 * c]) = v;
+  }
+  for (int rho = lane; rho < R; rho += 64) {
+    float m = 0.f, z = 0.f, c = 0.f;
+    if (rho < rows) {
+      const int64_t ri = int64_t(it.prompt) * RT + (rho / G) * Hq + g * G + rho % G;
+      const float2 st = rowstat[ri];
+      m = st.x;
+      z = st.y;
+      c = center[ri];
+    }
+    sM[rho] = m;
+    sZ[rho] = z;
+    sC[rho] = c;
+  }
+  __syncthreads();
+  u32x4_t qf[RB][DSTEPS];
+  float mN[RB], zN[RB], cN[RB];  // this lane's row (N index) of each row block
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int s = 0; s < DSTEPS; ++s) qf[rb][s] = load16(&sq[(32 * rb + n) * VROW + 16 * s + 8 * half]);
+    mN[rb] = sM[32 * rb + n];
+    zN[rb] = sZ[32 * rb + n];
+    cN[rb] = sC[32 * rb + n];
+  }
+  // Transposing-read lane pattern (the forward's V^T reads): 16-lane group s = lane % 16,
+  // head-dim half (lane / 16) % 2, row half `half`.
+  const int vs = lane & 15, vdh = (lane >> 4) & 1;
+  const int t_lane = (4 * half + (vs >> 2)) * VROW + 16 * vdh + 4 * (vs & 3);
+
+  f32x16_t aq[RB][DBLK];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b) aq[rb][b] = f32x16_t{};
+
+  for (int d = it.d0; d < it.d1; ++d) {
+    const int a = dof[d], e = dof[d + 1];
+    const float gk = dscores[it.score_base + (d - it.d0)];
+    for (int t0 = a; t0 < e; t0 += 32) {
+      const int nk = min(32, e - t0);
+      __syncthreads();  // the previous block's LDS reads are done
+      {
+        const rsrc_t r = make_rsrc(K + int64_t(t0) * kv_stride + g * D, nk * int(kv_stride) * 2);
+#pragma unroll
+        for (int p = 0; p < 32 * KCH / 64; ++p) {
+          const int u = p * 64 + lane, row = u / KCH, c = u % KCH;
+          *reinterpret_cast<u32x4_t*>(&sk[row * VROW + 8 * c]) =
+              buf_load16(r, uint32_t((row * int(kv_stride) + 8 * c) * 2));
+        }
+      }
+      __syncthreads();
+      u32x4_t kf[DSTEPS];
+#pragma unroll
+      for (int s = 0; s < DSTEPS; ++s) kf[s] = load16(&sk[n * VROW + 16 * s + 8 * half]);
+      f32x16_t ak[DBLK];
+#pragma unroll
+      for (int b = 0; b < DBLK; ++b) ak[b] = f32x16_t{};
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        // z^T: keys on M (register r: key t0 + 8 (r / 4) + 4 half + r % 4), this lane's row on N.
+        f32x16_t zt = f32x16_t{}, z = f32x16_t{};
+#pragma unroll
+        for (int s = 0; s < DSTEPS; ++s) {
+          zt = mfma32(kf[s], qf[rb][s], zt);
+          z = mfma32(qf[rb][s], kf[s], z);
+        }
+        uint32_t pk[8], pd[8];
+        const float wN = (gk - cN[rb]) * inv_hq;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const int kk = 8 * (r >> 2) + 4 * half + (r & 3);
+          const float a0 = kk < nk ? fast_exp2(fmaf(zt[r], scale_log2, -mN[rb])) * zN[rb] : 0.f;
+          const float a1 = kk + 1 < nk ? fast_exp2(fmaf(zt[r + 1], scale_log2, -mN[rb])) * zN[rb] : 0.f;
+          pk[r >> 1] = pack_bf16x2(a0 * wN, a1 * wN);
+          // z: signal rows on M (register r: row 32 rb + kk), this lane's key on N.
+          const int r0 = 32 * rb + kk;
+          const float b0 = fast_exp2(fmaf(z[r], scale_log2, -sM[r0])) * sZ[r0] * (gk - sC[r0]) * inv_hq;
+          const float b1 = fast_exp2(fmaf(z[r + 1], scale_log2, -sM[r0 + 1])) * sZ[r0 + 1] * (gk - sC[r0 + 1]) * inv_hq;
+          pd[r >> 1] = pack_bf16x2(b0, b1);
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const u32x4_t bk = {pk[4 * m], pk[4 * m + 1], pk[4 * m + 2], pk[4 * m + 3]};
+          const u32x4_t bq = {pd[4 * m], pd[4 * m + 1], pd[4 * m + 2], pd[4 * m + 3]};
+          const uint16_t* kt = &sk[t_lane + 16 * m * VROW];
+          const uint16_t* qt = &sq[t_lane + (32 * rb + 16 * m) * VROW];
+#pragma unroll
+          for (int b = 0; b < DBLK; ++b) {
+            const u32x2_t klo = lds_read_tr16(kt + 32 * b), khi = lds_read_tr16(kt + 8 * VROW + 32 * b);
+            aq[rb][b] = mfma32(u32x4_t{klo[0], klo[1], khi[0], khi[1]}, bk, aq[rb][b]);
+            const u32x2_t qlo = lds_read_tr16(qt + 32 * b), qhi = lds_read_tr16(qt + 8 * VROW + 32 * b);
+            ak[b] = mfma32(u32x4_t{qlo[0], qlo[1], qhi[0], qhi[1]}, bq, ak[b]);
+          }
+        }
+      }
+      // ak[b] register r: head-dim element 32 b + 8 (r / 4) + 4 half + r % 4 of key t0 + n.
+      if (n < nk) {
+        float* dst = dK + (int64_t(t0 + n) * Hkv + g) * D + 4 * half;
+#pragma unroll
+        for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            f32x4_t v = f32x4_t{ak[b][4 * j], ak[b][4 * j + 1], ak[b][4 * j + 2], ak[b][4 * j + 3]} * scale;
+            f32x4_t* p = reinterpret_cast<f32x4_t*>(dst + 32 * b + 8 * j);
+            if (accumulate) v += *p;
+            *p = v;
+          }
+      }
+    }
+  }
+  // aq[rb][b] register r: head-dim element 32 b + 8 (r / 4) + 4 half + r % 4 of row 32 rb + n.
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float* dst = part + ((int64_t(item) * Hkv + g) * RB + rb) * 32 * D + n * D + 4 * half;
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4_t*>(dst + 32 * b + 8 * j) =
+            f32x4_t{aq[rb][b][4 * j], aq[rb][b][4 * j + 1], aq[rb][b][4 * j + 2], aq[rb][b][4 * j + 3]} * scale;
+  }
+}
+
+// dQ_S[b, i, h, :] = sum over prompt b's items of the group partials, in item order.
+template <int D>
+__global__ __launch_bounds__(256) void doc_bwd_reduce_kernel(const float* __restrict__ part,
+                                                             const int32_t* __restrict__ prompt_items,
+                                                             float* __restrict__ dQ_S, int num_prompts, int Hq,
+                                                             int Hkv, int n_signal, int RB) {
+  constexpr int CH = D / 4;
+  const int64_t unit = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int R = RB * 32;
+  const int64_t total = int64_t(num_prompts) * Hkv * R * CH;
+  if (unit >= total) return;
+  const int ch = int(unit % CH);
+  const int rho = int((unit / CH) % R);
+  const int g = int((unit / (int64_t(CH) * R)) % Hkv);
+  const int b = int(unit / (int64_t(CH) * R * Hkv));
+  const int G = Hq / Hkv;
+  if (rho >= n_signal * G) return;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int i = prompt_items[b]; i < prompt_items[b + 1]; ++i)
+    acc += *reinterpret_cast<const f32x4_t*>(part + ((int64_t(i) * Hkv + g) * RB + rho / 32) * 32 * D +
+                                             (rho % 32) * D + 4 * ch);
+  *reinterpret_cast<f32x4_t*>(dQ_S + ((int64_t(b) * n_signal + rho / G) * Hq + g * G + rho % G) * D + 4 * ch) = acc;
+}
+
+hipError_t launch_infonce(const float* scores, const int32_t* prompt_base, const int32_t* gold, float tau,
+                          int num_prompts, float* loss, float* dscores, hipStream_t stream) {
+  infonce_kernel<<<unsigned(num_prompts), 256, 0, stream>>>(scores, prompt_base, gold, 1.f / tau, loss, dscores);
+  return hipGetLastError();
+}
+
+template <int D, int RB>
+static hipError_t launch_doc_bwd_t(const DocBwdLaunch& a, hipStream_t stream) {
+  const int RT = a.n_signal * a.num_q_heads;
+  const int row_groups = (RT + 255) / 256;
+  doc_center_kernel<<<unsigned(a.num_prompts * row_groups), 256, 0, stream>>>(a.ml, a.rowstat, a.prompt_base,
+                                                                              a.dscores, a.center, RT, row_groups);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  doc_bwd_kernel<D, RB><<<unsigned(a.n_items * a.num_kv_heads), 64, 0, stream>>>(
+      a.Q_S, a.K, a.items, a.doc_offsets, a.rowstat, a.center, a.dscores, a.dK, a.part, a.num_q_heads, a.num_kv_heads,
+      a.n_signal, a.scale, a.scale * kLog2e, a.accumulate);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t units = int64_t(a.num_prompts) * a.num_kv_heads * RB * 32 * (D / 4);
+  doc_bwd_reduce_kernel<D><<<unsigned((units + 255) / 256), 256, 0, stream>>>(
+      a.part, a.prompt_items, a.dQ_S, a.num_prompts, a.num_q_heads, a.num_kv_heads, a.n_signal, RB);
+  return hipGetLastError();
+}
+
+hipError_t launch_doc_bwd(const DocBwdLaunch& a, hipStream_t stream) {
+  if (a.head_dim == 128) return a.row_blocks == 1 ? launch_doc_bwd_t<128, 1>(a, stream) : launch_doc_bwd_t<128, 2>(a, stream);
+  return a.row_blocks == 1 ? launch_doc_bwd_t<64, 1>(a, stream) : launch_doc_bwd_t<64, 2>(a, stream);
+}
+
+}  // namespace br

@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256) void doc_final_kernel(const float2* __restrict
   }
 }
 
-hipError_t launch_doc_scores(const ScoreLaunch& a, hipStream_t stream) {
+hipError_t launch_doc_stats(const ScoreLaunch& a, hipStream_t stream) {
   const int64_t waves = a.n_items * a.num_kv_heads * a.row_blocks;
   const dim3 grid(unsigned((waves + 3) / 4));
   if (a.head_dim == 128)
@@ -213,8 +213,14 @@ hipError_t launch_doc_scores(const ScoreLaunch& a, hipStream_t stream) {
   float2* rowstat = a.ml + int64_t(a.n_docs) * RT;
   doc_rowstat_kernel<<<dim3(unsigned(a.num_prompts * row_groups)), 256, 0, stream>>>(a.ml, a.prompt_base, rowstat,
                                                                                       RT, row_groups);
-  e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_doc_scores(const ScoreLaunch& a, hipStream_t stream) {
+  hipError_t e = launch_doc_stats(a, stream);
   if (e != hipSuccess) return e;
+  const int RT = a.n_signal * a.num_q_heads;
+  const float2* rowstat = a.ml + int64_t(a.n_docs) * RT;
   doc_final_kernel<<<dim3(unsigned(a.n_docs)), 256, 0, stream>>>(
       a.ml, rowstat, a.prompt_base, a.scores, a.head_scores, a.num_prompts, a.n_signal, a.num_q_heads, a.n_docs);
   return hipGetLastError();

@@ -42,6 +42,30 @@ struct ScoreLaunch {
   float scale_log2;
 };
 hipError_t launch_doc_scores(const ScoreLaunch& a, hipStream_t stream);
+// The readout's per-document (m_k, e_k) and per-row (M, 1/Z) only (rowstat at ml + n_docs * RT).
+hipError_t launch_doc_stats(const ScoreLaunch& a, hipStream_t stream);
+
+struct DocBwdLaunch {
+  const uint16_t* Q_S;
+  const uint16_t* K;
+  const ScoreItem* items;
+  const int32_t* doc_offsets;
+  const int32_t* prompt_base;
+  const int32_t* prompt_items;
+  const float2* ml;
+  const float2* rowstat;
+  float* center;
+  const float* dscores;
+  float* dK;
+  float* part;
+  float* dQ_S;
+  int64_t n_items;
+  int num_prompts, num_q_heads, num_kv_heads, head_dim, n_signal, row_blocks, accumulate;
+  float scale;
+};
+hipError_t launch_doc_bwd(const DocBwdLaunch& a, hipStream_t stream);
+hipError_t launch_infonce(const float* scores, const int32_t* prompt_base, const int32_t* gold, float tau,
+                          int num_prompts, float* loss, float* dscores, hipStream_t stream);
 
 constexpr int kSortMaxDocs = 8192;
 constexpr int kSortPromptsPerLaunch = 256;

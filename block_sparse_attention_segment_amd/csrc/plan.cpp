@@ -548,4 +548,50 @@ Error build_bwd_plan(const br_dims& dims, const int32_t* so, const int32_t* sp, 
   return {};
 }
 
+// ---------------------------------------------------------------------------------------------
+// readout backward and InfoNCE
+
+Error build_doc_bwd_plan(const br_dims& dims, int32_t n_signal, const int32_t* dof, const int32_t* dp,
+                         DocBwdPlan* plan) {
+  *plan = DocBwdPlan{};
+  Error e = build_score_plan(dims, n_signal, dof, dp, &plan->fwd);
+  if (!e.ok()) return e;
+  DocBwdPlan& P = *plan;
+  if (P.fwd.rows_per_kv > kDocBwdMaxRows)
+    return fail(BR_ERR_UNSUPPORTED, "readout backward supports n_signal * G <= %lld signal rows per KV head (got %lld)",
+                kDocBwdMaxRows, P.fwd.rows_per_kv);
+  const int B = dims.num_prompts;
+  P.prompt_items.assign(size_t(B) + 1, 0);
+  for (const ScoreItem& it : P.fwd.items) P.prompt_items[size_t(it.prompt) + 1]++;
+  for (int b = 0; b < B; ++b) P.prompt_items[size_t(b) + 1] += P.prompt_items[size_t(b)];
+  const size_t rt = size_t(n_signal) * size_t(dims.num_q_heads);
+  const size_t rb = size_t(P.fwd.row_blocks);
+  P.off_prompt_items = align_up(P.fwd.total_bytes, 256);
+  P.off_center = align_up(P.off_prompt_items + size_t(B + 1) * 4, 256);
+  P.off_part = align_up(P.off_center + size_t(B) * rt * 4, 256);
+  P.total_bytes = align_up(P.off_part + P.fwd.items.size() * size_t(dims.num_kv_heads) * rb * kRowsPerWave *
+                                            size_t(dims.head_dim) * 4, 256);
+  return {};
+}
+
+size_t infonce_workspace_bytes(int32_t num_prompts) {
+  return align_up(size_t(num_prompts + 1) * 4, 256) + align_up(size_t(num_prompts) * 4, 256);
+}
+
+Error validate_infonce(int32_t num_prompts, const int32_t* dp, const int32_t* gold, float tau) {
+  if (num_prompts < 1) return fail(BR_ERR_INVALID_ARG, "num_prompts must be >= 1 (got %lld)", num_prompts);
+  if (!dp || !gold) return fail(BR_ERR_INVALID_ARG, "doc_ptr and gold must be non-NULL host arrays");
+  if (!(tau > 0.f) || std::isinf(tau)) return Error{BR_ERR_INVALID_ARG, "tau must be finite and positive"};
+  if (dp[0] != 0) return fail(BR_ERR_INVALID_ARG, "doc_ptr[0] must be 0 (got %lld)", dp[0]);
+  for (int b = 0; b < num_prompts; ++b) {
+    const int64_t n = int64_t(dp[b + 1]) - dp[b] - 1;
+    if (n < 1) return fail(BR_ERR_INVALID_ARG, "prompt %lld has no documents", b);
+    if (n > kInfoNceMaxDocs)
+      return fail(BR_ERR_UNSUPPORTED, "prompt %lld has %lld documents; at most %lld", b, n, kInfoNceMaxDocs);
+    if (gold[b] < 0 || gold[b] >= n)
+      return fail(BR_ERR_INVALID_ARG, "prompt %lld: gold index %lld outside [0, %lld)", b, gold[b], n);
+  }
+  return {};
+}
+
 }  // namespace br

@@ -95,6 +95,17 @@ struct BwdPlan {
          off_dvec = 0, total_bytes = 0;
 };
 
+// Backward of the readout: the forward score plan (its items stream each document's keys once)
+// plus, per prompt, the range of its items (for summing the per-item dQ_S partials).  Signal
+// rows per KV head (n_signal * G) are limited to kDocBwdMaxRows.
+constexpr int kDocBwdMaxRows = 64;
+constexpr int kInfoNceMaxDocs = 8192;
+struct DocBwdPlan {
+  ScorePlan fwd;
+  std::vector<int32_t> prompt_items;  // [B + 1]
+  size_t off_prompt_items = 0, off_center = 0, off_part = 0, total_bytes = 0;
+};
+
 // Rotary embedding runs: rows [start[r], start[r + 1]) take positions pos0[r] + (row - start[r]).
 // Runs are non-empty and ascending; start has n_runs + 1 entries, the last being the row count.
 struct RopePlan {
@@ -141,6 +152,12 @@ Error build_score_plan(const br_dims& dims, int32_t n_signal, const int32_t* doc
 
 // Backward plan: the forward plan's items for dQ, key-major items for dK and dV, workspace layout.
 Error build_bwd_plan(const br_dims& dims, const int32_t* segment_offsets, const int32_t* seg_ptr, BwdPlan* plan);
+
+Error build_doc_bwd_plan(const br_dims& dims, int32_t n_signal, const int32_t* doc_offsets, const int32_t* doc_ptr,
+                         DocBwdPlan* plan);
+// InfoNCE over each prompt's scores: validates doc_ptr and gold; workspace [prompt bases | gold].
+Error validate_infonce(int32_t num_prompts, const int32_t* doc_ptr, const int32_t* gold, float tau);
+size_t infonce_workspace_bytes(int32_t num_prompts);
 
 // Permutation-invariant positions: instruction token i at i; token j of a document at
 // j + (docs_after_instruction ? instruction length : 0); query token i at query_pos0 + i.

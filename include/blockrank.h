@@ -243,6 +243,45 @@ br_status br_attn_bwd_plan_items(const br_dims* dims, const int32_t* segment_off
                                  int64_t* n_items, int32_t* n_slots);
 
 /*
+ * InfoNCE auxiliary loss on the readout scores (BlockRank summary, section 3.4 "auxiliary
+ * contrastive loss"; blog, attention supervision): per prompt b with documents k = 0..N_b-1,
+ *   loss[b] = -log(exp(s_gold / tau) / sum_k exp(s_k / tau)),
+ *   dscores[k] = d(sum_b loss[b]) / ds_k = (softmax(s / tau)_k - [k == gold]) / tau.
+ *   scores, dscores: device fp32 [sum_b N_b] (br_doc_scores order);  loss: device fp32 [B].
+ *   doc_ptr: HOST int32[B + 1] as for br_doc_scores;  gold: HOST int32[B], 0 <= gold[b] < N_b.
+ *   tau > 0 and finite (the pages use 0.05); N_b <= 8192.  fp32 arithmetic.
+ *   workspace: device, >= br_infonce_workspace_bytes(B), 16-byte aligned.
+ */
+br_status br_infonce_workspace_bytes(int32_t num_prompts, size_t* bytes);
+br_status br_infonce(const float* scores, const int32_t* doc_ptr, int32_t num_prompts, const int32_t* gold,
+                     float tau, float* loss, float* dscores, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/*
+ * Backward of br_doc_scores: the gradient of sum_k dscores_k s_k with respect to Q_S and K
+ * (BlockRank summary, section 3.4: the auxiliary loss's gradient flows back through the
+ * readout's attention).  With alpha the readout softmax over the prompt's document tokens of
+ * z = scale Q_S K^T and c_(i,h) = sum_k alpha-mass_(i,h,k) dscores_k:
+ *   dz = alpha * (dscores_k(j) - c) / Hq,  dQ_S = scale * dz K,  dK = scale * dz^T Q_S
+ * (query heads of a group add into their KV head).
+ *   Q_S, K, doc_offsets, doc_ptr, n_signal, softmax_scale: as for br_doc_scores.
+ *   dscores: device fp32 [sum_b N_b];  dQ_S: device fp32 [B, n_signal, Hq, d] (fully written);
+ *   dK: device fp32 [total_tokens, Hkv, d]: rows of document tokens are written
+ *       (accumulate == 0) or added to (accumulate == 1, e.g. onto br_attn_bwd's dK); other rows
+ *       are not touched.
+ *   n_signal * (Hq / Hkv) <= 64 (BR_ERR_UNSUPPORTED otherwise).
+ *   workspace: device, >= br_doc_scores_bwd_workspace_bytes(), 16-byte aligned.
+ * Arithmetic: alpha and dz in fp32, dz rounded to bf16 for the two MFMA products, fp32 sums; the
+ * per-group dQ_S partials are added in a fixed order (deterministic).
+ */
+br_status br_doc_scores_bwd_workspace_bytes(const br_dims* dims, int32_t n_signal, const int32_t* doc_offsets,
+                                            const int32_t* doc_ptr, size_t* bytes);
+br_status br_doc_scores_bwd(const br_dims* dims, const void* Q_S, int32_t n_signal, const void* K,
+                            const int32_t* doc_offsets, const int32_t* doc_ptr, const float* dscores,
+                            float* dQ_S, float* dK, int32_t accumulate, float softmax_scale, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/*
  * SSMax logit factor (BlockSearch, section 5.1, length-aware softmax): SSMax multiplies the
  * pre-softmax scores q.k / sqrt(d) by s * ln N, N the number of documents of the prompt.  Writes
  * *scale = s * ln(n_docs) / sqrt(head_dim), the value to pass as softmax_scale to

@@ -370,3 +370,34 @@ def test_bwd_plan_covers_exactly_the_mask(seed):
     used = sorted(s_ for v in key_owner.values() for s_ in v if s_ >= 0)
     assert used == list(range(slots))
     assert seed != 5 or slots > 0
+
+
+# ---- InfoNCE and readout backward (host side only) ----
+def test_infonce_and_readout_bwd_reject_before_any_hip_call():
+    lib = br.load_library()
+    p = lambda a: np.ascontiguousarray(a, dtype=np.int32).ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    f = _fake()
+    dp = np.array([0, 4, 7], dtype=np.int32)   # 3 and 2 documents
+    need = ctypes.c_size_t(0)
+    assert lib.br_infonce_workspace_bytes(2, ctypes.byref(need)) == 0 and need.value > 0
+    INV, WS, UNS = br._lib.BR_ERR_INVALID_ARG, br._lib.BR_ERR_WORKSPACE, br._lib.BR_ERR_UNSUPPORTED
+    call = lambda gold, tau, ws=f, nb=need.value: lib.br_infonce(f, p(dp), 2, p(gold), tau, f, f, ws, nb, None)
+    assert call([0, 2], 0.05) == INV            # gold 2 outside the second prompt's 2 documents
+    assert call([-1, 0], 0.05) == INV
+    assert call([0, 1], 0.0) == INV
+    assert call([0, 1], float("inf")) == INV
+    assert call([0, 1], 0.05, nb=need.value - 1) == WS
+    assert lib.br_infonce(f, p([0, 1, 2]), 2, p([0, 0]), 0.05, f, f, f, need.value, None) == INV  # empty prompt
+    # readout backward: too many signal rows per KV head, bad flags, workspace
+    seg, sp, dof, dptr = workloads.segment_tables([(8, [16, 12, 20], 8), (4, [10, 10], 9)])
+    dims = br.make_dims(2, 8, 1, 64, int(seg[-1]))   # G = 8
+    with pytest.raises(br.BlockRankError) as ei:
+        br.doc_scores_bwd_workspace_bytes(dims, 9, dof, dptr)     # 9 * 8 = 72 rows > 64
+    assert ei.value.status == UNS
+    nb = br.doc_scores_bwd_workspace_bytes(dims, 8, dof, dptr)
+    bwd = lambda acc, scale, ws, n: lib.br_doc_scores_bwd(ctypes.byref(dims), f, 8, f, p(dof), p(dptr), f, f, f, acc,
+                                                          scale, ws, n, None)
+    assert bwd(2, 0.0, f, nb) == INV
+    assert bwd(0, float("nan"), f, nb) == INV
+    assert bwd(0, 0.0, f, nb - 1) == WS
+    assert bwd(0, 0.0, None, nb) == WS
