@@ -327,6 +327,75 @@ def measure_rope(w, steps, warmup, log):
             "hbm_roofline_frac": round(gbps / PEAK_HBM_GBPS, 4)}
 
 
+def measure_backward(w, steps, warmup, log):
+    """Training side of the long prompt: the attention backward for an upstream dO (with the
+    forward's O and lse), and the auxiliary-loss chain readout -> InfoNCE -> readout backward
+    (adding into the attention's dK).  Inputs resident in HBM; the forward is outside the timed
+    region."""
+    import torch
+
+    import block_sparse_attention_segment_amd as br
+    import workloads
+
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    Q, K, V, Q_S = dev(w.Q), dev(w.K), dev(w.V), dev(w.Q_S)
+    T, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    rng = np.random.default_rng(7)
+    dO = dev(workloads.f32_to_bf16_bits(rng.standard_normal((T, Hq, d), dtype=np.float32)))
+    O, lse = br.attn_fwd(Q, K, V, w.segment_offsets, w.seg_ptr, lse=True)
+    dims = br.make_dims(w.num_prompts, Hq, Hkv, d, T)
+    ws = torch.empty(br.attn_bwd_workspace_bytes(dims, w.segment_offsets, w.seg_ptr), dtype=torch.uint8, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dQ, dK, dV = torch.empty((T, Hq, d), **f32), torch.empty((T, Hkv, d), **f32), torch.empty((T, Hkv, d), **f32)
+    gold = np.zeros(w.num_prompts, dtype=np.int32)
+    scores = torch.empty(w.num_docs, **f32)
+    loss, ds = torch.empty(w.num_prompts, **f32), torch.empty(w.num_docs, **f32)
+    dQs = torch.empty(tuple(w.Q_S.shape), **f32)
+    ws_s = torch.empty(br.doc_scores_workspace_bytes(dims, w.n_signal, w.doc_offsets, w.doc_ptr), dtype=torch.uint8,
+                       device="cuda")
+    ws_r = torch.empty(br.doc_scores_bwd_workspace_bytes(dims, w.n_signal, w.doc_offsets, w.doc_ptr), dtype=torch.uint8,
+                       device="cuda")
+    ws_i = torch.empty(1 << 12, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def attn_bwd():
+        br.attn_bwd(Q, K, V, O, dO, lse, w.segment_offsets, w.seg_ptr, dQ=dQ, dK=dK, dV=dV, workspace=ws, stream=stream)
+
+    def aux_chain():
+        br.doc_scores(Q_S, K, w.doc_offsets, w.doc_ptr, scores=scores, workspace=ws_s, stream=stream)
+        br.infonce(scores, w.doc_ptr, gold, loss=loss, dscores=ds, workspace=ws_i, stream=stream)
+        br.doc_scores_bwd(Q_S, K, w.doc_offsets, w.doc_ptr, ds, dQ_S=dQs, dK=dK, accumulate=True, workspace=ws_r,
+                          stream=stream)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_attn = timed(attn_bwd)
+    ms_aux = timed(aux_chain)
+    blk, _ = pair_counts(w)
+    flop = 10.0 * d * Hq * blk   # recomputed S, dP, dV, dQ, dK: five products of 2 d FLOPs per pair
+    io_bytes = float(T) * (3 * Hq * d * 2 + 2 * Hkv * d * 2 + Hq * 4 + Hq * d * 4 + 2 * Hkv * d * 4)
+    log(f"[bench] attention backward {ms_attn:.4f} ms, loss chain {ms_aux:.4f} ms")
+    return {"workload": f"long prompt backward: attention dQ/dK/dV for a random upstream dO; readout -> InfoNCE "
+                        f"(tau 0.05) -> readout backward adding into dK",
+            "attn_bwd_ms": round(ms_attn, 5),
+            "attn_bwd_tflops_allowed_pairs": round(flop / (ms_attn / 1e3) / 1e12, 3),
+            "attn_bwd_mfma_peak_frac": round(flop / (ms_attn / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "attn_bwd_io_bytes": io_bytes,
+            "attn_bwd_io_gbps": round(io_bytes / (ms_attn / 1e3) / 1e9, 1),
+            "aux_loss_chain_ms": round(ms_aux, 5)}
+
+
 def cpu_baseline(w, n_docs_sample, log):
     """Time the fp64 oracle on a bounded sample of the same prompt and scale to the whole step."""
     import oracle.oracle as orc
@@ -370,7 +439,7 @@ def main():
     ap.add_argument("--secondary", default="worked", help="extra config timed in the same run ('' for none)")
     ap.add_argument("--query-only", type=int, default=1,
                     help="also time query-only attention over the long prompt's cached corpus, top-256 routed "
-                         "attention and RoPE of Q and K (0 to skip)")
+                         "attention, RoPE of Q and K, and the backward (0 to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-docs", type=int, default=200, help="documents in the CPU oracle's timed sample")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -445,6 +514,7 @@ def main():
         line["query_only"] = measure_query_only(w, 16, 32, args.steps, args.warmup, args.seed, log)
         line["routed"] = measure_routed(w, 256, args.steps, args.warmup, log)
         line["rope"] = measure_rope(w, args.steps, args.warmup, log)
+        line["backward"] = measure_backward(w, args.steps, args.warmup, log)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, args.cpu_docs, log)
         line["cpu_baseline"] = {

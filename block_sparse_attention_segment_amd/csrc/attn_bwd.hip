@@ -13,8 +13,9 @@
 //                        (keys on M), dS^T in fp32, dQ^T += K^T dS^T with dS rounded to bf16
 //                        and K^T fragments from transposing LDS reads (as V^T in the forward).
 //   attn_bwd_dkv_kernel  key-major: 64 keys of one KV head per workgroup (2 waves of 32 keys);
-//                        the rows that read them stream through LDS 32 (token, head) rows at a
-//                        time: S = Q K^T and dP = dO V^T (rows on M), then dV^T += dO^T P and
+//                        the rows that read them stream through LDS 64 (token, head) rows at a
+//                        time (the next step's rows are loaded into registers meanwhile):
+//                        S = Q K^T and dP = dO V^T (rows on M), then dV^T += dO^T P and
 //                        dK^T += Q^T dS with the row-side operands read transposed from LDS.
 // Long row or key ranges are split; their fp32 partials are summed by the merge kernels in a
 // fixed order, so results are deterministic.  Outputs are fp32.
@@ -219,12 +220,14 @@ __global__ __launch_bounds__(128) void attn_bwd_dkv_kernel(const uint16_t* __res
                                                            float* __restrict__ dK, float* __restrict__ dV,
                                                            const KvItem* __restrict__ items, float* __restrict__ part_dkv,
                                                            int Hq, int Hkv, int kv_slots, float scale, float scale_log2) {
-  constexpr int TR = 32 / G;                 // row tokens per 32-row step (rows: token-major, G heads each)
+  constexpr int RS = 64;                     // rows per step: two 32-row MFMA blocks
+  constexpr int TR = RS / G;                 // row tokens per step (rows token-major, G heads each)
   constexpr int VROW = D == 128 ? 160 : 96;  // Q and dO rows: row reads and transposing reads
   constexpr int DSTEPS = D / 16, DBLK = D / 32, KCH = D / 8;
-  __shared__ __align__(16) uint16_t sq[32 * VROW];
-  __shared__ __align__(16) uint16_t sd[32 * VROW];
-  __shared__ float sl[32], sr[32];
+  constexpr int LPT = RS * KCH / 128;        // 16-byte chunks per thread per tensor per step
+  __shared__ __align__(16) uint16_t sq[RS * VROW];
+  __shared__ __align__(16) uint16_t sd[RS * VROW];
+  __shared__ float sl[RS], sr[RS];
 
   const int g = blockIdx.x % Hkv;
   const KvItem it = items[blockIdx.x / Hkv];
@@ -253,71 +256,89 @@ __global__ __launch_bounds__(128) void attn_bwd_dkv_kernel(const uint16_t* __res
     ak[b] = f32x16_t{};
     av[b] = f32x16_t{};
   }
-  // Row steps: the causal range first, then the unmasked one.
+  // Row steps: the causal range first, then the unmasked one.  Step i + 1's rows are loaded into
+  // registers while step i is computed.
   const int nC = it.c1 > it.c0 ? (it.c1 - it.c0 + TR - 1) / TR : 0;
   const int nU = it.u1 > it.u0 ? (it.u1 - it.u0 + TR - 1) / TR : 0;
-  for (int i = 0; i < nC + nU; ++i) {
-    const bool causal = i < nC;
-    const int t0 = causal ? it.c0 + i * TR : it.u0 + (i - nC) * TR;
-    const int tend = causal ? it.c1 : it.u1;
-    const int ntok = min(TR, tend - t0);
-    __syncthreads();  // the previous step's LDS reads are done
-    {
-      // 32 rows x KCH chunks of Q and of dO: row rr = token rr / G, head g G + rr % G.
-      const rsrc_t rq = make_rsrc(Q + (int64_t(t0) * Hq + g * G) * D, ntok * q_stride * 2);
-      const rsrc_t rd = make_rsrc(dO + (int64_t(t0) * Hq + g * G) * D, ntok * q_stride * 2);
+  const int nS = nC + nU;
+  auto step_t0 = [&](int i) { return i < nC ? it.c0 + i * TR : it.u0 + (i - nC) * TR; };
+  auto step_end = [&](int i) { return i < nC ? it.c1 : it.u1; };
+  u32x4_t rq[LPT], rd[LPT];
+  float rl = INFINITY, rr_ = 0.f;
+  auto load_step = [&](int i) {
+    const int t0 = step_t0(i), ntok = min(TR, step_end(i) - t0);
+    const rsrc_t bq = make_rsrc(Q + (int64_t(t0) * Hq + g * G) * D, ntok * q_stride * 2);
+    const rsrc_t bd = make_rsrc(dO + (int64_t(t0) * Hq + g * G) * D, ntok * q_stride * 2);
 #pragma unroll
-      for (int p = 0; p < 32 * KCH / 128; ++p) {
-        const int u = p * 128 + tid, rr = u / KCH, c = u % KCH;
-        const uint32_t off = uint32_t(((rr / G) * q_stride + (rr % G) * D + 8 * c) * 2);
-        *reinterpret_cast<u32x4_t*>(&sq[rr * VROW + 8 * c]) = buf_load16(rq, off);
-        *reinterpret_cast<u32x4_t*>(&sd[rr * VROW + 8 * c]) = buf_load16(rd, off);
-      }
-      if (tid < 32) {
-        const int tok = t0 + tid / G;
-        const bool ok = tid / G < ntok;
-        const int64_t rix = int64_t(tok) * Hq + g * G + tid % G;
-        sl[tid] = ok ? lse[rix] * kLog2e : INFINITY;  // rows past the range get P = 0
-        sr[tid] = ok ? dvec[rix] : 0.f;
-      }
+    for (int p = 0; p < LPT; ++p) {
+      const int u = p * 128 + tid, row = u / KCH, c = u % KCH;
+      const uint32_t off = uint32_t(((row / G) * q_stride + (row % G) * D + 8 * c) * 2);
+      rq[p] = buf_load16(bq, off);
+      rd[p] = buf_load16(bd, off);
+    }
+    if (tid < RS) {
+      const bool ok = tid / G < ntok;  // rows past the range get P = 0
+      const int64_t rix = int64_t(t0 + tid / G) * Hq + g * G + tid % G;
+      rl = ok ? lse[rix] * kLog2e : INFINITY;
+      rr_ = ok ? dvec[rix] : 0.f;
+    }
+  };
+  if (nS > 0) load_step(0);
+  for (int i = 0; i < nS; ++i) {
+    const bool causal = i < nC;
+    const int t0 = step_t0(i);
+    __syncthreads();  // the previous step's LDS reads are done
+#pragma unroll
+    for (int p = 0; p < LPT; ++p) {
+      const int u = p * 128 + tid, row = u / KCH, c = u % KCH;
+      *reinterpret_cast<u32x4_t*>(&sq[row * VROW + 8 * c]) = rq[p];
+      *reinterpret_cast<u32x4_t*>(&sd[row * VROW + 8 * c]) = rd[p];
+    }
+    if (tid < RS) {
+      sl[tid] = rl;
+      sr[tid] = rr_;
     }
     __syncthreads();
-    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-    const uint16_t* qp = &sq[n * VROW + 8 * half];
-    const uint16_t* dq = &sd[n * VROW + 8 * half];
+    if (i + 1 < nS) load_step(i + 1);
 #pragma unroll
-    for (int st = 0; st < DSTEPS; ++st) {
-      s = mfma32(load16(qp + 16 * st), kf[st], s);
-      dp = mfma32(load16(dq + 16 * st), vf[st], dp);
-    }
-    // Register r holds row 8 (r / 4) + 4 half + r % 4 of the step (token t0 + row / G) for this
-    // lane's key.  Causal rows read the key only if its token is not before the key.
-    uint32_t pp[8], pd[8];
+    for (int rb = 0; rb < 2; ++rb) {
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+      const uint16_t* qp = &sq[(32 * rb + n) * VROW + 8 * half];
+      const uint16_t* dq = &sd[(32 * rb + n) * VROW + 8 * half];
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      float p[2], ds[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int rr = 8 * (r >> 2) + 4 * half + (r & 3) + e;
-        const bool ok = !causal || key <= t0 + rr / G;
-        p[e] = ok ? fast_exp2(fmaf(s[r + e], scale_log2, -sl[rr])) : 0.f;
-        ds[e] = p[e] * (dp[r + e] - sr[rr]);
+      for (int st = 0; st < DSTEPS; ++st) {
+        s = mfma32(load16(qp + 16 * st), kf[st], s);
+        dp = mfma32(load16(dq + 16 * st), vf[st], dp);
       }
-      pp[r >> 1] = pack_bf16x2(p[0], p[1]);
-      pd[r >> 1] = pack_bf16x2(ds[0], ds[1]);
-    }
+      // Register r holds row 32 rb + 8 (r / 4) + 4 half + r % 4 of the step (token t0 + row / G)
+      // for this lane's key.  Causal rows read the key only if their token is not before it.
+      uint32_t pp[8], pd[8];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const u32x4_t bp = {pp[4 * m], pp[4 * m + 1], pp[4 * m + 2], pp[4 * m + 3]};
-      const u32x4_t bd = {pd[4 * m], pd[4 * m + 1], pd[4 * m + 2], pd[4 * m + 3]};
-      const uint16_t* dpt = &sd[r_lane + 16 * m * VROW];
-      const uint16_t* qpt = &sq[r_lane + 16 * m * VROW];
+      for (int r = 0; r < 16; r += 2) {
+        float pr[2], ds[2];
 #pragma unroll
-      for (int b = 0; b < DBLK; ++b) {
-        const u32x2_t dlo = lds_read_tr16(dpt + 32 * b), dhi = lds_read_tr16(dpt + 8 * VROW + 32 * b);
-        av[b] = mfma32(u32x4_t{dlo[0], dlo[1], dhi[0], dhi[1]}, bp, av[b]);
-        const u32x2_t qlo = lds_read_tr16(qpt + 32 * b), qhi = lds_read_tr16(qpt + 8 * VROW + 32 * b);
-        ak[b] = mfma32(u32x4_t{qlo[0], qlo[1], qhi[0], qhi[1]}, bd, ak[b]);
+        for (int e = 0; e < 2; ++e) {
+          const int row = 32 * rb + 8 * (r >> 2) + 4 * half + (r & 3) + e;
+          const bool ok = !causal || key <= t0 + row / G;
+          pr[e] = ok ? fast_exp2(fmaf(s[r + e], scale_log2, -sl[row])) : 0.f;
+          ds[e] = pr[e] * (dp[r + e] - sr[row]);
+        }
+        pp[r >> 1] = pack_bf16x2(pr[0], pr[1]);
+        pd[r >> 1] = pack_bf16x2(ds[0], ds[1]);
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const u32x4_t bp = {pp[4 * m], pp[4 * m + 1], pp[4 * m + 2], pp[4 * m + 3]};
+        const u32x4_t bd = {pd[4 * m], pd[4 * m + 1], pd[4 * m + 2], pd[4 * m + 3]};
+        const uint16_t* dpt = &sd[r_lane + (32 * rb + 16 * m) * VROW];
+        const uint16_t* qpt = &sq[r_lane + (32 * rb + 16 * m) * VROW];
+#pragma unroll
+        for (int b = 0; b < DBLK; ++b) {
+          const u32x2_t dlo = lds_read_tr16(dpt + 32 * b), dhi = lds_read_tr16(dpt + 8 * VROW + 32 * b);
+          av[b] = mfma32(u32x4_t{dlo[0], dlo[1], dhi[0], dhi[1]}, bp, av[b]);
+          const u32x2_t qlo = lds_read_tr16(qpt + 32 * b), qhi = lds_read_tr16(qpt + 8 * VROW + 32 * b);
+          ak[b] = mfma32(u32x4_t{qlo[0], qlo[1], qhi[0], qhi[1]}, bd, ak[b]);
+        }
       }
     }
   }

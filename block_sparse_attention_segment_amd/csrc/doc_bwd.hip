@@ -53,22 +53,35 @@ __global__ __launch_bounds__(256) void infonce_kernel(const float* __restrict__ 
   if (tid == 0) loss[b] = lse - scores[k0 + gd] * inv_tau;
 }
 
-// c[b * RT + r] = (1/Z_r) sum_k e_k,r 2^(m_k,r - M_r) g_k over prompt b's documents.
+// c[b * RT + r] = (1/Z_r) sum_k e_k,r 2^(m_k,r - M_r) g_k over prompt b's documents.  A workgroup
+// covers 4 rows x 64 document lanes (the rowstat kernel's layout); the 64 lane sums of a row are
+// added in a fixed order.
+constexpr int kCenterRows = 4;
+constexpr int kCenterLanes = 64;
 __global__ __launch_bounds__(256) void doc_center_kernel(const float2* __restrict__ ml,
                                                          const float2* __restrict__ rowstat,
                                                          const int32_t* __restrict__ prompt_base,
                                                          const float* __restrict__ dscores, float* __restrict__ center,
                                                          int RT, int row_groups) {
-  const int b = blockIdx.x / row_groups;
-  const int r = (blockIdx.x % row_groups) * 256 + threadIdx.x;
-  if (r >= RT) return;
-  const float2 st = rowstat[int64_t(b) * RT + r];
+  __shared__ float red[kCenterRows][kCenterLanes];
+  const int b = blockIdx.x / row_groups, rg = blockIdx.x % row_groups;
+  const int rl = threadIdx.x % kCenterRows, kl = threadIdx.x / kCenterRows;
+  const int r = rg * kCenterRows + rl;
   float c = 0.f;
-  for (int k = prompt_base[b]; k < prompt_base[b + 1]; ++k) {
-    const float2 v = ml[int64_t(k) * RT + r];
-    c = fmaf(v.y * fast_exp2(v.x - st.x), dscores[k], c);
+  if (r < RT) {
+    const float M = rowstat[int64_t(b) * RT + r].x;
+    for (int k = prompt_base[b] + kl; k < prompt_base[b + 1]; k += kCenterLanes) {
+      const float2 v = ml[int64_t(k) * RT + r];
+      c = fmaf(v.y * fast_exp2(v.x - M), dscores[k], c);
+    }
   }
-  center[int64_t(b) * RT + r] = c * st.y;
+  red[rl][kl] = c;
+  __syncthreads();
+  if (kl == 0 && r < RT) {
+    float t = 0.f;
+    for (int j = 0; j < kCenterLanes; ++j) t += red[rl][j];
+    center[int64_t(b) * RT + r] = t * rowstat[int64_t(b) * RT + r].y;
+  }
 }
 
 template <int D, int RB>
@@ -225,28 +238,35 @@ __global__ __launch_bounds__(64) void doc_bwd_kernel(const uint16_t* __restrict_
   }
 }
 
-// dQ_S[b, i, h, :] = sum over prompt b's items of the group partials, in item order.
+// dQ_S[b, i, h, :] = sum over prompt b's items of the group partials.  One workgroup per
+// (prompt, KV head, signal row): 8 item slices x (D / 4) element groups; each slice sums every
+// 8th item and the slices are added in a fixed order (deterministic).
+constexpr int kReduceSlices = 8;
 template <int D>
-__global__ __launch_bounds__(256) void doc_bwd_reduce_kernel(const float* __restrict__ part,
-                                                             const int32_t* __restrict__ prompt_items,
-                                                             float* __restrict__ dQ_S, int num_prompts, int Hq,
-                                                             int Hkv, int n_signal, int RB) {
+__global__ __launch_bounds__(kReduceSlices * D / 4) void doc_bwd_reduce_kernel(const float* __restrict__ part,
+                                                                             const int32_t* __restrict__ prompt_items,
+                                                                             float* __restrict__ dQ_S, int Hq, int Hkv,
+                                                                             int n_signal, int RB) {
   constexpr int CH = D / 4;
-  const int64_t unit = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  __shared__ f32x4_t red[kReduceSlices][CH];
   const int R = RB * 32;
-  const int64_t total = int64_t(num_prompts) * Hkv * R * CH;
-  if (unit >= total) return;
-  const int ch = int(unit % CH);
-  const int rho = int((unit / CH) % R);
-  const int g = int((unit / (int64_t(CH) * R)) % Hkv);
-  const int b = int(unit / (int64_t(CH) * R * Hkv));
+  const int rho = blockIdx.x % R;
+  const int g = (blockIdx.x / R) % Hkv;
+  const int b = blockIdx.x / (R * Hkv);
   const int G = Hq / Hkv;
-  if (rho >= n_signal * G) return;
+  if (rho >= n_signal * G) return;  // uniform per workgroup
+  const int ch = threadIdx.x % CH, sl = threadIdx.x / CH;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int i = prompt_items[b]; i < prompt_items[b + 1]; ++i)
+  for (int i = prompt_items[b] + sl; i < prompt_items[b + 1]; i += kReduceSlices)
     acc += *reinterpret_cast<const f32x4_t*>(part + ((int64_t(i) * Hkv + g) * RB + rho / 32) * 32 * D +
                                              (rho % 32) * D + 4 * ch);
-  *reinterpret_cast<f32x4_t*>(dQ_S + ((int64_t(b) * n_signal + rho / G) * Hq + g * G + rho % G) * D + 4 * ch) = acc;
+  red[sl][ch] = acc;
+  __syncthreads();
+  if (sl == 0) {
+    f32x4_t t = red[0][ch];
+    for (int j = 1; j < kReduceSlices; ++j) t += red[j][ch];
+    *reinterpret_cast<f32x4_t*>(dQ_S + ((int64_t(b) * n_signal + rho / G) * Hq + g * G + rho % G) * D + 4 * ch) = t;
+  }
 }
 
 hipError_t launch_infonce(const float* scores, const int32_t* prompt_base, const int32_t* gold, float tau,
@@ -258,7 +278,7 @@ hipError_t launch_infonce(const float* scores, const int32_t* prompt_base, const
 template <int D, int RB>
 static hipError_t launch_doc_bwd_t(const DocBwdLaunch& a, hipStream_t stream) {
   const int RT = a.n_signal * a.num_q_heads;
-  const int row_groups = (RT + 255) / 256;
+  const int row_groups = (RT + kCenterRows - 1) / kCenterRows;
   doc_center_kernel<<<unsigned(a.num_prompts * row_groups), 256, 0, stream>>>(a.ml, a.rowstat, a.prompt_base,
                                                                               a.dscores, a.center, RT, row_groups);
   hipError_t e = hipGetLastError();
@@ -268,9 +288,8 @@ static hipError_t launch_doc_bwd_t(const DocBwdLaunch& a, hipStream_t stream) {
       a.n_signal, a.scale, a.scale * kLog2e, a.accumulate);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t units = int64_t(a.num_prompts) * a.num_kv_heads * RB * 32 * (D / 4);
-  doc_bwd_reduce_kernel<D><<<unsigned((units + 255) / 256), 256, 0, stream>>>(
-      a.part, a.prompt_items, a.dQ_S, a.num_prompts, a.num_q_heads, a.num_kv_heads, a.n_signal, RB);
+  doc_bwd_reduce_kernel<D><<<unsigned(a.num_prompts * a.num_kv_heads * RB * 32), kReduceSlices * D / 4, 0, stream>>>(
+      a.part, a.prompt_items, a.dQ_S, a.num_q_heads, a.num_kv_heads, a.n_signal, RB);
   return hipGetLastError();
 }
 
