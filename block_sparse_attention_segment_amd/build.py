@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libblockrank.so")
-SOURCES = ["plan.cpp", "api.cpp", "attn_fwd.hip", "doc_scores.hip", "sort_docs.hip", "rope.hip", "attn_bwd.hip", "doc_bwd.hip"]
+SOURCES = ["plan.cpp", "plan_extra.cpp", "api.cpp", "attn_fwd.hip", "doc_scores.hip", "sort_docs.hip", "rope.hip", "attn_bwd.hip", "doc_bwd.hip"]
 ARCH = "gfx950"
 
 
