@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void attn_bwd_rowdot_kernel(const uint16_t* __
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                                                           const float* __restrict__ lse, const float* __restrict__ dvec,
                                                           float* __restrict__ dQ, const AttnItem* __restrict__ items,
@@ -131,44 +131,39 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const uint16_t* __rest
     if (i + 1 < nt) load_tile(t_start(i + 1), t_end(i + 1));
     const int start = t_start(i), end = t_end(i);
     const bool causal = i >= nA;
-    f32x16_t s[NKB], dp[NKB];
+    // Register r of block kb holds key start + 32 kb + 8 (r / 4) + 4 half + r % 4.
+    const int lim = (causal ? min(end, row_tok + 1) : end) - start - 4 * half;
+    // One 32-key block at a time keeps few values live (two workgroups fit on a CU).
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = f32x16_t{};
-      dp[kb] = f32x16_t{};
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
       const uint16_t* kp = &sk[(kb * 32 + n) * VROW + 8 * half];
       const uint16_t* vp = &sv[(kb * 32 + n) * KROW + 8 * half];
 #pragma unroll
       for (int st = 0; st < DSTEPS; ++st) {
-        s[kb] = mfma32(load16(kp + 16 * st), qf[st], s[kb]);
-        dp[kb] = mfma32(load16(vp + 16 * st), df[st], dp[kb]);
+        s = mfma32(load16(kp + 16 * st), qf[st], s);
+        dp = mfma32(load16(vp + 16 * st), df[st], dp);
       }
-    }
-    // Register r of block kb holds key start + 32 kb + 8 (r / 4) + 4 half + r % 4.
-    const int lim = (causal ? min(end, row_tok + 1) : end) - start - 4 * half;
-    uint32_t pk[NKB][8];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      uint32_t pk[8];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const bool ok0 = row_ok && (kb * 32 + 8 * (r >> 2) + (r & 3)) < lim;
         const bool ok1 = row_ok && (kb * 32 + 8 * (r >> 2) + (r & 3) + 1) < lim;
-        const float p0 = ok0 ? fast_exp2(fmaf(s[kb][r], scale_log2, -l2)) : 0.f;
-        const float p1 = ok1 ? fast_exp2(fmaf(s[kb][r + 1], scale_log2, -l2)) : 0.f;
-        pk[kb][r >> 1] = pack_bf16x2(p0 * (dp[kb][r] - dr), p1 * (dp[kb][r + 1] - dr));
+        const float p0 = ok0 ? fast_exp2(fmaf(s[r], scale_log2, -l2)) : 0.f;
+        const float p1 = ok1 ? fast_exp2(fmaf(s[r + 1], scale_log2, -l2)) : 0.f;
+        pk[r >> 1] = pack_bf16x2(p0 * (dp[r] - dr), p1 * (dp[r + 1] - dr));
       }
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
       for (int m = 0; m < 2; ++m) {
-        const u32x4_t pv = {pk[kb][4 * m], pk[kb][4 * m + 1], pk[kb][4 * m + 2], pk[kb][4 * m + 3]};
-        const uint16_t* kp = &sk[k_lane + (32 * kb + 16 * m) * VROW];
+        const u32x4_t pv = {pk[4 * m], pk[4 * m + 1], pk[4 * m + 2], pk[4 * m + 3]};
+        const uint16_t* kq = &sk[k_lane + (32 * kb + 16 * m) * VROW];
 #pragma unroll
         for (int b = 0; b < DBLK; ++b) {
-          const u32x2_t lo = lds_read_tr16(kp + 32 * b), hi = lds_read_tr16(kp + 8 * VROW + 32 * b);
+          const u32x2_t lo = lds_read_tr16(kq + 32 * b), hi = lds_read_tr16(kq + 8 * VROW + 32 * b);
           acc[b] = mfma32(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pv, acc[b]);
         }
       }
+    }
   }
   // acc[b] register r holds head-dim element 32 b + 8 (r / 4) + 4 half + r % 4 of this lane's row.
   if (it.slot < 0) {
