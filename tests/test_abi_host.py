@@ -401,3 +401,27 @@ def test_infonce_and_readout_bwd_reject_before_any_hip_call():
     assert bwd(0, float("nan"), f, nb) == INV
     assert bwd(0, 0.0, f, nb - 1) == WS
     assert bwd(0, 0.0, None, nb) == WS
+
+
+def test_attn_bwd_rejects_before_any_hip_call():
+    lib = br.load_library()
+    seg, sp, _, _ = workloads.segment_tables([(8, [16, 12, 20], 8), (4, [10, 10], 6)])
+    dims = br.make_dims(2, 8, 2, 64, int(seg[-1]))
+    need = br._lib.attn_bwd_workspace_bytes(dims, seg, sp)
+    assert need > 0
+    p = lambda a: np.ascontiguousarray(a, dtype=np.int32).ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    f = _fake()
+    INV, WS = br._lib.BR_ERR_INVALID_ARG, br._lib.BR_ERR_WORKSPACE
+    call = lambda *a: lib.br_attn_bwd(ctypes.byref(dims), *a)
+    args = lambda **kw: [kw.get(k, v) for k, v in (("Q", f), ("K", f), ("V", f), ("O", f), ("dO", f), ("lse", f),
+                                                 ("so", p(seg)), ("sp", p(sp)), ("dQ", f), ("dK", f), ("dV", f),
+                                                 ("scale", 0.0), ("ws", f), ("n", need), ("st", None))]
+    assert call(*args(n=need - 1)) == WS
+    assert call(*args(ws=None)) == WS
+    assert call(*args(dO=None)) == INV
+    assert call(*args(lse=None)) == INV
+    assert call(*args(dK=ctypes.c_void_p(0x10004))) == INV          # misaligned
+    assert call(*args(scale=float("inf"))) == INV
+    assert call(*args(sp=p([0, 5, 3]))) == INV                        # bad segment table
+    bad = br.make_dims(2, 8, 3, 64, int(seg[-1]))                     # Hq not a multiple of Hkv
+    assert lib.br_attn_bwd(ctypes.byref(bad), *args()) == INV
