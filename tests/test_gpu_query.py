@@ -86,3 +86,30 @@ def test_query_attn_other_queries_do_not_leak():
     for q in (0, 2):
         lo, hi = int(qo[q]) - 500, int(qo[q + 1]) - 500
         assert torch.equal(a[lo:hi], b[lo:hi]), q
+
+
+def test_query_attn_long_corpus_bench_config():
+    """The bench's query-only configuration at full size: 16 queries of 32 tokens over the long
+    prompt's cached corpus (instruction + 500 documents, 100,064 tokens).  Queries are independent,
+    so three of them are checked against the oracle run on the corpus plus that query alone."""
+    w = workloads.make("long", 0)
+    offs = [int(x) for x in w.segment_offsets]
+    corpus = offs[-2]
+    Hq, d, Hkv = w.Q.shape[1], w.Q.shape[2], w.K.shape[1]
+    rng = np.random.default_rng(1000)
+    nq, ql = 16, 32
+    bf = lambda a: workloads.f32_to_bf16_bits(a.astype(np.float32))
+    Kq, Vq = bf(rng.standard_normal((nq * ql, Hkv, d))), bf(rng.standard_normal((nq * ql, Hkv, d)))
+    Qq = bf(rng.standard_normal((nq * ql, Hq, d)))
+    K = np.concatenate([w.K[:corpus], Kq]); V = np.concatenate([w.V[:corpus], Vq])
+    qo = (np.arange(nq + 1) * ql + corpus).astype(np.int32)
+    log(f"[query long] {nq} x {ql} tokens over a {corpus}-token corpus")
+    out, lse = br.query_attn(dev_bf16(Qq), dev_bf16(K), dev_bf16(V), corpus, qo, lse=True)
+    torch.cuda.synchronize()
+    for b in (0, 7, 15):
+        a, e = b * ql, (b + 1) * ql
+        Ks = np.concatenate([w.K[:corpus], Kq[a:e]]); Vs = np.concatenate([w.V[:corpus], Vq[a:e]])
+        O_ref, lse_ref = orc.query_attn(Qq[a:e], Ks, Vs, corpus, [corpus, corpus + ql])
+        check_attn(out[a:e], O_ref, what=f"query {b}")
+        rel = np.abs(lse[a:e].cpu().numpy() - lse_ref) / np.maximum(np.abs(lse_ref), 1.0)
+        assert rel.max() <= LSE_RTOL, f"query {b}: lse rel err {rel.max():.3e}"
