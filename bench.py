@@ -432,8 +432,8 @@ def cpu_baseline(w, n_docs_sample, log):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="long", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--secondary", default="worked", help="extra config timed in the same run ('' for none)")
