@@ -105,3 +105,32 @@ def test_attn_bwd_long_prompt_identities():
     log(f"  sum dV vs sum dO: {err_v:.2e};  |sum dK| / sum |dK|: {err_k:.2e}")
     assert err_v <= 1e-2 and err_k <= 1e-2
     assert torch.isfinite(dQ).all() and torch.isfinite(dK).all() and torch.isfinite(dV).all()
+
+
+def test_attn_bwd_edge_shapes():
+    """Degenerate tables: no instruction, one-token documents and queries, a single document, and
+    the largest group size."""
+    prompts = [(0, [1, 1, 5], 1), (3, [1], 1), (0, [7], 2), (1, [2, 1, 1, 1], 3)]
+    for hq, hkv, d in ((8, 1, 64), (4, 4, 128)):
+        w = workloads.make_custom(prompts, hq, hkv, d, 1, 2800 + hq)
+        log(f"[attn bwd edge] Hq={hq} Hkv={hkv} d={d} T={w.total_tokens}")
+        dQ, dK, dV, dO_bits = run_case(w, 13)
+        rQ, rK, rV = orc.attn_bwd(w.Q, w.K, w.V, dO_bits, w.segment_offsets, w.seg_ptr)
+        check_grad(dQ, rQ, "dQ")
+        check_grad(dK, rK, "dK")
+        check_grad(dV, rV, "dV")
+
+
+def test_readout_bwd_single_document_is_zero():
+    """With one document per prompt every score is |S| whatever Q_S and K are: the readout's
+    gradient is exactly zero (and InfoNCE's loss is zero)."""
+    prompts = [(4, [9], 3), (0, [5], 2)]
+    w = workloads.make_custom(prompts, 8, 2, 64, 2, 2900)
+    dev = upload(w)
+    log("[readout bwd] one document per prompt")
+    scores = br.doc_scores(dev["Q_S"], dev["K"], w.doc_offsets, w.doc_ptr)
+    loss, ds = br.infonce(scores, w.doc_ptr, np.zeros(2, dtype=np.int32))
+    dQs, dK = br.doc_scores_bwd(dev["Q_S"], dev["K"], w.doc_offsets, w.doc_ptr, ds)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(loss) == 0 and torch.count_nonzero(ds) == 0
+    assert torch.count_nonzero(dQs) == 0 and torch.count_nonzero(dK) == 0
