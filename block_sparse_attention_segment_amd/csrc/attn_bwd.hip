@@ -9,7 +9,7 @@
 //   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO
 // Only allowed (row, key) pairs are visited, through the same host plans as the forward:
 //   attn_bwd_dq_kernel   query-major over the forward plan's row tiles (128 (token, head) rows,
-//                        4 waves of 32 rows): per 64-key tile S^T = K Q^T and dP^T = V dO^T
+//                        4 waves of 32 rows); it also forms Dr for its rows: per 64-key tile S^T = K Q^T and dP^T = V dO^T
 //                        (keys on M), dS^T in fp32, dQ^T += K^T dS^T with dS rounded to bf16
 //                        and K^T fragments from transposing LDS reads (as V^T in the forward).
 //   attn_bwd_dkv_kernel  key-major: 64 keys of one KV head per workgroup (2 waves of 32 keys);
@@ -25,33 +25,11 @@
 
 namespace br {
 
-// Dr[t, h] = sum_d dO[t, h, d] O[t, h, d] in fp32: 16 lanes per row of D = 128 (8 for D = 64).
-template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_rowdot_kernel(const uint16_t* __restrict__ O,
-                                                              const uint16_t* __restrict__ dO,
-                                                              float* __restrict__ dvec, int64_t rows) {
-  constexpr int L = D / 8;
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t row = i / L;
-  const int c = int(i % L);
-  float acc = 0.f;
-  if (row < rows) {
-    const u32x4_t a = load16(O + row * D + 8 * c), b = load16(dO + row * D + 8 * c);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc = fmaf(__uint_as_float(a[j] << 16), __uint_as_float(b[j] << 16), acc);
-      acc = fmaf(__uint_as_float(a[j] & 0xffff0000u), __uint_as_float(b[j] & 0xffff0000u), acc);
-    }
-  }
-#pragma unroll
-  for (int m = L / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, L);
-  if (row < rows && c == 0) dvec[row] = acc;
-}
-
 template <int D, int G>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                                                          const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                                                          const float* __restrict__ lse, const float* __restrict__ dvec,
+                                                          const uint16_t* __restrict__ V, const uint16_t* __restrict__ O,
+                                                          const uint16_t* __restrict__ dO,
+                                                          const float* __restrict__ lse, float* __restrict__ dvec,
                                                           float* __restrict__ dQ, const AttnItem* __restrict__ items,
                                                           float* __restrict__ part_dq, int Hq, int Hkv, float scale,
                                                           float scale_log2) {
@@ -87,7 +65,26 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __r
   }
   const int64_t rix = int64_t(row_tok) * Hq + h;
   const float l2 = row_ok ? lse[rix] * kLog2e : 0.f;
-  const float dr = row_ok ? dvec[rix] : 0.f;
+  // Dr = rowsum(dO * O) for this lane's row: each lane half holds 64 of the row's elements.  The
+  // item that owns the row's output (a direct tile, or the split chunk that carries the causal
+  // part) also stores it for the key-major kernel that runs next.
+  float dr;
+  {
+    const rsrc_t ro = make_rsrc(O + (int64_t(it.row0) * Hq + g * G) * D, rows * q_stride * 2);
+    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int s = 0; s < DSTEPS; ++s) {
+      const u32x4_t ov = buf_load16(ro, q_off + 32 * s);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc0 = fmaf(__uint_as_float(ov[j] << 16), __uint_as_float(df[s][j] << 16), acc0);
+        acc1 = fmaf(__uint_as_float(ov[j] & 0xffff0000u), __uint_as_float(df[s][j] & 0xffff0000u), acc1);
+      }
+    }
+    dr = acc0 + acc1;
+    dr += other_half(dr);
+    if (row_ok && half == 0 && (it.slot < 0 || it.b_end > it.b_start)) dvec[rix] = dr;
+  }
 
   const int kcc = tid % KCH, kr0 = tid / KCH;
   const uint32_t k_off = uint32_t((kr0 * kv_stride + 8 * kcc) * 2);
@@ -388,14 +385,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_merge_kernel(float* __restri
 
 template <int D, int G>
 static hipError_t launch_bwd_t(const BwdLaunch& a, hipStream_t stream) {
-  const int64_t rows = a.total_tokens * a.num_q_heads;
-  const int64_t lanes = rows * (D / 8);
-  attn_bwd_rowdot_kernel<D><<<unsigned((lanes + 255) / 256), 256, 0, stream>>>(a.O, a.dO, a.dvec, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
   if (a.n_items > 0) {
     attn_bwd_dq_kernel<D, G><<<unsigned(a.n_items * a.num_kv_heads), 256, 0, stream>>>(
-        a.Q, a.K, a.V, a.dO, a.lse, a.dvec, a.dQ, a.items, a.part_dq, a.num_q_heads, a.num_kv_heads, a.scale,
+        a.Q, a.K, a.V, a.O, a.dO, a.lse, a.dvec, a.dQ, a.items, a.part_dq, a.num_q_heads, a.num_kv_heads, a.scale,
         a.scale * kLog2e);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
