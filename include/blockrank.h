@@ -21,6 +21,14 @@
  *   br_sort_docs    per prompt, document indices by descending s_k (ties: lower index)
  *                   (BlockRank summary, "Efficient Attention-Based Inference" step 3;
  *                   blog, direct output).
+ * and around that path:
+ *   br_query_attn_fwd   query rows only, over a cached corpus (BlockSearch, section 3.2);
+ *   br_attn_routed_fwd  attention over a top-B subset of the documents (BlockSearch, 5.1);
+ *   br_ssmax_softmax_scale  the SSMax logit factor s ln N / sqrt(d) (BlockSearch, 5.1);
+ *   br_rope_fwd, br_rope_signal_fwd  RoPE at permutation-invariant positions (BlockRank
+ *                   summary, 3.4; BlockSearch, 3.2);
+ *   br_attn_bwd, br_infonce, br_doc_scores_bwd  the backward of the attention, the InfoNCE
+ *                   auxiliary loss and the readout (BlockRank summary, 3.4).
  *
  * Conventions (all entry points):
  *   - Every function returns br_status; BR_OK == 0.  Nothing aborts or throws.
