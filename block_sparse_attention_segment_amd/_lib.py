@@ -205,9 +205,8 @@ def attn_fwd(Q, K, V, segment_offsets, seg_ptr, out=None, lse=None, softmax_scal
         lse = torch.empty((T, Hq), dtype=torch.float32, device=Q.device)
     elif lse is False:
         lse = None
-    nbytes = attn_workspace_bytes(dims, so, sp)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+    if workspace is None:  # a caller's workspace is checked by the library
+        workspace = torch.empty(attn_workspace_bytes(dims, so, sp), dtype=torch.uint8, device=Q.device)
     ev0, ev1 = kernel_events if kernel_events is not None else (None, None)
     _check(lib.br_attn_fwd_timed(ctypes.byref(dims), Q.data_ptr(), K.data_ptr(), V.data_ptr(), _ptr_i32(so),
                                  _ptr_i32(sp), out.data_ptr(), _dev_ptr(lse), float(softmax_scale),
@@ -248,9 +247,8 @@ def attn_routed(Q, K, V, segment_offsets, seg_ptr, keep_ptr, keep, out=None, lse
         lse = torch.zeros((T, Hq), dtype=torch.float32, device=Q.device)
     elif lse is False:
         lse = None
-    nbytes = attn_routed_workspace_bytes(dims, so, sp, kp, kk)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+    if workspace is None:  # a caller's workspace is checked by the library
+        workspace = torch.empty(attn_routed_workspace_bytes(dims, so, sp, kp, kk), dtype=torch.uint8, device=Q.device)
     _check(lib.br_attn_routed_fwd(ctypes.byref(dims), Q.data_ptr(), K.data_ptr(), V.data_ptr(), _ptr_i32(so),
                                   _ptr_i32(sp), _ptr_i32(kp), _ptr_i32(kk), out.data_ptr(), _dev_ptr(lse),
                                   float(softmax_scale), workspace.data_ptr(), workspace.numel(),
@@ -299,9 +297,8 @@ def attn_bwd(Q, K, V, O, dO, lse, segment_offsets, seg_ptr, softmax_scale: float
     dQ = torch.empty((T, Hq, d), **f32) if dQ is None else dQ
     dK = torch.empty((T, Hkv, d), **f32) if dK is None else dK
     dV = torch.empty((T, Hkv, d), **f32) if dV is None else dV
-    nbytes = attn_bwd_workspace_bytes(dims, so, sp)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+    if workspace is None:  # a caller's workspace is checked by the library
+        workspace = torch.empty(attn_bwd_workspace_bytes(dims, so, sp), dtype=torch.uint8, device=Q.device)
     _check(lib.br_attn_bwd(ctypes.byref(dims), Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), dO.data_ptr(),
                            lse.data_ptr(), _ptr_i32(so), _ptr_i32(sp), dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(),
                            float(softmax_scale), workspace.data_ptr(), workspace.numel(), _stream_handle(stream)))
@@ -320,9 +317,9 @@ def infonce(scores, doc_ptr, gold, tau: float = 0.05, loss=None, dscores=None, w
         raise ValueError("gold must have one entry per prompt")
     loss = torch.empty(B, dtype=torch.float32, device=scores.device) if loss is None else loss
     dscores = torch.empty_like(scores) if dscores is None else dscores
-    out = ctypes.c_size_t(0)
-    _check(lib.br_infonce_workspace_bytes(B, ctypes.byref(out)))
-    if workspace is None or workspace.numel() < out.value:
+    if workspace is None:  # a caller's workspace is checked by the library
+        out = ctypes.c_size_t(0)
+        _check(lib.br_infonce_workspace_bytes(B, ctypes.byref(out)))
         workspace = torch.empty(out.value, dtype=torch.uint8, device=scores.device)
     _check(lib.br_infonce(scores.data_ptr(), _ptr_i32(dp), B, _ptr_i32(gd), float(tau), loss.data_ptr(),
                           dscores.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream_handle(stream)))
@@ -354,9 +351,8 @@ def doc_scores_bwd(Q_S, K, doc_offsets, doc_ptr, dscores, softmax_scale: float =
     dims = make_dims(B, Hq, Hkv, d, T)
     dQ_S = torch.empty((B, S, Hq, d), dtype=torch.float32, device=K.device) if dQ_S is None else dQ_S
     dK = torch.zeros((T, Hkv, d), dtype=torch.float32, device=K.device) if dK is None else dK
-    nbytes = doc_scores_bwd_workspace_bytes(dims, S, do, dp)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=K.device)
+    if workspace is None:  # a caller's workspace is checked by the library
+        workspace = torch.empty(doc_scores_bwd_workspace_bytes(dims, S, do, dp), dtype=torch.uint8, device=K.device)
     _check(lib.br_doc_scores_bwd(ctypes.byref(dims), Q_S.data_ptr(), int(S), K.data_ptr(), _ptr_i32(do), _ptr_i32(dp),
                                  dscores.data_ptr(), dQ_S.data_ptr(), dK.data_ptr(), int(bool(accumulate)),
                                  float(softmax_scale), workspace.data_ptr(), workspace.numel(), _stream_handle(stream)))
@@ -421,9 +417,8 @@ def rope(Q, K, segment_offsets, seg_ptr, rope_theta: float = 10000.0, query_pos0
         Q_out = Q if inplace else torch.empty_like(Q)
     if K is not None and K_out is None:
         K_out = K if inplace else torch.empty_like(K)
-    nbytes = rope_workspace_bytes(dims, sp)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=ref.device)
+    if workspace is None:  # a caller's workspace is checked by the library
+        workspace = torch.empty(rope_workspace_bytes(dims, sp), dtype=torch.uint8, device=ref.device)
     _check(lib.br_rope_fwd(ctypes.byref(dims), _dev_ptr(Q), _dev_ptr(K), _dev_ptr(Q_out), _dev_ptr(K_out),
                            _ptr_i32(so), _ptr_i32(sp), float(rope_theta), int(query_pos0),
                            int(bool(docs_after_instruction)), int(bool(interleaved)), workspace.data_ptr(),
@@ -446,9 +441,8 @@ def rope_signal(Q_S, segment_offsets, seg_ptr, rope_theta: float = 10000.0, quer
     dims = make_dims(B, Hq, num_kv_heads or Hq, d, int(so[sp[-1] - 1]))
     if out is None:
         out = Q_S if inplace else torch.empty_like(Q_S)
-    nbytes = rope_workspace_bytes(dims, sp)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q_S.device)
+    if workspace is None:  # a caller's workspace is checked by the library
+        workspace = torch.empty(rope_workspace_bytes(dims, sp), dtype=torch.uint8, device=Q_S.device)
     _check(lib.br_rope_signal_fwd(ctypes.byref(dims), Q_S.data_ptr(), out.data_ptr(), int(S), _ptr_i32(so),
                                   _ptr_i32(sp), float(rope_theta), int(query_pos0), int(bool(interleaved)),
                                   workspace.data_ptr(), workspace.numel(), _stream_handle(stream)))
@@ -486,9 +480,8 @@ def query_attn(Q, K, V, corpus_len: int, query_offsets, out=None, lse=None, soft
         lse = torch.empty((Tq, Hq), dtype=torch.float32, device=Q.device)
     elif lse is False:
         lse = None
-    nbytes = query_attn_workspace_bytes(dims, corpus_len, qo)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+    if workspace is None:  # a caller's workspace is checked by the library
+        workspace = torch.empty(query_attn_workspace_bytes(dims, corpus_len, qo), dtype=torch.uint8, device=Q.device)
     _check(lib.br_query_attn_fwd(ctypes.byref(dims), Q.data_ptr(), K.data_ptr(), V.data_ptr(), int(corpus_len),
                                  _ptr_i32(qo), out.data_ptr(), _dev_ptr(lse), float(softmax_scale),
                                  workspace.data_ptr(), workspace.numel(), _stream_handle(stream)))
@@ -526,9 +519,8 @@ def doc_scores(Q_S, K, doc_offsets, doc_ptr, head_scores: bool = False, softmax_
     if scores is None:
         scores = torch.empty(n_docs, dtype=torch.float32, device=K.device)
     hs = torch.empty((Hq, n_docs), dtype=torch.float32, device=K.device) if head_scores else None
-    nbytes = doc_scores_workspace_bytes(dims, S, do, dp)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=K.device)
+    if workspace is None:  # a caller's workspace is checked by the library
+        workspace = torch.empty(doc_scores_workspace_bytes(dims, S, do, dp), dtype=torch.uint8, device=K.device)
     _check(lib.br_doc_scores(ctypes.byref(dims), Q_S.data_ptr(), int(S), K.data_ptr(), _ptr_i32(do), _ptr_i32(dp),
                              scores.data_ptr(), _dev_ptr(hs), float(softmax_scale), workspace.data_ptr(),
                              workspace.numel(), _stream_handle(stream)))

@@ -14,7 +14,6 @@
 #include <cmath>
 #include <cstdio>
 #include <functional>
-#include <queue>
 #include <utility>
 #include <vector>
 
@@ -136,7 +135,7 @@ void add_query_rows(int64_t qs, int64_t qe, int64_t u0, int64_t u1, const ItemMa
   add_query_rows(qs, qe, ranges, mk, plan, out);
 }
 
-// Workspace layout and the default schedule.
+// Workspace layout (the schedule is made per device, by the caller).
 void finish_plan(const br_dims& dims, AttnPlan* plan) {
   AttnPlan& P = *plan;
   const size_t hkv = size_t(dims.num_kv_heads), d = size_t(dims.head_dim);
@@ -146,7 +145,6 @@ void finish_plan(const br_dims& dims, AttnPlan* plan) {
   P.off_part_o = align_up(P.off_merges + P.merges.size() * sizeof(MergeItem), 256);
   P.off_part_ml = align_up(P.off_part_o + size_t(P.n_slots) * hkv * kRowsPerTile * d * 4, 256);
   P.total_bytes = align_up(P.off_part_ml + size_t(P.n_slots) * hkv * kRowsPerTile * 2 * 4, 256);
-  schedule_attn_plan(dims.num_kv_heads, 256 * kAttnWgPerCu, plan);
 }
 
 // Longest items first (the split query chunks), the rest after in the order given.
@@ -332,15 +330,20 @@ void schedule_attn_plan(int num_kv_heads, int workgroups, AttnPlan* plan) {
   P.wg_per_head = W;
   std::vector<int32_t> owner(static_cast<size_t>(n_items));
   std::vector<int32_t> count(size_t(W), 0);
-  using Slot = std::pair<int64_t, int32_t>;  // (time the workgroup becomes free, workgroup)
-  std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> free_at;
-  for (int w = 0; w < W; ++w) free_at.push({0, w});
+  std::vector<int64_t> free_at(size_t(W), 0);  // time each workgroup becomes free
   for (int64_t i = 0; i < n_items; ++i) {
-    const Slot s = free_at.top();
-    free_at.pop();
-    owner[size_t(i)] = s.second;
-    ++count[size_t(s.second)];
-    free_at.push({s.first + attn_item_cost(P.items[size_t(i)]), s.second});
+    // earliest-free workgroup, ties to the lowest index (a linear scan over at most a few
+    // hundred workgroups is cheaper than a heap here)
+    int best = 0;
+    int64_t t = free_at[0];
+    for (int w = 1; w < W; ++w)
+      if (free_at[size_t(w)] < t) {
+        t = free_at[size_t(w)];
+        best = w;
+      }
+    owner[size_t(i)] = best;
+    ++count[size_t(best)];
+    free_at[size_t(best)] = t + attn_item_cost(P.items[size_t(i)]);
   }
   P.ranges.assign(size_t(W) + 1, 0);
   for (int w = 0; w < W; ++w) P.ranges[size_t(w) + 1] = P.ranges[size_t(w)] + count[size_t(w)];
