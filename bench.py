@@ -146,34 +146,38 @@ def measure(config, seed, steps, warmup, log):
     out = torch.empty_like(Q)
     scores = torch.empty(w.num_docs, dtype=torch.float32, device="cuda")
     order = torch.empty(w.num_docs, dtype=torch.int32, device="cuda")
-    ws_a = torch.empty(br.attn_workspace_bytes(dims, w.segment_offsets, w.seg_ptr), dtype=torch.uint8, device="cuda")
-    ws_s = torch.empty(br.doc_scores_workspace_bytes(dims, w.n_signal, w.doc_offsets, w.doc_ptr), dtype=torch.uint8,
-                       device="cuda")
+    ws = torch.empty(br.rank_workspace_bytes(dims, w.segment_offsets, w.seg_ptr, w.n_signal, w.doc_offsets, w.doc_ptr),
+                     dtype=torch.uint8, device="cuda")
     ev = HipEvents(2 * steps)
     stream = torch.cuda.current_stream()
 
     def step(kernel_events=None):
-        br.attn_fwd(Q, K, V, w.segment_offsets, w.seg_ptr, out=out, workspace=ws_a, stream=stream,
-                    kernel_events=kernel_events)
-        br.doc_scores(Q_S, K, w.doc_offsets, w.doc_ptr, scores=scores, workspace=ws_s, stream=stream)
-        br.sort_docs(scores, w.doc_ptr, order=order, stream=stream)
+        # attention (+ split-key merge), readout and rank in one library call (br_rank_prompts)
+        br.rank_step(Q, K, V, Q_S, w.segment_offsets, w.seg_ptr, w.doc_offsets, w.doc_ptr, out=out, scores=scores,
+                     order=order, workspace=ws, stream=stream, kernel_events=kernel_events)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     log(f"[bench] {config}: {warmup} warm-up steps done")
-    # Timed region: K back-to-back steps between two events; the attention kernel's own duration
-    # per step comes from events the library records around it on the same stream.
+    # Timed region: K back-to-back steps between two events, with nothing else recorded (an event
+    # between two kernels costs the stream a few microseconds).
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     e0.record(stream)
     for i in range(steps):
-        step(kernel_events=(ev.ev[2 * i], ev.ev[2 * i + 1]))
+        step()
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = e0.elapsed_time(e1) / steps
+    # Kernel region: K more back-to-back steps, the attention kernel's own duration per step from
+    # events the library records around it on its launch stream.
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(kernel_events=(ev.ev[2 * i], ev.ev[2 * i + 1]))
+    torch.cuda.synchronize()
     kern = [ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(steps)]
     ev.close()
     # Per-step latency distribution (one step at a time, each between two events).

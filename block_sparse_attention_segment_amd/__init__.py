@@ -8,14 +8,14 @@ from ._lib import (BlockRankError, BrDims, EXPORTED, LIB_PATH, attn_bwd, attn_bw
                    attn_routed, attn_routed_workspace_bytes,
                    attn_workspace_bytes, doc_scores, doc_scores_bwd, doc_scores_bwd_workspace_bytes, doc_scores_workspace_bytes,
                    infonce, load_library,
-                   make_dims, query_attn, query_attn_workspace_bytes, rope, rope_positions, rope_signal,
+                   make_dims, query_attn, query_attn_workspace_bytes, rank_step, rank_workspace_bytes, rope, rope_positions, rope_signal,
                    rope_workspace_bytes, sort_docs, ssmax_scale, version)
 
 __all__ = ["BlockRankError", "BrDims", "EXPORTED", "LIB_PATH", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd", "attn_plan_items", "attn_plan_schedule",
            "attn_routed", "attn_routed_workspace_bytes",
            "attn_workspace_bytes", "doc_scores", "doc_scores_bwd", "doc_scores_bwd_workspace_bytes",
            "doc_scores_workspace_bytes", "infonce", "load_library",
-           "make_dims", "query_attn", "query_attn_workspace_bytes", "rope", "rope_positions", "rope_signal",
+           "make_dims", "query_attn", "query_attn_workspace_bytes", "rank_step", "rank_workspace_bytes", "rope", "rope_positions", "rope_signal",
            "rope_workspace_bytes", "sort_docs", "ssmax_scale", "version", "rank_prompts"]
 
 

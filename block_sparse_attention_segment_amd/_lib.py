@@ -19,7 +19,7 @@ BR_OK, BR_ERR_INVALID_ARG, BR_ERR_UNSUPPORTED, BR_ERR_WORKSPACE, BR_ERR_HIP = ra
 
 # Symbols the header declares; the CPU test checks the library exports each of them.
 EXPORTED = ("br_attn_workspace_bytes", "br_attn_fwd", "br_attn_fwd_timed", "br_doc_scores_workspace_bytes", "br_doc_scores",
-            "br_sort_docs", "br_attn_plan_items", "br_attn_plan_schedule", "br_query_attn_workspace_bytes", "br_query_attn_fwd", "br_attn_routed_workspace_bytes", "br_attn_routed_fwd",
+            "br_sort_docs", "br_rank_workspace_bytes", "br_rank_prompts", "br_rank_prompts_timed", "br_attn_plan_items", "br_attn_plan_schedule", "br_query_attn_workspace_bytes", "br_query_attn_fwd", "br_attn_routed_workspace_bytes", "br_attn_routed_fwd",
             "br_attn_bwd_workspace_bytes", "br_attn_bwd", "br_attn_bwd_plan_items",
             "br_infonce_workspace_bytes", "br_infonce", "br_doc_scores_bwd_workspace_bytes", "br_doc_scores_bwd",
             "br_ssmax_softmax_scale", "br_rope_workspace_bytes", "br_rope_fwd", "br_rope_signal_fwd", "br_rope_positions",
@@ -65,6 +65,11 @@ def load_library() -> ctypes.CDLL:
         "br_doc_scores": [dims_p, _P, ctypes.c_int32, _P, _I32P, _I32P, _P, _P, ctypes.c_float, _P,
                           ctypes.c_size_t, _P],
         "br_sort_docs": [_P, _I32P, ctypes.c_int32, _P, _P],
+        "br_rank_workspace_bytes": [dims_p, _I32P, _I32P, ctypes.c_int32, _I32P, _I32P, sz_p],
+        "br_rank_prompts": [dims_p, _P, _P, _P, _P, ctypes.c_int32, _I32P, _I32P, _I32P, _I32P, _P, _P, _P, _P, _P,
+                            ctypes.c_float, _P, ctypes.c_size_t, _P],
+        "br_rank_prompts_timed": [dims_p, _P, _P, _P, _P, ctypes.c_int32, _I32P, _I32P, _I32P, _I32P, _P, _P, _P, _P,
+                                  _P, ctypes.c_float, _P, ctypes.c_size_t, _P, _P, _P],
         "br_attn_plan_items": [dims_p, _I32P, _I32P, _I32P, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64),
                                ctypes.POINTER(ctypes.c_int32)],
         "br_attn_routed_workspace_bytes": [dims_p, _I32P, _I32P, _I32P, _I32P, ctypes.POINTER(ctypes.c_size_t)],
@@ -539,6 +544,49 @@ def sort_docs(scores, doc_ptr, order=None, stream=None):
     _check(lib.br_sort_docs(scores.data_ptr(), _ptr_i32(dp), len(dp) - 1, order.data_ptr(),
                             _stream_handle(stream)))
     return order
+
+
+def rank_workspace_bytes(dims: BrDims, segment_offsets, seg_ptr, n_signal: int, doc_offsets, doc_ptr) -> int:
+    lib = load_library()
+    so, sp, do, dp = _host_i32(segment_offsets), _host_i32(seg_ptr), _host_i32(doc_offsets), _host_i32(doc_ptr)
+    out = ctypes.c_size_t(0)
+    _check(lib.br_rank_workspace_bytes(ctypes.byref(dims), _ptr_i32(so), _ptr_i32(sp), int(n_signal), _ptr_i32(do),
+                                       _ptr_i32(dp), ctypes.byref(out)))
+    return int(out.value)
+
+
+def rank_step(Q, K, V, Q_S, segment_offsets, seg_ptr, doc_offsets, doc_ptr, softmax_scale: float = 0.0, out=None,
+              lse=None, scores=None, head_scores=None, order=None, workspace=None, stream=None, kernel_events=None):
+    """The whole hot path in one library call (br_rank_prompts): attention output, document scores
+    and per-prompt order, bit-identical to attn_fwd + doc_scores + sort_docs."""
+    import torch
+    lib = load_library()
+    for name, t, nd in (("Q", Q, 3), ("K", K, 3), ("V", V, 3), ("Q_S", Q_S, 4)):
+        _check_bf16(name, t, nd)
+    T, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    if K.shape != (T, Hkv, d) or V.shape != K.shape or Q_S.shape[2:] != (Hq, d):
+        raise ValueError("shapes: Q [T,Hq,d], K/V [T,Hkv,d], Q_S [B,S,Hq,d]")
+    so, sp, do, dp = _host_i32(segment_offsets), _host_i32(seg_ptr), _host_i32(doc_offsets), _host_i32(doc_ptr)
+    B, S = Q_S.shape[0], Q_S.shape[1]
+    dims = make_dims(B, Hq, Hkv, d, T)
+    n_docs = int(dp[-1]) - B
+    out = torch.empty_like(Q) if out is None else out
+    if lse is True:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=Q.device)
+    elif lse is False:
+        lse = None
+    scores = torch.empty(n_docs, dtype=torch.float32, device=Q.device) if scores is None else scores
+    order = torch.empty(n_docs, dtype=torch.int32, device=Q.device) if order is None else order
+    if workspace is None:  # a caller's workspace is checked by the library
+        workspace = torch.empty(rank_workspace_bytes(dims, so, sp, S, do, dp), dtype=torch.uint8, device=Q.device)
+    ev0, ev1 = kernel_events if kernel_events is not None else (None, None)
+    _check(lib.br_rank_prompts_timed(ctypes.byref(dims), Q.data_ptr(), K.data_ptr(), V.data_ptr(), Q_S.data_ptr(), int(S),
+                                     _ptr_i32(so), _ptr_i32(sp), _ptr_i32(do), _ptr_i32(dp), out.data_ptr(),
+                                     _dev_ptr(lse), scores.data_ptr(), _dev_ptr(head_scores), order.data_ptr(),
+                                     float(softmax_scale), workspace.data_ptr(), workspace.numel(),
+                                     _stream_handle(stream), ev0, ev1))
+    return out, scores, order
 
 
 def version() -> str:

@@ -904,3 +904,165 @@ br_status br_doc_scores_bwd(const br_dims* dims, const void* Q_S, int32_t n_sign
 }
 
 }  // extern "C"
+
+// ---- one call for the whole hot path: attention, readout, rank ----------------------------------
+
+namespace {
+
+// Workspace of the fused call: [attention plan image | readout plan image | attention partials |
+// readout statistics], so that both plans go up in one copy.
+struct RankLayout {
+  size_t score_plan = 0, attn_part = 0, score_ml = 0, total = 0;
+};
+RankLayout rank_layout(const br::AttnPlan& ap, const br::ScorePlan& sp) {
+  RankLayout L;
+  L.score_plan = br::align_up(ap.off_part_o, 256);
+  L.attn_part = br::align_up(L.score_plan + sp.off_ml, 256);
+  L.score_ml = br::align_up(L.attn_part + (ap.total_bytes - ap.off_part_o), 256);
+  L.total = br::align_up(L.score_ml + (sp.total_bytes - sp.off_ml), 256);
+  return L;
+}
+
+br_status check_sort_table(const int32_t* doc_ptr, int num_prompts, std::vector<int32_t>* base) {
+  base->resize(size_t(num_prompts) + 1);
+  for (int b = 0; b <= num_prompts; ++b) (*base)[size_t(b)] = doc_ptr[b] - b;
+  for (int b = 0; b < num_prompts; ++b)
+    if ((*base)[size_t(b) + 1] - (*base)[size_t(b)] > br::kSortMaxDocs)
+      return record(BR_ERR_UNSUPPORTED, "prompt " + std::to_string(b) + " has more than " +
+                                            std::to_string(br::kSortMaxDocs) + " documents to sort");
+  return BR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+br_status br_rank_workspace_bytes(const br_dims* dims, const int32_t* segment_offsets, const int32_t* seg_ptr,
+                                  int32_t n_signal, const int32_t* doc_offsets, const int32_t* doc_ptr,
+                                  size_t* bytes) {
+  return guarded([&]() -> br_status {
+    if (!bytes) return record(BR_ERR_INVALID_ARG, "bytes is NULL");
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    br::AttnPlan ap;
+    e = br::build_attn_plan(*dims, segment_offsets, seg_ptr, &ap);
+    if (!e.ok()) return record(e);
+    br::ScorePlan sp;
+    e = br::build_score_plan(*dims, n_signal, doc_offsets, doc_ptr, &sp);
+    if (!e.ok()) return record(e);
+    *bytes = rank_layout(ap, sp).total;
+    return BR_OK;
+  });
+}
+
+br_status br_rank_prompts_timed(const br_dims* dims, const void* Q, const void* K, const void* V, const void* Q_S,
+                                int32_t n_signal, const int32_t* segment_offsets, const int32_t* seg_ptr,
+                                const int32_t* doc_offsets, const int32_t* doc_ptr, void* out, float* lse,
+                                float* scores, float* head_scores, int32_t* order, float softmax_scale,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t kernel_start, hipEvent_t kernel_stop) {
+  return guarded([&]() -> br_status {
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    br_status st = check_attn_buffers(Q, K, V, out, lse, softmax_scale);
+    if (st != BR_OK) return st;
+    if (!Q_S || !scores || !order) return record(BR_ERR_INVALID_ARG, "Q_S, scores and order must be non-NULL");
+    if (!aligned(Q_S, 16) || !aligned(scores, 4) || !aligned(order, 4) || (head_scores && !aligned(head_scores, 4)))
+      return record(BR_ERR_INVALID_ARG, "Q_S must be 16-byte aligned; scores, head_scores and order 4-byte");
+    br::AttnPlan ap;
+    e = br::build_attn_plan(*dims, segment_offsets, seg_ptr, &ap);
+    if (!e.ok()) return record(e);
+    br::ScorePlan sp;
+    e = br::build_score_plan(*dims, n_signal, doc_offsets, doc_ptr, &sp);
+    if (!e.ok()) return record(e);
+    std::vector<int32_t> base;
+    st = check_sort_table(doc_ptr, dims->num_prompts, &base);
+    if (st != BR_OK) return st;
+    const RankLayout L = rank_layout(ap, sp);
+    if (!workspace || workspace_bytes < L.total)
+      return record(BR_ERR_WORKSPACE, "workspace is NULL or smaller than br_rank_workspace_bytes() = " +
+                                          std::to_string(L.total));
+    if (!aligned(workspace, 16)) return record(BR_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    int workgroups = 0;
+    hipError_t he = attn_workgroups(&workgroups);
+    if (he != hipSuccess) return hip_fail(he, "device query");
+    br::schedule_attn_plan(dims->num_kv_heads, workgroups, &ap);
+
+    // One host image for both plans, one copy.
+    const int B = dims->num_prompts;
+    std::vector<unsigned char> host(L.score_plan + sp.off_ml, 0);
+    std::memcpy(host.data() + ap.off_items, ap.sched.data(), ap.sched.size() * sizeof(br::AttnItem));
+    std::memcpy(host.data() + ap.off_ranges, ap.ranges.data(), ap.ranges.size() * sizeof(int32_t));
+    if (!ap.merges.empty())
+      std::memcpy(host.data() + ap.off_merges, ap.merges.data(), ap.merges.size() * sizeof(br::MergeItem));
+    unsigned char* hs = host.data() + L.score_plan;
+    std::memcpy(hs + sp.off_items, sp.items.data(), sp.items.size() * sizeof(br::ScoreItem));
+    std::memcpy(hs + sp.off_doc_offsets, doc_offsets, size_t(doc_ptr[B]) * sizeof(int32_t));
+    std::memcpy(hs + sp.off_prompt_base, sp.prompt_score_base.data(), size_t(B + 1) * sizeof(int32_t));
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    st = upload(ws, host.data(), host.size(), stream);
+    if (st != BR_OK) return st;
+
+    br::AttnLaunch a;
+    a.Q = static_cast<const uint16_t*>(Q);
+    a.K = static_cast<const uint16_t*>(K);
+    a.V = static_cast<const uint16_t*>(V);
+    a.O = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    a.items = reinterpret_cast<const br::AttnItem*>(ws + ap.off_items);
+    a.ranges = reinterpret_cast<const int32_t*>(ws + ap.off_ranges);
+    a.merges = reinterpret_cast<const br::MergeItem*>(ws + ap.off_merges);
+    a.part_o = reinterpret_cast<float*>(ws + L.attn_part);
+    a.part_ml = reinterpret_cast<float*>(ws + L.attn_part + (ap.off_part_ml - ap.off_part_o));
+    a.n_items = int64_t(ap.items.size());
+    a.n_merges = int64_t(ap.merges.size());
+    a.wg_per_head = ap.wg_per_head;
+    a.num_q_heads = dims->num_q_heads;
+    a.num_kv_heads = dims->num_kv_heads;
+    a.head_dim = dims->head_dim;
+    const float scale = resolve_scale(softmax_scale, dims->head_dim);
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.q_row_base = 0;
+    a.ev_start = kernel_start;
+    a.ev_stop = kernel_stop;
+    he = br::launch_attn(a, stream);
+    if (he != hipSuccess) return hip_fail(he, "attention kernel launch");
+
+    unsigned char* wsp = ws + L.score_plan;
+    br::ScoreLaunch r;
+    r.Q_S = static_cast<const uint16_t*>(Q_S);
+    r.K = static_cast<const uint16_t*>(K);
+    r.items = reinterpret_cast<const br::ScoreItem*>(wsp + sp.off_items);
+    r.doc_offsets = reinterpret_cast<const int32_t*>(wsp + sp.off_doc_offsets);
+    r.prompt_base = reinterpret_cast<const int32_t*>(wsp + sp.off_prompt_base);
+    r.ml = reinterpret_cast<float2*>(ws + L.score_ml);
+    r.scores = scores;
+    r.head_scores = head_scores;
+    r.n_items = int64_t(sp.items.size());
+    r.num_prompts = B;
+    r.num_q_heads = dims->num_q_heads;
+    r.num_kv_heads = dims->num_kv_heads;
+    r.head_dim = dims->head_dim;
+    r.n_signal = n_signal;
+    r.row_blocks = sp.row_blocks;
+    r.n_docs = sp.n_docs;
+    r.scale_log2 = a.scale_log2;
+    he = br::launch_doc_scores(r, stream);
+    if (he != hipSuccess) return hip_fail(he, "doc score kernel launch");
+    he = br::launch_sort_docs(scores, base.data(), B, order, stream);
+    if (he != hipSuccess) return hip_fail(he, "sort kernel launch");
+    return BR_OK;
+  });
+}
+
+br_status br_rank_prompts(const br_dims* dims, const void* Q, const void* K, const void* V, const void* Q_S,
+                          int32_t n_signal, const int32_t* segment_offsets, const int32_t* seg_ptr,
+                          const int32_t* doc_offsets, const int32_t* doc_ptr, void* out, float* lse, float* scores,
+                          float* head_scores, int32_t* order, float softmax_scale, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  return br_rank_prompts_timed(dims, Q, K, V, Q_S, n_signal, segment_offsets, seg_ptr, doc_offsets, doc_ptr, out,
+                               lse, scores, head_scores, order, softmax_scale, workspace, workspace_bytes, stream,
+                               nullptr, nullptr);
+}
+
+}  // extern "C"

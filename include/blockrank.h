@@ -171,6 +171,29 @@ br_status br_attn_routed_fwd(const br_dims* dims, const void* Q, const void* K, 
                              hipStream_t stream);
 
 /*
+ * The whole hot path in one call: br_attn_fwd, br_doc_scores and br_sort_docs on the same
+ * inputs, with both work plans uploaded in one copy.  Arguments, layouts and rules as in those
+ * three calls (softmax_scale serves the attention and the readout); outputs are bit-identical to
+ * theirs.  workspace: >= br_rank_workspace_bytes(), 16-byte aligned.  br_rank_prompts_timed
+ * also records kernel_start / kernel_stop (hipEvent_t, may be NULL) on `stream` immediately
+ * around the attention kernel.
+ */
+br_status br_rank_workspace_bytes(const br_dims* dims, const int32_t* segment_offsets, const int32_t* seg_ptr,
+                                  int32_t n_signal, const int32_t* doc_offsets, const int32_t* doc_ptr,
+                                  size_t* bytes);
+br_status br_rank_prompts(const br_dims* dims, const void* Q, const void* K, const void* V, const void* Q_S,
+                          int32_t n_signal, const int32_t* segment_offsets, const int32_t* seg_ptr,
+                          const int32_t* doc_offsets, const int32_t* doc_ptr, void* out, float* lse,
+                          float* scores, float* head_scores, int32_t* order, float softmax_scale,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+br_status br_rank_prompts_timed(const br_dims* dims, const void* Q, const void* K, const void* V,
+                                const void* Q_S, int32_t n_signal, const int32_t* segment_offsets,
+                                const int32_t* seg_ptr, const int32_t* doc_offsets, const int32_t* doc_ptr,
+                                void* out, float* lse, float* scores, float* head_scores, int32_t* order,
+                                float softmax_scale, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream, hipEvent_t kernel_start, hipEvent_t kernel_stop);
+
+/*
  * Query-only attention over a cached corpus ("prefill once, score many queries"; BlockSearch,
  * section 3.2: the query block attends over the full corpus and causally to itself).
  * The key/value token axis holds the corpus [0, corpus_len) (e.g. an instruction and its

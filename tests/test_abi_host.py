@@ -425,3 +425,34 @@ def test_attn_bwd_rejects_before_any_hip_call():
     assert call(*args(sp=p([0, 5, 3]))) == INV                        # bad segment table
     bad = br.make_dims(2, 8, 3, 64, int(seg[-1]))                     # Hq not a multiple of Hkv
     assert lib.br_attn_bwd(ctypes.byref(bad), *args()) == INV
+
+
+def test_rank_workspace_and_rejects_before_any_hip_call():
+    lib = br.load_library()
+    seg, sp, dof, dptr = workloads.segment_tables([(8, [16, 12, 20], 8), (4, [10, 10], 6)])
+    dims = br.make_dims(2, 8, 2, 64, int(seg[-1]))
+    need = br.rank_workspace_bytes(dims, seg, sp, 4, dof, dptr)
+    assert need >= br.attn_workspace_bytes(dims, seg, sp) + br.doc_scores_workspace_bytes(dims, 4, dof, dptr) - 4096
+    p = lambda a: np.ascontiguousarray(a, dtype=np.int32).ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    f = _fake()
+    INV, WS, UNS = br._lib.BR_ERR_INVALID_ARG, br._lib.BR_ERR_WORKSPACE, br._lib.BR_ERR_UNSUPPORTED
+    def call(**kw):
+        a = dict(Q=f, K=f, V=f, QS=f, S=4, so=p(seg), sp=p(sp), do=p(dof), dp=p(dptr), out=f, lse=None, sc=f, hs=None,
+                 order=f, scale=0.0, ws=f, n=need)
+        a.update(kw)
+        return lib.br_rank_prompts(ctypes.byref(dims), a["Q"], a["K"], a["V"], a["QS"], a["S"], a["so"], a["sp"],
+                                   a["do"], a["dp"], a["out"], a["lse"], a["sc"], a["hs"], a["order"], a["scale"],
+                                   a["ws"], a["n"], None)
+    assert call(n=need - 1) == WS
+    assert call(QS=None) == INV
+    assert call(order=None) == INV
+    assert call(S=0) == INV                    # no signal rows
+    assert call(scale=float("nan")) == INV
+    big = workloads.segment_tables([(2, [1] * 8193, 2)])
+    dims2 = br.make_dims(1, 8, 2, 64, int(big[0][-1]))
+    nb = ctypes.c_size_t(0)
+    assert lib.br_rank_workspace_bytes(ctypes.byref(dims2), p(big[0]), p(big[1]), 1, p(big[2]), p(big[3]),
+                                       ctypes.byref(nb)) == 0
+    rc = lib.br_rank_prompts(ctypes.byref(dims2), f, f, f, f, 1, p(big[0]), p(big[1]), p(big[2]), p(big[3]), f, None,
+                             f, None, f, 0.0, f, nb.value, None)
+    assert rc == UNS                           # more documents than the sort takes

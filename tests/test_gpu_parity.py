@@ -147,3 +147,22 @@ def test_bitwise_determinism():
         r.append((out.view(torch.int16).cpu().numpy(), lse.cpu().numpy(), s.cpu().numpy(), o.cpu().numpy()))
     for a, b in zip(r[0], r[1]):
         np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("config", ["worked", "batched", "ragged"])
+def test_rank_step_matches_separate_calls(config):
+    """br_rank_prompts (one call, one plan upload) gives bit-identical attention output, lse, scores,
+    head scores and order to br_attn_fwd + br_doc_scores + br_sort_docs."""
+    w = workloads.make(config, 0)
+    dev = upload(w)
+    log(f"[gpu] fused rank step vs separate calls: {config}")
+    a_out, a_lse = br.attn_fwd(dev["Q"], dev["K"], dev["V"], w.segment_offsets, w.seg_ptr, lse=True)
+    a_s, a_hs = br.doc_scores(dev["Q_S"], dev["K"], w.doc_offsets, w.doc_ptr, head_scores=True)
+    a_o = br.sort_docs(a_s, w.doc_ptr)
+    hs = torch.empty_like(a_hs)
+    lse = torch.empty_like(a_lse)
+    out, s, o = br.rank_step(dev["Q"], dev["K"], dev["V"], dev["Q_S"], w.segment_offsets, w.seg_ptr, w.doc_offsets,
+                             w.doc_ptr, lse=lse, head_scores=hs)
+    torch.cuda.synchronize()
+    assert torch.equal(out, a_out) and torch.equal(lse, a_lse)
+    assert torch.equal(s, a_s) and torch.equal(hs, a_hs) and torch.equal(o, a_o)
