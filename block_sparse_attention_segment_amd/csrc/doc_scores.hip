@@ -20,7 +20,7 @@
 namespace br {
 
 template <int D>
-__global__ __launch_bounds__(256) void doc_partial_kernel(const uint16_t* __restrict__ Q_S,
+__global__ __launch_bounds__(256, 4) void doc_partial_kernel(const uint16_t* __restrict__ Q_S,
                                                           const uint16_t* __restrict__ K,
                                                           const ScoreItem* __restrict__ items,
                                                           const int32_t* __restrict__ dof, float2* __restrict__ ml,
@@ -64,10 +64,14 @@ __global__ __launch_bounds__(256) void doc_partial_kernel(const uint16_t* __rest
     for (int s = 0; s < DSTEPS; ++s)
       kr[s] = buf_load16(r, uint32_t(((KRI * s + lane / KCH) * kv_stride + 8 * (lane % KCH)) * 2));
   };
-  auto to_frags = [&](const u32x4_t* kr, u32x4_t* kf) {
+  // One register set of raw rows: they go to LDS before the next block's loads reuse them, so
+  // the wave holds raw rows, fragments and Q (about 112 registers) and four waves share a SIMD.
+  auto stage = [&](const u32x4_t* kr) {
 #pragma unroll
     for (int s = 0; s < DSTEPS; ++s)
       *reinterpret_cast<u32x4_t*>(&kst[(KRI * s + lane / KCH) * KROW + 8 * (lane % KCH)]) = kr[s];
+  };
+  auto read_frags = [&](u32x4_t* kf) {
 #pragma unroll
     for (int s = 0; s < DSTEPS; ++s) kf[s] = load16(&kst[n * KROW + 16 * s + 8 * half]);
   };
@@ -75,18 +79,19 @@ __global__ __launch_bounds__(256) void doc_partial_kernel(const uint16_t* __rest
   int d = it.d0;
   int a = dof[d], e = dof[d + 1];
   int t0 = a;
-  u32x4_t kcur[DSTEPS], knext[DSTEPS], kf[DSTEPS];
-  load_rows(t0, e, kcur);
+  u32x4_t kraw[DSTEPS], kf[DSTEPS];
+  load_rows(t0, e, kraw);
   float m_run = -INFINITY, e_run = 0.f;
   while (true) {
+    stage(kraw);
     int nd = d, nt0 = t0 + 32, ne = e;
     if (nt0 >= e) {
       nd = d + 1;
       if (nd < it.d1) { nt0 = dof[nd]; ne = dof[nd + 1]; }
     }
     const bool has_next = nd < it.d1;
-    if (has_next) load_rows(nt0, ne, knext);
-    to_frags(kcur, kf);
+    if (has_next) load_rows(nt0, ne, kraw);
+    read_frags(kf);
 
     f32x16_t s = f32x16_t{};
 #pragma unroll
@@ -118,8 +123,6 @@ __global__ __launch_bounds__(256) void doc_partial_kernel(const uint16_t* __rest
       e_run = 0.f;
     }
     if (!has_next) break;
-#pragma unroll
-    for (int st = 0; st < DSTEPS; ++st) kcur[st] = knext[st];
     d = nd; t0 = nt0; e = ne;
   }
 }
