@@ -41,8 +41,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __r
   constexpr int DSTEPS = D / 16, DBLK = D / 32, KCH = D / 8;
   constexpr int RPP = 256 / KCH;             // key rows per load pass
   constexpr int KPASS = BN / RPP;
-  __shared__ __align__(16) uint16_t sk[BN * VROW];
-  __shared__ __align__(16) uint16_t sv[BN * KROW];
+  // Two K/V tile buffers: tile i is read from buffer i % 2 while tile i + 1 is written to the
+  // other, so one barrier per tile suffices.
+  __shared__ __align__(16) uint16_t sk[2][BN * VROW];
+  __shared__ __align__(16) uint16_t sv[2][BN * KROW];
 
   const int g = blockIdx.x % Hkv;
   const AttnItem it = items[blockIdx.x / Hkv];
@@ -99,12 +101,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __r
       vreg[p] = buf_load16(rv, k_off + p * RPP * kv_stride * 2);
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < KPASS; ++p) {
       const int r = kr0 + p * RPP;
-      *reinterpret_cast<u32x4_t*>(&sk[r * VROW + 8 * kcc]) = kreg[p];
-      *reinterpret_cast<u32x4_t*>(&sv[r * KROW + 8 * kcc]) = vreg[p];
+      *reinterpret_cast<u32x4_t*>(&sk[buf][r * VROW + 8 * kcc]) = kreg[p];
+      *reinterpret_cast<u32x4_t*>(&sv[buf][r * KROW + 8 * kcc]) = vreg[p];
     }
   };
   // K^T fragments for dQ^T += K^T dS^T: the forward's V^T read pattern on the K tile.
@@ -120,11 +122,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __r
   f32x16_t acc[DBLK];
 #pragma unroll
   for (int b = 0; b < DBLK; ++b) acc[b] = f32x16_t{};
-  if (nt > 0) load_tile(t_start(0), t_end(0));
+  if (nt > 0) {
+    load_tile(t_start(0), t_end(0));
+    store_tile(0);
+  }
+  __syncthreads();
   for (int i = 0; i < nt; ++i) {
-    __syncthreads();  // the previous tile's reads are done
-    store_tile();
-    __syncthreads();
+    const int buf = i & 1;
     if (i + 1 < nt) load_tile(t_start(i + 1), t_end(i + 1));
     const int start = t_start(i), end = t_end(i);
     const bool causal = i >= nA;
@@ -134,8 +138,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __r
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-      const uint16_t* kp = &sk[(kb * 32 + n) * VROW + 8 * half];
-      const uint16_t* vp = &sv[(kb * 32 + n) * KROW + 8 * half];
+      const uint16_t* kp = &sk[buf][(kb * 32 + n) * VROW + 8 * half];
+      const uint16_t* vp = &sv[buf][(kb * 32 + n) * KROW + 8 * half];
 #pragma unroll
       for (int st = 0; st < DSTEPS; ++st) {
         s = mfma32(load16(kp + 16 * st), qf[st], s);
@@ -153,7 +157,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __r
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const u32x4_t pv = {pk[4 * m], pk[4 * m + 1], pk[4 * m + 2], pk[4 * m + 3]};
-        const uint16_t* kq = &sk[k_lane + (32 * kb + 16 * m) * VROW];
+        const uint16_t* kq = &sk[buf][k_lane + (32 * kb + 16 * m) * VROW];
 #pragma unroll
         for (int b = 0; b < DBLK; ++b) {
           const u32x2_t lo = lds_read_tr16(kq + 32 * b), hi = lds_read_tr16(kq + 8 * VROW + 32 * b);
@@ -161,6 +165,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __r
         }
       }
     }
+    // The other buffer was last read in the previous tile, before the barrier that ended it.
+    if (i + 1 < nt) store_tile(buf ^ 1);
+    __syncthreads();
   }
   // acc[b] register r holds head-dim element 32 b + 8 (r / 4) + 4 half + r % 4 of this lane's row.
   if (it.slot < 0) {
