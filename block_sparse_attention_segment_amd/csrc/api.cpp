@@ -1025,6 +1025,7 @@ br_status br_rank_prompts_timed(const br_dims* dims, const void* Q, const void* 
     a.q_row_base = 0;
     a.ev_start = kernel_start;
     a.ev_stop = kernel_stop;
+    a.defer_merge = true;  // merged in the launch of the readout's partial kernel below
     he = br::launch_attn(a, stream);
     if (he != hipSuccess) return hip_fail(he, "attention kernel launch");
 
@@ -1047,8 +1048,8 @@ br_status br_rank_prompts_timed(const br_dims* dims, const void* Q, const void* 
     r.row_blocks = sp.row_blocks;
     r.n_docs = sp.n_docs;
     r.scale_log2 = a.scale_log2;
-    he = br::launch_doc_scores(r, stream);
-    if (he != hipSuccess) return hip_fail(he, "doc score kernel launch");
+    he = br::launch_merge_doc_scores(a, r, stream);
+    if (he != hipSuccess) return hip_fail(he, "merge and doc score kernel launch");
     he = br::launch_sort_docs(scores, base.data(), B, order, stream);
     if (he != hipSuccess) return hip_fail(he, "sort kernel launch");
     return BR_OK;

@@ -34,6 +34,7 @@
 // Q rows (loaded once the last tile's S^T is formed) into MFMA fragments through its own 32
 // rows of that buffer, then this item's normalised output rows the other way.  Query rows of long prompts are split over key
 // chunks; their fp32 partials (m, l, o) are combined by attn_merge_kernel.
+#include "attn_merge.h"
 #include "device_common.h"
 #include "launch.h"
 #include "plan.h"
@@ -368,63 +369,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
   }
 }
 
-// Combine split-key partials of one query tile: M = max m_c, L = sum l_c 2^(m_c - M),
-// o = sum o_c 2^(m_c - M) / L, accumulated in one pass with a running maximum.  One thread
-// per (row, 4 head-dim elements); a workgroup covers 256 such units, so one (query tile, KV
-// head) spreads over 128 * D / 4 / 256 workgroups.  Chunks are visited eight at a time so
-// their loads are in flight together; the order of the sums is fixed, so the result is
-// deterministic.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(uint16_t* __restrict__ O, float* __restrict__ lse,
                                                          const MergeItem* __restrict__ merges,
                                                          const float* __restrict__ part_o,
                                                          const float* __restrict__ part_ml, int Hq, int Hkv, int G,
                                                          int q_row_base) {
-  constexpr int CH = D / 4;                          // 4-element units per row
-  constexpr int WG_PER_TILE = kRowsPerTile * CH / 256;
-  const int tile = blockIdx.x / WG_PER_TILE, part = blockIdx.x % WG_PER_TILE;
-  const int g = tile % Hkv;
-  const MergeItem mi = merges[tile / Hkv];
-  const int unit = part * 256 + threadIdx.x;
-  const int rho = unit / CH, ch = unit % CH;
-  const int TM = kRowsPerTile / G;
-  const int tok = mi.row0 + rho % TM, h = g * G + rho / TM;
-  if (tok >= mi.row_limit) return;
-  const int64_t stride = int64_t(Hkv) * kRowsPerTile;  // rows between consecutive slots
-  const int64_t row = (int64_t(mi.slot0) * Hkv + g) * kRowsPerTile + rho;
-  const float2* ml = reinterpret_cast<const float2*>(part_ml);
-  const int n = mi.nslots;
-  // One pass with a running maximum: chunk c scales the state by 2^(M - M') and adds its own
-  // partials with weight 2^(m_c - M').  Eight chunks' loads are issued together per round.
-  float M = -INFINITY, L = 0.f;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  auto add = [&](float2 v, f32x4_t o) {
-    const float Mn = fmaxf(M, v.x);
-    if (Mn == -INFINITY) return;  // nothing seen yet
-    const float a = fast_exp2(M - Mn), wgt = fast_exp2(v.x - Mn);
-    L = L * a + v.y * wgt;
-    acc = acc * a + wgt * o;
-    M = Mn;
-  };
-  constexpr int U = 8;
-  int c = 0;
-  for (; c + U <= n; c += U) {
-    float2 v[U];
-    f32x4_t o[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      v[u] = ml[row + (c + u) * stride];
-      o[u] = *reinterpret_cast<const f32x4_t*>(part_o + (row + (c + u) * stride) * D + ch * 4);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) add(v[u], o[u]);
-  }
-  for (; c < n; ++c)
-    add(ml[row + c * stride], *reinterpret_cast<const f32x4_t*>(part_o + (row + c * stride) * D + ch * 4));
-  const float inv = 1.f / L;
-  const u32x2_t v = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
-  *reinterpret_cast<u32x2_t*>(O + (int64_t(tok - q_row_base) * Hq + h) * D + ch * 4) = v;
-  if (lse && ch == 0) lse[int64_t(tok - q_row_base) * Hq + h] = (M + __log2f(L)) * kLn2;
+  attn_merge_block<D>(blockIdx.x, O, lse, merges, part_o, part_ml, Hq, Hkv, G, q_row_base);
 }
 
 template <int D, int G>
@@ -444,8 +395,8 @@ static hipError_t launch_attn_t(const AttnLaunch& a, hipStream_t stream) {
       if (e != hipSuccess) return e;
     }
   }
-  if (a.n_merges > 0) {
-    const dim3 grid(unsigned(a.n_merges * a.num_kv_heads * (kRowsPerTile * (D / 4) / 256)));
+  if (a.n_merges > 0 && !a.defer_merge) {
+    const dim3 grid(unsigned(a.n_merges * a.num_kv_heads * merge_wg_per_tile<D>()));
     attn_merge_kernel<D><<<grid, 256, 0, stream>>>(a.O, a.lse, a.merges, a.part_o, a.part_ml, a.num_q_heads,
                                                    a.num_kv_heads, G, a.q_row_base);
     return hipGetLastError();

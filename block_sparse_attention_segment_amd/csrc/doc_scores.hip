@@ -13,6 +13,7 @@
 //   2. doc_rowstat_kernel: per row, M = max_k m_k and Z = sum_k e_k 2^(m_k - M).
 //   3. doc_final_kernel: one workgroup per document, head_scores[h,k] = sum_i e_k 2^(m_k - M)/Z
 //      and s_k = mean over heads, summed in a fixed order (deterministic).
+#include "attn_merge.h"
 #include "device_common.h"
 #include "launch.h"
 #include "plan.h"
@@ -20,15 +21,14 @@
 namespace br {
 
 template <int D>
-__global__ __launch_bounds__(256, 4) void doc_partial_kernel(const uint16_t* __restrict__ Q_S,
-                                                          const uint16_t* __restrict__ K,
-                                                          const ScoreItem* __restrict__ items,
-                                                          const int32_t* __restrict__ dof, float2* __restrict__ ml,
-                                                          int64_t n_items, int Hq, int Hkv, int n_signal,
-                                                          int row_blocks, float scale_log2) {
+__device__ __forceinline__ void doc_partial_block(int64_t block, const uint16_t* __restrict__ Q_S,
+                                                  const uint16_t* __restrict__ K, const ScoreItem* __restrict__ items,
+                                                  const int32_t* __restrict__ dof, float2* __restrict__ ml,
+                                                  int64_t n_items, int Hq, int Hkv, int n_signal, int row_blocks,
+                                                  float scale_log2) {
   constexpr int DSTEPS = D / 16;
   const int lane = threadIdx.x & 63, n = lane & 31, half = lane >> 5;
-  const int64_t wid = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t wid = block * 4 + (threadIdx.x >> 6);
   if (wid >= n_items * Hkv * row_blocks) return;  // whole wave exits together
   const int g = int(wid % Hkv);
   const int64_t rest = wid / Hkv;
@@ -127,6 +127,33 @@ __global__ __launch_bounds__(256, 4) void doc_partial_kernel(const uint16_t* __r
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(256, 4) void doc_partial_kernel(const uint16_t* __restrict__ Q_S,
+                                                          const uint16_t* __restrict__ K,
+                                                          const ScoreItem* __restrict__ items,
+                                                          const int32_t* __restrict__ dof, float2* __restrict__ ml,
+                                                          int64_t n_items, int Hq, int Hkv, int n_signal,
+                                                          int row_blocks, float scale_log2) {
+  doc_partial_block<D>(blockIdx.x, Q_S, K, items, dof, ml, n_items, Hq, Hkv, n_signal, row_blocks, scale_log2);
+}
+
+// The attention's split-key merge (workgroups [0, merge_blocks)) and the readout's partials (the
+// rest) in one launch: both only read what earlier launches wrote, and neither reads the other's
+// output.
+template <int D>
+__global__ __launch_bounds__(256, 4) void merge_doc_partial_kernel(
+    int merge_blocks, uint16_t* __restrict__ O, float* __restrict__ lse, const MergeItem* __restrict__ merges,
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, int G, int q_row_base,
+    const uint16_t* __restrict__ Q_S, const uint16_t* __restrict__ K, const ScoreItem* __restrict__ items,
+    const int32_t* __restrict__ dof, float2* __restrict__ ml, int64_t n_items, int Hq, int Hkv, int n_signal,
+    int row_blocks, float scale_log2) {
+  if (int(blockIdx.x) < merge_blocks)
+    attn_merge_block<D>(blockIdx.x, O, lse, merges, part_o, part_ml, Hq, Hkv, G, q_row_base);
+  else
+    doc_partial_block<D>(int64_t(blockIdx.x) - merge_blocks, Q_S, K, items, dof, ml, n_items, Hq, Hkv, n_signal,
+                         row_blocks, scale_log2);
+}
+
 // rowstat[b * RT + r] = (M, 1/Z) for row r = i*Hq + h of prompt b, with M = max_k m_k and
 // Z = sum_k e_k 2^(m_k - M).  A workgroup covers 4 rows x 64 document lanes; each lane keeps an
 // online (max, sum) over its documents, and the 64 lanes of a row are combined in a fixed order.
@@ -196,20 +223,39 @@ __global__ __launch_bounds__(256) void doc_final_kernel(const float2* __restrict
   }
 }
 
-hipError_t launch_doc_stats(const ScoreLaunch& a, hipStream_t stream) {
-  const int64_t waves = a.n_items * a.num_kv_heads * a.row_blocks;
-  const dim3 grid(unsigned((waves + 3) / 4));
+// Workgroups of the readout's partial kernel (four waves each).
+static int64_t doc_partial_blocks(const ScoreLaunch& a) {
+  return (a.n_items * a.num_kv_heads * a.row_blocks + 3) / 4;
+}
+
+template <int D>
+static hipError_t launch_merge_doc_partial_t(const AttnLaunch* m, const ScoreLaunch& a, hipStream_t stream) {
+  const int merge_blocks = m ? int(m->n_merges * m->num_kv_heads * merge_wg_per_tile<D>()) : 0;
+  const dim3 grid(unsigned(merge_blocks + doc_partial_blocks(a)));
+  if (merge_blocks == 0) {
+    doc_partial_kernel<D><<<grid, 256, 0, stream>>>(a.Q_S, a.K, a.items, a.doc_offsets, a.ml, a.n_items, a.num_q_heads,
+                                                    a.num_kv_heads, a.n_signal, a.row_blocks, a.scale_log2);
+  } else {
+    merge_doc_partial_kernel<D><<<grid, 256, 0, stream>>>(
+        merge_blocks, m->O, m->lse, m->merges, m->part_o, m->part_ml, m->num_q_heads / m->num_kv_heads,
+        m->q_row_base, a.Q_S, a.K, a.items, a.doc_offsets, a.ml, a.n_items, a.num_q_heads, a.num_kv_heads,
+        a.n_signal, a.row_blocks, a.scale_log2);
+  }
+  return hipGetLastError();
+}
+
+// The readout's partials (with the attention's deferred merge when `m` is given), then its row
+// statistics.
+static hipError_t launch_stats(const AttnLaunch* m, const ScoreLaunch& a, hipStream_t stream) {
+  if (m && (m->head_dim != a.head_dim || m->num_q_heads != a.num_q_heads || m->num_kv_heads != a.num_kv_heads))
+    return hipErrorInvalidValue;
+  hipError_t e;
   if (a.head_dim == 128)
-    doc_partial_kernel<128><<<grid, 256, 0, stream>>>(a.Q_S, a.K, a.items, a.doc_offsets, a.ml, a.n_items,
-                                                      a.num_q_heads, a.num_kv_heads, a.n_signal, a.row_blocks,
-                                                      a.scale_log2);
+    e = launch_merge_doc_partial_t<128>(m, a, stream);
   else if (a.head_dim == 64)
-    doc_partial_kernel<64><<<grid, 256, 0, stream>>>(a.Q_S, a.K, a.items, a.doc_offsets, a.ml, a.n_items,
-                                                     a.num_q_heads, a.num_kv_heads, a.n_signal, a.row_blocks,
-                                                     a.scale_log2);
+    e = launch_merge_doc_partial_t<64>(m, a, stream);
   else
     return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int RT = a.n_signal * a.num_q_heads;
   const int row_groups = (RT + kStatRows - 1) / kStatRows;
@@ -219,14 +265,26 @@ hipError_t launch_doc_stats(const ScoreLaunch& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_doc_scores(const ScoreLaunch& a, hipStream_t stream) {
-  hipError_t e = launch_doc_stats(a, stream);
-  if (e != hipSuccess) return e;
+hipError_t launch_doc_stats(const ScoreLaunch& a, hipStream_t stream) { return launch_stats(nullptr, a, stream); }
+
+static hipError_t launch_final(const ScoreLaunch& a, hipStream_t stream) {
   const int RT = a.n_signal * a.num_q_heads;
   const float2* rowstat = a.ml + int64_t(a.n_docs) * RT;
   doc_final_kernel<<<dim3(unsigned(a.n_docs)), 256, 0, stream>>>(
       a.ml, rowstat, a.prompt_base, a.scores, a.head_scores, a.num_prompts, a.n_signal, a.num_q_heads, a.n_docs);
   return hipGetLastError();
+}
+
+hipError_t launch_merge_doc_scores(const AttnLaunch& attn, const ScoreLaunch& a, hipStream_t stream) {
+  hipError_t e = launch_stats(&attn, a, stream);
+  if (e != hipSuccess) return e;
+  return launch_final(a, stream);
+}
+
+hipError_t launch_doc_scores(const ScoreLaunch& a, hipStream_t stream) {
+  hipError_t e = launch_doc_stats(a, stream);
+  if (e != hipSuccess) return e;
+  return launch_final(a, stream);
 }
 
 }  // namespace br

@@ -25,6 +25,7 @@ struct AttnLaunch {
   float scale_log2;         // softmax scale * log2(e)
   int q_row_base = 0;       // token index of Q/O/lse row 0 (the corpus length for query-only runs)
   hipEvent_t ev_start = nullptr, ev_stop = nullptr;  // optional, recorded around the main kernel
+  bool defer_merge = false;  // leave the split-key merge to launch_merge_doc_scores
 };
 hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream);
 
@@ -44,6 +45,9 @@ struct ScoreLaunch {
 hipError_t launch_doc_scores(const ScoreLaunch& a, hipStream_t stream);
 // The readout's per-document (m_k, e_k) and per-row (M, 1/Z) only (rowstat at ml + n_docs * RT).
 hipError_t launch_doc_stats(const ScoreLaunch& a, hipStream_t stream);
+// The readout with the attention's deferred split-key merge (launch_attn with defer_merge) in the
+// launch of its partial kernel; same results as launch_attn followed by launch_doc_scores.
+hipError_t launch_merge_doc_scores(const AttnLaunch& attn, const ScoreLaunch& a, hipStream_t stream);
 
 struct DocBwdLaunch {
   const uint16_t* Q_S;
