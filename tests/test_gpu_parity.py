@@ -149,11 +149,22 @@ def test_bitwise_determinism():
         np.testing.assert_array_equal(a, b)
 
 
-@pytest.mark.parametrize("config", ["worked", "batched", "ragged"])
+# Many short documents per prompt (two prompts of unequal size), and many query heads per KV head.
+RANK_CUSTOM = {
+    "many_docs": ([(16, [8] * 600, 16), (8, [3] * 40, 8)], dict(hq=8, hkv=2, d=64, n_signal=4)),
+    "wide_heads": ([(8, [4] * 300, 8)], dict(hq=64, hkv=8, d=64, n_signal=2)),
+}
+
+
+@pytest.mark.parametrize("config", ["worked", "batched", "ragged", "many_docs", "wide_heads"])
 def test_rank_step_matches_separate_calls(config):
     """br_rank_prompts (one call, one plan upload) gives bit-identical attention output, lse, scores,
     head scores and order to br_attn_fwd + br_doc_scores + br_sort_docs."""
-    w = workloads.make(config, 0)
+    if config in RANK_CUSTOM:
+        prompts, kw = RANK_CUSTOM[config]
+        w = workloads.make_custom(prompts, seed=3, **kw)
+    else:
+        w = workloads.make(config, 0)
     dev = upload(w)
     log(f"[gpu] fused rank step vs separate calls: {config}")
     a_out, a_lse = br.attn_fwd(dev["Q"], dev["K"], dev["V"], w.segment_offsets, w.seg_ptr, lse=True)
