@@ -41,12 +41,15 @@ __device__ __forceinline__ void attn_merge_block(int block, uint16_t* __restrict
   // partials with weight 2^(m_c - M').  Eight chunks' loads are issued together per round.
   float M = -INFINITY, L = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  // Explicit fused multiply-adds: the body is inlined into two kernels (the attention path's
+  // merge and the ranking step's merge with the readout), and must round the same in both.
   auto add = [&](float2 v, f32x4_t o) {
     const float Mn = fmaxf(M, v.x);
     if (Mn == -INFINITY) return;  // nothing seen yet
     const float a = fast_exp2(M - Mn), wgt = fast_exp2(v.x - Mn);
-    L = L * a + v.y * wgt;
-    acc = acc * a + wgt * o;
+    L = fmaf(v.y, wgt, L * a);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(wgt, o[e], acc[e] * a);
     M = Mn;
   };
   constexpr int U = 8;

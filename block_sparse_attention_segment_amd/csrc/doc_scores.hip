@@ -111,13 +111,13 @@ __device__ __forceinline__ void doc_partial_block(int64_t block, const uint16_t*
     float acc = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc += fast_exp2(fmaf(s[r], scale_log2, -mu));
-    e_run = e_run * fast_exp2(m_run - mu) + acc;
+    e_run = fmaf(e_run, fast_exp2(m_run - mu), acc);  // explicit: the body is inlined into two kernels
     m_run = m_new;
 
     if (t0 + 32 >= e) {  // document d is complete: combine the two halves and store (m_k, e_k)
       const float mo = other_half(m_run), eo = other_half(e_run);
       const float M = fmaxf(m_run, mo);
-      const float E = e_run * fast_exp2(m_run - M) + eo * fast_exp2(mo - M);
+      const float E = fmaf(e_run, fast_exp2(m_run - M), eo * fast_exp2(mo - M));
       if (row_ok && half == 0) ml[int64_t(it.score_base + (d - it.d0)) * RT + int64_t(i) * Hq + h] = float2{M, E};
       m_run = -INFINITY;
       e_run = 0.f;
