@@ -149,14 +149,16 @@ def test_bitwise_determinism():
         np.testing.assert_array_equal(a, b)
 
 
-# Many short documents per prompt (two prompts of unequal size), and many query heads per KV head.
+# Many short documents per prompt (two prompts of unequal size), many query heads per KV head, and
+# a prompt of more than a thousand documents.
 RANK_CUSTOM = {
     "many_docs": ([(16, [8] * 600, 16), (8, [3] * 40, 8)], dict(hq=8, hkv=2, d=64, n_signal=4)),
     "wide_heads": ([(8, [4] * 300, 8)], dict(hq=64, hkv=8, d=64, n_signal=2)),
+    "over_1024_docs": ([(4, [2] * 1100, 4), (4, [5] * 7, 4)], dict(hq=4, hkv=2, d=64, n_signal=2)),
 }
 
 
-@pytest.mark.parametrize("config", ["worked", "batched", "ragged", "many_docs", "wide_heads"])
+@pytest.mark.parametrize("config", ["worked", "batched", "ragged", "many_docs", "wide_heads", "over_1024_docs"])
 def test_rank_step_matches_separate_calls(config):
     """br_rank_prompts (one call, one plan upload) gives bit-identical attention output, lse, scores,
     head scores and order to br_attn_fwd + br_doc_scores + br_sort_docs."""
