@@ -440,7 +440,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="long", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--secondary", default="worked", help="extra config timed in the same run ('' for none)")
+    ap.add_argument("--secondary", default="worked,batched",
+                    help="extra configs timed in the same run, comma-separated ('' for none)")
     ap.add_argument("--query-only", type=int, default=1,
                     help="also time query-only attention over the long prompt's cached corpus, top-256 routed "
                          "attention, RoPE of Q and K, and the backward (0 to skip)")
@@ -507,13 +508,17 @@ def main():
                      "kernel": "attn_fwd_kernel", "bytes_per_launch": r["bytes_alg"],
                      "traffic_gbps": None if traffic is None else round(traffic / r["kernel_s"] / 1e9, 1)},
     }
-    if args.secondary and args.secondary != args.config:
-        r2 = measure(args.secondary, args.seed, args.steps, args.warmup, log)
+    for name in [s for s in args.secondary.split(",") if s and s != args.config]:
+        if name not in WORKLOAD_NAMES:
+            raise SystemExit(f"unknown secondary config {name!r}")
+        r2 = measure(name, args.seed, args.steps, args.warmup, log)
         s2 = r2["ms_step"] / 1e3
-        line["secondary"] = {"workload": WORKLOAD_NAMES[args.secondary], "ms_per_step": round(r2["ms_step"], 5),
-                             "prompts_per_s": round(r2["w"].num_prompts / s2, 2),
-                             "tflops_closed_form_pairs": round(r2["flop_blk"] / s2 / 1e12, 3),
-                             "attention_kernel_ms": round(r2["kernel_ms"], 5)}
+        entry = {"workload": WORKLOAD_NAMES[name], "ms_per_step": round(r2["ms_step"], 5),
+                 "prompts_per_s": round(r2["w"].num_prompts / s2, 2),
+                 "tflops_closed_form_pairs": round(r2["flop_blk"] / s2 / 1e12, 3),
+                 "attention_kernel_ms": round(r2["kernel_ms"], 5)}
+        # the first extra config keeps the key "secondary"; the others are keyed by name
+        line["secondary" if "secondary" not in line else name] = entry
     if args.query_only and args.config == "long":
         line["query_only"] = measure_query_only(w, 16, 32, args.steps, args.warmup, args.seed, log)
         line["routed"] = measure_routed(w, 256, args.steps, args.warmup, log)
