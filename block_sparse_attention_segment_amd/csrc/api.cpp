@@ -1109,14 +1109,14 @@ br_status br_rank_prompts_timed(const br_dims* dims, const void* Q, const void* 
     he = hipEventRecord(side->fork, stream);
     if (he == hipSuccess) he = hipStreamWaitEvent(side->stream, side->fork, 0);
     if (he != hipSuccess) return hip_fail(he, "readout fork");
+    he = br::launch_attn(a, stream);  // first: it takes every CU; the readout fills its tail
+    if (he != hipSuccess) return hip_fail(he, "attention kernel launch");
     he = br::launch_doc_scores(r, side->stream);
     if (he != hipSuccess) return hip_fail(he, "doc score kernel launch");
     he = br::launch_sort_docs(scores, base.data(), B, order, side->stream);
     if (he != hipSuccess) return hip_fail(he, "sort kernel launch");
     he = hipEventRecord(side->join, side->stream);
     if (he != hipSuccess) return hip_fail(he, "readout join");
-    he = br::launch_attn(a, stream);
-    if (he != hipSuccess) return hip_fail(he, "attention kernel launch");
     he = hipStreamWaitEvent(stream, side->join, 0);
     if (he != hipSuccess) return hip_fail(he, "readout join");
     return BR_OK;
