@@ -1085,7 +1085,14 @@ br_status br_rank_prompts_timed(const br_dims* dims, const void* Q, const void* 
     r.row_blocks = sp.row_blocks;
     r.n_docs = sp.n_docs;
     r.scale_log2 = a.scale_log2;
-    if (kernel_start || kernel_stop || dims->total_tokens < kSideStreamMinTokens) {
+    // The side stream, for large batches when the call is not timed (if it cannot be created, the
+    // step runs on the caller's stream alone).
+    SideStream* side = nullptr;
+    if (!kernel_start && !kernel_stop && dims->total_tokens >= kSideStreamMinTokens && side_stream(&side) != hipSuccess) {
+      side = nullptr;
+      (void)hipGetLastError();  // clear it, so the launches below do not report it
+    }
+    if (!side) {
       // Everything on the caller's stream, the split-key merge in the launch of the readout's
       // partial kernel: for short batches (the fork and join cost more than the overlap saves:
       // measured at 12,864 tokens) and when timed (the events around the attention kernel then
@@ -1102,9 +1109,6 @@ br_status br_rank_prompts_timed(const br_dims* dims, const void* Q, const void* 
     // The readout and rank read only the inputs: they run on the side stream, forked after the
     // plan upload, while the attention and its merge run on the caller's stream; the caller's
     // stream then waits for them.
-    SideStream* side = nullptr;
-    he = side_stream(&side);
-    if (he != hipSuccess) return hip_fail(he, "side stream creation");
     std::lock_guard<std::mutex> guard(side->lock);
     he = hipEventRecord(side->fork, stream);
     if (he == hipSuccess) he = hipStreamWaitEvent(side->stream, side->fork, 0);
