@@ -44,6 +44,10 @@ Error validate_dims(const br_dims* dims) {
   if (dims->head_dim <= 0) return fail(BR_ERR_INVALID_ARG, "head_dim must be positive (got %lld)", dims->head_dim);
   if (dims->head_dim != 64 && dims->head_dim != 128)
     return fail(BR_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %lld)", dims->head_dim);
+  // Kernels address a tile of up to 128 token rows of all query heads with 32-bit byte offsets.
+  if (int64_t(dims->num_q_heads) * dims->head_dim > kMaxHeadsTimesDim)
+    return fail(BR_ERR_UNSUPPORTED, "num_q_heads * head_dim = %lld exceeds %lld",
+                int64_t(dims->num_q_heads) * dims->head_dim, int64_t(kMaxHeadsTimesDim));
   if (dims->total_tokens < 1) return fail(BR_ERR_INVALID_ARG, "total_tokens must be >= 1 (got %lld)", dims->total_tokens);
   if (dims->total_tokens > (int64_t(1) << 30))
     return fail(BR_ERR_UNSUPPORTED, "total_tokens %lld exceeds 2^30", dims->total_tokens);

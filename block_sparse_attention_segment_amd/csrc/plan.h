@@ -18,6 +18,7 @@ constexpr int kRowsPerTile = kRowsPerWave * kWaves;  // 128 (token, head) rows p
 constexpr int kKeyTile = 64;                      // keys staged in LDS per step
 constexpr int kAttnWgPerCu = 2;                   // persistent attention workgroups per CU
 constexpr int kMaxAttnWgPerHead = 4096;           // bound on workgroups sharing one KV head
+constexpr int kMaxHeadsTimesDim = 65536;          // bound on num_q_heads * head_dim (512 heads at d = 128)
 
 inline int tokens_per_tile(int group) { return kRowsPerTile / group; }
 

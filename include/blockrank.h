@@ -45,7 +45,8 @@
  *   - Tensors are token-major and packed over all prompts ("THD"), bf16 = IEEE bfloat16
  *     bit patterns, contiguous, 16-byte aligned base pointers.
  *   - Supported: head_dim in {64, 128}; num_q_heads % num_kv_heads == 0 with
- *     G = num_q_heads / num_kv_heads in {1, 2, 4, 8}; query head h reads KV head h / G.
+ *     G = num_q_heads / num_kv_heads in {1, 2, 4, 8}; query head h reads KV head h / G;
+ *     num_q_heads * head_dim <= 65536 (512 query heads at d = 128); others: BR_ERR_UNSUPPORTED.
  */
 #ifndef BLOCKRANK_H
 #define BLOCKRANK_H

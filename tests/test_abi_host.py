@@ -164,7 +164,7 @@ def test_noncontiguous_prompts_rejected():
 
 
 @pytest.mark.parametrize("hq,hkv,d,status", [(4, 3, 64, 1), (16, 1, 64, 2), (4, 2, 96, 2), (4, 2, 0, 1),
-                                             (0, 1, 64, 1)])
+                                             (0, 1, 64, 1), (1024, 128, 128, 2), (2048, 256, 64, 2)])
 def test_bad_dims_rejected(hq, hkv, d, status):
     dims = br.make_dims(1, hq, hkv, d, 10)
     with pytest.raises(br.BlockRankError) as ei:
