@@ -179,3 +179,45 @@ def test_rank_step_matches_separate_calls(config):
     torch.cuda.synchronize()
     assert torch.equal(out, a_out) and torch.equal(lse, a_lse)
     assert torch.equal(s, a_s) and torch.equal(hs, a_hs) and torch.equal(o, a_o)
+
+
+def test_rank_step_side_stream_from_two_host_threads():
+    """Batches of 32,768 tokens or more run the readout on the library's side stream.  Two host
+    threads, each with its own stream, workspace and outputs, call the step at once, five times
+    each: every result equals the separate calls' bit for bit (the side stream's fork and join
+    events are shared, and a lock keeps the two threads' enqueues apart)."""
+    import threading
+    w = workloads.make_custom([(32, [150] * 110, 32), (32, [150] * 110, 32)], hq=8, hkv=2, d=64, n_signal=4,
+                              seed=5)
+    assert w.total_tokens >= 32768
+    dev = upload(w)
+    log(f"[gpu] side-stream rank step from two threads: T={w.total_tokens}")
+    a_out = br.attn_fwd(dev["Q"], dev["K"], dev["V"], w.segment_offsets, w.seg_ptr)
+    a_s = br.doc_scores(dev["Q_S"], dev["K"], w.doc_offsets, w.doc_ptr)
+    a_o = br.sort_docs(a_s, w.doc_ptr)
+    torch.cuda.synchronize()
+    results, errors = {}, []
+
+    def worker(tid):
+        try:
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                got = []
+                for _ in range(5):
+                    out, s, o = br.rank_step(dev["Q"], dev["K"], dev["V"], dev["Q_S"], w.segment_offsets,
+                                             w.seg_ptr, w.doc_offsets, w.doc_ptr, stream=stream)
+                    got.append((out, s, o))
+                stream.synchronize()
+            results[tid] = got
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for tid in range(2):
+        for out, s, o in results[tid]:
+            assert torch.equal(out, a_out) and torch.equal(s, a_s) and torch.equal(o, a_o)
