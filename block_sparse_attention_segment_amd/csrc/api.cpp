@@ -10,6 +10,8 @@
 #include <cmath>
 #include <cstring>
 #include <exception>
+#include <list>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -973,6 +975,69 @@ br_status check_sort_table(const int32_t* doc_ptr, int num_prompts, std::vector<
   return BR_OK;
 }
 
+
+// Ranking-step plans, validated and scheduled, with their upload image.  Serving repeats prompt
+// shapes (BlockRank pads documents to fixed chunk lengths), and planning costs about 0.15 ms per
+// call at 100K tokens, so the last few plans are kept and reused when a call's dimensions and
+// host tables equal an entry's element by element (and the device and its workgroup count
+// match).  Entries are immutable once inserted; a mutex guards the list.
+struct RankPlan {
+  int device = -1, workgroups = 0;
+  br_dims dims{};
+  int32_t n_signal = 0;
+  std::vector<int32_t> seg_ptr, seg, doc_ptr, doc;
+  br::AttnPlan ap;
+  br::ScorePlan sp;
+  std::vector<int32_t> base;
+  RankLayout L;
+  std::vector<unsigned char> host;  // the upload image
+};
+
+bool same_tables(const RankPlan& e, const br_dims& d, int32_t n_signal, const int32_t* so, const int32_t* sp,
+                 const int32_t* dof, const int32_t* dp) {
+  if (e.dims.num_prompts != d.num_prompts || e.dims.num_q_heads != d.num_q_heads ||
+      e.dims.num_kv_heads != d.num_kv_heads || e.dims.head_dim != d.head_dim ||
+      e.dims.total_tokens != d.total_tokens || e.n_signal != n_signal)
+    return false;
+  const size_t B = size_t(d.num_prompts);
+  // The pointer tables first: equal to a validated entry's, they bound what the arrays hold.
+  if (std::memcmp(e.seg_ptr.data(), sp, (B + 1) * sizeof(int32_t)) != 0) return false;
+  if (std::memcmp(e.doc_ptr.data(), dp, (B + 1) * sizeof(int32_t)) != 0) return false;
+  return std::memcmp(e.seg.data(), so, e.seg.size() * sizeof(int32_t)) == 0 &&
+         std::memcmp(e.doc.data(), dof, e.doc.size() * sizeof(int32_t)) == 0;
+}
+
+class RankPlanCache {
+ public:
+  std::shared_ptr<const RankPlan> find(const br_dims& d, int32_t n_signal, const int32_t* so, const int32_t* sp,
+                                       const int32_t* dof, const int32_t* dp) {
+    std::lock_guard<std::mutex> lock(mu_);
+    for (auto it = lru_.begin(); it != lru_.end(); ++it)
+      if (same_tables(**it, d, n_signal, so, sp, dof, dp)) {
+        auto hit = *it;
+        lru_.erase(it);
+        lru_.push_front(hit);
+        return hit;
+      }
+    return nullptr;
+  }
+  void insert(std::shared_ptr<const RankPlan> e) {
+    std::lock_guard<std::mutex> lock(mu_);
+    lru_.push_front(std::move(e));
+    while (lru_.size() > kEntries) lru_.pop_back();
+  }
+
+ private:
+  static constexpr size_t kEntries = 4;
+  std::mutex mu_;
+  std::list<std::shared_ptr<const RankPlan>> lru_;
+};
+
+RankPlanCache& rank_plans() {
+  static RankPlanCache* c = new RankPlanCache;  // kept until the process ends
+  return *c;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1009,36 +1074,67 @@ br_status br_rank_prompts_timed(const br_dims* dims, const void* Q, const void* 
     if (!Q_S || !scores || !order) return record(BR_ERR_INVALID_ARG, "Q_S, scores and order must be non-NULL");
     if (!aligned(Q_S, 16) || !aligned(scores, 4) || !aligned(order, 4) || (head_scores && !aligned(head_scores, 4)))
       return record(BR_ERR_INVALID_ARG, "Q_S must be 16-byte aligned; scores, head_scores and order 4-byte");
-    br::AttnPlan ap;
-    e = br::build_attn_plan(*dims, segment_offsets, seg_ptr, &ap);
-    if (!e.ok()) return record(e);
-    br::ScorePlan sp;
-    e = br::build_score_plan(*dims, n_signal, doc_offsets, doc_ptr, &sp);
-    if (!e.ok()) return record(e);
-    std::vector<int32_t> base;
-    st = check_sort_table(doc_ptr, dims->num_prompts, &base);
-    if (st != BR_OK) return st;
-    const RankLayout L = rank_layout(ap, sp);
-    if (!workspace || workspace_bytes < L.total)
+    // A cached plan for these exact tables (validated when it was made), else a new one.
+    const bool tables = segment_offsets && seg_ptr && doc_offsets && doc_ptr;
+    std::shared_ptr<const RankPlan> plan =
+        tables ? rank_plans().find(*dims, n_signal, segment_offsets, seg_ptr, doc_offsets, doc_ptr) : nullptr;
+    std::shared_ptr<RankPlan> fresh;
+    if (!plan) {
+      fresh = std::make_shared<RankPlan>();
+      e = br::build_attn_plan(*dims, segment_offsets, seg_ptr, &fresh->ap);
+      if (!e.ok()) return record(e);
+      e = br::build_score_plan(*dims, n_signal, doc_offsets, doc_ptr, &fresh->sp);
+      if (!e.ok()) return record(e);
+      st = check_sort_table(doc_ptr, dims->num_prompts, &fresh->base);
+      if (st != BR_OK) return st;
+      fresh->L = rank_layout(fresh->ap, fresh->sp);
+    }
+    const RankLayout& L0 = plan ? plan->L : fresh->L;
+    if (!workspace || workspace_bytes < L0.total)
       return record(BR_ERR_WORKSPACE, "workspace is NULL or smaller than br_rank_workspace_bytes() = " +
-                                          std::to_string(L.total));
+                                          std::to_string(L0.total));
     if (!aligned(workspace, 16)) return record(BR_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-    int workgroups = 0;
+    int workgroups = 0, device = 0;
     hipError_t he = attn_workgroups(&workgroups);
+    if (he == hipSuccess) he = hipGetDevice(&device);
     if (he != hipSuccess) return hip_fail(he, "device query");
-    br::schedule_attn_plan(dims->num_kv_heads, workgroups, &ap);
-
-    // One host image for both plans, one copy.
     const int B = dims->num_prompts;
-    std::vector<unsigned char> host(L.score_plan + sp.off_ml, 0);
-    std::memcpy(host.data() + ap.off_items, ap.sched.data(), ap.sched.size() * sizeof(br::AttnItem));
-    std::memcpy(host.data() + ap.off_ranges, ap.ranges.data(), ap.ranges.size() * sizeof(int32_t));
-    if (!ap.merges.empty())
-      std::memcpy(host.data() + ap.off_merges, ap.merges.data(), ap.merges.size() * sizeof(br::MergeItem));
-    unsigned char* hs = host.data() + L.score_plan;
-    std::memcpy(hs + sp.off_items, sp.items.data(), sp.items.size() * sizeof(br::ScoreItem));
-    std::memcpy(hs + sp.off_doc_offsets, doc_offsets, size_t(doc_ptr[B]) * sizeof(int32_t));
-    std::memcpy(hs + sp.off_prompt_base, sp.prompt_score_base.data(), size_t(B + 1) * sizeof(int32_t));
+    if (plan && (plan->workgroups != workgroups || plan->device != device)) {
+      fresh = std::make_shared<RankPlan>(*plan);  // same tables, another device: reschedule
+      plan = nullptr;
+    }
+    if (!plan) {
+      RankPlan& P = *fresh;
+      br::schedule_attn_plan(dims->num_kv_heads, workgroups, &P.ap);
+      P.device = device;
+      P.workgroups = workgroups;
+      P.dims = *dims;
+      P.n_signal = n_signal;
+      P.seg_ptr.assign(seg_ptr, seg_ptr + B + 1);
+      P.seg.assign(segment_offsets, segment_offsets + seg_ptr[B]);
+      P.doc_ptr.assign(doc_ptr, doc_ptr + B + 1);
+      P.doc.assign(doc_offsets, doc_offsets + doc_ptr[B]);
+      // One host image for both plans, one copy.
+      const br::AttnPlan& ap = P.ap;
+      const br::ScorePlan& sp = P.sp;
+      P.host.assign(P.L.score_plan + sp.off_ml, 0);
+      unsigned char* h = P.host.data();
+      std::memcpy(h + ap.off_items, ap.sched.data(), ap.sched.size() * sizeof(br::AttnItem));
+      std::memcpy(h + ap.off_ranges, ap.ranges.data(), ap.ranges.size() * sizeof(int32_t));
+      if (!ap.merges.empty())
+        std::memcpy(h + ap.off_merges, ap.merges.data(), ap.merges.size() * sizeof(br::MergeItem));
+      unsigned char* hs = h + P.L.score_plan;
+      std::memcpy(hs + sp.off_items, sp.items.data(), sp.items.size() * sizeof(br::ScoreItem));
+      std::memcpy(hs + sp.off_doc_offsets, doc_offsets, size_t(doc_ptr[B]) * sizeof(int32_t));
+      std::memcpy(hs + sp.off_prompt_base, sp.prompt_score_base.data(), size_t(B + 1) * sizeof(int32_t));
+      rank_plans().insert(fresh);
+      plan = fresh;
+    }
+    const br::AttnPlan& ap = plan->ap;
+    const br::ScorePlan& sp = plan->sp;
+    const std::vector<int32_t>& base = plan->base;
+    const RankLayout& L = plan->L;
+    const std::vector<unsigned char>& host = plan->host;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     st = upload(ws, host.data(), host.size(), stream);
     if (st != BR_OK) return st;

@@ -183,6 +183,9 @@ br_status br_attn_routed_fwd(const br_dims* dims, const void* Q, const void* K, 
  * priority, created on first use and kept until the process ends), forked from `stream` after
  * the plan upload and joined back into it; work enqueued on `stream` afterwards, and a
  * synchronisation of `stream`, see every output.  Otherwise everything runs on `stream`.
+ * Plans: the library keeps the last four validated and scheduled plans (process lifetime) and
+ * reuses one when a call's dims, n_signal and four host tables equal an entry's element by
+ * element on the same device; the host arrays are still read during the call only.
  */
 br_status br_rank_workspace_bytes(const br_dims* dims, const int32_t* segment_offsets, const int32_t* seg_ptr,
                                   int32_t n_signal, const int32_t* doc_offsets, const int32_t* doc_ptr,

@@ -221,3 +221,28 @@ def test_rank_step_side_stream_from_two_host_threads():
     for tid in range(2):
         for out, s, o in results[tid]:
             assert torch.equal(out, a_out) and torch.equal(s, a_s) and torch.equal(o, a_o)
+
+
+def test_rank_step_plan_cache_tells_tables_apart():
+    """The ranking step keeps its last few plans and reuses one when a call's dimensions and host
+    tables are equal element by element.  Tables of the same size that differ only in document
+    lengths, and the same tables with more signal rows, alternate: every call still equals the
+    separate calls bit for bit."""
+    kw = dict(hq=4, hkv=2, d=64, seed=9)
+    variants = [workloads.make_custom([(16, [30, 50, 20], 16)], n_signal=4, **kw),
+                workloads.make_custom([(16, [50, 30, 20], 16)], n_signal=4, **kw),
+                workloads.make_custom([(16, [30, 50, 20], 16)], n_signal=8, **kw)]
+    assert len({w.total_tokens for w in variants}) == 1
+    refs = []
+    for w in variants:
+        dev = upload(w)
+        out = br.attn_fwd(dev["Q"], dev["K"], dev["V"], w.segment_offsets, w.seg_ptr)
+        s = br.doc_scores(dev["Q_S"], dev["K"], w.doc_offsets, w.doc_ptr)
+        refs.append((dev, out, s, br.sort_docs(s, w.doc_ptr)))
+    log("[gpu] rank step plan cache: three tables of one size, alternating")
+    for rep in range(3):
+        for w, (dev, a_out, a_s, a_o) in zip(variants, refs):
+            out, s, o = br.rank_step(dev["Q"], dev["K"], dev["V"], dev["Q_S"], w.segment_offsets, w.seg_ptr,
+                                     w.doc_offsets, w.doc_ptr)
+            torch.cuda.synchronize()
+            assert torch.equal(out, a_out) and torch.equal(s, a_s) and torch.equal(o, a_o), (rep, w.prompts)
