@@ -246,3 +246,28 @@ def test_rank_step_plan_cache_tells_tables_apart():
                                      w.doc_offsets, w.doc_ptr)
             torch.cuda.synchronize()
             assert torch.equal(out, a_out) and torch.equal(s, a_s) and torch.equal(o, a_o), (rep, w.prompts)
+
+
+def test_many_prompts_rank_and_attention():
+    """300 small prompts in one call (more than one sort launch's 256 prompts): attention against
+    the dense oracle, scores and per-prompt order against the oracle's, and the one-call step equal
+    to the separate calls."""
+    r = np.random.default_rng(21)
+    prompts = [(int(r.integers(0, 4)), [int(x) for x in r.integers(1, 6, size=int(r.integers(1, 4)))], 2)
+               for _ in range(300)]
+    w = workloads.make_custom(prompts, hq=2, hkv=1, d=64, n_signal=2, seed=21)
+    dev = upload(w)
+    log(f"[gpu] many prompts: B={w.num_prompts} T={w.total_tokens}")
+    out = run_attn(w, dev)
+    ref, _ = orc.attn_dense(w.Q, w.K, w.V, w.segment_offsets, w.seg_ptr)
+    check_attn(out, ref, what="300 prompts")
+    s = br.doc_scores(dev["Q_S"], dev["K"], w.doc_offsets, w.doc_ptr)
+    o = br.sort_docs(s, w.doc_ptr)
+    torch.cuda.synchronize()
+    ref_s, _ = orc.doc_scores(w.Q_S, w.K, w.doc_offsets, w.doc_ptr)
+    check_scores(s.cpu().numpy().astype(np.float64), ref_s, w.n_signal, "300 prompts")
+    check_order(o.cpu().numpy(), ref_s, w.doc_ptr, "300 prompts")
+    out2, s2, o2 = br.rank_step(dev["Q"], dev["K"], dev["V"], dev["Q_S"], w.segment_offsets, w.seg_ptr,
+                                w.doc_offsets, w.doc_ptr)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out) and torch.equal(s2, s) and torch.equal(o2, o)
