@@ -12,28 +12,40 @@
 //
 // Work item = 128 (token, head) rows: TM = 128 / G consecutive tokens of the G query heads
 // that share one KV head (grouped-query packing), so each K/V tile staged in LDS serves G
-// heads.  Wave w owns 32 rows.  Per 64-key tile:
-//   S^T = K Q^T   with v_mfma_f32_32x32x16_bf16 (keys on M, query rows on N), so every lane
-//                 holds one query row and 32 of the tile's keys: row max/sum need only one
+// heads.  Wave w owns 32 rows.  Keys are visited in tiles of 32:
+//   S^T = K Q^T   v_mfma_f32_32x32x16_bf16 with keys on M and query rows on N, so each lane
+//                 holds one query row and 16 of the tile's keys; the row max needs one
 //                 cross-half exchange (v_permlane32_swap);
-//   online softmax in fp32 (log2 domain, exp2), lazy rescaling of the accumulator;
-//   O^T += V^T P^T with P rounded to bf16; V is staged row-major and its transposed MFMA
-//                 fragments come from transposing LDS reads (ds_read_b64_tr_b16).
+//   online softmax in fp32 (log2 domain, exp2) with lazy rescaling of the accumulator;
+//   O^T += V^T P^T with P rounded to bf16; the transposed V fragments come from transposing
+//                 LDS reads (ds_read_b64_tr_b16).
 //
-// The kernel is persistent: each workgroup serves one KV head and runs its share of the item
-// list (a host-side list schedule).  Tiles stream through one software pipeline across item
-// boundaries: while a tile is computed, the next tile's K/V (on an item's last tile, the next
-// item's first tile) is loaded into registers, one load per two S^T MFMAs, then written to the
-// other LDS buffer.  Loads and stores go through buffer resources sized to the valid rows, so
-// rows past a range end read as zero and writes past a tile's last token are dropped by the
-// hardware.
+// Software pipeline.  The kernel is persistent: each workgroup serves one KV head and walks the
+// key tiles of its share of the item list (a host list schedule) as one flat sequence that runs
+// across item boundaries.  Iteration j of a wave issues
+//   the P.V products of tile j-1, the S^T products of tile j+1        (matrix cores)
+//   the softmax of tile j                                                (vector ALU)
+// so the exponentials of one tile overlap the matrix products of its neighbours.  K and V tiles
+// go from memory straight into LDS (buffer loads with the LDS flag: no register staging) through
+// rings of NS slots, NS - 1 tiles ahead of use; one wait for the wave's own loads plus one
+// barrier per tile publishes them.  The next item's Q fragments are loaded into registers while
+// the current item runs.  Loads use buffer resources sized to the valid rows: rows past a range
+// end read as zero, and output rows past a tile's last token are dropped by the hardware.
 //
-// Q and O move as whole rows (1 KB per wave instruction over 8 full cache lines, instead of
-// 32 B from each of 32 rows) and are redistributed through LDS: the tile buffer the item's
-// last tile used is free until the next item's second tile.  Each wave passes the next item's
-// Q rows (loaded once the last tile's S^T is formed) into MFMA fragments through its own 32
-// rows of that buffer, then this item's normalised output rows the other way.  Query rows of long prompts are split over key
-// chunks; their fp32 partials (m, l, o) are combined by attn_merge_kernel.
+// LDS layouts (16-byte units, XOR-swizzled instead of padded, because a direct-to-LDS load
+// fills 1 KB of consecutive LDS per wave instruction):
+//   K tile: row k at k * D * 2 bytes, unit c of the row stored at unit c ^ swz_k(k), so the 16
+//           keys a quarter-wave reads at one unit fall in 16 different bank groups;
+//   V tile: unit c of row k at unit c ^ swz_v(k), so a half-wave's transposing read (4 keys x 4
+//           units) touches 16 different bank groups.
+// Q fragments use a permutation of the head dimension inside each 16-wide MFMA step (lane half
+// 0 takes units 0..D/16-1 of a row, half 1 the rest) so a lane loads one contiguous half-row;
+// the K fragments are read with the same permutation, and the contraction over d is unchanged.
+//
+// Query rows of long prompts are split over key chunks; their fp32 partials (m, l, o) are
+// combined by attn_merge_kernel.
+#include <type_traits>
+
 #include "attn_merge.h"
 #include "device_common.h"
 #include "launch.h"
@@ -44,329 +56,499 @@ namespace br {
 // Accumulator rescaling is skipped until the running maximum grows by more than this many
 // log2 units, so probabilities stay <= 2^8 before normalisation (exact in fp32 and bf16 range).
 constexpr float kRescaleSlack = 8.0f;
+constexpr int kFwdKeys = 32;   // keys per LDS tile
+constexpr int kFwdSlots = 3;   // tiles per ring (K ring and V ring): loads run two tiles ahead
 
-template <int D, int G>
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding), then a workgroup
+// barrier.  The asm statement also keeps the compiler from moving memory accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// s_waitcnt vmcnt(N) alone.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_vm_dyn(int n) {
+  switch (min(n, 63) >> 2) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<4>(); break;
+    case 2: wait_vm<8>(); break;
+    case 3: wait_vm<12>(); break;
+    case 4: wait_vm<16>(); break;
+    case 5: wait_vm<20>(); break;
+    case 6: wait_vm<24>(); break;
+    case 7: wait_vm<28>(); break;
+    case 8: wait_vm<32>(); break;
+    case 9: wait_vm<36>(); break;
+    case 10: wait_vm<40>(); break;
+    case 11: wait_vm<44>(); break;
+    case 12: wait_vm<48>(); break;
+    case 13: wait_vm<52>(); break;
+    case 14: wait_vm<56>(); break;
+    default: wait_vm<60>(); break;
+  }
+}
+
+// The same with a barrier after the wait.
+__device__ __forceinline__ void wait_vm_barrier_dyn(int n) {
+  switch (min(n, 63) >> 2) {
+    case 0: wait_vm_barrier<0>(); break;
+    case 1: wait_vm_barrier<4>(); break;
+    case 2: wait_vm_barrier<8>(); break;
+    case 3: wait_vm_barrier<12>(); break;
+    case 4: wait_vm_barrier<16>(); break;
+    case 5: wait_vm_barrier<20>(); break;
+    case 6: wait_vm_barrier<24>(); break;
+    case 7: wait_vm_barrier<28>(); break;
+    case 8: wait_vm_barrier<32>(); break;
+    case 9: wait_vm_barrier<36>(); break;
+    case 10: wait_vm_barrier<40>(); break;
+    case 11: wait_vm_barrier<44>(); break;
+    case 12: wait_vm_barrier<48>(); break;
+    case 13: wait_vm_barrier<52>(); break;
+    case 14: wait_vm_barrier<56>(); break;
+    default: wait_vm_barrier<60>(); break;
+  }
+}
+
+template <int D, int G, int NS>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                        const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                                                        float* __restrict__ lse, const AttnItem* __restrict__ items,
                                                        const int32_t* __restrict__ ranges, float* __restrict__ part_o,
                                                        float* __restrict__ part_ml, int Hq, int Hkv, float scale_log2,
                                                        int q_row_base) {
-  constexpr int TM = kRowsPerTile / G;  // tokens per tile
-  constexpr int BN = kKeyTile;          // keys per LDS tile
-  constexpr int NKB = BN / 32;          // 32-key MFMA blocks per tile
-  constexpr int KROW = D + 8;           // K row stride in LDS (elements): +16 B breaks bank aliasing
-  // V row stride in LDS (elements): 4 or 12 (mod 16) 16-byte units, so the 4 rows x 4 units that
-  // one half-wave of a transposing read touches fall in 16 different bank groups.
-  constexpr int VROW = D == 128 ? 160 : 96;
-  static_assert(VROW >= D && ((VROW / 8) % 16 == 4 || (VROW / 8) % 16 == 12), "V row stride");
+  constexpr int TM = kRowsPerTile / G;  // tokens per item
+  constexpr int BN = kFwdKeys;
+  constexpr int RB = 2 * D;             // bytes per row of one head
+  constexpr int TB = BN * RB;           // bytes per K or V tile
+  constexpr int UPR = D / 8;            // 16-byte units per row
   constexpr int DSTEPS = D / 16;        // MFMA k-steps over the head dimension
   constexpr int DBLK = D / 32;          // 32-wide output blocks over the head dimension
-  constexpr int KCH = D / 8;            // 16-byte chunks per K/V row
-  constexpr int KROWS_PER_PASS = 256 / KCH;
-  constexpr int KPASS = BN / KROWS_PER_PASS;
+  constexpr int KPI = 1024 / RB;        // key rows per direct-to-LDS wave instruction
+  constexpr int NDMA = BN / KPI / 4;    // such instructions per wave per tile, for K and for V
+  constexpr int LOADS = 2 * NDMA;       // vector-memory loads a wave issues per iteration
+  constexpr int WIN = 6;                // descriptor window = loop unroll factor
+  static_assert(NDMA >= 1 && NDMA * KPI * 4 == BN, "tile split over four waves");
+  static_assert(NS == 3, "the loop below is unrolled for three ring slots and two register sets");
+  static_assert(DSTEPS * KPI == 32, "one wave's Q rows in DSTEPS direct-to-LDS instructions");
 
-  // LDS buffer b holds K tile b (BN x KROW) followed by V tile b (BN x VROW), both row-major.
-  // Between an item's last tile and the next item's second tile, the buffer the last tile used
-  // is free and redistributes Q and O rows ([row][D + 8], 32 rows per wave).
-  constexpr int KBUF = BN * KROW;
-  constexpr int TILE = KBUF + BN * VROW;
-  __shared__ __align__(16) uint16_t skv[2][TILE];
+  __shared__ __align__(1024) uint8_t vring[NS][TB];
+  __shared__ __align__(1024) uint8_t kring[NS][TB];
+  __shared__ __align__(1024) uint8_t qbuf[kRowsPerTile * RB];  // an item's Q rows (wave w: rows 32w..)
 
   const int g = blockIdx.x % Hkv;
   const int wg = blockIdx.x / Hkv;
   const int it_begin = ranges[wg], it_end = ranges[wg + 1];
   if (it_begin >= it_end) return;  // uniform per workgroup
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, half = lane >> 5;
-  const int rho = w * 32 + n;  // this lane's row within the tile
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, half = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
+  const int rho = w * 32 + n;  // this lane's row within the item
   const int hh = rho / TM, tt = rho % TM;
   const int h = g * G + hh;
   const int q_stride = Hq * D, kv_stride = Hkv * D;  // elements between consecutive tokens
 
-  // Per-lane byte offsets inside a row block (Q, O) or a key tile (K, V).
-  const uint32_t q_off = uint32_t((tt * q_stride + hh * D + 8 * half) * 2);
-  const int kcc = tid % KCH, kr0 = tid / KCH;  // K and V: 16-byte chunk and first row of this thread
-  const uint32_t k_off = uint32_t((kr0 * kv_stride + 8 * kcc) * 2);
-  // P.V A-operand reads (transposing, see lds_read_tr16): in each 16-lane group (s = lane % 16,
-  // head-dim half dh = (lane / 16) % 2, key half `half`) lane s points at key 4 half + s / 4 and
-  // head-dim element 16 dh + 4 (s % 4) of a block; blocks differ by compile-time offsets.
+  // ---- swizzles (16-byte units within a row) ----
+  auto swz_k = [](int k) { return D == 128 ? (k & 15) : ((k >> 1) & 7); };
+  auto swz_v = [](int k) { return D == 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); };
+
+  // LDS byte addresses (M0 values of the direct-to-LDS loads): this wave's share of each ring slot.
+  const uint32_t k_lds = lds_addr_of(kring) + 1024 * NDMA * w;
+  const uint32_t v_lds = lds_addr_of(vring) + 1024 * NDMA * w;
+  const uint32_t q_lds = lds_addr_of(qbuf) + 32 * RB * w;
+  // K fragment of k-step st for this lane: key n, unit st + half * DSTEPS (head-dim permutation).
+  uint32_t kofs[DSTEPS];
+#pragma unroll
+  for (int st = 0; st < DSTEPS; ++st) kofs[st] = uint32_t(n * RB + 16 * ((st + half * DSTEPS) ^ swz_k(n)));
+  // Transposing V reads: in each 16-lane group (s = lane % 16, head-dim half dh = (lane / 16) % 2)
+  // lane s points at key 4 half + s / 4 and head-dim element 16 dh + 4 (s % 4) of a 32-wide block;
+  // keys 16 m (+8) shift the row by a multiple of 8, which leaves the swizzle unchanged.
   const int vs = lane & 15, vdh = (lane >> 4) & 1;
-  const int v_lane = KBUF + (4 * half + (vs >> 2)) * VROW + 16 * vdh + 4 * (vs & 3);
+  const int vkey = 4 * half + (vs >> 2);
+  uint32_t vofs[DBLK];
+#pragma unroll
+  for (int b = 0; b < DBLK; ++b)
+    vofs[b] = uint32_t(vkey * RB + 16 * ((4 * b + 2 * vdh + ((vs & 3) >> 1)) ^ swz_v(vkey)) + 8 * (vs & 1));
+  // Direct-to-LDS loads: wave instruction r of this wave fills LDS bytes [i KB, (i + 1) KB) of a
+  // tile, i = NDMA w + r, i.e. key rows KPI i .. KPI i + KPI - 1; lane l fills unit l % UPR of
+  // row KPI i + l / UPR with source unit (l % UPR) ^ swz(row).
+  uint32_t kdma[NDMA], vdma[NDMA];
+#pragma unroll
+  for (int r = 0; r < NDMA; ++r) {
+    const int key = KPI * (NDMA * w + r) + lane / UPR, u = lane % UPR;
+    kdma[r] = uint32_t(key * kv_stride * 2 + 16 * (u ^ swz_k(key)));
+    vdma[r] = uint32_t(key * kv_stride * 2 + 16 * (u ^ swz_v(key)));
+  }
 
-  // Q fragments: B operand of S^T = K Q^T (row n, head-dim elements 16 s + 8 half .. +8).
-  // Resource over a tile's valid rows of a [T, Hq, D] tensor, based at its first row and head.
-  auto row_rsrc = [&](const uint16_t* base, const AttnItem& it) {
-    const int rows = min(TM, it.row_limit - it.row0);
-    return make_rsrc(base + (int64_t(it.row0 - q_row_base) * Hq + g * G) * D, rows * q_stride * 2);
+  // ---- the flat tile sequence ----
+  // A tile is {first key, (item << 9) | (keys << 3) | flags, first row of its item}: keys =
+  // valid keys of the tile (1..32); flags 1 causal range, 2 first tile of its item, 4 last tile
+  // of its item.  Items past it_end are "no tile": nothing to read, and they count as one-tile
+  // items so that the stages around them reset cleanly.
+  constexpr int F_CAUSAL = 1, F_FIRST = 2, F_LAST = 4, IT_SHIFT = 9;
+  auto code_it = [](int code) { return code >> IT_SHIFT; };
+  auto code_keys = [](int code) { return (code >> 3) & 63; };
+  auto n_tiles = [](int a0, int a1) { return a1 > a0 ? (a1 - a0 + BN - 1) / BN : 0; };
+  // Lead cursor: item c_it (its key ranges and first row cached), tile c_t of c_nt (c_na unmasked).
+  int c_it = it_begin, c_t = 0, c_a0, c_a1, c_b0, c_b1, c_na, c_nt, c_row0;
+  auto load_item = [&]() {
+    if (c_it < it_end) {
+      const AttnItem it = items[c_it];
+      c_row0 = it.row0;
+      c_a0 = it.a_start;
+      c_a1 = it.a_end;
+      c_b0 = it.b_start;
+      c_b1 = it.b_end;
+      c_na = n_tiles(c_a0, c_a1);
+      c_nt = c_na + n_tiles(c_b0, c_b1);
+    }
   };
+  load_item();
+  auto take = [&](int& start, int& code, int& row0) {
+    if (c_it >= it_end) {
+      start = row0 = 0;
+      code = (it_end << IT_SHIFT) | F_FIRST | F_LAST;
+      return;
+    }
+    const bool causal = c_t >= c_na;
+    start = causal ? c_b0 + (c_t - c_na) * BN : c_a0 + c_t * BN;
+    const int keys = min(BN, (causal ? c_b1 : c_a1) - start);
+    code = (c_it << IT_SHIFT) | (keys << 3) | (causal ? F_CAUSAL : 0) | (c_t == 0 ? F_FIRST : 0) |
+           (c_t + 1 == c_nt ? F_LAST : 0);
+    row0 = c_row0;
+    if (++c_t == c_nt) {
+      c_t = 0;
+      ++c_it;
+      load_item();
+    }
+  };
+  int n_total = 0;
+  for (int i = it_begin; i < it_end; ++i) {
+    const int4 rg = *reinterpret_cast<const int4*>(&items[i].a_start);  // a_start, a_end, b_start, b_end
+    n_total += n_tiles(rg.x, rg.y) + n_tiles(rg.z, rg.w);
+  }
+
+  // ---- loads ----
+  // One resource per tensor based at this KV head's column; a tile is addressed by the scalar
+  // offset start * kv_stride * 2 and bounded by a record count that ends at its last valid key, so
+  // key rows past a range end read as zero (the host keeps K and V under 4 GB).
+  const uint16_t* const k_base = K + g * D;
+  const uint16_t* const v_base = V + g * D;
+  auto issue_k = [&](int start, int code, int slot) {  // "no tile" has start 0 and no keys
+    const uint32_t s0 = uint32_t(start) * uint32_t(kv_stride * 2);
+    const uint32_t end = s0 + uint32_t(code_keys(code)) * uint32_t(kv_stride * 2);
+    const rsrc_t r = make_rsrc(k_base, int(end));
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) buf_load16_lds(r, k_lds + slot * TB + 1024 * i, kdma[i], s0);
+  };
+  auto issue_v = [&](int start, int code, int slot) {  // "no tile" has start 0 and no keys
+    const uint32_t s0 = uint32_t(start) * uint32_t(kv_stride * 2);
+    const uint32_t end = s0 + uint32_t(code_keys(code)) * uint32_t(kv_stride * 2);
+    const rsrc_t r = make_rsrc(v_base, int(end));
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) buf_load16_lds(r, v_lds + slot * TB + 1024 * i, vdma[i], s0);
+  };
+  // Resource over an item's valid rows of a [T, Hq, D] tensor, based at its first row and head.
+  auto row_rsrc = [&](const uint16_t* base, int row0, int row_limit) {
+    const int rows = min(TM, row_limit - row0);
+    return make_rsrc(base + (int64_t(row0 - q_row_base) * Hq + g * G) * D, rows * q_stride * 2);
+  };
+  // Q rows of an item go to qbuf with direct-to-LDS loads (each wave its own 32 rows, laid out and
+  // swizzled like a K tile), then into the fragments `qf` (B operand of S^T, the head-dim
+  // permutation of the K fragments).  Each wave reads back only rows it loaded itself, so its own
+  // vector-memory wait suffices and no barrier is involved.
   u32x4_t qf[DSTEPS];
-  auto load_q = [&](const AttnItem& it, u32x4_t* dst) {
-    const rsrc_t r = row_rsrc(Q, it);
-#pragma unroll
-    for (int s = 0; s < DSTEPS; ++s) dst[s] = buf_load16(r, q_off + 32 * s);
-  };
-  // The same rows loaded coalesced: instruction s of wave w reads QRI whole rows (1 KB, 8 full
-  // cache lines) instead of 32 B from each of 32 rows; the fragments are then redistributed
-  // through LDS ([row][QROW]).  Lane l takes chunk l % KCH of row 32 w + QRI s + l / KCH.
-  constexpr int QROW = D + 8;        // staged Q row stride (elements): same bank pattern as K
-  constexpr int QRI = 512 / D;       // rows per coalesced instruction
-  static_assert(kRowsPerTile * QROW <= TILE && QRI * DSTEPS == kRowsPerWave, "Q staging fits a tile buffer");
-  auto load_q_rows = [&](const AttnItem& it, bool valid) {
-    const rsrc_t r = valid ? row_rsrc(Q, it) : make_rsrc(Q, 0);  // zero bytes: reads nothing
-#pragma unroll
-    for (int s = 0; s < DSTEPS; ++s) {
-      const int rr = 32 * w + QRI * s + lane / KCH;
-      qf[s] = buf_load16(r, uint32_t(((rr % TM) * q_stride + (rr / TM) * D + 8 * (lane % KCH)) * 2));
+  auto issue_q = [&](int it) {
+    rsrc_t r = make_rsrc(Q, 0);
+    if (it < it_end) {
+      const int2 rr = *reinterpret_cast<const int2*>(&items[it].row0);
+      r = row_rsrc(Q, rr.x, rr.y);
     }
-  };
-  auto stage_q_rows = [&](uint16_t* st) {
+    // Per-lane offsets are formed here (the opaque copy of the lane index keeps the compiler
+    // from hoisting them into registers that stay live across the whole loop).
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int s = 0; s < DSTEPS; ++s)
-      *reinterpret_cast<u32x4_t*>(&st[(32 * w + QRI * s + lane / KCH) * QROW + 8 * (lane % KCH)]) = qf[s];
-  };
-  auto read_q_frags = [&](const uint16_t* st) {
-#pragma unroll
-    for (int s = 0; s < DSTEPS; ++s) qf[s] = load16(&st[rho * QROW + 16 * s + 8 * half]);
-  };
-
-  // ---- global -> registers -> LDS staging of one K/V tile ----
-  // KCH adjacent threads load one key row of K and of V (coalesced 256-byte reads) and write it
-  // to the same row of the LDS tiles.
-  u32x4_t kreg[KPASS], vreg[KPASS];
-  // The next tile's loads are issued one at a time among the current tile's S^T MFMAs: issued
-  // together at the top of a tile, the loads of all waves on the CU queue in the texture
-  // address unit and each wave's in-order issue stalls behind them.  `next_k`/`next_v` cover
-  // the next tile's valid keys (zero bytes when there is none, so the loads read nothing).
-  rsrc_t next_k, next_v;
-  auto plan_tile = [&](int start, int end) {
-    const int keys = min(BN, end - start);
-    next_k = make_rsrc(K + int64_t(start) * kv_stride + g * D, keys * kv_stride * 2);
-    next_v = make_rsrc(V + int64_t(start) * kv_stride + g * D, keys * kv_stride * 2);
-  };
-  auto no_tile = [&]() {
-    next_k = make_rsrc(K, 0);
-    next_v = make_rsrc(V, 0);
-  };
-  constexpr int LOAD_STEPS = 2 * KPASS;
-  auto load_step = [&](int j) {
-    const int p = j >> 1;
-    const uint32_t off = k_off + p * KROWS_PER_PASS * kv_stride * 2;
-    if (j & 1)
-      vreg[p] = buf_load16(next_v, off);
-    else
-      kreg[p] = buf_load16(next_k, off);
-  };
-  auto load_tile = [&](int start, int end) {
-    plan_tile(start, end);
-#pragma unroll
-    for (int j = 0; j < LOAD_STEPS; ++j) load_step(j);
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < KPASS; ++p) {
-      const int row = kr0 + p * KROWS_PER_PASS;
-      *reinterpret_cast<u32x4_t*>(&skv[buf][row * KROW + 8 * kcc]) = kreg[p];
-      *reinterpret_cast<u32x4_t*>(&skv[buf][KBUF + row * VROW + 8 * kcc]) = vreg[p];
+    for (int i = 0; i < DSTEPS; ++i) {  // DSTEPS instructions of KPI rows cover the wave's 32 rows
+      const int rq = KPI * i + ln / UPR, u = ln % UPR, rr = 32 * w + rq;
+      const uint32_t off = uint32_t(((rr % TM) * q_stride + (rr / TM) * D) * 2 + 16 * (u ^ swz_k(rq)));
+      buf_load16_lds(r, q_lds + 1024 * i, off);
     }
   };
 
-  // Key tile i of an item: the unmasked range's tiles come first, then the causal range's.
-  auto n_unmasked = [](const AttnItem& it) { return it.a_end > it.a_start ? (it.a_end - it.a_start + BN - 1) / BN : 0; };
-  auto n_tiles = [&](const AttnItem& it) {
-    return n_unmasked(it) + (it.b_end > it.b_start ? (it.b_end - it.b_start + BN - 1) / BN : 0);
-  };
-  auto tile_start = [&](const AttnItem& it, int nA, int i) { return i < nA ? it.a_start + i * BN : it.b_start + (i - nA) * BN; };
-  auto tile_end = [&](const AttnItem& it, int nA, int i) { return i < nA ? it.a_end : it.b_end; };
-
+  // ---- pipeline state ----
   f32x16_t o[DBLK];
-  float m_run, l_run;
+#pragma unroll
+  for (int b = 0; b < DBLK; ++b) o[b] = f32x16_t{};
+  f32x16_t sb[2] = {f32x16_t{}, f32x16_t{}};  // S^T of tiles j (sb[(j + 1) & 1]) and j + 1
+  uint32_t pk[8];  // bf16 P: of tile j - 1 until its P.V products have read it, then of tile j
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pk[i] = 0u;
+  float m_run = -INFINITY, l_run = 0.f, m_prev = -INFINITY, l_prev = 0.f;
 
-  // One tile: S^T, mask, online softmax, O^T += V^T P^T.  `row_tok` is this lane's token.
-  // `after_s` runs once the S^T MFMAs have consumed the Q fragments (on an item's last tile it
-  // loads the next item's Q rows into them).
-  auto compute = [&](int buf, int start, int end, bool causal, int row0, int row_tok, bool first, auto&& after_s) {
-    f32x16_t s[NKB];
-    static_assert(NKB * DSTEPS == 2 * LOAD_STEPS, "one next-tile load per two S^T MFMAs");
+  // Descriptor window: tile t at index (t + 1) mod WIN; iteration j uses tiles j - 1 .. j + NS.
+  int d_start[WIN], d_code[WIN], d_row0[WIN];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = f32x16_t{};
-      const uint16_t* kp = &skv[buf][(kb * 32 + n) * KROW + 8 * half];
+  for (int k = 0; k < WIN; ++k) {
+    d_start[k] = d_row0[k] = 0;
+    d_code[k] = (it_end << IT_SHIFT) | F_FIRST | F_LAST;  // tiles -2 and -1: none
+  }
 #pragma unroll
-      for (int st = 0; st < DSTEPS; ++st) {
-        s[kb] = mfma32(load16(kp + 16 * st), qf[st], s[kb]);
-        if (st & 1) load_step((kb * DSTEPS + st) >> 1);
+  for (int t = 0; t < NS; ++t) take(d_start[t + 1], d_code[t + 1], d_row0[t + 1]);  // tiles 0 .. NS - 1
+
+  // Prologue: the first item's Q (iteration -1 reads it into qf), then the loads of virtual
+  // iterations j = -NS .. -2, each issuing K of tile j + NS and V of tile j + NS - 2 (none for
+  // negative tiles: zero-size loads that still write zeros, so every slot is initialised).
+  issue_q(it_begin);
+#pragma unroll
+  for (int jv = -NS; jv <= -2; ++jv) {
+    const int kt = jv + NS, vt = jv + NS - 2;
+    issue_k(d_start[kt + 1], d_code[kt + 1], kt % NS);
+    const int vi = vt >= 0 ? vt + 1 : 0;
+    issue_v(d_start[vi], d_code[vi], (jv - 2 + 2 * NS) % NS);
+  }
+  // Vector-memory operations issued after the last Q batch that always issue (for the wait before
+  // its rows are read): the prologue's K/V loads.
+  int since_q = (NS - 1) * LOADS;
+  // Unconditional vector-memory operations (Q batches, output stores) that iterations j - 1 and
+  // j - 2 issued after their K/V loads.
+  int ex_prev = 0, ex_prev2 = 0;
+  // Row range and partial slot of the item whose last P.V products run in the next iteration.
+  int e_row0 = 0, e_row_limit = 0, e_slot = -1;
+
+  // ---- one pipeline iteration (PH = (j + 1) mod WIN, compile-time) ----
+  auto iteration = [&](auto ph_tag) {
+    constexpr int PH = decltype(ph_tag)::value;
+    constexpr int KSLOT_LOAD = (PH + NS - 1) % NS;  // slot of K tile j + NS  (= j mod NS)
+    constexpr int VSLOT_LOAD = (PH + NS - 3) % NS;  // slot of V tile j + NS - 2
+    constexpr int KSLOT_S = PH % NS;                 // slot of K tile j + 1
+    constexpr int VSLOT_PV = (PH + NS - 2) % NS;     // slot of V tile j - 1
+    constexpr int CUR = PH & 1, NXT = CUR ^ 1;       // S^T register sets of tiles j and j + 1
+    // Window index of tile j + k is (PH + k) mod WIN.
+    constexpr int IP = (PH + WIN - 1) % WIN, IC = PH, IS = (PH + 1) % WIN;  // tiles j - 1, j, j + 1
+    constexpr int IK = (PH + NS) % WIN, IV = (PH + NS - 2) % WIN;           // tiles j + NS, j + NS - 2
+    constexpr int INEW = (PH + NS + 1) % WIN;                                 // tile j + NS + 1
+    f32x16_t& s_cur = sb[CUR];
+    f32x16_t& s_nxt = sb[NXT];
+
+    // 1. K of tile j + 1 and V of tile j - 1 have landed in every wave: they were issued in
+    // iteration j + 1 - NS (= j - 2); after them came that iteration's extra operations, the K/V
+    // loads of iteration j - 1 and its extra operations (vector-memory operations complete in
+    // issue order on gfx9, stores included).
+    {
+      const int x = ex_prev + ex_prev2;
+      if (x == 0)
+        wait_vm_barrier<(NS - 2) * LOADS>();
+      else
+        wait_vm_barrier_dyn((NS - 2) * LOADS + x);
+      ex_prev2 = ex_prev;
+      ex_prev = 0;
+    }
+    // 2. Loads NS - 1 tiles ahead: K of tile j + NS, V of tile j + NS - 2.
+    issue_k(d_start[IK], d_code[IK], KSLOT_LOAD);
+    issue_v(d_start[IV], d_code[IV], VSLOT_LOAD);
+    since_q += LOADS;
+    // 3. Tile j + 1 starts an item: read its Q fragments, then load the next item's Q rows.
+    const int s_code = d_code[IS];
+    if ((s_code & F_FIRST) && code_it(s_code) < it_end) {
+      wait_vm_dyn(since_q);  // the Q batch (and everything older) has landed
+      // The wave's Q region offset is made opaque here so that the compiler forms these
+      // addresses when needed instead of keeping eight more registers live across the loop.
+      uint32_t qw = uint32_t(32 * RB) * uint32_t(w);
+      asm volatile("" : "+s"(qw));
+#pragma unroll
+      for (int st = 0; st < DSTEPS; ++st) qf[st] = *reinterpret_cast<const u32x4_t*>(&qbuf[qw + kofs[st]]);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the buffer is refilled
+      issue_q(code_it(s_code) + 1);
+      since_q = 0;
+      ex_prev += DSTEPS;
+    }
+    // 4. Softmax of tile j, part 1: mask.
+    const int c_code = d_code[IC], c_start = d_start[IC], c_row0 = d_row0[IC];
+    const int c_keys = code_keys(c_code);
+    const bool c_valid = code_it(c_code) < it_end;
+    const bool c_first = (c_code & F_FIRST) != 0;
+    const bool c_causal = (c_code & F_CAUSAL) != 0;
+    if (c_first) {
+      m_prev = m_run;
+      l_prev = l_run;
+    }
+    if (!c_valid || c_keys < BN || (c_causal && c_start + BN - 1 > c_row0)) {
+      // Register r holds key start + 8 (r / 4) + 4 half + r % 4.
+      const int lim = (c_valid ? (c_causal ? min(c_keys, c_row0 + tt + 1 - c_start) : c_keys) : 0) - 4 * half;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_cur[r] = (8 * (r >> 2) + (r & 3)) < lim ? s_cur[r] : -INFINITY;
+    }
+
+    // 5. Matrix products of tiles j - 1 (P.V) and j + 1 (S^T), softmax of tile j, in three phases
+    // separated by scheduling fences, each pairing matrix-core work with independent vector work:
+    //   A  P.V MFMAs of tile j - 1, keys 0..15    | row maximum of tile j
+    //   B  P.V MFMAs of tile j - 1, keys 16..31   | exponentials of keys whose P slots A freed
+    //   C  S^T MFMAs of tile j + 1                | remaining exponentials, row sum
+    // Each phase's LDS operands are read one phase ahead.  P of tile j overwrites P of tile j - 1
+    // in the registers the P.V products have finished reading.
+    const uint8_t* vt_base = &vring[VSLOT_PV][0];
+    const uint8_t* kt_base = &kring[KSLOT_S][0];
+    u32x4_t vf[2][DBLK];
+    auto read_v = [&](int m) {
+#pragma unroll
+      for (int b = 0; b < DBLK; ++b) {
+        const uint16_t* vp = reinterpret_cast<const uint16_t*>(vt_base + vofs[b] + 16 * m * RB);
+        const u32x2_t lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 8 * D);
+        vf[m][b] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
       }
-    }
-    // Instruction order for the scheduler: (2 LDS reads, 2 MFMAs, 1 global load) repeated.
-#pragma unroll
-    for (int j = 0; j < LOAD_STEPS; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-    after_s();
-    // Mask only tiles that cross the range end or the causal diagonal of some row.  Register r of
-    // block kb holds key start + 32 kb + 8 (r / 4) + 4 half + r % 4.
-    if ((start + BN > end) || (causal && start + BN - 1 > row0)) {
-      const int lim = (causal ? min(end, row_tok + 1) : end) - start - 4 * half;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3)) < lim ? s[kb][r] : -INFINITY;
-    }
-    float mt = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-    mt = max_halves(mt) * scale_log2;
-    if (first) {
-      m_run = mt;  // the accumulator is still zero: nothing to rescale
-    } else {
-      const bool need = mt > m_run + kRescaleSlack;
-      if (__any(need)) {
-        const float m_new = need ? mt : m_run;
-        const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int b = 0; b < DBLK; ++b) o[b] *= alpha;
-      }
-    }
-    const float mu = m_run == -INFINITY ? 0.f : m_run;
-    uint32_t pk[NKB][8];
-    float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // four partial row sums shorten the add chain
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    };
+    u32x4_t kf[DSTEPS];
+    float lsum0 = 0.f, lsum1 = 0.f;  // two partial row sums shorten the add chain
+    float mu = 0.f;
+    // Exponentials of s_cur registers [r0, r1) (pairs), packed into pk[r / 2].
+    auto exps = [&](int r0, int r1) {
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(fmaf(s[kb][r], scale_log2, -mu));
-        const float p1 = fast_exp2(fmaf(s[kb][r + 1], scale_log2, -mu));
-        pk[kb][r >> 1] = pack_bf16x2(p0, p1);
-        lsum[(r >> 1) & 3] += p0 + p1;
+        if (r < r0 || r >= r1) continue;
+        const float p0 = fast_exp2(fmaf(s_cur[r], scale_log2, -mu));
+        const float p1 = fast_exp2(fmaf(s_cur[r + 1], scale_log2, -mu));
+        pk[r >> 1] = pack_bf16x2(p0, p1);
+        if (r & 2)
+          lsum1 += p0 + p1;
+        else
+          lsum0 += p0 + p1;
       }
-    l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
-    // O^T += V^T P^T, 16 keys per MFMA.  Lane half h of P holds keys 16 m + 4 h + 0..3 and
-    // 16 m + 8 + 4 h + 0..3 of block kb (the S^T accumulator order); the two transposing reads
-    // give the V^T fragment the same key order.
+    };
+    constexpr int R_B = 6;  // exponentials of registers [0, R_B) in phase B, the rest in C
+    read_v(0);
+    __builtin_amdgcn_sched_barrier(0);
+    // Phase A.
+    {
+      const u32x4_t pv = {pk[0], pk[1], pk[2], pk[3]};
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int b = 0; b < DBLK; ++b) o[b] = mfma32(vf[0][b], pv, o[b]);
+    }
+    read_v(1);
+    float mt = fmaxf(fmaxf(s_cur[0], s_cur[1]), s_cur[2]);
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const u32x4_t pv = {pk[kb][4 * m], pk[kb][4 * m + 1], pk[kb][4 * m + 2], pk[kb][4 * m + 3]};
-        const uint16_t* vp = &skv[buf][v_lane + (32 * kb + 16 * m) * VROW];
+    for (int r = 3; r < 15; r += 2) mt = fmaxf(fmaxf(mt, s_cur[r]), s_cur[r + 1]);
+    mt = fmaxf(mt, s_cur[15]);
+    mt = max_halves(mt) * scale_log2;
+    const bool need = !c_first && mt > m_run + kRescaleSlack;
+    const float m_new = c_first ? mt : (need ? mt : m_run);
+    const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
+    m_run = m_new;
+    mu = m_new == -INFINITY ? 0.f : m_new;
+    __builtin_amdgcn_sched_barrier(0);
+    // Phase B.
+    {
+      const u32x4_t pv = {pk[4], pk[5], pk[6], pk[7]};
 #pragma unroll
-        for (int b = 0; b < DBLK; ++b) {
-          const u32x2_t lo = lds_read_tr16(vp + 32 * b), hi = lds_read_tr16(vp + 8 * VROW + 32 * b);
-          o[b] = mfma32(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pv, o[b]);
+      for (int b = 0; b < DBLK; ++b) o[b] = mfma32(vf[1][b], pv, o[b]);
+    }
+#pragma unroll
+    for (int st = 0; st < DSTEPS; ++st) kf[st] = *reinterpret_cast<const u32x4_t*>(kt_base + kofs[st]);
+    exps(0, R_B);
+    __builtin_amdgcn_sched_barrier(0);
+    // Phase C (the second half of the K fragments is read while the first half is used).
+    s_nxt = f32x16_t{};
+#pragma unroll
+    for (int st = 0; st < DSTEPS; ++st) s_nxt = mfma32(kf[st], qf[st], s_nxt);
+    exps(R_B, 16);
+    l_run = (c_first ? 0.f : l_run * alpha) + (lsum0 + lsum1);
+    __builtin_amdgcn_sched_barrier(0);
+    // Keep the softmax results here: otherwise the compiler sinks them past the loop exit test
+    // into the next iteration, where nothing overlaps them.
+    asm volatile("" ::"v"(pk[0]), "v"(pk[1]), "v"(pk[2]), "v"(pk[3]), "v"(pk[4]), "v"(pk[5]), "v"(pk[6]),
+                 "v"(pk[7]), "v"(l_run));
+
+    // 6. Lazy rescale of the accumulator (tile j continues the item of tile j - 1).
+    if (__any(need)) {
+#pragma unroll
+      for (int b = 0; b < DBLK; ++b) o[b] *= alpha;
+    }
+    // 7. Tile j - 1 ended its item: normalise and store its rows (or split-key partials).  The
+    // item's row range and slot were loaded at the end of the previous iteration (e_row0 ..).
+    const int p_code = d_code[IP];
+    if ((p_code & F_LAST) && code_it(p_code) < it_end) {
+      const float l_tot = l_prev + other_half(l_prev);
+      const int prow = e_row0 + tt;
+      if (e_slot < 0) {
+        const float inv = __builtin_amdgcn_rcpf(l_tot);
+        const rsrc_t ro = row_rsrc(O, e_row0, e_row_limit);  // rows past the item's last token are dropped
+#pragma unroll
+        for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int j0 = 2 * t, j1 = 2 * t + 1;
+            const uint32_t a0 = pack_bf16x2(o[b][4 * j0] * inv, o[b][4 * j0 + 1] * inv);
+            const uint32_t a1 = pack_bf16x2(o[b][4 * j0 + 2] * inv, o[b][4 * j0 + 3] * inv);
+            const uint32_t b0 = pack_bf16x2(o[b][4 * j1] * inv, o[b][4 * j1 + 1] * inv);
+            const uint32_t b1 = pack_bf16x2(o[b][4 * j1 + 2] * inv, o[b][4 * j1 + 3] * inv);
+            const uint32_t x0 = half ? a0 : b0, x1 = half ? a1 : b1;
+            const auto r0 = __builtin_amdgcn_permlane32_swap(x0, x0, false, false);
+            const auto r1 = __builtin_amdgcn_permlane32_swap(x1, x1, false, false);
+            const u32x4_t v = half ? u32x4_t{r0[0], r1[0], b0, b1} : u32x4_t{a0, a1, r0[1], r1[1]};
+            buf_store16(v, ro, uint32_t((tt * q_stride + hh * D + 32 * b + 16 * t + 8 * half) * 2));
+          }
+        since_q += 2 * DBLK;
+        ex_prev += 2 * DBLK;
+        if (lse && half == 0 && prow < e_row_limit)
+          lse[int64_t(prow - q_row_base) * Hq + h] = (m_prev + __log2f(l_tot)) * kLn2;
+      } else {
+        const int64_t sl = int64_t(e_slot) * Hkv + g;
+        int pl = lane;  // opaque: the address is formed here rather than held across the loop
+        asm volatile("" : "+v"(pl));
+        float* po = part_o + (sl * kRowsPerTile + w * 32 + (pl & 31)) * D + 4 * (pl >> 5);
+#pragma unroll
+        for (int b = 0; b < DBLK; ++b)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            *reinterpret_cast<f32x4_t*>(po + 32 * b + 8 * jj) =
+                f32x4_t{o[b][4 * jj], o[b][4 * jj + 1], o[b][4 * jj + 2], o[b][4 * jj + 3]};
+        since_q += 4 * DBLK;
+        ex_prev += 4 * DBLK;
+        if (half == 0) {
+          part_ml[(sl * kRowsPerTile + rho) * 2] = m_prev;
+          part_ml[(sl * kRowsPerTile + rho) * 2 + 1] = l_tot;
         }
       }
+    }
+    if ((p_code & F_LAST) && code_it(p_code) < it_end) {
+#pragma unroll
+      for (int b = 0; b < DBLK; ++b) o[b] = f32x16_t{};
+    }
+    // Tile j ends its item: fetch the item's row range and slot for the next iteration's epilogue.
+    if ((c_code & F_LAST) && c_valid) {
+      const int4 rr = *reinterpret_cast<const int4*>(&items[code_it(c_code)].row0);  // row0, row_limit, a_*
+      e_row0 = rr.x;
+      e_row_limit = rr.y;
+      e_slot = items[code_it(c_code)].slot;
+    }
+    // 8. The window slot of tile j - 2 takes tile j + NS + 1.
+    take(d_start[INEW], d_code[INEW], d_row0[INEW]);
   };
 
-  // Pipeline prologue: the first item's Q and first tile.
-  AttnItem cur = items[it_begin];
-  load_q(cur, qf);
-  {
-    const int nA = n_unmasked(cur);
-    load_tile(tile_start(cur, nA, 0), tile_end(cur, nA, 0));
+  // Iterations j = -1 .. n_total (P.V of the last tile runs in iteration n_total), unrolled by WIN
+  // = 6 so that every ring slot (j mod 3), S^T register set (j mod 2) and window index is a
+  // compile-time choice.
+  for (int j = -1; j <= n_total; j += WIN) {
+    iteration(std::integral_constant<int, 0>{});
+    if (j + 1 > n_total) break;
+    iteration(std::integral_constant<int, 1>{});
+    if (j + 2 > n_total) break;
+    iteration(std::integral_constant<int, 2>{});
+    if (j + 3 > n_total) break;
+    iteration(std::integral_constant<int, 3>{});
+    if (j + 4 > n_total) break;
+    iteration(std::integral_constant<int, 4>{});
+    if (j + 5 > n_total) break;
+    iteration(std::integral_constant<int, 5>{});
   }
-  store_tile(0);
-  __syncthreads();
-  int buf = 0;
-
-  for (int it = it_begin; it < it_end; ++it) {
-    const bool more = it + 1 < it_end;
-    const AttnItem nxt = items[more ? it + 1 : it];
-    const int nA = n_unmasked(cur), nt = n_tiles(cur);
-    const int row_tok = cur.row0 + tt;
-#pragma unroll
-    for (int b = 0; b < DBLK; ++b) o[b] = f32x16_t{};
-    m_run = -INFINITY;
-    l_run = 0.f;
-
-    // Every tile prefetches the next one: the item's next tile, or on the last tile the next
-    // item's first tile.  The last tile is written out separately: it also loads the next item's
-    // Q rows, so that the compiler sees those loads on that path only.
-    for (int i = 0; i + 1 < nt; ++i) {
-      plan_tile(tile_start(cur, nA, i + 1), tile_end(cur, nA, i + 1));
-      compute(buf, tile_start(cur, nA, i), tile_end(cur, nA, i), i >= nA, cur.row0, row_tok, i == 0, [] {});
-      store_tile(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
-    }
-    if (more) {
-      const int nA_next = n_unmasked(nxt);
-      plan_tile(tile_start(nxt, nA_next, 0), tile_end(nxt, nA_next, 0));
-    } else {
-      no_tile();
-    }
-    compute(buf, tile_start(cur, nA, nt - 1), tile_end(cur, nA, nt - 1), nt - 1 >= nA, cur.row0, row_tok, nt == 1,
-            [&] { load_q_rows(nxt, more); });
-    if (more) store_tile(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    // The buffer the last tile used is free until the next item's second tile.  Each wave uses
-    // its own 32 rows of it ([row][QROW]) to redistribute the next item's Q rows and then this
-    // item's outputs; a wave's LDS operations complete in order, so only the barrier at the end
-    // of the epilogue is needed.  (Done after the last item too, on zero rows, so that every
-    // path reaches the next tile with the fragments read from LDS and the compiler adds no
-    // memory-counter waits there.)
-    uint16_t* const xbuf = skv[buf ^ 1];
-    stage_q_rows(xbuf);
-    read_q_frags(xbuf);
-
-    // Epilogue: normalise and store this item's rows (or its split-key partials).
-    const float l_tot = l_run + other_half(l_run);
-    if (cur.slot < 0) {
-      const float inv = 1.f / l_tot;
-      const rsrc_t ro = row_rsrc(O, cur);  // rows past the tile's last token are dropped
-#pragma unroll
-      for (int b = 0; b < DBLK; ++b)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          // Lane half 0 holds head-dim elements 8j..8j+3 and half 1 holds 8j+4..8j+7 of each
-          // 8-element group j; swapping one group pair across halves gives every lane 8
-          // contiguous outputs: half 0 stages group 2t, half 1 stages group 2t+1.
-          const int j0 = 2 * t, j1 = 2 * t + 1;
-          const uint32_t a0 = pack_bf16x2(o[b][4 * j0] * inv, o[b][4 * j0 + 1] * inv);
-          const uint32_t a1 = pack_bf16x2(o[b][4 * j0 + 2] * inv, o[b][4 * j0 + 3] * inv);
-          const uint32_t b0 = pack_bf16x2(o[b][4 * j1] * inv, o[b][4 * j1 + 1] * inv);
-          const uint32_t b1 = pack_bf16x2(o[b][4 * j1 + 2] * inv, o[b][4 * j1 + 3] * inv);
-          const uint32_t x0 = half ? a0 : b0, x1 = half ? a1 : b1;
-          const auto r0 = __builtin_amdgcn_permlane32_swap(x0, x0, false, false);
-          const auto r1 = __builtin_amdgcn_permlane32_swap(x1, x1, false, false);
-          const u32x4_t v = half ? u32x4_t{r0[0], r1[0], b0, b1} : u32x4_t{a0, a1, r0[1], r1[1]};
-          *reinterpret_cast<u32x4_t*>(&xbuf[rho * QROW + 32 * b + 16 * t + 8 * half]) = v;
-        }
-      if (lse && half == 0 && row_tok < cur.row_limit)
-        lse[int64_t(row_tok - q_row_base) * Hq + h] = (m_run + __log2f(l_tot)) * kLn2;
-      // Whole-row stores of this wave's rows: instruction s writes QRI rows (1 KB, 8 full
-      // cache lines), lane l chunk l % KCH of row 32 w + QRI s + l / KCH.
-#pragma unroll
-      for (int s2 = 0; s2 < DSTEPS; ++s2) {
-        const int rr = 32 * w + QRI * s2 + lane / KCH;
-        buf_store16(load16(&xbuf[rr * QROW + 8 * (lane % KCH)]), ro,
-                    uint32_t(((rr % TM) * q_stride + (rr / TM) * D + 8 * (lane % KCH)) * 2));
-      }
-    } else {
-      const int64_t sl = int64_t(cur.slot) * Hkv + g;
-      float* po = part_o + (sl * kRowsPerTile + rho) * D + 4 * half;
-#pragma unroll
-      for (int b = 0; b < DBLK; ++b)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<f32x4_t*>(po + 32 * b + 8 * j) =
-              f32x4_t{o[b][4 * j], o[b][4 * j + 1], o[b][4 * j + 2], o[b][4 * j + 3]};
-      if (half == 0) {
-        part_ml[(sl * kRowsPerTile + rho) * 2] = m_run;
-        part_ml[(sl * kRowsPerTile + rho) * 2 + 1] = l_tot;
-      }
-    }
-    __syncthreads();  // the freed buffer takes the tile after the next item's first
-    if (more) cur = nxt;
-  }
+  // Drain this wave's direct-to-LDS loads (zero-size ones past the end) before the workgroup exits.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 template <int D>
@@ -386,8 +568,9 @@ static hipError_t launch_attn_t(const AttnLaunch& a, hipStream_t stream) {
       hipError_t e = hipEventRecord(a.ev_start, stream);
       if (e != hipSuccess) return e;
     }
-    attn_fwd_kernel<D, G><<<grid, 256, 0, stream>>>(a.Q, a.K, a.V, a.O, a.lse, a.items, a.ranges, a.part_o, a.part_ml,
-                                                    a.num_q_heads, a.num_kv_heads, a.scale_log2, a.q_row_base);
+    attn_fwd_kernel<D, G, kFwdSlots><<<grid, 256, 0, stream>>>(a.Q, a.K, a.V, a.O, a.lse, a.items, a.ranges, a.part_o,
+                                                               a.part_ml, a.num_q_heads, a.num_kv_heads, a.scale_log2,
+                                                               a.q_row_base);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.ev_stop) {

@@ -76,8 +76,29 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
 __device__ __forceinline__ u32x4_t buf_load16(rsrc_t r, uint32_t byte_offset) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0);
 }
+__device__ __forceinline__ void buf_store8(u32x2_t v, rsrc_t r, uint32_t byte_offset) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_offset, 0, 0);
+}
 __device__ __forceinline__ void buf_store16(u32x4_t v, rsrc_t r, uint32_t byte_offset) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_offset, 0, 0);
+}
+// Direct-to-LDS buffer load (gfx950 buffer_load_dwordx4 ... lds): lane l's 16 bytes at
+// soffset + byte_offset go to LDS byte address lds_addr + 16 l (lds_addr: wave-uniform, from
+// lds_addr_of).  Loads whose soffset + byte_offset reaches the resource's size write zeros (the
+// scalar offset counts in the range check: checked on gfx950).  Completion is tracked by the vector-memory
+// counter only: the caller waits for it (s_waitcnt vmcnt) before anything reads that LDS.  The
+// instruction is issued from inline assembly so that the compiler does not add its own
+// conservative vector-memory waits before every later LDS read; it has no register result.
+__device__ __forceinline__ void buf_load16_lds(rsrc_t r, uint32_t lds_addr, uint32_t byte_offset,
+                                               uint32_t soffset = 0) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds_addr), "v"(byte_offset),
+               "s"(r), "s"(soffset)
+               : "memory", "m0");
+}
+// LDS byte address of a __shared__ object (for M0).
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  typedef __attribute__((address_space(3))) const void lds_void_t;
+  return uint32_t(uintptr_t((lds_void_t*)p));
 }
 // a.x * b.x + a.y * b.y + c for two packed bf16 pairs, fp32 accumulation.
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {

@@ -51,6 +51,10 @@ Error validate_dims(const br_dims* dims) {
   if (dims->total_tokens < 1) return fail(BR_ERR_INVALID_ARG, "total_tokens must be >= 1 (got %lld)", dims->total_tokens);
   if (dims->total_tokens > (int64_t(1) << 30))
     return fail(BR_ERR_UNSUPPORTED, "total_tokens %lld exceeds 2^30", dims->total_tokens);
+  // The attention kernel addresses K and V tiles with 32-bit byte offsets from the tensor base.
+  if (dims->total_tokens * dims->num_kv_heads * dims->head_dim * 2 > int64_t(0xFFFFFFFFll))
+    return fail(BR_ERR_UNSUPPORTED, "K and V must each be below 4 GiB (total_tokens %lld x %lld KV heads x head_dim %lld)",
+                dims->total_tokens, dims->num_kv_heads, dims->head_dim);
   return {};
 }
 

@@ -46,7 +46,9 @@
  *     bit patterns, contiguous, 16-byte aligned base pointers.
  *   - Supported: head_dim in {64, 128}; num_q_heads % num_kv_heads == 0 with
  *     G = num_q_heads / num_kv_heads in {1, 2, 4, 8}; query head h reads KV head h / G;
- *     num_q_heads * head_dim <= 65536 (512 query heads at d = 128); others: BR_ERR_UNSUPPORTED.
+ *     num_q_heads * head_dim <= 65536 (512 query heads at d = 128); total_tokens <= 2^30 and
+ *     total_tokens * num_kv_heads * head_dim * 2 < 2^32 (K and V each below 4 GiB: the attention
+ *     kernel addresses them with 32-bit offsets); others: BR_ERR_UNSUPPORTED.
  */
 #ifndef BLOCKRANK_H
 #define BLOCKRANK_H
