@@ -4,14 +4,16 @@ document scores and per-prompt ranking, behind the C ABI of include/blockrank.h.
 The Python layer only marshals arguments to libblockrank.so; all computation runs in its
 hand-written HIP kernels.
 """
-from ._lib import (BlockRankError, BrDims, EXPORTED, LIB_PATH, attn_bwd, attn_bwd_workspace_bytes, attn_fwd, attn_plan_items, attn_plan_schedule,
+from ._lib import (BlockRankError, BrDims, EXPORTED, LIB_PATH, NOALLOC_SCRATCH_BYTES, attn_bwd, attn_bwd_workspace_bytes, attn_fwd,
+                   attn_fwd_noalloc, attn_plan_items, attn_plan_schedule,
                    attn_routed, attn_routed_workspace_bytes,
                    attn_workspace_bytes, doc_scores, doc_scores_bwd, doc_scores_bwd_workspace_bytes, doc_scores_workspace_bytes,
                    infonce, load_library,
                    make_dims, query_attn, query_attn_workspace_bytes, rank_step, rank_workspace_bytes, rope, rope_positions, rope_signal,
                    rope_workspace_bytes, sort_docs, ssmax_scale, version)
 
-__all__ = ["BlockRankError", "BrDims", "EXPORTED", "LIB_PATH", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd", "attn_plan_items", "attn_plan_schedule",
+__all__ = ["BlockRankError", "BrDims", "EXPORTED", "LIB_PATH", "NOALLOC_SCRATCH_BYTES", "attn_bwd", "attn_bwd_workspace_bytes",
+           "attn_fwd", "attn_fwd_noalloc", "attn_plan_items", "attn_plan_schedule",
            "attn_routed", "attn_routed_workspace_bytes",
            "attn_workspace_bytes", "doc_scores", "doc_scores_bwd", "doc_scores_bwd_workspace_bytes",
            "doc_scores_workspace_bytes", "infonce", "load_library",

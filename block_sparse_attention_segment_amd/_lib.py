@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libblockrank.so")
 BR_OK, BR_ERR_INVALID_ARG, BR_ERR_UNSUPPORTED, BR_ERR_WORKSPACE, BR_ERR_HIP = range(5)
 
 # Symbols the header declares; the CPU test checks the library exports each of them.
-EXPORTED = ("br_attn_workspace_bytes", "br_attn_fwd", "br_attn_fwd_timed", "br_doc_scores_workspace_bytes", "br_doc_scores",
+EXPORTED = ("br_attn_workspace_bytes", "br_attn_fwd", "br_attn_fwd_timed", "br_attn_fwd_noalloc", "br_doc_scores_workspace_bytes", "br_doc_scores",
             "br_sort_docs", "br_rank_workspace_bytes", "br_rank_prompts", "br_rank_prompts_timed", "br_attn_plan_items", "br_attn_plan_schedule", "br_query_attn_workspace_bytes", "br_query_attn_fwd", "br_attn_routed_workspace_bytes", "br_attn_routed_fwd",
             "br_attn_bwd_workspace_bytes", "br_attn_bwd", "br_attn_bwd_plan_items",
             "br_infonce_workspace_bytes", "br_infonce", "br_doc_scores_bwd_workspace_bytes", "br_doc_scores_bwd",
@@ -61,6 +61,7 @@ def load_library() -> ctypes.CDLL:
         "br_attn_fwd": [dims_p, _P, _P, _P, _I32P, _I32P, _P, _P, ctypes.c_float, _P, ctypes.c_size_t, _P],
         "br_attn_fwd_timed": [dims_p, _P, _P, _P, _I32P, _I32P, _P, _P, ctypes.c_float, _P, ctypes.c_size_t, _P,
                               _P, _P],
+        "br_attn_fwd_noalloc": [dims_p, _P, _P, _P, _I32P, _I32P, _P, _P, ctypes.c_float, _P],
         "br_doc_scores_workspace_bytes": [dims_p, ctypes.c_int32, _I32P, _I32P, sz_p],
         "br_doc_scores": [dims_p, _P, ctypes.c_int32, _P, _I32P, _I32P, _P, _P, ctypes.c_float, _P,
                           ctypes.c_size_t, _P],
@@ -217,6 +218,33 @@ def attn_fwd(Q, K, V, segment_offsets, seg_ptr, out=None, lse=None, softmax_scal
                                  _ptr_i32(sp), out.data_ptr(), _dev_ptr(lse), float(softmax_scale),
                                  workspace.data_ptr(), workspace.numel(), _stream_handle(stream), ev0, ev1))
     return (out, lse) if lse is not None else out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # BR_NOALLOC_SCRATCH_BYTES in include/blockrank.h
+
+
+def attn_fwd_noalloc(Q, K, V, segment_offsets, seg_ptr, out, lse=None, softmax_scale: float = 0.0, stream=None):
+    """br_attn_fwd_noalloc: the attention with the library's own per-GPU workspace; the caller
+    passes every output (``out`` bf16 [T,Hq,d], optional ``lse`` fp32 [T,Hq]) and this wrapper
+    allocates nothing.  Calls that overlap on one GPU race (one shared workspace)."""
+    import torch
+    lib = load_library()
+    for name, t in (("Q", Q), ("K", K), ("V", V), ("out", out)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 3:
+            raise ValueError(f"{name} must be a contiguous 3-D bfloat16 CUDA tensor")
+    T, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    if K.shape != (T, Hkv, d) or V.shape != K.shape or out.shape != Q.shape:
+        raise ValueError("K and V must be [T, Hkv, d] and out [T, Hq, d], matching Q")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous()
+                            or tuple(lse.shape) != (T, Hq)):
+        raise ValueError("lse must be a contiguous float32 CUDA tensor [T, Hq]")
+    so, sp = _host_i32(segment_offsets), _host_i32(seg_ptr)
+    dims = make_dims(len(sp) - 1, Hq, Hkv, d, T)
+    _check(lib.br_attn_fwd_noalloc(ctypes.byref(dims), Q.data_ptr(), K.data_ptr(), V.data_ptr(), _ptr_i32(so),
+                                   _ptr_i32(sp), out.data_ptr(), _dev_ptr(lse), float(softmax_scale),
+                                   _stream_handle(stream)))
+    return out
 
 
 def attn_routed_workspace_bytes(dims: BrDims, segment_offsets, seg_ptr, keep_ptr, keep) -> int:

@@ -290,7 +290,7 @@ br_status check_attn_buffers(const void* Q, const void* K, const void* V, const 
 // addressed relative to token q_row_base.
 br_status run_attn(const br_dims& dims, br::AttnPlan& plan, const void* Q, const void* K, const void* V, void* out,
                    float* lse, float softmax_scale, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                   int q_row_base, hipEvent_t kernel_start, hipEvent_t kernel_stop) {
+                   int q_row_base, hipEvent_t kernel_start, hipEvent_t kernel_stop, bool pageable_upload = false) {
   if (!workspace || workspace_bytes < plan.total_bytes)
     return record(BR_ERR_WORKSPACE, "workspace is NULL or smaller than the workspace size query's " +
                                         std::to_string(plan.total_bytes) + " bytes");
@@ -308,8 +308,15 @@ br_status run_attn(const br_dims& dims, br::AttnPlan& plan, const void* Q, const
   if (!plan.merges.empty())
     std::memcpy(host.data() + plan.off_merges, plan.merges.data(), plan.merges.size() * sizeof(br::MergeItem));
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  br_status st = upload(ws, host.data(), host.size(), stream);
-  if (st != BR_OK) return st;
+  if (pageable_upload) {
+    // Straight from pageable host memory: the runtime has copied the source out before the call
+    // returns, and nothing is allocated here.
+    hipError_t ce = hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, stream);
+    if (ce != hipSuccess) return hip_fail(ce, "plan upload");
+  } else {
+    br_status st = upload(ws, host.data(), host.size(), stream);
+    if (st != BR_OK) return st;
+  }
 
   br::AttnLaunch a;
   a.Q = static_cast<const uint16_t*>(Q);
@@ -380,7 +387,59 @@ br_status run_rope(const br_dims& dims, const int32_t* seg_ptr, const br::RopePl
 }
 
 
+// Workspace of the allocation-free attention entry point: a file-scope device array (one copy
+// per GPU, held until the process ends).  Host code never uses the array's name as an address:
+// the device address comes from hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kNoAllocScratchBytes = size_t(BR_NOALLOC_SCRATCH_BYTES);
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t scratch_address(void** out) {
+  static std::mutex mu;
+  static std::vector<void*> per_device;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if (size_t(dev) >= per_device.size()) per_device.resize(size_t(dev) + 1, nullptr);
+  if (!per_device[size_t(dev)]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    per_device[size_t(dev)] = p;
+  }
+  *out = per_device[size_t(dev)];
+  return hipSuccess;
+}
+
 }  // namespace
+
+extern "C" {
+
+br_status br_attn_fwd_noalloc(const br_dims* dims, const void* Q, const void* K, const void* V,
+                              const int32_t* segment_offsets, const int32_t* seg_ptr, void* out, float* lse,
+                              float softmax_scale, hipStream_t stream) {
+  return guarded([&]() -> br_status {
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    br_status st = check_attn_buffers(Q, K, V, out, lse, softmax_scale);
+    if (st != BR_OK) return st;
+    br::AttnPlan plan;
+    e = br::build_attn_plan(*dims, segment_offsets, seg_ptr, &plan);
+    if (!e.ok()) return record(e);
+    if (plan.total_bytes > kNoAllocScratchBytes)
+      return record(BR_ERR_UNSUPPORTED, "this segment table needs " + std::to_string(plan.total_bytes) +
+                                            " bytes of workspace; br_attn_fwd_noalloc has " +
+                                            std::to_string(kNoAllocScratchBytes) + " (use br_attn_fwd)");
+    void* ws = nullptr;
+    hipError_t he = scratch_address(&ws);
+    if (he != hipSuccess) return hip_fail(he, "hipGetSymbolAddress(scratch)");
+    return run_attn(*dims, plan, Q, K, V, out, lse, softmax_scale, ws, kNoAllocScratchBytes, stream, 0, nullptr,
+                    nullptr, /*pageable_upload=*/true);
+  });
+}
+
+}  // extern "C"
 
 extern "C" {
 

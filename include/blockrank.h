@@ -121,6 +121,22 @@ br_status br_attn_fwd_timed(const br_dims* dims, const void* Q, const void* K, c
                             hipEvent_t kernel_stop);
 
 /*
+ * br_attn_fwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same computation, bit for bit,
+ * with no workspace argument.  Its workspace is a device array inside the library of
+ * BR_NOALLOC_SCRATCH_BYTES bytes per GPU, held until the process ends; segment tables whose
+ * br_attn_workspace_bytes exceeds it return BR_ERR_UNSUPPORTED.  The plan is copied from
+ * pageable host memory with hipMemcpyAsync; nothing is allocated (no hipMalloc, hipFree or
+ * pinned staging).  Every call on a GPU uses that GPU's one array: calls that overlap on one
+ * GPU (two streams, or a second host thread) race and must be serialised by the caller.
+ * Other arguments, rules and errors as br_attn_fwd.
+ */
+#define BR_NOALLOC_SCRATCH_BYTES (32u << 20)
+br_status br_attn_fwd_noalloc(const br_dims* dims, const void* Q, const void* K, const void* V,
+                              const int32_t* segment_offsets, const int32_t* seg_ptr, void* out,
+                              float* lse, float softmax_scale, hipStream_t stream);
+
+/*
  * Document spans (host int32).  Prompt b owns doc_offsets[doc_ptr[b] .. doc_ptr[b+1]),
  * N_b + 1 increasing absolute token offsets (normally segment_offsets[1 .. N_b+2) of that
  * prompt); document k of prompt b is [doc_offsets[doc_ptr[b]+k], doc_offsets[doc_ptr[b]+k+1]).

@@ -456,3 +456,13 @@ def test_rank_workspace_and_rejects_before_any_hip_call():
     rc = lib.br_rank_prompts(ctypes.byref(dims2), f, f, f, f, 1, p(big[0]), p(big[1]), p(big[2]), p(big[3]), f, None,
                              f, None, f, 0.0, f, nb.value, None)
     assert rc == UNS                           # more documents than the sort takes
+
+
+def test_noalloc_scratch_size_matches_header():
+    """The binding's BR_NOALLOC_SCRATCH_BYTES copy equals the header's definition."""
+    import os
+    import re
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "blockrank.h")).read()
+    m = re.search(r"#define BR_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert m, "BR_NOALLOC_SCRATCH_BYTES not found"
+    assert br.NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
