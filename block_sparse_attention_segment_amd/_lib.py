@@ -7,6 +7,8 @@ library is missing, loading raises: there is no fallback implementation.
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import os
 from typing import Optional, Tuple
 
@@ -148,6 +150,25 @@ def _stream_handle(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
+def _on_stream(fn):
+    """Run ``fn`` with its ``stream`` argument (when given) as torch's current stream, so that the
+    outputs, workspaces and zero fills it allocates belong to, and are ordered on, the stream its
+    kernels run on: torch's caching allocator then reuses a freed workspace only for later work on
+    that same stream."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        stream = sig.bind_partial(*args, **kwargs).arguments.get("stream")
+        if stream is None:
+            return fn(*args, **kwargs)
+        import torch
+        with torch.cuda.stream(stream):
+            return fn(*args, **kwargs)
+    wrapper.runs_on_its_stream = True
+    return wrapper
+
+
 def attn_workspace_bytes(dims: BrDims, segment_offsets, seg_ptr) -> int:
     lib = load_library()
     so, sp = _host_i32(segment_offsets), _host_i32(seg_ptr)
@@ -185,6 +206,7 @@ def attn_plan_schedule(dims: BrDims, segment_offsets, seg_ptr, workgroups: int) 
     return items[:int(n.value)], ranges
 
 
+@_on_stream
 def attn_fwd(Q, K, V, segment_offsets, seg_ptr, out=None, lse=None, softmax_scale: float = 0.0,
              workspace=None, stream=None, kernel_events=None):
     """Block-sparse prefill attention.  Q [T,Hq,d], K/V [T,Hkv,d] bf16 CUDA tensors.
@@ -223,6 +245,7 @@ def attn_fwd(Q, K, V, segment_offsets, seg_ptr, out=None, lse=None, softmax_scal
 NOALLOC_SCRATCH_BYTES = 32 << 20  # BR_NOALLOC_SCRATCH_BYTES in include/blockrank.h
 
 
+@_on_stream
 def attn_fwd_noalloc(Q, K, V, segment_offsets, seg_ptr, out, lse=None, softmax_scale: float = 0.0, stream=None):
     """br_attn_fwd_noalloc: the attention with the library's own per-GPU workspace; the caller
     passes every output (``out`` bf16 [T,Hq,d], optional ``lse`` fp32 [T,Hq]) and this wrapper
@@ -256,6 +279,7 @@ def attn_routed_workspace_bytes(dims: BrDims, segment_offsets, seg_ptr, keep_ptr
     return int(out.value)
 
 
+@_on_stream
 def attn_routed(Q, K, V, segment_offsets, seg_ptr, keep_ptr, keep, out=None, lse=None, softmax_scale: float = 0.0,
                 workspace=None, stream=None):
     """Top-B routed attention: prompt b keeps documents keep[keep_ptr[b]:keep_ptr[b+1]] (local
@@ -310,6 +334,7 @@ def attn_bwd_plan_items(dims: BrDims, segment_offsets, seg_ptr):
     return items[:n.value], int(slots.value)
 
 
+@_on_stream
 def attn_bwd(Q, K, V, O, dO, lse, segment_offsets, seg_ptr, softmax_scale: float = 0.0, dQ=None, dK=None, dV=None,
              workspace=None, stream=None):
     """Gradients (dQ [T,Hq,d], dK, dV [T,Hkv,d], fp32) of the block-sparse attention for the upstream
@@ -338,6 +363,7 @@ def attn_bwd(Q, K, V, O, dO, lse, segment_offsets, seg_ptr, softmax_scale: float
     return dQ, dK, dV
 
 
+@_on_stream
 def infonce(scores, doc_ptr, gold, tau: float = 0.05, loss=None, dscores=None, workspace=None, stream=None):
     """Per-prompt InfoNCE loss [B] and its gradient with respect to the scores [sum N_b] (fp32)."""
     import torch
@@ -368,6 +394,7 @@ def doc_scores_bwd_workspace_bytes(dims: BrDims, n_signal: int, doc_offsets, doc
     return int(out.value)
 
 
+@_on_stream
 def doc_scores_bwd(Q_S, K, doc_offsets, doc_ptr, dscores, softmax_scale: float = 0.0, dQ_S=None, dK=None,
                    accumulate: bool = False, workspace=None, stream=None):
     """Gradient of sum_k dscores_k s_k through the readout: dQ_S [B,S,Hq,d] and dK [T,Hkv,d] (fp32).
@@ -425,6 +452,7 @@ def _check_bf16(name, t, ndim):
         raise ValueError(f"{name} must be a contiguous {ndim}-D bfloat16 CUDA tensor")
 
 
+@_on_stream
 def rope(Q, K, segment_offsets, seg_ptr, rope_theta: float = 10000.0, query_pos0: int = 8192,
          docs_after_instruction: bool = True, interleaved: bool = False, Q_out=None, K_out=None,
          inplace: bool = False, workspace=None, stream=None):
@@ -459,6 +487,7 @@ def rope(Q, K, segment_offsets, seg_ptr, rope_theta: float = 10000.0, query_pos0
     return Q_out, K_out
 
 
+@_on_stream
 def rope_signal(Q_S, segment_offsets, seg_ptr, rope_theta: float = 10000.0, query_pos0: int = 8192,
                 interleaved: bool = False, out=None, inplace: bool = False, num_kv_heads: Optional[int] = None,
                 workspace=None, stream=None):
@@ -490,6 +519,7 @@ def query_attn_workspace_bytes(dims: BrDims, corpus_len: int, query_offsets) -> 
     return int(out.value)
 
 
+@_on_stream
 def query_attn(Q, K, V, corpus_len: int, query_offsets, out=None, lse=None, softmax_scale: float = 0.0,
                workspace=None, stream=None):
     """Query-only attention over a cached corpus.  K/V [T,Hkv,d] hold the corpus [0, corpus_len)
@@ -530,6 +560,7 @@ def doc_scores_workspace_bytes(dims: BrDims, n_signal: int, doc_offsets, doc_ptr
     return int(out.value)
 
 
+@_on_stream
 def doc_scores(Q_S, K, doc_offsets, doc_ptr, head_scores: bool = False, softmax_scale: float = 0.0,
                scores=None, workspace=None, stream=None):
     """Attention-mass scores.  Q_S [B,S,Hq,d], K [T,Hkv,d] bf16 CUDA tensors.
@@ -560,6 +591,7 @@ def doc_scores(Q_S, K, doc_offsets, doc_ptr, head_scores: bool = False, softmax_
     return (scores, hs) if head_scores else scores
 
 
+@_on_stream
 def sort_docs(scores, doc_ptr, order=None, stream=None):
     """Per-prompt local document indices by descending score (ties: lower index)."""
     import torch
@@ -583,6 +615,7 @@ def rank_workspace_bytes(dims: BrDims, segment_offsets, seg_ptr, n_signal: int, 
     return int(out.value)
 
 
+@_on_stream
 def rank_step(Q, K, V, Q_S, segment_offsets, seg_ptr, doc_offsets, doc_ptr, softmax_scale: float = 0.0, out=None,
               lse=None, scores=None, head_scores=None, order=None, workspace=None, stream=None, kernel_events=None):
     """The whole hot path in one library call (br_rank_prompts): attention output, document scores

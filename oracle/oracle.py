@@ -347,6 +347,75 @@ def attn_bwd(Q, K, V, dO, segment_offsets, seg_ptr, scale: Optional[float] = Non
     return dQ, dK, dV
 
 
+def attn_bwd_sampled(Q, K, V, dO, segment_offsets, seg_ptr, rows=(), keys=(), scale: Optional[float] = None,
+                     kv_heads=None, row_block: int = 256):
+    """Selected entries of attn_bwd's gradients, for prompts too long for the dense per-prompt
+    evaluation: dQ at the given rows, dK and dV at the given keys.
+
+    The per-row formulas are attn_bwd's: for row i and query head h (KV head g),
+        P_i  = softmax over the keys row i may read of scale * Q_i K^T
+        dP_i = dO_i V^T,   dS_i = P_i * (dP_i - sum_j P_ij dP_ij)
+        dQ_i = scale * dS_i K,   dK_j += scale * dS_ij Q_i,   dV_j += P_ij dO_i
+    Only the rows that matter are evaluated: the selected rows, and every row that may read a
+    selected key (each such row's softmax still runs over all of its keys).  Rows are taken in
+    blocks of one segment, each block against the keys any of its rows may read.
+    kv_heads: KV heads to evaluate (default all); the outputs of other heads stay zero.
+    Returns (dQ [R,Hq,d], dK [Kn,Hkv,d], dV [Kn,Hkv,d]) in float64, in the order given."""
+    Kf, Vf = to_f64(K), to_f64(V)
+    Hkv, d = Kf.shape[1], Kf.shape[2]
+    Hq = np.asarray(Q).shape[1]
+    sc = _scale(d, scale)
+    tables = token_tables(segment_offsets, seg_ptr)
+    prompt, seg, _ = tables
+    so = np.asarray(segment_offsets, dtype=np.int64); sp = np.asarray(seg_ptr, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+    keys = np.asarray(keys, dtype=np.int64).reshape(-1)
+    heads = [h for h in range(Hq) if kv_heads is None or kv_head(h, Hq, Hkv) in set(kv_heads)]
+    dQ = np.zeros((len(rows), Hq, d)); dK = np.zeros((len(keys), Hkv, d)); dV = np.zeros((len(keys), Hkv, d))
+    # rows that may read a selected key
+    readers = [rows]
+    for b in np.unique(prompt[keys]):
+        pa, pe = int(so[sp[b]]), int(so[sp[b + 1] - 1])
+        idx = np.arange(pa, pe)
+        kb = np.unique(keys[prompt[keys] == b])
+        hit = np.zeros(len(idx), dtype=bool)
+        for c0 in range(0, len(kb), 64):
+            hit |= allowed(idx[:, None], kb[None, c0:c0 + 64], tables).any(axis=1)
+        readers.append(idx[hit])
+    ev = np.unique(np.concatenate(readers))
+    order = np.argsort(seg[ev], kind="stable")
+    starts = [0] + [n for n in range(1, len(order)) if seg[ev[order[n]]] != seg[ev[order[n - 1]]]]
+    starts.append(len(order))
+    for a_, e_ in zip(starts[:-1], starts[1:]):
+        for c0 in range(a_, e_, row_block):
+            r = ev[order[c0:min(c0 + row_block, e_)]]
+            b = int(prompt[r[0]])
+            pa, pe = int(so[sp[b]]), int(so[sp[b + 1] - 1])
+            cand = np.arange(pa, pe)
+            m = allowed(r[:, None], cand[None, :], tables)
+            cols = cand[m.any(axis=0)]
+            mc = m[:, m.any(axis=0)]
+            qr, dor = to_f64(np.asarray(Q)[r]), to_f64(np.asarray(dO)[r])
+            # output slots: selected rows in this block, selected keys among its columns
+            in_block = set(r.tolist())
+            q_out = [(n, int(np.searchsorted(r, rows[n]))) for n in range(len(rows)) if int(rows[n]) in in_block]
+            colpos = {int(c): n for n, c in enumerate(cols)}
+            k_out = [(n, colpos[int(keys[n])]) for n in range(len(keys)) if int(keys[n]) in colpos]
+            for h in heads:
+                g = kv_head(h, Hq, Hkv)
+                s = np.where(mc, (qr[:, h] @ Kf[cols, g].T) * sc, -np.inf)
+                P = np.exp(s - s.max(axis=1, keepdims=True))
+                P /= P.sum(axis=1, keepdims=True)
+                dP = dor[:, h] @ Vf[cols, g].T
+                dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+                for n, i in q_out:
+                    dQ[n, h] = sc * (dS[i] @ Kf[cols, g])
+                for n, c in k_out:
+                    dK[n, g] += sc * (dS[:, c] @ qr[:, h])
+                    dV[n, g] += P[:, c] @ dor[:, h]
+    return dQ, dK, dV
+
+
 def infonce(scores, doc_ptr, gold, tau: float = 0.05):
     """[BR] auxiliary loss per prompt: L_b = -log(exp(s_gold / tau) / sum_k exp(s_k / tau)) over the
     prompt's documents; gold holds each prompt's local index of the relevant document.

@@ -64,6 +64,8 @@ def pin_closed_form_counts(orc):
         assert want_blk == ref_blk, (prompts, want_blk, ref_blk)
         assert blk == ref_blk, (prompts, blk, ref_blk)
         assert exact == ref_blk - diag, (prompts, exact, ref_blk - diag)
+        # the (causal, whole-diagonal) pair of counts, in that order
+        assert orc.allowed_pair_counts(seg, sp) == (ref_blk - diag, ref_blk), prompts
 
 
 def pin_worked_example(orc):
@@ -677,6 +679,46 @@ def pin_attn_bwd_autograd(orc):
     assert np.allclose(v.grad.permute(1, 0, 2).numpy(), dV, atol=1e-10)
 
 
+def _autograd_grads(orc, w, Q, K, V, dO, G):
+    """dQ, dK, dV from torch's autograd through scaled_dot_product_attention (float64, CPU) with
+    the prompt's boolean mask, KV heads repeated G times."""
+    tables = orc.token_tables(w.segment_offsets, w.seg_ptr)
+    idx = np.arange(w.total_tokens)
+    mask = torch.from_numpy(orc.allowed(idx[:, None], idx[None, :], tables))
+    q = torch.from_numpy(Q).permute(1, 0, 2).contiguous().requires_grad_(True)
+    k = torch.from_numpy(K).permute(1, 0, 2).contiguous().requires_grad_(True)
+    v = torch.from_numpy(V).permute(1, 0, 2).contiguous().requires_grad_(True)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        q, k.repeat_interleave(G, dim=0), v.repeat_interleave(G, dim=0), attn_mask=mask)
+    out.backward(torch.from_numpy(dO).permute(1, 0, 2))
+    return (x.grad.permute(1, 0, 2).numpy() for x in (q, k, v))
+
+
+def pin_attn_bwd_sampled(orc):
+    """The sampled backward (selected rows' dQ, selected keys' dK and dV) against torch's autograd
+    at those entries: rows and keys of every kind, repeats, several row blocks per segment, and
+    a KV-head subset whose other heads stay zero."""
+    rng = random.Random(77)
+    prompts = random_prompts(rng, batch=2, p_max=9, n_max=4, l_max=11, q_max=7)
+    w = workloads.make_custom(prompts, 4, 2, 8, 1, 4077)
+    nrng = np.random.default_rng(77)
+    T = w.total_tokens
+    Q, K, V = (nrng.standard_normal((T, h, 8)) for h in (4, 2, 2))
+    dO = nrng.standard_normal((T, 4, 8))
+    gQ, gK, gV = _autograd_grads(orc, w, Q, K, V, dO, 2)
+    rows = np.concatenate([nrng.integers(0, T, 12), [0, T - 1, 5, 5]])
+    keys = np.concatenate([nrng.integers(0, T, 12), [0, T - 1, 3, 3]])
+    for rb in (256, 3):
+        dQ, dK, dV = orc.attn_bwd_sampled(Q, K, V, dO, w.segment_offsets, w.seg_ptr, rows, keys, row_block=rb)
+        assert np.allclose(dQ, gQ[rows], atol=1e-10), rb
+        assert np.allclose(dK, gK[keys], atol=1e-10), rb
+        assert np.allclose(dV, gV[keys], atol=1e-10), rb
+    dQ, dK, dV = orc.attn_bwd_sampled(Q, K, V, dO, w.segment_offsets, w.seg_ptr, rows, keys, kv_heads=[1])
+    assert np.allclose(dQ[:, 2:], gQ[rows][:, 2:], atol=1e-10) and not dQ[:, :2].any()
+    assert np.allclose(dK[:, 1], gK[keys][:, 1], atol=1e-10) and not dK[:, 0].any()
+    assert np.allclose(dV[:, 1], gV[keys][:, 1], atol=1e-10) and not dV[:, 0].any()
+
+
 def pin_infonce(orc):
     """Equal scores give loss ln N and gradient (1/N - onehot)/tau; the gradient sums to zero per
     prompt; it matches central differences of the loss; the loss is torch's cross entropy of the
@@ -750,6 +792,7 @@ ALL_PINS = [
     pin_routing_keep_all, pin_routing_is_compaction, pin_routing_ignores_dropped,
     pin_ssmax_gold_weight, pin_ssmax_readout_gold_mass, pin_rope_positions_golden, pin_rope_rotation_values,
     pin_rope_relative_position, pin_rope_permutation_invariance, pin_signal_positions,
-    pin_attn_bwd_finite_differences, pin_attn_bwd_identities, pin_attn_bwd_autograd, pin_infonce,
+    pin_attn_bwd_finite_differences, pin_attn_bwd_identities, pin_attn_bwd_autograd, pin_attn_bwd_sampled,
+    pin_infonce,
     pin_readout_bwd_finite_differences, pin_readout_bwd_identities,
 ]

@@ -466,3 +466,33 @@ def test_noalloc_scratch_size_matches_header():
     m = re.search(r"#define BR_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
     assert m, "BR_NOALLOC_SCRATCH_BYTES not found"
     assert br.NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+
+
+def test_binding_functions_run_on_their_stream(monkeypatch):
+    """Every binding call that takes a ``stream`` makes it torch's current stream before it
+    allocates outputs or workspace, so the caching allocator orders them on the kernels' stream."""
+    import contextlib
+    import inspect
+    import torch
+    from block_sparse_attention_segment_amd import _lib
+    takes_stream = [n for n, f in inspect.getmembers(_lib, inspect.isfunction)
+                    if not n.startswith("_") and "stream" in inspect.signature(f).parameters]
+    assert len(takes_stream) >= 10, takes_stream
+    for n in takes_stream:
+        assert getattr(getattr(_lib, n), "runs_on_its_stream", False), n
+    entered = []
+
+    @contextlib.contextmanager
+    def fake_stream(s):
+        entered.append(s)
+        yield
+
+    monkeypatch.setattr(torch.cuda, "stream", fake_stream)
+    marker = object()
+    x = torch.zeros((4, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):  # host tensors are refused inside, with the stream current
+        br.attn_fwd(x, x, x, [0, 4], [0, 1], stream=marker)
+    assert entered == [marker]
+    with pytest.raises(ValueError):
+        br.attn_fwd(x, x, x, [0, 4], [0, 1])
+    assert entered == [marker]

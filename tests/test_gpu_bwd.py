@@ -107,6 +107,56 @@ def test_attn_bwd_long_prompt_identities():
     assert torch.isfinite(dQ).all() and torch.isfinite(dK).all() and torch.isfinite(dV).all()
 
 
+def _long_samples(w):
+    """Rows and keys of every kind in the long prompt: instruction, documents 0, 250 and 499 (first,
+    second, middle and last token), and query tokens."""
+    so = np.asarray(w.segment_offsets)
+    T = w.total_tokens
+    instr = [0, 1, int(so[1]) // 2, int(so[1]) - 1]
+    docs = []
+    for k in (0, 250, 499):
+        a, e = int(so[1 + k]), int(so[2 + k])
+        docs += [a, a + 1, (a + e) // 2, e - 1]
+    query = [int(so[-2]), int(so[-2]) + 1, T - 9, T - 1]
+    return instr, docs, query
+
+
+@pytest.fixture(scope="module")
+def long_bwd():
+    w = workloads.make("long", 0)
+    log(f"[attn bwd long samples] T={w.total_tokens}: GPU forward + backward")
+    dQ, dK, dV, dO_bits = run_case(w, 11)
+    return w, dQ.cpu(), dK.cpu(), dV.cpu(), dO_bits
+
+
+def test_attn_bwd_long_prompt_sampled_rows_and_document_keys(long_bwd):
+    """The long ranking prompt at full size: dQ at instruction, document and query rows and dK, dV
+    at document and query keys, element by element against the oracle's sampled backward (each
+    key's gradient summed over every row that reads it, the query rows included)."""
+    w, dQ, dK, dV, dO_bits = long_bwd
+    instr, docs, query = _long_samples(w)
+    rows = instr + docs + query
+    keys = docs + query
+    log(f"  oracle: {len(rows)} rows, {len(keys)} keys, all heads")
+    rQ, rK, rV = orc.attn_bwd_sampled(w.Q, w.K, w.V, dO_bits, w.segment_offsets, w.seg_ptr, rows, keys)
+    check_grad(dQ[rows], rQ, "dQ rows")
+    check_grad(dK[keys], rK, "dK document/query keys")
+    check_grad(dV[keys], rV, "dV document/query keys")
+
+
+def test_attn_bwd_long_prompt_instruction_keys(long_bwd):
+    """dK and dV of instruction keys, which every one of the ~100k rows reads (the GPU sums them over
+    split row ranges), for two KV heads against the oracle's sampled backward."""
+    w, dQ, dK, dV, dO_bits = long_bwd
+    instr, _, _ = _long_samples(w)
+    heads = [0, 5]
+    log(f"  oracle: instruction keys {instr}, KV heads {heads}, every reading row")
+    _, rK, rV = orc.attn_bwd_sampled(w.Q, w.K, w.V, dO_bits, w.segment_offsets, w.seg_ptr, [], instr,
+                                     kv_heads=heads)
+    check_grad(dK[instr][:, heads], rK[:, heads], "dK instruction keys")
+    check_grad(dV[instr][:, heads], rV[:, heads], "dV instruction keys")
+
+
 def test_attn_bwd_edge_shapes():
     """Degenerate tables: no instruction, one-token documents and queries, a single document, and
     the largest group size."""

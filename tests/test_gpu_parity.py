@@ -223,6 +223,33 @@ def test_rank_step_side_stream_from_two_host_threads():
             assert torch.equal(out, a_out) and torch.equal(s, a_s) and torch.equal(o, a_o)
 
 
+def test_calls_on_a_stream_that_is_not_current():
+    """Calls given a stream that is not torch's current one, with outputs and workspace left to
+    the binding, equal the calls on the current stream bit for bit, also when the default-stream
+    memory they would otherwise reuse is being rewritten meanwhile."""
+    w = workloads.make("worked", 0)
+    dev = upload(w)
+    log(f"[gpu] non-current stream: T={w.total_tokens}")
+    a_out, a_lse = br.attn_fwd(dev["Q"], dev["K"], dev["V"], w.segment_offsets, w.seg_ptr, lse=True)
+    a_s = br.doc_scores(dev["Q_S"], dev["K"], w.doc_offsets, w.doc_ptr)
+    a_o = br.sort_docs(a_s, w.doc_ptr)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    got = []
+    for _ in range(3):
+        out, lse = br.attn_fwd(dev["Q"], dev["K"], dev["V"], w.segment_offsets, w.seg_ptr, lse=True, stream=side)
+        s = br.doc_scores(dev["Q_S"], dev["K"], w.doc_offsets, w.doc_ptr, stream=side)
+        o = br.sort_docs(s, w.doc_ptr, stream=side)
+        got.append((out, lse, s, o))
+        # default-stream work that allocates and writes while the side stream may still run
+        junk = torch.full((4 << 20,), 7.0, device="cuda")
+        del junk
+    side.synchronize()
+    for out, lse, s, o in got:
+        assert torch.equal(out, a_out) and torch.equal(lse, a_lse)
+        assert torch.equal(s, a_s) and torch.equal(o, a_o)
+
+
 def test_rank_step_plan_cache_tells_tables_apart():
     """The ranking step keeps its last few plans and reuses one when a call's dimensions and host
     tables are equal element by element.  Tables of the same size that differ only in document

@@ -207,6 +207,7 @@ def _routing_drops_everything(Q, K, V, so, sp, keep_ptr, keep, rows, scale=None)
 
 
 _real_attn_routed = orc.attn_routed
+_real_bwd_sampled = orc.attn_bwd_sampled
 
 
 
@@ -360,6 +361,24 @@ def _readout_bwd_sum_heads(Q_S, K, doc_offsets, doc_ptr, dscores, scale=None):
     return dQs * Hq, dK * Hq
 
 
+def _bwd_sampled_own_segment_readers(Q, K, V, dO, so, sp, rows=(), keys=(), scale=None, kv_heads=None,
+                                     row_block=256):
+    """dK and dV of a key summed over the rows of its own segment only (the query rows, and for an
+    instruction key the document rows, forgotten)"""
+    tables = orc.token_tables(so, sp)
+    seg = tables[1]
+    keys = np.asarray(keys, dtype=np.int64).reshape(-1)
+    dQ = _real_bwd_sampled(Q, K, V, dO, so, sp, rows, (), scale, kv_heads, row_block)[0]
+    Kf, Vf = orc.to_f64(K), orc.to_f64(V)
+    dK, dV = np.zeros((len(keys),) + Kf.shape[1:]), np.zeros((len(keys),) + Vf.shape[1:])
+    for n, j in enumerate(keys):
+        own = np.flatnonzero(seg == seg[j])
+        _, full_k, full_v = orc.attn_bwd(Q, K, V, np.where(np.isin(np.arange(len(seg)), own)[:, None, None], dO, 0.0),
+                                         so, sp, scale)
+        dK[n], dV[n] = full_k[j], full_v[j]
+    return dQ, dK, dV
+
+
 MUTATIONS = {
     "mask_no_causal": ("allowed", _no_causal),
     "mask_docs_skip_prefix": ("allowed", _docs_skip_prefix),
@@ -393,6 +412,7 @@ MUTATIONS = {
     "attn_bwd_no_centering": ("attn_bwd", _attn_bwd_no_centering),
     "attn_bwd_first_head_only": ("attn_bwd", _attn_bwd_first_head_only),
     "attn_bwd_dk_unscaled": ("attn_bwd", _attn_bwd_dk_unscaled),
+    "bwd_sampled_own_segment_readers": ("attn_bwd_sampled", _bwd_sampled_own_segment_readers),
     "infonce_sign": ("infonce", _infonce_sign),
     "infonce_no_tau": ("infonce", _infonce_no_tau),
     "readout_bwd_no_centering": ("doc_scores_bwd", _readout_bwd_no_centering),
