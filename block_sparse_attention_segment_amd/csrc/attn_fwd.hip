@@ -12,7 +12,10 @@
 //
 // Work item = 128 (token, head) rows: TM = 128 / G consecutive tokens of the G query heads
 // that share one KV head (grouped-query packing), so each K/V tile staged in LDS serves G
-// heads.  Wave w owns 32 rows.  Keys are visited in tiles of 32:
+// heads.  Rows are token-major (row 32 w + n of wave w is token (32 w + n) / G, head
+// (32 w + n) % G), so wave w owns 32 / G whole tokens; a wave whose tokens all lie past an
+// item's last token (the short last row tile of a document) skips that item's arithmetic.
+// Keys are visited in tiles of 32:
 //   S^T = K Q^T   v_mfma_f32_32x32x16_bf16 with keys on M and query rows on N, so each lane
 //                 holds one query row and 16 of the tile's keys; the row max needs one
 //                 cross-half exchange (v_permlane32_swap);
@@ -31,6 +34,9 @@
 // barrier per tile publishes them.  The next item's Q fragments are loaded into registers while
 // the current item runs.  Loads use buffer resources sized to the valid rows: rows past a range
 // end read as zero, and output rows past a tile's last token are dropped by the hardware.
+// Output rows are staged through the wave's own part of the Q buffer (between reading one
+// item's Q fragments and loading the next item's rows) so each store writes whole 128-byte
+// lines: stores of 32 bytes per row were measured to cost about a sixth of the kernel time.
 //
 // LDS layouts (16-byte units, XOR-swizzled instead of padded, because a direct-to-LDS load
 // fills 1 KB of consecutive LDS per wave instruction):
@@ -150,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, half = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
   const int rho = w * 32 + n;  // this lane's row within the item
-  const int hh = rho / TM, tt = rho % TM;
+  const int tt = rho / G, hh = rho % G;  // token-major: a token's G heads are adjacent rows
   const int h = g * G + hh;
   const int q_stride = Hq * D, kv_stride = Hkv * D;  // elements between consecutive tokens
 
@@ -191,16 +197,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
   // valid keys of the tile (1..32); flags 1 causal range, 2 first tile of its item, 4 last tile
   // of its item.  Items past it_end are "no tile": nothing to read, and they count as one-tile
   // items so that the stages around them reset cleanly.
-  constexpr int F_CAUSAL = 1, F_FIRST = 2, F_LAST = 4, IT_SHIFT = 9;
+  constexpr int F_CAUSAL = 1, F_FIRST = 2, F_LAST = 4, F_IDLE = 512, IT_SHIFT = 10;
   auto code_it = [](int code) { return code >> IT_SHIFT; };
   auto code_keys = [](int code) { return (code >> 3) & 63; };
   auto n_tiles = [](int a0, int a1) { return a1 > a0 ? (a1 - a0 + BN - 1) / BN : 0; };
   // Lead cursor: item c_it (its key ranges and first row cached), tile c_t of c_nt (c_na unmasked).
-  int c_it = it_begin, c_t = 0, c_a0, c_a1, c_b0, c_b1, c_na, c_nt, c_row0;
+  int c_it = it_begin, c_t = 0, c_a0, c_a1, c_b0, c_b1, c_na, c_nt, c_row0, c_idle;
+  const int w_tok0 = 32 * w / G;  // first token of this wave's rows
   auto load_item = [&]() {
     if (c_it < it_end) {
       const AttnItem it = items[c_it];
       c_row0 = it.row0;
+      c_idle = w_tok0 >= it.row_limit - it.row0 ? F_IDLE : 0;
       c_a0 = it.a_start;
       c_a1 = it.a_end;
       c_b0 = it.b_start;
@@ -213,13 +221,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
   auto take = [&](int& start, int& code, int& row0) {
     if (c_it >= it_end) {
       start = row0 = 0;
-      code = (it_end << IT_SHIFT) | F_FIRST | F_LAST;
+      code = (it_end << IT_SHIFT) | F_FIRST | F_LAST | F_IDLE;
       return;
     }
     const bool causal = c_t >= c_na;
     start = causal ? c_b0 + (c_t - c_na) * BN : c_a0 + c_t * BN;
     const int keys = min(BN, (causal ? c_b1 : c_a1) - start);
-    code = (c_it << IT_SHIFT) | (keys << 3) | (causal ? F_CAUSAL : 0) | (c_t == 0 ? F_FIRST : 0) |
+    code = (c_it << IT_SHIFT) | (keys << 3) | c_idle | (causal ? F_CAUSAL : 0) | (c_t == 0 ? F_FIRST : 0) |
            (c_t + 1 == c_nt ? F_LAST : 0);
     row0 = c_row0;
     if (++c_t == c_nt) {
@@ -264,22 +272,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
   // permutation of the K fragments).  Each wave reads back only rows it loaded itself, so its own
   // vector-memory wait suffices and no barrier is involved.
   u32x4_t qf[DSTEPS];
+  // Per-lane source offsets of the Q loads: DSTEPS instructions of KPI rows cover the wave's 32 rows.
+  uint32_t qdma[DSTEPS];
+#pragma unroll
+  for (int i = 0; i < DSTEPS; ++i) {
+    const int rq = KPI * i + lane / UPR, u = lane % UPR, rr = 32 * w + rq;
+    qdma[i] = uint32_t(((rr / G) * q_stride + (rr % G) * D) * 2 + 16 * (u ^ swz_k(rq)));
+  }
   auto issue_q = [&](int it) {
     rsrc_t r = make_rsrc(Q, 0);
     if (it < it_end) {
       const int2 rr = *reinterpret_cast<const int2*>(&items[it].row0);
       r = row_rsrc(Q, rr.x, rr.y);
     }
-    // Per-lane offsets are formed here (the opaque copy of the lane index keeps the compiler
-    // from hoisting them into registers that stay live across the whole loop).
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int i = 0; i < DSTEPS; ++i) {  // DSTEPS instructions of KPI rows cover the wave's 32 rows
-      const int rq = KPI * i + ln / UPR, u = ln % UPR, rr = 32 * w + rq;
-      const uint32_t off = uint32_t(((rr % TM) * q_stride + (rr / TM) * D) * 2 + 16 * (u ^ swz_k(rq)));
-      buf_load16_lds(r, q_lds + 1024 * i, off);
-    }
+    for (int i = 0; i < DSTEPS; ++i) buf_load16_lds_nt(r, q_lds + 1024 * i, qdma[i]);
   };
 
   // ---- pipeline state ----
@@ -297,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
 #pragma unroll
   for (int k = 0; k < WIN; ++k) {
     d_start[k] = d_row0[k] = 0;
-    d_code[k] = (it_end << IT_SHIFT) | F_FIRST | F_LAST;  // tiles -2 and -1: none
+    d_code[k] = (it_end << IT_SHIFT) | F_FIRST | F_LAST | F_IDLE;  // tiles -2 and -1: none
   }
 #pragma unroll
   for (int t = 0; t < NS; ++t) take(d_start[t + 1], d_code[t + 1], d_row0[t + 1]);  // tiles 0 .. NS - 1
@@ -316,6 +323,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
   // Vector-memory operations issued after the last Q batch that always issue (for the wait before
   // its rows are read): the prologue's K/V loads.
   int since_q = (NS - 1) * LOADS;
+  // Q buffer state: 0 the next item's rows are loading (or loaded); 1 read this iteration, the
+  // epilogue of the item before runs next iteration through the buffer; 2 free, load item q_next.
+  int q_state = 0, q_next = 0;
   // Unconditional vector-memory operations (Q batches, output stores) that iterations j - 1 and
   // j - 2 issued after their K/V loads.
   int ex_prev = 0, ex_prev2 = 0;
@@ -354,9 +364,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
     issue_k(d_start[IK], d_code[IK], KSLOT_LOAD);
     issue_v(d_start[IV], d_code[IV], VSLOT_LOAD);
     since_q += LOADS;
-    // 3. Tile j + 1 starts an item: read its Q fragments, then load the next item's Q rows.
+    // 3. Tile j + 1 starts an item: read its Q fragments.  Its Q rows were loaded after the
+    // previous epilogue; when that epilogue has not happened yet (the item before is a single
+    // tile), load them now.
     const int s_code = d_code[IS];
     if ((s_code & F_FIRST) && code_it(s_code) < it_end) {
+      if (q_state != 0) {
+        issue_q(code_it(s_code));
+        since_q = 0;
+        ex_prev += DSTEPS;
+      }
       wait_vm_dyn(since_q);  // the Q batch (and everything older) has landed
       // The wave's Q region offset is made opaque here so that the compiler forms these
       // addresses when needed instead of keeping eight more registers live across the loop.
@@ -364,10 +381,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
       asm volatile("" : "+s"(qw));
 #pragma unroll
       for (int st = 0; st < DSTEPS; ++st) qf[st] = *reinterpret_cast<const u32x4_t*>(&qbuf[qw + kofs[st]]);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the buffer is refilled
-      issue_q(code_it(s_code) + 1);
-      since_q = 0;
-      ex_prev += DSTEPS;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the buffer is reused
+      q_state = 1;
+      q_next = code_it(s_code) + 1;
     }
     // 4. Softmax of tile j, part 1: mask.
     const int c_code = d_code[IC], c_start = d_start[IC], c_row0 = d_row0[IC];
@@ -379,105 +395,114 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
       m_prev = m_run;
       l_prev = l_run;
     }
-    if (!c_valid || c_keys < BN || (c_causal && c_start + BN - 1 > c_row0)) {
-      // Register r holds key start + 8 (r / 4) + 4 half + r % 4.
-      const int lim = (c_valid ? (c_causal ? min(c_keys, c_row0 + tt + 1 - c_start) : c_keys) : 0) - 4 * half;
+    // Tiles j - 1, j and j + 1 all belong to items where this wave has no valid rows: skip the
+    // arithmetic (the loads, waits and barriers above still run).
+    const bool idle3 = (d_code[IP] & d_code[IC] & d_code[IS] & F_IDLE) != 0;
+    if (!idle3) {
+      if (!c_valid || c_keys < BN || (c_causal && c_start + BN - 1 > c_row0)) {
+        // Register r holds key start + 8 (r / 4) + 4 half + r % 4.
+        const int lim = (c_valid ? (c_causal ? min(c_keys, c_row0 + tt + 1 - c_start) : c_keys) : 0) - 4 * half;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s_cur[r] = (8 * (r >> 2) + (r & 3)) < lim ? s_cur[r] : -INFINITY;
-    }
-
-    // 5. Matrix products of tiles j - 1 (P.V) and j + 1 (S^T), softmax of tile j, in three phases
-    // separated by scheduling fences, each pairing matrix-core work with independent vector work:
-    //   A  P.V MFMAs of tile j - 1, keys 0..15    | row maximum of tile j
-    //   B  P.V MFMAs of tile j - 1, keys 16..31   | exponentials of keys whose P slots A freed
-    //   C  S^T MFMAs of tile j + 1                | remaining exponentials, row sum
-    // Each phase's LDS operands are read one phase ahead.  P of tile j overwrites P of tile j - 1
-    // in the registers the P.V products have finished reading.
-    const uint8_t* vt_base = &vring[VSLOT_PV][0];
-    const uint8_t* kt_base = &kring[KSLOT_S][0];
-    u32x4_t vf[2][DBLK];
-    auto read_v = [&](int m) {
-#pragma unroll
-      for (int b = 0; b < DBLK; ++b) {
-        const uint16_t* vp = reinterpret_cast<const uint16_t*>(vt_base + vofs[b] + 16 * m * RB);
-        const u32x2_t lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 8 * D);
-        vf[m][b] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        for (int r = 0; r < 16; ++r) s_cur[r] = (8 * (r >> 2) + (r & 3)) < lim ? s_cur[r] : -INFINITY;
       }
-    };
-    u32x4_t kf[DSTEPS];
-    float lsum0 = 0.f, lsum1 = 0.f;  // two partial row sums shorten the add chain
-    float mu = 0.f;
-    // Exponentials of s_cur registers [r0, r1) (pairs), packed into pk[r / 2].
-    auto exps = [&](int r0, int r1) {
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        if (r < r0 || r >= r1) continue;
-        const float p0 = fast_exp2(fmaf(s_cur[r], scale_log2, -mu));
-        const float p1 = fast_exp2(fmaf(s_cur[r + 1], scale_log2, -mu));
-        pk[r >> 1] = pack_bf16x2(p0, p1);
-        if (r & 2)
-          lsum1 += p0 + p1;
-        else
-          lsum0 += p0 + p1;
-      }
-    };
-    constexpr int R_B = 6;  // exponentials of registers [0, R_B) in phase B, the rest in C
-    read_v(0);
-    __builtin_amdgcn_sched_barrier(0);
-    // Phase A.
-    {
-      const u32x4_t pv = {pk[0], pk[1], pk[2], pk[3]};
-#pragma unroll
-      for (int b = 0; b < DBLK; ++b) o[b] = mfma32(vf[0][b], pv, o[b]);
-    }
-    read_v(1);
-    float mt = fmaxf(fmaxf(s_cur[0], s_cur[1]), s_cur[2]);
-#pragma unroll
-    for (int r = 3; r < 15; r += 2) mt = fmaxf(fmaxf(mt, s_cur[r]), s_cur[r + 1]);
-    mt = fmaxf(mt, s_cur[15]);
-    mt = max_halves(mt) * scale_log2;
-    const bool need = !c_first && mt > m_run + kRescaleSlack;
-    const float m_new = c_first ? mt : (need ? mt : m_run);
-    const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
-    m_run = m_new;
-    mu = m_new == -INFINITY ? 0.f : m_new;
-    __builtin_amdgcn_sched_barrier(0);
-    // Phase B.
-    {
-      const u32x4_t pv = {pk[4], pk[5], pk[6], pk[7]};
-#pragma unroll
-      for (int b = 0; b < DBLK; ++b) o[b] = mfma32(vf[1][b], pv, o[b]);
-    }
-#pragma unroll
-    for (int st = 0; st < DSTEPS; ++st) kf[st] = *reinterpret_cast<const u32x4_t*>(kt_base + kofs[st]);
-    exps(0, R_B);
-    __builtin_amdgcn_sched_barrier(0);
-    // Phase C (the second half of the K fragments is read while the first half is used).
-    s_nxt = f32x16_t{};
-#pragma unroll
-    for (int st = 0; st < DSTEPS; ++st) s_nxt = mfma32(kf[st], qf[st], s_nxt);
-    exps(R_B, 16);
-    l_run = (c_first ? 0.f : l_run * alpha) + (lsum0 + lsum1);
-    __builtin_amdgcn_sched_barrier(0);
-    // Keep the softmax results here: otherwise the compiler sinks them past the loop exit test
-    // into the next iteration, where nothing overlaps them.
-    asm volatile("" ::"v"(pk[0]), "v"(pk[1]), "v"(pk[2]), "v"(pk[3]), "v"(pk[4]), "v"(pk[5]), "v"(pk[6]),
-                 "v"(pk[7]), "v"(l_run));
 
-    // 6. Lazy rescale of the accumulator (tile j continues the item of tile j - 1).
-    if (__any(need)) {
+      // 5. Matrix products of tiles j - 1 (P.V) and j + 1 (S^T), softmax of tile j, in three phases
+      // separated by scheduling fences, each pairing matrix-core work with independent vector work:
+      //   A  P.V MFMAs of tile j - 1, keys 0..15    | row maximum of tile j
+      //   B  P.V MFMAs of tile j - 1, keys 16..31   | exponentials of keys whose P slots A freed
+      //   C  S^T MFMAs of tile j + 1                | remaining exponentials, row sum
+      // Each phase's LDS operands are read one phase ahead.  P of tile j overwrites P of tile j - 1
+      // in the registers the P.V products have finished reading.
+      const uint8_t* vt_base = &vring[VSLOT_PV][0];
+      const uint8_t* kt_base = &kring[KSLOT_S][0];
+      u32x4_t vf[2][DBLK];
+      auto read_v = [&](int m) {
 #pragma unroll
-      for (int b = 0; b < DBLK; ++b) o[b] *= alpha;
+        for (int b = 0; b < DBLK; ++b) {
+          const uint16_t* vp = reinterpret_cast<const uint16_t*>(vt_base + vofs[b] + 16 * m * RB);
+          const u32x2_t lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 8 * D);
+          vf[m][b] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        }
+      };
+      u32x4_t kf[DSTEPS];
+      float lsum0 = 0.f, lsum1 = 0.f;  // two partial row sums shorten the add chain
+      float mu = 0.f;
+      // Exponentials of s_cur registers [r0, r1) (pairs), packed into pk[r / 2].
+      auto exps = [&](int r0, int r1) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          if (r < r0 || r >= r1) continue;
+          const float p0 = fast_exp2(fmaf(s_cur[r], scale_log2, -mu));
+          const float p1 = fast_exp2(fmaf(s_cur[r + 1], scale_log2, -mu));
+          pk[r >> 1] = pack_bf16x2(p0, p1);
+          if (r & 2)
+            lsum1 += p0 + p1;
+          else
+            lsum0 += p0 + p1;
+        }
+      };
+      constexpr int R_B = 6;  // exponentials of registers [0, R_B) in phase B, the rest in C
+      read_v(0);
+      __builtin_amdgcn_sched_barrier(0);
+      // Phase A.
+      {
+        const u32x4_t pv = {pk[0], pk[1], pk[2], pk[3]};
+#pragma unroll
+        for (int b = 0; b < DBLK; ++b) o[b] = mfma32(vf[0][b], pv, o[b]);
+      }
+      read_v(1);
+      float mt = fmaxf(fmaxf(s_cur[0], s_cur[1]), s_cur[2]);
+#pragma unroll
+      for (int r = 3; r < 15; r += 2) mt = fmaxf(fmaxf(mt, s_cur[r]), s_cur[r + 1]);
+      mt = fmaxf(mt, s_cur[15]);
+      mt = max_halves(mt) * scale_log2;
+      const bool need = !c_first && mt > m_run + kRescaleSlack;
+      const float m_new = c_first ? mt : (need ? mt : m_run);
+      const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
+      m_run = m_new;
+      mu = m_new == -INFINITY ? 0.f : m_new;
+      __builtin_amdgcn_sched_barrier(0);
+      // Phase B.
+      {
+        const u32x4_t pv = {pk[4], pk[5], pk[6], pk[7]};
+#pragma unroll
+        for (int b = 0; b < DBLK; ++b) o[b] = mfma32(vf[1][b], pv, o[b]);
+      }
+#pragma unroll
+      for (int st = 0; st < DSTEPS; ++st) kf[st] = *reinterpret_cast<const u32x4_t*>(kt_base + kofs[st]);
+      exps(0, R_B);
+      __builtin_amdgcn_sched_barrier(0);
+      // Phase C (the second half of the K fragments is read while the first half is used).
+      s_nxt = f32x16_t{};
+#pragma unroll
+      for (int st = 0; st < DSTEPS; ++st) s_nxt = mfma32(kf[st], qf[st], s_nxt);
+      exps(R_B, 16);
+      l_run = (c_first ? 0.f : l_run * alpha) + (lsum0 + lsum1);
+      __builtin_amdgcn_sched_barrier(0);
+      // Keep the softmax results here: otherwise the compiler sinks them past the loop exit test
+      // into the next iteration, where nothing overlaps them.
+      asm volatile("" ::"v"(pk[0]), "v"(pk[1]), "v"(pk[2]), "v"(pk[3]), "v"(pk[4]), "v"(pk[5]), "v"(pk[6]),
+                   "v"(pk[7]), "v"(l_run));
+
+      // 6. Lazy rescale of the accumulator (tile j continues the item of tile j - 1).
+      if (__any(need)) {
+#pragma unroll
+        for (int b = 0; b < DBLK; ++b) o[b] *= alpha;
+      }
     }
     // 7. Tile j - 1 ended its item: normalise and store its rows (or split-key partials).  The
     // item's row range and slot were loaded at the end of the previous iteration (e_row0 ..).
     const int p_code = d_code[IP];
-    if ((p_code & F_LAST) && code_it(p_code) < it_end) {
+    if ((p_code & F_LAST) && !(p_code & F_IDLE) && code_it(p_code) < it_end) {
       const float l_tot = l_prev + other_half(l_prev);
       const int prow = e_row0 + tt;
       if (e_slot < 0) {
+        // Normalised bf16 rows go through this wave's region of the Q buffer (free until the next
+        // item's Q rows are loaded), so that each store writes whole 128-byte lines: written with
+        // the Q layout (row n, unit u at u ^ swz_k(n)), read back the way the Q loads fill it, and
+        // stored with the Q loads' offsets.
         const float inv = __builtin_amdgcn_rcpf(l_tot);
-        const rsrc_t ro = row_rsrc(O, e_row0, e_row_limit);  // rows past the item's last token are dropped
+        uint8_t* const stage = &qbuf[32 * RB * w];
 #pragma unroll
         for (int b = 0; b < DBLK; ++b)
 #pragma unroll
@@ -487,14 +512,22 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
             const uint32_t a1 = pack_bf16x2(o[b][4 * j0 + 2] * inv, o[b][4 * j0 + 3] * inv);
             const uint32_t b0 = pack_bf16x2(o[b][4 * j1] * inv, o[b][4 * j1 + 1] * inv);
             const uint32_t b1 = pack_bf16x2(o[b][4 * j1 + 2] * inv, o[b][4 * j1 + 3] * inv);
-            const uint32_t x0 = half ? a0 : b0, x1 = half ? a1 : b1;
-            const auto r0 = __builtin_amdgcn_permlane32_swap(x0, x0, false, false);
-            const auto r1 = __builtin_amdgcn_permlane32_swap(x1, x1, false, false);
-            const u32x4_t v = half ? u32x4_t{r0[0], r1[0], b0, b1} : u32x4_t{a0, a1, r0[1], r1[1]};
-            buf_store16(v, ro, uint32_t((tt * q_stride + hh * D + 32 * b + 16 * t + 8 * half) * 2));
+            // Lane n holds d 16t + 4 half + {0..3} (a) and 16t + 8 + 4 half + {0..3} (b); after
+            // swapping a of the upper half with b of the lower half, lane n holds d 16t + 0..7 and
+            // lane n + 32 holds d 16t + 8..15 of block b: 16-byte unit 4b + 2t + half of row n.
+            const auto r0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+            const auto r1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+            const int u = (32 * b + 16 * t + 8 * half) / 8;
+            *reinterpret_cast<u32x4_t*>(stage + n * RB + 16 * (u ^ swz_k(n))) = u32x4_t{r0[0], r1[0], r0[1], r1[1]};
           }
-        since_q += 2 * DBLK;
-        ex_prev += 2 * DBLK;
+        const rsrc_t ro = row_rsrc(O, e_row0, e_row_limit);  // rows past the item's last token are dropped
+#pragma unroll
+        for (int i = 0; i < DSTEPS; ++i) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + 1024 * i + 16 * lane);
+          buf_store16(v, ro, qdma[i]);
+        }
+        since_q += DSTEPS;
+        ex_prev += DSTEPS;
         if (lse && half == 0 && prow < e_row_limit)
           lse[int64_t(prow - q_row_base) * Hq + h] = (m_prev + __log2f(l_tot)) * kLn2;
       } else {
@@ -519,6 +552,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
     if ((p_code & F_LAST) && code_it(p_code) < it_end) {
 #pragma unroll
       for (int b = 0; b < DBLK; ++b) o[b] = f32x16_t{};
+    }
+    // The Q buffer is free once the epilogue that followed the last Q read is done.
+    if (q_state == 2) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // staged rows read back before the refill
+      issue_q(q_next);
+      since_q = 0;
+      ex_prev += DSTEPS;
+      q_state = 0;
+    } else if (q_state == 1) {
+      q_state = 2;
     }
     // Tile j ends its item: fetch the item's row range and slot for the next iteration's epilogue.
     if ((c_code & F_LAST) && c_valid) {

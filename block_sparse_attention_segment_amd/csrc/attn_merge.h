@@ -30,8 +30,7 @@ __device__ __forceinline__ void attn_merge_block(int block, uint16_t* __restrict
   const MergeItem mi = merges[tile / Hkv];
   const int unit = part * 256 + threadIdx.x;
   const int rho = unit / CH, ch = unit % CH;
-  const int TM = kRowsPerTile / G;
-  const int tok = mi.row0 + rho % TM, h = g * G + rho / TM;
+  const int tok = mi.row0 + rho / G, h = g * G + rho % G;  // token-major rows
   if (tok >= mi.row_limit) return;
   const int64_t stride = int64_t(Hkv) * kRowsPerTile;  // rows between consecutive slots
   const int64_t row = (int64_t(mi.slot0) * Hkv + g) * kRowsPerTile + rho;

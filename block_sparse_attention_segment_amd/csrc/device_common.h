@@ -95,6 +95,13 @@ __device__ __forceinline__ void buf_load16_lds(rsrc_t r, uint32_t lds_addr, uint
                "s"(r), "s"(soffset)
                : "memory", "m0");
 }
+// The same with the non-temporal hint, for data read once (query rows): the L2 then keeps the
+// lines that are re-read (keys and values) in preference to these.
+__device__ __forceinline__ void buf_load16_lds_nt(rsrc_t r, uint32_t lds_addr, uint32_t byte_offset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds" ::"s"(lds_addr), "v"(byte_offset),
+               "s"(r)
+               : "memory", "m0");
+}
 // LDS byte address of a __shared__ object (for M0).
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   typedef __attribute__((address_space(3))) const void lds_void_t;
