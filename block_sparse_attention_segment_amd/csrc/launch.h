@@ -71,7 +71,7 @@ hipError_t launch_doc_bwd(const DocBwdLaunch& a, hipStream_t stream);
 hipError_t launch_infonce(const float* scores, const int32_t* prompt_base, const int32_t* gold, float tau,
                           int num_prompts, float* loss, float* dscores, hipStream_t stream);
 
-constexpr int kSortMaxDocs = 8192;
+constexpr int kSortMaxDocs = 65536;  // documents per prompt (the counting sort is O(N^2) per prompt)
 constexpr int kSortPromptsPerLaunch = 256;
 hipError_t launch_sort_docs(const float* scores, const int32_t* prompt_base, int num_prompts, int32_t* order,
                             hipStream_t stream);

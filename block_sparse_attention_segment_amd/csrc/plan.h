@@ -100,7 +100,7 @@ struct BwdPlan {
 // plus, per prompt, the range of its items (for summing the per-item dQ_S partials).  Signal
 // rows per KV head (n_signal * G) are limited to kDocBwdMaxRows.
 constexpr int kDocBwdMaxRows = 64;
-constexpr int kInfoNceMaxDocs = 8192;
+constexpr int kInfoNceMaxDocs = 65536;
 struct DocBwdPlan {
   ScorePlan fwd;
   std::vector<int32_t> prompt_items;  // [B + 1]

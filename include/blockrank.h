@@ -165,7 +165,8 @@ br_status br_doc_scores(const br_dims* dims, const void* Q_S, int32_t n_signal, 
  * them; doc_ptr: host int32[B + 1] as above (only differences are used: N_b =
  * doc_ptr[b+1] - doc_ptr[b] - 1).  order: device int32 [sum_b N_b]; for prompt b, entries
  * doc_ptr[b]-b .. +N_b hold local document indices in descending score order, ties to the
- * lower index; NaN scores rank as -infinity.  N_b <= 8192.
+ * lower index; NaN scores rank as -infinity.  N_b <= 65,536 (BR_ERR_UNSUPPORTED above: the
+ * exact counting sort does N_b^2 comparisons per prompt).
  */
 br_status br_sort_docs(const float* scores, const int32_t* doc_ptr, int32_t num_prompts,
                        int32_t* order, hipStream_t stream);
@@ -307,7 +308,7 @@ br_status br_attn_bwd_plan_items(const br_dims* dims, const int32_t* segment_off
  *   dscores[k] = d(sum_b loss[b]) / ds_k = (softmax(s / tau)_k - [k == gold]) / tau.
  *   scores, dscores: device fp32 [sum_b N_b] (br_doc_scores order);  loss: device fp32 [B].
  *   doc_ptr: HOST int32[B + 1] as for br_doc_scores;  gold: HOST int32[B], 0 <= gold[b] < N_b.
- *   tau > 0 and finite (the pages use 0.05); N_b <= 8192.  fp32 arithmetic.
+ *   tau > 0 and finite (the pages use 0.05); N_b <= 65,536.  fp32 arithmetic.
  *   workspace: device, >= br_infonce_workspace_bytes(B), 16-byte aligned.
  */
 br_status br_infonce_workspace_bytes(int32_t num_prompts, size_t* bytes);

@@ -47,6 +47,11 @@ Readings taken where the pages are silent or disagree (each also listed in the d
     of a head vector turns by pos * theta^(-2k/d).  Two pairings exist in practice, adjacent
     entries (2k, 2k+1) as in RoFormer's definition, or halves (k, k + d/2) as in the GPT-NeoX
     layout; both are provided.  The base theta is not on the pages: a parameter.
+  * Additive sink ([BS] 5.1 and its appendix note on the sink): its equation is not on the page;
+    from the text, exp(b) is appended to every row's softmax denominator (b one scalar per call,
+    the layer's threshold b_L, a caller input), which equals the plain output times the gate
+    sigma(lse - b) that the appendix describes, lse being the row's natural log-sum-exp of its
+    scaled scores.
   * Backward ([BR] 3.4, auxiliary loss): gradients of the block-sparse attention with respect to
     Q, K and V for an upstream dO; the InfoNCE loss per prompt with temperature tau = 0.05 on the
     readout scores s_k (the sum over prompts is the total); and the readout's gradient with
@@ -176,6 +181,21 @@ def _masked_softmax_av(q, k, v, mask, scale):
     return out, lse
 
 
+def _masked_softmax_sink_av(q, k, v, mask, scale, sink):
+    """The same with an additive sink ([BS] 5.1, length-aware softmax): the constant exp(sink) is
+    appended to every row's softmax denominator, so the weights of a row sum to less than one.
+    q [R,d], k/v [C,d], mask [R,C] -> (out [R,d], lse [R]); lse is the plain log-sum-exp of the
+    row's scores, without the sink."""
+    s = (q @ k.T) * scale
+    s = np.where(mask, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True)
+    out = (p @ v) / (l + np.exp(sink - m))
+    lse = (m + np.log(l))[:, 0]
+    return out, lse
+
+
 def attn_dense(Q, K, V, segment_offsets, seg_ptr, scale: Optional[float] = None):
     """Materialise the whole T x T boolean mask and run masked softmax attention per head.
 
@@ -196,13 +216,14 @@ def attn_dense(Q, K, V, segment_offsets, seg_ptr, scale: Optional[float] = None)
 
 
 def attn_rows(Q, K, V, segment_offsets, seg_ptr, rows=None, scale: Optional[float] = None,
-              row_block: int = 256):
+              row_block: int = 256, sink: Optional[float] = None):
     """Attention for selected rows: per block of rows of one segment, evaluate the predicate
     against every key of the prompt, gather the keys any row may read, and run a dense
     float64 masked softmax over them.
 
-    rows: absolute token indices (default: all).  Returns (O [R,Hq,d], lse [R,Hq]) in the
-    order of ``rows``.
+    rows: absolute token indices (default: all).  sink: the additive sink's constant b ([BS] 5.1;
+    None for the plain softmax), appended to every row's denominator as exp(b).  Returns
+    (O [R,Hq,d], lse [R,Hq]) in the order of ``rows``; lse never includes the sink.
     """
     T = int(np.asarray(segment_offsets)[-1])
     rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
@@ -231,7 +252,11 @@ def attn_rows(Q, K, V, segment_offsets, seg_ptr, rows=None, scale: Optional[floa
             qr = to_f64(np.asarray(Q)[r])
             for h in range(Hq):
                 g = kv_head(h, Hq, Hkv)
-                O[sel, h], lse[sel, h] = _masked_softmax_av(qr[:, h], Kf[cols, g], Vf[cols, g], mc, sc)
+                if sink is None:
+                    O[sel, h], lse[sel, h] = _masked_softmax_av(qr[:, h], Kf[cols, g], Vf[cols, g], mc, sc)
+                else:
+                    O[sel, h], lse[sel, h] = _masked_softmax_sink_av(qr[:, h], Kf[cols, g], Vf[cols, g], mc, sc,
+                                                                     float(sink))
     return O, lse
 
 

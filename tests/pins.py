@@ -134,6 +134,36 @@ def pin_textbook_rows_no_prefix(orc):
     _check_textbook(orc, w, O)
 
 
+def pin_sink_limits_and_gate(orc):
+    """Additive sink ([BS] 5.1): b = -inf leaves the plain softmax output exactly; a huge b drives
+    the output to zero; for every b the output is the plain output times sigma(lse - b), the gate
+    form of the appendix note on the sink."""
+    w = small_case(61, hq=4, hkv=2, d=8, batch=2)
+    O, lse = orc.attn_rows(w.Q, w.K, w.V, w.segment_offsets, w.seg_ptr)
+    O1, lse1 = orc.attn_rows(w.Q, w.K, w.V, w.segment_offsets, w.seg_ptr, sink=-math.inf)
+    assert np.array_equal(O, O1) and np.array_equal(lse, lse1)
+    O2, _ = orc.attn_rows(w.Q, w.K, w.V, w.segment_offsets, w.seg_ptr, sink=600.0)
+    assert np.abs(O2).max() < 1e-200
+    for b in (-3.0, 0.0, 1.5, 4.0):
+        Ob, lb = orc.attn_rows(w.Q, w.K, w.V, w.segment_offsets, w.seg_ptr, sink=b, row_block=5)
+        assert np.allclose(lb, lse, rtol=1e-13, atol=1e-13)  # other row blocks: other summation order
+        gate = 1.0 / (1.0 + np.exp(b - lse))
+        assert np.allclose(Ob, O * gate[:, :, None], rtol=1e-12, atol=1e-15), b
+
+
+def pin_sink_single_key(orc):
+    """A row that reads one key (the prompt's first token) has the closed form
+    v / (1 + exp(b - s)), s = q.k / sqrt(d): the sink is the only other slot of its softmax."""
+    w = small_case(62, hq=2, hkv=1, d=8, batch=1)
+    q, k, v = (workloads.bf16_bits_to_f32(x[0]).astype(np.float64) for x in (w.Q, w.K, w.V))
+    for b in (-2.0, 0.3, 3.0):
+        O, _ = orc.attn_rows(w.Q, w.K, w.V, w.segment_offsets, w.seg_ptr, rows=[0], sink=b)
+        for h in range(2):
+            s_ = float(q[h] @ k[0]) / math.sqrt(8)
+            want = v[0] / (1.0 + math.exp(b - s_))
+            assert np.allclose(O[0, h], want, rtol=1e-12, atol=1e-15), (b, h)
+
+
 # --------------------------------------------------------------------------------------
 # brute force from the chunked formulation (BlockRank summary, chunked implementation):
 # documents attend to [K_Inst, K_k], the query to everything, the instruction causally.
@@ -793,6 +823,6 @@ ALL_PINS = [
     pin_ssmax_gold_weight, pin_ssmax_readout_gold_mass, pin_rope_positions_golden, pin_rope_rotation_values,
     pin_rope_relative_position, pin_rope_permutation_invariance, pin_signal_positions,
     pin_attn_bwd_finite_differences, pin_attn_bwd_identities, pin_attn_bwd_autograd, pin_attn_bwd_sampled,
-    pin_infonce,
+    pin_infonce, pin_sink_limits_and_gate, pin_sink_single_key,
     pin_readout_bwd_finite_differences, pin_readout_bwd_identities,
 ]

@@ -216,7 +216,7 @@ def test_doc_scores_and_sort_reject_bad_arguments():
     beyond = np.array([4, 6, 11], dtype=np.int32)
     assert lib.br_doc_scores(ctypes.byref(dims), f, 2, f, p(beyond), p(dp), f, None, 0.0, f, need,
                              None) == br._lib.BR_ERR_INVALID_ARG
-    big = np.array([0, 8194], dtype=np.int32)
+    big = np.array([0, 65538], dtype=np.int32)  # 65,537 documents: one more than the sort takes
     assert lib.br_sort_docs(f, p(big), 1, f, None) == br._lib.BR_ERR_UNSUPPORTED
     assert lib.br_sort_docs(f, p(np.array([0, 1], dtype=np.int32)), 1, f, None) == br._lib.BR_ERR_INVALID_ARG
     assert lib.br_sort_docs(None, p(dp), 1, f, None) == br._lib.BR_ERR_INVALID_ARG
@@ -388,6 +388,9 @@ def test_infonce_and_readout_bwd_reject_before_any_hip_call():
     assert call([0, 1], float("inf")) == INV
     assert call([0, 1], 0.05, nb=need.value - 1) == WS
     assert lib.br_infonce(f, p([0, 1, 2]), 2, p([0, 0]), 0.05, f, f, f, need.value, None) == INV  # empty prompt
+    n1 = ctypes.c_size_t(0)
+    assert lib.br_infonce_workspace_bytes(1, ctypes.byref(n1)) == 0
+    assert lib.br_infonce(f, p([0, 65538]), 1, p([0]), 0.05, f, f, f, n1.value, None) == UNS  # 65,537 documents
     # readout backward: too many signal rows per KV head, bad flags, workspace
     seg, sp, dof, dptr = workloads.segment_tables([(8, [16, 12, 20], 8), (4, [10, 10], 9)])
     dims = br.make_dims(2, 8, 1, 64, int(seg[-1]))   # G = 8
@@ -448,7 +451,7 @@ def test_rank_workspace_and_rejects_before_any_hip_call():
     assert call(order=None) == INV
     assert call(S=0) == INV                    # no signal rows
     assert call(scale=float("nan")) == INV
-    big = workloads.segment_tables([(2, [1] * 8193, 2)])
+    big = workloads.segment_tables([(2, [1] * 65537, 2)])
     dims2 = br.make_dims(1, 8, 2, 64, int(big[0][-1]))
     nb = ctypes.c_size_t(0)
     assert lib.br_rank_workspace_bytes(ctypes.byref(dims2), p(big[0]), p(big[1]), 1, p(big[2]), p(big[3]),

@@ -122,13 +122,13 @@ def test_document_isolation_bit_exact():
 
 def test_sort_matches_oracle_rank_bit_exact():
     r = np.random.default_rng(11)
-    n_list = [1, 7, 100, 500, 33, 8192]
+    n_list = [1, 7, 100, 500, 33, 8192, 10000, 16384]  # more than 8,192: several LDS chunks
     scores = np.concatenate([(np.round(r.random(n) * 64) / 64).astype(np.float32) for n in n_list])
     scores[5] = -0.0
     scores[6] = 0.0
     scores[20] = np.nan
     dp = np.cumsum([0] + [n + 1 for n in n_list]).astype(np.int32)
-    log("[gpu] sort: ties, signed zeros, NaN, N up to 8192")
+    log("[gpu] sort: ties, signed zeros, NaN, N up to 16,384")
     got = br.sort_docs(torch.from_numpy(scores).cuda(), dp).cpu().numpy()
     ref_in = np.where(np.isnan(scores), -np.inf, scores)
     np.testing.assert_array_equal(got, orc.rank(ref_in, dp))
@@ -155,13 +155,16 @@ RANK_CUSTOM = {
     "many_docs": ([(16, [8] * 600, 16), (8, [3] * 40, 8)], dict(hq=8, hkv=2, d=64, n_signal=4)),
     "wide_heads": ([(8, [4] * 300, 8)], dict(hq=64, hkv=8, d=64, n_signal=2)),
     "over_1024_docs": ([(4, [2] * 1100, 4), (4, [5] * 7, 4)], dict(hq=4, hkv=2, d=64, n_signal=2)),
+    "over_8192_docs": ([(4, [2] * 10000, 4)], dict(hq=4, hkv=2, d=64, n_signal=2)),
 }
 
 
-@pytest.mark.parametrize("config", ["worked", "batched", "ragged", "many_docs", "wide_heads", "over_1024_docs"])
+@pytest.mark.parametrize("config", ["worked", "batched", "ragged", "many_docs", "wide_heads", "over_1024_docs",
+                                    "over_8192_docs"])
 def test_rank_step_matches_separate_calls(config):
     """br_rank_prompts (one call, one plan upload) gives bit-identical attention output, lse, scores,
-    head scores and order to br_attn_fwd + br_doc_scores + br_sort_docs."""
+    head scores and order to br_attn_fwd + br_doc_scores + br_sort_docs, and the order is the
+    oracle's rank of the scores, bit for bit (up to 10,000 documents in one prompt)."""
     if config in RANK_CUSTOM:
         prompts, kw = RANK_CUSTOM[config]
         w = workloads.make_custom(prompts, seed=3, **kw)
@@ -179,6 +182,8 @@ def test_rank_step_matches_separate_calls(config):
     torch.cuda.synchronize()
     assert torch.equal(out, a_out) and torch.equal(lse, a_lse)
     assert torch.equal(s, a_s) and torch.equal(hs, a_hs) and torch.equal(o, a_o)
+    sc = s.cpu().numpy()
+    np.testing.assert_array_equal(o.cpu().numpy(), orc.rank(np.where(np.isnan(sc), -np.inf, sc), w.doc_ptr))
 
 
 def test_rank_step_side_stream_from_two_host_threads():

@@ -34,10 +34,10 @@ def check_grad(got: np.ndarray, ref: np.ndarray, what: str, fro_tol=FRO_RTOL, ma
 
 def test_infonce_parity():
     rng = np.random.default_rng(0)
-    counts = [1, 5, 100, 500, 3000]
+    counts = [1, 5, 100, 500, 3000, 10000, 16384]
     dp = np.concatenate([[0], np.cumsum(np.array(counts) + 1)]).astype(np.int32)
     s = np.concatenate([rng.uniform(0, 2, n) for n in counts]).astype(np.float32)
-    gold = np.array([0, 4, 17, 250, 2999], dtype=np.int32)
+    gold = np.array([0, 4, 17, 250, 2999, 9000, 16383], dtype=np.int32)
     log(f"[infonce] documents per prompt {counts}")
     loss, ds = br.infonce(torch.from_numpy(s).cuda(), dp, gold, tau=0.05)
     torch.cuda.synchronize()

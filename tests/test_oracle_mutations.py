@@ -379,6 +379,24 @@ def _bwd_sampled_own_segment_readers(Q, K, V, dO, so, sp, rows=(), keys=(), scal
     return dQ, dK, dV
 
 
+def _sink_wrong_sign(q, k, v, mask, scale, sink):
+    """exp(-b) appended to the denominator instead of exp(b)"""
+    return _ORIG_SINK(q, k, v, mask, scale, -sink)
+
+
+def _sink_outside_shift(q, k, v, mask, scale, sink):
+    """exp(b) added to the max-shifted sum without the same shift"""
+    s_ = (q @ k.T) * scale
+    s_ = np.where(mask, s_, -np.inf)
+    m = s_.max(axis=1, keepdims=True)
+    p = np.exp(s_ - m)
+    l = p.sum(axis=1, keepdims=True)
+    return (p @ v) / (l + np.exp(sink)), (m + np.log(l))[:, 0]
+
+
+_ORIG_SINK = orc._masked_softmax_sink_av
+
+
 MUTATIONS = {
     "mask_no_causal": ("allowed", _no_causal),
     "mask_docs_skip_prefix": ("allowed", _docs_skip_prefix),
@@ -414,6 +432,8 @@ MUTATIONS = {
     "attn_bwd_dk_unscaled": ("attn_bwd", _attn_bwd_dk_unscaled),
     "bwd_sampled_own_segment_readers": ("attn_bwd_sampled", _bwd_sampled_own_segment_readers),
     "infonce_sign": ("infonce", _infonce_sign),
+    "sink_wrong_sign": ("_masked_softmax_sink_av", _sink_wrong_sign),
+    "sink_outside_shift": ("_masked_softmax_sink_av", _sink_outside_shift),
     "infonce_no_tau": ("infonce", _infonce_no_tau),
     "readout_bwd_no_centering": ("doc_scores_bwd", _readout_bwd_no_centering),
     "readout_bwd_sum_heads": ("doc_scores_bwd", _readout_bwd_sum_heads),
