@@ -290,7 +290,8 @@ br_status check_attn_buffers(const void* Q, const void* K, const void* V, const 
 // addressed relative to token q_row_base.
 br_status run_attn(const br_dims& dims, br::AttnPlan& plan, const void* Q, const void* K, const void* V, void* out,
                    float* lse, float softmax_scale, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                   int q_row_base, hipEvent_t kernel_start, hipEvent_t kernel_stop, bool pageable_upload = false) {
+                   int q_row_base, hipEvent_t kernel_start, hipEvent_t kernel_stop, bool pageable_upload = false,
+                   float sink_log2 = -__builtin_inff()) {
   if (!workspace || workspace_bytes < plan.total_bytes)
     return record(BR_ERR_WORKSPACE, "workspace is NULL or smaller than the workspace size query's " +
                                         std::to_string(plan.total_bytes) + " bytes");
@@ -337,6 +338,7 @@ br_status run_attn(const br_dims& dims, br::AttnPlan& plan, const void* Q, const
   a.head_dim = dims.head_dim;
   a.scale_log2 = resolve_scale(softmax_scale, dims.head_dim) * 1.4426950408889634f;
   a.q_row_base = q_row_base;
+  a.sink_log2 = sink_log2;
   a.ev_start = kernel_start;
   a.ev_stop = kernel_stop;
   hipError_t he = br::launch_attn(a, stream);
@@ -596,6 +598,25 @@ br_status br_attn_fwd(const br_dims* dims, const void* Q, const void* K, const v
                       float softmax_scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return br_attn_fwd_timed(dims, Q, K, V, segment_offsets, seg_ptr, out, lse, softmax_scale, workspace,
                            workspace_bytes, stream, nullptr, nullptr);
+}
+
+br_status br_attn_fwd_sink(const br_dims* dims, const void* Q, const void* K, const void* V,
+                           const int32_t* segment_offsets, const int32_t* seg_ptr, void* out, float* lse,
+                           float softmax_scale, float sink, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  return guarded([&]() -> br_status {
+    if (std::isnan(sink)) return record(BR_ERR_INVALID_ARG, "sink must not be NaN (-inf disables it)");
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    br_status st = check_attn_buffers(Q, K, V, out, lse, softmax_scale);
+    if (st != BR_OK) return st;
+    br::AttnPlan plan;
+    e = br::build_attn_plan(*dims, segment_offsets, seg_ptr, &plan);
+    if (!e.ok()) return record(e);
+    const float sink_log2 = std::isinf(sink) ? sink : float(double(sink) * 1.4426950408889634);
+    return run_attn(*dims, plan, Q, K, V, out, lse, softmax_scale, workspace, workspace_bytes, stream, 0, nullptr,
+                    nullptr, false, sink_log2);
+  });
 }
 
 br_status br_doc_scores_workspace_bytes(const br_dims* dims, int32_t n_signal, const int32_t* doc_offsets,

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
                                                        float* __restrict__ lse, const AttnItem* __restrict__ items,
                                                        const int32_t* __restrict__ ranges, float* __restrict__ part_o,
                                                        float* __restrict__ part_ml, int Hq, int Hkv, float scale_log2,
-                                                       int q_row_base) {
+                                                       int q_row_base, float sink_log2) {
   constexpr int TM = kRowsPerTile / G;  // tokens per item
   constexpr int BN = kFwdKeys;
   constexpr int RB = 2 * D;             // bytes per row of one head
@@ -501,7 +501,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
         // item's Q rows are loaded), so that each store writes whole 128-byte lines: written with
         // the Q layout (row n, unit u at u ^ swz_k(n)), read back the way the Q loads fill it, and
         // stored with the Q loads' offsets.
-        const float inv = __builtin_amdgcn_rcpf(l_tot);
+        // The additive sink appends exp(b) to the denominator: 2^(b log2(e) - m) in the units of
+        // l (zero when b = -inf, which leaves the plain softmax bit for bit).
+        const float inv = __builtin_amdgcn_rcpf(l_tot + fast_exp2(sink_log2 - m_prev));
         uint8_t* const stage = &qbuf[32 * RB * w];
 #pragma unroll
         for (int b = 0; b < DBLK; ++b)
@@ -599,8 +601,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(uint16_t* __restrict__ 
                                                          const MergeItem* __restrict__ merges,
                                                          const float* __restrict__ part_o,
                                                          const float* __restrict__ part_ml, int Hq, int Hkv, int G,
-                                                         int q_row_base) {
-  attn_merge_block<D>(blockIdx.x, O, lse, merges, part_o, part_ml, Hq, Hkv, G, q_row_base);
+                                                         int q_row_base, float sink_log2) {
+  attn_merge_block<D>(blockIdx.x, O, lse, merges, part_o, part_ml, Hq, Hkv, G, q_row_base, sink_log2);
 }
 
 template <int D, int G>
@@ -613,7 +615,7 @@ static hipError_t launch_attn_t(const AttnLaunch& a, hipStream_t stream) {
     }
     attn_fwd_kernel<D, G, kFwdSlots><<<grid, 256, 0, stream>>>(a.Q, a.K, a.V, a.O, a.lse, a.items, a.ranges, a.part_o,
                                                                a.part_ml, a.num_q_heads, a.num_kv_heads, a.scale_log2,
-                                                               a.q_row_base);
+                                                               a.q_row_base, a.sink_log2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.ev_stop) {
@@ -624,7 +626,7 @@ static hipError_t launch_attn_t(const AttnLaunch& a, hipStream_t stream) {
   if (a.n_merges > 0 && !a.defer_merge) {
     const dim3 grid(unsigned(a.n_merges * a.num_kv_heads * merge_wg_per_tile<D>()));
     attn_merge_kernel<D><<<grid, 256, 0, stream>>>(a.O, a.lse, a.merges, a.part_o, a.part_ml, a.num_q_heads,
-                                                   a.num_kv_heads, G, a.q_row_base);
+                                                   a.num_kv_heads, G, a.q_row_base, a.sink_log2);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -22,7 +22,7 @@ template <int D>
 __device__ __forceinline__ void attn_merge_block(int block, uint16_t* __restrict__ O, float* __restrict__ lse,
                                                  const MergeItem* __restrict__ merges, const float* __restrict__ part_o,
                                                  const float* __restrict__ part_ml, int Hq, int Hkv, int G,
-                                                 int q_row_base) {
+                                                 int q_row_base, float sink_log2) {
   constexpr int CH = D / 4;                          // 4-element units per row
   constexpr int WG_PER_TILE = kRowsPerTile * CH / 256;
   const int tile = block / WG_PER_TILE, part = block % WG_PER_TILE;
@@ -66,7 +66,7 @@ __device__ __forceinline__ void attn_merge_block(int block, uint16_t* __restrict
   }
   for (; c < n; ++c)
     add(ml[row + c * stride], *reinterpret_cast<const f32x4_t*>(part_o + (row + c * stride) * D + ch * 4));
-  const float inv = 1.f / L;
+  const float inv = 1.f / (L + fast_exp2(sink_log2 - M));  // the sink slot adds exp(b) / 2^M; 0 when b = -inf
   const u32x2_t v = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
   *reinterpret_cast<u32x2_t*>(O + (int64_t(tok - q_row_base) * Hq + h) * D + ch * 4) = v;
   if (lse && ch == 0) lse[int64_t(tok - q_row_base) * Hq + h] = (M + __log2f(L)) * kLn2;

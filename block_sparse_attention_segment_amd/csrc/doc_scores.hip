@@ -143,12 +143,12 @@ __global__ __launch_bounds__(256, 4) void doc_partial_kernel(const uint16_t* __r
 template <int D>
 __global__ __launch_bounds__(256, 4) void merge_doc_partial_kernel(
     int merge_blocks, uint16_t* __restrict__ O, float* __restrict__ lse, const MergeItem* __restrict__ merges,
-    const float* __restrict__ part_o, const float* __restrict__ part_ml, int G, int q_row_base,
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, int G, int q_row_base, float sink_log2,
     const uint16_t* __restrict__ Q_S, const uint16_t* __restrict__ K, const ScoreItem* __restrict__ items,
     const int32_t* __restrict__ dof, float2* __restrict__ ml, int64_t n_items, int Hq, int Hkv, int n_signal,
     int row_blocks, float scale_log2) {
   if (int(blockIdx.x) < merge_blocks)
-    attn_merge_block<D>(blockIdx.x, O, lse, merges, part_o, part_ml, Hq, Hkv, G, q_row_base);
+    attn_merge_block<D>(blockIdx.x, O, lse, merges, part_o, part_ml, Hq, Hkv, G, q_row_base, sink_log2);
   else
     doc_partial_block<D>(int64_t(blockIdx.x) - merge_blocks, Q_S, K, items, dof, ml, n_items, Hq, Hkv, n_signal,
                          row_blocks, scale_log2);
@@ -238,7 +238,7 @@ static hipError_t launch_merge_doc_partial_t(const AttnLaunch* m, const ScoreLau
   } else {
     merge_doc_partial_kernel<D><<<grid, 256, 0, stream>>>(
         merge_blocks, m->O, m->lse, m->merges, m->part_o, m->part_ml, m->num_q_heads / m->num_kv_heads,
-        m->q_row_base, a.Q_S, a.K, a.items, a.doc_offsets, a.ml, a.n_items, a.num_q_heads, a.num_kv_heads,
+        m->q_row_base, m->sink_log2, a.Q_S, a.K, a.items, a.doc_offsets, a.ml, a.n_items, a.num_q_heads, a.num_kv_heads,
         a.n_signal, a.row_blocks, a.scale_log2);
   }
   return hipGetLastError();

@@ -24,6 +24,7 @@ struct AttnLaunch {
   int num_q_heads, num_kv_heads, head_dim;
   float scale_log2;         // softmax scale * log2(e)
   int q_row_base = 0;       // token index of Q/O/lse row 0 (the corpus length for query-only runs)
+  float sink_log2 = -__builtin_inff();  // additive sink b * log2(e); -inf: none
   hipEvent_t ev_start = nullptr, ev_stop = nullptr;  // optional, recorded around the main kernel
   bool defer_merge = false;  // leave the split-key merge to launch_merge_doc_scores
 };

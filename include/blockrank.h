@@ -108,6 +108,21 @@ br_status br_attn_fwd(const br_dims* dims, const void* Q, const void* K, const v
                       hipStream_t stream);
 
 /*
+ * The same attention with BlockSearch's additive sink ("Can Language Models Actually Retrieve
+ * In-Context?", section 5.1 "Length-aware softmax", and its appendix note on the sink): the
+ * constant exp(sink) is appended to every row's softmax denominator, so
+ *   out = softmax(s) V * sigma(lse - sink),   s the scaled logits, lse their log-sum-exp,
+ * the gate sigma(lse - b_L) the note describes (b_L one scalar per layer, supplied by the
+ * caller).  sink = -INFINITY gives br_attn_fwd's output bit for bit; NaN is rejected
+ * (BR_ERR_INVALID_ARG).  lse (if non-NULL) is the plain log-sum-exp, without the sink.  Other
+ * arguments, workspace size and errors as for br_attn_fwd.
+ */
+br_status br_attn_fwd_sink(const br_dims* dims, const void* Q, const void* K, const void* V,
+                           const int32_t* segment_offsets, const int32_t* seg_ptr, void* out,
+                           float* lse, float softmax_scale, float sink, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/*
  * br_attn_fwd, plus timing: records `kernel_start` on `stream` immediately before the main
  * attention kernel is enqueued and `kernel_stop` immediately after it (the split-key merge
  * kernel, if any, follows `kernel_stop`).  Either event may be NULL.  For measuring the

@@ -499,3 +499,16 @@ def test_binding_functions_run_on_their_stream(monkeypatch):
     with pytest.raises(ValueError):
         br.attn_fwd(x, x, x, [0, 4], [0, 1])
     assert entered == [marker]
+
+
+def test_sink_rejects_nan_before_any_hip_call():
+    lib = br.load_library()
+    p = lambda a: np.ascontiguousarray(a, dtype=np.int32).ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    f = _fake()
+    seg, sp, _, _ = workloads.segment_tables([(4, [5, 6], 3)])
+    dims = br.make_dims(1, 4, 2, 64, int(seg[-1]))
+    need = br.attn_workspace_bytes(dims, seg, sp)
+    rc = lib.br_attn_fwd_sink(ctypes.byref(dims), f, f, f, p(seg), p(sp), f, None, 0.0, float("nan"), f, need, None)
+    assert rc == br._lib.BR_ERR_INVALID_ARG
+    rc = lib.br_attn_fwd_sink(ctypes.byref(dims), f, f, f, p(seg), p(sp), f, None, 0.0, 1.0, f, need - 1, None)
+    assert rc == br._lib.BR_ERR_WORKSPACE
