@@ -156,6 +156,41 @@ def measure(config, seed, steps, warmup, log):
         br.rank_step(Q, K, V, Q_S, w.segment_offsets, w.seg_ptr, w.doc_offsets, w.doc_ptr, out=out, scores=scores,
                      order=order, workspace=ws, stream=stream, kernel_events=kernel_events)
 
+    # Measured first (they also bring the GPU to its working clocks before the timed steps): the
+    # attention alone (br_attn_fwd, nothing else on the GPU), for comparison with its duration
+    # inside a step, ...
+    attn_ws = torch.empty(br.attn_workspace_bytes(dims, w.segment_offsets, w.seg_ptr), dtype=torch.uint8,
+                          device="cuda")
+    # A GPU that has been idle runs its first milliseconds of work measurably slower (about 15% at
+    # this size): bring it to its working clocks with half a second of the attention first.
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < 0.5:
+        for _ in range(4):
+            br.attn_fwd(Q, K, V, w.segment_offsets, w.seg_ptr, out=out, workspace=attn_ws, stream=stream)
+        torch.cuda.synchronize()
+    for i in range(steps):
+        br.attn_fwd(Q, K, V, w.segment_offsets, w.seg_ptr, out=out, workspace=attn_ws, stream=stream,
+                    kernel_events=(ev.ev[2 * i], ev.ev[2 * i + 1]))
+    torch.cuda.synchronize()
+    kern_iso = [ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(steps)]
+    del attn_ws
+    # ... and the readout alone (br_doc_scores: partials, row statistics, scores), between torch
+    # events on the same stream.
+    sc_ws = torch.empty(br.doc_scores_workspace_bytes(dims, w.n_signal, w.doc_offsets, w.doc_ptr), dtype=torch.uint8,
+                        device="cuda")
+    for _ in range(max(1, warmup // 2)):
+        br.doc_scores(Q_S, K, w.doc_offsets, w.doc_ptr, scores=scores, workspace=sc_ws, stream=stream)
+    torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    for _ in range(steps):
+        br.doc_scores(Q_S, K, w.doc_offsets, w.doc_ptr, scores=scores, workspace=sc_ws, stream=stream)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    readout_ms = r0.elapsed_time(r1) / steps
+    del sc_ws
+    doc_tokens = int(sum(sum(lens) for (_, lens, _) in w.prompts))
+    readout_bytes = float(doc_tokens * Hkv * d * 2 + Q_S.numel() * 2 + w.num_docs * 4)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -173,7 +208,9 @@ def measure(config, seed, steps, warmup, log):
     wall = time.perf_counter() - wall0
     ms_step = e0.elapsed_time(e1) / steps
     # Kernel region: K more back-to-back steps, the attention kernel's own duration per step from
-    # events the library records around it on its launch stream.
+    # events the library records around it on its launch stream; the step takes the same path as
+    # in the timed region (the readout on the side stream for large batches), so this is the
+    # kernel's duration inside a step.
     torch.cuda.synchronize()
     for i in range(steps):
         step(kernel_events=(ev.ev[2 * i], ev.ev[2 * i + 1]))
@@ -189,17 +226,61 @@ def measure(config, seed, steps, warmup, log):
         b.record(stream)
         b.synchronize()
         lat.append(a.elapsed_time(b))
+    cold = cold_plan_latency(w, Q, K, V, Q_S, stream, log)
     peak_mb = torch.cuda.max_memory_allocated() / 2**20
-    log(f"[bench] {config}: {steps} timed steps, {ms_step:.4f} ms/step, attention kernel {np.mean(kern):.4f} ms")
+    log(f"[bench] {config}: {steps} timed steps, {ms_step:.4f} ms/step, attention kernel {np.mean(kern):.4f} ms "
+        f"in the step, {np.mean(kern_iso):.4f} ms alone; readout {readout_ms:.4f} ms")
     blk, exact = pair_counts(w)
     flop_blk = 4.0 * d * Hq * blk
     flop_exact = 4.0 * d * Hq * exact
     kernel_s = float(np.mean(kern)) / 1e3
     bytes_alg = float(T) * (2 * Hq + 2 * Hkv) * d * 2
     return dict(w=w, ms_step=ms_step, wall_s=wall, kernel_ms=float(np.mean(kern)), kernel_ms_p50=float(np.median(kern)),
+                kernel_ms_isolated=float(np.mean(kern_iso)), readout_ms=readout_ms, readout_bytes=readout_bytes,
+                cold=cold,
                 flop_blk=flop_blk, flop_exact=flop_exact, pairs_blk=blk, pairs_exact=exact, bytes_alg=bytes_alg,
                 kernel_s=kernel_s, lat_p50=float(np.percentile(lat, 50)), lat_p95=float(np.percentile(lat, 95)),
                 peak_mb=peak_mb, visited_pairs=tile_efficiency(w, dims))
+
+
+def cold_plan_latency(w, Q, K, V, Q_S, stream, log, n_tables=5, rounds=2):
+    """Single-step host-to-completion latency of br_rank_prompts when its plan is not cached: the
+    batch's first prompt with one token moved between its first two documents, in n_tables (more
+    than the library's four cached plans) variants visited in turn, so every call builds,
+    schedules and uploads a fresh plan; beside it, the same latency with the original table (a
+    cached plan)."""
+    import torch
+
+    import block_sparse_attention_segment_amd as br
+    import workloads
+    p0, lens0, q0 = w.prompts[0]
+    if len(lens0) < 2 or min(lens0[0], lens0[1]) <= n_tables:
+        return None
+    tables = []
+    for i in range(1, n_tables + 1):
+        prompts = [(p0, [lens0[0] - i, lens0[1] + i] + list(lens0[2:]), q0)] + list(w.prompts[1:])
+        tables.append(workloads.segment_tables(prompts))
+    T, Hq, d = Q.shape
+    dims = br.make_dims(w.num_prompts, Hq, K.shape[1], d, T)
+    need = max(br.rank_workspace_bytes(dims, seg, sp, w.n_signal, do, dp) for (seg, sp, do, dp) in tables)
+    need = max(need, br.rank_workspace_bytes(dims, w.segment_offsets, w.seg_ptr, w.n_signal, w.doc_offsets, w.doc_ptr))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(Q)
+    scores = torch.empty(w.num_docs, dtype=torch.float32, device="cuda")
+    order = torch.empty(w.num_docs, dtype=torch.int32, device="cuda")
+
+    def one(seg, sp, do, dp):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        br.rank_step(Q, K, V, Q_S, seg, sp, do, dp, out=out, scores=scores, order=order, workspace=ws, stream=stream)
+        stream.synchronize()
+        return (time.perf_counter() - t) * 1e3
+
+    cold = [one(*tables[i % n_tables]) for i in range(rounds * n_tables)]
+    warm = [one(w.segment_offsets, w.seg_ptr, w.doc_offsets, w.doc_ptr) for _ in range(rounds * n_tables + 1)][1:]
+    log(f"[bench] single-step latency: fresh plan {np.median(cold):.3f} ms, cached plan {np.median(warm):.3f} ms")
+    return dict(fresh_plan_ms_p50=round(float(np.median(cold)), 4), cached_plan_ms_p50=round(float(np.median(warm)), 4),
+                calls=len(cold))
 
 
 def measure_query_only(w, n_queries, q_len, steps, warmup, seed, log):
@@ -325,10 +406,42 @@ def measure_rope(w, steps, warmup, log):
     alg = 2.0 * w.total_tokens * (Hq + Hkv) * d * 2
     gbps = alg / (ms / 1e3) / 1e9
     log(f"[bench] rope Q+K: {ms:.4f} ms/call, {gbps:.0f} GB/s")
+    # Rotation followed by attention, two ways: the separate pass over Q and K then br_attn_fwd,
+    # or K rotated alone and Q rotated inside the attention kernel (br_attn_fwd_rope).
+    V = dev(w.V)
+    out = torch.empty_like(Q)
+    attn_ws = torch.empty(br.attn_workspace_bytes(dims, w.segment_offsets, w.seg_ptr), dtype=torch.uint8, device="cuda")
+    fused_ws = torch.empty(br.attn_fwd_rope_workspace_bytes(dims, w.segment_offsets, w.seg_ptr), dtype=torch.uint8,
+                           device="cuda")
+
+    def separate():
+        call()
+        br.attn_fwd(Qo, Ko, V, w.segment_offsets, w.seg_ptr, out=out, workspace=attn_ws, stream=stream)
+
+    def fused():
+        br.rope(None, K, w.segment_offsets, w.seg_ptr, 10000.0, K_out=Ko, workspace=ws, stream=stream)
+        br.attn_fwd_rope(Q, Ko, V, w.segment_offsets, w.seg_ptr, 10000.0, out=out, workspace=fused_ws, stream=stream)
+
+    times = {}
+    for name, fn in (("separate", separate), ("fused", fused), ("separate2", separate), ("fused2", fused)):
+        for _ in range(max(1, warmup)):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.setdefault(name.rstrip("2"), []).append(e0.elapsed_time(e1) / steps)
+    sep, fus = min(times["separate"]), min(times["fused"])
+    log(f"[bench] rope + attention: separate {sep:.4f} ms, Q rotated inside the attention kernel {fus:.4f} ms")
     return {"workload": f"RoPE of the long prompt's Q and K ({w.total_tokens} tokens, {Hq} Q / {Hkv} KV heads, d={d}) "
                         f"at permutation-invariant positions, out of place",
             "bound": "hbm", "ms": round(ms, 5), "bytes_per_call": alg, "achieved_gbps": round(gbps, 1),
-            "hbm_roofline_frac": round(gbps / PEAK_HBM_GBPS, 4)}
+            "hbm_roofline_frac": round(gbps / PEAK_HBM_GBPS, 4),
+            "with_attention": {"separate_rope_then_attention_ms": round(sep, 5),
+                               "k_rope_then_attention_rotating_q_ms": round(fus, 5),
+                               "note": "best of two interleaved runs of K calls each"}}
 
 
 def measure_backward(w, steps, warmup, log):
@@ -433,6 +546,26 @@ def cpu_baseline(w, n_docs_sample, log):
     return dict(est_s=est, threads=threads, k=k, N=N, sampled_s=sum(timings.values()))
 
 
+def cpu_model():
+    """The host CPU's model name as lscpu reports it (from /proc/cpuinfo when lscpu is absent)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:  # pragma: no cover
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return platform.processor() or platform.machine()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -440,7 +573,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="long", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--secondary", default="worked,batched",
+    ap.add_argument("--secondary", default="worked,batched,ragged",
                     help="extra configs timed in the same run, comma-separated ('' for none)")
     ap.add_argument("--query-only", type=int, default=1,
                     help="also time query-only attention over the long prompt's cached corpus, top-256 routed "
@@ -476,6 +609,7 @@ def main():
     value = r["flop_blk"] / step_s / 1e12
     attn_tflops_blk = r["flop_blk"] / r["kernel_s"] / 1e12
     achieved_gbps = r["bytes_alg"] / r["kernel_s"] / 1e9
+    iso_s = r["kernel_ms_isolated"] / 1e3
     traffic = measured_traffic(args.config)
     line = {
         "metric": METRIC,
@@ -501,12 +635,22 @@ def main():
         "mfma_peak_frac_step": round(value / PEAK_BF16_TFLOPS, 4),
         "allowed_pairs": {"closed_form": r["pairs_blk"], "exact_causal": r["pairs_exact"]},
         "attention_kernel": {"ms": round(r["kernel_ms"], 5), "ms_p50": round(r["kernel_ms_p50"], 5),
+                             "timing": "inside the timed steps (same launch path, readout alongside)",
+                             "ms_isolated": round(r["kernel_ms_isolated"], 5),
                              "tflops_closed_form_pairs": round(attn_tflops_blk, 3),
-                             "mfma_peak_frac": round(attn_tflops_blk / PEAK_BF16_TFLOPS, 4)},
+                             "mfma_peak_frac": round(attn_tflops_blk / PEAK_BF16_TFLOPS, 4),
+                             "mfma_peak_frac_isolated": round(r["flop_blk"] / iso_s / 1e12 / PEAK_BF16_TFLOPS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic,
                      "kernel": "attn_fwd_kernel", "bytes_per_launch": r["bytes_alg"],
+                     "timing": "kernel duration inside the timed steps",
+                     "frac_isolated": round(r["bytes_alg"] / iso_s / 1e9 / PEAK_HBM_GBPS, 4),
                      "traffic_gbps": None if traffic is None else round(traffic / r["kernel_s"] / 1e9, 1)},
+        "readout": {"kernels": "br_doc_scores (partials, row statistics, scores)", "ms": round(r["readout_ms"], 5),
+                    "algorithmic_bytes": r["readout_bytes"],
+                    "hbm_gbps": round(r["readout_bytes"] / r["readout_ms"] / 1e6, 1),
+                    "hbm_roofline_frac": round(r["readout_bytes"] / r["readout_ms"] / 1e6 / PEAK_HBM_GBPS, 4)},
+        "single_step_latency": r["cold"],
     }
     for name in [s for s in args.secondary.split(",") if s and s != args.config]:
         if name not in WORKLOAD_NAMES:
@@ -516,7 +660,10 @@ def main():
         entry = {"workload": WORKLOAD_NAMES[name], "ms_per_step": round(r2["ms_step"], 5),
                  "prompts_per_s": round(r2["w"].num_prompts / s2, 2),
                  "tflops_closed_form_pairs": round(r2["flop_blk"] / s2 / 1e12, 3),
-                 "attention_kernel_ms": round(r2["kernel_ms"], 5)}
+                 "attention_kernel_ms": round(r2["kernel_ms"], 5),
+                 "attention_kernel_ms_isolated": round(r2["kernel_ms_isolated"], 5),
+                 "readout_hbm_gbps": round(r2["readout_bytes"] / r2["readout_ms"] / 1e6, 1),
+                 "single_step_latency": r2["cold"]}
         # the first extra config keeps the key "secondary"; the others are keyed by name
         line["secondary" if "secondary" not in line else name] = entry
     if args.query_only and args.config == "long":
@@ -525,14 +672,17 @@ def main():
         line["rope"] = measure_rope(w, args.steps, args.warmup, log)
         line["backward"] = measure_backward(w, args.steps, args.warmup, log)
     if not args.no_cpu_baseline:
-        cb = cpu_baseline(w, args.cpu_docs, log)
+        runs = [cpu_baseline(w, args.cpu_docs, log) for _ in range(3)]
+        cb = sorted(runs, key=lambda x: x["est_s"])[1]  # the median of three runs
+        run_list = ", ".join(f"{x['est_s']:.1f}" for x in runs)
         line["cpu_baseline"] = {
             "value": round(r["flop_blk"] / cb["est_s"] / 1e12, 6), "unit": "TFLOP/s", "cores": cb["threads"],
             "kind": "oracle",
             "sample": (f"fp64 NumPy oracle on instruction rows, {cb['k']} of {cb['N']} documents' rows and all "
                        f"query rows, plus the full readout and rank ({cb['sampled_s']:.1f}s measured); time "
-                       f"scaled to all {cb['N']} documents ({cb['est_s']:.1f}s per step); host "
-                       f"{platform.processor() or platform.machine()}, os.cpu_count()={os.cpu_count()}"),
+                       f"scaled to all {cb['N']} documents ({cb['est_s']:.1f}s per step, the median of 3 runs: "
+                       f"{run_list}s); host "
+                       f"{cpu_model()}, os.cpu_count()={os.cpu_count()}"),
         }
     print(json.dumps(line), flush=True)
 

@@ -5,7 +5,8 @@ The Python layer only marshals arguments to libblockrank.so; all computation run
 hand-written HIP kernels.
 """
 from ._lib import (BlockRankError, BrDims, EXPORTED, LIB_PATH, NOALLOC_SCRATCH_BYTES, attn_bwd, attn_bwd_workspace_bytes, attn_fwd,
-                   attn_fwd_noalloc, attn_fwd_sink, attn_plan_items, attn_plan_schedule,
+                   attn_fwd_noalloc, attn_fwd_rope, attn_fwd_rope_workspace_bytes, attn_fwd_sink,
+                   attn_plan_items, attn_plan_schedule,
                    attn_routed, attn_routed_workspace_bytes,
                    attn_workspace_bytes, doc_scores, doc_scores_bwd, doc_scores_bwd_workspace_bytes, doc_scores_workspace_bytes,
                    infonce, load_library,
@@ -13,7 +14,7 @@ from ._lib import (BlockRankError, BrDims, EXPORTED, LIB_PATH, NOALLOC_SCRATCH_B
                    rope_workspace_bytes, sort_docs, ssmax_scale, version)
 
 __all__ = ["BlockRankError", "BrDims", "EXPORTED", "LIB_PATH", "NOALLOC_SCRATCH_BYTES", "attn_bwd", "attn_bwd_workspace_bytes",
-           "attn_fwd", "attn_fwd_noalloc", "attn_fwd_sink", "attn_plan_items", "attn_plan_schedule",
+           "attn_fwd", "attn_fwd_noalloc", "attn_fwd_rope", "attn_fwd_rope_workspace_bytes", "attn_fwd_sink", "attn_plan_items", "attn_plan_schedule",
            "attn_routed", "attn_routed_workspace_bytes",
            "attn_workspace_bytes", "doc_scores", "doc_scores_bwd", "doc_scores_bwd_workspace_bytes",
            "doc_scores_workspace_bytes", "infonce", "load_library",

@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libblockrank.so")
 BR_OK, BR_ERR_INVALID_ARG, BR_ERR_UNSUPPORTED, BR_ERR_WORKSPACE, BR_ERR_HIP = range(5)
 
 # Symbols the header declares; the CPU test checks the library exports each of them.
-EXPORTED = ("br_attn_workspace_bytes", "br_attn_fwd", "br_attn_fwd_timed", "br_attn_fwd_noalloc", "br_attn_fwd_sink", "br_doc_scores_workspace_bytes", "br_doc_scores",
+EXPORTED = ("br_attn_workspace_bytes", "br_attn_fwd", "br_attn_fwd_timed", "br_attn_fwd_noalloc", "br_attn_fwd_sink",
+            "br_attn_fwd_rope_workspace_bytes", "br_attn_fwd_rope", "br_doc_scores_workspace_bytes", "br_doc_scores",
             "br_sort_docs", "br_rank_workspace_bytes", "br_rank_prompts", "br_rank_prompts_timed", "br_attn_plan_items", "br_attn_plan_schedule", "br_query_attn_workspace_bytes", "br_query_attn_fwd", "br_attn_routed_workspace_bytes", "br_attn_routed_fwd",
             "br_attn_bwd_workspace_bytes", "br_attn_bwd", "br_attn_bwd_plan_items",
             "br_infonce_workspace_bytes", "br_infonce", "br_doc_scores_bwd_workspace_bytes", "br_doc_scores_bwd",
@@ -66,6 +67,9 @@ def load_library() -> ctypes.CDLL:
         "br_attn_fwd_noalloc": [dims_p, _P, _P, _P, _I32P, _I32P, _P, _P, ctypes.c_float, _P],
         "br_attn_fwd_sink": [dims_p, _P, _P, _P, _I32P, _I32P, _P, _P, ctypes.c_float, ctypes.c_float, _P,
                              ctypes.c_size_t, _P],
+        "br_attn_fwd_rope_workspace_bytes": [dims_p, _I32P, _I32P, ctypes.c_int32, ctypes.c_int32, sz_p],
+        "br_attn_fwd_rope": [dims_p, _P, _P, _P, _I32P, _I32P, _P, _P, ctypes.c_float, ctypes.c_float, ctypes.c_int32,
+                             ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_size_t, _P],
         "br_doc_scores_workspace_bytes": [dims_p, ctypes.c_int32, _I32P, _I32P, sz_p],
         "br_doc_scores": [dims_p, _P, ctypes.c_int32, _P, _I32P, _I32P, _P, _P, ctypes.c_float, _P,
                           ctypes.c_size_t, _P],
@@ -269,6 +273,47 @@ def attn_fwd_sink(Q, K, V, segment_offsets, seg_ptr, sink: float, out=None, lse=
         workspace = torch.empty(attn_workspace_bytes(dims, so, sp), dtype=torch.uint8, device=Q.device)
     _check(lib.br_attn_fwd_sink(ctypes.byref(dims), Q.data_ptr(), K.data_ptr(), V.data_ptr(), _ptr_i32(so),
                                 _ptr_i32(sp), out.data_ptr(), _dev_ptr(lse), float(softmax_scale), float(sink),
+                                workspace.data_ptr(), workspace.numel(), _stream_handle(stream)))
+    return (out, lse) if lse is not None else out
+
+
+def attn_fwd_rope_workspace_bytes(dims: BrDims, segment_offsets, seg_ptr, query_pos0: int = 8192,
+                                  docs_after_instruction: bool = True) -> int:
+    lib = load_library()
+    so, sp = _host_i32(segment_offsets), _host_i32(seg_ptr)
+    out = ctypes.c_size_t(0)
+    _check(lib.br_attn_fwd_rope_workspace_bytes(ctypes.byref(dims), _ptr_i32(so), _ptr_i32(sp), int(query_pos0),
+                                                int(bool(docs_after_instruction)), ctypes.byref(out)))
+    return out.value
+
+
+@_on_stream
+def attn_fwd_rope(Q, K, V, segment_offsets, seg_ptr, rope_theta: float = 10000.0, query_pos0: int = 8192,
+                  docs_after_instruction: bool = True, interleaved: bool = False, out=None, lse=None,
+                  softmax_scale: float = 0.0, workspace=None, stream=None):
+    """Attention with Q rotated inside the kernel (K already rotated, e.g. rope(None, K, ...));
+    results equal rope on Q followed by attn_fwd."""
+    import torch
+    lib = load_library()
+    for name, t in (("Q", Q), ("K", K), ("V", V)):
+        _check_bf16(name, t, 3)
+    T, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    if K.shape != (T, Hkv, d) or V.shape != K.shape:
+        raise ValueError("K and V must be [T, Hkv, d] matching Q")
+    so, sp = _host_i32(segment_offsets), _host_i32(seg_ptr)
+    dims = make_dims(len(sp) - 1, Hq, Hkv, d, T)
+    out = torch.empty_like(Q) if out is None else out
+    if lse is True:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=Q.device)
+    elif lse is False:
+        lse = None
+    if workspace is None:
+        workspace = torch.empty(attn_fwd_rope_workspace_bytes(dims, so, sp, query_pos0, docs_after_instruction),
+                                dtype=torch.uint8, device=Q.device)
+    _check(lib.br_attn_fwd_rope(ctypes.byref(dims), Q.data_ptr(), K.data_ptr(), V.data_ptr(), _ptr_i32(so),
+                                _ptr_i32(sp), out.data_ptr(), _dev_ptr(lse), float(softmax_scale), float(rope_theta),
+                                int(query_pos0), int(bool(docs_after_instruction)), int(bool(interleaved)),
                                 workspace.data_ptr(), workspace.numel(), _stream_handle(stream)))
     return (out, lse) if lse is not None else out
 

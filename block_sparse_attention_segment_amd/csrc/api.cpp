@@ -288,13 +288,65 @@ br_status check_attn_buffers(const void* Q, const void* K, const void* V, const 
 
 // Upload a validated attention plan into the workspace and launch it.  Q, out and lse rows are
 // addressed relative to token q_row_base.
+// The fused rotation's cos/sin table covers each distinct position once: the rotation runs
+// (instruction, each document, query) of all prompts merged into intervals of consecutive
+// positions; table row = interval offset + position - interval start.
+struct RopeTable {
+  std::vector<int32_t> iv_pos0, iv_off, run_row0;
+  int64_t rows = 0;
+  size_t off_pidx = 0, off_ivp = 0, off_ivo = 0, off_freq = 0, off_table = 0, bytes = 0;  // after the plan
+};
+
+void build_rope_table(const br::RopePlan& rp, int head_dim, size_t n_items, RopeTable* t) {
+  const size_t nr = rp.pos0.size();
+  std::vector<std::pair<int64_t, int64_t>> spans(nr);
+  for (size_t r = 0; r < nr; ++r) spans[r] = {rp.pos0[r], int64_t(rp.pos0[r]) + (rp.start[r + 1] - rp.start[r])};
+  std::sort(spans.begin(), spans.end());
+  t->iv_pos0.clear();
+  t->iv_off.clear();
+  int64_t cur0 = 0, cur1 = -1;
+  for (const auto& sp : spans) {
+    if (cur1 >= 0 && sp.first <= cur1) {
+      cur1 = std::max(cur1, sp.second);
+      continue;
+    }
+    if (cur1 >= 0) {
+      t->iv_pos0.push_back(int32_t(cur0));
+      t->iv_off.push_back(int32_t(t->rows));
+      t->rows += cur1 - cur0;
+    }
+    cur0 = sp.first;
+    cur1 = sp.second;
+  }
+  if (cur1 >= 0) {
+    t->iv_pos0.push_back(int32_t(cur0));
+    t->iv_off.push_back(int32_t(t->rows));
+    t->rows += cur1 - cur0;
+  }
+  t->run_row0.resize(nr);
+  for (size_t r = 0; r < nr; ++r) {
+    const size_t i = size_t(std::upper_bound(t->iv_pos0.begin(), t->iv_pos0.end(), rp.pos0[r]) - t->iv_pos0.begin()) - 1;
+    t->run_row0[r] = t->iv_off[i] + (rp.pos0[r] - t->iv_pos0[i]);
+  }
+  const size_t niv = t->iv_pos0.size();
+  t->off_pidx = 0;
+  t->off_ivp = br::align_up(n_items * 4, 256);
+  t->off_ivo = t->off_ivp + br::align_up(niv * 4, 16);
+  t->off_freq = t->off_ivo + br::align_up(niv * 4, 16);
+  t->off_table = br::align_up(t->off_freq + size_t(head_dim / 2) * 8, 256);
+  t->bytes = br::align_up(t->off_table + size_t(t->rows) * size_t(head_dim) * 4, 256);
+}
+
 br_status run_attn(const br_dims& dims, br::AttnPlan& plan, const void* Q, const void* K, const void* V, void* out,
                    float* lse, float softmax_scale, void* workspace, size_t workspace_bytes, hipStream_t stream,
                    int q_row_base, hipEvent_t kernel_start, hipEvent_t kernel_stop, bool pageable_upload = false,
-                   float sink_log2 = -__builtin_inff()) {
-  if (!workspace || workspace_bytes < plan.total_bytes)
+                   float sink_log2 = -__builtin_inff(), const br::RopePlan* rope = nullptr, int rope_layout = 0) {
+  RopeTable rt;
+  if (rope) build_rope_table(*rope, dims.head_dim, plan.items.size(), &rt);
+  const size_t need = plan.total_bytes + rt.bytes;
+  if (!workspace || workspace_bytes < need)
     return record(BR_ERR_WORKSPACE, "workspace is NULL or smaller than the workspace size query's " +
-                                        std::to_string(plan.total_bytes) + " bytes");
+                                        std::to_string(need) + " bytes");
   if (!aligned(workspace, 16)) return record(BR_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   // All arguments are valid: only now touch the runtime (device query for the schedule).
   int workgroups = 0;
@@ -320,6 +372,36 @@ br_status run_attn(const br_dims& dims, br::AttnPlan& plan, const void* Q, const
   }
 
   br::AttnLaunch a;
+  if (rope) {
+    // Per scheduled item, the table row of its first token (an item lies in one segment, i.e. one
+    // rotation run, whose positions are consecutive); then the intervals, frequencies and table.
+    unsigned char* wr = ws + plan.total_bytes;
+    std::vector<unsigned char> hx(rt.off_table, 0);
+    int32_t* pidx = reinterpret_cast<int32_t*>(hx.data() + rt.off_pidx);
+    for (size_t i = 0; i < plan.sched.size(); ++i) {
+      const int32_t row0 = plan.sched[i].row0;
+      const size_t r = size_t(std::upper_bound(rope->start.begin(), rope->start.end() - 1, row0) - rope->start.begin()) - 1;
+      pidx[i] = rt.run_row0[r] + (row0 - rope->start[r]);
+    }
+    std::memcpy(hx.data() + rt.off_ivp, rt.iv_pos0.data(), rt.iv_pos0.size() * 4);
+    std::memcpy(hx.data() + rt.off_ivo, rt.iv_off.data(), rt.iv_off.size() * 4);
+    std::memcpy(hx.data() + rt.off_freq, rope->inv_freq.data(), rope->inv_freq.size() * 8);
+    if (pageable_upload) {
+      hipError_t ce = hipMemcpyAsync(wr, hx.data(), hx.size(), hipMemcpyHostToDevice, stream);
+      if (ce != hipSuccess) return hip_fail(ce, "rotation table upload");
+    } else {
+      br_status st = upload(wr, hx.data(), hx.size(), stream);
+      if (st != BR_OK) return st;
+    }
+    hipError_t te = br::launch_rope_table(reinterpret_cast<const int32_t*>(wr + rt.off_ivp),
+                                          reinterpret_cast<const int32_t*>(wr + rt.off_ivo), int(rt.iv_pos0.size()),
+                                          rt.rows, dims.head_dim, reinterpret_cast<const double*>(wr + rt.off_freq),
+                                          reinterpret_cast<float*>(wr + rt.off_table), stream);
+    if (te != hipSuccess) return hip_fail(te, "rotation table kernel launch");
+    a.rope = rope_layout;
+    a.rope_cs = reinterpret_cast<const float*>(wr + rt.off_table);
+    a.item_pidx = reinterpret_cast<const int32_t*>(wr + rt.off_pidx);
+  }
   a.Q = static_cast<const uint16_t*>(Q);
   a.K = static_cast<const uint16_t*>(K);
   a.V = static_cast<const uint16_t*>(V);
@@ -616,6 +698,50 @@ br_status br_attn_fwd_sink(const br_dims* dims, const void* Q, const void* K, co
     const float sink_log2 = std::isinf(sink) ? sink : float(double(sink) * 1.4426950408889634);
     return run_attn(*dims, plan, Q, K, V, out, lse, softmax_scale, workspace, workspace_bytes, stream, 0, nullptr,
                     nullptr, false, sink_log2);
+  });
+}
+
+br_status br_attn_fwd_rope_workspace_bytes(const br_dims* dims, const int32_t* segment_offsets, const int32_t* seg_ptr,
+                                           int32_t query_pos0, int32_t docs_after_instruction, size_t* bytes) {
+  return guarded([&]() -> br_status {
+    if (!bytes) return record(BR_ERR_INVALID_ARG, "bytes is NULL");
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    if (docs_after_instruction != 0 && docs_after_instruction != 1)
+      return record(BR_ERR_INVALID_ARG, "docs_after_instruction must be 0 or 1");
+    br::AttnPlan plan;
+    e = br::build_attn_plan(*dims, segment_offsets, seg_ptr, &plan);
+    if (!e.ok()) return record(e);
+    br::RopePlan rp;
+    e = br::build_rope_plan(*dims, segment_offsets, seg_ptr, 10000.f, query_pos0, docs_after_instruction, &rp);
+    if (!e.ok()) return record(e);
+    RopeTable rt;
+    build_rope_table(rp, dims->head_dim, plan.items.size(), &rt);
+    *bytes = plan.total_bytes + rt.bytes;
+    return BR_OK;
+  });
+}
+
+br_status br_attn_fwd_rope(const br_dims* dims, const void* Q, const void* K, const void* V,
+                           const int32_t* segment_offsets, const int32_t* seg_ptr, void* out, float* lse,
+                           float softmax_scale, float rope_theta, int32_t query_pos0, int32_t docs_after_instruction,
+                           int32_t interleaved, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return guarded([&]() -> br_status {
+    br::Error e = br::validate_dims(dims);
+    if (!e.ok()) return record(e);
+    if (docs_after_instruction != 0 && docs_after_instruction != 1)
+      return record(BR_ERR_INVALID_ARG, "docs_after_instruction must be 0 or 1");
+    if (interleaved != 0 && interleaved != 1) return record(BR_ERR_INVALID_ARG, "interleaved must be 0 or 1");
+    br_status st = check_attn_buffers(Q, K, V, out, lse, softmax_scale);
+    if (st != BR_OK) return st;
+    br::AttnPlan plan;
+    e = br::build_attn_plan(*dims, segment_offsets, seg_ptr, &plan);
+    if (!e.ok()) return record(e);
+    br::RopePlan rp;
+    e = br::build_rope_plan(*dims, segment_offsets, seg_ptr, rope_theta, query_pos0, docs_after_instruction, &rp);
+    if (!e.ok()) return record(e);
+    return run_attn(*dims, plan, Q, K, V, out, lse, softmax_scale, workspace, workspace_bytes, stream, 0, nullptr,
+                    nullptr, false, -__builtin_inff(), &rp, interleaved ? 2 : 1);
   });
 }
 
@@ -1261,18 +1387,18 @@ br_status br_rank_prompts_timed(const br_dims* dims, const void* Q, const void* 
     r.row_blocks = sp.row_blocks;
     r.n_docs = sp.n_docs;
     r.scale_log2 = a.scale_log2;
-    // The side stream, for large batches when the call is not timed (if it cannot be created, the
-    // step runs on the caller's stream alone).
+    // The side stream, for large batches (if it cannot be created, the step runs on the caller's
+    // stream alone).  Events around the attention kernel are recorded on the caller's stream in
+    // either case, so a timed step measures the kernel as it runs in an untimed one.
     SideStream* side = nullptr;
-    if (!kernel_start && !kernel_stop && dims->total_tokens >= kSideStreamMinTokens && side_stream(&side) != hipSuccess) {
+    if (dims->total_tokens >= kSideStreamMinTokens && side_stream(&side) != hipSuccess) {
       side = nullptr;
       (void)hipGetLastError();  // clear it, so the launches below do not report it
     }
     if (!side) {
       // Everything on the caller's stream, the split-key merge in the launch of the readout's
       // partial kernel: for short batches (the fork and join cost more than the overlap saves:
-      // measured at 12,864 tokens) and when timed (the events around the attention kernel then
-      // see it alone).
+      // measured at 12,864 tokens).
       a.defer_merge = true;
       he = br::launch_attn(a, stream);
       if (he != hipSuccess) return hip_fail(he, "attention kernel launch");

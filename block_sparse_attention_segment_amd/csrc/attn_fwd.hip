@@ -44,9 +44,12 @@
 //           keys a quarter-wave reads at one unit fall in 16 different bank groups;
 //   V tile: unit c of row k at unit c ^ swz_v(k), so a half-wave's transposing read (4 keys x 4
 //           units) touches 16 different bank groups.
-// Q fragments use a permutation of the head dimension inside each 16-wide MFMA step (lane half
-// 0 takes units 0..D/16-1 of a row, half 1 the rest) so a lane loads one contiguous half-row;
-// the K fragments are read with the same permutation, and the contraction over d is unchanged.
+// Q fragments use a permutation of the head dimension inside each 16-wide MFMA step: with
+// H = D/32, k-step st of lane half h takes unit (st % H) + H h + 2H (st / H) of a row, so a lane
+// holds units u and u + D/16 (elements e and e + D/2) together; the K fragments are read with the
+// same permutation, and the contraction over d is unchanged.  Holding both halves of a row lets
+// the rotary embedding be applied to Q in registers: pairs (e, e + D/2) in the split layout, and
+// pairs inside a unit in the adjacent layout (the ROPE variants of the kernel).
 //
 // Query rows of long prompts are split over key chunks; their fp32 partials (m, l, o) are
 // combined by attn_merge_kernel.
@@ -122,13 +125,18 @@ __device__ __forceinline__ void wait_vm_barrier_dyn(int n) {
   }
 }
 
-template <int D, int G, int NS>
+// ROPE: 0 Q is used as given; 1 or 2 each item's Q rows are rotated after they are read (split
+// or adjacent pairs) with cos/sin from `rope_cs` ([table row][D/2 pairs][cos, sin] fp32), the
+// item's first token at table row item_pidx[item] and its later tokens at the rows after it.
+template <int D, int G, int NS, int ROPE>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                        const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                                                        float* __restrict__ lse, const AttnItem* __restrict__ items,
                                                        const int32_t* __restrict__ ranges, float* __restrict__ part_o,
                                                        float* __restrict__ part_ml, int Hq, int Hkv, float scale_log2,
-                                                       int q_row_base, float sink_log2) {
+                                                       int q_row_base, float sink_log2,
+                                                       const float* __restrict__ rope_cs,
+                                                       const int32_t* __restrict__ item_pidx) {
   constexpr int TM = kRowsPerTile / G;  // tokens per item
   constexpr int BN = kFwdKeys;
   constexpr int RB = 2 * D;             // bytes per row of one head
@@ -168,10 +176,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
   const uint32_t k_lds = lds_addr_of(kring) + 1024 * NDMA * w;
   const uint32_t v_lds = lds_addr_of(vring) + 1024 * NDMA * w;
   const uint32_t q_lds = lds_addr_of(qbuf) + 32 * RB * w;
-  // K fragment of k-step st for this lane: key n, unit st + half * DSTEPS (head-dim permutation).
+  // K fragment of k-step st for this lane: key n, unit qunit(st) (the head-dim permutation).
+  constexpr int HU = DSTEPS / 2;  // units of each half of the head dimension held by one lane
+  auto qunit = [&](int st) { return (st % HU) + HU * half + 2 * HU * (st / HU); };
   uint32_t kofs[DSTEPS];
 #pragma unroll
-  for (int st = 0; st < DSTEPS; ++st) kofs[st] = uint32_t(n * RB + 16 * ((st + half * DSTEPS) ^ swz_k(n)));
+  for (int st = 0; st < DSTEPS; ++st) kofs[st] = uint32_t(n * RB + 16 * (qunit(st) ^ swz_k(n)));
   // Transposing V reads: in each 16-lane group (s = lane % 16, head-dim half dh = (lane / 16) % 2)
   // lane s points at key 4 half + s / 4 and head-dim element 16 dh + 4 (s % 4) of a 32-wide block;
   // keys 16 m (+8) shift the row by a multiple of 8, which leaves the swizzle unchanged.
@@ -249,6 +259,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
   const uint16_t* const k_base = K + g * D;
   const uint16_t* const v_base = V + g * D;
   auto issue_k = [&](int start, int code, int slot) {  // "no tile" has start 0 and no keys
+    start = __builtin_amdgcn_readfirstlane(start);  // uniform: keeps the offsets in scalar registers
+    code = __builtin_amdgcn_readfirstlane(code);
     const uint32_t s0 = uint32_t(start) * uint32_t(kv_stride * 2);
     const uint32_t end = s0 + uint32_t(code_keys(code)) * uint32_t(kv_stride * 2);
     const rsrc_t r = make_rsrc(k_base, int(end));
@@ -256,6 +268,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
     for (int i = 0; i < NDMA; ++i) buf_load16_lds(r, k_lds + slot * TB + 1024 * i, kdma[i], s0);
   };
   auto issue_v = [&](int start, int code, int slot) {  // "no tile" has start 0 and no keys
+    start = __builtin_amdgcn_readfirstlane(start);
+    code = __builtin_amdgcn_readfirstlane(code);
     const uint32_t s0 = uint32_t(start) * uint32_t(kv_stride * 2);
     const uint32_t end = s0 + uint32_t(code_keys(code)) * uint32_t(kv_stride * 2);
     const rsrc_t r = make_rsrc(v_base, int(end));
@@ -382,6 +396,32 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
 #pragma unroll
       for (int st = 0; st < DSTEPS; ++st) qf[st] = *reinterpret_cast<const u32x4_t*>(&qbuf[qw + kofs[st]]);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the buffer is reused
+      if constexpr (ROPE != 0) {
+        // This lane's token: cos/sin of its table row, then the rotation of qf in registers, with
+        // the arithmetic of the separate rotation kernel (fp32, rounded once to bf16).
+        const float* tr = rope_cs + int64_t(item_pidx[code_it(s_code)] + tt) * D;
+#pragma unroll
+        for (int st = 0; st < (ROPE == 1 ? HU : DSTEPS); ++st) {
+          const int u = qunit(st);
+          if constexpr (ROPE == 1) {
+            // units u (elements 8u..8u+7) and u + D/16 hold the pairs 8u .. 8u+7
+            const f32x4_t c0 = *reinterpret_cast<const f32x4_t*>(tr + 16 * u);
+            const f32x4_t c1 = *reinterpret_cast<const f32x4_t*>(tr + 16 * u + 4);
+            const f32x4_t c2 = *reinterpret_cast<const f32x4_t*>(tr + 16 * u + 8);
+            const f32x4_t c3 = *reinterpret_cast<const f32x4_t*>(tr + 16 * u + 12);
+            const float cs[8] = {c0[0], c0[2], c1[0], c1[2], c2[0], c2[2], c3[0], c3[2]};
+            const float sn[8] = {c0[1], c0[3], c1[1], c1[3], c2[1], c2[3], c3[1], c3[3]};
+            rope_rotate_split8(qf[st], qf[st + HU], cs, sn);
+          } else {
+            // unit u holds the pairs 4u .. 4u+3
+            const f32x4_t c0 = *reinterpret_cast<const f32x4_t*>(tr + 8 * u);
+            const f32x4_t c1 = *reinterpret_cast<const f32x4_t*>(tr + 8 * u + 4);
+            const float cs[4] = {c0[0], c0[2], c1[0], c1[2]};
+            const float sn[4] = {c0[1], c0[3], c1[1], c1[3]};
+            rope_rotate_adjacent4(qf[st], cs, sn);
+          }
+        }
+      }
       q_state = 1;
       q_next = code_it(s_code) + 1;
     }
@@ -613,9 +653,18 @@ static hipError_t launch_attn_t(const AttnLaunch& a, hipStream_t stream) {
       hipError_t e = hipEventRecord(a.ev_start, stream);
       if (e != hipSuccess) return e;
     }
-    attn_fwd_kernel<D, G, kFwdSlots><<<grid, 256, 0, stream>>>(a.Q, a.K, a.V, a.O, a.lse, a.items, a.ranges, a.part_o,
-                                                               a.part_ml, a.num_q_heads, a.num_kv_heads, a.scale_log2,
-                                                               a.q_row_base, a.sink_log2);
+    if (a.rope == 0)
+      attn_fwd_kernel<D, G, kFwdSlots, 0><<<grid, 256, 0, stream>>>(
+          a.Q, a.K, a.V, a.O, a.lse, a.items, a.ranges, a.part_o, a.part_ml, a.num_q_heads, a.num_kv_heads,
+          a.scale_log2, a.q_row_base, a.sink_log2, nullptr, nullptr);
+    else if (a.rope == 1)
+      attn_fwd_kernel<D, G, kFwdSlots, 1><<<grid, 256, 0, stream>>>(
+          a.Q, a.K, a.V, a.O, a.lse, a.items, a.ranges, a.part_o, a.part_ml, a.num_q_heads, a.num_kv_heads,
+          a.scale_log2, a.q_row_base, a.sink_log2, a.rope_cs, a.item_pidx);
+    else
+      attn_fwd_kernel<D, G, kFwdSlots, 2><<<grid, 256, 0, stream>>>(
+          a.Q, a.K, a.V, a.O, a.lse, a.items, a.ranges, a.part_o, a.part_ml, a.num_q_heads, a.num_kv_heads,
+          a.scale_log2, a.q_row_base, a.sink_log2, a.rope_cs, a.item_pidx);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.ev_stop) {

@@ -82,6 +82,29 @@ __device__ __forceinline__ void buf_store8(u32x2_t v, rsrc_t r, uint32_t byte_of
 __device__ __forceinline__ void buf_store16(u32x4_t v, rsrc_t r, uint32_t byte_offset) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_offset, 0, 0);
 }
+// Rotary embedding of packed bf16 pairs, fp32 arithmetic, one rounding to bf16 (shared by the
+// rotation kernel and the attention kernel's in-register rotation of Q, so both round alike).
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+// Split layout: x0 holds the first entries of pairs 0..7 (two per dword), x1 the second entries.
+__device__ __forceinline__ void rope_rotate_split8(u32x4_t& x0, u32x4_t& x1, const float* cs, const float* sn) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a0 = bf16_lo(x0[i]), a1 = bf16_hi(x0[i]), b0 = bf16_lo(x1[i]), b1 = bf16_hi(x1[i]);
+    const int j = 2 * i;
+    x0[i] = pack_bf16x2(fmaf(a0, cs[j], -b0 * sn[j]), fmaf(a1, cs[j + 1], -b1 * sn[j + 1]));
+    x1[i] = pack_bf16x2(fmaf(a0, sn[j], b0 * cs[j]), fmaf(a1, sn[j + 1], b1 * cs[j + 1]));
+  }
+}
+// Adjacent layout: dword i of x is pair i (first entry in the low half).
+__device__ __forceinline__ void rope_rotate_adjacent4(u32x4_t& x, const float* cs, const float* sn) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = bf16_lo(x[i]), b = bf16_hi(x[i]);
+    x[i] = pack_bf16x2(fmaf(a, cs[i], -b * sn[i]), fmaf(a, sn[i], b * cs[i]));
+  }
+}
+
 // Direct-to-LDS buffer load (gfx950 buffer_load_dwordx4 ... lds): lane l's 16 bytes at
 // soffset + byte_offset go to LDS byte address lds_addr + 16 l (lds_addr: wave-uniform, from
 // lds_addr_of).  Loads whose soffset + byte_offset reaches the resource's size write zeros (the

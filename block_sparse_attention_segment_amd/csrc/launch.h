@@ -25,6 +25,9 @@ struct AttnLaunch {
   float scale_log2;         // softmax scale * log2(e)
   int q_row_base = 0;       // token index of Q/O/lse row 0 (the corpus length for query-only runs)
   float sink_log2 = -__builtin_inff();  // additive sink b * log2(e); -inf: none
+  int rope = 0;                      // 0 none; 1 / 2: rotate Q in the kernel (split / adjacent pairs)
+  const float* rope_cs = nullptr;    // [table rows][D/2][cos, sin]
+  const int32_t* item_pidx = nullptr;  // per scheduled item: table row of its first token
   hipEvent_t ev_start = nullptr, ev_stop = nullptr;  // optional, recorded around the main kernel
   bool defer_merge = false;  // leave the split-key merge to launch_merge_doc_scores
 };
@@ -107,5 +110,8 @@ struct RopeLaunch {
   bool adjacent;            // pairs (2k, 2k+1) instead of (k, k + d/2)
 };
 hipError_t launch_rope(const RopeLaunch& a, hipStream_t stream);
+// cos/sin table of the attention's fused Q rotation ([rows][head_dim / 2] pairs of fp32).
+hipError_t launch_rope_table(const int32_t* iv_pos0, const int32_t* iv_off, int n_iv, int64_t rows, int head_dim,
+                             const double* inv_freq, float* table, hipStream_t stream);
 
 }  // namespace br

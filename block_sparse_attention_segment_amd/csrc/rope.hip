@@ -25,6 +25,15 @@ namespace br {
 constexpr double kRopeTwoPi = 6.283185307179586476925286766559;
 constexpr double kRopeInvTwoPi = 0.15915494309189533576888376337251;
 
+// cos and sin of pos * inv_freq: the angle is formed and reduced modulo 2*pi in fp64, sin/cos in
+// fp32 (shared by the rotation kernel and the cos/sin table of the attention's fused rotation).
+__device__ __forceinline__ void rope_cos_sin(double pos, double inv_freq, float* cs, float* sn) {
+  const double ang = pos * inv_freq;
+  const double turns = rint(ang * kRopeInvTwoPi);
+  const float r = float(fma(-turns, kRopeTwoPi, ang));
+  sincosf(r, sn, cs);
+}
+
 struct RopeArgs {
   const uint16_t* q;
   uint16_t* q_out;
@@ -37,31 +46,15 @@ struct RopeArgs {
   int n_runs, q_heads, k_heads;
 };
 
-__device__ __forceinline__ float rope_lo(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float rope_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-
-// Rotate the 8 pairs of one head: `a` and `b` hold the pairs' first and second entries
-// (split layout) or eight interleaved (first, second) entries over two vectors (adjacent layout).
+// Rotate the 8 pairs of one head: x0 and x1 hold the pairs' first and second entries (split
+// layout) or eight interleaved (first, second) entries over two vectors (adjacent layout).
 template <bool kAdjacent>
 __device__ __forceinline__ void rope_rotate8(u32x4_t& x0, u32x4_t& x1, const float* cs, const float* sn) {
   if constexpr (!kAdjacent) {
-    // x0: first entries of pairs 0..7 (two per dword), x1: second entries of the same pairs.
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a0 = rope_lo(x0[i]), a1 = rope_hi(x0[i]), b0 = rope_lo(x1[i]), b1 = rope_hi(x1[i]);
-      const int j = 2 * i;
-      x0[i] = pack_bf16x2(fmaf(a0, cs[j], -b0 * sn[j]), fmaf(a1, cs[j + 1], -b1 * sn[j + 1]));
-      x1[i] = pack_bf16x2(fmaf(a0, sn[j], b0 * cs[j]), fmaf(a1, sn[j + 1], b1 * cs[j + 1]));
-    }
+    rope_rotate_split8(x0, x1, cs, sn);
   } else {
-    // dword i of x0 is pair i (first entry low), dword i of x1 is pair 4 + i.
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = rope_lo(x0[i]), b = rope_hi(x0[i]);
-      x0[i] = pack_bf16x2(fmaf(a, cs[i], -b * sn[i]), fmaf(a, sn[i], b * cs[i]));
-      const float c = rope_lo(x1[i]), d = rope_hi(x1[i]);
-      x1[i] = pack_bf16x2(fmaf(c, cs[4 + i], -d * sn[4 + i]), fmaf(c, sn[4 + i], d * cs[4 + i]));
-    }
+    rope_rotate_adjacent4(x0, cs, sn);          // pairs 0..3
+    rope_rotate_adjacent4(x1, cs + 4, sn + 4);  // pairs 4..7
   }
 }
 
@@ -113,13 +106,7 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
   const double pos = double(a.run_pos0[lo]) + double(row - a.run_start[lo]);
   float cs[8], sn[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    // pair index: 8 consecutive pairs per thread in both layouts
-    const double ang = pos * a.inv_freq[8 * c + j];
-    const double turns = rint(ang * kRopeInvTwoPi);
-    const float r = float(fma(-turns, kRopeTwoPi, ang));
-    sincosf(r, &sn[j], &cs[j]);
-  }
+  for (int j = 0; j < 8; ++j) rope_cos_sin(pos, a.inv_freq[8 * c + j], &cs[j], &sn[j]);  // 8 consecutive pairs
   if (a.q_heads) rope_rotate_heads<D, kAdjacent>(a.q, a.q_out, a.q_heads, row, c, cs, sn);
   if (a.k_heads) rope_rotate_heads<D, kAdjacent>(a.k, a.k_out, a.k_heads, row, c, cs, sn);
 }
@@ -135,6 +122,36 @@ hipError_t launch(const RopeArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Table of cos/sin per distinct position: table row t is position iv_pos0[i] + (t - iv_off[i])
+// for the interval i holding row t; entry [t][k] = (cos, sin) of pair k.  One thread per entry.
+__global__ __launch_bounds__(256) void rope_table_kernel(const int32_t* __restrict__ iv_pos0,
+                                                         const int32_t* __restrict__ iv_off, int n_iv, int64_t rows,
+                                                         int half, const double* __restrict__ inv_freq,
+                                                         float2* __restrict__ table) {
+  const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= rows * half) return;
+  const int64_t t = e / half;
+  const int k = int(e % half);
+  int lo = 0, hi = n_iv - 1;  // the last interval starting at or before row t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (iv_off[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const double pos = double(iv_pos0[lo]) + double(t - iv_off[lo]);
+  float cs, sn;
+  rope_cos_sin(pos, inv_freq[k], &cs, &sn);
+  table[e] = float2{cs, sn};
+}
+
+hipError_t launch_rope_table(const int32_t* iv_pos0, const int32_t* iv_off, int n_iv, int64_t rows, int head_dim,
+                             const double* inv_freq, float* table, hipStream_t stream) {
+  const int64_t n = rows * (head_dim / 2);
+  if (n <= 0) return hipSuccess;
+  rope_table_kernel<<<dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream>>>(
+      iv_pos0, iv_off, n_iv, rows, head_dim / 2, inv_freq, reinterpret_cast<float2*>(table));
+  return hipGetLastError();
+}
 
 hipError_t launch_rope(const RopeLaunch& l, hipStream_t stream) {
   if (l.rows <= 0 || (l.q_heads == 0 && l.k_heads == 0)) return hipSuccess;

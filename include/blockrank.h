@@ -212,7 +212,7 @@ br_status br_attn_routed_fwd(const br_dims* dims, const void* Q, const void* K, 
  * theirs.  workspace: >= br_rank_workspace_bytes(), 16-byte aligned.  br_rank_prompts_timed
  * also records kernel_start / kernel_stop (hipEvent_t, may be NULL) on `stream` immediately
  * around the attention kernel.
- * Streams: for batches of at least 32,768 tokens (and no kernel events), the readout and rank,
+ * Streams: for batches of at least 32,768 tokens (timed or not), the readout and rank,
  * which read only the inputs, run on a stream the library owns (one per device, default
  * priority, created on first use and kept until the process ends), forked from `stream` after
  * the plan upload and joined back into it; work enqueued on `stream` afterwards, and a
@@ -235,6 +235,27 @@ br_status br_rank_prompts_timed(const br_dims* dims, const void* Q, const void* 
                                 void* out, float* lse, float* scores, float* head_scores, int32_t* order,
                                 float softmax_scale, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream, hipEvent_t kernel_start, hipEvent_t kernel_stop);
+
+/*
+ * Block-sparse attention with the rotary embedding of Q applied inside the attention kernel
+ * (BlockRank summary, section 3.4 "Permutation-invariant position embeddings"): Q is given
+ * unrotated and each work item rotates its Q rows in registers as it reads them, with cos/sin
+ * from a table of the prompts' distinct positions (built on the device by the rotation kernel's
+ * own code, so the rotated values equal br_rope_fwd's); K must already be rotated with the same
+ * rule (br_rope_fwd with Q = NULL).  rope_theta, query_pos0, docs_after_instruction and
+ * interleaved as for br_rope_fwd.  Output: bit-identical to br_rope_fwd on Q followed by
+ * br_attn_fwd.  workspace: >= br_attn_fwd_rope_workspace_bytes() (the attention plan plus the
+ * table: (distinct positions) x d x 4 bytes), 256-byte aligned.  Errors as br_attn_fwd and
+ * br_rope_fwd.
+ */
+br_status br_attn_fwd_rope_workspace_bytes(const br_dims* dims, const int32_t* segment_offsets,
+                                           const int32_t* seg_ptr, int32_t query_pos0,
+                                           int32_t docs_after_instruction, size_t* bytes);
+br_status br_attn_fwd_rope(const br_dims* dims, const void* Q, const void* K, const void* V,
+                           const int32_t* segment_offsets, const int32_t* seg_ptr, void* out, float* lse,
+                           float softmax_scale, float rope_theta, int32_t query_pos0,
+                           int32_t docs_after_instruction, int32_t interleaved, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Query-only attention over a cached corpus ("prefill once, score many queries"; BlockSearch,

@@ -205,3 +205,51 @@ def test_rope_long_prompt_sampled_rows():
     rt = torch.as_tensor(rows, device="cuda")
     check_rotation(Qr[rt], orc.rope_apply(w.Q[rows], pos[rows], 10000.0), w.Q[rows], False, "long Q")
     check_rotation(Kr[rt], orc.rope_apply(w.K[rows], pos[rows], 10000.0), w.K[rows], False, "long K")
+
+
+FUSED = [  # seed, Hq, Hkv, d, rule, interleaved
+    (0, 32, 8, 128, BLOCKRANK, False), (1, 8, 2, 64, BLOCKSEARCH, True), (2, 16, 16, 128, BLOCKRANK, True),
+    (3, 8, 1, 64, BLOCKRANK, False), (4, 32, 4, 128, BLOCKSEARCH, False),
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=[f"s{c[0]}_Hq{c[1]}_Hkv{c[2]}_d{c[3]}_q{c[4]['query_pos0']}_i{int(c[5])}"
+                                             for c in FUSED])
+def test_q_rotated_inside_attention_is_bit_identical(case):
+    """br_attn_fwd_rope (K rotated beforehand, Q rotated by the attention kernel from a cos/sin
+    table of the distinct positions) equals br_rope_fwd on Q and K followed by br_attn_fwd, bit
+    for bit, output and lse; and it matches the oracle's rotate-then-attend rows."""
+    seed, hq, hkv, d, rule, inter = case
+    rng = random.Random(1700 + seed)
+    prompts = random_prompts(rng, batch=3, p_max=60, n_max=7, l_max=140, q_max=70, p_min=0 if seed % 2 else 1)
+    w = workloads.make_custom(prompts, hq, hkv, d, 1, 1800 + seed)
+    dev = upload(w)
+    log(f"[rope fused] seed={seed} Hq={hq} Hkv={hkv} d={d} {rule} interleaved={inter} T={w.total_tokens}")
+    Qr, Kr = br.rope(dev["Q"], dev["K"], w.segment_offsets, w.seg_ptr, 10000.0, interleaved=inter, **rule)
+    ref_out, ref_lse = br.attn_fwd(Qr, Kr, dev["V"], w.segment_offsets, w.seg_ptr, lse=True)
+    _, Kr2 = br.rope(None, dev["K"], w.segment_offsets, w.seg_ptr, 10000.0, interleaved=inter, **rule)
+    out, lse = br.attn_fwd_rope(dev["Q"], Kr2, dev["V"], w.segment_offsets, w.seg_ptr, 10000.0, interleaved=inter,
+                                lse=True, **rule)
+    torch.cuda.synchronize()
+    assert torch.equal(Kr2, Kr)
+    assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+    # and against the oracle: rotate in fp64, round to bf16 as the kernel does, attend
+    pos = orc.rope_positions(w.segment_offsets, w.seg_ptr, rule["query_pos0"], rule["docs_after_instruction"])
+    Qo = round_bf16(orc.rope_apply(w.Q, pos, 10000.0, inter))
+    Ko = round_bf16(orc.rope_apply(w.K, pos, 10000.0, inter))
+    ref, _ = orc.attn_rows(Qo, Ko, w.V, w.segment_offsets, w.seg_ptr)
+    check_attn(out, ref, what="fused rope attention")
+
+
+def test_q_rotated_inside_attention_long_prompt():
+    """The long ranking prompt (split-key query rows, 100,096 tokens): bit-identical to the separate
+    rotation followed by attention."""
+    w = workloads.make("long", 0)
+    dev = upload(w)
+    log(f"[rope fused] long prompt T={w.total_tokens}")
+    Qr, Kr = br.rope(dev["Q"], dev["K"], w.segment_offsets, w.seg_ptr, 10000.0)
+    ref = br.attn_fwd(Qr, Kr, dev["V"], w.segment_offsets, w.seg_ptr)
+    del Qr
+    out = br.attn_fwd_rope(dev["Q"], Kr, dev["V"], w.segment_offsets, w.seg_ptr, 10000.0)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
