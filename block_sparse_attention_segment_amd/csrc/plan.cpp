@@ -323,9 +323,11 @@ Error build_routed_plan(const br_dims& dims, const int32_t* so, const int32_t* s
 
 int64_t attn_item_cost(const AttnItem& it) {
   // Measured on gfx950: a key tile of a split query chunk (keys streamed from memory, fp32
-  // partials) costs about 1.3 document key tiles; loading a row tile's queries and storing its
-  // outputs costs about four key tiles.
-  return it.slot < 0 ? 4 * int64_t(it.ntiles) + 16 : 5 * int64_t(it.ntiles) + 24;
+  // partials) costs about 1.25 document key tiles; loading a row tile's queries and storing its
+  // outputs about two key tiles (the kernel overlaps them with the neighbouring items' tiles).
+  // Against per-item costs of 1, 4 and 8 key tiles (same split-chunk slope): 2 was fastest or
+  // within noise at the worked, long, batched and ragged shapes (worked -4%, batched -1% from 4).
+  return it.slot < 0 ? 4 * int64_t(it.ntiles) + 8 : 5 * int64_t(it.ntiles) + 16;
 }
 
 void schedule_attn_plan(int num_kv_heads, int workgroups, AttnPlan* plan) {
