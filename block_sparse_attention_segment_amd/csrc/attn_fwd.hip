@@ -595,12 +595,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
 #pragma unroll
       for (int b = 0; b < DBLK; ++b) o[b] = f32x16_t{};
     }
-    // The Q buffer is free once the epilogue that followed the last Q read is done.
+    // The Q buffer is free once the epilogue that followed the last Q read is done.  Past the
+    // workgroup's last item nothing is loaded: a load of no rows still writes zeros into the
+    // buffer, and the last item's epilogue stages its rows there without waiting for it.
     if (q_state == 2) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // staged rows read back before the refill
-      issue_q(q_next);
-      since_q = 0;
-      ex_prev += DSTEPS;
+      if (q_next < it_end) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // staged rows read back before the refill
+        issue_q(q_next);
+        since_q = 0;
+        ex_prev += DSTEPS;
+      }
       q_state = 0;
     } else if (q_state == 1) {
       q_state = 2;
