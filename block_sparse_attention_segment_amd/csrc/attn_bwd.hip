@@ -12,11 +12,11 @@
 //                        4 waves of 32 rows); it also forms Dr for its rows: per 64-key tile S^T = K Q^T and dP^T = V dO^T
 //                        (keys on M), dS^T in fp32, dQ^T += K^T dS^T with dS rounded to bf16
 //                        and K^T fragments from transposing LDS reads (as V^T in the forward).
-//   attn_bwd_dkv_kernel  key-major: 64 keys of one KV head per workgroup (2 waves of 32 keys);
-//                        the rows that read them stream through LDS 64 (token, head) rows at a
-//                        time (the next step's rows are loaded into registers meanwhile):
-//                        S = Q K^T and dP = dO V^T (rows on M), then dV^T += dO^T P and
-//                        dK^T += Q^T dS with the row-side operands read transposed from LDS.
+//   attn_bwd_dkv_kernel  key-major: 64 keys of one KV head per workgroup (4 waves of 16 keys,
+//                        16x16x32 products); the rows that read them stream through LDS 64
+//                        (token, head) rows at a time by direct-to-LDS loads, the next step's
+//                        in flight: S = Q K^T and dP = dO V^T (rows on M), then dV^T += dO^T P
+//                        and dK^T += Q^T dS with the row-side operands read transposed from LDS.
 // Long row or key ranges are split; their fp32 partials are summed by the merge kernels in a
 // fixed order, so results are deterministic.  Outputs are fp32.
 #include "device_common.h"
@@ -212,155 +212,199 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_merge_kernel(float* __restric
   *reinterpret_cast<f32x4_t*>(dQ + (int64_t(tok) * Hq + h) * D + 4 * ch) = a;
 }
 
+// MFMA v_mfma_f32_16x16x32_bf16 lane layout: A (16 x 32, M x K): lane l holds A[l % 16][8 (l / 16) + t];
+// B (32 x 16, K x N): lane l holds B[8 (l / 16) + t][l % 16]; D (16 x 16): lane l, register r holds
+// D[4 (l / 16) + r][l % 16].
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Key-major dK / dV.  A workgroup of four waves takes one item (at most 64 keys of one segment
+// and KV head); wave w holds keys k0 + 16 w .. + 15, one per lane column, with their K and V
+// fragments (B operands of S = Q K^T and dP = dO V^T) and fp32 dK^T, dV^T accumulators in
+// registers.  The rows that read the keys stream through LDS RS (token, head) rows per step
+// (token-major, G heads per token), loaded by direct-to-LDS loads into two slots: step i + 1 is
+// in flight while step i is computed, with one barrier per step.  Per step and wave:
+//   S = Q K^T, dP = dO V^T          rows on M (16-row blocks), keys on N, d as K
+//   P = exp2(S scale log2e - lse log2e) on allowed pairs, dS = P (dP - Dr)
+//   dV^T += dO^T P, dK^T += Q^T dS  d on M, keys on N, rows as K (32 rows per product), with dO^T
+//                                   and Q^T read from LDS by transposing reads
+// The 32 rows of one product are, for lane group u = l / 16, rows 4u .. 4u + 3 and 16 + 4u ..
+// 16 + 4u + 3 of a 32-row half step: the rows an S register block already holds, so P and dS
+// go from the S layout to the B operand without any exchange.
+// LDS rows are 2D bytes, 16-byte unit c of row r stored at c ^ swz(r), so that the row reads (16
+// rows at one unit) and the transposing reads (8 rows x one unit pair) touch distinct banks.
 template <int D, int G>
-__global__ __launch_bounds__(128) void attn_bwd_dkv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                                                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                                                           const float* __restrict__ lse, const float* __restrict__ dvec,
-                                                           float* __restrict__ dK, float* __restrict__ dV,
-                                                           const KvItem* __restrict__ items, float* __restrict__ part_dkv,
-                                                           int Hq, int Hkv, int kv_slots, float scale, float scale_log2) {
-  constexpr int RS = 64;                     // rows per step: two 32-row MFMA blocks
-  constexpr int TR = RS / G;                 // row tokens per step (rows token-major, G heads each)
-  constexpr int VROW = D == 128 ? 160 : 96;  // Q and dO rows: row reads and transposing reads
-  constexpr int DSTEPS = D / 16, DBLK = D / 32, KCH = D / 8;
-  constexpr int LPT = RS * KCH / 128;        // 16-byte chunks per thread per tensor per step
-  __shared__ __align__(16) uint16_t sq[RS * VROW];
-  __shared__ __align__(16) uint16_t sd[RS * VROW];
-  __shared__ float sl[RS], sr[RS];
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                             const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                                                             const float* __restrict__ lse, const float* __restrict__ dvec,
+                                                             float* __restrict__ dK, float* __restrict__ dV,
+                                                             const KvItem* __restrict__ items, float* __restrict__ part_dkv,
+                                                             int Hq, int Hkv, int kv_slots, float scale, float scale_log2) {
+  constexpr int RS = 64;                // rows per step
+  constexpr int TR = RS / G;            // row tokens per step
+  constexpr int RB = 2 * D;             // bytes per row
+  constexpr int UPR = D / 8;            // 16-byte units per row
+  constexpr int KPI = 1024 / RB;        // rows per direct-to-LDS wave instruction
+  constexpr int NDMA = RS / KPI / 4;    // such instructions per wave per tensor per step
+  constexpr int KS = D / 32;            // k-steps of S and dP
+  constexpr int DB = D / 16;            // 16-wide head-dim blocks of dK^T and dV^T
+  constexpr int NRB = RS / 16;          // 16-row blocks per step
+  constexpr int TILE = RS * RB;         // bytes per tensor per slot
+  static_assert(NDMA >= 1 && NDMA * KPI * 4 == RS, "a step's rows split over four waves");
+  __shared__ __align__(1024) uint8_t sq[2][TILE];
+  __shared__ __align__(1024) uint8_t sd[2][TILE];
+  __shared__ __align__(256) float sl[2][64];  // the rows' lse (natural log), then their Dr
+  __shared__ __align__(256) float sr[2][64];
 
   const int g = blockIdx.x % Hkv;
   const KvItem it = items[blockIdx.x / Hkv];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, half = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, u = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q_stride = Hq * D, kv_stride = Hkv * D;
-  const int key = it.k0 + 32 * w + n;  // this lane's key (N index of every product)
+  const int key = it.k0 + 16 * w + m;  // this lane's key (N index of every product)
 
-  // This lane's key row: K and V fragments (B operands of S = Q K^T and dP = dO V^T).
+  auto swz = [](int r) { return D == 128 ? 2 * (r & 7) + ((r >> 3) & 1) : 2 * ((r >> 1) & 3) + ((r >> 3) & 1); };
+
+  // K and V fragments: lane l holds K[key][32 st + 8 u + t] (B operand of S = Q K^T).
   const int nkeys = it.k_limit - it.k0;
   const rsrc_t rk = make_rsrc(K + int64_t(it.k0) * kv_stride + g * D, nkeys * kv_stride * 2);
   const rsrc_t rv = make_rsrc(V + int64_t(it.k0) * kv_stride + g * D, nkeys * kv_stride * 2);
-  const uint32_t k_off = uint32_t(((32 * w + n) * kv_stride + 8 * half) * 2);
-  u32x4_t kf[DSTEPS], vf[DSTEPS];
+  const uint32_t k_off = uint32_t(((16 * w + m) * kv_stride + 8 * u) * 2);
+  u32x4_t kf[KS], vf[KS];
 #pragma unroll
-  for (int s = 0; s < DSTEPS; ++s) {
-    kf[s] = buf_load16(rk, k_off + 32 * s);
-    vf[s] = buf_load16(rv, k_off + 32 * s);
+  for (int st = 0; st < KS; ++st) {
+    kf[st] = buf_load16(rk, k_off + 64 * st);
+    vf[st] = buf_load16(rv, k_off + 64 * st);
   }
-  // Transposed reads of the row tiles (the forward's V^T pattern, rows in place of keys).
-  const int vs = lane & 15, vdh = (lane >> 4) & 1;
-  const int r_lane = (4 * half + (vs >> 2)) * VROW + 16 * vdh + 4 * (vs & 3);
+  // Row reads (A operands of S and dP): row 16 rb + m, unit 4 st + u.
+  uint32_t aofs[KS];
+#pragma unroll
+  for (int st = 0; st < KS; ++st) aofs[st] = uint32_t(m * RB + 16 * ((4 * st + u) ^ swz(m)));
+  // Transposing reads (A operands of dV^T and dK^T): in lane group u, lane m points at row
+  // 4u + m / 4 (+ 16, + 32 j) and head-dim element 16 db + 4 (m % 4), and receives column 16 db + m
+  // of rows 4u .. 4u + 3.  Rows + 16 and + 32 leave the swizzle unchanged.
+  const int tr_row = 4 * u + (m >> 2);
+  uint32_t tofs[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    tofs[db] = uint32_t(tr_row * RB + 16 * ((2 * db + ((m & 3) >> 1)) ^ swz(tr_row)) + 8 * (m & 1));
+  // Direct-to-LDS loads: instruction r of wave w fills LDS bytes [1 KB i, 1 KB (i + 1)) of a slot,
+  // i = NDMA w + r: rows KPI i .. KPI i + KPI - 1, lane l unit l % UPR of row KPI i + l / UPR from
+  // source unit (l % UPR) ^ swz(row).  Row r is token r / G, head g G + r % G of the step.
+  uint32_t dofs[NDMA];
+#pragma unroll
+  for (int r = 0; r < NDMA; ++r) {
+    const int row = KPI * (NDMA * w + r) + lane / UPR, c = (lane % UPR) ^ swz(row);
+    dofs[r] = uint32_t(((row / G) * q_stride + (row % G) * D) * 2 + 16 * c);
+  }
+  const uint32_t lofs = uint32_t(((lane / G) * Hq + lane % G) * 4);  // lse / Dr of row `lane`
 
-  f32x16_t ak[DBLK], av[DBLK];
+  f32x4_t ak[DB], av[DB];
 #pragma unroll
-  for (int b = 0; b < DBLK; ++b) {
-    ak[b] = f32x16_t{};
-    av[b] = f32x16_t{};
+  for (int db = 0; db < DB; ++db) {
+    ak[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    av[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  // Row steps: the causal range first, then the unmasked one.  Step i + 1's rows are loaded into
-  // registers while step i is computed.
+  // Row steps: the causal range first, then the unmasked one.
   const int nC = it.c1 > it.c0 ? (it.c1 - it.c0 + TR - 1) / TR : 0;
   const int nU = it.u1 > it.u0 ? (it.u1 - it.u0 + TR - 1) / TR : 0;
   const int nS = nC + nU;
   auto step_t0 = [&](int i) { return i < nC ? it.c0 + i * TR : it.u0 + (i - nC) * TR; };
   auto step_end = [&](int i) { return i < nC ? it.c1 : it.u1; };
-  u32x4_t rq[LPT], rd[LPT];
-  float rl = INFINITY, rr_ = 0.f;
-  auto load_step = [&](int i) {
-    const int t0 = step_t0(i), ntok = min(TR, step_end(i) - t0);
-    const rsrc_t bq = make_rsrc(Q + (int64_t(t0) * Hq + g * G) * D, ntok * q_stride * 2);
-    const rsrc_t bd = make_rsrc(dO + (int64_t(t0) * Hq + g * G) * D, ntok * q_stride * 2);
+  // Rows past the range's end load as zeros (Q, dO, lse, Dr): their S and dP are 0, so they add
+  // P = 1 times a zero dO row to dV and dS = 0 to dK, i.e. nothing.
+  auto issue = [&](int i, int slot) {
+    const int t0 = __builtin_amdgcn_readfirstlane(step_t0(i));
+    const int ntok = __builtin_amdgcn_readfirstlane(min(TR, step_end(i) - t0));
+    const int64_t base = (int64_t(t0) * Hq + g * G);
+    const rsrc_t bq = make_rsrc(Q + base * D, ntok * q_stride * 2);
+    const rsrc_t bd = make_rsrc(dO + base * D, ntok * q_stride * 2);
+    const uint32_t lq = lds_addr_of(&sq[slot][0]) + 1024 * NDMA * w, ld = lds_addr_of(&sd[slot][0]) + 1024 * NDMA * w;
 #pragma unroll
-    for (int p = 0; p < LPT; ++p) {
-      const int u = p * 128 + tid, row = u / KCH, c = u % KCH;
-      const uint32_t off = uint32_t(((row / G) * q_stride + (row % G) * D + 8 * c) * 2);
-      rq[p] = buf_load16(bq, off);
-      rd[p] = buf_load16(bd, off);
-    }
-    if (tid < RS) {
-      const bool ok = tid / G < ntok;  // rows past the range get P = 0
-      const int64_t rix = int64_t(t0 + tid / G) * Hq + g * G + tid % G;
-      rl = ok ? lse[rix] * kLog2e : INFINITY;
-      rr_ = ok ? dvec[rix] : 0.f;
-    }
+    for (int r = 0; r < NDMA; ++r) buf_load16_lds(bq, lq + 1024 * r, dofs[r]);
+#pragma unroll
+    for (int r = 0; r < NDMA; ++r) buf_load16_lds(bd, ld + 1024 * r, dofs[r]);
+    if (w == 0) buf_load4_lds(make_rsrc(lse + base, ntok * Hq * 4), lds_addr_of(&sl[slot][0]), lofs);
+    if (w == 1) buf_load4_lds(make_rsrc(dvec + base, ntok * Hq * 4), lds_addr_of(&sr[slot][0]), lofs);
   };
-  if (nS > 0) load_step(0);
+  if (nS > 0) issue(0, 0);
   for (int i = 0; i < nS; ++i) {
+    const int slot = i & 1;
+    // This wave's loads of step i have landed; after the barrier every wave's have, and every wave
+    // has finished step i - 1, whose slot the next loads overwrite.
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (i + 1 < nS) issue(i + 1, slot ^ 1);
     const bool causal = i < nC;
     const int t0 = step_t0(i);
-    __syncthreads();  // the previous step's LDS reads are done
+    const uint8_t* qs = &sq[slot][0];
+    const uint8_t* ds = &sd[slot][0];
 #pragma unroll
-    for (int p = 0; p < LPT; ++p) {
-      const int u = p * 128 + tid, row = u / KCH, c = u % KCH;
-      *reinterpret_cast<u32x4_t*>(&sq[row * VROW + 8 * c]) = rq[p];
-      *reinterpret_cast<u32x4_t*>(&sd[row * VROW + 8 * c]) = rd[p];
-    }
-    if (tid < RS) {
-      sl[tid] = rl;
-      sr[tid] = rr_;
-    }
-    __syncthreads();
-    if (i + 1 < nS) load_step(i + 1);
+    for (int hs = 0; hs < NRB / 2; ++hs) {  // 32-row half steps
+      f32x4_t s[2], dp[2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-      const uint16_t* qp = &sq[(32 * rb + n) * VROW + 8 * half];
-      const uint16_t* dq = &sd[(32 * rb + n) * VROW + 8 * half];
+      for (int b = 0; b < 2; ++b) {
+        const int rb = 2 * hs + b;
+        s[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        dp[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < DSTEPS; ++st) {
-        s = mfma32(load16(qp + 16 * st), kf[st], s);
-        dp = mfma32(load16(dq + 16 * st), vf[st], dp);
-      }
-      // Register r holds row 32 rb + 8 (r / 4) + 4 half + r % 4 of the step (token t0 + row / G)
-      // for this lane's key.  Causal rows read the key only if their token is not before it.
-      uint32_t pp[8], pd[8];
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float pr[2], ds[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int row = 32 * rb + 8 * (r >> 2) + 4 * half + (r & 3) + e;
-          const bool ok = !causal || key <= t0 + row / G;
-          pr[e] = ok ? fast_exp2(fmaf(s[r + e], scale_log2, -sl[row])) : 0.f;
-          ds[e] = pr[e] * (dp[r + e] - sr[row]);
+        for (int st = 0; st < KS; ++st) {
+          s[b] = mfma16(load16(qs + aofs[st] + 16 * RB * rb), kf[st], s[b]);
+          dp[b] = mfma16(load16(ds + aofs[st] + 16 * RB * rb), vf[st], dp[b]);
         }
-        pp[r >> 1] = pack_bf16x2(pr[0], pr[1]);
-        pd[r >> 1] = pack_bf16x2(ds[0], ds[1]);
       }
+      // Register r of block b holds row 32 hs + 16 b + 4 u + r of the step, for this lane's key.
+      uint32_t pp[4], pd[4];
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const u32x4_t bp = {pp[4 * m], pp[4 * m + 1], pp[4 * m + 2], pp[4 * m + 3]};
-        const u32x4_t bd = {pd[4 * m], pd[4 * m + 1], pd[4 * m + 2], pd[4 * m + 3]};
-        const uint16_t* dpt = &sd[r_lane + (32 * rb + 16 * m) * VROW];
-        const uint16_t* qpt = &sq[r_lane + (32 * rb + 16 * m) * VROW];
+      for (int b = 0; b < 2; ++b) {
+        const int r0 = 32 * hs + 16 * b + 4 * u;
+        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(&sl[slot][r0]);
+        const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&sr[slot][r0]);
+        float pr[4], dsv[4];
 #pragma unroll
-        for (int b = 0; b < DBLK; ++b) {
-          const u32x2_t dlo = lds_read_tr16(dpt + 32 * b), dhi = lds_read_tr16(dpt + 8 * VROW + 32 * b);
-          av[b] = mfma32(u32x4_t{dlo[0], dlo[1], dhi[0], dhi[1]}, bp, av[b]);
-          const u32x2_t qlo = lds_read_tr16(qpt + 32 * b), qhi = lds_read_tr16(qpt + 8 * VROW + 32 * b);
-          ak[b] = mfma32(u32x4_t{qlo[0], qlo[1], qhi[0], qhi[1]}, bd, ak[b]);
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = !causal || key <= t0 + (r0 + r) / G;
+          pr[r] = ok ? fast_exp2(fmaf(s[b][r], scale_log2, -(l4[r] * kLog2e))) : 0.f;
+          dsv[r] = pr[r] * (dp[b][r] - d4[r]);
         }
+        pp[2 * b] = pack_bf16x2(pr[0], pr[1]);
+        pp[2 * b + 1] = pack_bf16x2(pr[2], pr[3]);
+        pd[2 * b] = pack_bf16x2(dsv[0], dsv[1]);
+        pd[2 * b + 1] = pack_bf16x2(dsv[2], dsv[3]);
+      }
+      const u32x4_t bp = {pp[0], pp[1], pp[2], pp[3]};
+      const u32x4_t bd = {pd[0], pd[1], pd[2], pd[3]};
+      const uint32_t hrow = 32 * RB * hs;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint8_t* dpt = ds + hrow + tofs[db];  // rows 4u .. 4u + 3; + 16 RB: rows 16 + 4u ..
+        const uint8_t* qpt = qs + hrow + tofs[db];
+        const u32x2_t dlo = lds_read_tr16(reinterpret_cast<const uint16_t*>(dpt));
+        const u32x2_t dhi = lds_read_tr16(reinterpret_cast<const uint16_t*>(dpt + 16 * RB));
+        av[db] = mfma16(u32x4_t{dlo[0], dlo[1], dhi[0], dhi[1]}, bp, av[db]);
+        const u32x2_t qlo = lds_read_tr16(reinterpret_cast<const uint16_t*>(qpt));
+        const u32x2_t qhi = lds_read_tr16(reinterpret_cast<const uint16_t*>(qpt + 16 * RB));
+        ak[db] = mfma16(u32x4_t{qlo[0], qlo[1], qhi[0], qhi[1]}, bd, ak[db]);
       }
     }
   }
   if (key >= it.k_limit) return;
-  // ak / av[b] register r holds head-dim element 32 b + 8 (r / 4) + 4 half + r % 4 of this key.
+  // ak / av[db] register r holds head-dim element 16 db + 4 u + r of this lane's key.
   float *pk_, *pv_;
   if (it.slot < 0) {
     pk_ = dK + (int64_t(key) * Hkv + g) * D;
     pv_ = dV + (int64_t(key) * Hkv + g) * D;
   } else {
-    const int64_t base = ((int64_t(it.slot) * Hkv + g) * kBwdKeyTile + 32 * w + n) * D;
+    const int64_t base = ((int64_t(it.slot) * Hkv + g) * kBwdKeyTile + 16 * w + m) * D;
     pk_ = part_dkv + base;
     pv_ = part_dkv + int64_t(kv_slots) * Hkv * kBwdKeyTile * D + base;
   }
 #pragma unroll
-  for (int b = 0; b < DBLK; ++b)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = 32 * b + 8 * j + 4 * half;
-      *reinterpret_cast<f32x4_t*>(pk_ + e) =
-          f32x4_t{ak[b][4 * j], ak[b][4 * j + 1], ak[b][4 * j + 2], ak[b][4 * j + 3]} * scale;
-      *reinterpret_cast<f32x4_t*>(pv_ + e) = f32x4_t{av[b][4 * j], av[b][4 * j + 1], av[b][4 * j + 2], av[b][4 * j + 3]};
-    }
+  for (int db = 0; db < DB; ++db) {
+    const int e = 16 * db + 4 * u;
+    *reinterpret_cast<f32x4_t*>(pk_ + e) = ak[db] * scale;
+    *reinterpret_cast<f32x4_t*>(pv_ + e) = av[db];
+  }
 }
 
 // Sum the split dK / dV partials of one key tile (fixed order).  One thread per (key, 4 elements).
@@ -407,7 +451,7 @@ static hipError_t launch_bwd_t(const BwdLaunch& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (a.n_kv_items > 0) {
-    attn_bwd_dkv_kernel<D, G><<<unsigned(a.n_kv_items * a.num_kv_heads), 128, 0, stream>>>(
+    attn_bwd_dkv_kernel<D, G><<<unsigned(a.n_kv_items * a.num_kv_heads), 256, 0, stream>>>(
         a.Q, a.K, a.V, a.dO, a.lse, a.dvec, a.dK, a.dV, a.kv_items, a.part_dkv, a.num_q_heads, a.num_kv_heads,
         a.kv_slots, a.scale, a.scale * kLog2e);
     e = hipGetLastError();

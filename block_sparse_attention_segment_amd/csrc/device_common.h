@@ -125,6 +125,11 @@ __device__ __forceinline__ void buf_load16_lds_nt(rsrc_t r, uint32_t lds_addr, u
                "s"(r)
                : "memory", "m0");
 }
+// The same for 4 bytes per lane (buffer_load_dword ... lds): lane l's dword goes to lds_addr + 4 l.
+__device__ __forceinline__ void buf_load4_lds(rsrc_t r, uint32_t lds_addr, uint32_t byte_offset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds_addr), "v"(byte_offset), "s"(r)
+               : "memory", "m0");
+}
 // LDS byte address of a __shared__ object (for M0).
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   typedef __attribute__((address_space(3))) const void lds_void_t;
