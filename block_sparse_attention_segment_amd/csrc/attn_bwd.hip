@@ -43,8 +43,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __r
   constexpr int KPASS = BN / RPP;
   // Two K/V tile buffers: tile i is read from buffer i % 2 while tile i + 1 is written to the
   // other, so one barrier per tile suffices.
-  __shared__ __align__(16) uint16_t sk[2][BN * VROW];
-  __shared__ __align__(16) uint16_t sv[2][BN * KROW];
+  // One LDS block: the K and V tile buffers, and after the last tile each wave's 32 output rows
+  // (fp32, rows padded by 16 bytes) staged for whole-row stores.
+  constexpr int SROW = 4 * D + 16;
+  constexpr int TILE_BYTES = 2 * BN * VROW * 2 + 2 * BN * KROW * 2;
+  static_assert(TILE_BYTES >= kRowsPerTile * SROW, "the output rows fit in the tile buffers");
+  __shared__ __align__(16) uint8_t lds[TILE_BYTES];
+  uint16_t(*sk)[BN * VROW] = reinterpret_cast<uint16_t(*)[BN * VROW]>(lds);
+  uint16_t(*sv)[BN * KROW] = reinterpret_cast<uint16_t(*)[BN * KROW]>(lds + 2 * BN * VROW * 2);
 
   const int g = blockIdx.x % Hkv;
   const AttnItem it = items[blockIdx.x / Hkv];
@@ -134,6 +140,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __r
     const bool causal = i >= nA;
     // Register r of block kb holds key start + 32 kb + 8 (r / 4) + 4 half + r % 4.
     const int lim = (causal ? min(end, row_tok + 1) : end) - start - 4 * half;
+    // Only a short tile or one crossing the diagonal needs the mask.  Rows past the item's last
+    // token need none: their Q and dO are zero and their lse term 0, so P = 1 and dS = 0.
+    const bool masked = end - start < BN || (causal && start + BN - 1 > it.row0);
     // One 32-key block at a time keeps few values live (two workgroups fit on a CU).
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -148,10 +157,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __r
       uint32_t pk[8];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const bool ok0 = row_ok && (kb * 32 + 8 * (r >> 2) + (r & 3)) < lim;
-        const bool ok1 = row_ok && (kb * 32 + 8 * (r >> 2) + (r & 3) + 1) < lim;
-        const float p0 = ok0 ? fast_exp2(fmaf(s[r], scale_log2, -l2)) : 0.f;
-        const float p1 = ok1 ? fast_exp2(fmaf(s[r + 1], scale_log2, -l2)) : 0.f;
+        float p0 = fast_exp2(fmaf(s[r], scale_log2, -l2));
+        float p1 = fast_exp2(fmaf(s[r + 1], scale_log2, -l2));
+        if (masked) {
+          p0 = row_ok && (kb * 32 + 8 * (r >> 2) + (r & 3)) < lim ? p0 : 0.f;
+          p1 = row_ok && (kb * 32 + 8 * (r >> 2) + (r & 3) + 1) < lim ? p1 : 0.f;
+        }
         pk[r >> 1] = pack_bf16x2(p0 * (dp[r] - dr), p1 * (dp[r + 1] - dr));
       }
 #pragma unroll
@@ -170,23 +181,28 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __r
     __syncthreads();
   }
   // acc[b] register r holds head-dim element 32 b + 8 (r / 4) + 4 half + r % 4 of this lane's row.
-  if (it.slot < 0) {
-    if (!row_ok) return;
-    float* dst = dQ + rix * D + 4 * half;
+  // The rows go through this wave's part of the (now idle) tile buffers, so that each store
+  // instruction writes whole rows (two at d = 128) instead of 32 bytes of each of 32 rows.
+  uint8_t* const stage = lds + w * 32 * SROW;
 #pragma unroll
-    for (int b = 0; b < DBLK; ++b)
+  for (int b = 0; b < DBLK; ++b)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<f32x4_t*>(dst + 32 * b + 8 * j) =
-            f32x4_t{acc[b][4 * j], acc[b][4 * j + 1], acc[b][4 * j + 2], acc[b][4 * j + 3]} * scale;
-  } else {
-    float* dst = part_dq + ((int64_t(it.slot) * Hkv + g) * kRowsPerTile + rho) * D + 4 * half;
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<f32x4_t*>(stage + n * SROW + 4 * (32 * b + 8 * j + 4 * half)) =
+          f32x4_t{acc[b][4 * j], acc[b][4 * j + 1], acc[b][4 * j + 2], acc[b][4 * j + 3]} * scale;
+  constexpr int CPR = D / 4;     // 16-byte columns per row
+  constexpr int RPI = 64 / CPR;  // rows per store instruction
+  const int c = lane % CPR;
 #pragma unroll
-    for (int b = 0; b < DBLK; ++b)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<f32x4_t*>(dst + 32 * b + 8 * j) =
-            f32x4_t{acc[b][4 * j], acc[b][4 * j + 1], acc[b][4 * j + 2], acc[b][4 * j + 3]} * scale;
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = RPI * i + lane / CPR, rr = w * 32 + r;  // row r of this wave, rr of the item
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage + r * SROW + 16 * c);
+    if (it.slot < 0) {
+      const int tok = it.row0 + rr % TM;
+      if (tok < it.row_limit) *reinterpret_cast<f32x4_t*>(dQ + (int64_t(tok) * Hq + g * G + rr / TM) * D + 4 * c) = v;
+    } else {
+      *reinterpret_cast<f32x4_t*>(part_dq + ((int64_t(it.slot) * Hkv + g) * kRowsPerTile + rr) * D + 4 * c) = v;
+    }
   }
 }
 
@@ -335,8 +351,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(const uint16_t* __
     // has finished step i - 1, whose slot the next loads overwrite.
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     if (i + 1 < nS) issue(i + 1, slot ^ 1);
-    const bool causal = i < nC;
     const int t0 = step_t0(i);
+    // Causal steps whose first token is at or after the last key read every key: no mask.
+    const bool masked = i < nC && t0 < it.k_limit - 1;
     const uint8_t* qs = &sq[slot][0];
     const uint8_t* ds = &sd[slot][0];
 #pragma unroll
@@ -363,8 +380,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(const uint16_t* __
         float pr[4], dsv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const bool ok = !causal || key <= t0 + (r0 + r) / G;
-          pr[r] = ok ? fast_exp2(fmaf(s[b][r], scale_log2, -(l4[r] * kLog2e))) : 0.f;
+          pr[r] = fast_exp2(fmaf(s[b][r], scale_log2, -(l4[r] * kLog2e)));
+          if (masked) pr[r] = key <= t0 + (r0 + r) / G ? pr[r] : 0.f;
           dsv[r] = pr[r] * (dp[b][r] - d4[r]);
         }
         pp[2 * b] = pack_bf16x2(pr[0], pr[1]);
