@@ -36,25 +36,27 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __r
   constexpr int TM = kRowsPerTile / G;
   constexpr int BN = kKeyTile;
   constexpr int NKB = BN / 32;
-  constexpr int VROW = D == 128 ? 160 : 96;  // K: row reads and transposing reads (as V in the forward)
-  constexpr int KROW = D + 8;                // V: row reads only
-  constexpr int DSTEPS = D / 16, DBLK = D / 32, KCH = D / 8;
-  constexpr int RPP = 256 / KCH;             // key rows per load pass
-  constexpr int KPASS = BN / RPP;
-  // Two K/V tile buffers: tile i is read from buffer i % 2 while tile i + 1 is written to the
-  // other, so one barrier per tile suffices.
-  // One LDS block: the K and V tile buffers, and after the last tile each wave's 32 output rows
-  // (fp32, rows padded by 16 bytes) staged for whole-row stores.
-  constexpr int SROW = 4 * D + 16;
-  constexpr int TILE_BYTES = 2 * BN * VROW * 2 + 2 * BN * KROW * 2;
-  static_assert(TILE_BYTES >= kRowsPerTile * SROW, "the output rows fit in the tile buffers");
-  __shared__ __align__(16) uint8_t lds[TILE_BYTES];
-  uint16_t(*sk)[BN * VROW] = reinterpret_cast<uint16_t(*)[BN * VROW]>(lds);
-  uint16_t(*sv)[BN * KROW] = reinterpret_cast<uint16_t(*)[BN * KROW]>(lds + 2 * BN * VROW * 2);
+  constexpr int RB = 2 * D;           // bytes per K or V row
+  constexpr int UPR = D / 8;          // 16-byte units per row
+  constexpr int KPI = 1024 / RB;      // key rows per direct-to-LDS wave instruction
+  constexpr int NDMA = BN / KPI / 4;  // such instructions per wave per tensor per tile
+  constexpr int TB = BN * RB;         // bytes per K or V tile
+  constexpr int DSTEPS = D / 16, DBLK = D / 32;
+  static_assert(NDMA >= 1 && NDMA * KPI * 4 == BN, "a tile's rows split over four waves");
+  static_assert(4 * TB >= kRowsPerTile * 4 * D, "the output rows fit in the tile buffers");
+  // LDS: the K and V tiles of two slots (tile i in slot i % 2 while tile i + 1 loads into the
+  // other, one barrier per tile); after the last tile, each wave's 32 fp32 output rows.
+  __shared__ __align__(1024) uint8_t lds[4 * TB];
+  // Swizzles of the 16-byte units of a row: K is read by rows (16 keys at one unit) and by
+  // transposing reads (4 keys x 2 unit pairs per half-wave, keys + 8 with the swizzle ^ 2); V by
+  // rows only.  Both repeat every 16 rows.
+  auto swz_k = [](int r) { return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3); };
+  auto swz_v = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
 
   const int g = blockIdx.x % Hkv;
   const AttnItem it = items[blockIdx.x / Hkv];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, half = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, half = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in a scalar register
   const int rho = w * 32 + n, hh = rho / TM, tt = rho % TM, h = g * G + hh;
   const int row_tok = it.row0 + tt;
   const bool row_ok = row_tok < it.row_limit;
@@ -94,30 +96,35 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __r
     if (row_ok && half == 0 && (it.slot < 0 || it.b_end > it.b_start)) dvec[rix] = dr;
   }
 
-  const int kcc = tid % KCH, kr0 = tid / KCH;
-  const uint32_t k_off = uint32_t((kr0 * kv_stride + 8 * kcc) * 2);
-  u32x4_t kreg[KPASS], vreg[KPASS];
-  auto load_tile = [&](int start, int end) {
-    const int keys = min(BN, end - start);
-    const rsrc_t rk = make_rsrc(K + int64_t(start) * kv_stride + g * D, keys * kv_stride * 2);
-    const rsrc_t rv = make_rsrc(V + int64_t(start) * kv_stride + g * D, keys * kv_stride * 2);
+  // Row reads (A operands of S^T and dP^T): key 32 kb + n, unit 2 st + half.
+  uint32_t kro[DSTEPS], vro[DSTEPS];
 #pragma unroll
-    for (int p = 0; p < KPASS; ++p) {
-      kreg[p] = buf_load16(rk, k_off + p * RPP * kv_stride * 2);
-      vreg[p] = buf_load16(rv, k_off + p * RPP * kv_stride * 2);
-    }
-  };
-  auto store_tile = [&](int buf) {
+  for (int st = 0; st < DSTEPS; ++st) {
+    kro[st] = uint32_t(n * RB + 16 * ((2 * st + half) ^ swz_k(n)));
+    vro[st] = uint32_t(n * RB + 16 * ((2 * st + half) ^ swz_v(n)));
+  }
+  // K^T fragments for dQ^T += K^T dS^T (transposing reads, the forward's V^T pattern): in each
+  // 16-lane group, lane s points at key 4 half + s / 4 (+ 8 for the upper four) and head-dim
+  // element 32 b + 16 vdh + 4 (s % 4).
+  const int vs = lane & 15, vdh = (lane >> 4) & 1, tr_r = 4 * half + (vs >> 2);
+  uint32_t ktl[DBLK], kth[DBLK];
 #pragma unroll
-    for (int p = 0; p < KPASS; ++p) {
-      const int r = kr0 + p * RPP;
-      *reinterpret_cast<u32x4_t*>(&sk[buf][r * VROW + 8 * kcc]) = kreg[p];
-      *reinterpret_cast<u32x4_t*>(&sv[buf][r * KROW + 8 * kcc]) = vreg[p];
-    }
-  };
-  // K^T fragments for dQ^T += K^T dS^T: the forward's V^T read pattern on the K tile.
-  const int vs = lane & 15, vdh = (lane >> 4) & 1;
-  const int k_lane = (4 * half + (vs >> 2)) * VROW + 16 * vdh + 4 * (vs & 3);
+  for (int b = 0; b < DBLK; ++b) {
+    const int unit = 4 * b + 2 * vdh + ((vs & 3) >> 1);
+    ktl[b] = uint32_t(tr_r * RB + 16 * (unit ^ swz_k(tr_r)) + 8 * (vs & 1));
+    kth[b] = uint32_t((tr_r + 8) * RB + 16 * (unit ^ swz_k(tr_r + 8)) + 8 * (vs & 1));
+  }
+  // Direct-to-LDS loads: instruction r of wave w fills bytes [1 KB i, 1 KB (i + 1)) of a tile,
+  // i = NDMA w + r: lane l unit l % UPR of key row KPI i + l / UPR, from source unit
+  // (l % UPR) ^ swz(row).  Keys past the range's end load as zeros.
+  uint32_t kdma[NDMA], vdma[NDMA];
+#pragma unroll
+  for (int r = 0; r < NDMA; ++r) {
+    const int row = KPI * (NDMA * w + r) + lane / UPR, u = lane % UPR;
+    kdma[r] = uint32_t(row * kv_stride * 2 + 16 * (u ^ swz_k(row)));
+    vdma[r] = uint32_t(row * kv_stride * 2 + 16 * (u ^ swz_v(row)));
+  }
+  const uint32_t lds0 = lds_addr_of(lds);
 
   const int nA = it.a_end > it.a_start ? (it.a_end - it.a_start + BN - 1) / BN : 0;
   const int nB = it.b_end > it.b_start ? (it.b_end - it.b_start + BN - 1) / BN : 0;
@@ -125,17 +132,30 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __r
   auto t_start = [&](int i) { return i < nA ? it.a_start + i * BN : it.b_start + (i - nA) * BN; };
   auto t_end = [&](int i) { return i < nA ? it.a_end : it.b_end; };
 
+  auto issue = [&](int i, int slot) {
+    const int start = __builtin_amdgcn_readfirstlane(t_start(i));
+    const int keys = __builtin_amdgcn_readfirstlane(min(BN, t_end(i) - start));
+    const rsrc_t rk = make_rsrc(K + int64_t(start) * kv_stride + g * D, keys * kv_stride * 2);
+    const rsrc_t rv = make_rsrc(V + int64_t(start) * kv_stride + g * D, keys * kv_stride * 2);
+    const uint32_t lk = lds0 + slot * 2 * TB + 1024 * NDMA * w;
+#pragma unroll
+    for (int r = 0; r < NDMA; ++r) buf_load16_lds(rk, lk + 1024 * r, kdma[r]);
+#pragma unroll
+    for (int r = 0; r < NDMA; ++r) buf_load16_lds(rv, lk + TB + 1024 * r, vdma[r]);
+  };
+
   f32x16_t acc[DBLK];
 #pragma unroll
   for (int b = 0; b < DBLK; ++b) acc[b] = f32x16_t{};
-  if (nt > 0) {
-    load_tile(t_start(0), t_end(0));
-    store_tile(0);
-  }
-  __syncthreads();
+  if (nt > 0) issue(0, 0);
   for (int i = 0; i < nt; ++i) {
-    const int buf = i & 1;
-    if (i + 1 < nt) load_tile(t_start(i + 1), t_end(i + 1));
+    const int slot = i & 1;
+    // This wave's loads of tile i have landed; after the barrier every wave's have, and every wave
+    // has finished tile i - 1, whose slot the next loads overwrite.
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (i + 1 < nt) issue(i + 1, slot ^ 1);
+    const uint8_t* const kt = lds + slot * 2 * TB;
+    const uint8_t* const vt = kt + TB;
     const int start = t_start(i), end = t_end(i);
     const bool causal = i >= nA;
     // Register r of block kb holds key start + 32 kb + 8 (r / 4) + 4 half + r % 4.
@@ -147,12 +167,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __r
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-      const uint16_t* kp = &sk[buf][(kb * 32 + n) * VROW + 8 * half];
-      const uint16_t* vp = &sv[buf][(kb * 32 + n) * KROW + 8 * half];
 #pragma unroll
       for (int st = 0; st < DSTEPS; ++st) {
-        s = mfma32(load16(kp + 16 * st), qf[st], s);
-        dp = mfma32(load16(vp + 16 * st), df[st], dp);
+        s = mfma32(load16(kt + 32 * RB * kb + kro[st]), qf[st], s);
+        dp = mfma32(load16(vt + 32 * RB * kb + vro[st]), df[st], dp);
       }
       uint32_t pk[8];
 #pragma unroll
@@ -168,27 +186,27 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __r
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const u32x4_t pv = {pk[4 * m], pk[4 * m + 1], pk[4 * m + 2], pk[4 * m + 3]};
-        const uint16_t* kq = &sk[buf][k_lane + (32 * kb + 16 * m) * VROW];
+        const uint8_t* kq = kt + (32 * kb + 16 * m) * RB;
 #pragma unroll
         for (int b = 0; b < DBLK; ++b) {
-          const u32x2_t lo = lds_read_tr16(kq + 32 * b), hi = lds_read_tr16(kq + 8 * VROW + 32 * b);
+          const u32x2_t lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(kq + ktl[b]));
+          const u32x2_t hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(kq + kth[b]));
           acc[b] = mfma32(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pv, acc[b]);
         }
       }
     }
-    // The other buffer was last read in the previous tile, before the barrier that ended it.
-    if (i + 1 < nt) store_tile(buf ^ 1);
-    __syncthreads();
   }
+  __syncthreads();  // every wave is done with the tiles before the rows are staged over them
   // acc[b] register r holds head-dim element 32 b + 8 (r / 4) + 4 half + r % 4 of this lane's row.
   // The rows go through this wave's part of the (now idle) tile buffers, so that each store
   // instruction writes whole rows (two at d = 128) instead of 32 bytes of each of 32 rows.
-  uint8_t* const stage = lds + w * 32 * SROW;
+  // Row n at 4D n bytes, its 16-byte unit c at c ^ (n mod 16).
+  uint8_t* const stage = lds + w * 32 * 4 * D;
 #pragma unroll
   for (int b = 0; b < DBLK; ++b)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<f32x4_t*>(stage + n * SROW + 4 * (32 * b + 8 * j + 4 * half)) =
+      *reinterpret_cast<f32x4_t*>(stage + n * 4 * D + 16 * ((8 * b + 2 * j + half) ^ (n & 15))) =
           f32x4_t{acc[b][4 * j], acc[b][4 * j + 1], acc[b][4 * j + 2], acc[b][4 * j + 3]} * scale;
   constexpr int CPR = D / 4;     // 16-byte columns per row
   constexpr int RPI = 64 / CPR;  // rows per store instruction
@@ -196,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __r
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
     const int r = RPI * i + lane / CPR, rr = w * 32 + r;  // row r of this wave, rr of the item
-    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage + r * SROW + 16 * c);
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage + r * 4 * D + 16 * (c ^ (r & 15)));
     if (it.slot < 0) {
       const int tok = it.row0 + rr % TM;
       if (tok < it.row_limit) *reinterpret_cast<f32x4_t*>(dQ + (int64_t(tok) * Hq + g * G + rr / TM) * D + 4 * c) = v;
