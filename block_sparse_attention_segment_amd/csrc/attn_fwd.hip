@@ -36,7 +36,8 @@
 // end read as zero, and output rows past a tile's last token are dropped by the hardware.
 // Output rows are staged through the wave's own part of the Q buffer (between reading one
 // item's Q fragments and loading the next item's rows) so each store writes whole 128-byte
-// lines: stores of 32 bytes per row were measured to cost about a sixth of the kernel time.
+// lines (stores of 32 bytes per row were measured to cost about a sixth of the kernel time),
+// with the non-temporal hint, which leaves the L2 to the K/V tiles that are re-read.
 //
 // LDS layouts (16-byte units, XOR-swizzled instead of padded, because a direct-to-LDS load
 // fills 1 KB of consecutive LDS per wave instruction):
@@ -566,7 +567,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
 #pragma unroll
         for (int i = 0; i < DSTEPS; ++i) {
           const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + 1024 * i + 16 * lane);
-          buf_store16(v, ro, qdma[i]);
+          buf_store16_nt(v, ro, qdma[i]);  // whole lines, not read again by this kernel
         }
         since_q += DSTEPS;
         ex_prev += DSTEPS;

@@ -82,6 +82,11 @@ __device__ __forceinline__ void buf_store8(u32x2_t v, rsrc_t r, uint32_t byte_of
 __device__ __forceinline__ void buf_store16(u32x4_t v, rsrc_t r, uint32_t byte_offset) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_offset, 0, 0);
 }
+// The same with the non-temporal hint (cache policy bit 1, "nt" on gfx950), for whole-line writes
+// that are not read again soon: the L2 then keeps the lines that are re-read in preference.
+__device__ __forceinline__ void buf_store16_nt(u32x4_t v, rsrc_t r, uint32_t byte_offset) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_offset, 0, 2);
+}
 // Rotary embedding of packed bf16 pairs, fp32 arithmetic, one rounding to bf16 (shared by the
 // rotation kernel and the attention kernel's in-register rotation of Q, so both round alike).
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
