@@ -145,6 +145,13 @@ void add_query_rows(int64_t qs, int64_t qe, int64_t u0, int64_t u1, const ItemMa
   add_query_rows(qs, qe, ranges, mk, plan, out);
 }
 
+Error check_item_count(const AttnPlan& plan) {
+  if (int64_t(plan.items.size()) >= kMaxAttnItems)
+    return fail(BR_ERR_UNSUPPORTED, "the attention plan has %lld work items; at most %lld are supported",
+                (long long)plan.items.size(), kMaxAttnItems - 1);
+  return {};
+}
+
 // Workspace layout (the schedule is made per device, by the caller).
 void finish_plan(const br_dims& dims, AttnPlan* plan) {
   AttnPlan& P = *plan;
@@ -207,6 +214,8 @@ Error build_attn_plan(const br_dims& dims, const int32_t* so, const int32_t* sp,
   // schedule hands them to different workgroups at about the same time and the document's keys
   // are fetched once and re-read from the shared L2.
   order_items(std::move(query_items), other_items, plan);
+  e = check_item_count(*plan);
+  if (!e.ok()) return e;
   finish_plan(dims, plan);
   return {};
 }
@@ -238,6 +247,8 @@ Error build_query_plan(const br_dims& dims, int32_t corpus_len, const int32_t* q
   std::stable_sort(query_items.begin(), query_items.end(),
                    [](const AttnItem& x, const AttnItem& y) { return x.a_start < y.a_start; });
   plan->items = std::move(query_items);
+  e = check_item_count(*plan);
+  if (!e.ok()) return e;
   finish_plan(dims, plan);
   return {};
 }
@@ -317,6 +328,8 @@ Error build_routed_plan(const br_dims& dims, const int32_t* so, const int32_t* s
     add_query_rows(qs, qe, qranges[size_t(b)], mk, plan, &query_items);
   }
   order_items(std::move(query_items), other_items, plan);
+  e = check_item_count(*plan);
+  if (!e.ok()) return e;
   finish_plan(dims, plan);
   return {};
 }

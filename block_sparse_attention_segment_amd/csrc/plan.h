@@ -18,6 +18,9 @@ constexpr int kRowsPerTile = kRowsPerWave * kWaves;  // 128 (token, head) rows p
 constexpr int kKeyTile = 64;                      // keys staged in LDS per step
 constexpr int kAttnWgPerCu = 2;                   // persistent attention workgroups per CU
 constexpr int kMaxAttnWgPerHead = 4096;           // bound on workgroups sharing one KV head
+// Bound on the items of one attention plan: the kernel packs an item index into the upper bits of
+// a 32-bit tile code (21 bits above 10 bits of key count and flags).
+constexpr int64_t kMaxAttnItems = int64_t(1) << 21;
 constexpr int kMaxHeadsTimesDim = 65536;          // bound on num_q_heads * head_dim (512 heads at d = 128)
 
 inline int tokens_per_tile(int group) { return kRowsPerTile / group; }

@@ -48,7 +48,10 @@
  *     G = num_q_heads / num_kv_heads in {1, 2, 4, 8}; query head h reads KV head h / G;
  *     num_q_heads * head_dim <= 65536 (512 query heads at d = 128); total_tokens <= 2^30 and
  *     total_tokens * num_kv_heads * head_dim * 2 < 2^32 (K and V each below 4 GiB: the attention
- *     kernel addresses them with 32-bit offsets); others: BR_ERR_UNSUPPORTED.
+ *     kernel addresses them with 32-bit offsets); an attention plan of fewer than 2^21 work
+ *     items (row tiles of 128 (token, head) rows plus the query's split-key chunks: far beyond
+ *     what K and V below 4 GiB allow, except with very many one-token segments); others:
+ *     BR_ERR_UNSUPPORTED.
  */
 #ifndef BLOCKRANK_H
 #define BLOCKRANK_H

@@ -512,3 +512,19 @@ def test_sink_rejects_nan_before_any_hip_call():
     assert rc == br._lib.BR_ERR_INVALID_ARG
     rc = lib.br_attn_fwd_sink(ctypes.byref(dims), f, f, f, p(seg), p(sp), f, None, 0.0, 1.0, f, need - 1, None)
     assert rc == br._lib.BR_ERR_WORKSPACE
+
+
+def test_attention_plan_item_limit():
+    """A plan of 2^21 or more work items is refused as unsupported (the kernel packs an item index
+    into 21 bits of a tile code); one just below the limit is accepted.  One-token documents take
+    one item each; the query adds one item per 4,096-key chunk of the prefix."""
+    n_ok = (1 << 21) - 600
+    seg, sp, _, _ = workloads.segment_tables([(1, [1] * n_ok, 1)])
+    dims = br.make_dims(1, 8, 1, 64, int(seg[-1]))
+    items, _ = br.attn_plan_items(dims, seg, sp)
+    assert (1 << 21) - 600 < len(items) < (1 << 21)
+    seg, sp, _, _ = workloads.segment_tables([(1, [1] * (1 << 21), 1)])
+    dims = br.make_dims(1, 8, 1, 64, int(seg[-1]))
+    with pytest.raises(br.BlockRankError) as e:
+        br.attn_plan_items(dims, seg, sp)
+    assert e.value.status == br._lib.BR_ERR_UNSUPPORTED
