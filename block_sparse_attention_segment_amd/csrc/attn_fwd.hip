@@ -212,20 +212,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
   auto code_it = [](int code) { return code >> IT_SHIFT; };
   auto code_keys = [](int code) { return (code >> 3) & 63; };
   auto n_tiles = [](int a0, int a1) { return a1 > a0 ? (a1 - a0 + BN - 1) / BN : 0; };
-  // Lead cursor: item c_it (its key ranges and first row cached), tile c_t of c_nt (c_na unmasked).
-  int c_it = it_begin, c_t = 0, c_a0, c_a1, c_b0, c_b1, c_na, c_nt, c_row0, c_idle;
+  // Lead cursor: item c_it; its next tile starts at key c_cur of the range ending at c_end; c_left
+  // tiles of the item are left, c_la of them in the unmasked range; c_base holds the item's code
+  // bits (index, idle), c_fl the range and first-tile flags of the next tile.
+  int c_it = it_begin, c_cur, c_end, c_left, c_la, c_base, c_fl, c_row0, c_b0, c_b1;
   const int w_tok0 = 32 * w / G;  // first token of this wave's rows
   auto load_item = [&]() {
     if (c_it < it_end) {
       const AttnItem it = items[c_it];
+      const int na = n_tiles(it.a_start, it.a_end);
       c_row0 = it.row0;
-      c_idle = w_tok0 >= it.row_limit - it.row0 ? F_IDLE : 0;
-      c_a0 = it.a_start;
-      c_a1 = it.a_end;
+      c_base = (c_it << IT_SHIFT) | (w_tok0 >= it.row_limit - it.row0 ? F_IDLE : 0);
+      c_la = na;
+      c_left = na + n_tiles(it.b_start, it.b_end);
+      c_cur = na > 0 ? it.a_start : it.b_start;
+      c_end = na > 0 ? it.a_end : it.b_end;
+      c_fl = F_FIRST | (na > 0 ? 0 : F_CAUSAL);
       c_b0 = it.b_start;
       c_b1 = it.b_end;
-      c_na = n_tiles(c_a0, c_a1);
-      c_nt = c_na + n_tiles(c_b0, c_b1);
     }
   };
   load_item();
@@ -235,14 +239,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
       code = (it_end << IT_SHIFT) | F_FIRST | F_LAST | F_IDLE;
       return;
     }
-    const bool causal = c_t >= c_na;
-    start = causal ? c_b0 + (c_t - c_na) * BN : c_a0 + c_t * BN;
-    const int keys = min(BN, (causal ? c_b1 : c_a1) - start);
-    code = (c_it << IT_SHIFT) | (keys << 3) | c_idle | (causal ? F_CAUSAL : 0) | (c_t == 0 ? F_FIRST : 0) |
-           (c_t + 1 == c_nt ? F_LAST : 0);
+    start = c_cur;
+    code = c_base | c_fl | (min(BN, c_end - c_cur) << 3) | (c_left == 1 ? F_LAST : 0);
     row0 = c_row0;
-    if (++c_t == c_nt) {
-      c_t = 0;
+    c_fl &= ~F_FIRST;
+    c_cur += BN;
+    if (--c_la == 0) {  // the unmasked range is done: the causal range follows
+      c_cur = c_b0;
+      c_end = c_b1;
+      c_fl = F_CAUSAL;
+    }
+    if (--c_left == 0) {
       ++c_it;
       load_item();
     }
