@@ -191,6 +191,15 @@ def measure(config, seed, steps, warmup, log):
     del sc_ws
     doc_tokens = int(sum(sum(lens) for (_, lens, _) in w.prompts))
     readout_bytes = float(doc_tokens * Hkv * d * 2 + Q_S.numel() * 2 + w.num_docs * 4)
+    # The readout measurement leaves the GPU mostly idle, and a GPU that has been idle runs its
+    # first milliseconds slower: a quarter second of steps brings it back to its working clocks
+    # before the warm-up steps (without it, 20 timed steps at 100K tokens measured 0.70 ms per
+    # step after 5 warm-up steps and 0.65-0.67 ms after 25).
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < 0.25:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
