@@ -222,8 +222,8 @@ hipError_t attn_workgroups(int* out) {
 
 
 // Token count from which the ranking step runs its readout beside the attention (measured on
-// MI355X: 3% faster at 100,096 tokens, 1.4% at 16 x 13,500, 3% slower at 12,864).
-constexpr int64_t kSideStreamMinTokens = 32768;
+// MI355X: 3% faster at 100,096 tokens, 1.4% at 16 x 13,500 and 3% at 30,407; 14% slower at 12,864).
+constexpr int64_t kSideStreamMinTokens = 24576;
 
 // A second stream per device for the ranking step's readout, which depends only on the inputs
 // and runs beside the attention: forked from and joined back to the caller's stream with two

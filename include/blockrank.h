@@ -215,7 +215,7 @@ br_status br_attn_routed_fwd(const br_dims* dims, const void* Q, const void* K, 
  * theirs.  workspace: >= br_rank_workspace_bytes(), 16-byte aligned.  br_rank_prompts_timed
  * also records kernel_start / kernel_stop (hipEvent_t, may be NULL) on `stream` immediately
  * around the attention kernel.
- * Streams: for batches of at least 32,768 tokens (timed or not), the readout and rank,
+ * Streams: for batches of at least 24,576 tokens (timed or not), the readout and rank,
  * which read only the inputs, run on a stream the library owns (one per device, default
  * priority, created on first use and kept until the process ends), forked from `stream` after
  * the plan upload and joined back into it; work enqueued on `stream` afterwards, and a

@@ -1,5 +1,5 @@
 """GPU parity on the named workloads at their full sizes, in the launch configuration the bench
-times (one br_rank_prompts call per step: on the caller's stream below 32,768 tokens, with the
+times (one br_rank_prompts call per step: on the caller's stream below 24,576 tokens, with the
 readout on the side stream above): the worked shape (every row checked), the long list (sampled
 rows, all scores), the ragged lists with a planted document, and the 16-prompt batch."""
 import numpy as np
