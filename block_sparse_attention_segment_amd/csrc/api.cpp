@@ -974,6 +974,7 @@ br_status br_attn_bwd(const br_dims* dims, const void* Q, const void* K, const v
     a.dK = dK;
     a.dV = dV;
     a.dvec = reinterpret_cast<float*>(ws + plan.off_dvec);
+    a.nlse2 = a.dvec + dims->total_tokens * dims->num_q_heads;
     a.items = reinterpret_cast<const br::AttnItem*>(ws + plan.off_items);
     a.merges = reinterpret_cast<const br::MergeItem*>(ws + plan.off_merges);
     a.part_dq = reinterpret_cast<float*>(ws + plan.off_part_dq);

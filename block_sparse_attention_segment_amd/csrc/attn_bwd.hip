@@ -30,6 +30,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __r
                                                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ O,
                                                           const uint16_t* __restrict__ dO,
                                                           const float* __restrict__ lse, float* __restrict__ dvec,
+                                                          float* __restrict__ nlse2,
                                                           float* __restrict__ dQ, const AttnItem* __restrict__ items,
                                                           float* __restrict__ part_dq, int Hq, int Hkv, float scale,
                                                           float scale_log2) {
@@ -93,7 +94,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __r
     }
     dr = acc0 + acc1;
     dr += other_half(dr);
-    if (row_ok && half == 0 && (it.slot < 0 || it.b_end > it.b_start)) dvec[rix] = dr;
+    if (row_ok && half == 0 && (it.slot < 0 || it.b_end > it.b_start)) {
+      dvec[rix] = dr;
+      nlse2[rix] = -l2;  // the key-major kernel's exponent offset
+    }
   }
 
   // Row reads (A operands of S^T and dP^T): key 32 kb + n, unit 2 st + half.
@@ -271,7 +275,7 @@ __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
 template <int D, int G>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                              const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                                                             const float* __restrict__ lse, const float* __restrict__ dvec,
+                                                             const float* __restrict__ nlse2, const float* __restrict__ dvec,
                                                              float* __restrict__ dK, float* __restrict__ dV,
                                                              const KvItem* __restrict__ items, float* __restrict__ part_dkv,
                                                              int Hq, int Hkv, int kv_slots, float scale, float scale_log2) {
@@ -288,7 +292,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(const uint16_t* __
   static_assert(NDMA >= 1 && NDMA * KPI * 4 == RS, "a step's rows split over four waves");
   __shared__ __align__(1024) uint8_t sq[2][TILE];
   __shared__ __align__(1024) uint8_t sd[2][TILE];
-  __shared__ __align__(256) float sl[2][64];  // the rows' lse (natural log), then their Dr
+  __shared__ __align__(256) float sl[2][64];  // the rows' -lse log2(e), then their Dr
   __shared__ __align__(256) float sr[2][64];
 
   const int g = blockIdx.x % Hkv;
@@ -346,7 +350,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(const uint16_t* __
   const int nS = nC + nU;
   auto step_t0 = [&](int i) { return i < nC ? it.c0 + i * TR : it.u0 + (i - nC) * TR; };
   auto step_end = [&](int i) { return i < nC ? it.c1 : it.u1; };
-  // Rows past the range's end load as zeros (Q, dO, lse, Dr): their S and dP are 0, so they add
+  // Rows past the range's end load as zeros (Q, dO, -lse log2(e), Dr): their S and dP are 0, so they add
   // P = 1 times a zero dO row to dV and dS = 0 to dK, i.e. nothing.
   auto issue = [&](int i, int slot) {
     const int t0 = __builtin_amdgcn_readfirstlane(step_t0(i));
@@ -359,7 +363,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(const uint16_t* __
     for (int r = 0; r < NDMA; ++r) buf_load16_lds(bq, lq + 1024 * r, dofs[r]);
 #pragma unroll
     for (int r = 0; r < NDMA; ++r) buf_load16_lds(bd, ld + 1024 * r, dofs[r]);
-    if (w == 0) buf_load4_lds(make_rsrc(lse + base, ntok * Hq * 4), lds_addr_of(&sl[slot][0]), lofs);
+    if (w == 0) buf_load4_lds(make_rsrc(nlse2 + base, ntok * Hq * 4), lds_addr_of(&sl[slot][0]), lofs);
     if (w == 1) buf_load4_lds(make_rsrc(dvec + base, ntok * Hq * 4), lds_addr_of(&sr[slot][0]), lofs);
   };
   if (nS > 0) issue(0, 0);
@@ -398,7 +402,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(const uint16_t* __
         float pr[4], dsv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          pr[r] = fast_exp2(fmaf(s[b][r], scale_log2, -(l4[r] * kLog2e)));
+          pr[r] = fast_exp2(fmaf(s[b][r], scale_log2, l4[r]));
           if (masked) pr[r] = key <= t0 + (r0 + r) / G ? pr[r] : 0.f;
           dsv[r] = pr[r] * (dp[b][r] - d4[r]);
         }
@@ -474,7 +478,7 @@ static hipError_t launch_bwd_t(const BwdLaunch& a, hipStream_t stream) {
   hipError_t e = hipSuccess;
   if (a.n_items > 0) {
     attn_bwd_dq_kernel<D, G><<<unsigned(a.n_items * a.num_kv_heads), 256, 0, stream>>>(
-        a.Q, a.K, a.V, a.O, a.dO, a.lse, a.dvec, a.dQ, a.items, a.part_dq, a.num_q_heads, a.num_kv_heads, a.scale,
+        a.Q, a.K, a.V, a.O, a.dO, a.lse, a.dvec, a.nlse2, a.dQ, a.items, a.part_dq, a.num_q_heads, a.num_kv_heads, a.scale,
         a.scale * kLog2e);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -487,7 +491,7 @@ static hipError_t launch_bwd_t(const BwdLaunch& a, hipStream_t stream) {
   }
   if (a.n_kv_items > 0) {
     attn_bwd_dkv_kernel<D, G><<<unsigned(a.n_kv_items * a.num_kv_heads), 256, 0, stream>>>(
-        a.Q, a.K, a.V, a.dO, a.lse, a.dvec, a.dK, a.dV, a.kv_items, a.part_dkv, a.num_q_heads, a.num_kv_heads,
+        a.Q, a.K, a.V, a.dO, a.nlse2, a.dvec, a.dK, a.dV, a.kv_items, a.part_dkv, a.num_q_heads, a.num_kv_heads,
         a.kv_slots, a.scale, a.scale * kLog2e);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -85,6 +85,7 @@ struct BwdLaunch {
   const float* lse;          // [T, Hq] natural-log log-sum-exp from the forward
   float *dQ, *dK, *dV;       // fp32 outputs
   float* dvec;               // [T, Hq] workspace: rowsum(dO * O)
+  float* nlse2;              // [T, Hq] workspace: -lse * log2(e)
   const AttnItem* items;     // device copies of the forward plan's items and merges
   const MergeItem* merges;
   float* part_dq;

@@ -151,7 +151,7 @@ Error build_bwd_plan(const br_dims& dims, const int32_t* so, const int32_t* sp, 
   P.off_part_dq = align_up(P.off_kv_merges + P.kv_merges.size() * sizeof(KvMerge), 256);
   P.off_part_dkv = align_up(P.off_part_dq + size_t(P.fwd.n_slots) * hkv * kRowsPerTile * d * 4, 256);
   P.off_dvec = align_up(P.off_part_dkv + size_t(P.kv_slots) * hkv * kBwdKeyTile * d * 4 * 2, 256);
-  P.total_bytes = align_up(P.off_dvec + size_t(dims.total_tokens) * hq * 4, 256);
+  P.total_bytes = align_up(P.off_dvec + size_t(dims.total_tokens) * hq * 4 * 2, 256);  // Dr, then -lse log2(e)
   return {};
 }
 

@@ -318,7 +318,8 @@ br_status br_attn_plan_schedule(const br_dims* dims, const int32_t* segment_offs
  *   dQ: device fp32 [total_tokens, Hq, d];  dK, dV: device fp32 [total_tokens, Hkv, d]; every
  *       element is written.
  *   Segment tables, scale, alignment and errors as br_attn_fwd; workspace as sized by
- *   br_attn_bwd_workspace_bytes (it also holds rowsum(dO * O) and split partial sums).
+ *   br_attn_bwd_workspace_bytes (it also holds rowsum(dO * O), -lse * log2(e) and split partial
+ *   sums).
  * Arithmetic: P and dS in fp32, rounded to bf16 for the P^T dO, dS K and dS^T Q products,
  * fp32 accumulation; split partial sums are added in a fixed order (deterministic).
  */
