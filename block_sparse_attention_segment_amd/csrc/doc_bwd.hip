@@ -94,7 +94,9 @@ __global__ __launch_bounds__(64) void doc_bwd_kernel(const uint16_t* __restrict_
   constexpr int DSTEPS = D / 16, DBLK = D / 32, KCH = D / 8;
   constexpr int VROW = D == 128 ? 160 : 96;  // row reads and transposing reads (as V in the forward)
   constexpr int R = RB * 32;                 // signal rows handled (padded)
-  __shared__ __align__(16) uint16_t sk[32 * VROW];
+  constexpr int RBK = 2 * D;             // bytes per K row in LDS (unpadded, 16-byte units swizzled)
+  constexpr int UPR = D / 8, KPI = 1024 / RBK, NDMA = 32 / KPI;  // direct-to-LDS: rows per instruction
+  __shared__ __align__(1024) uint8_t sk[32 * RBK];
   __shared__ __align__(16) uint16_t sq[R * VROW];
   __shared__ float sM[R], sZ[R], sC[R];
 
@@ -143,6 +145,35 @@ __global__ __launch_bounds__(64) void doc_bwd_kernel(const uint16_t* __restrict_
   // head-dim half (lane / 16) % 2, row half `half`.
   const int vs = lane & 15, vdh = (lane >> 4) & 1;
   const int t_lane = (4 * half + (vs >> 2)) * VROW + 16 * vdh + 4 * (vs & 3);
+  // The K tile: row r at RBK r bytes, 16-byte unit c at c ^ swz(r), which keeps both its row reads
+  // (16 keys at one unit) and its transposing reads (4 keys x 2 unit pairs per half-wave, keys + 8
+  // with the swizzle ^ 2) free of bank conflicts; it repeats every 16 rows.
+  auto swz = [](int r) { return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3); };
+  uint32_t kro[DSTEPS];  // row reads: key n, unit 2 s + half
+#pragma unroll
+  for (int st = 0; st < DSTEPS; ++st) kro[st] = uint32_t(n * RBK + 16 * ((2 * st + half) ^ swz(n)));
+  const int tr_r = 4 * half + (vs >> 2);
+  uint32_t ktl[DBLK], kth[DBLK];  // transposing reads: keys tr_r (+ 8), head-dim element 32 b + 16 vdh + 4 (vs % 4)
+#pragma unroll
+  for (int b = 0; b < DBLK; ++b) {
+    const int unit = 4 * b + 2 * vdh + ((vs & 3) >> 1);
+    ktl[b] = uint32_t(tr_r * RBK + 16 * (unit ^ swz(tr_r)) + 8 * (vs & 1));
+    kth[b] = uint32_t((tr_r + 8) * RBK + 16 * (unit ^ swz(tr_r + 8)) + 8 * (vs & 1));
+  }
+  // Direct-to-LDS loads of a 32-key block: instruction i fills LDS bytes [1 KB i, 1 KB (i + 1)):
+  // lane l unit l % UPR of key row KPI i + l / UPR, from source unit (l % UPR) ^ swz(row).  Keys
+  // past the document's end load as zeros.
+  const uint32_t sk_lds = lds_addr_of(sk);
+  auto issue_k = [&](int t0, int nk) {
+    t0 = __builtin_amdgcn_readfirstlane(t0);
+    nk = __builtin_amdgcn_readfirstlane(nk);
+    const rsrc_t r = make_rsrc(K + int64_t(t0) * kv_stride + g * D, nk * int(kv_stride) * 2);
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const int row = KPI * i + lane / UPR, c = (lane % UPR) ^ swz(row);
+      buf_load16_lds(r, sk_lds + 1024 * i, uint32_t(row * int(kv_stride) * 2 + 16 * c));
+    }
+  };
 
   f32x16_t aq[RB][DBLK];
 #pragma unroll
@@ -150,25 +181,29 @@ __global__ __launch_bounds__(64) void doc_bwd_kernel(const uint16_t* __restrict_
 #pragma unroll
     for (int b = 0; b < DBLK; ++b) aq[rb][b] = f32x16_t{};
 
+  // Blocks of 32 keys inside each document of the group, in order.  Block i + 1's keys are loaded
+  // into the (single) K tile as soon as block i's last read of it is done, so that load overlaps
+  // block i's dK read-modify-write and stores.
+  if (it.d0 < it.d1) issue_k(dof[it.d0], min(32, dof[it.d0 + 1] - dof[it.d0]));
+  bool first = true;
   for (int d = it.d0; d < it.d1; ++d) {
     const int a = dof[d], e = dof[d + 1];
     const float gk = dscores[it.score_base + (d - it.d0)];
     for (int t0 = a; t0 < e; t0 += 32) {
       const int nk = min(32, e - t0);
-      __syncthreads();  // the previous block's LDS reads are done
-      {
-        const rsrc_t r = make_rsrc(K + int64_t(t0) * kv_stride + g * D, nk * int(kv_stride) * 2);
-#pragma unroll
-        for (int p = 0; p < 32 * KCH / 64; ++p) {
-          const int u = p * 64 + lane, row = u / KCH, c = u % KCH;
-          *reinterpret_cast<u32x4_t*>(&sk[row * VROW + 8 * c]) =
-              buf_load16(r, uint32_t((row * int(kv_stride) + 8 * c) * 2));
-        }
+      // This block's keys have landed: all that was issued after them is the previous block's
+      // dK stores (its dK loads were consumed before the stores).
+      if (first) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      } else if constexpr (D == 128) {
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
       }
-      __syncthreads();
+      first = false;
       u32x4_t kf[DSTEPS];
 #pragma unroll
-      for (int s = 0; s < DSTEPS; ++s) kf[s] = load16(&sk[n * VROW + 16 * s + 8 * half]);
+      for (int s = 0; s < DSTEPS; ++s) kf[s] = load16(sk + kro[s]);
       f32x16_t ak[DBLK];
 #pragma unroll
       for (int b = 0; b < DBLK; ++b) ak[b] = f32x16_t{};
@@ -199,16 +234,27 @@ __global__ __launch_bounds__(64) void doc_bwd_kernel(const uint16_t* __restrict_
         for (int m = 0; m < 2; ++m) {
           const u32x4_t bk = {pk[4 * m], pk[4 * m + 1], pk[4 * m + 2], pk[4 * m + 3]};
           const u32x4_t bq = {pd[4 * m], pd[4 * m + 1], pd[4 * m + 2], pd[4 * m + 3]};
-          const uint16_t* kt = &sk[t_lane + 16 * m * VROW];
+          const uint8_t* kt = sk + 16 * m * RBK;
           const uint16_t* qt = &sq[t_lane + (32 * rb + 16 * m) * VROW];
 #pragma unroll
           for (int b = 0; b < DBLK; ++b) {
-            const u32x2_t klo = lds_read_tr16(kt + 32 * b), khi = lds_read_tr16(kt + 8 * VROW + 32 * b);
+            const u32x2_t klo = lds_read_tr16(reinterpret_cast<const uint16_t*>(kt + ktl[b]));
+            const u32x2_t khi = lds_read_tr16(reinterpret_cast<const uint16_t*>(kt + kth[b]));
             aq[rb][b] = mfma32(u32x4_t{klo[0], klo[1], khi[0], khi[1]}, bk, aq[rb][b]);
             const u32x2_t qlo = lds_read_tr16(qt + 32 * b), qhi = lds_read_tr16(qt + 8 * VROW + 32 * b);
             ak[b] = mfma32(u32x4_t{qlo[0], qlo[1], qhi[0], qhi[1]}, bq, ak[b]);
           }
         }
+      }
+      // Every read of this block's K tile is done: load the next block's keys into it.
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      {
+        int nt0 = t0 + 32, nd = d;
+        if (nt0 >= e) {
+          ++nd;
+          nt0 = nd < it.d1 ? dof[nd] : 0;
+        }
+        if (nd < it.d1) issue_k(nt0, min(32, dof[nd + 1] - nt0));
       }
       // ak[b] register r: head-dim element 32 b + 8 (r / 4) + 4 half + r % 4 of key t0 + n.
       if (n < nk) {
