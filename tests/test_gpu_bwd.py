@@ -45,7 +45,8 @@ def run_case(w, seed, scale=0.0):
     return dQ, dK, dV, dO_bits
 
 
-CASES = [(0, 4, 1, 64), (1, 32, 8, 128), (2, 8, 8, 128), (3, 16, 2, 64), (4, 8, 1, 128)]
+CASES = [(0, 4, 1, 64), (1, 32, 8, 128), (2, 8, 8, 128), (3, 16, 2, 64), (4, 8, 1, 128), (5, 16, 8, 64),
+         (6, 8, 4, 128)]  # query heads per KV head 4, 4, 1, 8, 8, 2, 2
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"s{c[0]}_Hq{c[1]}_Hkv{c[2]}_d{c[3]}" for c in CASES])

@@ -47,10 +47,11 @@ def test_tiny_config(seed):
     _full_check(w, f"tiny seed={seed}")
 
 
-SHAPES = [(1, 1, 64), (2, 1, 64), (4, 1, 128), (8, 1, 64), (8, 2, 128), (32, 8, 128), (4, 4, 128), (16, 2, 64)]
+SHAPES = [(1, 1, 64), (2, 1, 64), (4, 1, 128), (8, 1, 64), (8, 2, 128), (32, 8, 128), (4, 4, 128), (16, 2, 64),
+          (8, 4, 128)]
 
 
-@pytest.mark.parametrize("case", range(16))
+@pytest.mark.parametrize("case", range(18))
 def test_random_small_tables(case):
     rng = random.Random(1000 + case)
     hq, hkv, d = SHAPES[case % len(SHAPES)]
