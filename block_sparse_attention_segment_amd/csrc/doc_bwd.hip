@@ -303,9 +303,12 @@ __global__ __launch_bounds__(kReduceSlices * D / 4) void doc_bwd_reduce_kernel(c
   if (rho >= n_signal * G) return;  // uniform per workgroup
   const int ch = threadIdx.x % CH, sl = threadIdx.x / CH;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const int64_t item_stride = int64_t(Hkv) * RB * 32 * D;
+  const float* src = part + (int64_t(g) * RB + rho / 32) * 32 * D + (rho % 32) * D + 4 * ch;
+  // Unrolled so that eight loads are in flight; the additions stay in item order.
+#pragma unroll 8
   for (int i = prompt_items[b] + sl; i < prompt_items[b + 1]; i += kReduceSlices)
-    acc += *reinterpret_cast<const f32x4_t*>(part + ((int64_t(i) * Hkv + g) * RB + rho / 32) * 32 * D +
-                                             (rho % 32) * D + 4 * ch);
+    acc += *reinterpret_cast<const f32x4_t*>(src + int64_t(i) * item_stride);
   red[sl][ch] = acc;
   __syncthreads();
   if (sl == 0) {
