@@ -246,7 +246,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_merge_kernel(float* __restric
   const int64_t stride = int64_t(Hkv) * kRowsPerTile * D;
   const float* src = part_dq + ((int64_t(mi.slot0) * Hkv + g) * kRowsPerTile + rho) * D + 4 * ch;
   f32x4_t a = {0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < mi.nslots; ++c) a += *reinterpret_cast<const f32x4_t*>(src + c * stride);
+#pragma unroll 8
+  for (int c = 0; c < mi.nslots; ++c) a += *reinterpret_cast<const f32x4_t*>(src + c * stride);  // slot order
   *reinterpret_cast<f32x4_t*>(dQ + (int64_t(tok) * Hq + h) * D + 4 * ch) = a;
 }
 
@@ -465,7 +466,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_merge_kernel(float* __restri
   const float* src = part_dkv + ((int64_t(mi.slot0) * Hkv + g) * kBwdKeyTile + kk) * D + 4 * ch;
   const float* srcv = src + int64_t(kv_slots) * stride;
   f32x4_t a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < mi.nslots; ++c) {
+#pragma unroll 8
+  for (int c = 0; c < mi.nslots; ++c) {  // slot order
     a += *reinterpret_cast<const f32x4_t*>(src + c * stride);
     b += *reinterpret_cast<const f32x4_t*>(srcv + c * stride);
   }
