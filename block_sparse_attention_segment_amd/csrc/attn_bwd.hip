@@ -9,9 +9,11 @@
 //   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO
 // Only allowed (row, key) pairs are visited, through the same host plans as the forward:
 //   attn_bwd_dq_kernel   query-major over the forward plan's row tiles (128 (token, head) rows,
-//                        4 waves of 32 rows); it also forms Dr for its rows: per 64-key tile S^T = K Q^T and dP^T = V dO^T
-//                        (keys on M), dS^T in fp32, dQ^T += K^T dS^T with dS rounded to bf16
-//                        and K^T fragments from transposing LDS reads (as V^T in the forward).
+//                        4 waves of 32 rows); it also forms Dr (and -lse log2 e) for its rows.
+//                        Per 64-key tile, loaded straight into LDS while the previous one is
+//                        used: S^T = K Q^T and dP^T = V dO^T (keys on M), dS^T in fp32,
+//                        dQ^T += K^T dS^T with dS rounded to bf16 and K^T fragments from
+//                        transposing LDS reads (as V^T in the forward).
 //   attn_bwd_dkv_kernel  key-major: 64 keys of one KV head per workgroup (4 waves of 16 keys,
 //                        16x16x32 products); the rows that read them stream through LDS 64
 //                        (token, head) rows at a time by direct-to-LDS loads, the next step's
