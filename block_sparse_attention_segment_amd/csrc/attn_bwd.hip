@@ -20,7 +20,9 @@
 //                        in flight: S = Q K^T and dP = dO V^T (rows on M), then dV^T += dO^T P
 //                        and dK^T += Q^T dS with the row-side operands read transposed from LDS.
 // Long row or key ranges are split; their fp32 partials are summed by the merge kernels in a
-// fixed order, so results are deterministic.  Outputs are fp32.
+// fixed order, so results are deterministic.  Outputs are fp32.  Both kernels stage their fp32
+// rows through LDS so that every store writes whole rows, and store them with the non-temporal
+// hint: nothing reads them again in this pass.
 #include "device_common.h"
 #include "launch.h"
 #include "plan.h"
@@ -205,7 +207,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __r
   __syncthreads();  // every wave is done with the tiles before the rows are staged over them
   // acc[b] register r holds head-dim element 32 b + 8 (r / 4) + 4 half + r % 4 of this lane's row.
   // The rows go through this wave's part of the (now idle) tile buffers, so that each store
-  // instruction writes whole rows (two at d = 128) instead of 32 bytes of each of 32 rows.
+  // instruction writes whole rows (two at d = 128) instead of 32 bytes of each of 32 rows.  Whole
+  // lines can take the non-temporal hint (partial lines written that way reach HBM unmerged).
   // Row n at 4D n bytes, its 16-byte unit c at c ^ (n mod 16).
   uint8_t* const stage = lds + w * 32 * 4 * D;
 #pragma unroll
@@ -223,9 +226,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const uint16_t* __r
     const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage + r * 4 * D + 16 * (c ^ (r & 15)));
     if (it.slot < 0) {
       const int tok = it.row0 + rr % TM;
-      if (tok < it.row_limit) *reinterpret_cast<f32x4_t*>(dQ + (int64_t(tok) * Hq + g * G + rr / TM) * D + 4 * c) = v;
+      if (tok < it.row_limit) __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(dQ + (int64_t(tok) * Hq + g * G + rr / TM) * D + 4 * c));
     } else {
-      *reinterpret_cast<f32x4_t*>(part_dq + ((int64_t(it.slot) * Hkv + g) * kRowsPerTile + rr) * D + 4 * c) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(part_dq + ((int64_t(it.slot) * Hkv + g) * kRowsPerTile + rr) * D + 4 * c));
     }
   }
 }
@@ -430,22 +433,39 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(const uint16_t* __
       }
     }
   }
-  if (key >= it.k_limit) return;
-  // ak / av[db] register r holds head-dim element 16 db + 4 u + r of this lane's key.
-  float *pk_, *pv_;
-  if (it.slot < 0) {
-    pk_ = dK + (int64_t(key) * Hkv + g) * D;
-    pv_ = dV + (int64_t(key) * Hkv + g) * D;
-  } else {
-    const int64_t base = ((int64_t(it.slot) * Hkv + g) * kBwdKeyTile + 16 * w + m) * D;
-    pk_ = part_dkv + base;
-    pv_ = part_dkv + int64_t(kv_slots) * Hkv * kBwdKeyTile * D + base;
-  }
+  __syncthreads();  // every wave is done with the last step's rows before they are overwritten
+  // ak / av[db] register r holds head-dim element 16 db + 4 u + r of this lane's key.  The fp32
+  // rows go through this wave's part of the idle row slots (dK^T in sq, dV^T in sd), so that each
+  // store writes whole rows.  Key row n at 4 D n bytes, its 16-byte unit c at c ^ (n mod 16).
+  uint8_t* const stk = &sq[0][0] + w * 16 * 4 * D;
+  uint8_t* const stv = &sd[0][0] + w * 16 * 4 * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
-    const int e = 16 * db + 4 * u;
-    *reinterpret_cast<f32x4_t*>(pk_ + e) = ak[db] * scale;
-    *reinterpret_cast<f32x4_t*>(pv_ + e) = av[db];
+    const int o = m * 4 * D + 16 * ((4 * db + u) ^ m);
+    *reinterpret_cast<f32x4_t*>(stk + o) = ak[db] * scale;
+    *reinterpret_cast<f32x4_t*>(stv + o) = av[db];
+  }
+  constexpr int CPR = D / 4;     // 16-byte columns per row
+  constexpr int RPI = 64 / CPR;  // rows per store instruction
+  const int c = lane % CPR;
+#pragma unroll
+  for (int i = 0; i < 16 / RPI; ++i) {
+    const int r = RPI * i + lane / CPR, kk = 16 * w + r;
+    if (it.k0 + kk >= it.k_limit) continue;
+    const int o = r * 4 * D + 16 * (c ^ r);
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(stk + o);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(stv + o);
+    float *pk_, *pv_;
+    if (it.slot < 0) {
+      pk_ = dK + (int64_t(it.k0 + kk) * Hkv + g) * D;
+      pv_ = dV + (int64_t(it.k0 + kk) * Hkv + g) * D;
+    } else {
+      const int64_t base = ((int64_t(it.slot) * Hkv + g) * kBwdKeyTile + kk) * D;
+      pk_ = part_dkv + base;
+      pv_ = part_dkv + int64_t(kv_slots) * Hkv * kBwdKeyTile * D + base;
+    }
+    __builtin_nontemporal_store(a, reinterpret_cast<f32x4_t*>(pk_ + 4 * c));
+    __builtin_nontemporal_store(b, reinterpret_cast<f32x4_t*>(pv_ + 4 * c));
   }
 }
 
