@@ -460,7 +460,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
       //   B  P.V MFMAs of tile j - 1, keys 16..31   | exponentials of keys whose P slots A freed
       //   C  S^T MFMAs of tile j + 1                | remaining exponentials, row sum
       // Each phase's LDS operands are read one phase ahead.  P of tile j overwrites P of tile j - 1
-      // in the registers the P.V products have finished reading.
+      // in the registers the P.V products have finished reading.  In phases A and B each product
+      // is followed by two of the next phase's LDS reads and a few vector instructions
+      // (scheduling groups), so a wave's in-order issue does not wait on a busy matrix core with
+      // independent work behind it.  The wave raises its issue priority for the three phases:
+      // when both waves of a SIMD can issue, the one with matrix work goes first.
       const uint8_t* vt_base = &vring[VSLOT_PV][0];
       const uint8_t* kt_base = &kring[KSLOT_S][0];
       u32x4_t vf[2][DBLK];
@@ -492,6 +496,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
       constexpr int R_B = 6;  // exponentials of registers [0, R_B) in phase B, the rest in C
       read_v(0);
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
       // Phase A.
       {
         const u32x4_t pv = {pk[0], pk[1], pk[2], pk[3]};
@@ -509,6 +514,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
       const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
       m_run = m_new;
       mu = m_new == -INFINITY ? 0.f : m_new;
+#pragma unroll
+      for (int i = 0; i < DBLK; ++i) {  // product, two LDS reads, four vector instructions
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
       // Phase B.
       {
@@ -519,6 +530,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
 #pragma unroll
       for (int st = 0; st < DSTEPS; ++st) kf[st] = *reinterpret_cast<const u32x4_t*>(kt_base + kofs[st]);
       exps(0, R_B);
+#pragma unroll
+      for (int i = 0; i < DBLK; ++i) {  // product, two LDS reads, six vector instructions
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
       // Phase C (the second half of the K fragments is read while the first half is used).
       s_nxt = f32x16_t{};
@@ -527,6 +544,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
       exps(R_B, 16);
       l_run = (c_first ? 0.f : l_run * alpha) + (lsum0 + lsum1);
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
       // Keep the softmax results here: otherwise the compiler sinks them past the loop exit test
       // into the next iteration, where nothing overlaps them.
       asm volatile("" ::"v"(pk[0]), "v"(pk[1]), "v"(pk[2]), "v"(pk[3]), "v"(pk[4]), "v"(pk[5]), "v"(pk[6]),
