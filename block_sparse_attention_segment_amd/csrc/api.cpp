@@ -1188,6 +1188,16 @@ br_status check_sort_table(const int32_t* doc_ptr, int num_prompts, std::vector<
 // call at 100K tokens, so the last few plans are kept and reused when a call's dimensions and
 // host tables equal an entry's element by element (and the device and its workgroup count
 // match).  Entries are immutable once inserted; a mutex guards the list.
+// Device copy of a cached plan's upload image.  A copy of the holder (the same tables rescheduled
+// for another device) starts without one.
+struct DeviceImage {
+  std::mutex mu;
+  void* ptr = nullptr;
+  DeviceImage() = default;
+  DeviceImage(const DeviceImage&) {}
+  DeviceImage& operator=(const DeviceImage&) = delete;
+};
+
 struct RankPlan {
   int device = -1, workgroups = 0;
   br_dims dims{};
@@ -1198,7 +1208,44 @@ struct RankPlan {
   std::vector<int32_t> base;
   RankLayout L;
   std::vector<unsigned char> host;  // the upload image
+  mutable DeviceImage image;        // on `device`, from the plan's first reuse
+  RankPlan() = default;
+  RankPlan(const RankPlan&) = default;
+  RankPlan& operator=(const RankPlan&) = delete;
+  // Calls already enqueued may still read the device copy: it is freed once the device is idle
+  // (if that cannot be established, it is left allocated).
+  ~RankPlan() {
+    if (!image.ptr) return;
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return;
+    if (hipSetDevice(device) == hipSuccess && hipDeviceSynchronize() == hipSuccess) (void)hipFree(image.ptr);
+    (void)hipSetDevice(cur);
+  }
 };
+
+// The device copy of a cached plan's image, made at the first call that reuses the plan: a
+// blocking copy followed by a device synchronisation, so that every later call, from any host
+// thread or stream, reads a complete image and uploads nothing.  nullptr when the copy cannot be
+// made (the call then uploads into its workspace, as for a new plan).
+const unsigned char* device_image(const RankPlan& p) {
+  std::lock_guard<std::mutex> guard(p.image.mu);
+  if (!p.image.ptr) {
+    void* d = nullptr;
+    if (hipMalloc(&d, p.host.size()) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    if (hipMemcpy(d, p.host.data(), p.host.size(), hipMemcpyHostToDevice) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+      (void)hipGetLastError();
+      (void)hipDeviceSynchronize();
+      (void)hipFree(d);
+      return nullptr;
+    }
+    p.image.ptr = d;
+  }
+  return static_cast<const unsigned char*>(p.image.ptr);
+}
 
 bool same_tables(const RankPlan& e, const br_dims& d, int32_t n_signal, const int32_t* so, const int32_t* sp,
                  const int32_t* dof, const int32_t* dp) {
@@ -1343,8 +1390,13 @@ br_status br_rank_prompts_timed(const br_dims* dims, const void* Q, const void* 
     const RankLayout& L = plan->L;
     const std::vector<unsigned char>& host = plan->host;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
-    st = upload(ws, host.data(), host.size(), stream);
-    if (st != BR_OK) return st;
+    // A reused plan is read from its device copy; a new one is uploaded into the workspace.
+    const unsigned char* img = fresh ? nullptr : device_image(*plan);
+    if (!img) {
+      st = upload(ws, host.data(), host.size(), stream);
+      if (st != BR_OK) return st;
+      img = ws;
+    }
 
     br::AttnLaunch a;
     a.Q = static_cast<const uint16_t*>(Q);
@@ -1352,9 +1404,9 @@ br_status br_rank_prompts_timed(const br_dims* dims, const void* Q, const void* 
     a.V = static_cast<const uint16_t*>(V);
     a.O = static_cast<uint16_t*>(out);
     a.lse = lse;
-    a.items = reinterpret_cast<const br::AttnItem*>(ws + ap.off_items);
-    a.ranges = reinterpret_cast<const int32_t*>(ws + ap.off_ranges);
-    a.merges = reinterpret_cast<const br::MergeItem*>(ws + ap.off_merges);
+    a.items = reinterpret_cast<const br::AttnItem*>(img + ap.off_items);
+    a.ranges = reinterpret_cast<const int32_t*>(img + ap.off_ranges);
+    a.merges = reinterpret_cast<const br::MergeItem*>(img + ap.off_merges);
     a.part_o = reinterpret_cast<float*>(ws + L.attn_part);
     a.part_ml = reinterpret_cast<float*>(ws + L.attn_part + (ap.off_part_ml - ap.off_part_o));
     a.n_items = int64_t(ap.items.size());
@@ -1369,7 +1421,7 @@ br_status br_rank_prompts_timed(const br_dims* dims, const void* Q, const void* 
     a.ev_start = kernel_start;
     a.ev_stop = kernel_stop;
 
-    unsigned char* wsp = ws + L.score_plan;
+    const unsigned char* wsp = img + L.score_plan;
     br::ScoreLaunch r;
     r.Q_S = static_cast<const uint16_t*>(Q_S);
     r.K = static_cast<const uint16_t*>(K);
@@ -1410,7 +1462,7 @@ br_status br_rank_prompts_timed(const br_dims* dims, const void* Q, const void* 
       return BR_OK;
     }
     // The readout and rank read only the inputs: they run on the side stream, forked after the
-    // plan upload, while the attention and its merge run on the caller's stream; the caller's
+    // plan upload (if any), while the attention and its merge run on the caller's stream; the caller's
     // stream then waits for them.
     std::lock_guard<std::mutex> guard(side->lock);
     he = hipEventRecord(side->fork, stream);

@@ -222,7 +222,11 @@ br_status br_attn_routed_fwd(const br_dims* dims, const void* Q, const void* K, 
  * synchronisation of `stream`, see every output.  Otherwise everything runs on `stream`.
  * Plans: the library keeps the last four validated and scheduled plans (process lifetime) and
  * reuses one when a call's dims, n_signal and four host tables equal an entry's element by
- * element on the same device; the host arrays are still read during the call only.
+ * element on the same device; the host arrays are still read during the call only.  A new plan
+ * is uploaded into the workspace.  The first call that reuses a plan copies its image (a few
+ * hundred KB at 100K tokens) into device memory the library allocates, with a blocking copy and
+ * a device synchronisation; that call and later ones read the plan there and upload nothing.
+ * Dropping a plan from the four frees its copy after a device synchronisation.
  */
 br_status br_rank_workspace_bytes(const br_dims* dims, const int32_t* segment_offsets, const int32_t* seg_ptr,
                                   int32_t n_signal, const int32_t* doc_offsets, const int32_t* doc_ptr,

@@ -281,6 +281,30 @@ def test_rank_step_plan_cache_tells_tables_apart():
             assert torch.equal(out, a_out) and torch.equal(s, a_s) and torch.equal(o, a_o), (rep, w.prompts)
 
 
+def test_rank_step_plan_device_copies_made_and_dropped():
+    """From a plan's first reuse the step reads the plan from a device copy; six table sets used
+    twice each in turn overflow the four kept plans, so copies are made and freed over and over
+    (the first call of a set after its eviction uploads into the workspace again).  Every call
+    equals the separate calls bit for bit."""
+    kw = dict(hq=4, hkv=2, d=64, seed=11)
+    lens = [[30, 50, 20], [50, 30, 20], [20, 30, 50], [40, 40, 20], [10, 60, 30], [25, 25, 50]]
+    variants = [workloads.make_custom([(16, l, 16)], n_signal=4, **kw) for l in lens]
+    refs = []
+    for w in variants:
+        dev = upload(w)
+        out = br.attn_fwd(dev["Q"], dev["K"], dev["V"], w.segment_offsets, w.seg_ptr)
+        s = br.doc_scores(dev["Q_S"], dev["K"], w.doc_offsets, w.doc_ptr)
+        refs.append((dev, out, s, br.sort_docs(s, w.doc_ptr)))
+    log("[gpu] rank step plan device copies: six table sets, two calls each, three rounds")
+    for rep in range(3):
+        for w, (dev, a_out, a_s, a_o) in zip(variants, refs):
+            for call in range(2):
+                out, s, o = br.rank_step(dev["Q"], dev["K"], dev["V"], dev["Q_S"], w.segment_offsets, w.seg_ptr,
+                                         w.doc_offsets, w.doc_ptr)
+                torch.cuda.synchronize()
+                assert torch.equal(out, a_out) and torch.equal(s, a_s) and torch.equal(o, a_o), (rep, call, w.prompts)
+
+
 def test_many_prompts_rank_and_attention():
     """300 small prompts in one call (more than one sort launch's 256 prompts): attention against
     the dense oracle, scores and per-prompt order against the oracle's, and the one-call step equal
