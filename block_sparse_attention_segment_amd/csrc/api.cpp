@@ -1226,10 +1226,17 @@ struct RankPlan {
 // The device copy of a cached plan's image, made at the first call that reuses the plan: a
 // blocking copy followed by a device synchronisation, so that every later call, from any host
 // thread or stream, reads a complete image and uploads nothing.  nullptr when the copy cannot be
-// made (the call then uploads into its workspace, as for a new plan).
-const unsigned char* device_image(const RankPlan& p) {
+// made, or while `stream` is being captured (the call then uploads into its workspace, as for a new
+// plan).
+const unsigned char* device_image(const RankPlan& p, hipStream_t stream) {
   std::lock_guard<std::mutex> guard(p.image.mu);
   if (!p.image.ptr) {
+    // Neither the allocation nor the synchronisation may happen while the stream is captured.
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
     void* d = nullptr;
     if (hipMalloc(&d, p.host.size()) != hipSuccess) {
       (void)hipGetLastError();
@@ -1391,7 +1398,7 @@ br_status br_rank_prompts_timed(const br_dims* dims, const void* Q, const void* 
     const std::vector<unsigned char>& host = plan->host;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     // A reused plan is read from its device copy; a new one is uploaded into the workspace.
-    const unsigned char* img = fresh ? nullptr : device_image(*plan);
+    const unsigned char* img = fresh ? nullptr : device_image(*plan, stream);
     if (!img) {
       st = upload(ws, host.data(), host.size(), stream);
       if (st != BR_OK) return st;
