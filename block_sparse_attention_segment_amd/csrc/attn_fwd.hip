@@ -672,7 +672,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(uint16_t* __restrict__ 
                                                          const float* __restrict__ part_o,
                                                          const float* __restrict__ part_ml, int Hq, int Hkv, int G,
                                                          int q_row_base, float sink_log2) {
-  attn_merge_block<D>(blockIdx.x, O, lse, merges, part_o, part_ml, Hq, Hkv, G, q_row_base, sink_log2);
+  attn_merge_block<D, 32>(blockIdx.x, O, lse, merges, part_o, part_ml, Hq, Hkv, G, q_row_base, sink_log2);
 }
 
 template <int D, int G>

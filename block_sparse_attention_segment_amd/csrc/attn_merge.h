@@ -15,10 +15,11 @@ constexpr int merge_wg_per_tile() { return kRowsPerTile * (D / 4) / 256; }
 // Combine split-key partials of one query tile: M = max m_c, L = sum l_c 2^(m_c - M),
 // o = sum o_c 2^(m_c - M) / L, accumulated in one pass with a running maximum.  One thread
 // per (row, 4 head-dim elements); a workgroup covers 256 such units, so one (query tile, KV
-// head) spreads over 128 * D / 4 / 256 workgroups.  Chunks are visited eight at a time so
-// their loads are in flight together; the order of the sums is fixed, so the result is
-// deterministic.
-template <int D>
+// head) spreads over 128 * D / 4 / 256 workgroups.  Chunks are visited U at a time so their
+// loads are in flight together (U is chosen per kernel by its register budget); the sums are
+// added in chunk order whatever U is, so the result is deterministic and the same in both
+// kernels.
+template <int D, int U = 8>
 __device__ __forceinline__ void attn_merge_block(int block, uint16_t* __restrict__ O, float* __restrict__ lse,
                                                  const MergeItem* __restrict__ merges, const float* __restrict__ part_o,
                                                  const float* __restrict__ part_ml, int Hq, int Hkv, int G,
@@ -51,21 +52,20 @@ __device__ __forceinline__ void attn_merge_block(int block, uint16_t* __restrict
     for (int e = 0; e < 4; ++e) acc[e] = fmaf(wgt, o[e], acc[e] * a);
     M = Mn;
   };
-  constexpr int U = 8;
-  int c = 0;
-  for (; c + U <= n; c += U) {
+  for (int c = 0; c < n; c += U) {
     float2 v[U];
     f32x4_t o[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      v[u] = ml[row + (c + u) * stride];
-      o[u] = *reinterpret_cast<const f32x4_t*>(part_o + (row + (c + u) * stride) * D + ch * 4);
+      if (c + u < n) {
+        v[u] = ml[row + (c + u) * stride];
+        o[u] = *reinterpret_cast<const f32x4_t*>(part_o + (row + (c + u) * stride) * D + ch * 4);
+      }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) add(v[u], o[u]);
+    for (int u = 0; u < U; ++u)
+      if (c + u < n) add(v[u], o[u]);
   }
-  for (; c < n; ++c)
-    add(ml[row + c * stride], *reinterpret_cast<const f32x4_t*>(part_o + (row + c * stride) * D + ch * 4));
   const float inv = 1.f / (L + fast_exp2(sink_log2 - M));  // the sink slot adds exp(b) / 2^M; 0 when b = -inf
   const u32x2_t v = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
   *reinterpret_cast<u32x2_t*>(O + (int64_t(tok - q_row_base) * Hq + h) * D + ch * 4) = v;
