@@ -65,28 +65,30 @@ __device__ __forceinline__ void rope_rotate_heads(const uint16_t* src, uint16_t*
   const int o0 = kAdjacent ? 16 * c : 8 * c;
   const int o1 = kAdjacent ? 16 * c + 8 : D / 2 + 8 * c;
   const int64_t base = row * heads * D;
+  // Every element is read once and written once: both with the non-temporal hint (whole
+  // 128-byte lines: eight threads cover each half of a head vector).
   constexpr int U = 4;
   int h = 0;
   for (; h + U <= heads; h += U) {
     u32x4_t x0[U], x1[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      x0[u] = load16(src + base + int64_t(h + u) * D + o0);
-      x1[u] = load16(src + base + int64_t(h + u) * D + o1);
+      x0[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + base + int64_t(h + u) * D + o0));
+      x1[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + base + int64_t(h + u) * D + o1));
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       rope_rotate8<kAdjacent>(x0[u], x1[u], cs, sn);
-      *reinterpret_cast<u32x4_t*>(dst + base + int64_t(h + u) * D + o0) = x0[u];
-      *reinterpret_cast<u32x4_t*>(dst + base + int64_t(h + u) * D + o1) = x1[u];
+      __builtin_nontemporal_store(x0[u], reinterpret_cast<u32x4_t*>(dst + base + int64_t(h + u) * D + o0));
+      __builtin_nontemporal_store(x1[u], reinterpret_cast<u32x4_t*>(dst + base + int64_t(h + u) * D + o1));
     }
   }
   for (; h < heads; ++h) {
-    u32x4_t x0 = load16(src + base + int64_t(h) * D + o0);
-    u32x4_t x1 = load16(src + base + int64_t(h) * D + o1);
+    u32x4_t x0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + base + int64_t(h) * D + o0));
+    u32x4_t x1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + base + int64_t(h) * D + o1));
     rope_rotate8<kAdjacent>(x0, x1, cs, sn);
-    *reinterpret_cast<u32x4_t*>(dst + base + int64_t(h) * D + o0) = x0;
-    *reinterpret_cast<u32x4_t*>(dst + base + int64_t(h) * D + o1) = x1;
+    __builtin_nontemporal_store(x0, reinterpret_cast<u32x4_t*>(dst + base + int64_t(h) * D + o0));
+    __builtin_nontemporal_store(x1, reinterpret_cast<u32x4_t*>(dst + base + int64_t(h) * D + o1));
   }
 }
 
