@@ -305,6 +305,34 @@ def test_rank_step_plan_device_copies_made_and_dropped():
                 assert torch.equal(out, a_out) and torch.equal(s, a_s) and torch.equal(o, a_o), (rep, call, w.prompts)
 
 
+def test_rank_step_plan_device_copies_on_the_side_stream():
+    """The same at 25,000+ tokens, where the readout and rank run on the library's side stream:
+    five table sets of one size (document lengths permuted), two calls each, twice over, so
+    plans are reused from their device copies, evicted and made again; every call equals the
+    separate calls bit for bit."""
+    kw = dict(hq=4, hkv=2, d=64, seed=13)
+    base = [200 + 10 * i for i in range(60)]  # 60 documents, 29,700 document tokens
+    variants = []
+    for v in range(5):
+        lens = base[v:] + base[:v]
+        variants.append(workloads.make_custom([(64, lens, 32)], n_signal=4, **kw))
+    assert all(w.total_tokens >= 24576 for w in variants)
+    refs = []
+    for w in variants:
+        dev = upload(w)
+        out = br.attn_fwd(dev["Q"], dev["K"], dev["V"], w.segment_offsets, w.seg_ptr)
+        s = br.doc_scores(dev["Q_S"], dev["K"], w.doc_offsets, w.doc_ptr)
+        refs.append((dev, out, s, br.sort_docs(s, w.doc_ptr)))
+    log(f"[gpu] rank step plan device copies, side stream: five table sets of {variants[0].total_tokens} tokens")
+    for rep in range(2):
+        for w, (dev, a_out, a_s, a_o) in zip(variants, refs):
+            for call in range(2):
+                out, s, o = br.rank_step(dev["Q"], dev["K"], dev["V"], dev["Q_S"], w.segment_offsets, w.seg_ptr,
+                                         w.doc_offsets, w.doc_ptr)
+                torch.cuda.synchronize()
+                assert torch.equal(out, a_out) and torch.equal(s, a_s) and torch.equal(o, a_o), (rep, call)
+
+
 def test_many_prompts_rank_and_attention():
     """300 small prompts in one call (more than one sort launch's 256 prompts): attention against
     the dense oracle, scores and per-prompt order against the oracle's, and the one-call step equal
