@@ -62,6 +62,15 @@ def test_random_small_tables(case):
     _full_check(w, f"random case={case} prompts={prompts}")
 
 
+@pytest.mark.parametrize("hq,hkv,d", [(4, 1, 64), (32, 8, 128)])
+def test_degenerate_segments(hq, hkv, d):
+    """The smallest segments: a one-token query carrying the one signal row, one- and two-token
+    documents, an empty and a one-token instruction, a prompt with a single document."""
+    prompts = [(0, [1, 2, 1], 1), (1, [1], 1), (0, [2], 1), (1, [1, 1, 2, 1], 1)]
+    w = workloads.make_custom(prompts, hq, hkv, d, 1, 77)
+    _full_check(w, f"degenerate segments hq={hq} hkv={hkv} d={d}")
+
+
 @pytest.mark.parametrize("case", range(4))
 def test_ragged_tails_and_long_segments(case):
     """Segments longer than several tiles with ragged tails; a long prefix that forces the split-key
