@@ -63,6 +63,20 @@ def test_attn_bwd_parity(case):
     check_grad(dV, rV, "dV")
 
 
+@pytest.mark.parametrize("hq,hkv,d", [(4, 1, 64), (8, 2, 128)])
+def test_attn_bwd_degenerate_segments(hq, hkv, d):
+    """The smallest segments: one-token queries and documents, empty and one-token instructions,
+    rows that see a single key (their P is 1, so their dQ and the dK they send are zero)."""
+    prompts = [(0, [1, 2, 1], 1), (1, [1], 1), (0, [2], 1), (1, [1, 1, 2, 1], 1), (3, [5, 1], 2)]
+    w = workloads.make_custom(prompts, hq, hkv, d, 1, 2700)
+    log(f"[attn bwd degenerate] Hq={hq} Hkv={hkv} d={d} T={w.total_tokens}")
+    dQ, dK, dV, dO_bits = run_case(w, 11)
+    rQ, rK, rV = orc.attn_bwd(w.Q, w.K, w.V, dO_bits, w.segment_offsets, w.seg_ptr)
+    check_grad(dQ, rQ, "dQ")
+    check_grad(dK, rK, "dK")
+    check_grad(dV, rV, "dV")
+
+
 def test_attn_bwd_split_rows_and_scale():
     """A prompt with more than 4096 rows after its instruction (the instruction keys' row range is
     split and summed) and a non-default softmax scale."""
