@@ -1183,11 +1183,6 @@ br_status check_sort_table(const int32_t* doc_ptr, int num_prompts, std::vector<
 }
 
 
-// Ranking-step plans, validated and scheduled, with their upload image.  Serving repeats prompt
-// shapes (BlockRank pads documents to fixed chunk lengths), and planning costs about 0.15 ms per
-// call at 100K tokens, so the last few plans are kept and reused when a call's dimensions and
-// host tables equal an entry's element by element (and the device and its workgroup count
-// match).  Entries are immutable once inserted; a mutex guards the list.
 // Device copy of a cached plan's upload image.  A copy of the holder (the same tables rescheduled
 // for another device) starts without one.
 struct DeviceImage {
@@ -1198,6 +1193,12 @@ struct DeviceImage {
   DeviceImage& operator=(const DeviceImage&) = delete;
 };
 
+// Ranking-step plans, validated and scheduled, with their upload image.  Serving repeats prompt
+// shapes (BlockRank pads documents to fixed chunk lengths), and planning costs about 0.15 ms per
+// call at 100K tokens, so the last few plans are kept and reused when a call's dimensions and
+// host tables equal an entry's element by element (and the device and its workgroup count
+// match).  Entries are immutable once inserted, except for the device copy of their image, made
+// once under its own mutex; a mutex guards the list.
 struct RankPlan {
   int device = -1, workgroups = 0;
   br_dims dims{};
