@@ -83,6 +83,11 @@ struct ScorePlan {
 // read the instruction) are split into chunks of kBwdRowChunk tokens with fp32 partials.
 constexpr int kBwdKeyTile = 64;
 constexpr int kBwdRowChunk = 4096;
+// Documents whose key tiles the dK/dV pass runs together: groups close once they hold this many
+// document tokens, so that the rows the group's tiles read (Q and dO: 2048 tokens x 4 heads x
+// 512 B = 4 MB at 4 query heads per KV head and d = 128) stay in the L2 of the XCD serving the
+// head between the tiles that re-read them.
+constexpr int kBwdGroupTokens = 2048;
 struct KvItem {
   int32_t k0, k_limit, c0, c1, u0, u1, slot, rows;  // rows: row tokens visited (for accounting)
 };
